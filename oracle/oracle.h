@@ -1,0 +1,89 @@
+/*
+ * oracle.h -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, double-precision CPU definition of one pre-LayerNorm GPT layer with a KV cache,
+ * and of the group-wise symmetric int8 weight quantizer. It exists so that the GPU library can be
+ * checked against something that is obviously correct. Only the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it; the GPU library never does, and the two share no
+ * source, header, table or helper.
+ *
+ * Sources (cited by page title and section; the pages are the text of public web pages):
+ *   [KP]  "DeepSpeed Inference 内核优化深度解析：多 GPU 自适应并行、算子融合推理内核与 MoQ 量化支持"
+ *         (blog.gitcode.com) -- section 三 (3.2: the four fusion regions of one transformer layer,
+ *         3.3: the mechanisms), section 五 (5.2: int8 inference with quantize_groups), section 四
+ *         (4.2: dtype fp32/fp16/int8, max_out_tokens).
+ *   [MP]  "DeepSpeed MoE 大规模稀疏模型推理实战指南" (blog.gitcode.com) -- the inference-config table,
+ *         row triangular_masking (default True: the attention score mask type).
+ *
+ * Where the pages are silent the oracle takes these readings (each is listed in the design doc):
+ *   LayerNorm uses the biased variance and eps = 1e-5 unless the caller passes another eps;
+ *   GeLU is the exact erf form u*Phi(u) unless gelu_tanh is set; the attention scale is 1/sqrt(d);
+ *   Q, K, V are rows [0,H), [H,2H), [2H,3H) of the fused projection, head j owning [j*d,(j+1)*d);
+ *   the order inside region 3 is Wo -> +bo -> +x -> LN2 -> W1 -> +b1 -> GeLU, then W2 -> +b2 -> +x2;
+ *   keys past a row's own position are excluded from its softmax (not added as -inf);
+ *   int8 groups are 64 consecutive elements along the reduction dimension of one weight row,
+ *   scale = fp16_RNE(amax/127), code = clamp(round_half_even(w/scale), -127, 127), amax = 0 -> 0.
+ *
+ * Layouts: every matrix is [N][K] row-major (K contiguous); activations are [B][T][width];
+ * the K and V caches are [B][heads][cap][head_dim]; lens[b] is the number of filled cache rows.
+ */
+#ifndef DS_ORACLE_H
+#define DS_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int hidden, heads, head_dim, ffn;
+  double ln_eps;
+  int gelu_tanh;           /* 0: u*Phi(u) with erf; 1: the tanh approximation            */
+  int triangular_masking;  /* 1: row at position p sees keys 0..p; 0: sees every key     */
+} ora_desc;
+
+typedef struct {
+  const double *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o;
+  const double *ln2_g, *ln2_b, *w_ff1, *b_ff1, *w_ff2, *b_ff2;
+} ora_weights;
+
+/* Optional per-stage outputs (NULL entries are skipped), each [B][T][width]. */
+typedef struct {
+  double *ln1;  /* width H  : LN1(x)                         */
+  double *qkv;  /* width 3H : Wqkv LN1(x) + bqkv             */
+  double *ctx;  /* width H  : attention output, heads concatenated */
+  double *x2;   /* width H  : x + Wo ctx + bo                */
+  double *ln2;  /* width H  : LN2(x2)                        */
+  double *ff1;  /* width F  : W1 LN2(x2) + b1 (pre-activation) */
+  double *act;  /* width F  : GeLU of ff1                    */
+} ora_stages;
+
+/* ---- single steps ---- */
+void   ora_layernorm(const double* x, int n, const double* g, const double* b, double eps, double* out);
+void   ora_linear(const double* w, const double* bias, const double* x, int n_out, int k, double* out);
+double ora_gelu(double u, int tanh_form);
+void   ora_softmax(const double* s, int n, double* p);
+/* One query against keys/values 0..nkeys-1 of one head ([nkeys][d] each). */
+void   ora_attend(const double* q, const double* keys, const double* vals, int nkeys, int d, double* out);
+
+/* ---- the layer ----
+ * Appends the T new rows of K and V at rows lens[b]..lens[b]+T-1, then attends, then advances
+ * lens[b] by T. Returns 0, or -1 when a shape is inconsistent or the cache would overflow. */
+int ora_layer_forward(const ora_desc* desc, const ora_weights* w, double* k_cache, double* v_cache,
+                      int cap, int* lens, const double* x, double* y, int batch, int ntok,
+                      ora_stages* stages);
+
+/* ---- IEEE binary16 ---- */
+uint16_t ora_fp16_from_double(double v); /* round to nearest, ties to even; overflow -> inf */
+double   ora_fp16_to_double(uint16_t h);
+
+/* ---- group-wise symmetric int8 ([KP] section 五 5.2) ----
+ * w: float32 [n][k]; q: int8 [n][k]; s: fp16 bits [n][k/group]. Returns 0, or -1 if k % group. */
+int  ora_quantize_i8(const float* w, int n, int k, int group, int8_t* q, uint16_t* s);
+/* w = q * s in double (exact). */
+int  ora_dequantize_i8(const int8_t* q, const uint16_t* s, int n, int k, int group, double* w);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

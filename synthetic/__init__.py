@@ -1,0 +1,108 @@
+"""Seeded synthetic inputs and the workload shapes.
+
+This module draws random numbers and names shapes; it holds none of the layer's arithmetic. Both
+the oracle side (tests, CPU baseline) and the GPU side (tests, benchmark, smoke check) take their
+inputs from here.
+
+Recipe (the pages' workloads are trained GPT-2 / GPT-Neo / Turing-NLG / GPT-3-like models whose
+weights are not available; seeded draws of the same shapes stand in for them):
+  weights ~ N(0, 0.02), biases ~ N(0, 0.01), LayerNorm gamma = 1, beta = 0,
+  activations x ~ N(0, 1), past K/V cache rows ~ N(0, 1).
+Draws are float32 from torch's generator on the requested device, seeded from
+(config id, layer, tensor id) through numpy's SeedSequence; the caller rounds them to the
+target dtype (round to nearest even). A given key always yields the same tensor on a given
+device type; CPU and GPU generators yield different (equally distributed) streams, so a parity
+test draws once and hands the same values to both sides.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+# tensor ids
+LN1_G, LN1_B, W_QKV, B_QKV, W_O, B_O, LN2_G, LN2_B, W_FF1, B_FF1, W_FF2, B_FF2, K_PAST, V_PAST = range(14)
+X_LAYER = 65535  # layer slot used for the stack input x
+
+WEIGHT_NAMES = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
+                "ln2_g", "ln2_b", "w_ff1", "b_ff1", "w_ff2", "b_ff2")
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg_id: int
+    hidden: int
+    heads: int
+    head_dim: int
+    ffn: int
+    layers: int
+    weight_dtype: str  # "f32" | "f16" | "i8"
+    act_dtype: str     # "f32" | "f16"
+    batch: int
+    past: int          # filled cache rows before the step (decode) or P0 (prefill)
+    seq: int = 1       # new rows per sequence: 1 for decode, S for prefill
+    group: int = 0     # int8 group size along the reduction dimension
+    extra: dict = field(default_factory=dict, compare=False, hash=False)
+
+    @property
+    def capacity(self) -> int:
+        # room for the past rows, this step's rows, and a little headroom, rounded to 64 rows
+        need = self.past + self.seq + 1
+        return (need + 63) // 64 * 64
+
+
+WORKLOADS = {
+    # one pre-LN layer, fp32, tiny: the parity case
+    "c1": Workload("c1-fp32-h256", 1, 256, 4, 64, 1024, 1, "f32", "f32", 1, 32),
+    # GPT-Neo-2.7B-shaped stack, fp16, batch-1 decode against 512 past rows
+    "c2": Workload("c2-gptneo2.7b-f16-b1-p512", 2, 2560, 20, 128, 10240, 32, "f16", "f16", 1, 512),
+    # 13B-shaped stack, fp16, batch-8 decode against 1024 past rows
+    "c3": Workload("c3-13b-f16-b8-p1024", 3, 5120, 40, 128, 20480, 40, "f16", "f16", 8, 1024),
+    # 13B shapes, int8 weights (group 64, fp16 scales), fp16 activations, batch 1 and 8
+    "c4b1": Workload("c4-13b-i8g64-b1-p1024", 4, 5120, 40, 128, 20480, 40, "i8", "f16", 1, 1024, group=64),
+    "c4b8": Workload("c4-13b-i8g64-b8-p1024", 4, 5120, 40, 128, 20480, 40, "i8", "f16", 8, 1024, group=64),
+    # prefill on the GPT-Neo-2.7B shapes: batch 4 x 512 prompt rows, causal
+    "c5": Workload("c5-gptneo2.7b-f16-prefill-b4s512", 5, 2560, 20, 128, 10240, 32, "f16", "f16", 4, 0, seq=512),
+}
+
+
+def seed_of(cfg_id: int, layer: int, tensor_id: int) -> int:
+    ss = np.random.SeedSequence([cfg_id, layer, tensor_id])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def normal(shape, std: float, cfg_id: int, layer: int, tensor_id: int, device="cpu") -> torch.Tensor:
+    """float32 N(0, std^2) draws of the given shape, seeded by (cfg_id, layer, tensor_id)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of(cfg_id, layer, tensor_id))
+    t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    return t.mul_(std) if std != 1.0 else t
+
+
+def layer_weights_f32(wl: Workload, layer: int, device="cpu") -> dict:
+    """The twelve float32 parameter tensors of one layer (weights [N,K] row-major)."""
+    H, F, c = wl.hidden, wl.ffn, wl.cfg_id
+    return {
+        "ln1_g": torch.ones(H, device=device), "ln1_b": torch.zeros(H, device=device),
+        "w_qkv": normal((3 * H, H), 0.02, c, layer, W_QKV, device),
+        "b_qkv": normal((3 * H,), 0.01, c, layer, B_QKV, device),
+        "w_o": normal((H, H), 0.02, c, layer, W_O, device),
+        "b_o": normal((H,), 0.01, c, layer, B_O, device),
+        "ln2_g": torch.ones(H, device=device), "ln2_b": torch.zeros(H, device=device),
+        "w_ff1": normal((F, H), 0.02, c, layer, W_FF1, device),
+        "b_ff1": normal((F,), 0.01, c, layer, B_FF1, device),
+        "w_ff2": normal((H, F), 0.02, c, layer, W_FF2, device),
+        "b_ff2": normal((H,), 0.01, c, layer, B_FF2, device),
+    }
+
+
+def past_kv_f32(wl: Workload, layer: int, device="cpu"):
+    """float32 [B, heads, past, head_dim] draws for the filled cache rows (K and V)."""
+    shape = (wl.batch, wl.heads, wl.past, wl.head_dim)
+    return (normal(shape, 1.0, wl.cfg_id, layer, K_PAST, device),
+            normal(shape, 1.0, wl.cfg_id, layer, V_PAST, device))
+
+
+def stack_input_f32(wl: Workload, device="cpu", step: int = 0) -> torch.Tensor:
+    """float32 [B, T, H] N(0,1) input rows of the stack."""
+    return normal((wl.batch, wl.seq, wl.hidden), 1.0, wl.cfg_id, X_LAYER, step, device)

@@ -1,0 +1,319 @@
+"""Pins of the oracle to things other than itself (CPU only).
+
+Each test checks the oracle against a closed form, an invariant, a hand-worked example
+(tests/golden/) or an independent library routine (torch float64 on the CPU), chosen so that a
+plausible mistake -- a dropped bias, a wrong sign or index, a transposed operand, an off-by-one in
+the mask, a wrong variance or scale -- fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fn
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+# ------------------------------------------------------------------ LayerNorm
+@pytest.mark.parametrize("n", [4, 63, 256, 2560])
+def test_layernorm_mean_zero_and_closed_form_variance(n):
+    x = rng.normal(0.3, 1.7, n)
+    out = oracle.layernorm(x, np.ones(n), np.zeros(n), 1e-5)
+    var = np.mean((x - x.mean()) ** 2)  # biased variance of the input
+    assert abs(out.mean()) < 1e-12
+    # with gamma=1, beta=0 the output variance is var/(var+eps) exactly
+    assert abs(np.mean(out ** 2) - var / (var + 1e-5)) < 1e-12
+
+
+def test_layernorm_hand_example():
+    # [1,2,3,4]: mean 2.5, biased variance 1.25
+    out = oracle.layernorm(np.array([1.0, 2, 3, 4]), np.ones(4), np.zeros(4), 1e-5)
+    expect = (np.array([1.0, 2, 3, 4]) - 2.5) / math.sqrt(1.25 + 1e-5)
+    assert np.max(np.abs(out - expect)) < 1e-15
+
+
+def test_layernorm_affine_and_torch():
+    n = 96
+    x, g, b = rng.normal(size=n), rng.normal(size=n), rng.normal(size=n)
+    plain = oracle.layernorm(x, np.ones(n), np.zeros(n), 1e-5)
+    out = oracle.layernorm(x, g, b, 1e-5)
+    assert np.max(np.abs(out - (plain * g + b))) < 1e-13
+    ref = Fn.layer_norm(torch.tensor(x), (n,), torch.tensor(g), torch.tensor(b), 1e-5).numpy()
+    assert np.max(np.abs(out - ref)) < 1e-13
+
+
+# ------------------------------------------------------------------ GEMV
+@pytest.mark.parametrize("n,k", [(1, 1), (3, 65), (63, 64), (64, 3), (65, 63)])
+def test_linear_small_integers_exact(n, k):
+    # small integers make every product and partial sum exact in double
+    w = rng.integers(-5, 6, (n, k)).astype(np.float64)
+    x = rng.integers(-5, 6, k).astype(np.float64)
+    b = rng.integers(-5, 6, n).astype(np.float64)
+    out = oracle.linear(w, b, x)
+    ref = (torch.tensor(w) @ torch.tensor(x) + torch.tensor(b)).numpy()
+    assert np.array_equal(out, ref)
+
+
+def test_linear_closed_forms():
+    k = 37
+    x = rng.normal(size=k)
+    assert np.array_equal(oracle.linear(np.eye(k), None, x), x)                # identity
+    ones = oracle.linear(np.ones((5, k)), np.arange(5.0), np.arange(1.0, k + 1))
+    assert np.array_equal(ones, k * (k + 1) / 2 + np.arange(5.0))              # sum 1..k + bias
+    # a non-square shape catches a transposed operand: row o of [n,k] meets x
+    w = np.zeros((3, k))
+    w[2, 5] = 1.0
+    assert np.array_equal(oracle.linear(w, None, x), np.array([0.0, 0.0, x[5]]))
+
+
+def test_linear_matches_torch_float64():
+    w, x, b = rng.normal(size=(70, 129)), rng.normal(size=129), rng.normal(size=70)
+    ref = Fn.linear(torch.tensor(x), torch.tensor(w), torch.tensor(b)).numpy()
+    assert np.max(np.abs(oracle.linear(w, b, x) - ref)) < 1e-13
+
+
+# ------------------------------------------------------------------ GeLU
+def test_gelu_textbook_values():
+    # GeLU(u) = u * Phi(u); Phi(1) = 0.8413447460685429, Phi(2) = 0.9772498680518208 (normal table)
+    assert oracle.gelu(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.gelu(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15
+    assert abs(oracle.gelu(np.array([-1.0]))[0] - (-1.0 + 0.8413447460685429)) < 1e-15
+    assert abs(oracle.gelu(np.array([2.0]))[0] - 2 * 0.9772498680518208) < 1e-15
+
+
+def test_gelu_odd_identity_and_torch():
+    u = rng.normal(0, 3, 200)
+    g, gm = oracle.gelu(u), oracle.gelu(-u)
+    assert np.max(np.abs(g - gm - u)) < 1e-14      # u Phi(u) - (-u) Phi(-u) = u since Phi(u) + Phi(-u) = 1
+    ref = Fn.gelu(torch.tensor(u)).numpy()
+    assert np.max(np.abs(g - ref)) < 1e-14
+    ref_t = Fn.gelu(torch.tensor(u), approximate="tanh").numpy()
+    assert np.max(np.abs(oracle.gelu(u, tanh_form=True) - ref_t)) < 1e-14
+
+
+# ------------------------------------------------------------------ softmax / attention
+def test_softmax_invariants():
+    s = rng.normal(size=50)
+    p = oracle.softmax(s)
+    assert abs(p.sum() - 1.0) < 1e-14
+    assert np.max(np.abs(oracle.softmax(s + 123.25) - p)) < 1e-15   # shift invariance
+    one = oracle.softmax(np.array([0.0, 1000.0, 0.0]))
+    assert np.array_equal(one, np.array([0.0, 1.0, 0.0]))
+    assert np.max(np.abs(p - torch.softmax(torch.tensor(s), 0).numpy())) < 1e-15
+
+
+def test_attend_single_key_and_identical_keys():
+    d = 64
+    q, k, v = rng.normal(size=d), rng.normal(size=(1, d)), rng.normal(size=(1, d))
+    assert np.array_equal(oracle.attend(q, k, v), v[0])          # one key: weight exactly 1
+    keys = np.tile(rng.normal(size=d), (7, 1))
+    vals = rng.normal(size=(7, d))
+    assert np.max(np.abs(oracle.attend(q, keys, vals) - vals.mean(0))) < 1e-15
+
+
+def test_attend_matches_sdpa():
+    d, n = 128, 33
+    q, k, v = rng.normal(size=d), rng.normal(size=(n, d)), rng.normal(size=(n, d))
+    ref = Fn.scaled_dot_product_attention(torch.tensor(q)[None, None], torch.tensor(k)[None],
+                                          torch.tensor(v)[None]).numpy()[0, 0]
+    assert np.max(np.abs(oracle.attend(q, k, v) - ref)) < 1e-14
+
+
+# ------------------------------------------------------------------ fp16 and the quantizer
+def test_fp16_golden_cases():
+    cases = json.load(open(os.path.join(GOLD, "fp16_rounding.json")))["cases"]
+    for c in cases:
+        assert int(oracle.fp16_from_double(np.array([c["x"]]))[0]) == c["bits"], c
+
+
+def test_fp16_matches_numpy_rounding():
+    # numpy's float64 -> float16 cast is round-to-nearest-even; probe normals, subnormals,
+    # exact midpoints between neighbours, and the overflow boundary
+    v = np.concatenate([rng.normal(0, 1, 2000), rng.normal(0, 1e-5, 500), rng.normal(0, 3e4, 500)])
+    h = np.arange(0, 0x7bff, 37, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (h[:-1] + np.nextafter(h[:-1].astype(np.float16), np.float16(np.inf)).astype(np.float64)) / 2
+    v = np.concatenate([v, mids, -mids, [65504.0, 65519.0, 65520.0, 1e6, 0.0]])
+    ours = oracle.fp16_from_double(v)
+    ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+    # and every non-NaN bit pattern widens to numpy's value
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    back = oracle.fp16_to_double(allh)
+    ref_back = allh.view(np.float16).astype(np.float64)
+    ok = ~np.isnan(ref_back)
+    assert np.array_equal(back[ok], ref_back[ok]) and np.all(np.isnan(back[~ok]))
+
+
+def test_quantizer_golden_examples():
+    gold = json.load(open(os.path.join(GOLD, "quant_group_examples.json")))
+    G = gold["group"]
+    for c in gold["cases"]:
+        w = np.zeros((1, G), dtype=np.float32)
+        w[0, :len(c["w_head"])] = c["w_head"]
+        q, s = oracle.quantize_i8(w, G)
+        assert int(s[0, 0]) == c["scale_bits"], c["name"]
+        assert oracle.fp16_to_double(s)[0, 0] == c["scale_value"]
+        assert list(q[0, :len(c["q_head"])]) == c["q_head"], c["name"]
+        assert not q[0, len(c["q_head"]):].any()
+
+
+def test_quantizer_bounds_and_idempotence():
+    w = (rng.normal(0, 0.02, (48, 256))).astype(np.float32)
+    w[3, 64:128] = 0.0                      # one all-zero group
+    w[5, 7] = 0.9                           # one outlier
+    q, s = oracle.quantize_i8(w, 64)
+    sv = oracle.fp16_to_double(s)
+    deq = oracle.dequantize_i8(q, s, 64)
+    per = np.repeat(sv, 64, axis=1)
+    assert np.all(np.abs(w.astype(np.float64) - deq) <= per / 2 * (1 + 1e-12))   # |w - q s| <= s/2
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    amax = np.abs(w.reshape(48, 4, 64)).max(-1)
+    qmax = np.abs(q.astype(int).reshape(48, 4, 64)).max(-1)
+    assert np.all(qmax[amax > 0] == 127) and np.all(qmax[amax == 0] == 0)
+    assert sv[3, 1] == 0.0
+    # dequantized values are exact in float32, and quantizing them again returns (q, s)
+    assert np.array_equal(deq.astype(np.float32).astype(np.float64), deq)
+    q2, s2 = oracle.quantize_i8(deq.astype(np.float32), 64)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+# ------------------------------------------------------------------ the whole layer
+def _rand_layer(H, nh, F, seed, zero=()):
+    r = np.random.default_rng(seed)
+    w = {"ln1_g": r.normal(1, 0.1, H), "ln1_b": r.normal(0, 0.1, H),
+         "w_qkv": r.normal(0, 0.05, (3 * H, H)), "b_qkv": r.normal(0, 0.1, 3 * H),
+         "w_o": r.normal(0, 0.05, (H, H)), "b_o": r.normal(0, 0.1, H),
+         "ln2_g": r.normal(1, 0.1, H), "ln2_b": r.normal(0, 0.1, H),
+         "w_ff1": r.normal(0, 0.05, (F, H)), "b_ff1": r.normal(0, 0.1, F),
+         "w_ff2": r.normal(0, 0.05, (H, F)), "b_ff2": r.normal(0, 0.1, H)}
+    for z in zero:
+        w[z] = np.zeros_like(w[z])
+    return w
+
+
+def _cache(B, nh, cap, d, past, seed):
+    r = np.random.default_rng(seed)
+    k = np.zeros((B, nh, cap, d))
+    v = np.zeros((B, nh, cap, d))
+    k[:, :, :past] = r.normal(size=(B, nh, past, d))
+    v[:, :, :past] = r.normal(size=(B, nh, past, d))
+    return k, v, np.full(B, past, dtype=np.int32)
+
+
+def _torch_layer(w, kpast, vpast, x, causal=True):
+    """float64 composition of torch library ops: layer_norm, linear, SDPA, gelu."""
+    t = {n: torch.tensor(a) for n, a in w.items()}
+    B, T, H = x.shape
+    nh, P, d = kpast.shape[1], kpast.shape[2], kpast.shape[3]
+    xt = torch.tensor(x)
+    h = Fn.layer_norm(xt, (H,), t["ln1_g"], t["ln1_b"], 1e-5)
+    z = Fn.linear(h, t["w_qkv"], t["b_qkv"])
+    q, k, v = z[..., :H], z[..., H:2 * H], z[..., 2 * H:]
+    sh = lambda a: a.reshape(B, T, nh, d).permute(0, 2, 1, 3)
+    K = torch.cat([torch.tensor(kpast), sh(k)], 2)
+    V = torch.cat([torch.tensor(vpast), sh(v)], 2)
+    mask = None
+    if causal:
+        pos_q = torch.arange(T)[:, None] + P
+        mask = torch.arange(P + T)[None, :] <= pos_q
+    ctx = Fn.scaled_dot_product_attention(sh(q), K, V, attn_mask=mask)
+    ctx = ctx.permute(0, 2, 1, 3).reshape(B, T, H)
+    x2 = xt + Fn.linear(ctx, t["w_o"], t["b_o"])
+    g = Fn.gelu(Fn.linear(Fn.layer_norm(x2, (H,), t["ln2_g"], t["ln2_b"], 1e-5), t["w_ff1"], t["b_ff1"]))
+    return (x2 + Fn.linear(g, t["w_ff2"], t["b_ff2"])).numpy(), K.numpy(), V.numpy()
+
+
+@pytest.mark.parametrize("B,T,past,causal", [(1, 1, 32, True), (2, 5, 7, True), (2, 4, 3, False), (1, 6, 0, True)])
+def test_layer_matches_torch_composition(B, T, past, causal):
+    H, nh, F = 64, 4, 128
+    d = H // nh
+    w = _rand_layer(H, nh, F, 5)
+    k, v, lens = _cache(B, nh, past + T + 2, d, past, 6)
+    x = np.random.default_rng(7).normal(size=(B, T, H))
+    kpast, vpast = k[:, :, :past].copy(), v[:, :, :past].copy()
+    desc = oracle.Desc(H, nh, d, F, triangular_masking=causal)
+    y = oracle.layer_forward(desc, w, k, v, lens, x)
+    ref, K, V = _torch_layer(w, kpast, vpast, x, causal)
+    assert np.max(np.abs(y - ref)) < 1e-12
+    assert np.max(np.abs(k[:, :, :past + T] - K)) < 1e-13 and np.max(np.abs(v[:, :, :past + T] - V)) < 1e-13
+    assert np.all(lens == past + T)
+
+
+def test_layer_zero_weights_is_identity():
+    H, nh, F = 64, 2, 96
+    w = _rand_layer(H, nh, F, 1, zero=("w_qkv", "b_qkv", "w_o", "b_o", "w_ff1", "b_ff1", "w_ff2", "b_ff2"))
+    k, v, lens = _cache(1, nh, 16, H // nh, 9, 2)
+    x = np.random.default_rng(3).normal(size=(1, 1, H))
+    y = oracle.layer_forward(oracle.Desc(H, nh, H // nh, F), w, k, v, lens, x)
+    assert np.array_equal(y, x)
+
+
+def test_layer_output_projections_zero_gives_biases():
+    H, nh, F = 64, 2, 96
+    w = _rand_layer(H, nh, F, 4, zero=("w_o", "w_ff2"))
+    k, v, lens = _cache(2, nh, 16, H // nh, 5, 2)
+    x = np.random.default_rng(3).normal(size=(2, 3, H))
+    y = oracle.layer_forward(oracle.Desc(H, nh, H // nh, F), w, k, v, lens, x)
+    assert np.array_equal(y, (x + w["b_o"]) + w["b_ff2"])
+
+
+def test_layer_batch_independence():
+    H, nh, F = 64, 4, 128
+    w = _rand_layer(H, nh, F, 8)
+    k, v, lens = _cache(3, nh, 20, H // nh, 6, 9)
+    x = np.random.default_rng(10).normal(size=(3, 2, H))
+    kk, vv, ll = k.copy(), v.copy(), lens.copy()
+    y = oracle.layer_forward(oracle.Desc(H, nh, H // nh, F), w, k, v, lens, x)
+    for b in range(3):
+        k1, v1, l1 = kk[b:b + 1].copy(), vv[b:b + 1].copy(), ll[b:b + 1].copy()
+        y1 = oracle.layer_forward(oracle.Desc(H, nh, H // nh, F), w, k1, v1, l1, x[b:b + 1])
+        assert np.array_equal(y1, y[b:b + 1])
+
+
+def test_layer_causal_zero_leakage_and_prefill_decode_consistency():
+    H, nh, F, S = 64, 4, 128, 9
+    desc = oracle.Desc(H, nh, H // nh, F)
+    w = _rand_layer(H, nh, F, 11)
+    x = np.random.default_rng(12).normal(size=(1, S, H))
+    k, v, lens = _cache(1, nh, 16, H // nh, 0, 0)
+    y = oracle.layer_forward(desc, w, k, v, lens, x)
+    # perturbing row 6 leaves rows 0..5 bit-identical
+    x2 = x.copy()
+    x2[0, 6] += 1.0
+    k2, v2, l2 = _cache(1, nh, 16, H // nh, 0, 0)
+    y2 = oracle.layer_forward(desc, w, k2, v2, l2, x2)
+    assert np.array_equal(y[0, :6], y2[0, :6]) and not np.array_equal(y[0, 6], y2[0, 6])
+    # prefill of S-1 rows, then one decode row, reproduces the last row of prefill(S)
+    k3, v3, l3 = _cache(1, nh, 16, H // nh, 0, 0)
+    oracle.layer_forward(desc, w, k3, v3, l3, x[:, :S - 1])
+    ylast = oracle.layer_forward(desc, w, k3, v3, l3, x[:, S - 1:])
+    assert np.max(np.abs(ylast[0, 0] - y[0, S - 1])) < 1e-12
+    assert np.max(np.abs(k3 - k)) < 1e-13
+
+
+def test_layer_stage_outputs_consistent():
+    H, nh, F = 64, 4, 128
+    desc = oracle.Desc(H, nh, H // nh, F)
+    w = _rand_layer(H, nh, F, 13)
+    k, v, lens = _cache(1, nh, 12, H // nh, 4, 14)
+    x = np.random.default_rng(15).normal(size=(1, 1, H))
+    y, st = oracle.layer_forward(desc, w, k, v, lens, x, stages=True)
+    ref = Fn.layer_norm(torch.tensor(x), (H,), torch.tensor(w["ln1_g"]), torch.tensor(w["ln1_b"]), 1e-5).numpy()
+    assert np.max(np.abs(st["ln1"] - ref)) < 1e-13
+    assert np.max(np.abs(st["x2"] - (x + st["ctx"] @ w["w_o"].T + w["b_o"]))) < 1e-12
+    assert np.max(np.abs(st["act"] - Fn.gelu(torch.tensor(st["ff1"])).numpy())) < 1e-13
+    assert np.max(np.abs(y - (st["x2"] + st["act"] @ w["w_ff2"].T + w["b_ff2"]))) < 1e-12
+
+
+def test_layer_rejects_overflow():
+    H, nh, F = 64, 4, 128
+    w = _rand_layer(H, nh, F, 1)
+    k, v, lens = _cache(1, nh, 8, H // nh, 8, 2)
+    with pytest.raises(ValueError):
+        oracle.layer_forward(oracle.Desc(H, nh, H // nh, F), w, k, v, lens, np.zeros((1, 1, H)))
