@@ -1,0 +1,168 @@
+/*
+ * ds_layer.h -- C ABI of libdslayer.so: one pre-LayerNorm GPT transformer layer with a KV cache,
+ * for small-batch decode and for prefill, on one AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes follows the customized transformer-block inference kernels described on
+ * the page "DeepSpeed Inference 内核优化深度解析：多 GPU 自适应并行、算子融合推理内核与 MoQ 量化支持"
+ * (blog.gitcode.com), cited below as [KP]:
+ *   [KP] section 三 3.2, region 1: input LayerNorm, then the Q, K, V GeMMs with their bias-adds;
+ *   [KP] section 三 3.2, region 2: the head "transform" merged into attention by implicit
+ *        addressing (here: K and V rows are written straight into the head-major cache);
+ *   [KP] section 三 3.2, region 3: intermediate FF with LayerNorm, bias-add, residual and GELU;
+ *   [KP] section 三 3.2, region 4: bias-add and residual on the layer output;
+ *   [KP] section 三 3.1: fusion boundaries sit at the two all-reduce points (after the attention
+ *        output GeMM and after the layer output GeMM);
+ *   [KP] section 五 5.2 and section 四 4.2: int8 weights with group-wise scales (quantize_groups),
+ *        dtype fp32 / fp16 / int8 (default fp16), max_out_tokens bounds the generated length.
+ * The attention mask follows the triangular_masking option (default true) of the inference-config
+ * table on the page "DeepSpeed MoE 大规模稀疏模型推理实战指南" (blog.gitcode.com), cited as [MP].
+ *
+ * Per new row at absolute position p of sequence b (pre-LN):
+ *   h  = LN(x; ln1_g, ln1_b)                  z = W_qkv h + b_qkv = [q | k | v]
+ *   K[b][j][p] = k_j, V[b][j][p] = v_j         (head j owns elements [j*d, (j+1)*d))
+ *   ctx_j = sum_i softmax_i(q_j . K[b][j][i] / sqrt(d)) V[b][j][i]   over keys i visible to p
+ *   x2 = x + W_o ctx + b_o
+ *   f  = GeLU(W_ff1 LN(x2; ln2_g, ln2_b) + b_ff1)
+ *   y  = x2 + W_ff2 f + b_ff2
+ * LayerNorm uses the biased variance; GeLU is u*Phi(u) (erf) or its tanh approximation.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked "host". The caller allocates and owns all device
+ *    memory (weights, scales, caches, lengths, activations, workspace); the library only borrows
+ *    it. Weights and caches must outlive every call that uses them. A ds_layer_t is a small host
+ *    object owned by the library, released by ds_layer_destroy.
+ *  - Matrices are [N][K] row-major (K contiguous): W_qkv [3H][H], W_o [H][H], W_ff1 [F][H],
+ *    W_ff2 [H][F]. int8 scales are fp16 [N][K/quant_group]: element (n,k) = q[n][k] * s[n][k/group].
+ *    Every weight, scale, bias, LayerNorm, cache and activation pointer must be 16-byte aligned.
+ *  - Enqueueing calls put their work on `stream` (a hipStream_t; NULL is the null stream) and
+ *    return without waiting. They allocate nothing and never synchronize, so they can be captured
+ *    into a HIP graph.
+ *  - Every call returns DS_OK (0) or a negative ds_status. Argument, shape and capacity errors are
+ *    found on the host before anything is enqueued and leave all buffers untouched; a failed
+ *    launch returns DS_ERR_HIP. ds_last_error() then gives a message (per calling thread).
+ *    No C++ exception crosses this interface.
+ */
+#ifndef DS_LAYER_H
+#define DS_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DS_F32 = 0, DS_F16 = 1, DS_I8 = 2 } ds_dtype;
+
+typedef enum {
+  DS_OK = 0,
+  DS_ERR_NULL = -1,        /* a required pointer is NULL                                      */
+  DS_ERR_SHAPE = -2,       /* inconsistent or unsupported sizes                               */
+  DS_ERR_DTYPE = -3,       /* unsupported (weight, activation) dtype pair or group size       */
+  DS_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                                */
+  DS_ERR_KV_FULL = -5,     /* the step would write past the cache capacity                    */
+  DS_ERR_UNSUPPORTED = -6, /* a valid request this build does not implement                   */
+  DS_ERR_HIP = -7,         /* the HIP runtime reported an error                               */
+  DS_ERR_WORKSPACE = -8    /* the workspace is smaller than ds_layer_workspace_bytes()        */
+} ds_status;
+
+/* The layer description ([KP] section 四 4.2 and section 五 5.2; [MP] config table). */
+typedef struct {
+  int32_t hidden;             /* H = heads * head_dim; a multiple of 64                         */
+  int32_t heads;              /* number of attention heads                                      */
+  int32_t head_dim;           /* d: 64 or 128                                                   */
+  int32_t ffn;                /* F: intermediate width, a multiple of 64                        */
+  int32_t weight_dtype;       /* ds_dtype of W_qkv, W_o, W_ff1, W_ff2                           */
+  int32_t act_dtype;          /* ds_dtype of x, y, the caches, biases and LayerNorm parameters  */
+                              /* supported pairs: (F32,F32) (F16,F16) (I8,F16)                  */
+  int32_t quant_group;        /* 64 when weight_dtype is DS_I8, else 0                          */
+  float ln_eps;               /* LayerNorm epsilon, > 0 (1e-5 by default)                       */
+  int32_t gelu_tanh;          /* 0: u*Phi(u) with erf (default); 1: tanh approximation          */
+  int32_t triangular_masking; /* 1 (default): a row at position p sees keys 0..p; 0: all keys   */
+} ds_layer_desc;
+
+/* Borrowed device pointers to one layer's parameters. s_* are the fp16 group scales of the int8
+ * matrices and must be NULL unless weight_dtype is DS_I8. Biases and LayerNorm vectors are in
+ * act_dtype. */
+typedef struct {
+  const void *ln1_g, *ln1_b;
+  const void *w_qkv, *b_qkv, *s_qkv;
+  const void *w_o, *b_o, *s_o;
+  const void *ln2_g, *ln2_b;
+  const void *w_ff1, *b_ff1, *s_ff1;
+  const void *w_ff2, *b_ff2, *s_ff2;
+} ds_layer_weights;
+
+/* A caller-owned KV cache for one layer. k and v are [batch][heads][capacity][head_dim] in
+ * act_dtype. d_len is a device int32[batch] holding the number of filled rows of each sequence;
+ * decode and prefill write the new rows at d_len[b].. and then add the number of new rows to it.
+ * h_len is an optional HOST int32[batch] mirror of d_len: when it is not NULL the library checks
+ * capacity against it before enqueueing and advances it at enqueue time (a graph replay does not
+ * advance it). When h_len is NULL the kernels clamp: a row that would land at or past capacity is
+ * not written and the sequence's length is not advanced. */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t* d_len;
+  int32_t* h_len;
+  int32_t batch;
+  int32_t capacity;
+} ds_kv_cache;
+
+typedef struct ds_layer ds_layer_t;
+
+/* Validates the description and the weight pointers on the host (no device work) and returns a
+ * handle that borrows the weights. Errors: DS_ERR_NULL, DS_ERR_SHAPE, DS_ERR_DTYPE, DS_ERR_ALIGN. */
+int ds_layer_create(const ds_layer_desc* desc, const ds_layer_weights* weights, ds_layer_t** out);
+
+/* Releases the handle (not the borrowed memory). NULL is accepted. */
+int ds_layer_destroy(ds_layer_t* layer);
+
+/* Bytes of device workspace that decode (max_tokens == 1) or prefill needs for up to max_batch
+ * sequences of max_tokens new rows against caches of `capacity` rows. Returns 0 on bad input. */
+size_t ds_layer_workspace_bytes(const ds_layer_t* layer, int32_t max_batch, int32_t max_tokens,
+                                int32_t capacity);
+
+/* Copies ntok new rows of keys and values, k_new and v_new [batch][ntok][hidden] in act_dtype,
+ * into cache rows d_len[b] .. d_len[b]+ntok-1 (head j taking elements [j*d,(j+1)*d)), then adds
+ * ntok to d_len[b] (and to h_len[b] when given). Used to fill a cache with given past rows. */
+int ds_kv_append(const ds_layer_t* layer, ds_kv_cache* kv, const void* k_new, const void* v_new,
+                 int32_t batch, int32_t ntok, void* stream);
+
+/* One decode step ([KP] section 三 3.2, regions 1-4) for `batch` sequences of one new row each:
+ * x, y [batch][hidden] in act_dtype (y may alias x; no other aliasing). Writes the new K and V
+ * rows at d_len[b], attends over rows 0..d_len[b], advances d_len[b] by one. The workspace must
+ * hold ds_layer_workspace_bytes(layer, batch, 1, kv->capacity) bytes; its contents need no
+ * initialization and are scratch between calls. */
+int ds_layer_forward_decode(const ds_layer_t* layer, ds_kv_cache* kv, const void* x, void* y,
+                            int32_t batch, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Prefill of `seq` new rows per sequence (the same layer, with the mask of triangular_masking):
+ * x, y [batch][seq][hidden] in act_dtype (y may alias x). Fills cache rows d_len[b]..+seq-1 and
+ * advances d_len[b] by seq. Workspace: ds_layer_workspace_bytes(layer, batch, seq, capacity). */
+int ds_layer_forward_prefill(const ds_layer_t* layer, ds_kv_cache* kv, const void* x, void* y,
+                             int32_t batch, int32_t seq, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Group-wise symmetric int8 quantization of float32 weights w [n][k] ([KP] section 五 5.2):
+ * per row and per group of `group` consecutive elements along k,
+ *   s = fp16_round_nearest_even(amax / 127)   (amax = max |w| over the group, taken in double),
+ *   q = clamp(round_half_even(w / s), -127, 127)   (the division in double), q = 0 when s == 0.
+ * Writes q int8 [n][k] and s fp16 [n][k/group]. Requires k % group == 0 and group a multiple of 16.
+ * Weights must be finite with |w| <= 127 * 65504 (so that every scale is a finite fp16); other
+ * inputs give unspecified codes. Enqueued on stream. */
+int ds_quantize_i8(const float* w, int8_t* q, void* s, int32_t n, int32_t k, int32_t group,
+                   void* stream);
+
+/* Expands int8 weights to float32: w[n][k] = q[n][k] * s[n][k/group], exactly as the GEMV
+ * kernels form each weight value. Enqueued on stream. */
+int ds_dequantize_i8(const int8_t* q, const void* s, float* w, int32_t n, int32_t k, int32_t group,
+                     void* stream);
+
+/* Message describing the last non-zero status returned on the calling thread. */
+const char* ds_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DS_LAYER_H */

@@ -1,0 +1,77 @@
+"""Shared test plumbing: seeded inputs for both sides, GPU layer construction, error metrics.
+
+The GPU side gets device tensors in its dtypes; the oracle gets exactly the same values widened
+to float64. No expected value here comes from the GPU path.
+"""
+import numpy as np
+import torch
+
+import synthetic as syn
+
+TOL = {"f32": 1e-4, "f16": 1e-2}  # relative L2 bars: fp32 configs, fp16-activation configs
+TORCH = {"f32": torch.float32, "f16": torch.float16}
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def gpu_layer_and_oracle_weights(wl: syn.Workload, layer: int, device="cuda", check_quant=True):
+    """Builds a library Layer for one layer of the workload and the oracle's float64 weights
+    (same values). For int8 the GPU quantizer makes the codes, and the oracle quantizer makes its
+    own from the same float32 draws; the two are compared bit for bit."""
+    import oracle
+    import transformer_gpt_layer_amd as tg
+
+    w32 = syn.layer_weights_f32(wl, layer, device)
+    act = TORCH[wl.act_dtype]
+    cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
+                         dtype={"f32": "fp32", "f16": "fp16", "i8": "int8"}[wl.weight_dtype],
+                         quantization_setting=(wl.group, False) if wl.weight_dtype == "i8" else None)
+    gw, ow = {}, {}
+    for name, t in w32.items():
+        if name.startswith("w_"):
+            if wl.weight_dtype == "i8":
+                q, s = tg.quantize_i8(t.contiguous(), wl.group)
+                gw[name], gw["s" + name[1:]] = q, s
+                if check_quant:
+                    oq, os_ = oracle.quantize_i8(t.cpu().numpy(), wl.group)
+                    assert np.array_equal(q.cpu().numpy(), oq), f"int8 codes of {name} differ from the oracle"
+                    assert np.array_equal(s.cpu().view(torch.int16).numpy().view(np.uint16), os_), \
+                        f"fp16 scales of {name} differ from the oracle"
+                    ow[name] = oracle.dequantize_i8(oq, os_, wl.group)
+                else:
+                    ow[name] = oracle.dequantize_i8(q.cpu().numpy(), s.cpu().view(torch.int16).numpy().view(np.uint16), wl.group)
+            else:
+                gw[name] = t.to(act).contiguous()
+                ow[name] = gw[name].double().cpu().numpy()
+        else:
+            gw[name] = t.to(act).contiguous()
+            ow[name] = gw[name].double().cpu().numpy()
+    return tg.Layer(cfg, gw), ow
+
+
+def filled_caches(wl: syn.Workload, layer: int, gl, device="cuda", past=None, cap=None, batch=None):
+    """A GPU KVCache holding `past` seeded rows (appended through ds_kv_append) and the oracle's
+    float64 copy of the same values."""
+    import transformer_gpt_layer_amd as tg
+
+    B = wl.batch if batch is None else batch
+    P = wl.past if past is None else past
+    cap = wl.capacity if cap is None else cap
+    act = TORCH[wl.act_dtype]
+    kv = tg.KVCache(B, wl.heads, cap, wl.head_dim, act, device)
+    ok = np.zeros((B, wl.heads, cap, wl.head_dim))
+    ov = np.zeros_like(ok)
+    if P > 0:
+        kp = syn.normal((B, P, wl.hidden), 1.0, wl.cfg_id, layer, syn.K_PAST, device).to(act)
+        vp = syn.normal((B, P, wl.hidden), 1.0, wl.cfg_id, layer, syn.V_PAST, device).to(act)
+        gl.kv_append(kv, kp.contiguous(), vp.contiguous())
+        kh = kp.double().cpu().numpy().reshape(B, P, wl.heads, wl.head_dim).transpose(0, 2, 1, 3)
+        vh = vp.double().cpu().numpy().reshape(B, P, wl.heads, wl.head_dim).transpose(0, 2, 1, 3)
+        ok[:, :, :P] = kh
+        ov[:, :, :P] = vh
+    lens = np.full(B, P, dtype=np.int32)
+    return kv, ok, ov, lens

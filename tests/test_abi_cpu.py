@@ -1,0 +1,143 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and rejects bad
+arguments before anything is enqueued (no GPU needed: these paths make no HIP call)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import transformer_gpt_layer_amd as tg
+from transformer_gpt_layer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced on these paths
+
+
+def _declared():
+    names = set()
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(ds_\w+)\s*\(", txt, re.M))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    L = _lib.lib()
+    declared = _declared()
+    assert declared == set(_lib.EXPORTS), declared ^ set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def _desc(**kw):
+    d = dict(hidden=256, heads=2, head_dim=128, ffn=512, weight_dtype=1, act_dtype=1, quant_group=0,
+             ln_eps=1e-5, gelu_tanh=0, triangular_masking=1)
+    d.update(kw)
+    return _lib.LayerDescC(**d)
+
+
+def _weights(int8=False, **kw):
+    vals = {n: FAKE for n in _lib.WEIGHT_FIELDS}
+    if not int8:
+        for n in ("s_qkv", "s_o", "s_ff1", "s_ff2"):
+            vals[n] = None
+    vals.update(kw)
+    return _lib.LayerWeightsC(**vals)
+
+
+def _create(desc, w):
+    h = C.c_void_p()
+    rc = _lib.lib().ds_layer_create(C.byref(desc), C.byref(w), C.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=250), _lib.DS_ERR_SHAPE),
+    (dict(head_dim=96, hidden=192, heads=2), _lib.DS_ERR_SHAPE),
+    (dict(heads=3), _lib.DS_ERR_SHAPE),
+    (dict(ffn=100), _lib.DS_ERR_SHAPE),
+    (dict(weight_dtype=2, act_dtype=2), _lib.DS_ERR_DTYPE),
+    (dict(weight_dtype=0, act_dtype=1), _lib.DS_ERR_DTYPE),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=24), _lib.DS_ERR_DTYPE),
+    (dict(quant_group=64), _lib.DS_ERR_DTYPE),
+    (dict(ln_eps=0.0), _lib.DS_ERR_SHAPE),
+    (dict(triangular_masking=2), _lib.DS_ERR_SHAPE),
+])
+def test_create_rejects_bad_descriptions(kw, code):
+    rc, h = _create(_desc(**kw), _weights(int8=kw.get("weight_dtype") == 2))
+    assert rc == code, (rc, _lib.lib().ds_last_error())
+    assert not h.value
+    assert _lib.lib().ds_last_error()
+
+
+def test_create_rejects_null_and_misaligned_pointers():
+    assert _create(_desc(), _weights(w_o=None))[0] == _lib.DS_ERR_NULL
+    assert _create(_desc(), _weights(w_ff1=FAKE + 8))[0] == _lib.DS_ERR_ALIGN
+    assert _create(_desc(), _weights(s_o=FAKE))[0] == _lib.DS_ERR_DTYPE       # scales on fp16 weights
+    assert _create(_desc(weight_dtype=2, quant_group=64), _weights(int8=True, s_ff2=None))[0] == _lib.DS_ERR_NULL
+    h = C.c_void_p()
+    assert _lib.lib().ds_layer_create(None, C.byref(_weights()), C.byref(h)) == _lib.DS_ERR_NULL
+
+
+def _layer():
+    rc, h = _create(_desc(), _weights())
+    assert rc == 0, _lib.lib().ds_last_error()
+    return h
+
+
+def test_workspace_bytes():
+    L, h = _lib.lib(), _layer()
+    a = L.ds_layer_workspace_bytes(h, 1, 1, 64)
+    b = L.ds_layer_workspace_bytes(h, 8, 1, 64)
+    c = L.ds_layer_workspace_bytes(h, 8, 1, 1024)
+    assert 0 < a < b < c
+    assert L.ds_layer_workspace_bytes(h, 0, 1, 64) == 0
+    assert L.ds_layer_workspace_bytes(None, 1, 1, 64) == 0
+    L.ds_layer_destroy(h)
+
+
+def test_forward_rejects_before_enqueue():
+    L, h = _lib.lib(), _layer()
+    hl = np.array([63, 10], dtype=np.int32)
+    kv = _lib.KVCacheC(FAKE, FAKE, FAKE, hl.ctypes.data_as(C.POINTER(C.c_int32)), 2, 64)
+    need = L.ds_layer_workspace_bytes(h, 2, 1, 64)
+    # every call below fails a host-side check, so no kernel is ever launched on the fake pointers
+    run = lambda batch=2, x=FAKE, ws=need: L.ds_layer_forward_decode(h, C.byref(kv), C.c_void_p(x), C.c_void_p(FAKE), batch, C.c_void_p(FAKE), ws, None)
+    hl[:] = [64, 10]
+    assert run() == _lib.DS_ERR_KV_FULL
+    assert list(hl) == [64, 10]                      # nothing advanced on failure
+    hl[:] = [3, 3]
+    assert run(batch=3) == _lib.DS_ERR_SHAPE         # more sequences than the cache holds
+    assert run(ws=need - 1) == _lib.DS_ERR_WORKSPACE
+    assert run(x=FAKE + 4) == _lib.DS_ERR_ALIGN
+    assert run(x=0) == _lib.DS_ERR_NULL
+    assert L.ds_layer_forward_prefill(h, C.byref(kv), C.c_void_p(FAKE), C.c_void_p(FAKE), 2, 62,
+                                      C.c_void_p(FAKE), 1 << 40, None) == _lib.DS_ERR_KV_FULL
+    assert L.ds_kv_append(h, C.byref(kv), C.c_void_p(FAKE), C.c_void_p(FAKE), 2, 70, None) == _lib.DS_ERR_KV_FULL
+    assert L.ds_quantize_i8(C.c_void_p(FAKE), C.c_void_p(FAKE), C.c_void_p(FAKE), 4, 100, 64, None) == _lib.DS_ERR_SHAPE
+    assert L.ds_dequantize_i8(C.c_void_p(FAKE), None, C.c_void_p(FAKE), 4, 128, 64, None) == _lib.DS_ERR_NULL
+    L.ds_layer_destroy(h)
+
+
+def test_python_errors_map_to_exceptions():
+    with pytest.raises(OverflowError):
+        _lib.check(_lib.DS_ERR_KV_FULL, "x")
+    with pytest.raises(ValueError):
+        _lib.check(_lib.DS_ERR_SHAPE, "x")
+    with pytest.raises(RuntimeError):
+        _lib.check(_lib.DS_ERR_HIP, "x")
+
+
+def test_config_merge_rules():
+    cfg = tg.make_config({"hidden": 256, "heads": 2, "ffn": 512}, dtype="int8")
+    assert cfg.dtype == _lib.DS_I8 and cfg.quant_group == 64 and cfg.triangular_masking and cfg.max_out_tokens == 1024
+    assert tg.make_config('{"hidden": 256, "heads": 4, "ffn": 512}').dtype == _lib.DS_F16   # fp16 default
+    assert tg.make_config(hidden=256, heads=2, ffn=512, dtype="int8", quantization_setting=(32, True)).quant_group == 32
+    with pytest.raises(ValueError, match="Conflicting"):
+        tg.make_config({"hidden": 256, "heads": 2, "ffn": 512, "dtype": "fp16"}, dtype="fp32")
+    with pytest.raises(ValueError):
+        tg.make_config(hidden=256, heads=2, ffn=512, quant_group=64)          # group on fp16 weights
+    with pytest.raises(ValueError):
+        tg.make_config(hidden=256, heads=2, ffn=512, bogus=1)

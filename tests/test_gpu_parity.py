@@ -1,0 +1,152 @@
+"""GPU parity of the HIP layer against the oracle (run on an MI355X).
+
+Inputs are seeded synthetic draws (synthetic.py); both sides receive the same values. Sizes span
+several tiles and ragged tails (batch not a multiple of the batch tile, past lengths not multiples
+of the attention chunk, rows not multiples of the row tile).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from tests._common import TOL, filled_caches, gpu_layer_and_oracle_weights, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(base, **kw):
+    return dataclasses.replace(syn.WORKLOADS[base] if isinstance(base, str) else base, **kw)
+
+
+def _run_decode(wl, layer=0, past=None, batch=None, cap=None):
+    gl, ow = gpu_layer_and_oracle_weights(wl, layer)
+    B = wl.batch if batch is None else batch
+    kv, ok, ov, lens = filled_caches(wl, layer, gl, past=past, batch=B, cap=cap)
+    x = syn.normal((B, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, layer).to(gl.cfg.torch_act_dtype)
+    x = x.cuda() if not x.is_cuda else x
+    y = gl.decode(kv, x)
+    torch.cuda.synchronize()
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
+    yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy()[:, None, :])[:, 0]
+    return gl, kv, x, y, yo, ok, ov, lens
+
+
+SMALL = {
+    "c1": _wl("c1"),
+    "f32-d128-b3": _wl("c1", hidden=256, heads=2, head_dim=128, ffn=512, batch=3, past=37, cfg_id=101),
+    "f16-d128-b3": _wl("c1", hidden=256, heads=2, head_dim=128, ffn=768, weight_dtype="f16", act_dtype="f16",
+                       batch=3, past=70, cfg_id=102),
+    "f16-d64-b9": _wl("c1", hidden=320, heads=5, head_dim=64, ffn=640, weight_dtype="f16", act_dtype="f16",
+                      batch=9, past=129, cfg_id=103),
+    "i8-d128-b5": _wl("c1", hidden=512, heads=4, head_dim=128, ffn=1024, weight_dtype="i8", act_dtype="f16",
+                      group=64, batch=5, past=65, cfg_id=104),
+    "i8-d64-b1-k256": _wl("c1", hidden=256, heads=4, head_dim=64, ffn=512, weight_dtype="i8", act_dtype="f16",
+                          group=64, batch=1, past=3, cfg_id=105),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_matches_oracle(name):
+    wl = SMALL[name]
+    print(f"[decode parity] {name}: {wl}", flush=True)
+    gl, kv, x, y, yo, ok, ov, lens = _run_decode(wl)
+    err = rel_l2(y.double().cpu().numpy(), yo)
+    print(f"  rel L2 = {err:.3e}", flush=True)
+    assert err <= TOL[wl.act_dtype], err
+    # the layer's own contribution (y - x) is the stricter view: the residual stream hides errors
+    xd = x.double().cpu().numpy()
+    err_d = rel_l2(y.double().cpu().numpy() - xd, yo - xd)
+    assert err_d <= 5 * TOL[wl.act_dtype], err_d
+    # the new K/V rows landed at row `past` of every head, and the lengths advanced
+    P = wl.past
+    kg = kv.k.double().cpu().numpy()
+    vg = kv.v.double().cpu().numpy()
+    assert rel_l2(kg[:, :, P], ok[:, :, P]) <= TOL[wl.act_dtype]
+    assert rel_l2(vg[:, :, P], ov[:, :, P]) <= TOL[wl.act_dtype]
+    assert np.array_equal(kg[:, :, :P], ok[:, :, :P]) and np.array_equal(vg[:, :, :P], ov[:, :, :P])
+    assert not kg[:, :, P + 1:].any()
+    assert kv.lengths() == [P + 1] * wl.batch and list(kv.h_len) == [P + 1] * wl.batch
+
+
+def test_decode_single_key_cache():
+    # P = 0: every head attends to its own new key only
+    wl = _wl(SMALL["f16-d128-b3"], past=0, cfg_id=110)
+    gl, kv, x, y, yo, *_ = _run_decode(wl)
+    assert rel_l2(y.double().cpu().numpy(), yo) <= TOL["f16"]
+
+
+def test_decode_batch_independent_and_deterministic():
+    wl = SMALL["f16-d64-b9"]
+    gl, ow = gpu_layer_and_oracle_weights(wl, 0)
+    x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").half()
+    kv, *_ = filled_caches(wl, 0, gl)
+    y = gl.decode(kv, x)
+    kv2, *_ = filled_caches(wl, 0, gl)
+    y2 = gl.decode(kv2, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "run-to-run results differ"
+    for b in (0, 4, 8):
+        kv1, *_ = filled_caches(wl, 0, gl, batch=1)
+        # sequence b's past rows are the draws of batch row b
+        kv1.k.copy_(kv.k[b:b + 1]); kv1.v.copy_(kv.v[b:b + 1])
+        kv1.set_lengths([wl.past])
+        y1 = gl.decode(kv1, x[b:b + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(y1[0], y[b]), f"sequence {b} depends on the rest of the batch"
+
+
+def test_decode_sequence_of_steps_tracks_oracle():
+    # four consecutive decode steps on one cache, each checked against the oracle
+    wl = SMALL["f16-d128-b3"]
+    gl, ow = gpu_layer_and_oracle_weights(wl, 0)
+    kv, ok, ov, lens = filled_caches(wl, 0, gl)
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
+    for step in range(4):
+        x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 10 + step, "cuda").half()
+        y = gl.decode(kv, x)
+        yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy()[:, None])[:, 0]
+        assert rel_l2(y.double().cpu().numpy(), yo) <= TOL["f16"], step
+    assert kv.lengths() == list(lens)
+
+
+def test_quantizer_and_dequant_bit_exact():
+    import transformer_gpt_layer_amd as tg
+    w = syn.normal((300, 1024), 0.02, 7, 0, 0, "cuda")
+    w[5, 64:128] = 0.0
+    w[9, 3] = 1.5
+    q, s = tg.quantize_i8(w, 64)
+    oq, os_ = oracle.quantize_i8(w.cpu().numpy(), 64)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().view(torch.int16).numpy().view(np.uint16), os_)
+    deq = tg.dequantize_i8(q, s, 64).cpu().numpy()
+    ref = oracle.dequantize_i8(oq, os_, 64).astype(np.float32)   # q*s is exact in float32
+    assert np.array_equal(deq.view(np.uint32), ref.view(np.uint32))
+
+
+def test_kv_full_raises_before_launch():
+    wl = SMALL["f16-d128-b3"]
+    gl, _ = gpu_layer_and_oracle_weights(wl, 0)
+    kv, *_ = filled_caches(wl, 0, gl, past=wl.capacity - 1)
+    x = torch.zeros((wl.batch, wl.hidden), dtype=torch.float16, device="cuda")
+    gl.decode(kv, x)  # fills the last row
+    with pytest.raises(OverflowError):
+        gl.decode(kv, x)
+    assert kv.lengths() == [wl.capacity] * wl.batch
+
+
+@pytest.mark.parametrize("name,S,P0", [("f16-d128-b3", 7, 5), ("f32-d128-b3", 5, 0), ("i8-d128-b5", 4, 9)])
+def test_prefill_matches_oracle(name, S, P0):
+    wl = SMALL[name]
+    gl, ow = gpu_layer_and_oracle_weights(wl, 0)
+    kv, ok, ov, lens = filled_caches(wl, 0, gl, past=P0)
+    x = syn.normal((wl.batch, S, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 3, "cuda").to(gl.cfg.torch_act_dtype)
+    y = gl.prefill(kv, x)
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
+    yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy())
+    assert rel_l2(y.double().cpu().numpy(), yo) <= TOL[wl.act_dtype]
+    kg = kv.k.double().cpu().numpy()
+    assert rel_l2(kg[:, :, :P0 + S], ok[:, :, :P0 + S]) <= TOL[wl.act_dtype]
+    assert kv.lengths() == [P0 + S] * wl.batch

@@ -1,0 +1,250 @@
+"""transformer_gpt_layer_amd: a fused pre-LN GPT layer with a KV cache for MI355X (gfx950).
+
+Python face of libdslayer.so (include/ds_layer.h). The classes here marshal torch tensors into the
+C ABI; every step of the layer runs in the library's HIP kernels.
+
+The configuration mirrors the inference config of the page "DeepSpeed Inference 内核优化深度解析"
+(blog.gitcode.com), section 四 4.2 (dtype fp32 / fp16 / int8 with fp16 as default, max_out_tokens
+1024) and section 五 5.2 (int8 with quantize_groups), plus triangular_masking (default True) from
+the config table of "DeepSpeed MoE 大规模稀疏模型推理实战指南". As in init_inference on that page, a
+config dict (or JSON text / file) and keyword arguments merge, and a key given both ways with
+different values raises.
+"""
+import ctypes as C
+import json
+import os
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import DS_F16, DS_F32, DS_I8, check, lib, ptr, stream_handle
+
+__all__ = ["LayerConfig", "make_config", "Layer", "KVCache", "quantize_i8", "dequantize_i8"]
+
+_DTYPE_NAMES = {"fp32": DS_F32, "float32": DS_F32, "float": DS_F32, "f32": DS_F32,
+                "fp16": DS_F16, "float16": DS_F16, "half": DS_F16, "f16": DS_F16,
+                "int8": DS_I8, "i8": DS_I8}
+_TORCH_DT = {DS_F32: torch.float32, DS_F16: torch.float16, DS_I8: torch.int8}
+
+
+def _dtype_code(v) -> int:
+    if isinstance(v, torch.dtype):
+        v = {torch.float32: "fp32", torch.float16: "fp16", torch.int8: "int8"}.get(v, str(v))
+    if isinstance(v, int) and v in (DS_F32, DS_F16, DS_I8):
+        return v
+    key = str(v).lower().replace("torch.", "")
+    if key not in _DTYPE_NAMES:
+        raise ValueError(f"unsupported dtype {v!r}: fp32, fp16 or int8")
+    return _DTYPE_NAMES[key]
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    hidden: int
+    heads: int
+    ffn: int
+    dtype: int = DS_F16            # weight dtype; activations are fp32 for fp32 weights, else fp16
+    quant_group: int = 0           # int8 only: elements per scale along the reduction dimension
+    ln_eps: float = 1e-5
+    gelu_tanh: bool = False
+    triangular_masking: bool = True
+    max_out_tokens: int = 1024
+
+    @property
+    def head_dim(self) -> int:
+        return self.hidden // self.heads
+
+    @property
+    def act_dtype(self) -> int:
+        return DS_F32 if self.dtype == DS_F32 else DS_F16
+
+    @property
+    def torch_act_dtype(self) -> torch.dtype:
+        return _TORCH_DT[self.act_dtype]
+
+    def c_desc(self) -> _lib.LayerDescC:
+        return _lib.LayerDescC(self.hidden, self.heads, self.head_dim, self.ffn, self.dtype,
+                               self.act_dtype, self.quant_group, self.ln_eps, int(self.gelu_tanh),
+                               int(self.triangular_masking))
+
+
+_CONFIG_KEYS = {"hidden", "heads", "ffn", "dtype", "quant_group", "ln_eps", "gelu_tanh",
+                "triangular_masking", "max_out_tokens", "quantization_setting"}
+
+
+def make_config(config=None, **kwargs) -> LayerConfig:
+    """Merge a config (dict, JSON text or JSON file path) with keyword arguments.
+
+    Keyword arguments add to the config; a key present in both with different values raises
+    ValueError. `quantization_setting` may give the int8 group size as an int or as a
+    (group, mlp_extra_grouping) pair; with int8 and no setting the group is 64.
+    """
+    base = {}
+    if config is not None:
+        if isinstance(config, str):
+            config = json.load(open(config)) if os.path.exists(config) else json.loads(config)
+        base = dict(config)
+    for k, v in kwargs.items():
+        if k in base and base[k] != v:
+            raise ValueError(f"Conflicting argument '{k}' in 'config':{base[k]!r} and kwargs:{v!r}")
+        base[k] = v
+    unknown = set(base) - _CONFIG_KEYS
+    if unknown:
+        raise ValueError(f"unknown config keys: {sorted(unknown)}")
+    dt = _dtype_code(base.pop("dtype", "fp16"))
+    qs = base.pop("quantization_setting", None)
+    group = base.pop("quant_group", None)
+    if qs is not None:
+        g = qs[0] if isinstance(qs, (tuple, list)) else qs
+        if group is not None and group != g:
+            raise ValueError("quant_group and quantization_setting disagree")
+        group = g
+    if dt == DS_I8:
+        group = 64 if group is None else int(group)
+    elif group not in (None, 0):
+        raise ValueError("quant_group applies to int8 weights only")
+    else:
+        group = 0
+    return LayerConfig(dtype=dt, quant_group=group, **base)
+
+
+class KVCache:
+    """Caller-owned K/V cache of one layer: k, v [batch][heads][capacity][head_dim] in the
+    activation dtype, device lengths d_len int32[batch] and an optional host mirror."""
+
+    def __init__(self, batch, heads, capacity, head_dim, dtype, device="cuda", track_host=True):
+        self.batch, self.heads, self.capacity, self.head_dim = batch, heads, capacity, head_dim
+        self.k = torch.zeros((batch, heads, capacity, head_dim), dtype=dtype, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.d_len = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.h_len = _lib.host_lengths([0] * batch) if track_host else None
+        self._c = None
+
+    def c_struct(self) -> _lib.KVCacheC:
+        hl = self.h_len.ctypes.data_as(C.POINTER(C.c_int32)) if self.h_len is not None else None
+        self._c = _lib.KVCacheC(self.k.data_ptr(), self.v.data_ptr(), self.d_len.data_ptr(), hl,
+                                self.batch, self.capacity)
+        return self._c
+
+    def set_lengths(self, lengths):
+        vals = [int(v) for v in lengths]
+        self.d_len.copy_(torch.tensor(vals, dtype=torch.int32))
+        if self.h_len is not None:
+            self.h_len[:] = vals
+
+    def lengths(self):
+        return self.d_len.cpu().tolist()
+
+
+class Layer:
+    """One layer bound to device weight tensors (borrowed: keep them alive with the layer)."""
+
+    _SHAPES = {"ln1_g": "H", "ln1_b": "H", "w_qkv": ("3H", "H"), "b_qkv": "3H", "w_o": ("H", "H"),
+               "b_o": "H", "ln2_g": "H", "ln2_b": "H", "w_ff1": ("F", "H"), "b_ff1": "F",
+               "w_ff2": ("H", "F"), "b_ff2": "H"}
+
+    def __init__(self, cfg: LayerConfig, weights: dict):
+        self.cfg = cfg
+        H, F = cfg.hidden, cfg.ffn
+        dims = {"H": H, "3H": 3 * H, "F": F}
+        wdt, adt = _TORCH_DT[cfg.dtype], cfg.torch_act_dtype
+        for name, shp in self._SHAPES.items():
+            t = weights.get(name)
+            if t is None:
+                raise ValueError(f"missing weight {name}")
+            want = tuple(dims[s] for s in shp) if isinstance(shp, tuple) else (dims[shp],)
+            if tuple(t.shape) != want:
+                raise ValueError(f"{name}: shape {tuple(t.shape)} != {want}")
+            exp = wdt if name.startswith("w_") else adt
+            if t.dtype != exp:
+                raise ValueError(f"{name}: dtype {t.dtype} != {exp}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if cfg.dtype == DS_I8:
+            for name in ("s_qkv", "s_o", "s_ff1", "s_ff2"):
+                t = weights.get(name)
+                if t is None or t.dtype != torch.float16 or not t.is_contiguous():
+                    raise ValueError(f"{name}: int8 weights need contiguous fp16 scales")
+        self._weights = dict(weights)
+        cw = _lib.LayerWeightsC(*[self._weights[n].data_ptr() if self._weights.get(n) is not None else None
+                                  for n in _lib.WEIGHT_FIELDS])
+        h = C.c_void_p()
+        check(lib().ds_layer_create(C.byref(cfg.c_desc()), C.byref(cw), C.byref(h)), "ds_layer_create")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib._LIB is not None:
+            _lib._LIB.ds_layer_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def workspace_bytes(self, batch, tokens, capacity) -> int:
+        return int(lib().ds_layer_workspace_bytes(self._h, batch, tokens, capacity))
+
+    def workspace(self, batch, tokens, capacity, device="cuda") -> torch.Tensor:
+        return torch.empty(self.workspace_bytes(batch, tokens, capacity), dtype=torch.uint8, device=device)
+
+    def _io(self, x, y, shape):
+        if tuple(x.shape) != shape or x.dtype != self.cfg.torch_act_dtype or not x.is_contiguous():
+            raise ValueError(f"x must be contiguous {shape} {self.cfg.torch_act_dtype}")
+        if y is None:
+            y = torch.empty_like(x)
+        elif tuple(y.shape) != shape or y.dtype != x.dtype or not y.is_contiguous():
+            raise ValueError("y must match x")
+        return y
+
+    def decode(self, kv: KVCache, x, y=None, workspace=None, stream=None):
+        """One decode step: x, y [batch, hidden]."""
+        B = x.shape[0]
+        y = self._io(x, y, (B, self.cfg.hidden))
+        if workspace is None:
+            workspace = self.workspace(B, 1, kv.capacity, x.device)
+        check(lib().ds_layer_forward_decode(self._h, C.byref(kv.c_struct()), ptr(x), ptr(y), B,
+                                            ptr(workspace), workspace.numel(), stream_handle(stream)),
+              "ds_layer_forward_decode")
+        return y
+
+    def prefill(self, kv: KVCache, x, y=None, workspace=None, stream=None):
+        """Prefill: x, y [batch, seq, hidden]."""
+        B, S = x.shape[0], x.shape[1]
+        y = self._io(x, y, (B, S, self.cfg.hidden))
+        if workspace is None:
+            workspace = self.workspace(B, S, kv.capacity, x.device)
+        check(lib().ds_layer_forward_prefill(self._h, C.byref(kv.c_struct()), ptr(x), ptr(y), B, S,
+                                             ptr(workspace), workspace.numel(), stream_handle(stream)),
+              "ds_layer_forward_prefill")
+        return y
+
+    def kv_append(self, kv: KVCache, k_new, v_new, stream=None):
+        """Copy k_new, v_new [batch, ntok, hidden] into the cache after the filled rows."""
+        B, T = k_new.shape[0], k_new.shape[1]
+        for t in (k_new, v_new):
+            if tuple(t.shape) != (B, T, self.cfg.hidden) or t.dtype != self.cfg.torch_act_dtype or not t.is_contiguous():
+                raise ValueError("k_new, v_new must be contiguous [batch, ntok, hidden] in the activation dtype")
+        check(lib().ds_kv_append(self._h, C.byref(kv.c_struct()), ptr(k_new), ptr(v_new), B, T,
+                                 stream_handle(stream)), "ds_kv_append")
+
+
+def quantize_i8(w: torch.Tensor, group: int = 64, stream=None):
+    """Group-wise symmetric int8 quantization on the GPU: w float32 [n, k] ->
+    (q int8 [n, k], s float16 [n, k/group])."""
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D float32 tensor")
+    n, k = w.shape
+    q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    s = torch.empty((n, k // group if group else 0), dtype=torch.float16, device=w.device)
+    check(lib().ds_quantize_i8(ptr(w), ptr(q), ptr(s), n, k, group, stream_handle(stream)), "ds_quantize_i8")
+    return q, s
+
+
+def dequantize_i8(q: torch.Tensor, s: torch.Tensor, group: int = 64, stream=None):
+    """w = q * s as float32, through the GEMV kernels' int8 -> fp16 conversion."""
+    n, k = q.shape
+    w = torch.empty((n, k), dtype=torch.float32, device=q.device)
+    check(lib().ds_dequantize_i8(ptr(q), ptr(s), ptr(w), n, k, group, stream_handle(stream)), "ds_dequantize_i8")
+    return w

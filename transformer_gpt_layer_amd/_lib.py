@@ -1,0 +1,103 @@
+"""ctypes binding of libdslayer.so (include/ds_layer.h).
+
+Argument marshalling only: torch tensors give device pointers and streams, every step of the layer
+runs in the library's HIP kernels. There is no fallback: if the library is missing, loading fails
+with an error that says so.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdslayer.so")
+
+DS_F32, DS_F16, DS_I8 = 0, 1, 2
+DS_OK, DS_ERR_NULL, DS_ERR_SHAPE, DS_ERR_DTYPE, DS_ERR_ALIGN = 0, -1, -2, -3, -4
+DS_ERR_KV_FULL, DS_ERR_UNSUPPORTED, DS_ERR_HIP, DS_ERR_WORKSPACE = -5, -6, -7, -8
+
+# every symbol the header declares
+EXPORTS = ("ds_layer_create", "ds_layer_destroy", "ds_layer_workspace_bytes", "ds_kv_append",
+           "ds_layer_forward_decode", "ds_layer_forward_prefill", "ds_quantize_i8",
+           "ds_dequantize_i8", "ds_last_error")
+
+
+class LayerDescC(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
+                ("ffn", C.c_int32), ("weight_dtype", C.c_int32), ("act_dtype", C.c_int32),
+                ("quant_group", C.c_int32), ("ln_eps", C.c_float), ("gelu_tanh", C.c_int32),
+                ("triangular_masking", C.c_int32)]
+
+
+WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "s_qkv", "w_o", "b_o", "s_o",
+                 "ln2_g", "ln2_b", "w_ff1", "b_ff1", "s_ff1", "w_ff2", "b_ff2", "s_ff2")
+
+
+class LayerWeightsC(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class KVCacheC(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("d_len", C.c_void_p),
+                ("h_len", C.POINTER(C.c_int32)), ("batch", C.c_int32), ("capacity", C.c_int32)]
+
+
+_LIB = None
+
+
+def lib():
+    """Load libdslayer.so. Raises if it has not been built: nothing runs without it."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32 = C.c_void_p, C.c_int32
+        L.ds_layer_create.argtypes = [C.POINTER(LayerDescC), C.POINTER(LayerWeightsC), C.POINTER(vp)]
+        L.ds_layer_destroy.argtypes = [vp]
+        L.ds_layer_workspace_bytes.argtypes = [vp, i32, i32, i32]
+        L.ds_layer_workspace_bytes.restype = C.c_size_t
+        L.ds_kv_append.argtypes = [vp, C.POINTER(KVCacheC), vp, vp, i32, i32, vp]
+        L.ds_layer_forward_decode.argtypes = [vp, C.POINTER(KVCacheC), vp, vp, i32, vp, C.c_size_t, vp]
+        L.ds_layer_forward_prefill.argtypes = [vp, C.POINTER(KVCacheC), vp, vp, i32, i32, vp, C.c_size_t, vp]
+        L.ds_quantize_i8.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        L.ds_dequantize_i8.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        L.ds_last_error.restype = C.c_char_p
+        for name in ("ds_layer_create", "ds_layer_destroy", "ds_kv_append", "ds_layer_forward_decode",
+                     "ds_layer_forward_prefill", "ds_quantize_i8", "ds_dequantize_i8"):
+            getattr(L, name).restype = C.c_int
+        _LIB = L
+    return _LIB
+
+
+def check(rc: int, what: str):
+    """Map a ds_status to a Python exception: ValueError for argument/shape/dtype errors,
+    OverflowError for a full KV cache, RuntimeError for HIP errors."""
+    if rc == DS_OK:
+        return
+    msg = f"{what}: {lib().ds_last_error().decode(errors='replace')} (status {rc})"
+    if rc == DS_ERR_KV_FULL:
+        raise OverflowError(msg)
+    if rc in (DS_ERR_HIP,):
+        raise RuntimeError(msg)
+    if rc == DS_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise ValueError(msg)
+
+
+def ptr(t):
+    """Device (or host) address of a tensor, or None."""
+    if t is None:
+        return None
+    return C.c_void_p(t.data_ptr())
+
+
+def stream_handle(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def host_lengths(values) -> np.ndarray:
+    return np.ascontiguousarray(values, dtype=np.int32)

@@ -1,0 +1,124 @@
+// ds_device.hpp -- device helpers shared by the gfx950 kernels of libdslayer.so:
+// 16-byte vector loads, wave64 reductions, fp16 packing, int8 -> fp16 conversion, GeLU.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- loads
+// Weight streams are read once per step: mark them non-temporal so they do not evict the small,
+// reused activation and cache lines from L2.
+__device__ __forceinline__ u32x4 ld_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T v) { return static_cast<float>(v); }
+
+// ---------------------------------------------------------------- wave64 reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+// Sum over aligned groups of G lanes (G a power of two <= 64); every lane gets its group's sum.
+template <int G> __device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Block-wide sum for a 256-thread block; `red` is 4 floats of LDS. All threads get the result.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// ---------------------------------------------------------------- fp16 packing
+// Bit casts take their operand by value: __builtin_bit_cast applied directly to an ext-vector
+// component (v.y) reads the vector's first component instead, so components are copied first.
+__device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// dot of 8 fp16 weights (one 16-byte load) with 8 fp16 activations, accumulated in fp32
+__device__ __forceinline__ float dot8_f16(u32x4 w, u32x4 a, float acc) {
+  acc = __builtin_amdgcn_fdot2(as_half2(w.x), as_half2(a.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_half2(w.y), as_half2(a.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_half2(w.z), as_half2(a.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_half2(w.w), as_half2(a.w), acc, false);
+  return acc;
+}
+
+// int8 -> fp16, exactly: with the byte offset to unsigned u = q + 128, the fp16 bit pattern
+// 0x6400 | u encodes 1024 + u (in [1024, 2048) the fp16 spacing is 1), so subtracting
+// 1152 = 1024 + 128 leaves q exactly. Two bytes of `w` (selected by `hi`) become one half2.
+__device__ __forceinline__ half2_t i8pair_to_half2(uint32_t w_biased, bool hi) {
+  uint32_t b0 = hi ? (w_biased >> 16) & 0xffu : w_biased & 0xffu;
+  uint32_t b1 = hi ? (w_biased >> 24) : (w_biased >> 8) & 0xffu;
+  uint32_t bits = 0x64006400u | b0 | (b1 << 16);
+  const half2_t off = {(half_t)1152.0f, (half_t)1152.0f};
+  return as_half2(bits) - off;
+}
+
+// dot of 16 int8 codes (one 16-byte load) with 16 fp16 activations (two 16-byte LDS reads),
+// fp32 accumulation; the group scale is applied by the caller.
+__device__ __forceinline__ float dot16_i8(u32x4 w, u32x4 a0, u32x4 a1) {
+  const uint32_t flip = 0x80808080u;  // q + 128 for every byte
+  uint32_t w0 = w.x ^ flip, w1 = w.y ^ flip, w2 = w.z ^ flip, w3 = w.w ^ flip;
+  float acc = 0.f;
+  acc = __builtin_amdgcn_fdot2(i8pair_to_half2(w0, false), as_half2(a0.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(i8pair_to_half2(w0, true), as_half2(a0.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(i8pair_to_half2(w1, false), as_half2(a0.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(i8pair_to_half2(w1, true), as_half2(a0.w), acc, false);
+  acc = __builtin_amdgcn_fdot2(i8pair_to_half2(w2, false), as_half2(a1.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(i8pair_to_half2(w2, true), as_half2(a1.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(i8pair_to_half2(w3, false), as_half2(a1.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(i8pair_to_half2(w3, true), as_half2(a1.w), acc, false);
+  return acc;
+}
+
+// dot of 4 fp32 weights with 4 fp32 activations
+__device__ __forceinline__ float dot4_f32(u32x4 w, float4_t a, float acc) {
+  acc = fmaf(as_f32(w.x), a.x, acc);
+  acc = fmaf(as_f32(w.y), a.y, acc);
+  acc = fmaf(as_f32(w.z), a.z, acc);
+  acc = fmaf(as_f32(w.w), a.w, acc);
+  return acc;
+}
+
+// ---------------------------------------------------------------- GeLU
+// u * Phi(u) = u/2 (1 + erf(u / sqrt 2)), or the tanh approximation
+// u/2 (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))); erf and tanh come from the ROCm device library.
+__device__ __forceinline__ float gelu(float u, bool tanh_form) {
+  if (tanh_form) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * u * (1.f + tanhf(c * (u + 0.044715f * u * u * u)));
+  }
+  return 0.5f * u * (1.f + erff(u * 0.7071067811865476f));
+}
+
+// ---------------------------------------------------------------- stores in the activation type
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ half_t from_f32<half_t>(float v) { return (half_t)v; }
+
+}  // namespace ds

@@ -1,0 +1,58 @@
+// ds_launch.hpp -- internal interface between the C ABI (layer.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ds {
+
+enum Dt { F32 = 0, F16 = 1, I8 = 2 };
+enum GemvKind { KIND_QKV = 0, KIND_OPROJ = 1, KIND_FF1 = 2, KIND_FF2 = 3 };
+
+// Arguments of one fused GEMV launch over `rows` activation rows (rows = batch * tokens).
+struct GemvArgs {
+  const void* w;       // [n][k] weights (f32, f16 or int8)
+  const void* s;       // fp16 [n][k/group] scales (int8 only)
+  const void* bias;    // [n] in the activation type
+  const void* in;      // [rows][k] input: activation type for KIND_QKV, else fp32 workspace
+  const void* ln_g;    // LayerNorm parameters (KIND_QKV, KIND_FF1), activation type
+  const void* ln_b;
+  const void* resid;   // [rows][n] residual: activation type (KIND_OPROJ) or fp32 (KIND_FF2)
+  void* out;           // fp32 [rows][n] (KIND_OPROJ, KIND_FF1), activation type (KIND_FF2)
+  // KIND_QKV scatter: q to fp32 [rows][H], k and v into the caches at row d_len[seq] + t
+  float* q_out;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* d_len;
+  uint32_t* attn_counters;  // zeroed by the KIND_QKV launch: rows * heads counters
+  int n, k, group, rows, tokens, cap, heads, head_dim, hidden;
+  float eps;
+  int gelu_tanh;
+};
+
+struct AttnArgs {
+  const float* q;      // [rows][H] fp32 (unscaled)
+  const void* k_cache; // [batch][heads][cap][d]
+  const void* v_cache;
+  const int32_t* d_len;
+  float* part;         // [rows][heads][nchunk][d + 2] partial (max, sum, acc[d])
+  uint32_t* counters;  // [rows][heads]
+  float* ctx;          // [rows][H] fp32 output
+  int rows, tokens, heads, head_dim, cap, chunk, nchunk, causal;
+};
+
+hipError_t launch_gemv(Dt wdt, Dt adt, GemvKind kind, const GemvArgs& a, hipStream_t st);
+hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st);
+int attn_chunk_for(int rows, int heads, int cap);
+
+hipError_t launch_kv_append(Dt adt, const void* k_new, const void* v_new, void* kc, void* vc,
+                            const int32_t* d_len, int batch, int ntok, int heads, int head_dim,
+                            int cap, hipStream_t st);
+// d_len[b] += ntok for b < batch, unless that would pass cap
+hipError_t launch_len_advance(int32_t* d_len, int batch, int ntok, int cap, hipStream_t st);
+hipError_t launch_quantize_i8(const float* w, int8_t* q, uint16_t* s, int n, int k, int group,
+                              hipStream_t st);
+hipError_t launch_dequantize_i8(const int8_t* q, const uint16_t* s, float* w, int n, int k,
+                                int group, hipStream_t st);
+
+}  // namespace ds

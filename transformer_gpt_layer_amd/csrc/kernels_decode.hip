@@ -1,0 +1,420 @@
+// kernels_decode.hip -- the fused skinny-GEMV kernels and KV-cache attention of one layer step.
+//
+// Source: the customized transformer-block inference kernels of the page "DeepSpeed Inference
+// 内核优化深度解析" (blog.gitcode.com), section 三: region 1 (input LayerNorm + Q/K/V GeMM + bias),
+// region 2 (head transform folded into attention), region 3 (FF + LayerNorm + bias + residual +
+// GELU), region 4 (bias + residual); section 三 3.3 names the mechanisms (on-chip staging of the
+// normalized vector, intra-warp reductions, a vector-matrix GeMM schedule with fused epilogues).
+//
+// gfx950 design: every weight byte is streamed once from HBM with 16-byte non-temporal loads,
+// each wave64 owns R output rows and splits the reduction dimension across its 64 lanes, the
+// (normalized) activation rows of a batch group sit in LDS, partial sums are reduced across the
+// wave with DPP/permute shuffles, and bias / residual / GeLU / KV scatter run in the epilogue.
+#include "ds_device.hpp"
+#include "ds_launch.hpp"
+
+namespace ds {
+
+template <typename WT> struct WTraits;
+template <> struct WTraits<float> { static constexpr int E = 4; typedef float LT; };
+template <> struct WTraits<half_t> { static constexpr int E = 8; typedef half_t LT; };
+template <> struct WTraits<int8_t> { static constexpr int E = 16; typedef half_t LT; };
+
+constexpr int kLdsActBytes = 64 * 1024;  // activation staging budget per workgroup
+
+// ------------------------------------------------------------------ wave GEMV core
+// acc[r][b] += sum_{k in [kbeg,kend)} W[row0 + r][k] * act[b][k - kbeg]   (one wave, 64 lanes)
+template <typename WT, int R, int BM, int U>
+__device__ __forceinline__ void gemv_rows(const WT* __restrict__ W, const half_t* __restrict__ S,
+                                          int K, int group, int row0, int nrows, int kbeg, int kend,
+                                          const typename WTraits<WT>::LT* act, int act_stride,
+                                          float (&acc)[R][BM], int lane) {
+  typedef typename WTraits<WT>::LT LT;
+  constexpr int E = WTraits<WT>::E;
+  constexpr int STEP = kWave * E;
+  const WT* wrow[R];
+  const half_t* srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + (r < nrows ? r : nrows - 1);  // surplus rows re-read a valid row
+    wrow[r] = W + (size_t)row * K;
+    srow[r] = S ? S + (size_t)row * (K / group) : nullptr;
+  }
+  int k = kbeg + lane * E;
+  auto consume = [&](const u32x4 (&w)[R], const float (&sc)[R], int kk) {
+#pragma unroll
+    for (int b = 0; b < BM; ++b) {
+      const LT* ap = act + b * act_stride + (kk - kbeg);
+      if constexpr (sizeof(WT) == 4) {
+        const float4_t a4 = *reinterpret_cast<const float4_t*>(ap);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][b] = dot4_f32(w[r], a4, acc[r][b]);
+      } else if constexpr (sizeof(WT) == 2) {
+        const u32x4 a8 = *reinterpret_cast<const u32x4*>(ap);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][b] = dot8_f16(w[r], a8, acc[r][b]);
+      } else {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 8);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][b] = fmaf(dot16_i8(w[r], a0, a1), sc[r], acc[r][b]);
+      }
+    }
+  };
+  for (; k + (U - 1) * STEP < kend; k += U * STEP) {
+    u32x4 w[U][R];
+    float sc[U][R];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        w[u][r] = ld_stream16(wrow[r] + k + u * STEP);
+        if constexpr (sizeof(WT) == 1) sc[u][r] = (float)srow[r][(k + u * STEP) / group];
+        else sc[u][r] = 1.f;
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) consume(w[u], sc[u], k + u * STEP);
+  }
+  for (; k < kend; k += STEP) {
+    u32x4 w[R];
+    float sc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      w[r] = ld_stream16(wrow[r] + k);
+      if constexpr (sizeof(WT) == 1) sc[r] = (float)srow[r][k / group];
+      else sc[r] = 1.f;
+    }
+    consume(w, sc, k);
+  }
+}
+
+template <typename T> __device__ __forceinline__ float ldf(const void* p, size_t i) {
+  return to_f32(reinterpret_cast<const T*>(p)[i]);
+}
+
+// ------------------------------------------------------------------ fused GEMV kernel
+// grid.x: row blocks of 4 waves x R rows; grid.y: activation-row groups of BM rows.
+template <typename WT, typename AT, int KIND, int BM, int R>
+__global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
+  typedef typename WTraits<WT>::LT LT;
+  constexpr int E = WTraits<WT>::E;
+  constexpr bool kLN = (KIND == KIND_QKV || KIND == KIND_FF1);
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  LT* act = reinterpret_cast<LT*>(smem_raw);
+  __shared__ float red[4];
+  __shared__ float s_mean[BM], s_rstd[BM];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int K = a.k, N = a.n;
+  const int row0 = (blockIdx.x * 4 + wave) * R;
+  const int r0 = blockIdx.y * BM;
+  const int nb = min(BM, a.rows - r0);
+
+  if (KIND == KIND_QKV && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = tid; i < a.rows * a.heads; i += 256) a.attn_counters[i] = 0u;
+
+  // LayerNorm statistics of each activation row (two passes over the row, biased variance)
+  if constexpr (kLN) {
+    for (int b = 0; b < nb; ++b) {
+      const size_t base = (size_t)(r0 + b) * K;
+      float s = 0.f;
+      for (int i = tid; i < K; i += 256)
+        s += (KIND == KIND_QKV) ? ldf<AT>(a.in, base + i) : ldf<float>(a.in, base + i);
+      const float mean = block_sum256(s, red) / K;
+      float v = 0.f;
+      for (int i = tid; i < K; i += 256) {
+        const float x = ((KIND == KIND_QKV) ? ldf<AT>(a.in, base + i) : ldf<float>(a.in, base + i)) - mean;
+        v += x * x;
+      }
+      const float var = block_sum256(v, red) / K;
+      if (tid == 0) {
+        s_mean[b] = mean;
+        s_rstd[b] = rsqrtf(var + a.eps);
+      }
+    }
+  }
+
+  // activation chunk length: a multiple of the per-iteration span 64*E
+  int KC = kLdsActBytes / (BM * (int)sizeof(LT));
+  KC = KC / (kWave * E) * (kWave * E);
+  if (KC > K) KC = K;
+
+  float acc[R][BM];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < BM; ++b) acc[r][b] = 0.f;
+
+  const int nrows = N - row0;
+  for (int kbeg = 0; kbeg < K; kbeg += KC) {
+    const int kend = min(K, kbeg + KC), len = kend - kbeg;
+    __syncthreads();  // LN statistics ready / previous chunk consumed
+    for (int idx = tid; idx < BM * len; idx += 256) {
+      const int b = idx / len, kk = idx - b * len, kg = kbeg + kk;
+      float v = 0.f;
+      if (b < nb) {
+        const size_t at = (size_t)(r0 + b) * K + kg;
+        if constexpr (KIND == KIND_QKV) v = ldf<AT>(a.in, at);
+        else v = ldf<float>(a.in, at);
+        if constexpr (kLN) v = (v - s_mean[b]) * s_rstd[b] * ldf<AT>(a.ln_g, kg) + ldf<AT>(a.ln_b, kg);
+      }
+      act[b * KC + kk] = (LT)v;
+    }
+    __syncthreads();
+    if (nrows > 0)
+      gemv_rows<WT, R, BM, 4>(reinterpret_cast<const WT*>(a.w), reinterpret_cast<const half_t*>(a.s),
+                              K, a.group, row0, nrows, kbeg, kend, act, KC, acc, lane);
+  }
+  if (nrows <= 0) return;
+
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < BM; ++b) acc[r][b] = wave_sum(acc[r][b]);
+
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < BM; ++b) {
+      if (lane != r * BM + b || r >= nrows || b >= nb) continue;
+      const int n = row0 + r, rr = r0 + b;
+      const float z = acc[r][b] + ldf<AT>(a.bias, n);
+      if constexpr (KIND == KIND_QKV) {
+        const int H = a.hidden, d = a.head_dim;
+        if (n < H) {
+          a.q_out[(size_t)rr * H + n] = z;
+        } else {
+          const int seq = rr / a.tokens, t = rr - seq * a.tokens;
+          const int pos = a.d_len[seq] + t;
+          const int m = (n < 2 * H) ? n - H : n - 2 * H;
+          const int j = m / d, e = m - j * d;
+          if (pos >= 0 && pos < a.cap) {
+            AT* cache = reinterpret_cast<AT*>(n < 2 * H ? a.k_cache : a.v_cache);
+            cache[(((size_t)seq * a.heads + j) * a.cap + pos) * d + e] = from_f32<AT>(z);
+          }
+        }
+      } else if constexpr (KIND == KIND_OPROJ) {
+        reinterpret_cast<float*>(a.out)[(size_t)rr * N + n] = ldf<AT>(a.resid, (size_t)rr * N + n) + z;
+      } else if constexpr (KIND == KIND_FF1) {
+        reinterpret_cast<float*>(a.out)[(size_t)rr * N + n] = gelu(z, a.gelu_tanh != 0);
+      } else {
+        reinterpret_cast<AT*>(a.out)[(size_t)rr * N + n] =
+            from_f32<AT>(ldf<float>(a.resid, (size_t)rr * N + n) + z);
+      }
+    }
+}
+
+template <typename WT, typename AT, int KIND, int BM>
+static hipError_t launch_gemv_bm(const GemvArgs& a, hipStream_t st) {
+  constexpr int R = 2;
+  typedef typename WTraits<WT>::LT LT;
+  constexpr int E = WTraits<WT>::E;
+  int KC = kLdsActBytes / (BM * (int)sizeof(LT));
+  KC = KC / (kWave * E) * (kWave * E);
+  if (KC > a.k) KC = a.k;
+  const size_t lds = (size_t)BM * KC * sizeof(LT);
+  dim3 grid((a.n + 4 * R - 1) / (4 * R), (a.rows + BM - 1) / BM);
+  hipLaunchKernelGGL((gemv_kernel<WT, AT, KIND, BM, R>), grid, dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <typename WT, typename AT, int KIND>
+static hipError_t launch_gemv_kind(const GemvArgs& a, hipStream_t st) {
+  if (a.rows >= 8) return launch_gemv_bm<WT, AT, KIND, 8>(a, st);
+  if (a.rows >= 4) return launch_gemv_bm<WT, AT, KIND, 4>(a, st);
+  if (a.rows >= 2) return launch_gemv_bm<WT, AT, KIND, 2>(a, st);
+  return launch_gemv_bm<WT, AT, KIND, 1>(a, st);
+}
+
+template <typename WT, typename AT>
+static hipError_t launch_gemv_t(GemvKind kind, const GemvArgs& a, hipStream_t st) {
+  switch (kind) {
+    case KIND_QKV: return launch_gemv_kind<WT, AT, KIND_QKV>(a, st);
+    case KIND_OPROJ: return launch_gemv_kind<WT, AT, KIND_OPROJ>(a, st);
+    case KIND_FF1: return launch_gemv_kind<WT, AT, KIND_FF1>(a, st);
+    case KIND_FF2: return launch_gemv_kind<WT, AT, KIND_FF2>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(Dt wdt, Dt adt, GemvKind kind, const GemvArgs& a, hipStream_t st) {
+  if (wdt == F32 && adt == F32) return launch_gemv_t<float, float>(kind, a, st);
+  if (wdt == F16 && adt == F16) return launch_gemv_t<half_t, half_t>(kind, a, st);
+  if (wdt == I8 && adt == F16) return launch_gemv_t<int8_t, half_t>(kind, a, st);
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------ decode attention
+// Region 2: for one (row, head) and one chunk of cached positions, q.K/sqrt(d) scores, a
+// wave-reduced max and sum, and the exp-weighted V sum; the last chunk workgroup to finish merges
+// the chunk partials (log-sum-exp) into ctx. grid = (nchunk, heads, rows).
+template <typename AT, int D, int C>
+__global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
+  constexpr int EK = 16 / (int)sizeof(AT);  // elements per 16-byte load
+  constexpr int LPK = D / EK;               // lanes per key
+  constexpr int KPI = kWave / LPK;          // keys per wave per load
+  constexpr int NIT = (C + 4 * KPI - 1) / (4 * KPI);
+  const float kNeg = -1e30f;
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float s_acc[4][D];
+  __shared__ int s_last;
+
+  const int c = blockIdx.x, j = blockIdx.y, rr = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int seq = rr / a.tokens, t = rr - seq * a.tokens;
+  const int len0 = a.d_len[seq];
+  int nkeys = a.causal ? len0 + t + 1 : len0 + a.tokens;
+  if (nkeys > a.cap) nkeys = a.cap;
+  const int nvalid = (nkeys + C - 1) / C;
+  if (c >= nvalid) return;
+  const int kb = c * C, ke = min(kb + C, nkeys);
+  const int H = a.heads * D;
+
+  // q slice of this lane, scaled by log2(e)/sqrt(d) so that scores feed exp2 directly
+  const int e0 = (lane % LPK) * EK;
+  const float qs = 1.4426950408889634f / sqrtf((float)D);
+  float qv[EK];
+#pragma unroll
+  for (int e = 0; e < EK; ++e) qv[e] = a.q[(size_t)rr * H + j * D + e0 + e] * qs;
+
+  const size_t head_base = (((size_t)seq * a.heads + j) * a.cap) * D;
+  const AT* Kp = reinterpret_cast<const AT*>(a.k_cache) + head_base;
+  const AT* Vp = reinterpret_cast<const AT*>(a.v_cache) + head_base;
+
+  float sc[NIT];
+  bool valid[NIT];
+  u32x4 raw[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int key = kb + (it * 4 + wave) * KPI + lane / LPK;
+    valid[it] = key < ke;
+    raw[it] = valid[it] ? ld16(Kp + (size_t)key * D + e0) : u32x4{0, 0, 0, 0};
+  }
+  float m = kNeg;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    float p = 0.f;
+    if constexpr (sizeof(AT) == 4) {
+      p = qv[0] * as_f32(raw[it].x) + qv[1] * as_f32(raw[it].y) + qv[2] * as_f32(raw[it].z) +
+          qv[3] * as_f32(raw[it].w);
+    } else {
+      const uint32_t wv[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const half2_t kk = as_half2(wv[h]);
+        p += qv[2 * h] * (float)kk.x + qv[2 * h + 1] * (float)kk.y;
+      }
+    }
+    p = group_sum<LPK>(p);
+    sc[it] = valid[it] ? p : kNeg;
+    m = fmaxf(m, sc[it]);
+  }
+  m = wave_max(m);
+
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int key = kb + (it * 4 + wave) * KPI + lane / LPK;
+    raw[it] = valid[it] ? ld16(Vp + (size_t)key * D + e0) : u32x4{0, 0, 0, 0};
+  }
+  float l = 0.f, acc[EK];
+#pragma unroll
+  for (int e = 0; e < EK; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const float p = valid[it] ? exp2f(sc[it] - m) : 0.f;
+    l += p;
+    if constexpr (sizeof(AT) == 4) {
+      acc[0] += p * as_f32(raw[it].x);
+      acc[1] += p * as_f32(raw[it].y);
+      acc[2] += p * as_f32(raw[it].z);
+      acc[3] += p * as_f32(raw[it].w);
+    } else {
+      const uint32_t wv[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const half2_t vv = as_half2(wv[h]);
+        acc[2 * h] += p * (float)vv.x;
+        acc[2 * h + 1] += p * (float)vv.y;
+      }
+    }
+  }
+  // reduce over the key slots of the wave (lanes with equal lane % LPK)
+#pragma unroll
+  for (int off = LPK; off < kWave; off <<= 1) {
+    l += __shfl_xor(l, off, kWave);
+#pragma unroll
+    for (int e = 0; e < EK; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
+  }
+  if (lane < LPK) {
+#pragma unroll
+    for (int e = 0; e < EK; ++e) s_acc[wave][e0 + e] = acc[e];
+    if (lane == 0) {
+      s_m[wave] = m;
+      s_l[wave] = l;
+    }
+  }
+  __syncthreads();
+
+  // workgroup partial: merge the four waves
+  float* part = a.part + (((size_t)rr * a.heads + j) * a.nchunk + c) * (D + 2);
+  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float f[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) f[w] = s_l[w] > 0.f ? exp2f(s_m[w] - M) : 0.f;
+  if (tid < D) part[2 + tid] = f[0] * s_acc[0][tid] + f[1] * s_acc[1][tid] + f[2] * s_acc[2][tid] + f[3] * s_acc[3][tid];
+  if (tid == 0) {
+    part[0] = M;
+    part[1] = f[0] * s_l[0] + f[1] * s_l[1] + f[2] * s_l[2] + f[3] * s_l[3];
+  }
+  __threadfence();
+  __syncthreads();
+  uint32_t* cnt = a.counters + (size_t)rr * a.heads + j;
+  if (tid == 0) s_last = (atomicAdd(cnt, 1u) == (uint32_t)(nvalid - 1));
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  // last workgroup of this (row, head): log-sum-exp merge of the nvalid chunk partials
+  const float* p0 = a.part + ((size_t)rr * a.heads + j) * a.nchunk * (D + 2);
+  if (tid < D) {
+    float MM = kNeg;
+    for (int cc = 0; cc < nvalid; ++cc) MM = fmaxf(MM, __builtin_nontemporal_load(p0 + (size_t)cc * (D + 2)));
+    float L = 0.f, A = 0.f;
+    for (int cc = 0; cc < nvalid; ++cc) {
+      const float* pc = p0 + (size_t)cc * (D + 2);
+      const float lc = __builtin_nontemporal_load(pc + 1);
+      const float w = lc > 0.f ? exp2f(__builtin_nontemporal_load(pc) - MM) : 0.f;
+      L += w * lc;
+      A += w * __builtin_nontemporal_load(pc + 2 + tid);
+    }
+    a.ctx[(size_t)rr * H + j * D + tid] = A / L;
+  }
+  if (tid == 0) *cnt = 0u;
+}
+
+constexpr int kAttnChunk = 64;
+
+int attn_chunk_for(int rows, int heads, int cap) {
+  (void)rows;
+  (void)heads;
+  (void)cap;
+  return kAttnChunk;
+}
+
+template <typename AT, int D>
+static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
+  dim3 grid(a.nchunk, a.heads, a.rows);
+  hipLaunchKernelGGL((attn_decode_kernel<AT, D, kAttnChunk>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st) {
+  if (a.chunk != kAttnChunk) return hipErrorInvalidValue;
+  if (adt == F32 && a.head_dim == 64) return launch_attn_t<float, 64>(a, st);
+  if (adt == F32 && a.head_dim == 128) return launch_attn_t<float, 128>(a, st);
+  if (adt == F16 && a.head_dim == 64) return launch_attn_t<half_t, 64>(a, st);
+  if (adt == F16 && a.head_dim == 128) return launch_attn_t<half_t, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ds

@@ -1,0 +1,159 @@
+// kernels_misc.hip -- KV-cache append, length advance, and the group-wise int8 weight quantizer.
+//
+// Source: int8 inference with group-wise quantization settings (quantize_groups) on the page
+// "DeepSpeed Inference 内核优化深度解析" (blog.gitcode.com), section 五 5.2; the KV cache bounded by
+// max_out_tokens (same page, section 四 4.2).
+#include "ds_device.hpp"
+#include "ds_launch.hpp"
+
+namespace ds {
+
+// ------------------------------------------------------------------ KV append
+// k_new/v_new [batch][ntok][H] -> cache [batch][heads][cap][d] at rows d_len[b] + t (16 bytes per
+// thread). Rows at or past capacity are skipped.
+template <typename AT>
+__global__ __launch_bounds__(256) void kv_append_kernel(const AT* __restrict__ kn, const AT* __restrict__ vn,
+                                                        AT* kc, AT* vc, const int32_t* d_len, int batch,
+                                                        int ntok, int heads, int d, int cap) {
+  constexpr int EK = 16 / (int)sizeof(AT);
+  const int H = heads * d;
+  const size_t nvec = (size_t)batch * ntok * H / EK;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nvec) return;
+  const size_t el = i * EK;
+  const int b = (int)(el / ((size_t)ntok * H));
+  const size_t rem = el - (size_t)b * ntok * H;
+  const int t = (int)(rem / H), m = (int)(rem - (size_t)t * H);
+  const int j = m / d, e = m - j * d;
+  const int pos = d_len[b] + t;
+  if (pos < 0 || pos >= cap) return;
+  const size_t at = (((size_t)b * heads + j) * cap + pos) * d + e;
+  *reinterpret_cast<u32x4*>(kc + at) = ld16(kn + el);
+  *reinterpret_cast<u32x4*>(vc + at) = ld16(vn + el);
+}
+
+__global__ void len_advance_kernel(int32_t* d_len, int batch, int ntok, int cap) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch && d_len[b] + ntok <= cap) d_len[b] += ntok;
+}
+
+hipError_t launch_kv_append(Dt adt, const void* k_new, const void* v_new, void* kc, void* vc,
+                            const int32_t* d_len, int batch, int ntok, int heads, int head_dim,
+                            int cap, hipStream_t st) {
+  const size_t el = (size_t)batch * ntok * heads * head_dim;
+  const int ek = adt == F32 ? 4 : 8;
+  const size_t nvec = el / ek;
+  if (nvec == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((nvec + 255) / 256);
+  if (adt == F32)
+    hipLaunchKernelGGL(kv_append_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)k_new,
+                       (const float*)v_new, (float*)kc, (float*)vc, d_len, batch, ntok, heads, head_dim, cap);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<half_t>, dim3(blocks), dim3(256), 0, st, (const half_t*)k_new,
+                       (const half_t*)v_new, (half_t*)kc, (half_t*)vc, d_len, batch, ntok, heads, head_dim, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_len_advance(int32_t* d_len, int batch, int ntok, int cap, hipStream_t st) {
+  hipLaunchKernelGGL(len_advance_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, d_len, batch, ntok, cap);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ int8 quantizer
+// IEEE 754 binary16 bits of a double, round to nearest, ties to even, built directly on the
+// double's bit fields: keep 10 fraction bits below the leading one (fewer in the subnormal range
+// below 2^-14), round on the discarded bits, and let a carry ripple into the exponent field.
+__device__ uint16_t f64_to_f16_bits_rne(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  const uint64_t mag = u & 0x7fffffffffffffffull;
+  if (mag >= 0x7ff0000000000000ull) return sign | (mag > 0x7ff0000000000000ull ? 0x7e00u : 0x7c00u);
+  if (mag == 0) return sign;
+  const int e = (int)(mag >> 52) - 1023;
+  if (e > 15) return sign | 0x7c00u;
+  if (e < -25) return sign;  // below 2^-25, half the smallest subnormal: rounds to zero
+  const uint64_t m = (mag & ((1ull << 52) - 1)) | (1ull << 52);  // doubles this small are normal
+  const int shift = (e >= -14) ? 42 : 42 + (-14 - e);
+  uint64_t q = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1), halfway = 1ull << (shift - 1);
+  if (rem > halfway || (rem == halfway && (q & 1))) ++q;
+  uint32_t bits = (e >= -14) ? (uint32_t)(((e + 14) << 10) + q) : (uint32_t)q;
+  if (bits >= 0x7c00u) bits = 0x7c00u;
+  return sign | (uint16_t)bits;
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
+  return (double)(float)__builtin_bit_cast(half_t, h);
+}
+
+// One thread per (row, group): amax in double, scale = fp16_RNE(amax/127), codes = clamp(rint(w/s)).
+__global__ __launch_bounds__(256) void quantize_i8_kernel(const float* __restrict__ w, int8_t* __restrict__ q,
+                                                          uint16_t* __restrict__ s, int n, int k, int group) {
+  const int ng = k / group;
+  const size_t gi = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= (size_t)n * ng) return;
+  const size_t row = gi / ng, g = gi - row * ng;
+  const float* src = w + row * k + g * group;
+  int8_t* dst = q + row * k + g * group;
+  double amax = 0.0;
+  for (int i = 0; i < group; i += 4) {
+    const float4_t v = *reinterpret_cast<const float4_t*>(src + i);
+    amax = fmax(amax, fabs((double)v.x));
+    amax = fmax(amax, fabs((double)v.y));
+    amax = fmax(amax, fabs((double)v.z));
+    amax = fmax(amax, fabs((double)v.w));
+  }
+  const uint16_t sb = f64_to_f16_bits_rne(amax / 127.0);
+  s[gi] = sb;
+  const double sv = f16_bits_to_f64(sb);
+  for (int i = 0; i < group; i += 16) {
+    uint32_t words[4];
+#pragma unroll
+    for (int wq = 0; wq < 4; ++wq) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int bq = 0; bq < 4; ++bq) {
+        double c = sv == 0.0 ? 0.0 : rint((double)src[i + wq * 4 + bq] / sv);
+        c = fmin(127.0, fmax(-127.0, c));
+        word |= ((uint32_t)(int32_t)c & 0xffu) << (8 * bq);
+      }
+      words[wq] = word;
+    }
+    *reinterpret_cast<u32x4*>(dst + i) = u32x4{words[0], words[1], words[2], words[3]};
+  }
+}
+
+// w = q * s through the same int8 -> fp16 conversion the GEMV kernels use (16 codes per thread).
+__global__ __launch_bounds__(256) void dequantize_i8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ s,
+                                                            float* __restrict__ w, int n, int k, int group) {
+  const size_t v = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= (size_t)n * k / 16) return;
+  const size_t el = v * 16, row = el / k, col = el - row * k;
+  const float sc = (float)__builtin_bit_cast(half_t, s[row * (k / group) + col / group]);
+  const u32x4 raw = ld16(q + el);
+  const uint32_t words[4] = {raw.x ^ 0x80808080u, raw.y ^ 0x80808080u, raw.z ^ 0x80808080u, raw.w ^ 0x80808080u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2_t lo = i8pair_to_half2(words[i], false), hi = i8pair_to_half2(words[i], true);
+    w[el + 4 * i + 0] = (float)lo.x * sc;
+    w[el + 4 * i + 1] = (float)lo.y * sc;
+    w[el + 4 * i + 2] = (float)hi.x * sc;
+    w[el + 4 * i + 3] = (float)hi.y * sc;
+  }
+}
+
+hipError_t launch_quantize_i8(const float* w, int8_t* q, uint16_t* s, int n, int k, int group, hipStream_t st) {
+  const size_t groups = (size_t)n * (k / group);
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_i8_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, w, q, s, n, k, group);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_i8(const int8_t* q, const uint16_t* s, float* w, int n, int k, int group, hipStream_t st) {
+  const size_t vecs = (size_t)n * k / 16;
+  if (vecs == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequantize_i8_kernel, dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, st, q, s, w, n, k, group);
+  return hipGetLastError();
+}
+
+}  // namespace ds

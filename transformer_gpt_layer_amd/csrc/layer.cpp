@@ -1,0 +1,274 @@
+// layer.cpp -- the C ABI of libdslayer.so (include/ds_layer.h): host-side validation, workspace
+// layout and the launch sequence of one layer step. No device memory is allocated here.
+//
+// The step follows the four fusion regions of one transformer layer on the page "DeepSpeed
+// Inference 内核优化深度解析" (blog.gitcode.com), section 三 3.2, with the kernel boundaries at the
+// two all-reduce points of section 三 3.1 (after the attention-output GeMM, after the FF2 GeMM):
+//   1 LN1 + QKV GEMV + bias, q to the workspace, k/v into the cache rows  (region 1 + transform)
+//   2 attention over the cache, chunked over positions, merged in-kernel  (region 2)
+//   3 output projection + bias + residual                                 (all-reduce point 1)
+//   4 LN2 + FF1 + bias + GeLU                                             (region 3)
+//   5 FF2 + bias + residual, then the cache length advances               (region 4, point 2)
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ds_layer.h"
+#include "ds_launch.hpp"
+
+struct ds_layer {
+  ds_layer_desc desc;
+  ds_layer_weights w;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(DS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+struct WsLayout {
+  size_t q, part, cnt, ctx, x2, f, total;
+  int chunk, nchunk;
+};
+
+WsLayout ws_layout(const ds_layer_desc& d, int rows, int cap) {
+  WsLayout L{};
+  L.chunk = ds::attn_chunk_for(rows, d.heads, cap);
+  L.nchunk = (cap + L.chunk - 1) / L.chunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
+  L.q = take((size_t)rows * d.hidden * 4);
+  L.part = take((size_t)rows * d.heads * L.nchunk * (d.head_dim + 2) * 4);
+  L.cnt = take((size_t)rows * d.heads * 4);
+  L.ctx = take((size_t)rows * d.hidden * 4);
+  L.x2 = take((size_t)rows * d.hidden * 4);
+  L.f = take((size_t)rows * d.ffn * 4);
+  L.total = off;
+  return L;
+}
+
+int check_kv(const ds_layer* L, const ds_kv_cache* kv, int batch, int ntok) {
+  if (!kv) return fail(DS_ERR_NULL, "kv cache is NULL");
+  if (!kv->k || !kv->v || !kv->d_len) return fail(DS_ERR_NULL, "kv cache k, v or d_len is NULL");
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(DS_ERR_ALIGN, "kv cache k or v is not 16-byte aligned");
+  if (kv->batch < 1 || kv->capacity < 1) return fail(DS_ERR_SHAPE, "kv cache batch %d / capacity %d must be >= 1", kv->batch, kv->capacity);
+  if (batch < 0 || batch > kv->batch) return fail(DS_ERR_SHAPE, "batch %d outside [0, %d]", batch, kv->batch);
+  if (ntok < 0) return fail(DS_ERR_SHAPE, "token count %d < 0", ntok);
+  if (kv->h_len)
+    for (int b = 0; b < batch; ++b)
+      if (kv->h_len[b] < 0 || (int64_t)kv->h_len[b] + ntok > kv->capacity)
+        return fail(DS_ERR_KV_FULL, "sequence %d: %d rows + %d new > capacity %d", b, kv->h_len[b], ntok, kv->capacity);
+  (void)L;
+  return DS_OK;
+}
+
+int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int batch, int ntok,
+                 void* ws, size_t ws_bytes, void* stream) {
+  if (!L) return fail(DS_ERR_NULL, "layer is NULL");
+  if (int rc = check_kv(L, kv, batch, ntok)) return rc;
+  if (batch == 0 || ntok == 0) return DS_OK;
+  if (!x || !y || !ws) return fail(DS_ERR_NULL, "x, y or workspace is NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return fail(DS_ERR_ALIGN, "x, y or workspace is not 16-byte aligned");
+  const ds_layer_desc& d = L->desc;
+  const int rows = batch * ntok;
+  const WsLayout W = ws_layout(d, rows, kv->capacity);
+  if (ws_bytes < W.total) return fail(DS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, W.total);
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
+  const int H = d.hidden, F = d.ffn;
+
+  ds::GemvArgs g{};
+  g.group = d.quant_group;
+  g.rows = rows;
+  g.tokens = ntok;
+  g.cap = kv->capacity;
+  g.heads = d.heads;
+  g.head_dim = d.head_dim;
+  g.hidden = H;
+  g.eps = d.ln_eps;
+  g.gelu_tanh = d.gelu_tanh;
+  g.d_len = kv->d_len;
+
+  // 1: LN1 + QKV + bias; q -> workspace, k/v -> cache rows d_len[b] + t
+  ds::GemvArgs a = g;
+  a.w = L->w.w_qkv; a.s = L->w.s_qkv; a.bias = L->w.b_qkv; a.in = x;
+  a.ln_g = L->w.ln1_g; a.ln_b = L->w.ln1_b;
+  a.n = 3 * H; a.k = H;
+  a.q_out = reinterpret_cast<float*>(base + W.q);
+  a.k_cache = kv->k; a.v_cache = kv->v;
+  a.attn_counters = reinterpret_cast<uint32_t*>(base + W.cnt);
+  if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_QKV, a, st)) return hip_fail(e, "ln_qkv launch");
+
+  // 2: attention over the cache
+  ds::AttnArgs at{};
+  at.q = reinterpret_cast<const float*>(base + W.q);
+  at.k_cache = kv->k; at.v_cache = kv->v; at.d_len = kv->d_len;
+  at.part = reinterpret_cast<float*>(base + W.part);
+  at.counters = reinterpret_cast<uint32_t*>(base + W.cnt);
+  at.ctx = reinterpret_cast<float*>(base + W.ctx);
+  at.rows = rows; at.tokens = ntok; at.heads = d.heads; at.head_dim = d.head_dim;
+  at.cap = kv->capacity; at.chunk = W.chunk; at.nchunk = W.nchunk; at.causal = d.triangular_masking;
+  if (hipError_t e = ds::launch_attn_decode(adt, at, st)) return hip_fail(e, "attention launch");
+
+  // 3: x2 = x + Wo ctx + bo
+  a = g;
+  a.w = L->w.w_o; a.s = L->w.s_o; a.bias = L->w.b_o;
+  a.in = base + W.ctx; a.resid = x; a.out = base + W.x2;
+  a.n = H; a.k = H;
+  if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_OPROJ, a, st)) return hip_fail(e, "o_proj launch");
+
+  // 4: f = GeLU(W1 LN2(x2) + b1)
+  a = g;
+  a.w = L->w.w_ff1; a.s = L->w.s_ff1; a.bias = L->w.b_ff1;
+  a.in = base + W.x2; a.ln_g = L->w.ln2_g; a.ln_b = L->w.ln2_b; a.out = base + W.f;
+  a.n = F; a.k = H;
+  if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_FF1, a, st)) return hip_fail(e, "ln_ff1 launch");
+
+  // 5: y = x2 + W2 f + b2, then d_len += ntok
+  a = g;
+  a.w = L->w.w_ff2; a.s = L->w.s_ff2; a.bias = L->w.b_ff2;
+  a.in = base + W.f; a.resid = base + W.x2; a.out = y;
+  a.n = H; a.k = F;
+  if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_FF2, a, st)) return hip_fail(e, "ff2 launch");
+  if (hipError_t e = ds::launch_len_advance(kv->d_len, batch, ntok, kv->capacity, st)) return hip_fail(e, "len advance launch");
+
+  if (kv->h_len)
+    for (int b = 0; b < batch; ++b) kv->h_len[b] += ntok;
+  return DS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ds_last_error(void) { return g_err.c_str(); }
+
+int ds_layer_create(const ds_layer_desc* desc, const ds_layer_weights* w, ds_layer_t** out) {
+  if (!desc || !w || !out) return fail(DS_ERR_NULL, "desc, weights or out is NULL");
+  *out = nullptr;
+  const ds_layer_desc& d = *desc;
+  if (d.heads < 1 || (d.head_dim != 64 && d.head_dim != 128))
+    return fail(DS_ERR_SHAPE, "heads %d must be >= 1 and head_dim %d must be 64 or 128", d.heads, d.head_dim);
+  if ((int64_t)d.heads * d.head_dim != d.hidden)
+    return fail(DS_ERR_SHAPE, "hidden %d != heads %d * head_dim %d", d.hidden, d.heads, d.head_dim);
+  if (d.hidden % 64 || d.ffn < 64 || d.ffn % 64 || d.hidden > 65536 || d.ffn > 262144)
+    return fail(DS_ERR_SHAPE, "hidden %d and ffn %d must be positive multiples of 64 (hidden <= 65536, ffn <= 262144)", d.hidden, d.ffn);
+  const bool pair_ok = (d.weight_dtype == DS_F32 && d.act_dtype == DS_F32) ||
+                       (d.weight_dtype == DS_F16 && d.act_dtype == DS_F16) ||
+                       (d.weight_dtype == DS_I8 && d.act_dtype == DS_F16);
+  if (!pair_ok) return fail(DS_ERR_DTYPE, "unsupported (weight, activation) dtype pair (%d, %d)", d.weight_dtype, d.act_dtype);
+  if (d.weight_dtype == DS_I8) {
+    if (d.quant_group < 16 || d.quant_group % 16 || d.hidden % d.quant_group || d.ffn % d.quant_group)
+      return fail(DS_ERR_DTYPE, "quant_group %d must be a multiple of 16 dividing hidden and ffn", d.quant_group);
+  } else if (d.quant_group != 0) {
+    return fail(DS_ERR_DTYPE, "quant_group %d must be 0 for non-int8 weights", d.quant_group);
+  }
+  if (!(d.ln_eps > 0.f) || !std::isfinite(d.ln_eps)) return fail(DS_ERR_SHAPE, "ln_eps must be finite and > 0");
+  if ((d.gelu_tanh != 0 && d.gelu_tanh != 1) || (d.triangular_masking != 0 && d.triangular_masking != 1))
+    return fail(DS_ERR_SHAPE, "gelu_tanh and triangular_masking must be 0 or 1");
+
+  const void* req[] = {w->ln1_g, w->ln1_b, w->w_qkv, w->b_qkv, w->w_o, w->b_o,
+                       w->ln2_g, w->ln2_b, w->w_ff1, w->b_ff1, w->w_ff2, w->b_ff2};
+  for (const void* p : req) {
+    if (!p) return fail(DS_ERR_NULL, "a weight, bias or LayerNorm pointer is NULL");
+    if (!aligned16(p)) return fail(DS_ERR_ALIGN, "a weight, bias or LayerNorm pointer is not 16-byte aligned");
+  }
+  const void* sc[] = {w->s_qkv, w->s_o, w->s_ff1, w->s_ff2};
+  for (const void* p : sc) {
+    if (d.weight_dtype == DS_I8) {
+      if (!p) return fail(DS_ERR_NULL, "int8 weights need all four scale pointers");
+      if (!aligned16(p)) return fail(DS_ERR_ALIGN, "a scale pointer is not 16-byte aligned");
+    } else if (p) {
+      return fail(DS_ERR_DTYPE, "scale pointers must be NULL for non-int8 weights");
+    }
+  }
+  ds_layer* L = new (std::nothrow) ds_layer;
+  if (!L) return fail(DS_ERR_NULL, "out of host memory");
+  L->desc = d;
+  L->w = *w;
+  *out = L;
+  return DS_OK;
+}
+
+int ds_layer_destroy(ds_layer_t* layer) {
+  delete layer;
+  return DS_OK;
+}
+
+size_t ds_layer_workspace_bytes(const ds_layer_t* layer, int32_t max_batch, int32_t max_tokens, int32_t capacity) {
+  if (!layer || max_batch < 1 || max_tokens < 1 || capacity < 1) return 0;
+  return ws_layout(layer->desc, max_batch * max_tokens, capacity).total;
+}
+
+int ds_kv_append(const ds_layer_t* layer, ds_kv_cache* kv, const void* k_new, const void* v_new,
+                 int32_t batch, int32_t ntok, void* stream) {
+  if (!layer) return fail(DS_ERR_NULL, "layer is NULL");
+  if (int rc = check_kv(layer, kv, batch, ntok)) return rc;
+  if (batch == 0 || ntok == 0) return DS_OK;
+  if (!k_new || !v_new) return fail(DS_ERR_NULL, "k_new or v_new is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(DS_ERR_ALIGN, "k_new or v_new is not 16-byte aligned");
+  const ds_layer_desc& d = layer->desc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipError_t e = ds::launch_kv_append(static_cast<ds::Dt>(d.act_dtype), k_new, v_new, kv->k, kv->v, kv->d_len,
+                                          batch, ntok, d.heads, d.head_dim, kv->capacity, st))
+    return hip_fail(e, "kv_append launch");
+  if (hipError_t e = ds::launch_len_advance(kv->d_len, batch, ntok, kv->capacity, st)) return hip_fail(e, "len advance launch");
+  if (kv->h_len)
+    for (int b = 0; b < batch; ++b) kv->h_len[b] += ntok;
+  return DS_OK;
+}
+
+int ds_layer_forward_decode(const ds_layer_t* layer, ds_kv_cache* kv, const void* x, void* y, int32_t batch,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_rows(layer, kv, x, y, batch, 1, workspace, workspace_bytes, stream);
+}
+
+int ds_layer_forward_prefill(const ds_layer_t* layer, ds_kv_cache* kv, const void* x, void* y, int32_t batch,
+                             int32_t seq, void* workspace, size_t workspace_bytes, void* stream) {
+  if (seq < 0) return fail(DS_ERR_SHAPE, "seq %d < 0", seq);
+  return forward_rows(layer, kv, x, y, batch, seq, workspace, workspace_bytes, stream);
+}
+
+int ds_quantize_i8(const float* w, int8_t* q, void* s, int32_t n, int32_t k, int32_t group, void* stream) {
+  if (!w || !q || !s) return fail(DS_ERR_NULL, "w, q or s is NULL");
+  if (n < 0 || k < 0 || group < 16 || group % 16 || k % group) return fail(DS_ERR_SHAPE, "need n, k >= 0, group a multiple of 16 dividing k");
+  if (!aligned16(w) || !aligned16(q)) return fail(DS_ERR_ALIGN, "w or q is not 16-byte aligned");
+  if (hipError_t e = ds::launch_quantize_i8(w, q, static_cast<uint16_t*>(s), n, k, group, reinterpret_cast<hipStream_t>(stream)))
+    return hip_fail(e, "quantize launch");
+  return DS_OK;
+}
+
+int ds_dequantize_i8(const int8_t* q, const void* s, float* w, int32_t n, int32_t k, int32_t group, void* stream) {
+  if (!w || !q || !s) return fail(DS_ERR_NULL, "q, s or w is NULL");
+  if (n < 0 || k < 0 || group < 16 || group % 16 || k % group) return fail(DS_ERR_SHAPE, "need n, k >= 0, group a multiple of 16 dividing k");
+  if (!aligned16(q)) return fail(DS_ERR_ALIGN, "q is not 16-byte aligned");
+  if (hipError_t e = ds::launch_dequantize_i8(q, static_cast<const uint16_t*>(s), w, n, k, group, reinterpret_cast<hipStream_t>(stream)))
+    return hip_fail(e, "dequantize launch");
+  return DS_OK;
+}
+
+}  // extern "C"
