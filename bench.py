@@ -1,0 +1,255 @@
+"""Decode throughput of the fused GPT-layer stack on one MI355X.
+
+One step = one decode token for every sequence of the batch through all L layers of the stack
+(LN1+QKV, attention over the KV cache, output projection, LN2+FF1+GeLU, FF2), starting from the
+same cache lengths each step. Weights and caches are seeded synthetic tensors resident in HBM
+(distinct per layer, so weights stream from HBM rather than the 256 MB last-level cache).
+
+Prints one JSON line: decode tokens/s and the achieved HBM GB/s per layer step (against the
+8 TB/s peak), the roofline entry of the dominant kernel, and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_bytes_per_layer(wl) -> dict:
+    """Bytes one layer step must move at least once (weights and scales, biases and LayerNorm
+    vectors, the past K/V rows read, the new K/V rows written, x read and y written)."""
+    H, F, B, P, T = wl.hidden, wl.ffn, wl.batch, wl.past, wl.seq
+    a = 4 if wl.act_dtype == "f32" else 2
+    nw = 3 * H * H + H * H + 2 * H * F
+    if wl.weight_dtype == "i8":
+        wbytes = nw + (nw // wl.group) * 2
+    else:
+        wbytes = nw * (4 if wl.weight_dtype == "f32" else 2)
+    small = (3 * H + H + F + H + 4 * H) * a
+    kv_read = 2 * B * P * H * a
+    kv_write = 2 * B * T * H * a
+    xy = 2 * B * T * H * a
+    return {"weights": wbytes, "small": small, "kv_read": kv_read, "kv_write": kv_write, "xy": xy,
+            "total": wbytes + small + kv_read + kv_write + xy}
+
+
+def build_stack(wl, torch, tg, syn, layers):
+    """Device weights, caches (P seeded rows each) and one shared workspace."""
+    dev = "cuda"
+    act = torch.float32 if wl.act_dtype == "f32" else torch.float16
+    cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
+                         dtype={"f32": "fp32", "f16": "fp16", "i8": "int8"}[wl.weight_dtype],
+                         quantization_setting=(wl.group, False) if wl.weight_dtype == "i8" else None)
+    stack, kvs = [], []
+    lens = torch.zeros((layers, wl.batch), dtype=torch.int32, device=dev)
+    for l in range(layers):
+        w32 = syn.layer_weights_f32(wl, l, dev)
+        gw = {}
+        for name, t in w32.items():
+            if name.startswith("w_") and wl.weight_dtype == "i8":
+                q, s = tg.quantize_i8(t.contiguous(), wl.group)
+                gw[name], gw["s" + name[1:]] = q, s
+            else:
+                gw[name] = t.to(act).contiguous()
+        del w32
+        layer = tg.Layer(cfg, gw)
+        kv = tg.KVCache(wl.batch, wl.heads, wl.capacity, wl.head_dim, act, dev, track_host=False)
+        kv.d_len = lens[l]  # one [L, B] tensor so one fill resets every layer
+        if wl.past:
+            kp, vp = syn.past_kv_f32(wl, l, dev)
+            to_rows = lambda t: t.permute(0, 2, 1, 3).reshape(wl.batch, wl.past, wl.hidden).to(act).contiguous()
+            layer.kv_append(kv, to_rows(kp), to_rows(vp))
+            del kp, vp
+        stack.append(layer)
+        kvs.append(kv)
+    torch.cuda.synchronize()
+    ws = stack[0].workspace(wl.batch, 1, wl.capacity)
+    return stack, kvs, lens, ws, act
+
+
+def cpu_baseline(wl, stack, kvs, target_s: float):
+    """The oracle (plain C, double, one thread) on a bounded sample: whole decode layer steps of
+    this workload, layer after layer, until about target_s seconds have run; scaled to tokens/s
+    of the full L-layer stack."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
+    x = np.random.default_rng(0).standard_normal((wl.batch, 1, wl.hidden))
+    done, spent = 0, 0.0
+    while spent < target_s and done < len(stack):
+        layer, kv = stack[done], kvs[done]
+        w = {}
+        for n in ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b", "w_ff1", "b_ff1", "w_ff2", "b_ff2"):
+            t = layer._weights[n]
+            if n.startswith("w_") and wl.weight_dtype == "i8":
+                s = layer._weights["s" + n[1:]]
+                w[n] = oracle.dequantize_i8(t.cpu().numpy(), s.cpu().view(torch.int16).numpy().view(np.uint16), wl.group)
+            else:
+                w[n] = t.double().cpu().numpy()
+        k = np.zeros((wl.batch, wl.heads, wl.capacity, wl.head_dim))
+        v = np.zeros_like(k)
+        k[:, :, :wl.past] = kv.k[:, :, :wl.past].double().cpu().numpy()
+        v[:, :, :wl.past] = kv.v[:, :, :wl.past].double().cpu().numpy()
+        lens = np.full(wl.batch, wl.past, dtype=np.int32)
+        t0 = time.perf_counter()
+        x = oracle.layer_forward(desc, w, k, v, lens, x)
+        spent += time.perf_counter() - t0
+        done += 1
+    per_layer = spent / done
+    return {"value": wl.batch / (per_layer * wl.layers), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} whole decode layer steps of {wl.name} (batch {wl.batch}, {wl.past} past rows) "
+                      f"in {spent:.1f} s on one host thread, scaled to the {wl.layers}-layer stack"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", help="workload key in synthetic.WORKLOADS (decode configs)")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: the workload's)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 disables)")
+    ap.add_argument("--mode", choices=["auto", "stack", "layers"], default="auto",
+                    help="stack: one persistent launch per step; layers: six kernels per layer")
+    ap.add_argument("--no-graph", action="store_true", help="layers mode: launch eagerly instead of a HIP graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synthetic as syn
+    import transformer_gpt_layer_amd as tg
+
+    wl = syn.WORKLOADS[args.config]
+    if wl.seq != 1:
+        raise SystemExit("bench.py times decode workloads")
+    layers = args.layers or wl.layers
+    torch.cuda.set_device(0)
+    stack, kvs, lens, ws, act = build_stack(wl, torch, tg, syn, layers)
+    x0 = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").to(act)
+    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+
+    def step():
+        lens.fill_(wl.past)
+        for l in range(layers):
+            stack[l].decode(kvs[l], x0 if l == 0 else bufs[l % 2], bufs[(l + 1) % 2], ws)
+
+    stream = torch.cuda.Stream()
+    use_stack = args.mode == "stack" or (args.mode == "auto" and wl.batch <= 4)
+    kernel_ms = None
+    if use_stack:
+        st = tg.Stack(stack, kvs, max_batch=wl.batch)
+        sws = st.workspace(wl.batch)
+        out = torch.empty_like(x0)
+
+        def launch():
+            st.decode(x0, out, sws)
+
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, args.warmup)):
+                lens.fill_(wl.past)
+                launch()
+        st.check()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(args.steps):
+                lens.fill_(wl.past)
+                starts[i].record(stream)
+                launch()
+                ends[i].record(stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        st.check()
+        ms = e0.elapsed_time(e1) / args.steps
+        kernel_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
+        launch_desc = f"persistent stack kernel, {st.groups} workgroups"
+    else:
+        def step():
+            lens.fill_(wl.past)
+            for l in range(layers):
+                stack[l].decode(kvs[l], x0 if l == 0 else bufs[l % 2], bufs[(l + 1) % 2], ws)
+
+        with torch.cuda.stream(stream):
+            step()
+        torch.cuda.synchronize()
+        if args.no_graph:
+            run = step
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step()
+            run = g.replay
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(args.steps):
+                run()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        out = bufs[layers % 2]
+        launch_desc = "per-layer kernels, " + ("eager" if args.no_graph else "hip-graph")
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+
+    per = algorithmic_bytes_per_layer(wl)
+    step_bytes = per["total"] * layers
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    tok_s = wl.batch / (ms * 1e-3)
+    if kernel_ms is not None:
+        kgbs = step_bytes / (kernel_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "stack_decode_kernel (all layers of one step)",
+                    "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": None,
+                    "kernel_ms": round(kernel_ms, 4), "bytes_per_launch": step_bytes}
+    else:
+        roofline = {"bound": "hbm", "kernel": "whole decode step (per-layer kernels)",
+                    "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    result = {
+        "metric": "decode tokens/s at batch 1/8 + achieved HBM GB/s (% of peak) per layer step",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "i8": "i8w-f16"}[wl.weight_dtype],
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) inputs and past K/V)",
+        "config": {"workload": wl.name, "layers": layers, "batch": wl.batch, "past_kv": wl.past,
+                   "hidden": wl.hidden, "heads": wl.heads, "ffn": wl.ffn,
+                   "launch": launch_desc},
+        "hbm_gbs_per_layer_step": round(gbs, 1),
+        "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "bytes_per_layer_step": per,
+        "roofline": roofline,
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(wl, stack, kvs, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -19,7 +19,7 @@ def _declared():
     for h in os.listdir(os.path.join(ROOT, "include")):
         if h.endswith(".h"):
             txt = open(os.path.join(ROOT, "include", h)).read()
-            names |= set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(ds_\w+)\s*\(", txt, re.M))
+            names |= set(re.findall(r"^\s*(?:int32_t|int|size_t|const char\*)\s+(ds_\w+)\s*\(", txt, re.M))
     return names
 
 

@@ -20,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import DS_F16, DS_F32, DS_I8, check, lib, ptr, stream_handle
 
-__all__ = ["LayerConfig", "make_config", "Layer", "KVCache", "quantize_i8", "dequantize_i8"]
+__all__ = ["LayerConfig", "make_config", "Layer", "KVCache", "Stack", "quantize_i8", "dequantize_i8"]
 
 _DTYPE_NAMES = {"fp32": DS_F32, "float32": DS_F32, "float": DS_F32, "f32": DS_F32,
                 "fp16": DS_F16, "float16": DS_F16, "half": DS_F16, "f16": DS_F16,
@@ -228,6 +228,62 @@ class Layer:
                 raise ValueError("k_new, v_new must be contiguous [batch, ntok, hidden] in the activation dtype")
         check(lib().ds_kv_append(self._h, C.byref(kv.c_struct()), ptr(k_new), ptr(v_new), B, T,
                                  stream_handle(stream)), "ds_kv_append")
+
+
+class Stack:
+    """Persistent decode of a whole stack: layers[l] bound to caches[l]; one launch per step.
+
+    The layers (and their weight tensors) and the caches must outlive the stack.
+    """
+
+    def __init__(self, layers, caches, max_batch: int = 1):
+        if len(layers) != len(caches) or not layers:
+            raise ValueError("need one cache per layer")
+        self.layers, self.caches, self.max_batch = list(layers), list(caches), max_batch
+        handles = (C.c_void_p * len(layers))(*[l.handle.value for l in layers])
+        self._cstructs = (_lib.KVCacheC * len(caches))(*[c.c_struct() for c in caches])
+        h = C.c_void_p()
+        check(lib().ds_stack_create(handles, self._cstructs, len(layers), max_batch, C.byref(h)), "ds_stack_create")
+        self._h = h
+        self.cfg = layers[0].cfg
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib._LIB is not None:
+            _lib._LIB.ds_stack_destroy(h)
+            self._h = None
+
+    @property
+    def groups(self) -> int:
+        return int(lib().ds_stack_groups(self._h))
+
+    def workspace_bytes(self, batch) -> int:
+        return int(lib().ds_stack_workspace_bytes(self._h, batch))
+
+    def workspace(self, batch, device="cuda") -> torch.Tensor:
+        n = self.workspace_bytes(batch)
+        if n == 0:
+            raise ValueError(f"batch {batch} outside 1..{self.max_batch}")
+        return torch.empty(n, dtype=torch.uint8, device=device)
+
+    def decode(self, x, y=None, workspace=None, stream=None):
+        """One decode step through every layer: x, y [batch, hidden]."""
+        B = x.shape[0]
+        if tuple(x.shape) != (B, self.cfg.hidden) or x.dtype != self.cfg.torch_act_dtype or not x.is_contiguous():
+            raise ValueError("x must be contiguous [batch, hidden] in the activation dtype")
+        y = torch.empty_like(x) if y is None else y
+        if workspace is None:
+            workspace = self.workspace(B, x.device)
+        check(lib().ds_stack_forward_decode(self._h, ptr(x), ptr(y), B, ptr(workspace), workspace.numel(),
+                                            stream_handle(stream)), "ds_stack_forward_decode")
+        return y
+
+    def check(self):
+        """Synchronize; raise if a step hit the grid-barrier timeout (the state is then reset)."""
+        check(lib().ds_stack_check(self._h), "ds_stack_check")
+
+    def set_timeout_us(self, us: int):
+        check(lib().ds_stack_set_timeout_us(self._h, int(us)), "ds_stack_set_timeout_us")
 
 
 def quantize_i8(w: torch.Tensor, group: int = 64, stream=None):

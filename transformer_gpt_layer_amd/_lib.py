@@ -20,7 +20,9 @@ DS_ERR_KV_FULL, DS_ERR_UNSUPPORTED, DS_ERR_HIP, DS_ERR_WORKSPACE = -5, -6, -7, -
 # every symbol the header declares
 EXPORTS = ("ds_layer_create", "ds_layer_destroy", "ds_layer_workspace_bytes", "ds_kv_append",
            "ds_layer_forward_decode", "ds_layer_forward_prefill", "ds_quantize_i8",
-           "ds_dequantize_i8", "ds_last_error")
+           "ds_dequantize_i8", "ds_last_error", "ds_stack_create", "ds_stack_destroy",
+           "ds_stack_workspace_bytes", "ds_stack_groups", "ds_stack_forward_decode",
+           "ds_stack_check", "ds_stack_set_timeout_us")
 
 
 class LayerDescC(C.Structure):
@@ -65,8 +67,19 @@ def lib():
         L.ds_quantize_i8.argtypes = [vp, vp, vp, i32, i32, i32, vp]
         L.ds_dequantize_i8.argtypes = [vp, vp, vp, i32, i32, i32, vp]
         L.ds_last_error.restype = C.c_char_p
+        L.ds_stack_create.argtypes = [C.POINTER(vp), C.POINTER(KVCacheC), i32, i32, C.POINTER(vp)]
+        L.ds_stack_destroy.argtypes = [vp]
+        L.ds_stack_workspace_bytes.argtypes = [vp, i32]
+        L.ds_stack_workspace_bytes.restype = C.c_size_t
+        L.ds_stack_groups.argtypes = [vp]
+        L.ds_stack_groups.restype = i32
+        L.ds_stack_forward_decode.argtypes = [vp, vp, vp, i32, vp, C.c_size_t, vp]
+        L.ds_stack_check.argtypes = [vp]
+        L.ds_stack_set_timeout_us.argtypes = [vp, C.c_int64]
         for name in ("ds_layer_create", "ds_layer_destroy", "ds_kv_append", "ds_layer_forward_decode",
-                     "ds_layer_forward_prefill", "ds_quantize_i8", "ds_dequantize_i8"):
+                     "ds_layer_forward_prefill", "ds_quantize_i8", "ds_dequantize_i8", "ds_stack_create",
+                     "ds_stack_destroy", "ds_stack_forward_decode", "ds_stack_check",
+                     "ds_stack_set_timeout_us"):
             getattr(L, name).restype = C.c_int
         _LIB = L
     return _LIB

@@ -116,6 +116,13 @@ __device__ __forceinline__ float gelu(float u, bool tanh_form) {
   return 0.5f * u * (1.f + erff(u * 0.7071067811865476f));
 }
 
+// ---------------------------------------------------------------- weight element traits
+// E: weight elements per 16-byte load; LT: type of the staged activation the weights meet.
+template <typename WT> struct WTraits;
+template <> struct WTraits<float> { static constexpr int E = 4; typedef float LT; };
+template <> struct WTraits<half_t> { static constexpr int E = 8; typedef half_t LT; };
+template <> struct WTraits<int8_t> { static constexpr int E = 16; typedef half_t LT; };
+
 // ---------------------------------------------------------------- stores in the activation type
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }

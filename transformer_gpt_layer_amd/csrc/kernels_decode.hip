@@ -15,11 +15,6 @@
 
 namespace ds {
 
-template <typename WT> struct WTraits;
-template <> struct WTraits<float> { static constexpr int E = 4; typedef float LT; };
-template <> struct WTraits<half_t> { static constexpr int E = 8; typedef half_t LT; };
-template <> struct WTraits<int8_t> { static constexpr int E = 16; typedef half_t LT; };
-
 constexpr int kLdsActBytes = 64 * 1024;  // activation staging budget per workgroup
 
 // ------------------------------------------------------------------ wave GEMV core

@@ -17,19 +17,14 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/ds_layer.h"
+#include "ds_internal.hpp"
 #include "ds_launch.hpp"
 
-struct ds_layer {
-  ds_layer_desc desc;
-  ds_layer_weights w;
-};
-
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+int ds::set_error(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -37,6 +32,13 @@ int fail(int code, const char* fmt, ...) {
   va_end(ap);
   g_err = buf;
   return code;
+}
+
+namespace {
+
+template <typename... Args>
+int fail(int code, const char* fmt, Args... args) {
+  return ds::set_error(code, fmt, args...);
 }
 
 int hip_fail(hipError_t e, const char* where) {

@@ -1,0 +1,231 @@
+// stack.cpp -- C ABI of the persistent multi-layer decode (ds_stack_* in include/ds_layer.h).
+//
+// A stack binds L layers that share one description to their L KV caches and runs a whole decode
+// step -- every fusion region of every layer ("DeepSpeed Inference 内核优化深度解析", section 三 3.2)
+// -- in one cooperative launch. The library owns two small device buffers per stack: the table of
+// layer pointers and the grid-barrier / attention-merge counters (zero at rest).
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "ds_internal.hpp"
+#include "ds_stack.hpp"
+
+struct ds_stack {
+  ds_layer_desc desc;
+  std::vector<ds_kv_cache> caches;
+  int n_layers = 0, max_batch = 0, G = 0, nchunk = 0, device = 0;
+  ds::StackLayer* d_layers = nullptr;
+  uint32_t* d_sync = nullptr;
+  size_t sync_words = 0;
+  uint64_t timeout_ticks = 200000000ull;  // 2 s at the 100 MHz wall clock
+};
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+int slice_elems(int wdt) { return wdt == DS_F32 ? 256 : (wdt == DS_F16 ? 512 : 1024); }
+size_t act_bytes(int adt) { return adt == DS_F32 ? 4 : 2; }
+
+struct StackWs {
+  size_t q, part, ctx, x2, f, y0, y1, total;
+};
+
+StackWs stack_ws(const ds_stack& S, int batch) {
+  const ds_layer_desc& d = S.desc;
+  const size_t a = act_bytes(d.act_dtype);
+  StackWs W{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
+  W.q = take((size_t)batch * d.hidden * 4);
+  W.part = take((size_t)batch * d.heads * S.nchunk * (d.head_dim + 2) * 4);
+  W.ctx = take((size_t)batch * d.hidden * a);
+  W.x2 = take((size_t)batch * d.hidden * 4);
+  W.f = take((size_t)batch * d.ffn * a);
+  W.y0 = take((size_t)batch * d.hidden * a);
+  W.y1 = take((size_t)batch * d.hidden * a);
+  W.total = off;
+  return W;
+}
+
+int hip_err(hipError_t e, const char* where) {
+  return ds::set_error(DS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, int32_t n_layers,
+                    int32_t max_batch, ds_stack_t** out) {
+  if (!layers || !caches || !out) return ds::set_error(DS_ERR_NULL, "layers, caches or out is NULL");
+  *out = nullptr;
+  if (n_layers < 1) return ds::set_error(DS_ERR_SHAPE, "n_layers %d < 1", n_layers);
+  if (max_batch < 1 || max_batch > 4)
+    return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode handles batch 1..4, got %d", max_batch);
+  if (layers[0] && layers[0]->desc.weight_dtype == DS_F32 && max_batch > 1)
+    return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode with fp32 weights handles batch 1 only");
+  for (int l = 0; l < n_layers; ++l)
+    if (!layers[l]) return ds::set_error(DS_ERR_NULL, "layer %d is NULL", l);
+  const ds_layer_desc d = layers[0]->desc;
+  for (int l = 1; l < n_layers; ++l)
+    if (std::memcmp(&layers[l]->desc, &d, sizeof d) != 0)
+      return ds::set_error(DS_ERR_SHAPE, "layer %d has a different description from layer 0", l);
+  const int sl = slice_elems(d.weight_dtype);
+  const size_t wsz = d.weight_dtype == DS_F32 ? 4 : (d.weight_dtype == DS_F16 ? 2 : 1);
+  if ((size_t)d.hidden * d.ffn * wsz >= (1ull << 31) || (size_t)3 * d.hidden * d.hidden * wsz >= (1ull << 31))
+    return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode needs every weight matrix under 2 GiB");
+  if (d.hidden % sl || d.ffn % sl || d.hidden > 8192)
+    return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode needs hidden and ffn multiples of %d and hidden <= 8192", sl);
+  for (int l = 0; l < n_layers; ++l) {
+    const ds_kv_cache& c = caches[l];
+    if (!c.k || !c.v || !c.d_len) return ds::set_error(DS_ERR_NULL, "cache %d: k, v or d_len is NULL", l);
+    if (!aligned16(c.k) || !aligned16(c.v)) return ds::set_error(DS_ERR_ALIGN, "cache %d is not 16-byte aligned", l);
+    if (c.batch < max_batch || c.capacity < 1 || c.capacity != caches[0].capacity)
+      return ds::set_error(DS_ERR_SHAPE, "cache %d: batch %d < %d or capacity differs from cache 0", l, c.batch, max_batch);
+    if ((size_t)c.batch * d.heads * c.capacity * d.head_dim * act_bytes(d.act_dtype) >= (1ull << 31))
+      return ds::set_error(DS_ERR_UNSUPPORTED, "cache %d is 2 GiB or larger", l);
+  }
+
+  ds_stack* S = new (std::nothrow) ds_stack;
+  if (!S) return ds::set_error(DS_ERR_NULL, "out of host memory");
+  S->desc = d;
+  S->caches.assign(caches, caches + n_layers);
+  S->n_layers = n_layers;
+  S->max_batch = max_batch;
+  S->nchunk = (caches[0].capacity + ds::kStackChunk - 1) / ds::kStackChunk;
+  const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
+  hipError_t e = hipGetDevice(&S->device);
+  int cus = 0;
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, S->device);
+  int G = 2 * cus;
+  for (int iter = 0; e == hipSuccess && iter < 3; ++iter) {
+    const size_t lds = ds::stack_lds_bytes(wdt, max_batch, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, G));
+    int fit = 0;
+    e = ds::stack_max_groups(wdt, adt, max_batch, lds, &fit);
+    if (e == hipSuccess) G = G < fit ? G : fit;
+  }
+  if (e != hipSuccess || G < 1) {
+    delete S;
+    return e != hipSuccess ? hip_err(e, "stack occupancy query") : ds::set_error(DS_ERR_UNSUPPORTED, "no co-resident workgroup fits");
+  }
+  S->G = G;
+
+  std::vector<ds::StackLayer> table(n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    const ds_layer_weights& w = layers[l]->w;
+    table[l] = ds::StackLayer{w.ln1_g, w.ln1_b, w.w_qkv, w.b_qkv, w.s_qkv, w.w_o, w.b_o, w.s_o,
+                              w.ln2_g, w.ln2_b, w.w_ff1, w.b_ff1, w.s_ff1, w.w_ff2, w.b_ff2, w.s_ff2,
+                              caches[l].k, caches[l].v, caches[l].d_len};
+  }
+  S->sync_words = ds::kSyncAttn + (size_t)max_batch * d.heads;
+  e = hipMalloc(reinterpret_cast<void**>(&S->d_layers), sizeof(ds::StackLayer) * n_layers);
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&S->d_sync), S->sync_words * 4);
+  if (e == hipSuccess) e = hipMemcpy(S->d_layers, table.data(), sizeof(ds::StackLayer) * n_layers, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(S->d_sync, 0, S->sync_words * 4);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(S->d_layers);
+    (void)hipFree(S->d_sync);
+    delete S;
+    return hip_err(e, "stack device state");
+  }
+  *out = S;
+  return DS_OK;
+}
+
+int ds_stack_destroy(ds_stack_t* S) {
+  if (!S) return DS_OK;
+  (void)hipFree(S->d_layers);
+  (void)hipFree(S->d_sync);
+  delete S;
+  return DS_OK;
+}
+
+size_t ds_stack_workspace_bytes(const ds_stack_t* S, int32_t batch) {
+  if (!S || batch < 1 || batch > S->max_batch) return 0;
+  return stack_ws(*S, batch).total;
+}
+
+int32_t ds_stack_groups(const ds_stack_t* S) { return S ? S->G : 0; }
+
+int ds_stack_forward_decode(ds_stack_t* S, const void* x, void* y, int32_t batch, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!S) return ds::set_error(DS_ERR_NULL, "stack is NULL");
+  if (batch < 1 || batch > S->max_batch) return ds::set_error(DS_ERR_SHAPE, "batch %d outside [1, %d]", batch, S->max_batch);
+  if (!x || !y || !ws) return ds::set_error(DS_ERR_NULL, "x, y or workspace is NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return ds::set_error(DS_ERR_ALIGN, "x, y or workspace is not 16-byte aligned");
+  const StackWs W = stack_ws(*S, batch);
+  if (ws_bytes < W.total) return ds::set_error(DS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, W.total);
+  const int cap = S->caches[0].capacity;
+  for (int l = 0; l < S->n_layers; ++l) {
+    const int32_t* hl = S->caches[l].h_len;
+    if (!hl) continue;
+    for (int b = 0; b < batch; ++b)
+      if (hl[b] < 0 || hl[b] + 1 > cap)
+        return ds::set_error(DS_ERR_KV_FULL, "layer %d sequence %d: %d rows + 1 > capacity %d", l, b, hl[b], cap);
+  }
+  const ds_layer_desc& d = S->desc;
+  char* base = static_cast<char*>(ws);
+  ds::StackArgs a{};
+  a.layers = S->d_layers;
+  a.n_layers = S->n_layers;
+  a.x = x;
+  a.y = y;
+  a.B = batch;
+  a.H = d.hidden;
+  a.nh = d.heads;
+  a.d = d.head_dim;
+  a.F = d.ffn;
+  a.cap = cap;
+  a.group = d.quant_group;
+  a.eps = d.ln_eps;
+  a.gelu_tanh = d.gelu_tanh;
+  a.q = reinterpret_cast<float*>(base + W.q);
+  a.part = reinterpret_cast<float*>(base + W.part);
+  a.ctx = base + W.ctx;
+  a.x2 = reinterpret_cast<float*>(base + W.x2);
+  a.f = base + W.f;
+  a.ybuf0 = base + W.y0;
+  a.ybuf1 = base + W.y1;
+  a.sync = S->d_sync;
+  a.G = S->G;
+  a.nchunk = S->nchunk;
+  a.timeout_ticks = S->timeout_ticks;
+  const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
+  const size_t lds = ds::stack_lds_bytes(wdt, batch, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->G));
+  if (hipError_t e = ds::launch_stack_decode(wdt, adt, a, lds, reinterpret_cast<hipStream_t>(stream)))
+    return hip_err(e, "persistent decode launch");
+  for (int l = 0; l < S->n_layers; ++l)
+    if (int32_t* hl = S->caches[l].h_len)
+      for (int b = 0; b < batch; ++b) hl[b] += 1;
+  return DS_OK;
+}
+
+int ds_stack_check(ds_stack_t* S) {
+  if (!S) return ds::set_error(DS_ERR_NULL, "stack is NULL");
+  uint32_t words[ds::kSyncAttn] = {0, 0, 0, 0};
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(words, S->d_sync, sizeof words, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_err(e, "stack check");
+  if (words[ds::kSyncError] != 0 || words[ds::kSyncArrive] != 0 || words[ds::kSyncExit] != 0) {
+    (void)hipMemset(S->d_sync, 0, S->sync_words * 4);
+    (void)hipDeviceSynchronize();
+    return ds::set_error(DS_ERR_HIP, "persistent decode: a grid barrier timed out (error %u, arrivals %u, exits %u); "
+                         "state reset, outputs of the failed step are invalid",
+                         words[ds::kSyncError], words[ds::kSyncArrive], words[ds::kSyncExit]);
+  }
+  return DS_OK;
+}
+
+int ds_stack_set_timeout_us(ds_stack_t* S, int64_t us) {
+  if (!S) return ds::set_error(DS_ERR_NULL, "stack is NULL");
+  if (us < 1) return ds::set_error(DS_ERR_SHAPE, "timeout must be >= 1 us");
+  S->timeout_ticks = (uint64_t)us * 100u;
+  return DS_OK;
+}
+
+}  // extern "C"
