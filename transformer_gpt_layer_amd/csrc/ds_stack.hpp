@@ -16,8 +16,19 @@ struct StackLayer {
   int32_t* d_len;
 };
 
-// sync[] layout (library-owned, zero at rest)
-enum { kSyncArrive = 0, kSyncExit = 1, kSyncError = 2, kSyncAttn = 4 };
+// sync[] layout in 32-bit words (library-owned, zero at rest). Barrier arrivals spread over
+// kSyncGroups counters, each on its own 256-byte line; the last arrival of a group bumps the top
+// counter, the last top arrival publishes the barrier's epoch in the release flag.
+constexpr int kSyncGroups = 16;
+constexpr int kSyncLine = 64;
+enum {
+  kSyncSub = 0,
+  kSyncTop = kSyncGroups * kSyncLine,
+  kSyncFlag = kSyncTop + kSyncLine,
+  kSyncExit = kSyncFlag + kSyncLine,
+  kSyncError = kSyncExit + kSyncLine,
+  kSyncAttn = kSyncError + kSyncLine,  // then B*nh attention-merge counters
+};
 
 struct StackArgs {
   const StackLayer* layers;
@@ -41,8 +52,9 @@ struct StackArgs {
   uint64_t timeout_ticks;  // per grid-barrier wait, in 100 MHz wall-clock ticks
 };
 
-constexpr int kStackChunk = 32;   // cache rows per attention work item
-constexpr int kStackThreads = 256;
+constexpr int kStackChunk = 64;    // cache rows per attention work item
+constexpr int kStackThreads = 512;  // 8 wave64 per workgroup, one workgroup per CU
+constexpr int kStackWaves = kStackThreads / 64;
 
 // Dynamic LDS bytes of one workgroup and the workgroup count the device can keep co-resident.
 size_t stack_lds_bytes(Dt wdt, int B, int H, int F, int rows_per_wg);
@@ -50,5 +62,7 @@ hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups);
 hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, size_t lds, hipStream_t st);
 // The largest per-workgroup row tile among the four projections for a grid of G workgroups.
 int stack_rows_per_wg(int H, int F, int G);
+// LDS the attention merge stages (it reuses the start of the dynamic LDS).
+size_t stack_merge_bytes(int nchunk, int head_dim);
 
 }  // namespace ds

@@ -7,25 +7,31 @@
 // fusion boundaries where partial results must meet (the all-reduce points); here those are the
 // grid-wide barriers between phases.
 //
-// gfx950 design. One cooperative launch keeps G workgroups (2 per CU) resident for the whole step.
-// Each projection is cut into per-workgroup row tiles; a tile is a list of 1 KB "slices" (one 16-byte
-// load per lane of a wave64) dealt round-robin to the four waves, so every phase is balanced
-// whatever its shape. Before each grid barrier a workgroup already issues the weight loads of its
-// next tile into registers: weights do not depend on the activations, so HBM keeps streaming while
-// the barrier settles. Activations that cross workgroups are written and read with sc1 buffer
-// operations (at the device coherence point, past the per-XCD L2 copies); barrier counters are
-// agent-scope atomics. Each grid-barrier wait is bounded by a wall-clock timeout that raises an
-// error flag, after which every workgroup leaves the kernel.
+// gfx950 design. One cooperative launch keeps one 8-wave workgroup per CU resident for the whole
+// step. Each projection is cut into per-workgroup row tiles; a tile is one contiguous range of the
+// row-major matrix, cut into 1 KB "slices" (one 16-byte load per lane of a wave64), and each wave
+// owns a contiguous block of slices, so every phase is balanced whatever its shape. As soon as a
+// workgroup has stored a phase's results it issues the weight loads of its next tile into
+// registers: weights do not depend on activations, so HBM keeps streaming through the epilogue,
+// the grid barrier and the next phase's staging. The loads complete in issue order, so waiting
+// until at most that many are outstanding (s_waitcnt vmcnt(N)) proves the earlier stores done
+// without waiting for the prefetch. Activations that cross workgroups are written and read with
+// sc1 buffer operations (at the device coherence point, past the per-XCD L2 copies); barrier
+// arrivals are agent-scope atomics spread over 16 counters. Every barrier wait is bounded by a
+// wall-clock timeout that raises an error flag, after which every workgroup leaves the kernel.
 #include "ds_device.hpp"
 #include "ds_stack.hpp"
 
 namespace ds {
 namespace {
 
-constexpr int kAuxCoherent = 16;       // sc1
-constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit dword format
+constexpr int NW = kStackWaves;
+constexpr int kAuxCoherent = 16;         // sc1
+constexpr int kAuxStream = 2;            // nt
+constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dword format
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // a buffer offset past every descriptor: loads return 0
 // Weight slices (16 B per lane) a wave holds in registers: 25 covers a whole row tile of the
-// GPT-Neo-2.7B shapes at 512 workgroups; int8 slices also carry a scale and widen in registers.
+// GPT-Neo-2.7B shapes on 256 workgroups; int8 slices also carry a scale and widen in registers.
 template <typename WT> struct MaxSlices { static constexpr int value = 25; };
 template <> struct MaxSlices<int8_t> { static constexpr int value = 16; };
 
@@ -42,9 +48,6 @@ __device__ __forceinline__ uint32_t coh_load4(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ void coh_store4(rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kAuxCoherent);
-}
-__device__ __forceinline__ void coh_store16(rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kAuxCoherent);
 }
 
 // coherent scalar access in the activation type
@@ -68,42 +71,85 @@ template <typename T> __device__ __forceinline__ float ldp(const void* p, int i)
   return (float)reinterpret_cast<const T*>(p)[i];
 }
 
-// ------------------------------------------------------------------ grid barrier
-// Arrive: this wave's stores are complete (s_waitcnt), the workgroup is in step, one atomic add.
-__device__ __forceinline__ void grid_arrive(uint32_t* sync) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(sync + kSyncArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima).
+template <int N> __device__ __forceinline__ void wait_vm_at_most() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
 }
 
-// Wait until `target` arrivals; false (for the whole workgroup) on timeout or a raised error flag.
-__device__ __forceinline__ bool grid_wait(uint32_t* sync, uint32_t target, uint64_t timeout, int* s_flag) {
-  if (threadIdx.x == 0) {
+// Workgroup barrier that waits only for LDS traffic, not for outstanding global loads.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Block-wide sums of two values at once; `red2` is NW float2 of LDS.
+__device__ __forceinline__ float2_t block_sum2(float2_t v, float2_t* red2, int tid) {
+  v.x = wave_sum(v.x);
+  v.y = wave_sum(v.y);
+  lds_barrier();
+  if ((tid & 63) == 0) red2[tid >> 6] = v;
+  lds_barrier();
+  float2_t s = {0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += red2[w];
+  return s;
+}
+
+// ------------------------------------------------------------------ grid barrier
+// Arrive at barrier `epoch` (1, 2, ...): one atomic add per workgroup on its group's counter; the
+// last of a group adds to the top counter; the last top arrival publishes the epoch. The caller
+// has made its own stores complete (vmcnt) before this.
+__device__ __forceinline__ void grid_arrive(uint32_t* sync, uint32_t epoch, int g, int G, int tid) {
+  lds_barrier();
+  if (tid == 0) {
+    const int ng = G < kSyncGroups ? G : kSyncGroups;
+    const int gi = g % ng;
+    const uint32_t members = (uint32_t)((G - gi + ng - 1) / ng);
+    const uint32_t old = __hip_atomic_fetch_add(sync + kSyncSub + gi * kSyncLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == epoch * members - 1u) {
+      const uint32_t top = __hip_atomic_fetch_add(sync + kSyncTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (top == epoch * (uint32_t)ng - 1u) __hip_atomic_store(sync + kSyncFlag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Wait until barrier `epoch` is released; false (for the whole workgroup) on timeout or a raised
+// error flag.
+__device__ __forceinline__ bool grid_wait(uint32_t* sync, uint32_t epoch, uint64_t timeout, int* s_flag, int tid) {
+  if (tid == 0) {
     int ok = 1;
     const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(sync + kSyncArrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(sync + kSyncFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch) {
       if (__hip_atomic_load(sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
           wall_clock64() - t0 > timeout) {
         __hip_atomic_store(sync + kSyncError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(2);
     }
     *s_flag = ok;
   }
-  __syncthreads();
+  lds_barrier();
   return *s_flag != 0;
 }
 
 // ------------------------------------------------------------------ weight tiles
 // A tile is rows [r0, r0+nr) of a row-major [N][K] matrix: one contiguous range of nr*K elements,
-// cut into slices of 64*E elements (one 16-byte load per lane of a wave). K is a multiple of the
-// slice, so slice s of the tile starts at element r0*K + s*64E and lies in tile row s / (K/64E).
-// Wave w owns the contiguous block of slices [w*M, min(T, (w+1)*M)), M = ceil(T/4), and holds up
-// to MaxSlices<WT> of them in registers at a time (one "round").
+// cut into slices of 64*E elements. K is a multiple of the slice, so slice s of the tile starts
+// at element r0*K + s*64E and lies in tile row s / (K/64E). Wave w owns the contiguous block of
+// slices [w*M, min(T, (w+1)*M)), M = ceil(T/NW), and holds up to MaxSlices<WT> of them in
+// registers at a time (one "round").
 template <typename WT> struct WRegs {
   static constexpr int N = MaxSlices<WT>::value;
+  // loads one round issues: the slices, plus their scales for int8
+  static constexpr int kLoads = sizeof(WT) == 1 ? 2 * N : N;
   u32x4 w[N];
   float sc[N];
 };
@@ -112,20 +158,20 @@ struct Block {
   int s0, cnt;
 };
 __device__ __forceinline__ Block wave_block(int T, int wave) {
-  const int M = (T + 3) >> 2;
+  const int M = (T + NW - 1) / NW;
   const int s0 = wave * M;
   const int e = min(T, s0 + M);
   return Block{s0, e > s0 ? e - s0 : 0};
 }
 
-// Issue the loads of slices [s, s + n) of the tile (n <= WRegs<WT>::N) into R. Buffer loads keep
-// one per-lane offset register for all of them (the slice offsets are uniform, in SGPRs), and
-// the descriptor's size bounds every access to the matrix. Non-temporal: weights are read once.
+// Issue exactly WRegs<WT>::kLoads loads: slices [s, s + n) of the tile (n <= N) into R, and
+// out-of-range loads (which return zero and touch no memory) for the rest, so that the number of
+// loads in flight after this call is known at compile time. Buffer loads keep one per-lane offset
+// register for all of them, and the descriptor's size bounds every access to the matrix.
 template <typename WT>
 __device__ __forceinline__ void issue_slices(WRegs<WT>& R, const WT* __restrict__ W, const half_t* __restrict__ S,
                                              int N, int K, int group, int r0, int s, int n, int lane) {
   constexpr int E = WTraits<WT>::E, SL = kWave * E;
-  constexpr int kAuxStream = 2;  // nt
   const rsrc_t rw = make_rsrc(W, (uint32_t)((size_t)N * K * sizeof(WT)));
   const uint32_t first = (uint32_t)((size_t)r0 * K + (size_t)s * SL);  // element index of slice s
   const uint32_t voff = (uint32_t)(lane * E * sizeof(WT));
@@ -134,28 +180,24 @@ __device__ __forceinline__ void issue_slices(WRegs<WT>& R, const WT* __restrict_
   const uint32_t svoff = sizeof(WT) == 1 ? (uint32_t)((lane * E / group) * 2) : 0u;
 #pragma unroll
   for (int i = 0; i < WRegs<WT>::N; ++i) {
-    // every entry is written, so the previous round's registers are dead from here on
-    if (i < n) {
-      const uint32_t e0 = first + (uint32_t)(i * SL);
-      R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff, e0 * (uint32_t)sizeof(WT), kAuxStream);
-      if constexpr (sizeof(WT) == 1) {
-        const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rs, svoff, (e0 / group) * 2, 0);
-        R.sc[i] = (float)__builtin_bit_cast(half_t, h);
-      }
-    } else {
-      R.w[i] = u32x4{0, 0, 0, 0};
-      R.sc[i] = 0.f;
+    const uint32_t e0 = first + (uint32_t)(i * SL);
+    const bool in = i < n;
+    R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff, in ? e0 * (uint32_t)sizeof(WT) : kOutOfRange, kAuxStream);
+    if constexpr (sizeof(WT) == 1) {
+      const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rs, svoff, in ? (e0 / group) * 2 : kOutOfRange, 0);
+      R.sc[i] = (float)__builtin_bit_cast(half_t, h);
     }
   }
 }
 
-// Round 0 of this wave's block (issued before a grid barrier).
+// Round 0 of this wave's block. Always issues WRegs<WT>::kLoads loads (an empty tile gets only
+// out-of-range ones).
 template <typename WT>
 __device__ __forceinline__ void prefetch_tile(WRegs<WT>& R, const WT* W, const half_t* S, int N, int K, int group,
                                               int r0, int nr, int wave, int lane) {
   constexpr int SL = kWave * WTraits<WT>::E;
-  const Block bl = wave_block(nr * (K / SL), wave);
-  if (bl.cnt > 0) issue_slices<WT>(R, W, S, N, K, group, r0, bl.s0, min(bl.cnt, WRegs<WT>::N), lane);
+  const Block bl = wave_block(nr > 0 ? nr * (K / SL) : 0, wave);
+  issue_slices<WT>(R, W, S, N, K, group, r0, bl.s0, min(bl.cnt, WRegs<WT>::N), lane);
 }
 
 template <int BM>
@@ -163,7 +205,7 @@ __device__ __forceinline__ void flush_rows(float (&acc)[BM], float* slots, int r
 #pragma unroll
   for (int b = 0; b < BM; ++b) {
     const float v = wave_sum(acc[b]);
-    if (lane == 0) slots[(rl * 4 + wave) * BM + b] = v;
+    if (lane == 0) slots[(rl * NW + wave) * BM + b] = v;
     acc[b] = 0.f;
   }
 }
@@ -215,112 +257,157 @@ __device__ __forceinline__ void gemv_tile(WRegs<WT>& R, const WT* __restrict__ W
 }
 
 // ------------------------------------------------------------------ activation staging
-// Copy BM rows of K elements of type IT (written by other workgroups: coherent loads) into LDS as LT.
+constexpr int kStageUnroll = 4;  // 16-byte loads a thread has in flight while staging
+
+// Copy B rows of K elements of type IT (written by other workgroups: coherent loads) into LDS as
+// LT, zero-filling rows B..BM-1.
 template <typename IT, typename LT, int BM>
 __device__ __forceinline__ void stage_plain(const void* in, int B, int K, LT* act, int tid) {
   constexpr int V = 16 / (int)sizeof(IT);
   const rsrc_t r = make_rsrc(in, (uint32_t)(B * K * sizeof(IT)));
   const int nvec = BM * K / V;
-  for (int j = tid; j < nvec; j += kStackThreads) {
-    const int b = (j * V) / K, k = j * V - b * K;
-    u32x4 raw = {0, 0, 0, 0};
-    if (b < B) raw = coh_load16(r, (uint32_t)((b * K + k) * sizeof(IT)));
-    if constexpr (sizeof(IT) == sizeof(LT)) {
-      *reinterpret_cast<u32x4*>(act + b * K + k) = raw;
-    } else {  // float input to half LDS
-      act[b * K + k + 0] = (LT)as_f32(raw.x);
-      act[b * K + k + 1] = (LT)as_f32(raw.y);
-      act[b * K + k + 2] = (LT)as_f32(raw.z);
-      act[b * K + k + 3] = (LT)as_f32(raw.w);
+  for (int j0 = tid; j0 < nvec; j0 += kStackThreads * kStageUnroll) {
+    u32x4 raw[kStageUnroll];
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int j = j0 + u * kStackThreads;
+      const uint32_t off = (uint32_t)(j * V * sizeof(IT));
+      raw[u] = coh_load16(r, j < nvec ? off : kOutOfRange);  // rows past B are out of range: zero
+    }
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int j = j0 + u * kStackThreads;
+      if (j >= nvec) break;
+      if constexpr (sizeof(IT) == sizeof(LT)) {
+        *reinterpret_cast<u32x4*>(act + j * V) = raw[u];
+      } else {  // float input to half LDS
+        act[j * V + 0] = (LT)as_f32(raw[u].x);
+        act[j * V + 1] = (LT)as_f32(raw[u].y);
+        act[j * V + 2] = (LT)as_f32(raw[u].z);
+        act[j * V + 3] = (LT)as_f32(raw[u].w);
+      }
     }
   }
 }
 
-// LayerNorm BM rows (biased variance, two passes) into LDS as LT. The raw rows are first copied
+// LayerNorm B rows (biased variance, two passes) into LDS as LT. The raw rows are first copied
 // to `raw` (BM*K floats of LDS) so that both passes read LDS, not global memory.
 template <typename IT, typename LT, typename AT, int BM>
 __device__ __forceinline__ void stage_ln(const void* in, int B, int K, const AT* __restrict__ g,
-                                         const AT* __restrict__ beta, float eps, LT* act, float* raw, float* red,
+                                         const AT* __restrict__ beta, float eps, LT* act, float* raw, float2_t* red2,
                                          int tid) {
   constexpr int V = 16 / (int)sizeof(IT);
   const rsrc_t r = make_rsrc(in, (uint32_t)(B * K * sizeof(IT)));
-  for (int j = tid; j < B * K / V; j += kStackThreads) {
-    const u32x4 v = coh_load16(r, (uint32_t)(j * 16));
-    if constexpr (sizeof(IT) == 4) {
-      *reinterpret_cast<u32x4*>(raw + j * V) = v;
-    } else {
-      const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+  const int nvec = B * K / V;
+  for (int j0 = tid; j0 < nvec; j0 += kStackThreads * kStageUnroll) {
+    u32x4 v[kStageUnroll];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const half2_t p = as_half2(ww[h]);
-        raw[j * V + 2 * h] = (float)p.x;
-        raw[j * V + 2 * h + 1] = (float)p.y;
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int j = j0 + u * kStackThreads;
+      v[u] = coh_load16(r, j < nvec ? (uint32_t)(j * 16) : kOutOfRange);
+    }
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int j = j0 + u * kStackThreads;
+      if (j >= nvec) break;
+      if constexpr (sizeof(IT) == 4) {
+        *reinterpret_cast<u32x4*>(raw + j * V) = v[u];
+      } else {
+        const uint32_t ww[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const half2_t p = as_half2(ww[h]);
+          raw[j * V + 2 * h] = (float)p.x;
+          raw[j * V + 2 * h + 1] = (float)p.y;
+        }
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int b = 0; b < BM; ++b) {
     if (b >= B) {
       for (int k = tid; k < K; k += kStackThreads) act[b * K + k] = (LT)0.f;
       continue;
     }
+    // one block reduction of the sums of d = x - x[0] and d^2: var = (sum d^2 - (sum d)^2 / K) / K;
+    // shifting by an element of the row keeps the subtraction well conditioned
     const float* xr = raw + b * K;
-    float s = 0.f;
-    for (int k = tid; k < K; k += kStackThreads) s += xr[k];
-    const float mean = block_sum256(s, red) / K;
-    float q = 0.f;
+    const float c0 = xr[0];
+    float s1 = 0.f, s2 = 0.f;
     for (int k = tid; k < K; k += kStackThreads) {
-      const float t = xr[k] - mean;
-      q += t * t;
+      const float d = xr[k] - c0;
+      s1 += d;
+      s2 += d * d;
     }
-    const float rstd = rsqrtf(block_sum256(q, red) / K + eps);
+    float2_t tot = block_sum2(float2_t{s1, s2}, red2, tid);
+    const float dm = tot.x / K;
+    const float mean = c0 + dm;
+    const float var = fmaxf(tot.y / K - dm * dm, 0.f);
+    const float rstd = rsqrtf(var + eps);
     for (int k = tid; k < K; k += kStackThreads)
       act[b * K + k] = (LT)((xr[k] - mean) * rstd * (float)g[k] + (float)beta[k]);
   }
 }
 
 // ------------------------------------------------------------------ attention work items
+// An item is (sequence b, head j, chunk c of kStackChunk cache rows). Lanes split a row into
+// 16-byte pieces (LPK lanes per row), a wave covers KPI rows per load, NW waves cover NW*KPI.
 template <typename AT, int D> struct AttnShape {
   static constexpr int EK = 16 / (int)sizeof(AT);
   static constexpr int LPK = D / EK;
   static constexpr int KPI = kWave / LPK;
-  static constexpr int NIT = (kStackChunk + 4 * KPI - 1) / (4 * KPI);
+  static constexpr int NIT = (kStackChunk + NW * KPI - 1) / (NW * KPI);
 };
 
 template <typename AT, int D> struct AttnRegs {
   u32x4 k[AttnShape<AT, D>::NIT], v[AttnShape<AT, D>::NIT];
+  static constexpr int kLoads = 2 * AttnShape<AT, D>::NIT;
 };
 
-// Issue the loads of the item's past rows (rows before the new one, written by earlier launches).
+__device__ __forceinline__ void item_coords(const StackArgs& a, int item, int& b, int& j, int& c) {
+  c = item % a.nchunk;
+  j = (item / a.nchunk) % a.nh;
+  b = item / (a.nchunk * a.nh);
+}
+
+// Issue exactly AttnRegs::kLoads loads: the item's past rows (before the new one, written by
+// earlier launches); rows outside the item or not yet filled load as zero (out of range).
 template <typename AT, int D>
 __device__ __forceinline__ void attn_prefetch(AttnRegs<AT, D>& A, const StackLayer& L, const StackArgs& a, int item,
                                               int tid) {
   typedef AttnShape<AT, D> S;
-  const int c = item % a.nchunk, j = (item / a.nchunk) % a.nh, b = item / (a.nchunk * a.nh);
-  const int len = L.d_len[b];
+  const int nitems = a.B * a.nh * a.nchunk;
+  int b = 0, j = 0, c = 0;
+  if (item < nitems) item_coords(a, item, b, j, c);
+  const int len = item < nitems ? L.d_len[b] : 0;
   const int wave = tid >> 6, lane = tid & 63;
+  const uint32_t bytes = (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(AT));
+  const rsrc_t rk = make_rsrc(L.k, bytes), rv = make_rsrc(L.v, bytes);
   const size_t head = (((size_t)b * a.nh + j) * a.cap) * D;
-  const AT* Kp = reinterpret_cast<const AT*>(L.k) + head;
-  const AT* Vp = reinterpret_cast<const AT*>(L.v) + head;
   const int e0 = (lane % S::LPK) * S::EK;
 #pragma unroll
   for (int it = 0; it < S::NIT; ++it) {
-    const int key = c * kStackChunk + (it * 4 + wave) * S::KPI + lane / S::LPK;
-    // rows not loaded stay zero: a zero weight times stale register bits could be NaN
-    const bool past = key < len && key < a.cap;
-    A.k[it] = past ? ld16(Kp + (size_t)key * D + e0) : u32x4{0, 0, 0, 0};
-    A.v[it] = past ? ld16(Vp + (size_t)key * D + e0) : u32x4{0, 0, 0, 0};
+    const int key = c * kStackChunk + (it * NW + wave) * S::KPI + lane / S::LPK;
+    const bool past = item < nitems && key < len && key < a.cap && key < (c + 1) * kStackChunk;
+    const uint32_t off = past ? (uint32_t)((head + (size_t)key * D + e0) * sizeof(AT)) : kOutOfRange;
+    A.k[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    A.v[it] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
   }
 }
 
+// One item: scores of q against the chunk's rows, wave-reduced max and sum, the exp-weighted V
+// sum; the partial (max, sum, acc[D]) goes to the workspace, and the workgroup that completes the
+// last chunk of a (sequence, head) merges the partials into ctx (log-sum-exp).
 template <typename AT, int D>
 __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& L, const StackArgs& a, int item,
-                                          bool prefetched, float* s_m, float* s_l, float* s_acc, int* s_flag, int tid) {
+                                          bool prefetched, float* s_m, float* s_l, float* s_acc, float* s_part,
+                                          int* s_flag, int tid) {
   typedef AttnShape<AT, D> S;
   constexpr int EK = S::EK, LPK = S::LPK, KPI = S::KPI, NIT = S::NIT;
   const float kNeg = -1e30f;
-  const int c = item % a.nchunk, j = (item / a.nchunk) % a.nh, b = item / (a.nchunk * a.nh);
+  int b, j, c;
+  item_coords(a, item, b, j, c);
   const int len = L.d_len[b];
   int nkeys = len + 1;
   if (nkeys > a.cap) nkeys = a.cap;
@@ -329,15 +416,15 @@ __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& 
   const int wave = tid >> 6, lane = tid & 63;
   const int H = a.nh * D;
   const size_t head = (((size_t)b * a.nh + j) * a.cap) * D;
-  const rsrc_t rk = make_rsrc(L.k, (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(AT)));
-  const rsrc_t rv = make_rsrc(L.v, (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(AT)));
+  const uint32_t bytes = (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(AT));
+  const rsrc_t rk = make_rsrc(L.k, bytes), rv = make_rsrc(L.v, bytes);
   const int e0 = (lane % LPK) * EK;
 
   if (!prefetched) attn_prefetch<AT, D>(A, L, a, item, tid);
   // the new row (position len) was written by the QKV phase of this launch: coherent loads
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int key = c * kStackChunk + (it * 4 + wave) * KPI + lane / LPK;
+    const int key = c * kStackChunk + (it * NW + wave) * KPI + lane / LPK;
     if (key == len && key < a.cap) {
       const uint32_t off = (uint32_t)((head + (size_t)key * D + e0) * sizeof(AT));
       A.k[it] = coh_load16(rk, off);
@@ -345,7 +432,7 @@ __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& 
     }
   }
   const rsrc_t rq = make_rsrc(a.q, (uint32_t)(a.B * H * 4));
-  const float qs = 1.4426950408889634f / sqrtf((float)D);
+  const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d): scores feed exp2
   float qv[EK];
 #pragma unroll
   for (int e = 0; e < EK; ++e) qv[e] = as_f32(coh_load4(rq, (uint32_t)((b * H + j * D + e0 + e) * 4))) * qs;
@@ -355,8 +442,8 @@ __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& 
   float m = kNeg;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int key = c * kStackChunk + (it * 4 + wave) * KPI + lane / LPK;
-    valid[it] = key < nkeys && key < c * kStackChunk + kStackChunk;
+    const int key = c * kStackChunk + (it * NW + wave) * KPI + lane / LPK;
+    valid[it] = key < nkeys && key < (c + 1) * kStackChunk;
     float p = 0.f;
     if constexpr (sizeof(AT) == 4) {
       p = qv[0] * as_f32(A.k[it].x) + qv[1] * as_f32(A.k[it].y) + qv[2] * as_f32(A.k[it].z) + qv[3] * as_f32(A.k[it].w);
@@ -401,7 +488,7 @@ __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& 
 #pragma unroll
     for (int e = 0; e < EK; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
   }
-  __syncthreads();  // LDS scratch of a previous item is free
+  lds_barrier();  // LDS scratch of a previous item is free
   if (lane < LPK) {
 #pragma unroll
     for (int e = 0; e < EK; ++e) s_acc[wave * D + e0 + e] = acc[e];
@@ -410,40 +497,48 @@ __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& 
       s_l[wave] = l;
     }
   }
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  float f[4];
+  lds_barrier();
+  float M = kNeg;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) f[w] = s_l[w] > 0.f ? exp2f(s_m[w] - M) : 0.f;
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w]);
+  float f[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) f[w] = s_l[w] > 0.f ? exp2f(s_m[w] - M) : 0.f;
   const size_t pbase = ((size_t)b * a.nh + j) * a.nchunk;
   const rsrc_t rp = make_rsrc(a.part, (uint32_t)((size_t)a.B * a.nh * a.nchunk * (D + 2) * 4));
-  if (tid < D)
-    coh_store4(rp, (uint32_t)(((pbase + c) * (D + 2) + 2 + tid) * 4),
-               __builtin_bit_cast(uint32_t, f[0] * s_acc[tid] + f[1] * s_acc[D + tid] + f[2] * s_acc[2 * D + tid] +
-                                                f[3] * s_acc[3 * D + tid]));
-  if (tid == 0) {
-    coh_store4(rp, (uint32_t)(((pbase + c) * (D + 2)) * 4), __builtin_bit_cast(uint32_t, M));
-    coh_store4(rp, (uint32_t)(((pbase + c) * (D + 2) + 1) * 4),
-               __builtin_bit_cast(uint32_t, f[0] * s_l[0] + f[1] * s_l[1] + f[2] * s_l[2] + f[3] * s_l[3]));
+  if (tid < D) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += f[w] * s_acc[w * D + tid];
+    coh_store4(rp, (uint32_t)(((pbase + c) * (D + 2) + 2 + tid) * 4), __builtin_bit_cast(uint32_t, v));
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if (tid == 0) {
+    float Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Ls += f[w] * s_l[w];
+    coh_store4(rp, (uint32_t)(((pbase + c) * (D + 2)) * 4), __builtin_bit_cast(uint32_t, M));
+    coh_store4(rp, (uint32_t)(((pbase + c) * (D + 2) + 1) * 4), __builtin_bit_cast(uint32_t, Ls));
+  }
+  wait_vm_at_most<0>();
+  lds_barrier();
   uint32_t* cnt = a.sync + kSyncAttn + b * a.nh + j;
   if (tid == 0)
     *s_flag = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nvalid - 1);
-  __syncthreads();
+  lds_barrier();
   if (!*s_flag) return;
-  // last chunk of this (sequence, head): merge the partials into ctx
+  // last chunk of this (sequence, head): all partials in one parallel load, then the merge
+  const int nw = nvalid * (D + 2);
+  for (int i = tid; i < nw; i += kStackThreads) s_part[i] = as_f32(coh_load4(rp, (uint32_t)((pbase * (D + 2) + i) * 4)));
+  lds_barrier();
   if (tid < D) {
     float MM = kNeg;
-    for (int cc = 0; cc < nvalid; ++cc) MM = fmaxf(MM, as_f32(coh_load4(rp, (uint32_t)(((pbase + cc) * (D + 2)) * 4))));
+    for (int cc = 0; cc < nvalid; ++cc) MM = fmaxf(MM, s_part[cc * (D + 2)]);
     float Lsum = 0.f, Acc = 0.f;
     for (int cc = 0; cc < nvalid; ++cc) {
-      const uint32_t o = (uint32_t)(((pbase + cc) * (D + 2)) * 4);
-      const float lc = as_f32(coh_load4(rp, o + 4));
-      const float w = lc > 0.f ? exp2f(as_f32(coh_load4(rp, o)) - MM) : 0.f;
-      Lsum += w * lc;
-      Acc += w * as_f32(coh_load4(rp, o + (2 + tid) * 4));
+      const float* pc = s_part + cc * (D + 2);
+      const float w = pc[1] > 0.f ? exp2f(pc[0] - MM) : 0.f;
+      Lsum += w * pc[1];
+      Acc += w * pc[2 + tid];
     }
     const rsrc_t rc = make_rsrc(a.ctx, (uint32_t)(a.B * H * sizeof(AT)));
     coh_st_act<AT>(rc, (uint32_t)(b * H + j * D + tid), Acc / Lsum);
@@ -455,11 +550,13 @@ __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& 
 
 // ------------------------------------------------------------------ the persistent kernel
 template <typename WT, typename AT, int BM, int D>
-__global__ __launch_bounds__(kStackThreads, 2) void stack_decode_kernel(const StackArgs a) {
+__global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const StackArgs a) {
   typedef typename WTraits<WT>::LT LT;
+  constexpr int kWLoads = WRegs<WT>::kLoads;
+  constexpr int kALoads = AttnRegs<AT, D>::kLoads;
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ float red[4];
-  __shared__ float s_m[4], s_l[4];
+  __shared__ float2_t red2[NW];
+  __shared__ float s_m[NW], s_l[NW];
   __shared__ int s_flag;
   const int H = a.H, F = a.F, B = a.B, G = a.G, g = blockIdx.x;
   const int KMAX = H > F ? H : F;
@@ -469,7 +566,8 @@ __global__ __launch_bounds__(kStackThreads, 2) void stack_decode_kernel(const St
   LT* act = reinterpret_cast<LT*>(smem);
   float* raw = reinterpret_cast<float*>(smem + (size_t)BM * H * sizeof(LT));  // LayerNorm input rows
   float* slots = reinterpret_cast<float*>(smem + act_bytes);
-  float* s_acc = slots;  // attention reuses the slot area (4 * D floats)
+  float* s_acc = slots;                                  // attention: NW x D floats
+  float* s_part = reinterpret_cast<float*>(smem);        // attention merge: nchunk x (D + 2) floats
   // Thread indices are re-derived through an opaque copy at every phase: otherwise the compiler
   // hoists every per-thread address of every phase out of the layer loop and keeps them all live.
   int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -491,18 +589,28 @@ __global__ __launch_bounds__(kStackThreads, 2) void stack_decode_kernel(const St
 
   WRegs<WT> R;
   AttnRegs<AT, D> A;
-  uint32_t nbar = 0;
+  uint32_t epoch = 0;
   auto slot_clear = [&](int nr) {
-    for (int i = tid; i < nr * 4 * BM; i += kStackThreads) slots[i] = 0.f;
+    for (int i = tid; i < nr * NW * BM; i += kStackThreads) slots[i] = 0.f;
   };
   auto row_sum = [&](int rl, int b) {
-    const float* p = slots + rl * 4 * BM + b;
-    return p[0] + p[BM] + p[2 * BM] + p[3 * BM];
+    const float* p = slots + rl * NW * BM + b;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += p[w * BM];
+    return s;
+  };
+  // after a phase's stores and the next prefetch: stores done, then arrive and wait
+  auto barrier = [&](auto wait_stores) -> bool {
+    wait_stores();
+    ++epoch;
+    grid_arrive(a.sync, epoch, g, G, tid);
+    return grid_wait(a.sync, epoch, a.timeout_ticks, &s_flag, tid);
   };
 
   {
     const StackLayer& L0 = a.layers[0];
-    if (nq > 0) prefetch_tile<WT>(R, (const WT*)L0.w_qkv, (const half_t*)L0.s_qkv, 3 * H, H, a.group, q0, nq, wave, lane);
+    prefetch_tile<WT>(R, (const WT*)L0.w_qkv, (const half_t*)L0.s_qkv, 3 * H, H, a.group, q0, nq, wave, lane);
   }
 
   for (int l = 0; l < a.n_layers; ++l) {
@@ -512,104 +620,133 @@ __global__ __launch_bounds__(kStackThreads, 2) void stack_decode_kernel(const St
 
     // ---- region 1: LN1 + QKV + bias; q -> workspace, k/v -> cache row d_len[b]
     fresh();
+    // epilogue inputs first: they travel with the staging loads instead of after the GEMV
+    float pb = 0.f, pr = 0.f;
+    int plen = 0;
+    if (tid < nq * B) {
+      const int rl = tid / B, b = tid - rl * B;
+      pb = ldp<AT>(L.b_qkv, q0 + rl);
+      plen = L.d_len[b];
+    }
     slot_clear(nq);
-    stage_ln<AT, LT, AT, BM>(xin, B, H, (const AT*)L.ln1_g, (const AT*)L.ln1_b, a.eps, act, raw, red, tid);
-    __syncthreads();
+    stage_ln<AT, LT, AT, BM>(xin, B, H, (const AT*)L.ln1_g, (const AT*)L.ln1_b, a.eps, act, raw, red2, tid);
+    lds_barrier();
     if (nq > 0) gemv_tile<WT, BM>(R, (const WT*)L.w_qkv, (const half_t*)L.s_qkv, 3 * H, H, a.group, q0, nq, act, slots, wave, lane);
-    __syncthreads();
+    lds_barrier();
     {
       const rsrc_t rqo = make_rsrc(a.q, (uint32_t)(B * H * 4));
       const uint32_t cache_bytes = (uint32_t)((size_t)B * a.nh * a.cap * D * sizeof(AT));
       const rsrc_t rk = make_rsrc(L.k, cache_bytes), rv = make_rsrc(L.v, cache_bytes);
       for (int t = tid; t < nq * B; t += kStackThreads) {
         const int rl = t / B, b = t - rl * B, n = q0 + rl;
-        const float z = row_sum(rl, b) + ldp<AT>(L.b_qkv, n);
+        const float z = row_sum(rl, b) + (t == tid ? pb : ldp<AT>(L.b_qkv, n));
         if (n < H) {
           coh_store4(rqo, (uint32_t)((b * H + n) * 4), __builtin_bit_cast(uint32_t, z));
         } else {
           const int m = n < 2 * H ? n - H : n - 2 * H, j = m / D, e = m - j * D;
-          const int pos = L.d_len[b];
+          const int pos = t == tid ? plen : L.d_len[b];
           if (pos >= 0 && pos < a.cap) coh_st_act<AT>(n < 2 * H ? rk : rv, (uint32_t)((((size_t)b * a.nh + j) * a.cap + pos) * D + e), z);
         }
       }
     }
-    grid_arrive(a.sync);
-    if (g < nitems) attn_prefetch<AT, D>(A, L, a, g, tid);
-    if (!grid_wait(a.sync, (++nbar) * (uint32_t)G, a.timeout_ticks, &s_flag)) return;
+    asm volatile("" ::: "memory");
+    attn_prefetch<AT, D>(A, L, a, g, tid);
+    if (!barrier([] { wait_vm_at_most<kALoads>(); })) return;
 
     // ---- region 2: attention over the cache, chunk partials merged by the last chunk
     fresh();
     for (int item = g; item < nitems; item += G)
-      attn_item<AT, D>(A, L, a, item, item == g, s_m, s_l, s_acc, &s_flag, tid);
-    grid_arrive(a.sync);
-    if (no > 0) prefetch_tile<WT>(R, (const WT*)L.w_o, (const half_t*)L.s_o, H, H, a.group, o0, no, wave, lane);
-    if (!grid_wait(a.sync, (++nbar) * (uint32_t)G, a.timeout_ticks, &s_flag)) return;
+      attn_item<AT, D>(A, L, a, item, item == g, s_m, s_l, s_acc, s_part, &s_flag, tid);
+    asm volatile("" ::: "memory");
+    prefetch_tile<WT>(R, (const WT*)L.w_o, (const half_t*)L.s_o, H, H, a.group, o0, no, wave, lane);
+    if (!barrier([] { wait_vm_at_most<kWLoads>(); })) return;
 
     // ---- output projection + bias + residual: x2 = x + Wo ctx + bo
     fresh();
+    {
+      const rsrc_t rx = make_rsrc(xin, (uint32_t)(B * H * sizeof(AT)));
+      if (tid < no * B) {
+        const int rl = tid / B, b = tid - rl * B;
+        pb = ldp<AT>(L.b_o, o0 + rl);
+        pr = coh_ld_act<AT>(rx, (uint32_t)(b * H + o0 + rl));
+      }
+    }
     slot_clear(no);
     stage_plain<AT, LT, BM>(a.ctx, B, H, act, tid);
-    __syncthreads();
+    lds_barrier();
     if (no > 0) gemv_tile<WT, BM>(R, (const WT*)L.w_o, (const half_t*)L.s_o, H, H, a.group, o0, no, act, slots, wave, lane);
-    __syncthreads();
+    lds_barrier();
     {
       const rsrc_t rx = make_rsrc(xin, (uint32_t)(B * H * sizeof(AT)));
       const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 4));
       for (int t = tid; t < no * B; t += kStackThreads) {
         const int rl = t / B, b = t - rl * B, n = o0 + rl;
-        const float z = row_sum(rl, b) + ldp<AT>(L.b_o, n);
-        coh_store4(rx2, (uint32_t)((b * H + n) * 4), __builtin_bit_cast(uint32_t, coh_ld_act<AT>(rx, (uint32_t)(b * H + n)) + z));
+        const float z = row_sum(rl, b) + (t == tid ? pb : ldp<AT>(L.b_o, n));
+        const float xr = t == tid ? pr : coh_ld_act<AT>(rx, (uint32_t)(b * H + n));
+        coh_store4(rx2, (uint32_t)((b * H + n) * 4), __builtin_bit_cast(uint32_t, xr + z));
       }
     }
-    grid_arrive(a.sync);
-    if (nf > 0) prefetch_tile<WT>(R, (const WT*)L.w_ff1, (const half_t*)L.s_ff1, F, H, a.group, f0, nf, wave, lane);
-    if (!grid_wait(a.sync, (++nbar) * (uint32_t)G, a.timeout_ticks, &s_flag)) return;
+    asm volatile("" ::: "memory");
+    prefetch_tile<WT>(R, (const WT*)L.w_ff1, (const half_t*)L.s_ff1, F, H, a.group, f0, nf, wave, lane);
+    if (!barrier([] { wait_vm_at_most<kWLoads>(); })) return;
 
     // ---- region 3: LN2 + FF1 + bias + GeLU
     fresh();
+    if (tid < nf * B) pb = ldp<AT>(L.b_ff1, f0 + tid / B);
     slot_clear(nf);
-    stage_ln<float, LT, AT, BM>(a.x2, B, H, (const AT*)L.ln2_g, (const AT*)L.ln2_b, a.eps, act, raw, red, tid);
-    __syncthreads();
+    stage_ln<float, LT, AT, BM>(a.x2, B, H, (const AT*)L.ln2_g, (const AT*)L.ln2_b, a.eps, act, raw, red2, tid);
+    lds_barrier();
     if (nf > 0) gemv_tile<WT, BM>(R, (const WT*)L.w_ff1, (const half_t*)L.s_ff1, F, H, a.group, f0, nf, act, slots, wave, lane);
-    __syncthreads();
+    lds_barrier();
     {
       const rsrc_t rf = make_rsrc(a.f, (uint32_t)(B * F * sizeof(AT)));
       for (int t = tid; t < nf * B; t += kStackThreads) {
         const int rl = t / B, b = t - rl * B, n = f0 + rl;
-        const float z = row_sum(rl, b) + ldp<AT>(L.b_ff1, n);
+        const float z = row_sum(rl, b) + (t == tid ? pb : ldp<AT>(L.b_ff1, n));
         coh_st_act<AT>(rf, (uint32_t)(b * F + n), gelu(z, a.gelu_tanh != 0));
       }
     }
-    grid_arrive(a.sync);
-    if (ny > 0) prefetch_tile<WT>(R, (const WT*)L.w_ff2, (const half_t*)L.s_ff2, H, F, a.group, y0, ny, wave, lane);
-    if (!grid_wait(a.sync, (++nbar) * (uint32_t)G, a.timeout_ticks, &s_flag)) return;
+    asm volatile("" ::: "memory");
+    prefetch_tile<WT>(R, (const WT*)L.w_ff2, (const half_t*)L.s_ff2, H, F, a.group, y0, ny, wave, lane);
+    if (!barrier([] { wait_vm_at_most<kWLoads>(); })) return;
 
     // ---- region 4: FF2 + bias + residual: y = x2 + W2 f + b2
     fresh();
+    {
+      const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 4));
+      if (tid < ny * B) {
+        const int rl = tid / B, b = tid - rl * B;
+        pb = ldp<AT>(L.b_ff2, y0 + rl);
+        pr = as_f32(coh_load4(rx2, (uint32_t)((b * H + y0 + rl) * 4)));
+      }
+    }
     slot_clear(ny);
     stage_plain<AT, LT, BM>(a.f, B, F, act, tid);
-    __syncthreads();
+    lds_barrier();
     if (ny > 0) gemv_tile<WT, BM>(R, (const WT*)L.w_ff2, (const half_t*)L.s_ff2, H, F, a.group, y0, ny, act, slots, wave, lane);
-    __syncthreads();
+    lds_barrier();
     {
       const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 4));
       const rsrc_t ry = make_rsrc(yout, (uint32_t)(B * H * sizeof(AT)));
       for (int t = tid; t < ny * B; t += kStackThreads) {
         const int rl = t / B, b = t - rl * B, n = y0 + rl;
-        const float z = row_sum(rl, b) + ldp<AT>(L.b_ff2, n);
-        coh_st_act<AT>(ry, (uint32_t)(b * H + n), as_f32(coh_load4(rx2, (uint32_t)((b * H + n) * 4))) + z);
+        const float z = row_sum(rl, b) + (t == tid ? pb : ldp<AT>(L.b_ff2, n));
+        const float xr = t == tid ? pr : as_f32(coh_load4(rx2, (uint32_t)((b * H + n) * 4)));
+        coh_st_act<AT>(ry, (uint32_t)(b * H + n), xr + z);
       }
     }
-    grid_arrive(a.sync);
-    if (l + 1 < a.n_layers && nq > 0) {
+    asm volatile("" ::: "memory");
+    if (l + 1 < a.n_layers) {
       const StackLayer& Ln = a.layers[l + 1];
       prefetch_tile<WT>(R, (const WT*)Ln.w_qkv, (const half_t*)Ln.s_qkv, 3 * H, H, a.group, q0, nq, wave, lane);
+      if (!barrier([] { wait_vm_at_most<kWLoads>(); })) return;
+    } else {
+      if (!barrier([] { wait_vm_at_most<0>(); })) return;
     }
-    if (!grid_wait(a.sync, (++nbar) * (uint32_t)G, a.timeout_ticks, &s_flag)) return;
   }
 
   // every layer has attended: advance the cache lengths, then the last workgroup out resets the
-  // barrier counter for the next launch
+  // barrier state for the next launch
   if (g == 0 && tid < B)
     for (int l = 0; l < a.n_layers; ++l) {
       int32_t* dl = a.layers[l].d_len;
@@ -618,7 +755,10 @@ __global__ __launch_bounds__(kStackThreads, 2) void stack_decode_kernel(const St
   if (tid == 0) {
     const uint32_t out = __hip_atomic_fetch_add(a.sync + kSyncExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (out == (uint32_t)G - 1) {
-      __hip_atomic_store(a.sync + kSyncArrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < kSyncGroups; ++i)
+        __hip_atomic_store(a.sync + kSyncSub + i * kSyncLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.sync + kSyncTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.sync + kSyncFlag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.sync + kSyncExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -638,10 +778,13 @@ size_t stack_lds_bytes(Dt wdt, int B, int H, int F, int rows_per_wg) {
   const size_t kmax = (size_t)(H > F ? H : F);
   size_t act = BM * kmax * lt;
   if ((size_t)BM * H * (lt + 4) > act) act = (size_t)BM * H * (lt + 4);  // LayerNorm rows in fp32 too
-  size_t slots = (size_t)rows_per_wg * 4 * BM * 4;
-  if (slots < 4 * 128 * 4) slots = 4 * 128 * 4;  // attention scratch: 4 waves x head_dim floats
+  size_t slots = (size_t)rows_per_wg * kStackWaves * BM * 4;
+  if (slots < (size_t)kStackWaves * 128 * 4) slots = (size_t)kStackWaves * 128 * 4;  // attention scratch
   return act + slots;
 }
+
+// The attention merge stages nchunk x (head_dim + 2) floats in the activation area.
+size_t stack_merge_bytes(int nchunk, int head_dim) { return (size_t)nchunk * (head_dim + 2) * 4; }
 
 template <typename WT, typename AT, int BM, int D>
 static const void* kernel_ptr() {
@@ -676,7 +819,7 @@ hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups) {
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   int cus = 0;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  if (per_cu > 2) per_cu = 2;
+  if (per_cu > 1) per_cu = 1;
   *groups = per_cu * cus;
   return hipSuccess;
 }

@@ -101,9 +101,10 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
   hipError_t e = hipGetDevice(&S->device);
   int cus = 0;
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, S->device);
-  int G = 2 * cus;
+  int G = cus;  // one workgroup of kStackThreads per CU
   for (int iter = 0; e == hipSuccess && iter < 3; ++iter) {
-    const size_t lds = ds::stack_lds_bytes(wdt, max_batch, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, G));
+    size_t lds = ds::stack_lds_bytes(wdt, max_batch, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, G));
+    if (ds::stack_merge_bytes(S->nchunk, d.head_dim) > lds) lds = ds::stack_merge_bytes(S->nchunk, d.head_dim);
     int fit = 0;
     e = ds::stack_max_groups(wdt, adt, max_batch, lds, &fit);
     if (e == hipSuccess) G = G < fit ? G : fit;
@@ -196,7 +197,8 @@ int ds_stack_forward_decode(ds_stack_t* S, const void* x, void* y, int32_t batch
   a.nchunk = S->nchunk;
   a.timeout_ticks = S->timeout_ticks;
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
-  const size_t lds = ds::stack_lds_bytes(wdt, batch, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->G));
+  size_t lds = ds::stack_lds_bytes(wdt, batch, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->G));
+  if (ds::stack_merge_bytes(S->nchunk, d.head_dim) > lds) lds = ds::stack_merge_bytes(S->nchunk, d.head_dim);
   if (hipError_t e = ds::launch_stack_decode(wdt, adt, a, lds, reinterpret_cast<hipStream_t>(stream)))
     return hip_err(e, "persistent decode launch");
   for (int l = 0; l < S->n_layers; ++l)
@@ -207,16 +209,18 @@ int ds_stack_forward_decode(ds_stack_t* S, const void* x, void* y, int32_t batch
 
 int ds_stack_check(ds_stack_t* S) {
   if (!S) return ds::set_error(DS_ERR_NULL, "stack is NULL");
-  uint32_t words[ds::kSyncAttn] = {0, 0, 0, 0};
+  std::vector<uint32_t> words(S->sync_words);
   hipError_t e = hipDeviceSynchronize();
-  if (e == hipSuccess) e = hipMemcpy(words, S->d_sync, sizeof words, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(words.data(), S->d_sync, S->sync_words * 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_err(e, "stack check");
-  if (words[ds::kSyncError] != 0 || words[ds::kSyncArrive] != 0 || words[ds::kSyncExit] != 0) {
+  size_t dirty = 0;
+  for (uint32_t w : words) dirty += w != 0u;
+  if (dirty) {
+    const uint32_t err = words[ds::kSyncError];
     (void)hipMemset(S->d_sync, 0, S->sync_words * 4);
     (void)hipDeviceSynchronize();
-    return ds::set_error(DS_ERR_HIP, "persistent decode: a grid barrier timed out (error %u, arrivals %u, exits %u); "
-                         "state reset, outputs of the failed step are invalid",
-                         words[ds::kSyncError], words[ds::kSyncArrive], words[ds::kSyncExit]);
+    return ds::set_error(DS_ERR_HIP, "persistent decode: a grid barrier timed out (error flag %u, %zu barrier words "
+                         "left set); state reset, outputs of the failed step are invalid", err, dirty);
   }
   return DS_OK;
 }
