@@ -18,7 +18,7 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def gpu_layer_and_oracle_weights(wl: syn.Workload, layer: int, device="cuda", check_quant=True):
+def gpu_layer_and_oracle_weights(wl: syn.Workload, layer: int, device="cuda", check_quant=True, **cfg_kw):
     """Builds a library Layer for one layer of the workload and the oracle's float64 weights
     (same values). For int8 the GPU quantizer makes the codes, and the oracle quantizer makes its
     own from the same float32 draws; the two are compared bit for bit."""
@@ -29,7 +29,7 @@ def gpu_layer_and_oracle_weights(wl: syn.Workload, layer: int, device="cuda", ch
     act = TORCH[wl.act_dtype]
     cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
                          dtype={"f32": "fp32", "f16": "fp16", "i8": "int8"}[wl.weight_dtype],
-                         quantization_setting=(wl.group, False) if wl.weight_dtype == "i8" else None)
+                         quantization_setting=(wl.group, False) if wl.weight_dtype == "i8" else None, **cfg_kw)
     gw, ow = {}, {}
     for name, t in w32.items():
         if name.startswith("w_"):

@@ -1,0 +1,116 @@
+"""GPU parity of the MFMA (many-row) path against the oracle: fp16 layers with at least 16 rows
+per step run LayerNorm rows, the fused-epilogue GEMMs and flash attention on matrix cores.
+
+Shapes span several GEMM tiles (128 rows by 160/256/320 columns) with ragged row and column tails,
+several 64-key attention tiles, past rows that are not a multiple of 64, head_dim 64 and 128, and
+both mask settings. The causal mask is also checked by construction: changing prompt row t' leaves
+every output row t < t' bit-identical.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from tests._common import TOL, filled_caches, gpu_layer_and_oracle_weights, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(**kw):
+    base = dict(hidden=256, heads=2, head_dim=128, ffn=768, weight_dtype="f16", act_dtype="f16", batch=2, past=0)
+    base.update(kw)
+    return dataclasses.replace(syn.WORKLOADS["c1"], **base)
+
+
+CASES = {
+    # rows 200: two row tiles, the second 72 rows; qkv N=768, ff1 N=768, ff2 K=768
+    "d128-b2-s100": (_wl(cfg_id=201), 100, 0),
+    # past rows 33 before 70 new ones: keys span two tiles with a ragged end; N=960 (3*320) and 640
+    "d64-b3-s70-p33": (_wl(hidden=320, heads=5, head_dim=64, ffn=640, batch=3, cfg_id=202), 70, 33),
+    # K=2048 for FF2 (64 k-steps), 512 rows, heads of 128
+    "d128-b2-s256": (_wl(hidden=512, heads=4, ffn=2048, cfg_id=203), 256, 0),
+    # exactly 16 rows: the smallest MFMA-path step
+    "d128-b1-s16-p5": (_wl(batch=1, cfg_id=204), 16, 5),
+}
+
+
+def _prefill_case(wl, S, P0, **cfg_kw):
+    wl = dataclasses.replace(wl, past=P0, seq=S)
+    cap = ((P0 + S + 1 + 63) // 64) * 64
+    gl, ow = gpu_layer_and_oracle_weights(wl, 0, **cfg_kw)
+    kv, ok, ov, lens = filled_caches(wl, 0, gl, past=P0, cap=cap)
+    x = syn.normal((wl.batch, S, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 7, "cuda").to(torch.float16)
+    return wl, gl, ow, kv, ok, ov, lens, x
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prefill_mfma_matches_oracle(name):
+    wl, S, P0 = CASES[name]
+    wl, gl, ow, kv, ok, ov, lens, x = _prefill_case(wl, S, P0)
+    print(f"case {name}: B={wl.batch} S={S} P0={P0} H={wl.hidden} F={wl.ffn} d={wl.head_dim}", flush=True)
+    y = gl.prefill(kv, x)
+    torch.cuda.synchronize()
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
+    yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy())
+    err = rel_l2(y.double().cpu().numpy(), yo)
+    assert err <= TOL["f16"], err
+    # the same metric on the layer's update y - x, a stricter view of the computed part
+    xd = x.double().cpu().numpy()
+    assert rel_l2(y.double().cpu().numpy() - xd, yo - xd) <= TOL["f16"]
+    n = P0 + S
+    assert rel_l2(kv.k.double().cpu().numpy()[:, :, :n], ok[:, :, :n]) <= TOL["f16"]
+    assert rel_l2(kv.v.double().cpu().numpy()[:, :, :n], ov[:, :, :n]) <= TOL["f16"]
+    assert kv.lengths() == [n] * wl.batch
+    assert torch.isfinite(y).all()
+
+
+def test_prefill_mfma_without_mask_matches_oracle():
+    wl, S, P0 = _wl(cfg_id=205, batch=2), 40, 10
+    wl, gl, ow, kv, ok, ov, lens, x = _prefill_case(wl, S, P0, triangular_masking=False)
+    y = gl.prefill(kv, x)
+    torch.cuda.synchronize()
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn, triangular_masking=False)
+    yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy())
+    assert rel_l2(y.double().cpu().numpy(), yo) <= TOL["f16"]
+
+
+def test_prefill_mfma_is_causal_bitwise():
+    wl, S, P0 = _wl(cfg_id=206, batch=1), 96, 0
+    wl, gl, ow, kv, ok, ov, lens, x = _prefill_case(wl, S, P0)
+    y1 = gl.prefill(kv, x).clone()
+    tp = 70
+    x2 = x.clone()
+    x2[:, tp] = -x2[:, tp] + 0.5
+    kv2, _, _, _ = filled_caches(wl, 0, gl, past=P0, cap=kv.capacity)
+    y2 = gl.prefill(kv2, x2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1[:, :tp], y2[:, :tp])
+    assert not torch.equal(y1[:, tp:], y2[:, tp:])
+
+
+def test_prefill_then_decode_matches_longer_prefill():
+    """prefill(S) then decode of row S equals the last row of prefill(S+1) (GPU both ways)."""
+    wl, S, P0 = _wl(cfg_id=207, batch=2), 40, 0
+    wl, gl, ow, kv, ok, ov, lens, x = _prefill_case(wl, S + 1, P0)
+    y_full = gl.prefill(kv, x)
+    kv2, _, _, _ = filled_caches(wl, 0, gl, past=P0, cap=kv.capacity)
+    gl.prefill(kv2, x[:, :S].contiguous())
+    y_last = gl.decode(kv2, x[:, S].contiguous())
+    torch.cuda.synchronize()
+    assert rel_l2(y_last.double().cpu().numpy(), y_full[:, S].double().cpu().numpy()) <= TOL["f16"]
+
+
+def test_large_batch_decode_uses_mfma_path_and_matches_oracle():
+    """A decode step of 24 sequences (24 rows) takes the MFMA path; check it against the oracle."""
+    wl = _wl(cfg_id=208, batch=24, hidden=320, heads=5, head_dim=64, ffn=640, past=77)
+    gl, ow = gpu_layer_and_oracle_weights(wl, 0)
+    kv, ok, ov, lens = filled_caches(wl, 0, gl, past=77, cap=128)
+    x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").to(torch.float16)
+    y = gl.decode(kv, x)
+    torch.cuda.synchronize()
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
+    yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy()[:, None, :])[:, 0]
+    assert rel_l2(y.double().cpu().numpy(), yo) <= TOL["f16"]

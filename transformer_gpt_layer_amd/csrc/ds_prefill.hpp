@@ -1,0 +1,55 @@
+// ds_prefill.hpp -- internal interface of the MFMA (many-row) path: LayerNorm rows, the fused-epilogue
+// GEMM and attention over the cache for many new rows per sequence.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ds_device.hpp"
+
+namespace ds {
+
+enum GemmEpi { EPI_QKV = 0, EPI_OPROJ = 1, EPI_FF1 = 2, EPI_FF2 = 3 };
+
+// C[M][N] = A[M][K] W[N][K]^T + bias, then by epilogue:
+//   EPI_QKV   columns [0,H) -> out fp16 [M][H] (q); [H,2H) and [2H,3H) -> k_cache / v_cache rows
+//             d_len[b] + t of sequence b = m / tokens, t = m % tokens, head-major [B][heads][cap][D]
+//   EPI_OPROJ out fp32 [M][N] = resid fp16 [M][N] + C
+//   EPI_FF1   out fp16 [M][N] = GeLU(C)
+//   EPI_FF2   out fp16 [M][N] = resid fp32 [M][N] + C
+// A, W: fp16, K a multiple of 32, M*K*2 and N*K*2 below 2^31 bytes.
+struct GemmArgs {
+  const half_t* a;
+  const half_t* w;
+  const half_t* bias;
+  void* out;
+  const void* resid;
+  half_t* k_cache;
+  half_t* v_cache;
+  const int32_t* d_len;
+  int M, N, K;
+  int tokens, heads, head_dim, cap, hidden;
+  int gelu_tanh;
+  int tiles_m, tiles_n;  // set by the launcher
+};
+
+// Attention of `tokens` new rows per sequence over keys 0..d_len[b]+tokens-1 of the cache (the new
+// rows already appended at d_len[b]..), causal or not; d_len is the length before this step.
+struct AttnPrefillArgs {
+  const half_t* q;        // [batch*tokens][H]
+  const half_t* k_cache;  // [batch][heads][cap][head_dim]
+  const half_t* v_cache;
+  const int32_t* d_len;
+  half_t* ctx;            // [batch*tokens][H]
+  int batch, tokens, heads, head_dim, cap, causal;
+  float scale;            // 1/sqrt(head_dim)
+};
+
+// BN (columns per workgroup tile) that best fills `cus` compute units for an M x N output.
+int gemm_pick_bn(int M, int N, int cus);
+hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int bn, int cus, hipStream_t st);
+// LayerNorm of `rows` rows of H elements (fp32 or fp16 input) into fp16.
+hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const half_t* b, half_t* out, int rows, int H,
+                          float eps, hipStream_t st);
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t st);
+
+}  // namespace ds

@@ -1,0 +1,484 @@
+// kernels_prefill.hip -- the many-row path of one layer (prefill, or decode with a large batch) on
+// gfx950 matrix cores, for fp16 weights and activations.
+//
+// The layer is the one of the page "DeepSpeed Inference 内核优化深度解析" (blog.gitcode.com), section
+// 三 3.2, with its four fusion regions. With many rows per weight the projections are dense GEMMs
+// (the QKV, output, FF1 and FF2 GeMMs of section 三 3.2), so they run on MFMA; the regions' element-
+// wise work rides in the GEMM epilogues:
+//   ln_rows       LayerNorm of each row into an fp16 copy (the A operand of the next GEMM)
+//   gemm QKV      h Wqkv^T + b; q to the workspace, k and v straight into the head-major cache
+//                 rows d_len[b] + t (the head "transform" of region 2 done by addressing)
+//   attn_prefill  causal attention over the cache, flash style (online softmax), on MFMA
+//   gemm OPROJ    x + ctx Wo^T + bo -> x2 (fp32)                              (region 3 start)
+//   gemm FF1      GeLU(h2 W1^T + b1) -> f (fp16)                              (region 3)
+//   gemm FF2      x2 + f W2^T + b2 -> y                                       (region 4)
+// The attention mask follows the triangular_masking option of the inference-config table on the
+// page "DeepSpeed MoE 大规模稀疏模型推理实战指南" (blog.gitcode.com): with it, the row at absolute
+// position p sees the keys 0..p; without it, every key of its sequence.
+//
+// GEMM design. C[M][N] = A[M][K] W[N][K]^T with both operands K-contiguous, which is the operand
+// order v_mfma_f32_16x16x32_f16 wants (lane l holds row l%16, k 8(l/16)..+7 of either operand).
+// A workgroup of four waves owns a 128 x BN tile, each wave a 64 x BN/2 quarter. K advances 32 at a
+// time through a four-stage LDS ring filled by buffer loads that write LDS directly (no VGPR
+// round trip); one barrier per k-step both publishes a stage and frees the oldest. LDS rows are
+// 64 bytes with the 16-byte chunk index XOR-ed by (row/2)%4, so the MFMA operand reads (16 rows,
+// one chunk) hit distinct banks. Tiles are numbered so that the workgroups the dispatcher sends to
+// one XCD (every 8th) hold consecutive tiles, which share their weight columns in that XCD's L2.
+#include "ds_device.hpp"
+#include "ds_prefill.hpp"
+
+namespace ds {
+namespace prefill {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;    // raw buffer, 32-bit dword format
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every valid range: loads give 0
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void* lds_ptr(const void* p) {
+  return reinterpret_cast<lds_void*>(reinterpret_cast<uintptr_t>(p));
+}
+
+// s_waitcnt vmcnt(n) for 0 <= n <= 15 (expcnt and lgkmcnt left unconstrained); larger n waits
+// for 15, which is stricter and therefore still correct.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break;
+    case 11: wait_vm<11>(); break;
+    case 12: wait_vm<12>(); break;
+    case 13: wait_vm<13>(); break;
+    case 14: wait_vm<14>(); break;
+    default: wait_vm<15>(); break;
+  }
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for its outstanding global
+// loads (a __syncthreads() would also drain the prefetched stages of the GEMM ring).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// ------------------------------------------------------------------ LayerNorm rows
+// One wave per row: mean, then the biased variance around it, then (x - mean) rstd g + b in fp16.
+template <typename IT>
+__global__ __launch_bounds__(256) void ln_rows_kernel(const IT* __restrict__ x, const half_t* __restrict__ g,
+                                                      const half_t* __restrict__ beta, half_t* __restrict__ out,
+                                                      int rows, int H, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const IT* xr = x + (size_t)row * H;
+  float s = 0.f;
+  for (int k = lane; k < H; k += kWave) s += (float)xr[k];
+  const float mean = wave_sum(s) / (float)H;
+  float v = 0.f;
+  for (int k = lane; k < H; k += kWave) {
+    const float d = (float)xr[k] - mean;
+    v += d * d;
+  }
+  const float rstd = rsqrtf(wave_sum(v) / (float)H + eps);
+  half_t* o = out + (size_t)row * H;
+  for (int k = lane; k < H; k += kWave) o[k] = (half_t)(((float)xr[k] - mean) * rstd * (float)g[k] + (float)beta[k]);
+}
+
+// ------------------------------------------------------------------ GEMM
+constexpr int kBM = 128, kBK = 32, kStages = 4, kGemmThreads = 256;
+
+template <int BN> struct GemmShape {
+  static constexpr int WN = BN / 2;               // columns of one wave's quarter
+  static constexpr int FM = 4, FN = WN / 16;      // 16x16 MFMA blocks per wave
+  static constexpr int A_BYTES = kBM * kBK * 2;   // 8 KB
+  static constexpr int B_BYTES = BN * kBK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LOADS = (kBM + BN) / 16;   // 1 KB wave loads (16 rows x 64 B) per stage
+  static constexpr int NJ = (LOADS + 3) / 4;      // per wave, at most
+  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
+};
+
+template <int BN> constexpr size_t gemm_lds_bytes() { return (size_t)kStages * GemmShape<BN>::STAGE; }
+
+// Swizzled byte offset of (row, 16-byte chunk) in a 64-byte-row LDS tile.
+__device__ __forceinline__ uint32_t swz(int row, int chunk) {
+  return (uint32_t)(row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4));
+}
+
+// This wave's share of one stage: wave loads u < n, each a per-lane global byte offset at k = 0
+// (kOutOfRange for rows past the matrix), its LDS byte offset in the stage, and its operand.
+constexpr int kMaxLoadsPerWave = 8;
+template <int NJ> struct LoadPlan {
+  static_assert(NJ <= kMaxLoadsPerWave, "too many wave loads per stage");
+  uint32_t voff[kMaxLoadsPerWave];
+  uint32_t ldso[kMaxLoadsPerWave];
+  bool isa[kMaxLoadsPerWave];
+  int n;
+};
+
+// Issue this wave's loads of k-step kt into its ring stage. Buffer descriptors are built here from
+// plain pointers: the host compiler rejects the descriptor type as a parameter (and, inside a
+// lambda, silently drops the kernel's launch stub).
+__device__ __forceinline__ void issue_stage(unsigned char* smem, int stage_bytes, int kt, const GemmArgs& g,
+                                            const uint32_t* voff, const uint32_t* ldso, const bool* isa, int n) {
+  const rsrc_t ra = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.K * 2));
+  const rsrc_t rw = make_rsrc(g.w, (uint32_t)((size_t)g.N * g.K * 2));
+  unsigned char* base = smem + (kt % kStages) * stage_bytes;
+  const uint32_t koff = (uint32_t)(kt * kBK * 2);
+#pragma unroll
+  for (int u = 0; u < kMaxLoadsPerWave; ++u) {
+    if (u < n) {
+      const uint32_t off = voff[u] == kOutOfRange ? kOutOfRange : voff[u] + koff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isa[u] ? ra : rw, lds_ptr(base + ldso[u]), 16, off, 0, 0, 0);
+    }
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void epilogue_store(const GemmArgs& g, int m, int n, float acc) {
+  if (m >= g.M || n >= g.N) return;
+  const float z = acc + (float)g.bias[n];
+  if constexpr (EPI == EPI_QKV) {
+    const int H = g.hidden;
+    if (n < H) {
+      static_cast<half_t*>(g.out)[(size_t)m * H + n] = (half_t)z;
+    } else {
+      int nn = n - H;
+      half_t* cache = nn < H ? g.k_cache : g.v_cache;
+      nn = nn < H ? nn : nn - H;
+      const int j = nn / g.head_dim, e = nn - j * g.head_dim;
+      const int b = m / g.tokens, t = m - b * g.tokens;
+      const int pos = g.d_len[b] + t;
+      if (pos >= 0 && pos < g.cap)  // the host rejects a full cache; a bad device length writes nothing
+        cache[(((size_t)b * g.heads + j) * g.cap + pos) * g.head_dim + e] = (half_t)z;
+    }
+  } else if constexpr (EPI == EPI_OPROJ) {
+    const size_t i = (size_t)m * g.N + n;
+    static_cast<float*>(g.out)[i] = (float)static_cast<const half_t*>(g.resid)[i] + z;
+  } else if constexpr (EPI == EPI_FF1) {
+    static_cast<half_t*>(g.out)[(size_t)m * g.N + n] = (half_t)gelu(z, g.gelu_tanh != 0);
+  } else {
+    const size_t i = (size_t)m * g.N + n;
+    static_cast<half_t*>(g.out)[i] = (half_t)(static_cast<const float*>(g.resid)[i] + z);
+  }
+}
+
+template <int BN, int EPI>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
+  typedef GemmShape<BN> S;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load set-up stays scalar
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a contiguous tile range.
+  const int T = g.tiles_m * g.tiles_n, i = blockIdx.x;
+  const int x = i & 7, per = T >> 3, rem = T & 7;
+  const int t = x * per + min(x, rem) + (i >> 3);
+  const int tm = t % g.tiles_m, tn = t / g.tiles_m;
+  const int m0 = tm * kBM, n0 = tn * BN;
+  const int M = g.M, N = g.N, K = g.K;
+
+  // This wave's wave loads j = wave + 4u: 16 rows of the A tile (j < 8) or of the W tile. Lane L
+  // fills LDS bytes 16L..16L+15 of the load's 1 KB: row L/4, physical chunk L%4, which holds the
+  // logical chunk (L%4) ^ ((row/2)%4).
+  const int lr = lane >> 2;
+  const int lc = (lane & 3) ^ ((lr >> 1) & 3);
+  LoadPlan<S::NJ> plan;
+  plan.n = 0;
+#pragma unroll
+  for (int u = 0; u < S::NJ; ++u) {
+    const int j = wave + 4 * u;
+    plan.voff[u] = kOutOfRange;
+    plan.ldso[u] = 0;
+    plan.isa[u] = true;
+    if (j < S::LOADS) {
+      ++plan.n;
+      if (j < kBM / 16) {
+        const int r = m0 + 16 * j + lr;
+        plan.voff[u] = r < M ? (uint32_t)(((size_t)r * K + lc * 8) * 2) : kOutOfRange;
+        plan.ldso[u] = (uint32_t)(j * 1024);
+      } else {
+        const int r = n0 + 16 * (j - kBM / 16) + lr;
+        plan.voff[u] = r < N ? (uint32_t)(((size_t)r * K + lc * 8) * 2) : kOutOfRange;
+        plan.ldso[u] = (uint32_t)(S::A_BYTES + (j - kBM / 16) * 1024);
+        plan.isa[u] = false;
+      }
+    }
+  }
+  const int nk = K / kBK;
+  float4_t acc[S::FM][S::FN];
+#pragma unroll
+  for (int a = 0; a < S::FM; ++a)
+#pragma unroll
+    for (int b = 0; b < S::FN; ++b) acc[a][b] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk) issue_stage(smem, S::STAGE, s, g, plan.voff, plan.ldso, plan.isa, plan.n);
+
+  const int frow = lane & 15, fch = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    // stages kt+1 .. min(kt+kStages-2, nk-1) may stay in flight
+    const int ahead = min(kStages - 2, nk - 1 - kt);
+    wait_vm_dyn(ahead * plan.n);
+    lds_barrier();
+    if (kt + kStages - 1 < nk) issue_stage(smem, S::STAGE, kt + kStages - 1, g, plan.voff, plan.ldso, plan.isa, plan.n);
+    const unsigned char* As = smem + (kt % kStages) * S::STAGE;
+    const unsigned char* Bs = As + S::A_BYTES;
+    half8_t af[S::FM], bf[S::FN];
+#pragma unroll
+    for (int a = 0; a < S::FM; ++a) af[a] = *reinterpret_cast<const half8_t*>(As + swz(wm * 64 + 16 * a + frow, fch));
+#pragma unroll
+    for (int b = 0; b < S::FN; ++b) bf[b] = *reinterpret_cast<const half8_t*>(Bs + swz(wn * S::WN + 16 * b + frow, fch));
+#pragma unroll
+    for (int a = 0; a < S::FM; ++a)
+#pragma unroll
+      for (int b = 0; b < S::FN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+  }
+
+  // lane l holds C[4(l/16) + r][l%16] of each 16x16 block
+#pragma unroll
+  for (int a = 0; a < S::FM; ++a)
+#pragma unroll
+    for (int b = 0; b < S::FN; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        epilogue_store<EPI>(g, m0 + wm * 64 + 16 * a + 4 * fch + r, n0 + wn * S::WN + 16 * b + frow, acc[a][b][r]);
+}
+
+// ------------------------------------------------------------------ attention over the cache
+// One workgroup per (sequence b, head j, 64 consecutive new rows); wave w owns rows 16w..16w+15.
+// Computed transposed so that MFMA results feed the next MFMA without a layout change:
+//   S^T[key][row] = K Q^T    (A = K rows from LDS, B = q rows from registers)
+//   O^T[d][row]  += V^T P^T  (A = V^T from LDS, B = the probabilities, already in B layout)
+// In S^T's accumulator layout a lane holds four keys of one row (column), and O^T's accumulators
+// in a lane also all belong to that row, so the online-softmax rescale is per lane.
+constexpr int kAttnRows = 64, kAttnKeys = 64;
+
+template <int D> struct AttnShape {
+  static constexpr int KROW = D * 2;                     // bytes of one K row in LDS
+  static constexpr int VTROW = kAttnKeys * 2 + 8;        // bytes of one V^T row (padded)
+  static constexpr int K_BYTES = kAttnKeys * KROW;
+  static constexpr int LDS = K_BYTES + D * VTROW;
+};
+
+template <int D> constexpr size_t attn_lds_bytes() { return (size_t)AttnShape<D>::LDS; }
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs g) {
+  typedef AttnShape<D> S;
+  constexpr int NCH = D / 8;  // 16-byte chunks per K row
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* Ks = smem;
+  unsigned char* Vt = smem + S::K_BYTES;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qtiles = (g.tokens + kAttnRows - 1) / kAttnRows;
+  const int qt = blockIdx.x % qtiles, bj = blockIdx.x / qtiles;
+  const int j = bj % g.heads, b = bj / g.heads;
+  const int H = g.heads * D;
+  const int len = min(max(g.d_len[b], 0), g.cap);  // rows already in the cache before this call
+  const int t0 = qt * kAttnRows;
+  const int tlast = min(t0 + kAttnRows, g.tokens) - 1;
+  const int kend = min(len + g.tokens, g.cap);      // keys present after this call's append
+  const int kmax = g.causal ? min(len + tlast + 1, kend) : kend;  // keys any row of this tile can see
+  const int frow = lane & 15, grp = lane >> 4;
+  const int trow = t0 + 16 * wave + frow;     // this lane's row (column of S^T and O^T)
+  const bool row_ok = trow < g.tokens;
+  const int vis = g.causal ? len + trow + 1 : kend;  // keys visible to this lane's row
+
+  // q of this lane's row as B operand: Q^T[k = d][n = row], d = 32 s + 8 grp + 0..7
+  half8_t qf[D / 32];
+  {
+    const half_t* qr = g.q + ((size_t)b * g.tokens + (row_ok ? trow : 0)) * H + (size_t)j * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      qf[s] = *reinterpret_cast<const half8_t*>(qr + 32 * s + 8 * grp);
+      if (!row_ok) qf[s] = half8_t{};
+    }
+  }
+  const float qscale = g.scale * 1.4426950408889634f;  // softmax in base 2
+  float4_t o[D / 16];
+#pragma unroll
+  for (int f = 0; f < D / 16; ++f) o[f] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun = -1e30f, lrun = 0.f;
+
+  const half_t* kbase = g.k_cache + ((size_t)b * g.heads + j) * g.cap * D;
+  const half_t* vbase = g.v_cache + ((size_t)b * g.heads + j) * g.cap * D;
+  for (int k0 = 0; k0 < kmax; k0 += kAttnKeys) {
+    __syncthreads();  // the previous tile is no longer read
+    // stage K [key][d] (chunk-swizzled) and V^T [d][key]; keys at or past kend are zeros
+    for (int c = tid; c < kAttnKeys * NCH; c += 256) {
+      const int kr = c / NCH, ch = c - kr * NCH, key = k0 + kr;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (key < kend) {
+        kv = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + ch * 8);
+        vv = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * D + ch * 8);
+      }
+      *reinterpret_cast<u32x4*>(Ks + kr * S::KROW + ((ch ^ (kr & 7)) << 4)) = kv;
+      const half8_t vh = __builtin_bit_cast(half8_t, vv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) *reinterpret_cast<half_t*>(Vt + (ch * 8 + e) * S::VTROW + kr * 2) = vh[e];
+    }
+    __syncthreads();
+
+    // S^T for 64 keys: four 16-key blocks; lane holds keys 16 f + 4 grp + r of its row
+    float4_t st[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      st[f] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const int kr = 16 * f + frow, ch = 4 * s + grp;
+        const half8_t kf = *reinterpret_cast<const half8_t*>(Ks + kr * S::KROW + ((ch ^ (kr & 7)) << 4));
+        st[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], st[f], 0, 0, 0);
+      }
+    }
+    float tmax = -1e30f;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + 16 * f + 4 * grp + r;
+        const float sv = key < vis ? st[f][r] * qscale : -1e30f;
+        st[f][r] = sv;
+        tmax = fmaxf(tmax, sv);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float mnew = fmaxf(mrun, tmax);
+    const float corr = exp2f(mrun - mnew);
+    float psum = 0.f;
+    half8_t pf[2];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = st[f][r] <= -1e29f ? 0.f : exp2f(st[f][r] - mnew);
+        psum += p;
+        pf[f >> 1][(f & 1) * 4 + r] = (half_t)p;
+      }
+    psum += __shfl_xor(psum, 16, kWave);
+    psum += __shfl_xor(psum, 32, kWave);
+    lrun = lrun * corr + psum;
+    mrun = mnew;
+#pragma unroll
+    for (int f = 0; f < D / 16; ++f) o[f] *= corr;
+    // O^T += V^T P^T: B element e of lane group grp is key 32 s + 4 grp + e (e < 4) or
+    // 32 s + 16 + 4 grp + (e - 4), matching the st layout; A (V^T) takes the same keys.
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int f = 0; f < D / 16; ++f) {
+        const unsigned char* vr = Vt + (16 * f + frow) * S::VTROW;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr + (32 * s + 4 * grp) * 2);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + (32 * s + 16 + 4 * grp) * 2);
+        const u32x4 vv = {lo.x, lo.y, hi.x, hi.y};
+        o[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, vv), pf[s], o[f], 0, 0, 0);
+      }
+  }
+  if (!row_ok) return;
+  const float inv = 1.f / lrun;
+  half_t* cr = g.ctx + ((size_t)b * g.tokens + trow) * H + (size_t)j * D;
+#pragma unroll
+  for (int f = 0; f < D / 16; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cr[16 * f + 4 * grp + r] = (half_t)(o[f][r] * inv);
+}
+
+template <int BN, int EPI>
+hipError_t launch_gemm_bn(const GemmArgs& a0, int cus, hipStream_t st) {
+  GemmArgs a = a0;
+  a.tiles_m = (a.M + kBM - 1) / kBM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  (void)cus;
+  const size_t lds = gemm_lds_bytes<BN>();
+  // above the default 64 KB of dynamic LDS; set on every launch (cheap, and per device)
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BN, EPI>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_kernel<BN, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(kGemmThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_gemm_epi(const GemmArgs& a, int bn, int cus, hipStream_t st) {
+  switch (bn) {
+    case 160: return launch_gemm_bn<160, EPI>(a, cus, st);
+    case 256: return launch_gemm_bn<256, EPI>(a, cus, st);
+    case 320: return launch_gemm_bn<320, EPI>(a, cus, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace prefill
+
+using namespace prefill;
+
+int gemm_pick_bn(int M, int N, int cus) {
+  const int cand[3] = {160, 256, 320};
+  int best = 160;
+  long best_cost = -1;
+  const int tm = (M + kBM - 1) / kBM;
+  for (int bn : cand) {
+    const long tiles = (long)tm * ((N + bn - 1) / bn);
+    const long cost = (tiles + cus - 1) / cus * bn;  // rounds of the grid times the work of one tile
+    if (best_cost < 0 || cost <= best_cost) {
+      best_cost = cost;
+      best = bn;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int bn, int cus, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  switch (epi) {
+    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(a, bn, cus, st);
+    case EPI_OPROJ: return launch_gemm_epi<EPI_OPROJ>(a, bn, cus, st);
+    case EPI_FF1: return launch_gemm_epi<EPI_FF1>(a, bn, cus, st);
+    case EPI_FF2: return launch_gemm_epi<EPI_FF2>(a, bn, cus, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const half_t* b, half_t* out, int rows, int H,
+                          float eps, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((rows + 3) / 4);
+  if (in_f32)
+    hipLaunchKernelGGL(ln_rows_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), g, b, out, rows, H, eps);
+  else
+    hipLaunchKernelGGL(ln_rows_kernel<half_t>, grid, dim3(256), 0, st, static_cast<const half_t*>(x), g, b, out, rows, H, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t st) {
+  const int qtiles = (a.tokens + kAttnRows - 1) / kAttnRows;
+  const dim3 grid(a.batch * a.heads * qtiles);
+  if (a.batch <= 0 || a.tokens <= 0) return hipSuccess;
+  if (a.head_dim == 128) {
+    hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), attn_lds_bytes<128>(), st, a);
+  } else if (a.head_dim == 64) {
+    hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), attn_lds_bytes<64>(), st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ds

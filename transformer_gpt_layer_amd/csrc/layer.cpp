@@ -9,6 +9,10 @@
 //   3 output projection + bias + residual                                 (all-reduce point 1)
 //   4 LN2 + FF1 + bias + GeLU                                             (region 3)
 //   5 FF2 + bias + residual, then the cache length advances               (region 4, point 2)
+// With fp16 weights and at least kMfmaMinRows rows per step (prefill, or a large decode batch) the
+// projections are dense GEMMs and run on the MFMA path instead (kernels_prefill.hip): LayerNorm
+// rows, the QKV GEMM scattering k/v into the cache, flash attention, and the O, FF1, FF2 GEMMs with
+// their bias, residual and GeLU epilogues.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -19,6 +23,7 @@
 
 #include "ds_internal.hpp"
 #include "ds_launch.hpp"
+#include "ds_prefill.hpp"
 
 namespace {
 thread_local std::string g_err;
@@ -51,7 +56,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct WsLayout {
-  size_t q, part, cnt, ctx, x2, f, total;
+  size_t q, part, cnt, ctx, x2, f, h, total;
   int chunk, nchunk;
 };
 
@@ -67,6 +72,7 @@ WsLayout ws_layout(const ds_layer_desc& d, int rows, int cap) {
   L.ctx = take((size_t)rows * d.hidden * 4);
   L.x2 = take((size_t)rows * d.hidden * 4);
   L.f = take((size_t)rows * d.ffn * 4);
+  L.h = take((size_t)rows * d.hidden * 2);  // fp16 LayerNorm rows of the MFMA path
   L.total = off;
   return L;
 }
@@ -86,6 +92,79 @@ int check_kv(const ds_layer* L, const ds_kv_cache* kv, int batch, int ntok) {
   return DS_OK;
 }
 
+constexpr int kMfmaMinRows = 16;
+
+// The MFMA path takes fp16 weights and activations, at least kMfmaMinRows rows, and operands whose
+// byte sizes stay inside one buffer descriptor's 31-bit range.
+bool use_mfma(const ds_layer_desc& d, int rows) {
+  if (d.weight_dtype != DS_F16 || d.act_dtype != DS_F16 || rows < kMfmaMinRows) return false;
+  const int64_t kmax = d.hidden > d.ffn ? d.hidden : d.ffn;
+  const int64_t lim = int64_t(1) << 31;
+  return (int64_t)rows * kmax * 2 < lim && (int64_t)d.ffn * d.hidden * 2 < lim && 3 * (int64_t)d.hidden * d.hidden * 2 < lim;
+}
+
+int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int batch, int ntok, char* base,
+                 const WsLayout& W, hipStream_t st) {
+  const ds_layer_desc& d = L->desc;
+  const int rows = batch * ntok, H = d.hidden, F = d.ffn;
+  int dev = 0, cus = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_fail(e, "hipGetDevice");
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) return hip_fail(e, "CU count");
+  auto* h = reinterpret_cast<ds::half_t*>(base + W.h);
+  auto* q = reinterpret_cast<ds::half_t*>(base + W.q);
+  auto* ctx = reinterpret_cast<ds::half_t*>(base + W.ctx);
+  auto* x2 = reinterpret_cast<float*>(base + W.x2);
+  auto* f = reinterpret_cast<ds::half_t*>(base + W.f);
+  auto hp = [](const void* p) { return static_cast<const ds::half_t*>(p); };
+
+  ds::GemmArgs g{};
+  g.d_len = kv->d_len;
+  g.tokens = ntok;
+  g.heads = d.heads;
+  g.head_dim = d.head_dim;
+  g.cap = kv->capacity;
+  g.hidden = H;
+  g.gelu_tanh = d.gelu_tanh;
+  g.k_cache = static_cast<ds::half_t*>(kv->k);
+  g.v_cache = static_cast<ds::half_t*>(kv->v);
+  g.M = rows;
+
+  // 1: h = LN1(x); [q | k | v] = h Wqkv^T + bqkv, k and v into the cache rows d_len[b] + t
+  if (hipError_t e = ds::launch_ln_rows(false, x, hp(L->w.ln1_g), hp(L->w.ln1_b), h, rows, H, d.ln_eps, st))
+    return hip_fail(e, "ln1 launch");
+  ds::GemmArgs a = g;
+  a.a = h; a.w = hp(L->w.w_qkv); a.bias = hp(L->w.b_qkv); a.out = q; a.N = 3 * H; a.K = H;
+  if (hipError_t e = ds::launch_gemm(ds::EPI_QKV, a, ds::gemm_pick_bn(rows, a.N, cus), cus, st)) return hip_fail(e, "qkv gemm launch");
+
+  // 2: attention of the new rows over the cache
+  ds::AttnPrefillArgs at{};
+  at.q = q; at.k_cache = g.k_cache; at.v_cache = g.v_cache; at.d_len = kv->d_len; at.ctx = ctx;
+  at.batch = batch; at.tokens = ntok; at.heads = d.heads; at.head_dim = d.head_dim; at.cap = kv->capacity;
+  at.causal = d.triangular_masking; at.scale = 1.f / std::sqrt((float)d.head_dim);
+  if (hipError_t e = ds::launch_attn_prefill(at, st)) return hip_fail(e, "attention launch");
+
+  // 3: x2 = x + ctx Wo^T + bo
+  a = g;
+  a.a = ctx; a.w = hp(L->w.w_o); a.bias = hp(L->w.b_o); a.out = x2; a.resid = x; a.N = H; a.K = H;
+  if (hipError_t e = ds::launch_gemm(ds::EPI_OPROJ, a, ds::gemm_pick_bn(rows, a.N, cus), cus, st)) return hip_fail(e, "o gemm launch");
+
+  // 4: f = GeLU(LN2(x2) W1^T + b1)
+  if (hipError_t e = ds::launch_ln_rows(true, x2, hp(L->w.ln2_g), hp(L->w.ln2_b), h, rows, H, d.ln_eps, st))
+    return hip_fail(e, "ln2 launch");
+  a = g;
+  a.a = h; a.w = hp(L->w.w_ff1); a.bias = hp(L->w.b_ff1); a.out = f; a.N = F; a.K = H;
+  if (hipError_t e = ds::launch_gemm(ds::EPI_FF1, a, ds::gemm_pick_bn(rows, a.N, cus), cus, st)) return hip_fail(e, "ff1 gemm launch");
+
+  // 5: y = x2 + f W2^T + b2, then d_len += ntok
+  a = g;
+  a.a = f; a.w = hp(L->w.w_ff2); a.bias = hp(L->w.b_ff2); a.out = y; a.resid = x2; a.N = H; a.K = F;
+  if (hipError_t e = ds::launch_gemm(ds::EPI_FF2, a, ds::gemm_pick_bn(rows, a.N, cus), cus, st)) return hip_fail(e, "ff2 gemm launch");
+  if (hipError_t e = ds::launch_len_advance(kv->d_len, batch, ntok, kv->capacity, st)) return hip_fail(e, "len advance launch");
+  if (kv->h_len)
+    for (int b = 0; b < batch; ++b) kv->h_len[b] += ntok;
+  return DS_OK;
+}
+
 int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int batch, int ntok,
                  void* ws, size_t ws_bytes, void* stream) {
   if (!L) return fail(DS_ERR_NULL, "layer is NULL");
@@ -100,6 +179,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
+  if (use_mfma(L->desc, rows)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, st);
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
   const int H = d.hidden, F = d.ffn;
 
