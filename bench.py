@@ -1,4 +1,4 @@
-"""Decode throughput of the fused GPT-layer stack on one MI355X.
+"""Decode throughput of the fused GPT-layer stack on one MI355X (and, with --config c5, prefill).
 
 One step = one decode token for every sequence of the batch through all L layers of the stack
 (LN1+QKV, attention over the KV cache, output projection, LN2+FF1+GeLU, FF2), starting from the
@@ -73,6 +73,118 @@ def build_stack(wl, torch, tg, syn, layers):
     return stack, kvs, lens, ws, act
 
 
+PEAK_F16_TFLOPS = 2500.0
+
+
+def prefill_flops_per_layer(wl) -> dict:
+    """Algorithmic FLOPs of one prefill layer step: the four weight GEMMs (2 M N K each, M = B S)
+    and causal attention (QK^T and PV over the visible keys only: S (S+1) / 2 per sequence and
+    head, 2 d FLOPs each for the two products)."""
+    H, F, B, S, nh, d = wl.hidden, wl.ffn, wl.batch, wl.seq, wl.heads, wl.head_dim
+    M = B * S
+    g = {"qkv": 2 * M * 3 * H * H, "o": 2 * M * H * H, "ff1": 2 * M * F * H, "ff2": 2 * M * H * F}
+    attn = 2 * 2 * d * nh * B * (S * (S + 1) // 2)
+    return {**g, "attention": attn, "gemm_total": sum(g.values()), "total": sum(g.values()) + attn}
+
+
+def _oracle_weights(layer, wl):
+    import numpy as np
+    import torch
+
+    import oracle
+
+    w = {}
+    for n in ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b", "w_ff1", "b_ff1", "w_ff2", "b_ff2"):
+        t = layer._weights[n]
+        if n.startswith("w_") and wl.weight_dtype == "i8":
+            s = layer._weights["s" + n[1:]]
+            w[n] = oracle.dequantize_i8(t.cpu().numpy(), s.cpu().view(torch.int16).numpy().view(np.uint16), wl.group)
+        else:
+            w[n] = t.double().cpu().numpy()
+    return w
+
+
+def cpu_baseline_prefill(wl, stack, target_rows: int = 64):
+    """The oracle (plain C, double, one thread) on a bounded sample: the first target_rows prompt
+    rows of one sequence through layer 0, scaled to prompt tokens/s of the full L-layer stack."""
+    import numpy as np
+
+    import oracle
+
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
+    w = _oracle_weights(stack[0], wl)
+    S = min(target_rows, wl.seq)
+    x = np.random.default_rng(0).standard_normal((1, S, wl.hidden))
+    k = np.zeros((1, wl.heads, wl.capacity, wl.head_dim))
+    v = np.zeros_like(k)
+    lens = np.zeros(1, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.layer_forward(desc, w, k, v, lens, x)
+    spent = time.perf_counter() - t0
+    return {"value": S / (spent * wl.layers), "unit": "prompt tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {S} prompt rows of one sequence of {wl.name} through one layer in {spent:.1f} s "
+                      f"on one host thread, scaled to the {wl.layers}-layer stack"}
+
+
+def run_prefill(args, wl, torch, tg, syn):
+    """C5-style workload: one step = the B x S prompt through all L layers (cache lengths reset to
+    0 each step), captured once in a HIP graph and replayed."""
+    layers = args.layers or wl.layers
+    stack, kvs, lens, _, act = build_stack(wl, torch, tg, syn, layers)
+    ws = stack[0].workspace(wl.batch, wl.seq, wl.capacity)
+    x0 = syn.normal((wl.batch, wl.seq, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").to(act)
+    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+
+    def step():
+        lens.zero_()
+        for l in range(layers):
+            stack[l].prefill(kvs[l], x0 if l == 0 else bufs[l % 2], bufs[(l + 1) % 2], ws)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    out = bufs[layers % 2]
+    assert torch.isfinite(out.float()).all(), "non-finite prefill output"
+    fl = prefill_flops_per_layer(wl)
+    tflops = fl["total"] * layers / (ms * 1e-3) / 1e12
+    gemm_tflops = fl["gemm_total"] * layers / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "prefill prompt tokens/s + MFMA utilization (weight-GEMM FLOPs / step time / 2.5 PF)",
+        "value": round(wl.batch * wl.seq / (ms * 1e-3), 1),
+        "unit": "prompt tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prompt rows)",
+        "config": {"workload": wl.name, "layers": layers, "batch": wl.batch, "seq": wl.seq,
+                   "hidden": wl.hidden, "heads": wl.heads, "ffn": wl.ffn,
+                   "launch": "per-layer kernels (LN, 4 MFMA GEMMs, flash attention), hip-graph"},
+        "flops_per_layer": fl,
+        "roofline": {"bound": "mfma", "kernel": "whole prefill step (weight GEMMs + attention)",
+                     "achieved": round(tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "gemm_flops_over_step_tflops": round(gemm_tflops, 1)},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_prefill(wl, stack)
+    print(json.dumps(result))
+
+
 def cpu_baseline(wl, stack, kvs, target_s: float):
     """The oracle (plain C, double, one thread) on a bounded sample: whole decode layer steps of
     this workload, layer after layer, until about target_s seconds have run; scaled to tokens/s
@@ -87,14 +199,7 @@ def cpu_baseline(wl, stack, kvs, target_s: float):
     done, spent = 0, 0.0
     while spent < target_s and done < len(stack):
         layer, kv = stack[done], kvs[done]
-        w = {}
-        for n in ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b", "w_ff1", "b_ff1", "w_ff2", "b_ff2"):
-            t = layer._weights[n]
-            if n.startswith("w_") and wl.weight_dtype == "i8":
-                s = layer._weights["s" + n[1:]]
-                w[n] = oracle.dequantize_i8(t.cpu().numpy(), s.cpu().view(torch.int16).numpy().view(np.uint16), wl.group)
-            else:
-                w[n] = t.double().cpu().numpy()
+        w = _oracle_weights(layer, wl)
         k = np.zeros((wl.batch, wl.heads, wl.capacity, wl.head_dim))
         v = np.zeros_like(k)
         k[:, :, :wl.past] = kv.k[:, :, :wl.past].double().cpu().numpy()
@@ -115,7 +220,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", help="workload key in synthetic.WORKLOADS (decode configs)")
+    ap.add_argument("--config", default="c2", help="workload key in synthetic.WORKLOADS (c5: prefill)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 disables)")
     ap.add_argument("--mode", choices=["auto", "stack", "layers"], default="auto",
@@ -134,8 +239,9 @@ def main():
     import transformer_gpt_layer_amd as tg
 
     wl = syn.WORKLOADS[args.config]
+    torch.cuda.set_device(0)
     if wl.seq != 1:
-        raise SystemExit("bench.py times decode workloads")
+        return run_prefill(args, wl, torch, tg, syn)
     layers = args.layers or wl.layers
     torch.cuda.set_device(0)
     stack, kvs, lens, ws, act = build_stack(wl, torch, tg, syn, layers)

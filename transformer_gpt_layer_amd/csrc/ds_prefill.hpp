@@ -16,7 +16,7 @@ enum GemmEpi { EPI_QKV = 0, EPI_OPROJ = 1, EPI_FF1 = 2, EPI_FF2 = 3 };
 //   EPI_OPROJ out fp32 [M][N] = resid fp16 [M][N] + C
 //   EPI_FF1   out fp16 [M][N] = GeLU(C)
 //   EPI_FF2   out fp16 [M][N] = resid fp32 [M][N] + C
-// A, W: fp16, K a multiple of 32, M*K*2 and N*K*2 below 2^31 bytes.
+// A, W: fp16, K a multiple of 64, M*K*2 and N*K*2 below 2^31 bytes.
 struct GemmArgs {
   const half_t* a;
   const half_t* w;

@@ -18,11 +18,11 @@
 //
 // GEMM design. C[M][N] = A[M][K] W[N][K]^T with both operands K-contiguous, which is the operand
 // order v_mfma_f32_16x16x32_f16 wants (lane l holds row l%16, k 8(l/16)..+7 of either operand).
-// A workgroup of four waves owns a 128 x BN tile, each wave a 64 x BN/2 quarter. K advances 32 at a
-// time through a four-stage LDS ring filled by buffer loads that write LDS directly (no VGPR
-// round trip); one barrier per k-step both publishes a stage and frees the oldest. LDS rows are
-// 64 bytes with the 16-byte chunk index XOR-ed by (row/2)%4, so the MFMA operand reads (16 rows,
-// one chunk) hit distinct banks. Tiles are numbered so that the workgroups the dispatcher sends to
+// A workgroup of four waves owns a 128 x BN tile, each wave a 64 x BN/2 quarter. K advances 64 at a
+// time (whole 128-byte lines of each row) through an LDS ring filled by buffer loads that write LDS
+// directly (no VGPR round trip); one barrier per k-step both publishes a stage and frees the
+// oldest. LDS rows are 128 bytes with the 16-byte chunk index XOR-ed by row % 8, so the MFMA
+// operand reads (16 rows, one chunk) hit distinct banks. Tiles are numbered so that the workgroups the dispatcher sends to
 // one XCD (every 8th) hold consecutive tiles, which share their weight columns in that XCD's L2.
 #include "ds_device.hpp"
 #include "ds_prefill.hpp"
@@ -77,51 +77,105 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ------------------------------------------------------------------ LayerNorm rows
-// One wave per row: mean, then the biased variance around it, then (x - mean) rstd g + b in fp16.
+// One wave per row with 16-byte input loads: the mean, then the biased variance around it, then
+// (x - mean) rstd g + b written as fp16. The second and third passes re-read the row from cache.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+template <int V> __device__ __forceinline__ void ld_halves(const half_t* p, float (&v)[V]) {
+  if constexpr (V == 8) {
+    const half8_t h = *reinterpret_cast<const half8_t*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)h[e];
+  } else {
+    const half4_t h = *reinterpret_cast<const half4_t*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (float)h[e];
+  }
+}
+template <int V> __device__ __forceinline__ void ld_row(const half_t* p, float (&v)[V]) { ld_halves<V>(p, v); }
+template <int V> __device__ __forceinline__ void ld_row(const float* p, float (&v)[V]) {
+  const float4_t f = *reinterpret_cast<const float4_t*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = f[e];
+}
+template <int V> __device__ __forceinline__ void st_halves(half_t* p, const float (&v)[V]) {
+  if constexpr (V == 8) {
+    half8_t h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (half_t)v[e];
+    *reinterpret_cast<half8_t*>(p) = h;
+  } else {
+    half4_t h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (half_t)v[e];
+    *reinterpret_cast<half4_t*>(p) = h;
+  }
+}
+
 template <typename IT>
 __global__ __launch_bounds__(256) void ln_rows_kernel(const IT* __restrict__ x, const half_t* __restrict__ g,
                                                       const half_t* __restrict__ beta, half_t* __restrict__ out,
                                                       int rows, int H, float eps) {
+  constexpr int V = 16 / (int)sizeof(IT);  // elements per 16-byte load
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const IT* xr = x + (size_t)row * H;
+  float v[V];
   float s = 0.f;
-  for (int k = lane; k < H; k += kWave) s += (float)xr[k];
-  const float mean = wave_sum(s) / (float)H;
-  float v = 0.f;
-  for (int k = lane; k < H; k += kWave) {
-    const float d = (float)xr[k] - mean;
-    v += d * d;
+  for (int k = lane * V; k < H; k += kWave * V) {
+    ld_row<V>(xr + k, v);
+#pragma unroll
+    for (int e = 0; e < V; ++e) s += v[e];
   }
-  const float rstd = rsqrtf(wave_sum(v) / (float)H + eps);
+  const float mean = wave_sum(s) / (float)H;
+  float q = 0.f;
+  for (int k = lane * V; k < H; k += kWave * V) {
+    ld_row<V>(xr + k, v);
+#pragma unroll
+    for (int e = 0; e < V; ++e) q += (v[e] - mean) * (v[e] - mean);
+  }
+  const float rstd = rsqrtf(wave_sum(q) / (float)H + eps);
   half_t* o = out + (size_t)row * H;
-  for (int k = lane; k < H; k += kWave) o[k] = (half_t)(((float)xr[k] - mean) * rstd * (float)g[k] + (float)beta[k]);
+  for (int k = lane * V; k < H; k += kWave * V) {
+    float gv[V], bv[V];
+    ld_row<V>(xr + k, v);
+    ld_halves<V>(g + k, gv);
+    ld_halves<V>(beta + k, bv);
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = (v[e] - mean) * rstd * gv[e] + bv[e];
+    st_halves<V>(o + k, v);
+  }
 }
 
 // ------------------------------------------------------------------ GEMM
-constexpr int kBM = 128, kBK = 32, kStages = 4, kGemmThreads = 256;
+constexpr int kBM = 128, kBK = 64, kGemmThreads = 256;
+#ifndef DS_GEMM_STAGES
+#define DS_GEMM_STAGES 2
+#endif
+constexpr int kStages = DS_GEMM_STAGES;
 
 template <int BN> struct GemmShape {
   static constexpr int WN = BN / 2;               // columns of one wave's quarter
   static constexpr int FM = 4, FN = WN / 16;      // 16x16 MFMA blocks per wave
-  static constexpr int A_BYTES = kBM * kBK * 2;   // 8 KB
+  static constexpr int A_BYTES = kBM * kBK * 2;   // 16 KB
   static constexpr int B_BYTES = BN * kBK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LOADS = (kBM + BN) / 16;   // 1 KB wave loads (16 rows x 64 B) per stage
+  static constexpr int LOADS = (kBM + BN) / 8;    // 1 KB wave loads (8 rows x 128 B) per stage
   static constexpr int NJ = (LOADS + 3) / 4;      // per wave, at most
   static_assert(BN % 32 == 0, "BN must be a multiple of 32");
 };
 
 template <int BN> constexpr size_t gemm_lds_bytes() { return (size_t)kStages * GemmShape<BN>::STAGE; }
 
-// Swizzled byte offset of (row, 16-byte chunk) in a 64-byte-row LDS tile.
+// Swizzled byte offset of (row, 16-byte chunk) in a 128-byte-row LDS tile: chunk c of row r sits
+// at position c ^ (r % 8), so 16 consecutive rows read at one chunk spread over all banks.
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
-  return (uint32_t)(row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4));
+  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
 }
 
 // This wave's share of one stage: wave loads u < n, each a per-lane global byte offset at k = 0
 // (kOutOfRange for rows past the matrix), its LDS byte offset in the stage, and its operand.
-constexpr int kMaxLoadsPerWave = 8;
+constexpr int kMaxLoadsPerWave = 16;
 template <int NJ> struct LoadPlan {
   static_assert(NJ <= kMaxLoadsPerWave, "too many wave loads per stage");
   uint32_t voff[kMaxLoadsPerWave];
@@ -193,11 +247,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
   const int m0 = tm * kBM, n0 = tn * BN;
   const int M = g.M, N = g.N, K = g.K;
 
-  // This wave's wave loads j = wave + 4u: 16 rows of the A tile (j < 8) or of the W tile. Lane L
-  // fills LDS bytes 16L..16L+15 of the load's 1 KB: row L/4, physical chunk L%4, which holds the
-  // logical chunk (L%4) ^ ((row/2)%4).
-  const int lr = lane >> 2;
-  const int lc = (lane & 3) ^ ((lr >> 1) & 3);
+  // This wave's wave loads j = wave + 4u: 8 rows of the A tile (j < 16) or of the W tile. Lane L
+  // fills LDS bytes 16L..16L+15 of the load's 1 KB: row L/8, physical chunk L%8, which holds the
+  // logical chunk (L%8) ^ row; eight lanes read one whole 128-byte line of a row.
+  const int lr = lane >> 3;
+  const int lc = (lane & 7) ^ lr;
   LoadPlan<S::NJ> plan;
   plan.n = 0;
 #pragma unroll
@@ -208,14 +262,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
     plan.isa[u] = true;
     if (j < S::LOADS) {
       ++plan.n;
-      if (j < kBM / 16) {
-        const int r = m0 + 16 * j + lr;
+      if (j < kBM / 8) {
+        const int r = m0 + 8 * j + lr;
         plan.voff[u] = r < M ? (uint32_t)(((size_t)r * K + lc * 8) * 2) : kOutOfRange;
         plan.ldso[u] = (uint32_t)(j * 1024);
       } else {
-        const int r = n0 + 16 * (j - kBM / 16) + lr;
+        const int r = n0 + 8 * (j - kBM / 8) + lr;
         plan.voff[u] = r < N ? (uint32_t)(((size_t)r * K + lc * 8) * 2) : kOutOfRange;
-        plan.ldso[u] = (uint32_t)(S::A_BYTES + (j - kBM / 16) * 1024);
+        plan.ldso[u] = (uint32_t)(S::A_BYTES + (j - kBM / 8) * 1024);
         plan.isa[u] = false;
       }
     }
@@ -240,15 +294,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
     if (kt + kStages - 1 < nk) issue_stage(smem, S::STAGE, kt + kStages - 1, g, plan.voff, plan.ldso, plan.isa, plan.n);
     const unsigned char* As = smem + (kt % kStages) * S::STAGE;
     const unsigned char* Bs = As + S::A_BYTES;
-    half8_t af[S::FM], bf[S::FN];
+    // two k-substeps of 32 per stage; all operand reads first, so the MFMAs of the first substep
+    // overlap the reads of the second
+    half8_t af[2][S::FM], bf[2][S::FN];
 #pragma unroll
-    for (int a = 0; a < S::FM; ++a) af[a] = *reinterpret_cast<const half8_t*>(As + swz(wm * 64 + 16 * a + frow, fch));
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int b = 0; b < S::FN; ++b) bf[b] = *reinterpret_cast<const half8_t*>(Bs + swz(wn * S::WN + 16 * b + frow, fch));
+      for (int a = 0; a < S::FM; ++a)
+        af[ks][a] = *reinterpret_cast<const half8_t*>(As + swz(wm * 64 + 16 * a + frow, 4 * ks + fch));
 #pragma unroll
-    for (int a = 0; a < S::FM; ++a)
+      for (int b = 0; b < S::FN; ++b)
+        bf[ks][b] = *reinterpret_cast<const half8_t*>(Bs + swz(wn * S::WN + 16 * b + frow, 4 * ks + fch));
+    }
 #pragma unroll
-      for (int b = 0; b < S::FN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int a = 0; a < S::FM; ++a)
+#pragma unroll
+        for (int b = 0; b < S::FN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ks][a], bf[ks][b], acc[a][b], 0, 0, 0);
   }
 
   // lane l holds C[4(l/16) + r][l%16] of each 16x16 block
@@ -419,8 +483,6 @@ template <int EPI>
 hipError_t launch_gemm_epi(const GemmArgs& a, int bn, int cus, hipStream_t st) {
   switch (bn) {
     case 160: return launch_gemm_bn<160, EPI>(a, cus, st);
-    case 256: return launch_gemm_bn<256, EPI>(a, cus, st);
-    case 320: return launch_gemm_bn<320, EPI>(a, cus, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -429,20 +491,14 @@ hipError_t launch_gemm_epi(const GemmArgs& a, int bn, int cus, hipStream_t st) {
 
 using namespace prefill;
 
+// 128 x 160 tiles with a two-stage ring (72 KB of LDS) let two workgroups share a CU, which hides
+// more load latency than wider tiles with one workgroup per CU (measured: 256- and 320-column tiles
+// ran 1.3x-1.7x slower on the GPT-Neo-2.7B prefill GEMMs).
 int gemm_pick_bn(int M, int N, int cus) {
-  const int cand[3] = {160, 256, 320};
-  int best = 160;
-  long best_cost = -1;
-  const int tm = (M + kBM - 1) / kBM;
-  for (int bn : cand) {
-    const long tiles = (long)tm * ((N + bn - 1) / bn);
-    const long cost = (tiles + cus - 1) / cus * bn;  // rounds of the grid times the work of one tile
-    if (best_cost < 0 || cost <= best_cost) {
-      best_cost = cost;
-      best = bn;
-    }
-  }
-  return best;
+  (void)M;
+  (void)N;
+  (void)cus;
+  return 160;
 }
 
 hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int bn, int cus, hipStream_t st) {
