@@ -36,6 +36,23 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
   return v;
 }
+// Sum over the wave with DPP lane moves instead of LDS permutes: prefix sums within each 16-lane
+// row (row_shr 1, 2, 4, 8), then row 0's total into row 1 and row 2's into row 3 (row_bcast:15),
+// then rows 0-1's total into rows 2-3 (row_bcast:31); lane 63 ends with the wave total, which
+// readlane hands to every lane. Lanes whose DPP source lies outside the row keep adding 0.
+template <int kCtrl, int kRowMask> __device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // Sum over aligned groups of G lanes (G a power of two <= 64); every lane gets its group's sum.
 template <int G> __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll

@@ -30,6 +30,49 @@ enum {
   kSyncAttn = kSyncError + kSyncLine,  // then B*nh attention-merge counters
 };
 
+// Workgroup shape: kStackSyncWaves waves stage activations, reduce, run the epilogues, attention
+// and the grid barriers; kStackWorkers waves stream the weights and compute the row dot products.
+constexpr int kStackSyncWaves = 4;
+constexpr int kStackWorkers = 12;
+constexpr int kStackWaves = kStackSyncWaves + kStackWorkers;
+constexpr int kStackThreads = 64 * kStackWaves;  // one workgroup per CU
+constexpr int kStackChunk = 64;                  // cache rows per attention work item
+constexpr int kStackLdsMax = 160 * 1024;
+
+// Dynamic LDS layout of one workgroup (byte offsets; the activation rows start at 0). Identical on
+// the host and the device.
+struct StackLds {
+  uint32_t raw;     // LayerNorm input rows (fp32), then gamma and beta, inside the activation region
+  uint32_t slots;   // per-(row, worker, batch row) partial sums
+  uint32_t scales;  // int8 scales of the current row tile
+  uint32_t wtab;    // the four weight-matrix pointers of every layer (8 bytes each)
+  uint32_t total;
+};
+
+__host__ __device__ inline uint32_t stack_align(uint32_t v) { return (v + 255u) & ~255u; }
+
+// wsize: weight element bytes (4, 2, 1); bm: batch rows of the kernel variant (1 or 4). The
+// activation region also holds the attention scratch (per-wave partials, then the chunk partials
+// of the merge), which is never live at the same time as staged activations.
+__host__ __device__ inline StackLds stack_lds_layout(int wsize, int bm, int H, int F, int rows_per_wg, int nchunk,
+                                                     int D, int group, int n_layers) {
+  StackLds L{};
+  const uint32_t lt = wsize == 4 ? 4u : 2u;
+  const uint32_t kmax = (uint32_t)(H > F ? H : F);
+  uint32_t region = (uint32_t)bm * kmax * lt;
+  const uint32_t ln = (uint32_t)bm * (uint32_t)H * (lt + 4u) + 2u * (uint32_t)H * lt;  // rows, fp32 copy, gamma/beta
+  const uint32_t attn = (uint32_t)kStackSyncWaves * D * 4u + (uint32_t)nchunk * (D + 2) * 4u;
+  if (ln > region) region = ln;
+  if (attn > region) region = attn;
+  L.raw = (uint32_t)bm * (uint32_t)H * lt;
+  L.slots = stack_align(region);
+  L.scales = stack_align(L.slots + (uint32_t)rows_per_wg * kStackWorkers * bm * 4u);
+  const uint32_t sc = wsize == 1 ? (uint32_t)rows_per_wg * (kmax / (uint32_t)group) * 2u : 0u;
+  L.wtab = stack_align(L.scales + sc);
+  L.total = stack_align(L.wtab + (uint32_t)n_layers * 4u * 8u);
+  return L;
+}
+
 struct StackArgs {
   const StackLayer* layers;
   int n_layers;
@@ -49,20 +92,13 @@ struct StackArgs {
   uint32_t* sync;  // kSync* words, then B*nh attention counters
   int G;           // workgroups (all co-resident)
   int nchunk;      // attention chunks of kStackChunk rows over the capacity
-  uint64_t timeout_ticks;  // per grid-barrier wait, in 100 MHz wall-clock ticks
+  StackLds lds;
+  uint64_t timeout_ticks;  // per wait, in 100 MHz wall-clock ticks
 };
 
-constexpr int kStackChunk = 64;    // cache rows per attention work item
-constexpr int kStackThreads = 512;  // 8 wave64 per workgroup, one workgroup per CU
-constexpr int kStackWaves = kStackThreads / 64;
-
-// Dynamic LDS bytes of one workgroup and the workgroup count the device can keep co-resident.
-size_t stack_lds_bytes(Dt wdt, int B, int H, int F, int rows_per_wg);
-hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups);
-hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, size_t lds, hipStream_t st);
 // The largest per-workgroup row tile among the four projections for a grid of G workgroups.
 int stack_rows_per_wg(int H, int F, int G);
-// LDS the attention merge stages (it reuses the start of the dynamic LDS).
-size_t stack_merge_bytes(int nchunk, int head_dim);
+hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups);
+hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, hipStream_t st);
 
 }  // namespace ds

@@ -7,38 +7,54 @@
 // fusion boundaries where partial results must meet (the all-reduce points); here those are the
 // grid-wide barriers between phases.
 //
-// gfx950 design. One cooperative launch keeps one 8-wave workgroup per CU resident for the whole
+// gfx950 design. One cooperative launch keeps one 16-wave workgroup per CU resident for the whole
 // step. Each projection is cut into per-workgroup row tiles; a tile is one contiguous range of the
-// row-major matrix, cut into 1 KB "slices" (one 16-byte load per lane of a wave64), and each wave
-// owns a contiguous block of slices, so every phase is balanced whatever its shape. As soon as a
-// workgroup has stored a phase's results it issues the weight loads of its next tile into
-// registers: weights do not depend on activations, so HBM keeps streaming through the epilogue,
-// the grid barrier and the next phase's staging. The loads complete in issue order, so waiting
-// until at most that many are outstanding (s_waitcnt vmcnt(N)) proves the earlier stores done
-// without waiting for the prefetch. Activations that cross workgroups are written and read with
-// sc1 buffer operations (at the device coherence point, past the per-XCD L2 copies); barrier
-// arrivals are agent-scope atomics spread over 16 counters. Every barrier wait is bounded by a
-// wall-clock timeout that raises an error flag, after which every workgroup leaves the kernel.
+// row-major matrix, cut into 1 KB "slices" (one 16-byte load per lane of a wave64).
+//
+// The waves are specialized so that HBM never waits for the step's serial parts:
+//  - 12 worker waves own contiguous blocks of each tile and walk the fixed sequence of all their
+//    slices of all layers. Each keeps kRing slices in flight in a rotating set of registers: a
+//    slice is multiplied with the staged activation (LDS) the moment it is consumed, and its
+//    registers at once load the slice kRing places further on, whatever phase or layer that is.
+//    Workers issue nothing but these loads, so their in-order load counter only ever waits for
+//    the oldest slice; row partial sums go to LDS.
+//  - 4 sync waves stage each phase's activation (LayerNorm included), reduce the workers' partial
+//    sums, run the epilogues (bias, residual, GeLU, the q/k/v scatter), compute attention over
+//    the cache and take the grid barriers.
+// So weight streaming continues straight through the barriers, the activation staging and the
+// epilogues. Activations that cross workgroups are written and read with sc1 buffer operations
+// (at the device coherence point, past the per-XCD L2 copies); barrier arrivals are agent-scope
+// atomics spread over 16 counters. Every wait, in LDS or on the grid, is bounded by a wall-clock
+// timeout that raises the error flag, after which every wave leaves the kernel.
 #include "ds_device.hpp"
 #include "ds_stack.hpp"
 
 namespace ds {
 namespace {
 
-constexpr int NW = kStackWaves;
-constexpr int kAuxCoherent = 16;         // sc1
-constexpr int kAuxStream = 2;            // nt
-constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit dword format
+constexpr int NS = kStackSyncWaves;
+constexpr int NT = NS * kWave;             // sync threads
+constexpr int NWK = kStackWorkers;
+// Weight slices a worker keeps in flight: 24 for fp16 weights and one batch row (24 KB per wave,
+// 288 KB per CU), 16 for fp32; variants with four batch rows or int8 weights (two 16-byte
+// activation reads per row) keep 12 so that a 128-VGPR wave still holds everything.
+template <typename WT, int BM> struct Ring { static constexpr int value = (sizeof(WT) == 1 || BM == 4) ? 12 : (sizeof(WT) == 2 ? 24 : 16); };
+constexpr int kAuxCoherent = 16;           // sc1
+constexpr int kAuxStream = 2;              // nt
+constexpr int kRsrcFlags = 0x00020000;     // raw buffer, 32-bit dword format
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // a buffer offset past every descriptor: loads return 0
-// Weight slices (16 B per lane) a wave holds in registers: 25 covers a whole row tile of the
-// GPT-Neo-2.7B shapes on 256 workgroups; int8 slices also carry a scale and widen in registers.
-template <typename WT> struct MaxSlices { static constexpr int value = 25; };
-template <> struct MaxSlices<int8_t> { static constexpr int value = 16; };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// Buffer descriptors must be wave-uniform (SGPRs). Pointers read from the layer table arrive in
+// VGPRs as far as the compiler knows, which would wrap every buffer access in a waterfall loop, so
+// the pointer and the size pass through readfirstlane (free for values already in SGPRs).
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcFlags);
 }
 __device__ __forceinline__ u32x4 coh_load16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxCoherent);
@@ -79,204 +95,359 @@ template <int N> __device__ __forceinline__ void wait_vm_at_most() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
 }
-
-// Workgroup barrier that waits only for LDS traffic, not for outstanding global loads.
-__device__ __forceinline__ void lds_barrier() {
+__device__ __forceinline__ void wait_lgkm0() {
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
   asm volatile("" ::: "memory");
 }
 
-// Block-wide sums of two values at once; `red2` is NW float2 of LDS.
-__device__ __forceinline__ float2_t block_sum2(float2_t v, float2_t* red2, int tid) {
-  v.x = wave_sum(v.x);
-  v.y = wave_sum(v.y);
-  lds_barrier();
-  if ((tid & 63) == 0) red2[tid >> 6] = v;
-  lds_barrier();
-  float2_t s = {0.f, 0.f};
-#pragma unroll
-  for (int w = 0; w < NW; ++w) s += red2[w];
-  return s;
+// ------------------------------------------------------------------ workgroup control block
+// LDS words shared by the sync and worker waves of one workgroup.
+struct Ctl {
+  uint32_t act_ready;    // 1 + sequence number of the phase whose activation is staged
+  uint32_t done[NWK];    // phases each worker has finished (its partial sums are in LDS)
+  uint32_t sbar;         // sync-wave barrier arrivals
+  uint32_t abort;        // set when any wait of this workgroup failed
+  int ok;                // grid-barrier outcome, broadcast to the sync waves
+  int flag;              // attention: this workgroup completed a (sequence, head)
+  float red[NS][8];      // LayerNorm sums: (sum, sum of squares) for up to 4 rows, per wave
+  float m[NS], l[NS];    // attention: per-wave max and sum
+  int tab[NWK][4][8];    // per worker and phase: the block geometry (see worker_table)
+};
+
+// Fields of a worker's phase-table entry.
+enum { T_CNT = 0, T_BASE = 1, T_BYTES = 2, T_K = 3, T_SPER = 4, T_RL0 = 5, T_KS0 = 6 };
+
+__device__ __forceinline__ uint32_t lds_ld(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void raise_abort(Ctl& c, uint32_t* sync) {
+  lds_st(&c.abort, 1u);
+  __hip_atomic_store(sync + kSyncError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin until pred() holds; false on this workgroup's abort, the grid error flag or a timeout
+// (which raises both). Only lane 0 of the wave polls (the other lanes would only add LDS traffic
+// that the workers' activation reads queue behind); the outcome is broadcast to the wave.
+template <typename Pred>
+__device__ __forceinline__ bool spin_until(Ctl& c, const StackArgs& a, Pred pred) {
+  int ok = 1;
+  if (__lane_id() == 0 && !pred()) {
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+      __builtin_amdgcn_s_sleep(2);
+      if (pred()) break;
+      if (lds_ld(&c.abort) != 0u) {
+        ok = 0;
+        break;
+      }
+      if (wall_clock64() - t0 > a.timeout_ticks ||
+          __hip_atomic_load(a.sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        raise_abort(c, a.sync);
+        ok = 0;
+        break;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+  return __builtin_amdgcn_readfirstlane(ok) != 0;
+}
+
+// The workers' wait: LDS only (a global load here would also wait for the whole weight ring, as
+// loads complete in order); grid errors reach a worker through the abort word the sync waves set.
+template <typename Pred>
+__device__ __forceinline__ bool worker_spin(Ctl& c, const StackArgs& a, Pred pred) {
+  int ok = 1;
+  if (__lane_id() == 0 && !pred()) {
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+      __builtin_amdgcn_s_sleep(1);
+      if (pred()) break;
+      if (lds_ld(&c.abort) != 0u) {
+        ok = 0;
+        break;
+      }
+      if (wall_clock64() - t0 > a.timeout_ticks) {
+        raise_abort(c, a.sync);
+        ok = 0;
+        break;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+  return __builtin_amdgcn_readfirstlane(ok) != 0;
+}
+
+// Barrier of the NS sync waves only (the workers never join it). `sb` counts these barriers.
+__device__ __forceinline__ bool sync_bar(Ctl& c, const StackArgs& a, uint32_t& sb, int st) {
+  ++sb;
+  wait_lgkm0();
+  if ((st & 63) == 0) __hip_atomic_fetch_add(&c.sbar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const uint32_t target = sb * (uint32_t)NS;
+  const bool ok = spin_until(c, a, [&] { return lds_ld(&c.sbar) >= target; });
+  asm volatile("" ::: "memory");
+  return ok;
 }
 
 // ------------------------------------------------------------------ grid barrier
 // Arrive at barrier `epoch` (1, 2, ...): one atomic add per workgroup on its group's counter; the
-// last of a group adds to the top counter; the last top arrival publishes the epoch. The caller
-// has made its own stores complete (vmcnt) before this.
-__device__ __forceinline__ void grid_arrive(uint32_t* sync, uint32_t epoch, int g, int G, int tid) {
-  lds_barrier();
-  if (tid == 0) {
-    const int ng = G < kSyncGroups ? G : kSyncGroups;
-    const int gi = g % ng;
-    const uint32_t members = (uint32_t)((G - gi + ng - 1) / ng);
-    const uint32_t old = __hip_atomic_fetch_add(sync + kSyncSub + gi * kSyncLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == epoch * members - 1u) {
-      const uint32_t top = __hip_atomic_fetch_add(sync + kSyncTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (top == epoch * (uint32_t)ng - 1u) __hip_atomic_store(sync + kSyncFlag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+// last of a group adds to the top counter; the last top arrival publishes the epoch. Then wait for
+// the release. Called by one thread after every sync wave's stores have completed.
+__device__ __forceinline__ bool grid_arrive_wait(Ctl& c, const StackArgs& a, uint32_t epoch, int g) {
+  uint32_t* sync = a.sync;
+  const int G = a.G;
+  const int ng = G < kSyncGroups ? G : kSyncGroups;
+  const int gi = g % ng;
+  const uint32_t members = (uint32_t)((G - gi + ng - 1) / ng);
+  const uint32_t old = __hip_atomic_fetch_add(sync + kSyncSub + gi * kSyncLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old == epoch * members - 1u) {
+    const uint32_t top = __hip_atomic_fetch_add(sync + kSyncTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (top == epoch * (uint32_t)ng - 1u) __hip_atomic_store(sync + kSyncFlag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  const uint64_t t0 = wall_clock64();
+  while (__hip_atomic_load(sync + kSyncFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch) {
+    if (__hip_atomic_load(sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+        lds_ld(&c.abort) != 0u || wall_clock64() - t0 > a.timeout_ticks) {
+      raise_abort(c, sync);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return true;
 }
 
-// Wait until barrier `epoch` is released; false (for the whole workgroup) on timeout or a raised
-// error flag.
-__device__ __forceinline__ bool grid_wait(uint32_t* sync, uint32_t epoch, uint64_t timeout, int* s_flag, int tid) {
-  if (tid == 0) {
-    int ok = 1;
-    const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(sync + kSyncFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch) {
-      if (__hip_atomic_load(sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
-          wall_clock64() - t0 > timeout) {
-        __hip_atomic_store(sync + kSyncError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    *s_flag = ok;
-  }
-  lds_barrier();
-  return *s_flag != 0;
-}
-
-// ------------------------------------------------------------------ weight tiles
-// A tile is rows [r0, r0+nr) of a row-major [N][K] matrix: one contiguous range of nr*K elements,
-// cut into slices of 64*E elements. K is a multiple of the slice, so slice s of the tile starts
-// at element r0*K + s*64E and lies in tile row s / (K/64E). Wave w owns the contiguous block of
-// slices [w*M, min(T, (w+1)*M)), M = ceil(T/NW), and holds up to MaxSlices<WT> of them in
-// registers at a time (one "round").
-template <typename WT> struct WRegs {
-  static constexpr int N = MaxSlices<WT>::value;
-  // loads one round issues: the slices, plus their scales for int8
-  static constexpr int kLoads = sizeof(WT) == 1 ? 2 * N : N;
-  u32x4 w[N];
-  float sc[N];
+// ------------------------------------------------------------------ row tiles
+// Phase ph (0 QKV, 1 O, 2 FF1, 3 FF2) of workgroup g: rows [r0, r0+nr) of the [N][K] matrix, one
+// contiguous range of nr*K elements cut into slices of SL elements (K is a multiple of SL), so
+// slice s lies in tile row s / (K/SL). Worker w owns the contiguous block [s0, s0+cnt).
+struct Geo {
+  int N, K, r0, nr, s0, cnt;
 };
 
-struct Block {
-  int s0, cnt;
-};
-__device__ __forceinline__ Block wave_block(int T, int wave) {
-  const int M = (T + NW - 1) / NW;
-  const int s0 = wave * M;
-  const int e = min(T, s0 + M);
-  return Block{s0, e > s0 ? e - s0 : 0};
+__device__ __forceinline__ Geo phase_geo(const StackArgs& a, int SL, int g, int w, int ph) {
+  const int H = a.H, F = a.F, G = a.G;
+  Geo p;
+  p.N = ph == 0 ? 3 * H : (ph == 2 ? F : H);
+  p.K = ph == 3 ? F : H;
+  const int rows = (p.N + G - 1) / G;
+  p.r0 = min(p.N, g * rows);
+  p.nr = min(p.N, p.r0 + rows) - p.r0;
+  const int T = p.nr * (p.K / SL);
+  const int M = (T + NWK - 1) / NWK;
+  p.s0 = min(T, w * M);
+  p.cnt = min(T, p.s0 + M) - p.s0;
+  return p;
 }
 
-// Issue exactly WRegs<WT>::kLoads loads: slices [s, s + n) of the tile (n <= N) into R, and
-// out-of-range loads (which return zero and touch no memory) for the rest, so that the number of
-// loads in flight after this call is known at compile time. Buffer loads keep one per-lane offset
-// register for all of them, and the descriptor's size bounds every access to the matrix.
-template <typename WT>
-__device__ __forceinline__ void issue_slices(WRegs<WT>& R, const WT* __restrict__ W, const half_t* __restrict__ S,
-                                             int N, int K, int group, int r0, int s, int n, int lane) {
-  constexpr int E = WTraits<WT>::E, SL = kWave * E;
-  const rsrc_t rw = make_rsrc(W, (uint32_t)((size_t)N * K * sizeof(WT)));
-  const uint32_t first = (uint32_t)((size_t)r0 * K + (size_t)s * SL);  // element index of slice s
-  const uint32_t voff = (uint32_t)(lane * E * sizeof(WT));
-  // int8 scales (unused otherwise): fp16 [N][K/group], the lane's group at (lane*E/group)
-  const rsrc_t rs = make_rsrc(S, sizeof(WT) == 1 ? (uint32_t)((size_t)N * (K / group) * 2) : 0u);
-  const uint32_t svoff = sizeof(WT) == 1 ? (uint32_t)((lane * E / group) * 2) : 0u;
-#pragma unroll
-  for (int i = 0; i < WRegs<WT>::N; ++i) {
-    const uint32_t e0 = first + (uint32_t)(i * SL);
-    const bool in = i < n;
-    R.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff, in ? e0 * (uint32_t)sizeof(WT) : kOutOfRange, kAuxStream);
-    if constexpr (sizeof(WT) == 1) {
-      const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rs, svoff, in ? (e0 / group) * 2 : kOutOfRange, 0);
-      R.sc[i] = (float)__builtin_bit_cast(half_t, h);
-    }
-  }
+__device__ __forceinline__ const void* phase_w(const StackLayer& L, int ph) {
+  return ph == 0 ? L.w_qkv : ph == 1 ? L.w_o : ph == 2 ? L.w_ff1 : L.w_ff2;
+}
+__device__ __forceinline__ const void* phase_s(const StackLayer& L, int ph) {
+  return ph == 0 ? L.s_qkv : ph == 1 ? L.s_o : ph == 2 ? L.s_ff1 : L.s_ff2;
 }
 
-// Round 0 of this wave's block. Always issues WRegs<WT>::kLoads loads (an empty tile gets only
-// out-of-range ones).
-template <typename WT>
-__device__ __forceinline__ void prefetch_tile(WRegs<WT>& R, const WT* W, const half_t* S, int N, int K, int group,
-                                              int r0, int nr, int wave, int lane) {
-  constexpr int SL = kWave * WTraits<WT>::E;
-  const Block bl = wave_block(nr > 0 ? nr * (K / SL) : 0, wave);
-  issue_slices<WT>(R, W, S, N, K, group, r0, bl.s0, min(bl.cnt, WRegs<WT>::N), lane);
-}
-
+// ------------------------------------------------------------------ worker waves
 template <int BM>
-__device__ __forceinline__ void flush_rows(float (&acc)[BM], float* slots, int rl, int wave, int lane) {
+__device__ __forceinline__ void flush_rows(float (&acc)[BM], float* slots, int rl, int w, int lane) {
 #pragma unroll
   for (int b = 0; b < BM; ++b) {
-    const float v = wave_sum(acc[b]);
-    if (lane == 0) slots[(rl * NW + wave) * BM + b] = v;
+    const float v = wave_sum_dpp(acc[b]);
+    if (lane == 0) slots[(rl * NWK + w) * BM + b] = v;
     acc[b] = 0.f;
   }
 }
 
-// Row sums of the tile into slots[row][wave][b] (round 0 must already be in R; later rounds are
-// loaded here). act holds BM staged rows of K elements.
+// Lane p (0..3) of worker w fills the table entry of phase p: slice count, byte offset of the
+// block's first slice in the matrix, matrix bytes, K, slices per row, first row and slice-in-row.
+template <typename WT>
+__device__ __forceinline__ void worker_table(const StackArgs& a, Ctl& c, int g, int w, int lane) {
+  constexpr int SL = kWave * WTraits<WT>::E;
+  if (lane < 4) {
+    const Geo p = phase_geo(a, SL, g, w, lane);
+    int* t = c.tab[w][lane];
+    const int sper = p.K / SL;
+    t[T_CNT] = p.cnt;
+    t[T_BASE] = (int)(((size_t)p.r0 * p.K + (size_t)p.s0 * SL) * sizeof(WT));
+    t[T_BYTES] = (int)((size_t)p.N * p.K * sizeof(WT));
+    t[T_K] = p.K;
+    t[T_SPER] = sper;
+    t[T_RL0] = p.s0 / sper;
+    t[T_KS0] = p.s0 - (p.s0 / sper) * sper;
+  }
+  wait_lgkm0();
+}
+
+__device__ __forceinline__ int tab_ld(const Ctl& c, int w, int ph, int f) {
+  return __builtin_amdgcn_readfirstlane(c.tab[w][ph][f]);
+}
+
+// Weight-matrix pointer of (layer, phase) from the LDS table, made wave-uniform.
+__device__ __forceinline__ const void* wtab_ld(const uint64_t* wtab, int l, int ph) {
+  const uint64_t u = wtab[l * 4 + ph];
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+
 template <typename WT, int BM>
-__device__ __forceinline__ void gemv_tile(WRegs<WT>& R, const WT* __restrict__ W, const half_t* __restrict__ S,
-                                          int N, int K, int group, int r0, int nr,
-                                          const typename WTraits<WT>::LT* act, float* slots, int wave, int lane) {
+__device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typename WTraits<WT>::LT* act, float* slots,
+                                       const half_t* scl, const uint64_t* wtab, int g, int w, int lane) {
   typedef typename WTraits<WT>::LT LT;
   constexpr int E = WTraits<WT>::E, SL = kWave * E;
-  const int Sper = K / SL;
-  const Block bl = wave_block(nr * Sper, wave);
-  if (bl.cnt <= 0) return;
+  constexpr int kRing = Ring<WT, BM>::value;
+  constexpr uint32_t SLB = (uint32_t)(SL * sizeof(WT));  // bytes of one slice
+  const int L = a.n_layers;
+  worker_table<WT>(a, c, g, w, lane);
+  const int per_layer = tab_ld(c, w, 0, T_CNT) + tab_ld(c, w, 1, T_CNT) + tab_ld(c, w, 2, T_CNT) + tab_ld(c, w, 3, T_CNT);
+  const int total = L * per_layer;
+
+  // issue cursor: the next slice to load (layer il, phase iph, slice is of icnt)
+  int il = 0, iph = 0, is = 0, icnt = tab_ld(c, w, 0, T_CNT);
+  while (il < L && icnt == 0) {
+    if (++iph == 4) {
+      iph = 0;
+      ++il;
+    }
+    icnt = tab_ld(c, w, iph, T_CNT);
+  }
+  const void* iw = wtab_ld(wtab, il < L ? il : 0, il < L ? iph : 0);
+  uint32_t ibytes = (uint32_t)tab_ld(c, w, iph, T_BYTES);
+  uint32_t ioff = (uint32_t)tab_ld(c, w, iph, T_BASE);
+  const uint32_t voff = (uint32_t)(lane * 16);
+
+  // consume cursor: the next slice to multiply (layer cl, phase cph, slice cs of ccnt)
+  int cl = 0, cph = 0, cs = 0, ccnt = tab_ld(c, w, 0, T_CNT);
+  int K = tab_ld(c, w, 0, T_K), Sper = tab_ld(c, w, 0, T_SPER);
+  int rl = tab_ld(c, w, 0, T_RL0), ks = tab_ld(c, w, 0, T_KS0);
+  bool wait_act = true;
+  // leave phase (cl, cph) [finished or empty], publishing it, and move to the next non-empty one
+  auto c_advance = [&]() {
+    for (;;) {
+      wait_lgkm0();  // this wave's slot writes are in LDS before the flag says so
+      if (lane == 0) lds_st(&c.done[w], (uint32_t)(cl * 4 + cph + 1));
+      if (++cph == 4) {
+        cph = 0;
+        ++cl;
+      }
+      if (cl >= L) return;
+      ccnt = tab_ld(c, w, cph, T_CNT);
+      if (ccnt > 0) break;
+    }
+    cs = 0;
+    K = tab_ld(c, w, cph, T_K);
+    Sper = tab_ld(c, w, cph, T_SPER);
+    rl = tab_ld(c, w, cph, T_RL0);
+    ks = tab_ld(c, w, cph, T_KS0);
+    wait_act = true;
+  };
+  if (ccnt == 0) c_advance();
+
   float acc[BM];
 #pragma unroll
   for (int b = 0; b < BM; ++b) acc[b] = 0.f;
-  int rl = bl.s0 / Sper, ks = bl.s0 - rl * Sper;
-  constexpr int NS = WRegs<WT>::N;
-  for (int done = 0; done < bl.cnt; done += NS) {
-    const int n = min(NS, bl.cnt - done);
-    if (done > 0) issue_slices<WT>(R, W, S, N, K, group, r0, bl.s0 + done, n, lane);
+
+  // issue one load: the next slice, or an out-of-range load (reads nothing) past the end
+#define DS_ISSUE(dst)                                                                            \
+  {                                                                                              \
+    const bool live = il < L;                                                                    \
+    const rsrc_t r = make_rsrc(iw, ibytes);                                                      \
+    dst = __builtin_amdgcn_raw_buffer_load_b128(r, voff, live ? ioff : kOutOfRange, kAuxStream); \
+    ioff += SLB;                                                                                 \
+    if (live && ++is >= icnt) {                                                                  \
+      is = 0;                                                                                    \
+      do {                                                                                       \
+        if (++iph == 4) {                                                                        \
+          iph = 0;                                                                               \
+          ++il;                                                                                  \
+        }                                                                                        \
+        icnt = tab_ld(c, w, iph, T_CNT);                                                         \
+      } while (il < L && icnt == 0);                                                             \
+      if (il < L) {                                                                              \
+        iw = wtab_ld(wtab, il, iph);                                                             \
+        ibytes = (uint32_t)tab_ld(c, w, iph, T_BYTES);                                           \
+        ioff = (uint32_t)tab_ld(c, w, iph, T_BASE);                                              \
+      }                                                                                          \
+    }                                                                                            \
+  }
+
+  u32x4 ring[kRing];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (i < n) {
-        const LT* ap = act + ks * SL + lane * E;
+  for (int u = 0; u < kRing; ++u) DS_ISSUE(ring[u])
+
+  bool ok = true;
+  for (int pos = 0; pos < total && ok;) {
 #pragma unroll
-        for (int b = 0; b < BM; ++b) {
-          if constexpr (sizeof(WT) == 4) {
-            acc[b] = dot4_f32(R.w[i], *reinterpret_cast<const float4_t*>(ap + b * K), acc[b]);
-          } else if constexpr (sizeof(WT) == 2) {
-            acc[b] = dot8_f16(R.w[i], *reinterpret_cast<const u32x4*>(ap + b * K), acc[b]);
-          } else {
-            acc[b] = fmaf(dot16_i8(R.w[i], *reinterpret_cast<const u32x4*>(ap + b * K),
-                                   *reinterpret_cast<const u32x4*>(ap + b * K + 8)),
-                          R.sc[i], acc[b]);
+    for (int u = 0; u < kRing; ++u) {
+      if (pos < total && ok) {
+        // the cursor is wave-uniform; say so, so that its bookkeeping stays in scalar registers
+        ks = __builtin_amdgcn_readfirstlane(ks);
+        rl = __builtin_amdgcn_readfirstlane(rl);
+        cs = __builtin_amdgcn_readfirstlane(cs);
+        wait_vm_at_most<kRing - 1>();  // exactly kRing loads are in flight: the oldest has landed
+        if (wait_act) {
+          const uint32_t need = (uint32_t)(cl * 4 + cph + 1);
+          ok = worker_spin(c, a, [&] { return lds_ld(&c.act_ready) >= need; });
+          wait_act = false;
+        }
+        if (ok) {
+          const LT* ap = act + ks * SL + lane * E;
+          float sc = 1.f;
+          if constexpr (sizeof(WT) == 1) sc = (float)scl[rl * (K / a.group) + (ks * SL + lane * E) / a.group];
+#pragma unroll
+          for (int b = 0; b < BM; ++b) {
+            if constexpr (sizeof(WT) == 4) {
+              acc[b] = dot4_f32(ring[u], *reinterpret_cast<const float4_t*>(ap + b * K), acc[b]);
+            } else if constexpr (sizeof(WT) == 2) {
+              acc[b] = dot8_f16(ring[u], *reinterpret_cast<const u32x4*>(ap + b * K), acc[b]);
+            } else {
+              acc[b] = fmaf(dot16_i8(ring[u], *reinterpret_cast<const u32x4*>(ap + b * K),
+                                     *reinterpret_cast<const u32x4*>(ap + b * K + 8)),
+                            sc, acc[b]);
+            }
+          }
+          if (++ks == Sper) {
+            flush_rows<BM>(acc, slots, rl, w, lane);
+            ks = 0;
+            ++rl;
+          }
+          if (++cs == ccnt) {
+            if (ks != 0) flush_rows<BM>(acc, slots, rl, w, lane);
+            c_advance();
           }
         }
-        if (++ks == Sper) {
-          flush_rows<BM>(acc, slots, rl, wave, lane);
-          ks = 0;
-          ++rl;
-        }
+        ++pos;
       }
+      DS_ISSUE(ring[u])
     }
   }
-  if (ks != 0) flush_rows<BM>(acc, slots, rl, wave, lane);
+#undef DS_ISSUE
+  wait_vm_at_most<0>();
 }
 
-// ------------------------------------------------------------------ activation staging
+// ------------------------------------------------------------------ sync waves: staging
 constexpr int kStageUnroll = 4;  // 16-byte loads a thread has in flight while staging
 
 // Copy B rows of K elements of type IT (written by other workgroups: coherent loads) into LDS as
 // LT, zero-filling rows B..BM-1.
 template <typename IT, typename LT, int BM>
-__device__ __forceinline__ void stage_plain(const void* in, int B, int K, LT* act, int tid) {
+__device__ __forceinline__ void stage_plain(const void* in, int B, int K, LT* act, int st) {
   constexpr int V = 16 / (int)sizeof(IT);
   const rsrc_t r = make_rsrc(in, (uint32_t)(B * K * sizeof(IT)));
   const int nvec = BM * K / V;
-  for (int j0 = tid; j0 < nvec; j0 += kStackThreads * kStageUnroll) {
+  for (int j0 = st; j0 < nvec; j0 += NT * kStageUnroll) {
     u32x4 raw[kStageUnroll];
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
-      const int j = j0 + u * kStackThreads;
-      const uint32_t off = (uint32_t)(j * V * sizeof(IT));
-      raw[u] = coh_load16(r, j < nvec ? off : kOutOfRange);  // rows past B are out of range: zero
+      const int j = j0 + u * NT;
+      raw[u] = coh_load16(r, j < nvec ? (uint32_t)(j * 16) : kOutOfRange);  // rows past B: zero
     }
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
-      const int j = j0 + u * kStackThreads;
+      const int j = j0 + u * NT;
       if (j >= nvec) break;
       if constexpr (sizeof(IT) == sizeof(LT)) {
         *reinterpret_cast<u32x4*>(act + j * V) = raw[u];
@@ -290,146 +461,166 @@ __device__ __forceinline__ void stage_plain(const void* in, int B, int K, LT* ac
   }
 }
 
-// LayerNorm B rows (biased variance, two passes) into LDS as LT. The raw rows are first copied
-// to `raw` (BM*K floats of LDS) so that both passes read LDS, not global memory.
+// LayerNorm B rows (biased variance) into LDS as LT. gamma and beta (this layer's, in AT) are
+// loaded as 16-byte vectors before the rows, so their latency hides under the rows' loads, and land
+// in LDS next to the fp32 copy of the rows (`raw`); then one reduction of the shifted sums of all
+// rows and the normalized rows.
 template <typename IT, typename LT, typename AT, int BM>
-__device__ __forceinline__ void stage_ln(const void* in, int B, int K, const AT* __restrict__ g,
-                                         const AT* __restrict__ beta, float eps, LT* act, float* raw, float2_t* red2,
-                                         int tid) {
+__device__ __forceinline__ bool stage_ln(Ctl& c, const StackArgs& a, uint32_t& sb, const void* in, int B, int K,
+                                         const AT* __restrict__ gam, const AT* __restrict__ beta, LT* act, float* raw,
+                                         AT* gb, int st) {
   constexpr int V = 16 / (int)sizeof(IT);
-  const rsrc_t r = make_rsrc(in, (uint32_t)(B * K * sizeof(IT)));
-  const int nvec = B * K / V;
-  for (int j0 = tid; j0 < nvec; j0 += kStackThreads * kStageUnroll) {
-    u32x4 v[kStageUnroll];
+  constexpr int VG = 16 / (int)sizeof(AT);
+  constexpr int kGB = 2;  // gamma/beta vectors per thread issued ahead of the rows
+  const int ngv = K / VG;
+  {
+    const rsrc_t rg = make_rsrc(gam, (uint32_t)(K * sizeof(AT))), rb = make_rsrc(beta, (uint32_t)(K * sizeof(AT)));
+    u32x4 gv[kGB], bv[kGB];
 #pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int j = j0 + u * kStackThreads;
-      v[u] = coh_load16(r, j < nvec ? (uint32_t)(j * 16) : kOutOfRange);
+    for (int u = 0; u < kGB; ++u) {
+      const int j = st + u * NT;
+      const uint32_t off = j < ngv ? (uint32_t)(j * 16) : kOutOfRange;
+      gv[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
+      bv[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
     }
+    const rsrc_t r = make_rsrc(in, (uint32_t)(B * K * sizeof(IT)));
+    const int nvec = B * K / V;
+    for (int j0 = st; j0 < nvec; j0 += NT * kStageUnroll) {
+      u32x4 v[kStageUnroll];
 #pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int j = j0 + u * kStackThreads;
-      if (j >= nvec) break;
-      if constexpr (sizeof(IT) == 4) {
-        *reinterpret_cast<u32x4*>(raw + j * V) = v[u];
-      } else {
-        const uint32_t ww[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      for (int u = 0; u < kStageUnroll; ++u) {
+        const int j = j0 + u * NT;
+        v[u] = coh_load16(r, j < nvec ? (uint32_t)(j * 16) : kOutOfRange);
+      }
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const half2_t p = as_half2(ww[h]);
-          raw[j * V + 2 * h] = (float)p.x;
-          raw[j * V + 2 * h + 1] = (float)p.y;
+      for (int u = 0; u < kStageUnroll; ++u) {
+        const int j = j0 + u * NT;
+        if (j >= nvec) break;
+        if constexpr (sizeof(IT) == 4) {
+          *reinterpret_cast<u32x4*>(raw + j * V) = v[u];
+        } else {
+          const uint32_t ww[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const half2_t p = as_half2(ww[h]);
+            raw[j * V + 2 * h] = (float)p.x;
+            raw[j * V + 2 * h + 1] = (float)p.y;
+          }
         }
       }
     }
+#pragma unroll
+    for (int u = 0; u < kGB; ++u) {
+      const int j = st + u * NT;
+      if (j < ngv) {
+        *reinterpret_cast<u32x4*>(gb + j * VG) = gv[u];
+        *reinterpret_cast<u32x4*>(gb + K + j * VG) = bv[u];
+      }
+    }
+    for (int j = st + kGB * NT; j < ngv; j += NT) {  // rows longer than kGB*NT vectors
+      *reinterpret_cast<u32x4*>(gb + j * VG) = __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(j * 16), 0, 0);
+      *reinterpret_cast<u32x4*>(gb + K + j * VG) = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(j * 16), 0, 0);
+    }
   }
-  lds_barrier();
+  if (!sync_bar(c, a, sb, st)) return false;
+  // sums of d = x - x[0] and d^2 per row: var = (sum d^2 - (sum d)^2 / K) / K; shifting by an
+  // element of the row keeps the subtraction well conditioned
+  float s1[BM], s2[BM];
+#pragma unroll
+  for (int b = 0; b < BM; ++b) {
+    s1[b] = 0.f;
+    s2[b] = 0.f;
+    if (b < B) {
+      const float* xr = raw + b * K;
+      const float c0 = xr[0];
+      for (int k = st; k < K; k += NT) {
+        const float d = xr[k] - c0;
+        s1[b] += d;
+        s2[b] += d * d;
+      }
+    }
+    s1[b] = wave_sum(s1[b]);
+    s2[b] = wave_sum(s2[b]);
+  }
+  if ((st & 63) == 0) {
+#pragma unroll
+    for (int b = 0; b < BM; ++b) {
+      c.red[st >> 6][2 * b] = s1[b];
+      c.red[st >> 6][2 * b + 1] = s2[b];
+    }
+  }
+  if (!sync_bar(c, a, sb, st)) return false;
 #pragma unroll
   for (int b = 0; b < BM; ++b) {
     if (b >= B) {
-      for (int k = tid; k < K; k += kStackThreads) act[b * K + k] = (LT)0.f;
+      for (int k = st; k < K; k += NT) act[b * K + k] = (LT)0.f;
       continue;
     }
-    // one block reduction of the sums of d = x - x[0] and d^2: var = (sum d^2 - (sum d)^2 / K) / K;
-    // shifting by an element of the row keeps the subtraction well conditioned
-    const float* xr = raw + b * K;
-    const float c0 = xr[0];
-    float s1 = 0.f, s2 = 0.f;
-    for (int k = tid; k < K; k += kStackThreads) {
-      const float d = xr[k] - c0;
-      s1 += d;
-      s2 += d * d;
+    float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NS; ++wv) {
+      t1 += c.red[wv][2 * b];
+      t2 += c.red[wv][2 * b + 1];
     }
-    float2_t tot = block_sum2(float2_t{s1, s2}, red2, tid);
-    const float dm = tot.x / K;
-    const float mean = c0 + dm;
-    const float var = fmaxf(tot.y / K - dm * dm, 0.f);
-    const float rstd = rsqrtf(var + eps);
-    for (int k = tid; k < K; k += kStackThreads)
-      act[b * K + k] = (LT)((xr[k] - mean) * rstd * (float)g[k] + (float)beta[k]);
+    const float* xr = raw + b * K;
+    const float dm = t1 / K;
+    const float mean = xr[0] + dm;
+    const float rstd = rsqrtf(fmaxf(t2 / K - dm * dm, 0.f) + a.eps);
+    for (int k = st; k < K; k += NT) act[b * K + k] = (LT)((xr[k] - mean) * rstd * (float)gb[k] + (float)gb[K + k]);
   }
+  return true;
 }
 
-// ------------------------------------------------------------------ attention work items
+// int8: the fp16 scales of the phase's row tile, [nr][K/group], into LDS.
+__device__ __forceinline__ void stage_scales(const void* s, int r0, int nr, int K, int group, half_t* scl, int st) {
+  const int n = nr * (K / group);
+  const half_t* src = static_cast<const half_t*>(s) + (size_t)r0 * (K / group);
+  for (int i = st; i < n; i += NT) scl[i] = src[i];
+}
+
+// ------------------------------------------------------------------ sync waves: attention
 // An item is (sequence b, head j, chunk c of kStackChunk cache rows). Lanes split a row into
-// 16-byte pieces (LPK lanes per row), a wave covers KPI rows per load, NW waves cover NW*KPI.
+// 16-byte pieces (LPK lanes per row), a wave covers KPI rows per load, NS waves cover NS*KPI.
 template <typename AT, int D> struct AttnShape {
   static constexpr int EK = 16 / (int)sizeof(AT);
   static constexpr int LPK = D / EK;
   static constexpr int KPI = kWave / LPK;
-  static constexpr int NIT = (kStackChunk + NW * KPI - 1) / (NW * KPI);
+  static constexpr int NIT = (kStackChunk + NS * KPI - 1) / (NS * KPI);
 };
-
-template <typename AT, int D> struct AttnRegs {
-  u32x4 k[AttnShape<AT, D>::NIT], v[AttnShape<AT, D>::NIT];
-  static constexpr int kLoads = 2 * AttnShape<AT, D>::NIT;
-};
-
-__device__ __forceinline__ void item_coords(const StackArgs& a, int item, int& b, int& j, int& c) {
-  c = item % a.nchunk;
-  j = (item / a.nchunk) % a.nh;
-  b = item / (a.nchunk * a.nh);
-}
-
-// Issue exactly AttnRegs::kLoads loads: the item's past rows (before the new one, written by
-// earlier launches); rows outside the item or not yet filled load as zero (out of range).
-template <typename AT, int D>
-__device__ __forceinline__ void attn_prefetch(AttnRegs<AT, D>& A, const StackLayer& L, const StackArgs& a, int item,
-                                              int tid) {
-  typedef AttnShape<AT, D> S;
-  const int nitems = a.B * a.nh * a.nchunk;
-  int b = 0, j = 0, c = 0;
-  if (item < nitems) item_coords(a, item, b, j, c);
-  const int len = item < nitems ? L.d_len[b] : 0;
-  const int wave = tid >> 6, lane = tid & 63;
-  const uint32_t bytes = (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(AT));
-  const rsrc_t rk = make_rsrc(L.k, bytes), rv = make_rsrc(L.v, bytes);
-  const size_t head = (((size_t)b * a.nh + j) * a.cap) * D;
-  const int e0 = (lane % S::LPK) * S::EK;
-#pragma unroll
-  for (int it = 0; it < S::NIT; ++it) {
-    const int key = c * kStackChunk + (it * NW + wave) * S::KPI + lane / S::LPK;
-    const bool past = item < nitems && key < len && key < a.cap && key < (c + 1) * kStackChunk;
-    const uint32_t off = past ? (uint32_t)((head + (size_t)key * D + e0) * sizeof(AT)) : kOutOfRange;
-    A.k[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-    A.v[it] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-  }
-}
 
 // One item: scores of q against the chunk's rows, wave-reduced max and sum, the exp-weighted V
 // sum; the partial (max, sum, acc[D]) goes to the workspace, and the workgroup that completes the
 // last chunk of a (sequence, head) merges the partials into ctx (log-sum-exp).
 template <typename AT, int D>
-__device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& L, const StackArgs& a, int item,
-                                          bool prefetched, float* s_m, float* s_l, float* s_acc, float* s_part,
-                                          int* s_flag, int tid) {
+__device__ __forceinline__ bool attn_item(Ctl& c, const StackArgs& a, uint32_t& sb, const StackLayer& L, int item, float* s_acc,
+                          float* s_part, int st) {
   typedef AttnShape<AT, D> S;
   constexpr int EK = S::EK, LPK = S::LPK, KPI = S::KPI, NIT = S::NIT;
   const float kNeg = -1e30f;
-  int b, j, c;
-  item_coords(a, item, b, j, c);
+  const int cc = item % a.nchunk;
+  const int j = (item / a.nchunk) % a.nh;
+  const int b = item / (a.nchunk * a.nh);
   const int len = L.d_len[b];
   int nkeys = len + 1;
   if (nkeys > a.cap) nkeys = a.cap;
   const int nvalid = (nkeys + kStackChunk - 1) / kStackChunk;
-  if (c >= nvalid) return;
-  const int wave = tid >> 6, lane = tid & 63;
+  if (cc >= nvalid) return true;
+  const int wave = st >> 6, lane = st & 63;
   const int H = a.nh * D;
   const size_t head = (((size_t)b * a.nh + j) * a.cap) * D;
   const uint32_t bytes = (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(AT));
   const rsrc_t rk = make_rsrc(L.k, bytes), rv = make_rsrc(L.v, bytes);
   const int e0 = (lane % LPK) * EK;
-
-  if (!prefetched) attn_prefetch<AT, D>(A, L, a, item, tid);
-  // the new row (position len) was written by the QKV phase of this launch: coherent loads
+  // rows of the chunk; the new row (position len) was written by the QKV phase of this launch, so
+  // every row is read with coherent loads
+  u32x4 kr[NIT], vr[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int key = c * kStackChunk + (it * NW + wave) * KPI + lane / LPK;
-    if (key == len && key < a.cap) {
-      const uint32_t off = (uint32_t)((head + (size_t)key * D + e0) * sizeof(AT));
-      A.k[it] = coh_load16(rk, off);
-      A.v[it] = coh_load16(rv, off);
-    }
+    const int key = cc * kStackChunk + (it * NS + wave) * KPI + lane / LPK;
+    const bool in = key < nkeys && key < (cc + 1) * kStackChunk;
+    const uint32_t off = in ? (uint32_t)((head + (size_t)key * D + e0) * sizeof(AT)) : kOutOfRange;
+    kr[it] = coh_load16(rk, off);
+    vr[it] = coh_load16(rv, off);
   }
   const rsrc_t rq = make_rsrc(a.q, (uint32_t)(a.B * H * 4));
   const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d): scores feed exp2
@@ -442,13 +633,13 @@ __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& 
   float m = kNeg;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int key = c * kStackChunk + (it * NW + wave) * KPI + lane / LPK;
-    valid[it] = key < nkeys && key < (c + 1) * kStackChunk;
+    const int key = cc * kStackChunk + (it * NS + wave) * KPI + lane / LPK;
+    valid[it] = key < nkeys && key < (cc + 1) * kStackChunk;
     float p = 0.f;
     if constexpr (sizeof(AT) == 4) {
-      p = qv[0] * as_f32(A.k[it].x) + qv[1] * as_f32(A.k[it].y) + qv[2] * as_f32(A.k[it].z) + qv[3] * as_f32(A.k[it].w);
+      p = qv[0] * as_f32(kr[it].x) + qv[1] * as_f32(kr[it].y) + qv[2] * as_f32(kr[it].z) + qv[3] * as_f32(kr[it].w);
     } else {
-      const uint32_t wv[4] = {A.k[it].x, A.k[it].y, A.k[it].z, A.k[it].w};
+      const uint32_t wv[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const half2_t kk = as_half2(wv[h]);
@@ -468,12 +659,12 @@ __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& 
     const float p = valid[it] ? exp2f(sc[it] - m) : 0.f;
     l += p;
     if constexpr (sizeof(AT) == 4) {
-      acc[0] += p * as_f32(A.v[it].x);
-      acc[1] += p * as_f32(A.v[it].y);
-      acc[2] += p * as_f32(A.v[it].z);
-      acc[3] += p * as_f32(A.v[it].w);
+      acc[0] += p * as_f32(vr[it].x);
+      acc[1] += p * as_f32(vr[it].y);
+      acc[2] += p * as_f32(vr[it].z);
+      acc[3] += p * as_f32(vr[it].w);
     } else {
-      const uint32_t wv[4] = {A.v[it].x, A.v[it].y, A.v[it].z, A.v[it].w};
+      const uint32_t wv[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const half2_t vv = as_half2(wv[h]);
@@ -488,271 +679,229 @@ __device__ __forceinline__ void attn_item(AttnRegs<AT, D>& A, const StackLayer& 
 #pragma unroll
     for (int e = 0; e < EK; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
   }
-  lds_barrier();  // LDS scratch of a previous item is free
+  if (!sync_bar(c, a, sb, st)) return false;  // the scratch of a previous item is free
   if (lane < LPK) {
 #pragma unroll
     for (int e = 0; e < EK; ++e) s_acc[wave * D + e0 + e] = acc[e];
     if (lane == 0) {
-      s_m[wave] = m;
-      s_l[wave] = l;
+      c.m[wave] = m;
+      c.l[wave] = l;
     }
   }
-  lds_barrier();
+  if (!sync_bar(c, a, sb, st)) return false;
   float M = kNeg;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w]);
-  float f[NW];
+  for (int wv = 0; wv < NS; ++wv) M = fmaxf(M, c.m[wv]);
+  float f[NS];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) f[w] = s_l[w] > 0.f ? exp2f(s_m[w] - M) : 0.f;
+  for (int wv = 0; wv < NS; ++wv) f[wv] = c.l[wv] > 0.f ? exp2f(c.m[wv] - M) : 0.f;
   const size_t pbase = ((size_t)b * a.nh + j) * a.nchunk;
   const rsrc_t rp = make_rsrc(a.part, (uint32_t)((size_t)a.B * a.nh * a.nchunk * (D + 2) * 4));
-  if (tid < D) {
+  if (st < D) {
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += f[w] * s_acc[w * D + tid];
-    coh_store4(rp, (uint32_t)(((pbase + c) * (D + 2) + 2 + tid) * 4), __builtin_bit_cast(uint32_t, v));
+    for (int wv = 0; wv < NS; ++wv) v += f[wv] * s_acc[wv * D + st];
+    coh_store4(rp, (uint32_t)(((pbase + cc) * (D + 2) + 2 + st) * 4), __builtin_bit_cast(uint32_t, v));
   }
-  if (tid == 0) {
+  if (st == 0) {
     float Ls = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) Ls += f[w] * s_l[w];
-    coh_store4(rp, (uint32_t)(((pbase + c) * (D + 2)) * 4), __builtin_bit_cast(uint32_t, M));
-    coh_store4(rp, (uint32_t)(((pbase + c) * (D + 2) + 1) * 4), __builtin_bit_cast(uint32_t, Ls));
+    for (int wv = 0; wv < NS; ++wv) Ls += f[wv] * c.l[wv];
+    coh_store4(rp, (uint32_t)(((pbase + cc) * (D + 2)) * 4), __builtin_bit_cast(uint32_t, M));
+    coh_store4(rp, (uint32_t)(((pbase + cc) * (D + 2) + 1) * 4), __builtin_bit_cast(uint32_t, Ls));
   }
   wait_vm_at_most<0>();
-  lds_barrier();
+  if (!sync_bar(c, a, sb, st)) return false;
   uint32_t* cnt = a.sync + kSyncAttn + b * a.nh + j;
-  if (tid == 0)
-    *s_flag = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nvalid - 1);
-  lds_barrier();
-  if (!*s_flag) return;
+  if (st == 0)
+    c.flag = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nvalid - 1);
+  if (!sync_bar(c, a, sb, st)) return false;
+  if (!c.flag) return true;
   // last chunk of this (sequence, head): all partials in one parallel load, then the merge
   const int nw = nvalid * (D + 2);
-  for (int i = tid; i < nw; i += kStackThreads) s_part[i] = as_f32(coh_load4(rp, (uint32_t)((pbase * (D + 2) + i) * 4)));
-  lds_barrier();
-  if (tid < D) {
+  for (int i = st; i < nw; i += NT) s_part[i] = as_f32(coh_load4(rp, (uint32_t)((pbase * (D + 2) + i) * 4)));
+  if (!sync_bar(c, a, sb, st)) return false;
+  if (st < D) {
     float MM = kNeg;
-    for (int cc = 0; cc < nvalid; ++cc) MM = fmaxf(MM, s_part[cc * (D + 2)]);
+    for (int ci = 0; ci < nvalid; ++ci) MM = fmaxf(MM, s_part[ci * (D + 2)]);
     float Lsum = 0.f, Acc = 0.f;
-    for (int cc = 0; cc < nvalid; ++cc) {
-      const float* pc = s_part + cc * (D + 2);
-      const float w = pc[1] > 0.f ? exp2f(pc[0] - MM) : 0.f;
-      Lsum += w * pc[1];
-      Acc += w * pc[2 + tid];
+    for (int ci = 0; ci < nvalid; ++ci) {
+      const float* pc = s_part + ci * (D + 2);
+      const float wgt = pc[1] > 0.f ? exp2f(pc[0] - MM) : 0.f;
+      Lsum += wgt * pc[1];
+      Acc += wgt * pc[2 + st];
     }
     const rsrc_t rc = make_rsrc(a.ctx, (uint32_t)(a.B * H * sizeof(AT)));
-    coh_st_act<AT>(rc, (uint32_t)(b * H + j * D + tid), Acc / Lsum);
+    coh_st_act<AT>(rc, (uint32_t)(b * H + j * D + st), Acc / Lsum);
   }
-  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (st == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
-}  // namespace
-
-// ------------------------------------------------------------------ the persistent kernel
+// ------------------------------------------------------------------ sync waves: the phase loop
 template <typename WT, typename AT, int BM, int D>
-__global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const StackArgs a) {
+__device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned char* smem, int g, int st_in) {
   typedef typename WTraits<WT>::LT LT;
-  constexpr int kWLoads = WRegs<WT>::kLoads;
-  constexpr int kALoads = AttnRegs<AT, D>::kLoads;
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ float2_t red2[NW];
-  __shared__ float s_m[NW], s_l[NW];
-  __shared__ int s_flag;
-  const int H = a.H, F = a.F, B = a.B, G = a.G, g = blockIdx.x;
-  const int KMAX = H > F ? H : F;
-  size_t act_bytes = (size_t)BM * KMAX * sizeof(LT);
-  const size_t ln_bytes = (size_t)BM * H * (sizeof(LT) + 4);
-  if (ln_bytes > act_bytes) act_bytes = ln_bytes;
   LT* act = reinterpret_cast<LT*>(smem);
-  float* raw = reinterpret_cast<float*>(smem + (size_t)BM * H * sizeof(LT));  // LayerNorm input rows
-  float* slots = reinterpret_cast<float*>(smem + act_bytes);
-  float* s_acc = slots;                                  // attention: NW x D floats
-  float* s_part = reinterpret_cast<float*>(smem);        // attention merge: nchunk x (D + 2) floats
+  float* raw = reinterpret_cast<float*>(smem + a.lds.raw);
+  AT* gb = reinterpret_cast<AT*>(smem + a.lds.raw + (uint32_t)BM * a.H * 4u);  // LayerNorm gamma, then beta
+  float* slots = reinterpret_cast<float*>(smem + a.lds.slots);
+  half_t* scl = reinterpret_cast<half_t*>(smem + a.lds.scales);
+  float* s_acc = reinterpret_cast<float*>(smem);                   // attention: NS x D floats
+  float* s_part = reinterpret_cast<float*>(smem) + NS * D;         // merge: nchunk x (D + 2) floats
+  const int H = a.H, F = a.F, B = a.B, G = a.G;
   // Thread indices are re-derived through an opaque copy at every phase: otherwise the compiler
   // hoists every per-thread address of every phase out of the layer loop and keeps them all live.
-  int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int st = st_in;
   auto fresh = [&]() {
-    int t = threadIdx.x;
+    int t = st_in;
     asm volatile("" : "+v"(t));
-    tid = t;
-    wave = t >> 6;
-    lane = t & 63;
+    st = t;
   };
+  uint32_t sb = 0, epoch = 0;
+  const int nitems = B * a.nh * a.nchunk;
 
-  // per-workgroup row tiles of each projection
+  // per-workgroup row tiles of each projection (the same split the workers use)
   const int rq = (3 * H + G - 1) / G, ro = (H + G - 1) / G, r1 = (F + G - 1) / G;
   const int q0 = min(3 * H, g * rq), nq = min(3 * H, q0 + rq) - q0;
   const int o0 = min(H, g * ro), no = min(H, o0 + ro) - o0;
   const int f0 = min(F, g * r1), nf = min(F, f0 + r1) - f0;
   const int y0 = o0, ny = no;
-  const int nitems = B * a.nh * a.nchunk;
 
-  WRegs<WT> R;
-  AttnRegs<AT, D> A;
-  uint32_t epoch = 0;
-  auto slot_clear = [&](int nr) {
-    for (int i = tid; i < nr * NW * BM; i += kStackThreads) slots[i] = 0.f;
-  };
   auto row_sum = [&](int rl, int b) {
-    const float* p = slots + rl * NW * BM + b;
+    const float* p = slots + rl * NWK * BM + b;
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) s += p[w * BM];
+    for (int w = 0; w < NWK; ++w) s += p[w * BM];
     return s;
   };
-  // after a phase's stores and the next prefetch: stores done, then arrive and wait
-  auto barrier = [&](auto wait_stores) -> bool {
-    wait_stores();
-    ++epoch;
-    grid_arrive(a.sync, epoch, g, G, tid);
-    return grid_wait(a.sync, epoch, a.timeout_ticks, &s_flag, tid);
+  auto clear_slots = [&](int nr) {
+    for (int i = st; i < nr * NWK * BM; i += NT) slots[i] = 0.f;
   };
-
-  {
-    const StackLayer& L0 = a.layers[0];
-    prefetch_tile<WT>(R, (const WT*)L0.w_qkv, (const half_t*)L0.s_qkv, 3 * H, H, a.group, q0, nq, wave, lane);
-  }
+  // publish the staged activation of phase `seq`, then wait for every worker to finish it
+  auto hand_over = [&](uint32_t seq) -> bool {
+    if (!sync_bar(c, a, sb, st)) return false;
+    if (st == 0) lds_st(&c.act_ready, seq + 1u);
+    bool ok = spin_until(c, a, [&] {
+      bool all = true;
+#pragma unroll
+      for (int w = 0; w < NWK; ++w) all = all && lds_ld(&c.done[w]) >= seq + 1u;
+      return all;
+    });
+    asm volatile("" ::: "memory");
+    return ok;
+  };
+  // after this phase's stores: every sync wave's stores complete, one arrival, the release
+  auto grid_barrier = [&]() -> bool {
+    wait_vm_at_most<0>();
+    if (!sync_bar(c, a, sb, st)) return false;
+    ++epoch;
+    if (st == 0) c.ok = grid_arrive_wait(c, a, epoch, g) ? 1 : 0;
+    if (!sync_bar(c, a, sb, st)) return false;
+    return c.ok != 0;
+  };
 
   for (int l = 0; l < a.n_layers; ++l) {
     const StackLayer& L = a.layers[l];
-    const void* xin = (l == 0) ? a.x : ((l & 1) ? a.ybuf0 : a.ybuf1);
-    void* yout = (l == a.n_layers - 1) ? a.y : ((l & 1) ? a.ybuf1 : a.ybuf0);
+    // layer outputs alternate between the two buffers; the pointers are selected as values (a
+    // select of two field addresses would make the compiler keep the arguments in scratch)
+    uintptr_t yb0 = reinterpret_cast<uintptr_t>(a.ybuf0), yb1 = reinterpret_cast<uintptr_t>(a.ybuf1);
+    uintptr_t xa = reinterpret_cast<uintptr_t>(a.x), ya = reinterpret_cast<uintptr_t>(a.y);
+    asm volatile("" : "+s"(yb0), "+s"(yb1), "+s"(xa), "+s"(ya));
+    const void* xin = reinterpret_cast<const void*>((l == 0) ? xa : ((l & 1) ? yb0 : yb1));
+    void* yout = reinterpret_cast<void*>((l == a.n_layers - 1) ? ya : ((l & 1) ? yb1 : yb0));
+    const uint32_t seq0 = (uint32_t)l * 4u;
 
     // ---- region 1: LN1 + QKV + bias; q -> workspace, k/v -> cache row d_len[b]
     fresh();
-    // epilogue inputs first: they travel with the staging loads instead of after the GEMV
-    float pb = 0.f, pr = 0.f;
-    int plen = 0;
-    if (tid < nq * B) {
-      const int rl = tid / B, b = tid - rl * B;
-      pb = ldp<AT>(L.b_qkv, q0 + rl);
-      plen = L.d_len[b];
-    }
-    slot_clear(nq);
-    stage_ln<AT, LT, AT, BM>(xin, B, H, (const AT*)L.ln1_g, (const AT*)L.ln1_b, a.eps, act, raw, red2, tid);
-    lds_barrier();
-    if (nq > 0) gemv_tile<WT, BM>(R, (const WT*)L.w_qkv, (const half_t*)L.s_qkv, 3 * H, H, a.group, q0, nq, act, slots, wave, lane);
-    lds_barrier();
+    clear_slots(nq);
+    if constexpr (sizeof(WT) == 1) stage_scales(L.s_qkv, q0, nq, H, a.group, scl, st);
+    if (!stage_ln<AT, LT, AT, BM>(c, a, sb, xin, B, H, (const AT*)L.ln1_g, (const AT*)L.ln1_b, act, raw, gb, st)) return;
+    if (!hand_over(seq0)) return;
     {
       const rsrc_t rqo = make_rsrc(a.q, (uint32_t)(B * H * 4));
       const uint32_t cache_bytes = (uint32_t)((size_t)B * a.nh * a.cap * D * sizeof(AT));
       const rsrc_t rk = make_rsrc(L.k, cache_bytes), rv = make_rsrc(L.v, cache_bytes);
-      for (int t = tid; t < nq * B; t += kStackThreads) {
+      for (int t = st; t < nq * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = q0 + rl;
-        const float z = row_sum(rl, b) + (t == tid ? pb : ldp<AT>(L.b_qkv, n));
+        const float z = row_sum(rl, b) + ldp<AT>(L.b_qkv, n);
         if (n < H) {
           coh_store4(rqo, (uint32_t)((b * H + n) * 4), __builtin_bit_cast(uint32_t, z));
         } else {
           const int m = n < 2 * H ? n - H : n - 2 * H, j = m / D, e = m - j * D;
-          const int pos = t == tid ? plen : L.d_len[b];
+          const int pos = L.d_len[b];
           if (pos >= 0 && pos < a.cap) coh_st_act<AT>(n < 2 * H ? rk : rv, (uint32_t)((((size_t)b * a.nh + j) * a.cap + pos) * D + e), z);
         }
       }
     }
-    asm volatile("" ::: "memory");
-    attn_prefetch<AT, D>(A, L, a, g, tid);
-    if (!barrier([] { wait_vm_at_most<kALoads>(); })) return;
+    if (!grid_barrier()) return;
 
     // ---- region 2: attention over the cache, chunk partials merged by the last chunk
     fresh();
     for (int item = g; item < nitems; item += G)
-      attn_item<AT, D>(A, L, a, item, item == g, s_m, s_l, s_acc, s_part, &s_flag, tid);
-    asm volatile("" ::: "memory");
-    prefetch_tile<WT>(R, (const WT*)L.w_o, (const half_t*)L.s_o, H, H, a.group, o0, no, wave, lane);
-    if (!barrier([] { wait_vm_at_most<kWLoads>(); })) return;
+      if (!attn_item<AT, D>(c, a, sb, L, item, s_acc, s_part, st)) return;
+    if (!grid_barrier()) return;
 
     // ---- output projection + bias + residual: x2 = x + Wo ctx + bo
     fresh();
-    {
-      const rsrc_t rx = make_rsrc(xin, (uint32_t)(B * H * sizeof(AT)));
-      if (tid < no * B) {
-        const int rl = tid / B, b = tid - rl * B;
-        pb = ldp<AT>(L.b_o, o0 + rl);
-        pr = coh_ld_act<AT>(rx, (uint32_t)(b * H + o0 + rl));
-      }
-    }
-    slot_clear(no);
-    stage_plain<AT, LT, BM>(a.ctx, B, H, act, tid);
-    lds_barrier();
-    if (no > 0) gemv_tile<WT, BM>(R, (const WT*)L.w_o, (const half_t*)L.s_o, H, H, a.group, o0, no, act, slots, wave, lane);
-    lds_barrier();
+    if (!sync_bar(c, a, sb, st)) return;  // the attention scratch (same LDS) is no longer read
+    clear_slots(no);
+    if constexpr (sizeof(WT) == 1) stage_scales(L.s_o, o0, no, H, a.group, scl, st);
+    stage_plain<AT, LT, BM>(a.ctx, B, H, act, st);
+    if (!hand_over(seq0 + 1u)) return;
     {
       const rsrc_t rx = make_rsrc(xin, (uint32_t)(B * H * sizeof(AT)));
       const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 4));
-      for (int t = tid; t < no * B; t += kStackThreads) {
+      for (int t = st; t < no * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = o0 + rl;
-        const float z = row_sum(rl, b) + (t == tid ? pb : ldp<AT>(L.b_o, n));
-        const float xr = t == tid ? pr : coh_ld_act<AT>(rx, (uint32_t)(b * H + n));
-        coh_store4(rx2, (uint32_t)((b * H + n) * 4), __builtin_bit_cast(uint32_t, xr + z));
+        const float z = row_sum(rl, b) + ldp<AT>(L.b_o, n);
+        coh_store4(rx2, (uint32_t)((b * H + n) * 4), __builtin_bit_cast(uint32_t, coh_ld_act<AT>(rx, (uint32_t)(b * H + n)) + z));
       }
     }
-    asm volatile("" ::: "memory");
-    prefetch_tile<WT>(R, (const WT*)L.w_ff1, (const half_t*)L.s_ff1, F, H, a.group, f0, nf, wave, lane);
-    if (!barrier([] { wait_vm_at_most<kWLoads>(); })) return;
+    if (!grid_barrier()) return;
 
     // ---- region 3: LN2 + FF1 + bias + GeLU
     fresh();
-    if (tid < nf * B) pb = ldp<AT>(L.b_ff1, f0 + tid / B);
-    slot_clear(nf);
-    stage_ln<float, LT, AT, BM>(a.x2, B, H, (const AT*)L.ln2_g, (const AT*)L.ln2_b, a.eps, act, raw, red2, tid);
-    lds_barrier();
-    if (nf > 0) gemv_tile<WT, BM>(R, (const WT*)L.w_ff1, (const half_t*)L.s_ff1, F, H, a.group, f0, nf, act, slots, wave, lane);
-    lds_barrier();
+    clear_slots(nf);
+    if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff1, f0, nf, H, a.group, scl, st);
+    if (!stage_ln<float, LT, AT, BM>(c, a, sb, a.x2, B, H, (const AT*)L.ln2_g, (const AT*)L.ln2_b, act, raw, gb, st)) return;
+    if (!hand_over(seq0 + 2u)) return;
     {
       const rsrc_t rf = make_rsrc(a.f, (uint32_t)(B * F * sizeof(AT)));
-      for (int t = tid; t < nf * B; t += kStackThreads) {
+      for (int t = st; t < nf * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = f0 + rl;
-        const float z = row_sum(rl, b) + (t == tid ? pb : ldp<AT>(L.b_ff1, n));
+        const float z = row_sum(rl, b) + ldp<AT>(L.b_ff1, n);
         coh_st_act<AT>(rf, (uint32_t)(b * F + n), gelu(z, a.gelu_tanh != 0));
       }
     }
-    asm volatile("" ::: "memory");
-    prefetch_tile<WT>(R, (const WT*)L.w_ff2, (const half_t*)L.s_ff2, H, F, a.group, y0, ny, wave, lane);
-    if (!barrier([] { wait_vm_at_most<kWLoads>(); })) return;
+    if (!grid_barrier()) return;
 
     // ---- region 4: FF2 + bias + residual: y = x2 + W2 f + b2
     fresh();
-    {
-      const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 4));
-      if (tid < ny * B) {
-        const int rl = tid / B, b = tid - rl * B;
-        pb = ldp<AT>(L.b_ff2, y0 + rl);
-        pr = as_f32(coh_load4(rx2, (uint32_t)((b * H + y0 + rl) * 4)));
-      }
-    }
-    slot_clear(ny);
-    stage_plain<AT, LT, BM>(a.f, B, F, act, tid);
-    lds_barrier();
-    if (ny > 0) gemv_tile<WT, BM>(R, (const WT*)L.w_ff2, (const half_t*)L.s_ff2, H, F, a.group, y0, ny, act, slots, wave, lane);
-    lds_barrier();
+    clear_slots(ny);
+    if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff2, y0, ny, F, a.group, scl, st);
+    stage_plain<AT, LT, BM>(a.f, B, F, act, st);
+    if (!hand_over(seq0 + 3u)) return;
     {
       const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 4));
       const rsrc_t ry = make_rsrc(yout, (uint32_t)(B * H * sizeof(AT)));
-      for (int t = tid; t < ny * B; t += kStackThreads) {
+      for (int t = st; t < ny * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = y0 + rl;
-        const float z = row_sum(rl, b) + (t == tid ? pb : ldp<AT>(L.b_ff2, n));
-        const float xr = t == tid ? pr : as_f32(coh_load4(rx2, (uint32_t)((b * H + n) * 4)));
-        coh_st_act<AT>(ry, (uint32_t)(b * H + n), xr + z);
+        const float z = row_sum(rl, b) + ldp<AT>(L.b_ff2, n);
+        coh_st_act<AT>(ry, (uint32_t)(b * H + n), as_f32(coh_load4(rx2, (uint32_t)((b * H + n) * 4))) + z);
       }
     }
-    asm volatile("" ::: "memory");
-    if (l + 1 < a.n_layers) {
-      const StackLayer& Ln = a.layers[l + 1];
-      prefetch_tile<WT>(R, (const WT*)Ln.w_qkv, (const half_t*)Ln.s_qkv, 3 * H, H, a.group, q0, nq, wave, lane);
-      if (!barrier([] { wait_vm_at_most<kWLoads>(); })) return;
-    } else {
-      if (!barrier([] { wait_vm_at_most<0>(); })) return;
-    }
+    if (!grid_barrier()) return;
   }
 
   // every layer has attended: advance the cache lengths, then the last workgroup out resets the
   // barrier state for the next launch
-  if (g == 0 && tid < B)
+  if (g == 0 && st < B)
     for (int l = 0; l < a.n_layers; ++l) {
       int32_t* dl = a.layers[l].d_len;
-      if (dl[tid] + 1 <= a.cap) dl[tid] += 1;
+      if (dl[st] + 1 <= a.cap) dl[st] += 1;
     }
-  if (tid == 0) {
+  if (st == 0) {
     const uint32_t out = __hip_atomic_fetch_add(a.sync + kSyncExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (out == (uint32_t)G - 1) {
       for (int i = 0; i < kSyncGroups; ++i)
@@ -764,6 +913,38 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
   }
 }
 
+}  // namespace
+
+// ------------------------------------------------------------------ the persistent kernel
+template <typename WT, typename AT, int BM, int D>
+__global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const StackArgs a) {
+  typedef typename WTraits<WT>::LT LT;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ Ctl c;
+  uint64_t* wtab = reinterpret_cast<uint64_t*>(smem + a.lds.wtab);
+  for (int i = threadIdx.x; i < a.n_layers * 4; i += kStackThreads)
+    wtab[i] = reinterpret_cast<uint64_t>(phase_w(a.layers[i >> 2], i & 3));
+  if (threadIdx.x == 0) {
+    c.act_ready = 0u;
+    for (int w = 0; w < NWK; ++w) c.done[w] = 0u;
+    c.sbar = 0u;
+    c.abort = 0u;
+    c.ok = 0;
+    c.flag = 0;
+  }
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  if (wave < NS) {
+    sync_side<WT, AT, BM, D>(a, c, smem, blockIdx.x, (int)threadIdx.x);
+    if (lds_ld(&c.abort) == 0u) return;
+    raise_abort(c, a.sync);  // a failed sync wave releases the workers
+  } else {
+    worker<WT, BM>(a, c, reinterpret_cast<const LT*>(smem), reinterpret_cast<float*>(smem + a.lds.slots),
+                   reinterpret_cast<const half_t*>(smem + a.lds.scales), wtab, blockIdx.x, wave - NS, lane);
+  }
+}
+
 // ------------------------------------------------------------------ host-side launch helpers
 int stack_rows_per_wg(int H, int F, int G) {
   int r = (3 * H + G - 1) / G;
@@ -771,20 +952,6 @@ int stack_rows_per_wg(int H, int F, int G) {
   r = max(r, (F + G - 1) / G);
   return r;
 }
-
-size_t stack_lds_bytes(Dt wdt, int B, int H, int F, int rows_per_wg) {
-  const int BM = B <= 1 ? 1 : 4;
-  const size_t lt = wdt == F32 ? 4 : 2;
-  const size_t kmax = (size_t)(H > F ? H : F);
-  size_t act = BM * kmax * lt;
-  if ((size_t)BM * H * (lt + 4) > act) act = (size_t)BM * H * (lt + 4);  // LayerNorm rows in fp32 too
-  size_t slots = (size_t)rows_per_wg * kStackWaves * BM * 4;
-  if (slots < (size_t)kStackWaves * 128 * 4) slots = (size_t)kStackWaves * 128 * 4;  // attention scratch
-  return act + slots;
-}
-
-// The attention merge stages nchunk x (head_dim + 2) floats in the activation area.
-size_t stack_merge_bytes(int nchunk, int head_dim) { return (size_t)nchunk * (head_dim + 2) * 4; }
 
 template <typename WT, typename AT, int BM, int D>
 static const void* kernel_ptr() {
@@ -814,7 +981,9 @@ hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups) {
   const void* k = pick(wdt, adt, B, 128);
   if (!k) return hipErrorInvalidValue;
   int per_cu = 0, dev = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kStackThreads, lds);
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kStackThreads, lds);
   if (e != hipSuccess) return e;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   int cus = 0;
@@ -824,12 +993,14 @@ hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups) {
   return hipSuccess;
 }
 
-hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, size_t lds, hipStream_t st) {
+hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, hipStream_t st) {
   const void* k = pick(wdt, adt, a.B, a.d);
   if (!k) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)a.lds.total);
+  if (e != hipSuccess) return e;
   StackArgs args = a;
   void* params[] = {&args};
-  return hipLaunchCooperativeKernel(k, dim3(a.G), dim3(kStackThreads), params, (unsigned)lds, st);
+  return hipLaunchCooperativeKernel(k, dim3(a.G), dim3(kStackThreads), params, (unsigned)a.lds.total, st);
 }
 
 }  // namespace ds

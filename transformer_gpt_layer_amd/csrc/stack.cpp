@@ -101,12 +101,18 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
   hipError_t e = hipGetDevice(&S->device);
   int cus = 0;
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, S->device);
+  const int wsz_i = d.weight_dtype == DS_F32 ? 4 : (d.weight_dtype == DS_F16 ? 2 : 1);
+  const int bm = max_batch <= 1 ? 1 : 4;
   int G = cus;  // one workgroup of kStackThreads per CU
   for (int iter = 0; e == hipSuccess && iter < 3; ++iter) {
-    size_t lds = ds::stack_lds_bytes(wdt, max_batch, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, G));
-    if (ds::stack_merge_bytes(S->nchunk, d.head_dim) > lds) lds = ds::stack_merge_bytes(S->nchunk, d.head_dim);
+    const ds::StackLds lay = ds::stack_lds_layout(wsz_i, bm, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, G),
+                                                  S->nchunk, d.head_dim, d.quant_group, n_layers);
+    if (lay.total > (uint32_t)ds::kStackLdsMax - 4096u) {  // the static control block takes the rest
+      delete S;
+      return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode: %u bytes of LDS per workgroup needed", lay.total);
+    }
     int fit = 0;
-    e = ds::stack_max_groups(wdt, adt, max_batch, lds, &fit);
+    e = ds::stack_max_groups(wdt, adt, max_batch, lay.total, &fit);
     if (e == hipSuccess) G = G < fit ? G : fit;
   }
   if (e != hipSuccess || G < 1) {
@@ -197,9 +203,10 @@ int ds_stack_forward_decode(ds_stack_t* S, const void* x, void* y, int32_t batch
   a.nchunk = S->nchunk;
   a.timeout_ticks = S->timeout_ticks;
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
-  size_t lds = ds::stack_lds_bytes(wdt, batch, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->G));
-  if (ds::stack_merge_bytes(S->nchunk, d.head_dim) > lds) lds = ds::stack_merge_bytes(S->nchunk, d.head_dim);
-  if (hipError_t e = ds::launch_stack_decode(wdt, adt, a, lds, reinterpret_cast<hipStream_t>(stream)))
+  const int wsz_i = d.weight_dtype == DS_F32 ? 4 : (d.weight_dtype == DS_F16 ? 2 : 1);
+  a.lds = ds::stack_lds_layout(wsz_i, batch <= 1 ? 1 : 4, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->G),
+                               S->nchunk, d.head_dim, d.quant_group, S->n_layers);
+  if (hipError_t e = ds::launch_stack_decode(wdt, adt, a, reinterpret_cast<hipStream_t>(stream)))
     return hip_err(e, "persistent decode launch");
   for (int l = 0; l < S->n_layers; ++l)
     if (int32_t* hl = S->caches[l].h_len)
