@@ -16,19 +16,24 @@ struct StackLayer {
   int32_t* d_len;
 };
 
-// sync[] layout in 32-bit words (library-owned, zero at rest). Barrier arrivals spread over
-// kSyncGroups counters, each on its own 256-byte line; the last arrival of a group bumps the top
-// counter, the last top arrival publishes the barrier's epoch in the release flag.
-constexpr int kSyncGroups = 16;
+// sync[] layout in 32-bit words (library-owned). Workgroups never wait for each other at a
+// barrier: every value that crosses workgroups is stored together with a tag naming the launch,
+// the layer and the phase that produced it, and a consumer polls until the tags it needs are
+// current. kSyncLaunch holds the launch counter (seeded per stack, advanced by the last workgroup
+// out); kSyncExit counts finished workgroups; kSyncError is raised by any wait that timed out.
 constexpr int kSyncLine = 64;
 enum {
-  kSyncSub = 0,
-  kSyncTop = kSyncGroups * kSyncLine,
-  kSyncFlag = kSyncTop + kSyncLine,
-  kSyncExit = kSyncFlag + kSyncLine,
-  kSyncError = kSyncExit + kSyncLine,
-  kSyncAttn = kSyncError + kSyncLine,  // then B*nh attention-merge counters
+  kSyncLaunch = 0,
+  kSyncExit = kSyncLine,
+  kSyncError = 2 * kSyncLine,
+  kSyncWords = 3 * kSyncLine,
 };
+
+// Tag of values produced in layer l by phase ph of launch `launch` (layer < 512, ph < 8).
+__host__ __device__ inline uint32_t stack_tag(uint32_t launch, int l, int ph) {
+  return (launch << 12) | (uint32_t)(l * 8 + ph);
+}
+enum { TAG_Q = 0, TAG_PART = 1, TAG_CTX = 2, TAG_X2 = 3, TAG_F = 4, TAG_Y = 5 };
 
 // Workgroup shape: kStackSyncWaves waves stage activations, reduce, run the epilogues, attention
 // and the grid barriers; kStackWorkers waves stream the weights and compute the row dot products.
@@ -46,6 +51,8 @@ struct StackLds {
   uint32_t slots;   // per-(row, worker, batch row) partial sums
   uint32_t scales;  // int8 scales of the current row tile
   uint32_t wtab;    // the four weight-matrix pointers of every layer (8 bytes each)
+  uint32_t res;     // this workgroup's rows of x2, then of the layer output (fp32, res_n each)
+  uint32_t res_n;
   uint32_t total;
 };
 
@@ -69,27 +76,31 @@ __host__ __device__ inline StackLds stack_lds_layout(int wsize, int bm, int H, i
   L.scales = stack_align(L.slots + (uint32_t)rows_per_wg * kStackWorkers * bm * 4u);
   const uint32_t sc = wsize == 1 ? (uint32_t)rows_per_wg * (kmax / (uint32_t)group) * 2u : 0u;
   L.wtab = stack_align(L.scales + sc);
-  L.total = stack_align(L.wtab + (uint32_t)n_layers * 4u * 8u);
+  L.res = stack_align(L.wtab + (uint32_t)n_layers * 4u * 8u);
+  L.res_n = (uint32_t)rows_per_wg * (uint32_t)bm;
+  L.total = stack_align(L.res + 2u * L.res_n * 4u);
   return L;
 }
 
+// A tagged value: the float's bits and the tag of the phase that stored it (one 8-byte store).
 struct StackArgs {
   const StackLayer* layers;
   int n_layers;
   const void* x;   // [B][H] stack input (activation type)
-  void* y;         // [B][H] stack output
+  void* y;         // [B][H] stack output (activation type)
   int B, H, nh, d, F, cap, group;
   float eps;
   int gelu_tanh;
-  // workspace
-  float* q;        // [B][H]
-  float* part;     // [B][nh][nchunk][d + 2]
-  void* ctx;       // [B][H] activation type
-  float* x2;       // [B][H]
-  void* f;         // [B][F] activation type
-  void* ybuf0;     // [B][H] activation type, layer outputs alternate between the two
-  void* ybuf1;
-  uint32_t* sync;  // kSync* words, then B*nh attention counters
+  // workspace: tagged values (8 bytes each)
+  uint2* q;        // [B][H]
+  uint2* knew;     // [B][H] the new K row of every head
+  uint2* vnew;     // [B][H]
+  uint2* part;     // [B][nh][nchunk][d + 2] attention partials (max, sum, acc[d])
+  uint2* ctx;      // [B][H]
+  uint2* x2;       // [B][H]
+  uint2* f;        // [B][F]
+  uint2* ybuf;     // [B][H] layer outputs except the last
+  uint32_t* sync;  // kSync* words
   int G;           // workgroups (all co-resident)
   int nchunk;      // attention chunks of kStackChunk rows over the capacity
   StackLds lds;

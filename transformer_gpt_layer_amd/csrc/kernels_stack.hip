@@ -108,8 +108,7 @@ struct Ctl {
   uint32_t done[NWK];    // phases each worker has finished (its partial sums are in LDS)
   uint32_t sbar;         // sync-wave barrier arrivals
   uint32_t abort;        // set when any wait of this workgroup failed
-  int ok;                // grid-barrier outcome, broadcast to the sync waves
-  int flag;              // attention: this workgroup completed a (sequence, head)
+  uint32_t launch;       // launch counter (tags of this launch)
   float red[NS][8];      // LayerNorm sums: (sum, sum of squares) for up to 4 rows, per wave
   float m[NS], l[NS];    // attention: per-wave max and sum
   int tab[NWK][4][8];    // per worker and phase: the block geometry (see worker_table)
@@ -193,31 +192,101 @@ __device__ __forceinline__ bool sync_bar(Ctl& c, const StackArgs& a, uint32_t& s
   return ok;
 }
 
-// ------------------------------------------------------------------ grid barrier
-// Arrive at barrier `epoch` (1, 2, ...): one atomic add per workgroup on its group's counter; the
-// last of a group adds to the top counter; the last top arrival publishes the epoch. Then wait for
-// the release. Called by one thread after every sync wave's stores have completed.
-__device__ __forceinline__ bool grid_arrive_wait(Ctl& c, const StackArgs& a, uint32_t epoch, int g) {
-  uint32_t* sync = a.sync;
-  const int G = a.G;
-  const int ng = G < kSyncGroups ? G : kSyncGroups;
-  const int gi = g % ng;
-  const uint32_t members = (uint32_t)((G - gi + ng - 1) / ng);
-  const uint32_t old = __hip_atomic_fetch_add(sync + kSyncSub + gi * kSyncLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (old == epoch * members - 1u) {
-    const uint32_t top = __hip_atomic_fetch_add(sync + kSyncTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (top == epoch * (uint32_t)ng - 1u) __hip_atomic_store(sync + kSyncFlag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  const uint64_t t0 = wall_clock64();
-  while (__hip_atomic_load(sync + kSyncFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch) {
-    if (__hip_atomic_load(sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
-        lds_ld(&c.abort) != 0u || wall_clock64() - t0 > a.timeout_ticks) {
-      raise_abort(c, sync);
-      return false;
+// ------------------------------------------------------------------ tagged values across workgroups
+// A value that crosses workgroups is one 8-byte store: the float's bits, then the tag of the phase
+// that produced it. Stores and loads go through sc1 (the device coherence point, past the per-XCD
+// L2s). A consumer re-reads the pairs whose tag is not yet the expected one, so workgroups never
+// meet at a barrier: each phase waits for exactly the values it reads.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void tstore(rsrc_t r, uint32_t idx, float v, uint32_t tag) {
+  const u32x2 pv = {__builtin_bit_cast(uint32_t, v), tag};
+  __builtin_amdgcn_raw_buffer_store_b64(pv, r, idx * 8u, 0, kAuxCoherent);
+}
+
+__device__ __forceinline__ bool grid_error(const StackArgs& a) {
+  return __hip_atomic_load(a.sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+}
+
+constexpr int kPollUnroll = 4;  // 16-byte loads (two tagged values each) a thread keeps in flight
+
+// Wait until the tagged values [0, n) at src all carry `tag`, handing each one once to put(i, v).
+// Threads st, st+NT, ... of the sync waves share the work.
+template <typename Put>
+__device__ __forceinline__ bool poll_range(Ctl& c, const StackArgs& a, const uint2* src, int n, uint32_t tag, int st,
+                                           Put put) {
+  const rsrc_t r = make_rsrc(src, (uint32_t)n * 8u);
+  const int nv = (n + 1) >> 1;
+  for (int j0 = st; j0 < nv; j0 += NT * kPollUnroll) {
+    bool need[kPollUnroll];
+#pragma unroll
+    for (int u = 0; u < kPollUnroll; ++u) need[u] = j0 + u * NT < nv;
+    uint64_t t0 = 0;
+    for (int round = 0;; ++round) {
+      u32x4 v[kPollUnroll];
+#pragma unroll
+      for (int u = 0; u < kPollUnroll; ++u) v[u] = coh_load16(r, need[u] ? (uint32_t)((j0 + u * NT) * 16) : kOutOfRange);
+      bool stale = false;
+#pragma unroll
+      for (int u = 0; u < kPollUnroll; ++u) {
+        if (!need[u]) continue;
+        const int i = 2 * (j0 + u * NT);
+        const bool second = i + 1 < n;
+        if (v[u].y == tag && (!second || v[u].w == tag)) {
+          put(i, as_f32(v[u].x));
+          if (second) put(i + 1, as_f32(v[u].z));
+          need[u] = false;
+        } else {
+          stale = true;
+        }
+      }
+      if (!stale) break;
+      if (round == 0) {
+        t0 = wall_clock64();
+      } else if (wall_clock64() - t0 > a.timeout_ticks || lds_ld(&c.abort) != 0u || grid_error(a)) {
+        raise_abort(c, a.sync);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
-    __builtin_amdgcn_s_sleep(2);
   }
   return true;
+}
+
+// One lane's run of `cnt` consecutive tagged values (cnt even), polled until current.
+template <int CNT>
+__device__ __forceinline__ bool poll_lane(Ctl& c, const StackArgs& a, rsrc_t r, uint32_t first, uint32_t tag,
+                                          float (&out)[CNT]) {
+  static_assert(CNT % 2 == 0, "pairs of tagged values");
+  bool need[CNT / 2];
+#pragma unroll
+  for (int u = 0; u < CNT / 2; ++u) need[u] = true;
+  uint64_t t0 = 0;
+  for (int round = 0;; ++round) {
+    bool stale = false;
+    u32x4 v[CNT / 2];
+#pragma unroll
+    for (int u = 0; u < CNT / 2; ++u) v[u] = coh_load16(r, need[u] ? (first + 2u * u) * 8u : kOutOfRange);
+#pragma unroll
+    for (int u = 0; u < CNT / 2; ++u) {
+      if (!need[u]) continue;
+      if (v[u].y == tag && v[u].w == tag) {
+        out[2 * u] = as_f32(v[u].x);
+        out[2 * u + 1] = as_f32(v[u].z);
+        need[u] = false;
+      } else {
+        stale = true;
+      }
+    }
+    if (!stale) return true;
+    if (round == 0) {
+      t0 = wall_clock64();
+    } else if (wall_clock64() - t0 > a.timeout_ticks || lds_ld(&c.abort) != 0u || grid_error(a)) {
+      raise_abort(c, a.sync);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
 
 // ------------------------------------------------------------------ row tiles
@@ -429,98 +498,38 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
 }
 
 // ------------------------------------------------------------------ sync waves: staging
-constexpr int kStageUnroll = 4;  // 16-byte loads a thread has in flight while staging
-
-// Copy B rows of K elements of type IT (written by other workgroups: coherent loads) into LDS as
-// LT, zero-filling rows B..BM-1.
-template <typename IT, typename LT, int BM>
-__device__ __forceinline__ void stage_plain(const void* in, int B, int K, LT* act, int st) {
-  constexpr int V = 16 / (int)sizeof(IT);
-  const rsrc_t r = make_rsrc(in, (uint32_t)(B * K * sizeof(IT)));
-  const int nvec = BM * K / V;
-  for (int j0 = st; j0 < nvec; j0 += NT * kStageUnroll) {
-    u32x4 raw[kStageUnroll];
-#pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int j = j0 + u * NT;
-      raw[u] = coh_load16(r, j < nvec ? (uint32_t)(j * 16) : kOutOfRange);  // rows past B: zero
-    }
-#pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int j = j0 + u * NT;
-      if (j >= nvec) break;
-      if constexpr (sizeof(IT) == sizeof(LT)) {
-        *reinterpret_cast<u32x4*>(act + j * V) = raw[u];
-      } else {  // float input to half LDS
-        act[j * V + 0] = (LT)as_f32(raw[u].x);
-        act[j * V + 1] = (LT)as_f32(raw[u].y);
-        act[j * V + 2] = (LT)as_f32(raw[u].z);
-        act[j * V + 3] = (LT)as_f32(raw[u].w);
-      }
-    }
-  }
-}
-
 // LayerNorm B rows (biased variance) into LDS as LT. gamma and beta (this layer's, in AT) are
-// loaded as 16-byte vectors before the rows, so their latency hides under the rows' loads, and land
-// in LDS next to the fp32 copy of the rows (`raw`); then one reduction of the shifted sums of all
-// rows and the normalized rows.
-template <typename IT, typename LT, typename AT, int BM>
-__device__ __forceinline__ bool stage_ln(Ctl& c, const StackArgs& a, uint32_t& sb, const void* in, int B, int K,
+// loaded as 16-byte vectors first, so their latency hides under the rows' loads (fill() puts the
+// rows into `raw` as fp32); they land in LDS next to the rows. Then one reduction of the shifted
+// sums of all rows and the normalized rows.
+template <typename LT, typename AT, int BM, typename Fill>
+__device__ __forceinline__ bool stage_ln(Ctl& c, const StackArgs& a, uint32_t& sb, int B, int K,
                                          const AT* __restrict__ gam, const AT* __restrict__ beta, LT* act, float* raw,
-                                         AT* gb, int st) {
-  constexpr int V = 16 / (int)sizeof(IT);
+                                         AT* gb, int st, Fill fill) {
   constexpr int VG = 16 / (int)sizeof(AT);
   constexpr int kGB = 2;  // gamma/beta vectors per thread issued ahead of the rows
   const int ngv = K / VG;
-  {
-    const rsrc_t rg = make_rsrc(gam, (uint32_t)(K * sizeof(AT))), rb = make_rsrc(beta, (uint32_t)(K * sizeof(AT)));
-    u32x4 gv[kGB], bv[kGB];
+  const rsrc_t rg = make_rsrc(gam, (uint32_t)(K * sizeof(AT))), rb = make_rsrc(beta, (uint32_t)(K * sizeof(AT)));
+  u32x4 gv[kGB], bv[kGB];
 #pragma unroll
-    for (int u = 0; u < kGB; ++u) {
-      const int j = st + u * NT;
-      const uint32_t off = j < ngv ? (uint32_t)(j * 16) : kOutOfRange;
-      gv[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
-      bv[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+  for (int u = 0; u < kGB; ++u) {
+    const int j = st + u * NT;
+    const uint32_t off = j < ngv ? (uint32_t)(j * 16) : kOutOfRange;
+    gv[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
+    bv[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+  }
+  if (!fill()) return false;
+#pragma unroll
+  for (int u = 0; u < kGB; ++u) {
+    const int j = st + u * NT;
+    if (j < ngv) {
+      *reinterpret_cast<u32x4*>(gb + j * VG) = gv[u];
+      *reinterpret_cast<u32x4*>(gb + K + j * VG) = bv[u];
     }
-    const rsrc_t r = make_rsrc(in, (uint32_t)(B * K * sizeof(IT)));
-    const int nvec = B * K / V;
-    for (int j0 = st; j0 < nvec; j0 += NT * kStageUnroll) {
-      u32x4 v[kStageUnroll];
-#pragma unroll
-      for (int u = 0; u < kStageUnroll; ++u) {
-        const int j = j0 + u * NT;
-        v[u] = coh_load16(r, j < nvec ? (uint32_t)(j * 16) : kOutOfRange);
-      }
-#pragma unroll
-      for (int u = 0; u < kStageUnroll; ++u) {
-        const int j = j0 + u * NT;
-        if (j >= nvec) break;
-        if constexpr (sizeof(IT) == 4) {
-          *reinterpret_cast<u32x4*>(raw + j * V) = v[u];
-        } else {
-          const uint32_t ww[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const half2_t p = as_half2(ww[h]);
-            raw[j * V + 2 * h] = (float)p.x;
-            raw[j * V + 2 * h + 1] = (float)p.y;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kGB; ++u) {
-      const int j = st + u * NT;
-      if (j < ngv) {
-        *reinterpret_cast<u32x4*>(gb + j * VG) = gv[u];
-        *reinterpret_cast<u32x4*>(gb + K + j * VG) = bv[u];
-      }
-    }
-    for (int j = st + kGB * NT; j < ngv; j += NT) {  // rows longer than kGB*NT vectors
-      *reinterpret_cast<u32x4*>(gb + j * VG) = __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(j * 16), 0, 0);
-      *reinterpret_cast<u32x4*>(gb + K + j * VG) = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(j * 16), 0, 0);
-    }
+  }
+  for (int j = st + kGB * NT; j < ngv; j += NT) {  // rows longer than kGB*NT vectors
+    *reinterpret_cast<u32x4*>(gb + j * VG) = __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(j * 16), 0, 0);
+    *reinterpret_cast<u32x4*>(gb + K + j * VG) = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(j * 16), 0, 0);
   }
   if (!sync_bar(c, a, sb, st)) return false;
   // sums of d = x - x[0] and d^2 per row: var = (sum d^2 - (sum d)^2 / K) / K; shifting by an
@@ -539,8 +548,8 @@ __device__ __forceinline__ bool stage_ln(Ctl& c, const StackArgs& a, uint32_t& s
         s2[b] += d * d;
       }
     }
-    s1[b] = wave_sum(s1[b]);
-    s2[b] = wave_sum(s2[b]);
+    s1[b] = wave_sum_dpp(s1[b]);
+    s2[b] = wave_sum_dpp(s2[b]);
   }
   if ((st & 63) == 0) {
 #pragma unroll
@@ -571,6 +580,38 @@ __device__ __forceinline__ bool stage_ln(Ctl& c, const StackArgs& a, uint32_t& s
   return true;
 }
 
+// The caller's B rows of K elements (AT, written before the launch) as fp32 into raw.
+template <typename AT>
+__device__ __forceinline__ void load_rows_plain(const void* in, int B, int K, float* raw, int st) {
+  constexpr int V = 16 / (int)sizeof(AT);
+  const rsrc_t r = make_rsrc(in, (uint32_t)(B * K * sizeof(AT)));
+  const int nvec = B * K / V;
+  for (int j0 = st; j0 < nvec; j0 += NT * kPollUnroll) {
+    u32x4 v[kPollUnroll];
+#pragma unroll
+    for (int u = 0; u < kPollUnroll; ++u) {
+      const int j = j0 + u * NT;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, j < nvec ? (uint32_t)(j * 16) : kOutOfRange, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kPollUnroll; ++u) {
+      const int j = j0 + u * NT;
+      if (j >= nvec) break;
+      if constexpr (sizeof(AT) == 4) {
+        *reinterpret_cast<u32x4*>(raw + j * V) = v[u];
+      } else {
+        const uint32_t ww[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const half2_t p = as_half2(ww[h]);
+          raw[j * V + 2 * h] = (float)p.x;
+          raw[j * V + 2 * h + 1] = (float)p.y;
+        }
+      }
+    }
+  }
+}
+
 // int8: the fp16 scales of the phase's row tile, [nr][K/group], into LDS.
 __device__ __forceinline__ void stage_scales(const void* s, int r0, int nr, int K, int group, half_t* scl, int st) {
   const int n = nr * (K / group);
@@ -588,12 +629,12 @@ template <typename AT, int D> struct AttnShape {
   static constexpr int NIT = (kStackChunk + NS * KPI - 1) / (NS * KPI);
 };
 
-// One item: scores of q against the chunk's rows, wave-reduced max and sum, the exp-weighted V
-// sum; the partial (max, sum, acc[D]) goes to the workspace, and the workgroup that completes the
-// last chunk of a (sequence, head) merges the partials into ctx (log-sum-exp).
+// One item's partial: scores of q against the chunk's rows (the past rows from the cache, the new
+// row at position len from this launch's tagged K/V), wave-reduced max and sum, the exp-weighted V
+// sum; (max, sum, acc[D]) is stored tagged for the workgroup that merges the (sequence, head).
 template <typename AT, int D>
-__device__ __forceinline__ bool attn_item(Ctl& c, const StackArgs& a, uint32_t& sb, const StackLayer& L, int item, float* s_acc,
-                          float* s_part, int st) {
+__device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_t& sb, const StackLayer& L, int item,
+                                             uint32_t tag_q, uint32_t tag_part, float* s_acc, int st) {
   typedef AttnShape<AT, D> S;
   constexpr int EK = S::EK, LPK = S::LPK, KPI = S::KPI, NIT = S::NIT;
   const float kNeg = -1e30f;
@@ -611,22 +652,49 @@ __device__ __forceinline__ bool attn_item(Ctl& c, const StackArgs& a, uint32_t& 
   const uint32_t bytes = (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(AT));
   const rsrc_t rk = make_rsrc(L.k, bytes), rv = make_rsrc(L.v, bytes);
   const int e0 = (lane % LPK) * EK;
-  // rows of the chunk; the new row (position len) was written by the QKV phase of this launch, so
-  // every row is read with coherent loads
+  // past rows (written by earlier launches) straight from the cache
   u32x4 kr[NIT], vr[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int key = cc * kStackChunk + (it * NS + wave) * KPI + lane / LPK;
-    const bool in = key < nkeys && key < (cc + 1) * kStackChunk;
-    const uint32_t off = in ? (uint32_t)((head + (size_t)key * D + e0) * sizeof(AT)) : kOutOfRange;
-    kr[it] = coh_load16(rk, off);
-    vr[it] = coh_load16(rv, off);
+    const bool past = key < len && key < a.cap && key < (cc + 1) * kStackChunk;
+    const uint32_t off = past ? (uint32_t)((head + (size_t)key * D + e0) * sizeof(AT)) : kOutOfRange;
+    kr[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    vr[it] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
   }
-  const rsrc_t rq = make_rsrc(a.q, (uint32_t)(a.B * H * 4));
-  const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d): scores feed exp2
+  // q of this head, this lane's EK elements
+  const rsrc_t rq = make_rsrc(a.q, (uint32_t)(a.B * H * 8));
   float qv[EK];
+  if (!poll_lane<EK>(c, a, rq, (uint32_t)(b * H + j * D + e0), tag_q, qv)) return false;
+  const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d): scores feed exp2
 #pragma unroll
-  for (int e = 0; e < EK; ++e) qv[e] = as_f32(coh_load4(rq, (uint32_t)((b * H + j * D + e0 + e) * 4))) * qs;
+  for (int e = 0; e < EK; ++e) qv[e] *= qs;
+  // the new row (position len) of this launch
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int key = cc * kStackChunk + (it * NS + wave) * KPI + lane / LPK;
+    if (key == len && key < a.cap) {
+      float kn[EK], vn[EK];
+      const rsrc_t rkn = make_rsrc(a.knew, (uint32_t)(a.B * H * 8)), rvn = make_rsrc(a.vnew, (uint32_t)(a.B * H * 8));
+      if (!poll_lane<EK>(c, a, rkn, (uint32_t)(b * H + j * D + e0), tag_q, kn)) return false;
+      if (!poll_lane<EK>(c, a, rvn, (uint32_t)(b * H + j * D + e0), tag_q, vn)) return false;
+      if constexpr (sizeof(AT) == 4) {
+        kr[it] = u32x4{__builtin_bit_cast(uint32_t, kn[0]), __builtin_bit_cast(uint32_t, kn[1]),
+                       __builtin_bit_cast(uint32_t, kn[2]), __builtin_bit_cast(uint32_t, kn[3])};
+        vr[it] = u32x4{__builtin_bit_cast(uint32_t, vn[0]), __builtin_bit_cast(uint32_t, vn[1]),
+                       __builtin_bit_cast(uint32_t, vn[2]), __builtin_bit_cast(uint32_t, vn[3])};
+      } else {
+        half8_t kh, vh;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kh[e] = (half_t)kn[e];
+          vh[e] = (half_t)vn[e];
+        }
+        kr[it] = __builtin_bit_cast(u32x4, kh);
+        vr[it] = __builtin_bit_cast(u32x4, vh);
+      }
+    }
+  }
 
   float sc[NIT];
   bool valid[NIT];
@@ -696,30 +764,38 @@ __device__ __forceinline__ bool attn_item(Ctl& c, const StackArgs& a, uint32_t& 
 #pragma unroll
   for (int wv = 0; wv < NS; ++wv) f[wv] = c.l[wv] > 0.f ? exp2f(c.m[wv] - M) : 0.f;
   const size_t pbase = ((size_t)b * a.nh + j) * a.nchunk;
-  const rsrc_t rp = make_rsrc(a.part, (uint32_t)((size_t)a.B * a.nh * a.nchunk * (D + 2) * 4));
+  const rsrc_t rp = make_rsrc(a.part, (uint32_t)((size_t)a.B * a.nh * a.nchunk * (D + 2) * 8));
   if (st < D) {
     float v = 0.f;
 #pragma unroll
     for (int wv = 0; wv < NS; ++wv) v += f[wv] * s_acc[wv * D + st];
-    coh_store4(rp, (uint32_t)(((pbase + cc) * (D + 2) + 2 + st) * 4), __builtin_bit_cast(uint32_t, v));
+    tstore(rp, (uint32_t)((pbase + cc) * (D + 2) + 2 + st), v, tag_part);
   }
   if (st == 0) {
     float Ls = 0.f;
 #pragma unroll
     for (int wv = 0; wv < NS; ++wv) Ls += f[wv] * c.l[wv];
-    coh_store4(rp, (uint32_t)(((pbase + cc) * (D + 2)) * 4), __builtin_bit_cast(uint32_t, M));
-    coh_store4(rp, (uint32_t)(((pbase + cc) * (D + 2) + 1) * 4), __builtin_bit_cast(uint32_t, Ls));
+    tstore(rp, (uint32_t)((pbase + cc) * (D + 2)), M, tag_part);
+    tstore(rp, (uint32_t)((pbase + cc) * (D + 2) + 1), Ls, tag_part);
   }
-  wait_vm_at_most<0>();
-  if (!sync_bar(c, a, sb, st)) return false;
-  uint32_t* cnt = a.sync + kSyncAttn + b * a.nh + j;
-  if (st == 0)
-    c.flag = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nvalid - 1);
-  if (!sync_bar(c, a, sb, st)) return false;
-  if (!c.flag) return true;
-  // last chunk of this (sequence, head): all partials in one parallel load, then the merge
-  const int nw = nvalid * (D + 2);
-  for (int i = st; i < nw; i += NT) s_part[i] = as_f32(coh_load4(rp, (uint32_t)((pbase * (D + 2) + i) * 4)));
+  return true;
+}
+
+// Merge of one (sequence b, head j): every chunk's partial (log-sum-exp) into ctx, rounded to AT
+// as the per-layer path stores it.
+template <typename AT, int D>
+__device__ __forceinline__ bool attn_merge(Ctl& c, const StackArgs& a, uint32_t& sb, const StackLayer& L, int b, int j,
+                                           uint32_t tag_part, uint32_t tag_ctx, float* s_part, int st) {
+  const float kNeg = -1e30f;
+  int nkeys = L.d_len[b] + 1;
+  if (nkeys > a.cap) nkeys = a.cap;
+  const int nvalid = (nkeys + kStackChunk - 1) / kStackChunk;
+  const int H = a.nh * D;
+  const size_t pbase = ((size_t)b * a.nh + j) * a.nchunk;
+  if (!sync_bar(c, a, sb, st)) return false;  // s_part (LDS) of a previous merge is free
+  if (!poll_range(c, a, a.part + pbase * (D + 2), nvalid * (D + 2), tag_part, st,
+                  [&](int i, float v) { s_part[i] = v; }))
+    return false;
   if (!sync_bar(c, a, sb, st)) return false;
   if (st < D) {
     float MM = kNeg;
@@ -731,24 +807,26 @@ __device__ __forceinline__ bool attn_item(Ctl& c, const StackArgs& a, uint32_t& 
       Lsum += wgt * pc[1];
       Acc += wgt * pc[2 + st];
     }
-    const rsrc_t rc = make_rsrc(a.ctx, (uint32_t)(a.B * H * sizeof(AT)));
-    coh_st_act<AT>(rc, (uint32_t)(b * H + j * D + st), Acc / Lsum);
+    const rsrc_t rc = make_rsrc(a.ctx, (uint32_t)(a.B * H * 8));
+    tstore(rc, (uint32_t)(b * H + j * D + st), (float)(AT)(Acc / Lsum), tag_ctx);
   }
-  if (st == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
 // ------------------------------------------------------------------ sync waves: the phase loop
 template <typename WT, typename AT, int BM, int D>
-__device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned char* smem, int g, int st_in) {
+__device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned char* smem, int g, int st_in,
+                                          uint32_t launch) {
   typedef typename WTraits<WT>::LT LT;
   LT* act = reinterpret_cast<LT*>(smem);
   float* raw = reinterpret_cast<float*>(smem + a.lds.raw);
   AT* gb = reinterpret_cast<AT*>(smem + a.lds.raw + (uint32_t)BM * a.H * 4u);  // LayerNorm gamma, then beta
   float* slots = reinterpret_cast<float*>(smem + a.lds.slots);
   half_t* scl = reinterpret_cast<half_t*>(smem + a.lds.scales);
-  float* s_acc = reinterpret_cast<float*>(smem);                   // attention: NS x D floats
-  float* s_part = reinterpret_cast<float*>(smem) + NS * D;         // merge: nchunk x (D + 2) floats
+  float* res_x2 = reinterpret_cast<float*>(smem + a.lds.res);        // this workgroup's x2 rows
+  float* res_y = res_x2 + a.lds.res_n;                                  // and its layer-output rows
+  float* s_acc = reinterpret_cast<float*>(smem);                       // attention: NS x D floats
+  float* s_part = reinterpret_cast<float*>(smem) + NS * D;             // merge: nchunk x (D + 2) floats
   const int H = a.H, F = a.F, B = a.B, G = a.G;
   // Thread indices are re-derived through an opaque copy at every phase: otherwise the compiler
   // hoists every per-thread address of every phase out of the layer loop and keeps them all live.
@@ -758,7 +836,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     asm volatile("" : "+v"(t));
     st = t;
   };
-  uint32_t sb = 0, epoch = 0;
+  uint32_t sb = 0;
   const int nitems = B * a.nh * a.nchunk;
 
   // per-workgroup row tiles of each projection (the same split the workers use)
@@ -778,6 +856,9 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
   auto clear_slots = [&](int nr) {
     for (int i = st; i < nr * NWK * BM; i += NT) slots[i] = 0.f;
   };
+  auto zero_rows = [&](int K) {  // activation rows past B
+    for (int i = B * K + st; i < BM * K; i += NT) act[i] = (LT)0.f;
+  };
   // publish the staged activation of phase `seq`, then wait for every worker to finish it
   auto hand_over = [&](uint32_t seq) -> bool {
     if (!sync_bar(c, a, sb, st)) return false;
@@ -791,128 +872,148 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     asm volatile("" ::: "memory");
     return ok;
   };
-  // after this phase's stores: every sync wave's stores complete, one arrival, the release
-  auto grid_barrier = [&]() -> bool {
-    wait_vm_at_most<0>();
-    if (!sync_bar(c, a, sb, st)) return false;
-    ++epoch;
-    if (st == 0) c.ok = grid_arrive_wait(c, a, epoch, g) ? 1 : 0;
-    if (!sync_bar(c, a, sb, st)) return false;
-    return c.ok != 0;
-  };
 
   for (int l = 0; l < a.n_layers; ++l) {
     const StackLayer& L = a.layers[l];
-    // layer outputs alternate between the two buffers; the pointers are selected as values (a
-    // select of two field addresses would make the compiler keep the arguments in scratch)
-    uintptr_t yb0 = reinterpret_cast<uintptr_t>(a.ybuf0), yb1 = reinterpret_cast<uintptr_t>(a.ybuf1);
-    uintptr_t xa = reinterpret_cast<uintptr_t>(a.x), ya = reinterpret_cast<uintptr_t>(a.y);
-    asm volatile("" : "+s"(yb0), "+s"(yb1), "+s"(xa), "+s"(ya));
-    const void* xin = reinterpret_cast<const void*>((l == 0) ? xa : ((l & 1) ? yb0 : yb1));
-    void* yout = reinterpret_cast<void*>((l == a.n_layers - 1) ? ya : ((l & 1) ? yb1 : yb0));
+    const bool last = l == a.n_layers - 1;
     const uint32_t seq0 = (uint32_t)l * 4u;
+    const uint32_t t_q = stack_tag(launch, l, TAG_Q), t_part = stack_tag(launch, l, TAG_PART);
+    const uint32_t t_ctx = stack_tag(launch, l, TAG_CTX), t_x2 = stack_tag(launch, l, TAG_X2);
+    const uint32_t t_f = stack_tag(launch, l, TAG_F), t_y = stack_tag(launch, l, TAG_Y);
 
-    // ---- region 1: LN1 + QKV + bias; q -> workspace, k/v -> cache row d_len[b]
+    // ---- region 1: LN1 + QKV + bias; q, k, v tagged; k, v also into the cache row d_len[b]
     fresh();
+    if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nq);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_qkv, q0, nq, H, a.group, scl, st);
-    if (!stage_ln<AT, LT, AT, BM>(c, a, sb, xin, B, H, (const AT*)L.ln1_g, (const AT*)L.ln1_b, act, raw, gb, st)) return;
+    {
+      bool ok;
+      if (l == 0) {
+        ok = stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)L.ln1_g, (const AT*)L.ln1_b, act, raw, gb, st, [&]() {
+          load_rows_plain<AT>(a.x, B, H, raw, st);
+          return true;
+        });
+      } else {
+        const uint32_t t_prev = stack_tag(launch, l - 1, TAG_Y);
+        ok = stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)L.ln1_g, (const AT*)L.ln1_b, act, raw, gb, st, [&]() {
+          return poll_range(c, a, a.ybuf, B * H, t_prev, st, [&](int i, float v) { raw[i] = v; });
+        });
+      }
+      if (!ok) return;
+    }
     if (!hand_over(seq0)) return;
     {
-      const rsrc_t rqo = make_rsrc(a.q, (uint32_t)(B * H * 4));
+      const rsrc_t rqo = make_rsrc(a.q, (uint32_t)(B * H * 8));
+      const rsrc_t rkn = make_rsrc(a.knew, (uint32_t)(B * H * 8)), rvn = make_rsrc(a.vnew, (uint32_t)(B * H * 8));
       const uint32_t cache_bytes = (uint32_t)((size_t)B * a.nh * a.cap * D * sizeof(AT));
       const rsrc_t rk = make_rsrc(L.k, cache_bytes), rv = make_rsrc(L.v, cache_bytes);
       for (int t = st; t < nq * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = q0 + rl;
         const float z = row_sum(rl, b) + ldp<AT>(L.b_qkv, n);
         if (n < H) {
-          coh_store4(rqo, (uint32_t)((b * H + n) * 4), __builtin_bit_cast(uint32_t, z));
+          tstore(rqo, (uint32_t)(b * H + n), z, t_q);
         } else {
           const int m = n < 2 * H ? n - H : n - 2 * H, j = m / D, e = m - j * D;
+          const float zr = (float)(AT)z;  // the value the cache holds
+          tstore(n < 2 * H ? rkn : rvn, (uint32_t)(b * H + m), zr, t_q);
           const int pos = L.d_len[b];
-          if (pos >= 0 && pos < a.cap) coh_st_act<AT>(n < 2 * H ? rk : rv, (uint32_t)((((size_t)b * a.nh + j) * a.cap + pos) * D + e), z);
+          if (pos >= 0 && pos < a.cap)
+            coh_st_act<AT>(n < 2 * H ? rk : rv, (uint32_t)((((size_t)b * a.nh + j) * a.cap + pos) * D + e), z);
         }
       }
     }
-    if (!grid_barrier()) return;
 
-    // ---- region 2: attention over the cache, chunk partials merged by the last chunk
+    // ---- region 2: attention over the cache; first every partial of this workgroup, then the
+    // merges it owns (chunk 0 of a head), so that no merge waits on a partial queued behind it
     fresh();
     for (int item = g; item < nitems; item += G)
-      if (!attn_item<AT, D>(c, a, sb, L, item, s_acc, s_part, st)) return;
-    if (!grid_barrier()) return;
+      if (!attn_partial<AT, D>(c, a, sb, L, item, t_q, t_part, s_acc, st)) return;
+    for (int item = g; item < nitems; item += G)
+      if (item % a.nchunk == 0 &&
+          !attn_merge<AT, D>(c, a, sb, L, item / (a.nchunk * a.nh), (item / a.nchunk) % a.nh, t_part, t_ctx, s_part, st))
+        return;
 
     // ---- output projection + bias + residual: x2 = x + Wo ctx + bo
     fresh();
-    if (!sync_bar(c, a, sb, st)) return;  // the attention scratch (same LDS) is no longer read
+    if (!sync_bar(c, a, sb, st)) return;  // the attention scratch (same LDS) and the slots are free
     clear_slots(no);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_o, o0, no, H, a.group, scl, st);
-    stage_plain<AT, LT, BM>(a.ctx, B, H, act, st);
+    zero_rows(H);
+    if (!poll_range(c, a, a.ctx, B * H, t_ctx, st, [&](int i, float v) { act[i] = (LT)v; })) return;
     if (!hand_over(seq0 + 1u)) return;
     {
-      const rsrc_t rx = make_rsrc(xin, (uint32_t)(B * H * sizeof(AT)));
-      const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 4));
+      const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 8));
       for (int t = st; t < no * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = o0 + rl;
         const float z = row_sum(rl, b) + ldp<AT>(L.b_o, n);
-        coh_store4(rx2, (uint32_t)((b * H + n) * 4), __builtin_bit_cast(uint32_t, coh_ld_act<AT>(rx, (uint32_t)(b * H + n)) + z));
+        const float xr = l == 0 ? ldp<AT>(a.x, b * H + n) : res_y[t];
+        const float v = xr + z;
+        res_x2[t] = v;
+        tstore(rx2, (uint32_t)(b * H + n), v, t_x2);
       }
     }
-    if (!grid_barrier()) return;
 
     // ---- region 3: LN2 + FF1 + bias + GeLU
     fresh();
+    if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nf);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff1, f0, nf, H, a.group, scl, st);
-    if (!stage_ln<float, LT, AT, BM>(c, a, sb, a.x2, B, H, (const AT*)L.ln2_g, (const AT*)L.ln2_b, act, raw, gb, st)) return;
+    if (!stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)L.ln2_g, (const AT*)L.ln2_b, act, raw, gb, st, [&]() {
+          return poll_range(c, a, a.x2, B * H, t_x2, st, [&](int i, float v) { raw[i] = v; });
+        }))
+      return;
     if (!hand_over(seq0 + 2u)) return;
     {
-      const rsrc_t rf = make_rsrc(a.f, (uint32_t)(B * F * sizeof(AT)));
+      const rsrc_t rf = make_rsrc(a.f, (uint32_t)(B * F * 8));
       for (int t = st; t < nf * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = f0 + rl;
         const float z = row_sum(rl, b) + ldp<AT>(L.b_ff1, n);
-        coh_st_act<AT>(rf, (uint32_t)(b * F + n), gelu(z, a.gelu_tanh != 0));
+        tstore(rf, (uint32_t)(b * F + n), (float)(AT)gelu(z, a.gelu_tanh != 0), t_f);
       }
     }
-    if (!grid_barrier()) return;
 
     // ---- region 4: FF2 + bias + residual: y = x2 + W2 f + b2
     fresh();
+    if (!sync_bar(c, a, sb, st)) return;  // the LayerNorm rows (same LDS) and the slots are free
     clear_slots(ny);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff2, y0, ny, F, a.group, scl, st);
-    stage_plain<AT, LT, BM>(a.f, B, F, act, st);
+    zero_rows(F);
+    if (!poll_range(c, a, a.f, B * F, t_f, st, [&](int i, float v) { act[i] = (LT)v; })) return;
     if (!hand_over(seq0 + 3u)) return;
     {
-      const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 4));
-      const rsrc_t ry = make_rsrc(yout, (uint32_t)(B * H * sizeof(AT)));
+      const rsrc_t ryt = make_rsrc(a.ybuf, (uint32_t)(B * H * 8));
+      const rsrc_t ry = make_rsrc(a.y, (uint32_t)(B * H * sizeof(AT)));
       for (int t = st; t < ny * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = y0 + rl;
         const float z = row_sum(rl, b) + ldp<AT>(L.b_ff2, n);
-        coh_st_act<AT>(ry, (uint32_t)(b * H + n), as_f32(coh_load4(rx2, (uint32_t)((b * H + n) * 4))) + z);
+        const float v = (float)(AT)(res_x2[t] + z);
+        res_y[t] = v;
+        if (last)
+          coh_st_act<AT>(ry, (uint32_t)(b * H + n), v);
+        else
+          tstore(ryt, (uint32_t)(b * H + n), v, t_y);
       }
     }
-    if (!grid_barrier()) return;
   }
 
-  // every layer has attended: advance the cache lengths, then the last workgroup out resets the
-  // barrier state for the next launch
-  if (g == 0 && st < B)
-    for (int l = 0; l < a.n_layers; ++l) {
-      int32_t* dl = a.layers[l].d_len;
-      if (dl[st] + 1 <= a.cap) dl[st] += 1;
-    }
+  // every store of this workgroup is complete; the last workgroup out advances the cache lengths
+  // (every other one has finished reading them) and the launch counter
+  wait_vm_at_most<0>();
+  if (!sync_bar(c, a, sb, st)) return;
   if (st == 0) {
     const uint32_t out = __hip_atomic_fetch_add(a.sync + kSyncExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (out == (uint32_t)G - 1) {
-      for (int i = 0; i < kSyncGroups; ++i)
-        __hip_atomic_store(a.sync + kSyncSub + i * kSyncLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.sync + kSyncTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.sync + kSyncFlag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int l = 0; l < a.n_layers; ++l)
+        for (int b = 0; b < B; ++b) {
+          int32_t* dl = a.layers[l].d_len + b;
+          const int v = __hip_atomic_load(dl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (v + 1 <= a.cap) __hip_atomic_store(dl, v + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       __hip_atomic_store(a.sync + kSyncExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.sync + kSyncLaunch, launch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
-
 }  // namespace
 
 // ------------------------------------------------------------------ the persistent kernel
@@ -929,14 +1030,14 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
     for (int w = 0; w < NWK; ++w) c.done[w] = 0u;
     c.sbar = 0u;
     c.abort = 0u;
-    c.ok = 0;
-    c.flag = 0;
+    c.launch = __hip_atomic_load(a.sync + kSyncLaunch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   if (wave < NS) {
-    sync_side<WT, AT, BM, D>(a, c, smem, blockIdx.x, (int)threadIdx.x);
+    const uint32_t launch = __builtin_amdgcn_readfirstlane(c.launch);
+    sync_side<WT, AT, BM, D>(a, c, smem, blockIdx.x, (int)threadIdx.x, launch);
     if (lds_ld(&c.abort) == 0u) return;
     raise_abort(c, a.sync);  // a failed sync wave releases the workers
   } else {

@@ -8,6 +8,7 @@
 
 #include <cstring>
 #include <new>
+#include <random>
 #include <vector>
 
 #include "ds_internal.hpp"
@@ -31,22 +32,23 @@ int slice_elems(int wdt) { return wdt == DS_F32 ? 256 : (wdt == DS_F16 ? 512 : 1
 size_t act_bytes(int adt) { return adt == DS_F32 ? 4 : 2; }
 
 struct StackWs {
-  size_t q, part, ctx, x2, f, y0, y1, total;
+  size_t q, knew, vnew, part, ctx, x2, f, y, total;
 };
 
+// Every value that crosses workgroups is stored tagged: 8 bytes per element.
 StackWs stack_ws(const ds_stack& S, int batch) {
   const ds_layer_desc& d = S.desc;
-  const size_t a = act_bytes(d.act_dtype);
   StackWs W{};
   size_t off = 0;
-  auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
-  W.q = take((size_t)batch * d.hidden * 4);
-  W.part = take((size_t)batch * d.heads * S.nchunk * (d.head_dim + 2) * 4);
-  W.ctx = take((size_t)batch * d.hidden * a);
-  W.x2 = take((size_t)batch * d.hidden * 4);
-  W.f = take((size_t)batch * d.ffn * a);
-  W.y0 = take((size_t)batch * d.hidden * a);
-  W.y1 = take((size_t)batch * d.hidden * a);
+  auto take = [&](size_t elems) { size_t at = off; off += up256(elems * 8); return at; };
+  W.q = take((size_t)batch * d.hidden);
+  W.knew = take((size_t)batch * d.hidden);
+  W.vnew = take((size_t)batch * d.hidden);
+  W.part = take((size_t)batch * d.heads * S.nchunk * (d.head_dim + 2));
+  W.ctx = take((size_t)batch * d.hidden);
+  W.x2 = take((size_t)batch * d.hidden);
+  W.f = take((size_t)batch * d.ffn);
+  W.y = take((size_t)batch * d.hidden);
   W.total = off;
   return W;
 }
@@ -128,11 +130,17 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
                               w.ln2_g, w.ln2_b, w.w_ff1, w.b_ff1, w.s_ff1, w.w_ff2, w.b_ff2, w.s_ff2,
                               caches[l].k, caches[l].v, caches[l].d_len};
   }
-  S->sync_words = ds::kSyncAttn + (size_t)max_batch * d.heads;
+  S->sync_words = ds::kSyncWords;
   e = hipMalloc(reinterpret_cast<void**>(&S->d_layers), sizeof(ds::StackLayer) * n_layers);
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&S->d_sync), S->sync_words * 4);
   if (e == hipSuccess) e = hipMemcpy(S->d_layers, table.data(), sizeof(ds::StackLayer) * n_layers, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemset(S->d_sync, 0, S->sync_words * 4);
+  if (e == hipSuccess) {
+    // the launch counter starts at a random value, so that tags of this stack never match values
+    // some earlier stack left in a reused workspace
+    std::vector<uint32_t> init(S->sync_words, 0u);
+    init[ds::kSyncLaunch] = std::random_device{}() & 0xfffffu;
+    e = hipMemcpy(S->d_sync, init.data(), S->sync_words * 4, hipMemcpyHostToDevice);
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(S->d_layers);
@@ -191,13 +199,14 @@ int ds_stack_forward_decode(ds_stack_t* S, const void* x, void* y, int32_t batch
   a.group = d.quant_group;
   a.eps = d.ln_eps;
   a.gelu_tanh = d.gelu_tanh;
-  a.q = reinterpret_cast<float*>(base + W.q);
-  a.part = reinterpret_cast<float*>(base + W.part);
-  a.ctx = base + W.ctx;
-  a.x2 = reinterpret_cast<float*>(base + W.x2);
-  a.f = base + W.f;
-  a.ybuf0 = base + W.y0;
-  a.ybuf1 = base + W.y1;
+  a.q = reinterpret_cast<uint2*>(base + W.q);
+  a.knew = reinterpret_cast<uint2*>(base + W.knew);
+  a.vnew = reinterpret_cast<uint2*>(base + W.vnew);
+  a.part = reinterpret_cast<uint2*>(base + W.part);
+  a.ctx = reinterpret_cast<uint2*>(base + W.ctx);
+  a.x2 = reinterpret_cast<uint2*>(base + W.x2);
+  a.f = reinterpret_cast<uint2*>(base + W.f);
+  a.ybuf = reinterpret_cast<uint2*>(base + W.y);
   a.sync = S->d_sync;
   a.G = S->G;
   a.nchunk = S->nchunk;
@@ -220,14 +229,17 @@ int ds_stack_check(ds_stack_t* S) {
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(words.data(), S->d_sync, S->sync_words * 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_err(e, "stack check");
-  size_t dirty = 0;
-  for (uint32_t w : words) dirty += w != 0u;
-  if (dirty) {
-    const uint32_t err = words[ds::kSyncError];
-    (void)hipMemset(S->d_sync, 0, S->sync_words * 4);
+  const uint32_t err = words[ds::kSyncError], exits = words[ds::kSyncExit];
+  if (err != 0u || exits != 0u) {
+    // a failed launch: clear the error and the exit count, and move the launch counter on so that
+    // no value that launch stored carries a tag the next one waits for
+    words[ds::kSyncError] = 0u;
+    words[ds::kSyncExit] = 0u;
+    words[ds::kSyncLaunch] = (words[ds::kSyncLaunch] + 1u) & 0xfffffu;
+    (void)hipMemcpy(S->d_sync, words.data(), S->sync_words * 4, hipMemcpyHostToDevice);
     (void)hipDeviceSynchronize();
-    return ds::set_error(DS_ERR_HIP, "persistent decode: a grid barrier timed out (error flag %u, %zu barrier words "
-                         "left set); state reset, outputs of the failed step are invalid", err, dirty);
+    return ds::set_error(DS_ERR_HIP, "persistent decode: a wait timed out (error flag %u, %u of %d workgroups "
+                         "finished); state reset, outputs of the failed step are invalid", err, exits, S->G);
   }
   return DS_OK;
 }
