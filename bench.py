@@ -20,6 +20,45 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 
+# HBM traffic of a kernel as counted by rocprofv3 (FETCH_SIZE and WRITE_SIZE, each scaled by what
+# the same counter reads for a copy of known size) is recorded in a profile summary together with
+# the SHA-256 of the kernel's source file; the figure is reported only while that source is
+# unchanged.
+TRAFFIC_RECORDS = {
+    "stack_decode_kernel": ("profiles/stack_decode_kernel_c2_f16_b1.md", "transformer_gpt_layer_amd/csrc/kernels_stack.hip"),
+}
+
+
+def measured_traffic(kernel: str, workload: str):
+    import hashlib
+    import re
+
+    if kernel not in TRAFFIC_RECORDS:
+        return None
+    summary, source = (os.path.join(ROOT, p) for p in TRAFFIC_RECORDS[kernel])
+    if not (os.path.exists(summary) and os.path.exists(source)):
+        return None
+    digest = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    for line in open(summary):
+        m = re.match(r"traffic-record: (\{.*\})\s*$", line.strip())
+        if m:
+            rec = json.loads(m.group(1))
+            if rec.get("workload") == workload and rec.get("source_sha256") == digest:
+                return int(rec["hbm_bytes_per_launch"])
+    return None
+
+
+def copy_calibration(torch, gib: int = 1):
+    """Three plain device-to-device copies of `gib` GiB (torch's copy kernel): the reference whose
+    FETCH_SIZE / WRITE_SIZE counters scale the kernels' counters to bytes."""
+    n = (gib << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4, "copies": 3}))
+
 
 def algorithmic_bytes_per_layer(wl) -> dict:
     """Bytes one layer step must move at least once (weights and scales, biases and LayerNorm
@@ -226,6 +265,8 @@ def main():
     ap.add_argument("--mode", choices=["auto", "stack", "layers"], default="auto",
                     help="stack: one persistent launch per step; layers: six kernels per layer")
     ap.add_argument("--no-graph", action="store_true", help="layers mode: launch eagerly instead of a HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three 1 GiB device copies (the reference for HBM traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -238,6 +279,9 @@ def main():
     import synthetic as syn
     import transformer_gpt_layer_amd as tg
 
+    if args.copy_calibration:
+        torch.cuda.set_device(0)
+        return copy_calibration(torch)
     wl = syn.WORKLOADS[args.config]
     torch.cuda.set_device(0)
     if wl.seq != 1:
@@ -325,7 +369,8 @@ def main():
         kgbs = step_bytes / (kernel_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": "stack_decode_kernel (all layers of one step)",
                     "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": None,
+                    "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                    "traffic": measured_traffic("stack_decode_kernel", wl.name) if layers == wl.layers else None,
                     "kernel_ms": round(kernel_ms, 4), "bytes_per_launch": step_bytes}
     else:
         roofline = {"bound": "hbm", "kernel": "whole decode step (per-layer kernels)",

@@ -1,0 +1,177 @@
+"""GPU parity at the workloads' full sizes, in the launch configurations the benchmark times.
+
+- GPT-Neo-2.7B shapes (hidden 2560, 20 heads, FF 10240, fp16, batch 1, 512 past rows): the whole
+  32-layer persistent decode step, every output element and every new cache row checked against
+  the oracle run layer after layer.
+- 13B shapes (hidden 5120, 40 heads, FF 20480, batch 8, 1024 past rows), fp16 and int8 (group 64):
+  one full-size layer through the per-layer kernels the benchmark uses at batch 8, and the int8
+  batch-1 layer through the persistent kernel. The kernels and their grids depend on the shapes,
+  not on the layer count, so one layer exercises exactly the kernels of the 40-layer step.
+- Prefill on the GPT-Neo-2.7B shapes (4 sequences x 512 prompt rows, causal): one full-size layer
+  through the MFMA kernels; the oracle checks sampled outputs (the first rows of two sequences,
+  which causality makes independent of later rows) and sampled cache rows of every sequence.
+
+Weights and caches are seeded synthetic draws; the oracle receives exactly the values the GPU
+used, widened to float64, one layer at a time so that host memory stays small.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+import transformer_gpt_layer_amd as tg
+from tests._common import TOL, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+_DT = {"f16": "fp16", "i8": "int8", "f32": "fp32"}
+
+
+def _config(wl):
+    return tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn, dtype=_DT[wl.weight_dtype],
+                          quantization_setting=(wl.group, False) if wl.weight_dtype == "i8" else None)
+
+
+def _gpu_layer(wl, layer, cfg):
+    act = torch.float16 if wl.act_dtype == "f16" else torch.float32
+    gw = {}
+    for name, t in syn.layer_weights_f32(wl, layer, "cuda").items():
+        if name.startswith("w_") and wl.weight_dtype == "i8":
+            q, s = tg.quantize_i8(t.contiguous(), wl.group)
+            gw[name], gw["s" + name[1:]] = q, s
+        else:
+            gw[name] = t.to(act).contiguous()
+    return tg.Layer(cfg, gw)
+
+
+def _oracle_weights(gl, wl):
+    """float64 copies of exactly the values the GPU layer holds (int8: dequantized by the oracle)."""
+    w = {}
+    for n in syn.WEIGHT_NAMES:
+        t = gl._weights[n]
+        if n.startswith("w_") and wl.weight_dtype == "i8":
+            s = gl._weights["s" + n[1:]].cpu().view(torch.int16).numpy().view(np.uint16)
+            w[n] = oracle.dequantize_i8(t.cpu().numpy(), s, wl.group)
+        else:
+            w[n] = t.double().cpu().numpy()
+    return w
+
+
+def _filled_cache(wl, layer, gl, act):
+    kv = tg.KVCache(wl.batch, wl.heads, wl.capacity, wl.head_dim, act, "cuda")
+    if wl.past:
+        kp, vp = syn.past_kv_f32(wl, layer, "cuda")
+        rows = lambda t: t.permute(0, 2, 1, 3).reshape(wl.batch, wl.past, wl.hidden).to(act).contiguous()
+        gl.kv_append(kv, rows(kp), rows(vp))
+    return kv
+
+
+def _oracle_cache(kv, past):
+    ok = np.zeros(tuple(kv.k.shape))
+    ov = np.zeros_like(ok)
+    ok[:, :, :past] = kv.k[:, :, :past].double().cpu().numpy()
+    ov[:, :, :past] = kv.v[:, :, :past].double().cpu().numpy()
+    return ok, ov
+
+
+def test_c2_full_stack_32_layers_matches_oracle():
+    wl = syn.WORKLOADS["c2"]
+    print(f"[full size] {wl.name}: persistent decode, {wl.layers} layers", flush=True)
+    cfg = _config(wl)
+    layers = [_gpu_layer(wl, l, cfg) for l in range(wl.layers)]
+    kvs = [_filled_cache(wl, l, layers[l], torch.float16) for l in range(wl.layers)]
+    # the oracle's copies of the past rows, taken before the step writes row P
+    past = [_oracle_cache(kv, wl.past) for kv in kvs]
+    st = tg.Stack(layers, kvs, max_batch=1)
+    print(f"  workgroups {st.groups}", flush=True)
+    x = syn.normal((1, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").half()
+    y = st.decode(x)
+    st.check()
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
+    h = x.double().cpu().numpy()[:, None, :]
+    for l in range(wl.layers):
+        ok, ov = past[l]
+        lens = np.full(1, wl.past, dtype=np.int32)
+        h = oracle.layer_forward(desc, _oracle_weights(layers[l], wl), ok, ov, lens, h)
+        P = wl.past
+        ek = rel_l2(kvs[l].k[:, :, P].double().cpu().numpy(), ok[:, :, P])
+        ev = rel_l2(kvs[l].v[:, :, P].double().cpu().numpy(), ov[:, :, P])
+        assert ek <= TOL["f16"] and ev <= TOL["f16"], (l, ek, ev)
+        assert kvs[l].lengths() == [P + 1]
+    err = rel_l2(y.double().cpu().numpy(), h[:, 0])
+    print(f"  32-layer output rel L2 {err:.3e}", flush=True)
+    assert err <= TOL["f16"], err
+
+
+@pytest.mark.parametrize("name", ["c3", "c4b8", "c4b1"])
+def test_13b_full_shape_layer_matches_oracle(name):
+    wl = syn.WORKLOADS[name]
+    use_stack = wl.batch <= 4  # the benchmark's choice: persistent kernel up to batch 4
+    print(f"[full size] {wl.name}: one layer, {'persistent' if use_stack else 'per-layer'} kernels", flush=True)
+    cfg = _config(wl)
+    gl = _gpu_layer(wl, 0, cfg)
+    if wl.weight_dtype == "i8":
+        # the GPU quantizer's codes and scales equal the oracle's, bit for bit, at full size
+        w32 = syn.layer_weights_f32(wl, 0, "cuda")
+        for n in ("w_qkv", "w_ff2"):
+            oq, os_ = oracle.quantize_i8(w32[n].cpu().numpy(), wl.group)
+            assert np.array_equal(gl._weights[n].cpu().numpy(), oq), n
+            assert np.array_equal(gl._weights["s" + n[1:]].cpu().view(torch.int16).numpy().view(np.uint16), os_), n
+        del w32
+    kv = _filled_cache(wl, 0, gl, torch.float16)
+    ok, ov = _oracle_cache(kv, wl.past)
+    x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").half()
+    if use_stack:
+        st = tg.Stack([gl], [kv], max_batch=wl.batch)
+        y = st.decode(x)
+        st.check()
+    else:
+        y = gl.decode(kv, x)
+    torch.cuda.synchronize()
+    lens = np.full(wl.batch, wl.past, dtype=np.int32)
+    yo = oracle.layer_forward(oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn), _oracle_weights(gl, wl), ok, ov,
+                              lens, x.double().cpu().numpy()[:, None, :])[:, 0]
+    yd, xd = y.double().cpu().numpy(), x.double().cpu().numpy()
+    err, err_delta = rel_l2(yd, yo), rel_l2(yd - xd, yo - xd)
+    print(f"  rel L2 {err:.3e}, on y - x {err_delta:.3e}", flush=True)
+    assert err <= TOL["f16"] and err_delta <= TOL["f16"], (err, err_delta)
+    P = wl.past
+    assert rel_l2(kv.k[:, :, P].double().cpu().numpy(), ok[:, :, P]) <= TOL["f16"]
+    assert rel_l2(kv.v[:, :, P].double().cpu().numpy(), ov[:, :, P]) <= TOL["f16"]
+
+
+def test_c5_full_shape_prefill_layer_sampled_rows():
+    wl = syn.WORKLOADS["c5"]
+    print(f"[full size] {wl.name}: one layer of MFMA prefill, sampled rows", flush=True)
+    cfg = _config(wl)
+    gl = _gpu_layer(wl, 0, cfg)
+    kv = tg.KVCache(wl.batch, wl.heads, wl.capacity, wl.head_dim, torch.float16, "cuda")
+    x = syn.stack_input_f32(wl, "cuda").half().contiguous()
+    y = gl.prefill(kv, x)
+    torch.cuda.synchronize()
+    assert kv.lengths() == [wl.seq] * wl.batch
+    ow = _oracle_weights(gl, wl)
+    xd = x.double().cpu().numpy()
+    H, nh, d = wl.hidden, wl.heads, wl.head_dim
+    # cache rows of every sequence at the start, middle and end of the prompt: K and V of row t
+    # are W_kv LN1(x_t) + b_kv and depend on row t alone
+    for b in range(wl.batch):
+        for t in (0, wl.seq // 2 - 1, wl.seq - 1):
+            h = oracle.layernorm(xd[b, t], ow["ln1_g"], ow["ln1_b"])
+            z = oracle.linear(ow["w_qkv"], ow["b_qkv"], h)
+            kg = kv.k[b, :, t].double().cpu().numpy().reshape(-1)
+            vg = kv.v[b, :, t].double().cpu().numpy().reshape(-1)
+            assert rel_l2(kg, z[H:2 * H]) <= TOL["f16"], (b, t)
+            assert rel_l2(vg, z[2 * H:]) <= TOL["f16"], (b, t)
+    # outputs of the first rows of two sequences: causal masking makes them independent of the
+    # rest of the prompt, so the oracle runs only those rows
+    desc = oracle.Desc(H, nh, d, wl.ffn)
+    for b, rows in ((0, 24), (wl.batch - 1, 12)):
+        ok = np.zeros((1, nh, wl.capacity, d))
+        ov = np.zeros_like(ok)
+        lens = np.zeros(1, dtype=np.int32)
+        yo = oracle.layer_forward(desc, ow, ok, ov, lens, xd[b:b + 1, :rows])[0]
+        err = rel_l2(y[b, :rows].double().cpu().numpy(), yo)
+        print(f"  sequence {b}, rows 0..{rows - 1}: rel L2 {err:.3e}", flush=True)
+        assert err <= TOL["f16"], (b, err)
