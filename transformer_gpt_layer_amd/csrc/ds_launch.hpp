@@ -39,10 +39,15 @@ struct AttnArgs {
   uint32_t* counters;  // [rows][heads]
   float* ctx;          // [rows][H] fp32 output
   int rows, tokens, heads, head_dim, cap, chunk, nchunk, causal;
+  // fp16 q and ctx in place of q and ctx (launch_attn_decode_f16)
+  const _Float16* q16;
+  _Float16* ctx16;
 };
 
 hipError_t launch_gemv(Dt wdt, Dt adt, GemvKind kind, const GemvArgs& a, hipStream_t st);
 hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st);
+// The same attention with fp16 q and ctx (q16, ctx16) and an fp16 cache.
+hipError_t launch_attn_decode_f16(const AttnArgs& a, hipStream_t st);
 int attn_chunk_for(int rows, int heads, int cap);
 
 hipError_t launch_kv_append(Dt adt, const void* k_new, const void* v_new, void* kc, void* vc,

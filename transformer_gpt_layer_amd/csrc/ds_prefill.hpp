@@ -30,6 +30,13 @@ struct GemmArgs {
   int tokens, heads, head_dim, cap, hidden;
   int gelu_tanh;
   int tiles_m, tiles_n;  // set by the launcher
+  // int8 weights (skinny path only): codes [N][K] and fp16 scales [N][K/group] in place of w
+  const int8_t* wq;
+  const half_t* wscale;
+  int group;
+  // skinny QKV launch: zeroes these attention merge counters first
+  uint32_t* attn_counters;
+  int n_counters;
 };
 
 // Attention of `tokens` new rows per sequence over keys 0..d_len[b]+tokens-1 of the cache (the new
@@ -51,5 +58,9 @@ hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int bn, int cus, hipStrea
 hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const half_t* b, half_t* out, int rows, int H,
                           float eps, hipStream_t st);
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t st);
+// The same product and epilogues for M <= 16 rows (decode of a few sequences): every weight row is
+// streamed once, with fp16 weights (w) or int8 codes and group-64 scales (wq, wscale, group).
+hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, hipStream_t st);
+constexpr int kSkinnyMaxRows = 16;
 
 }  // namespace ds

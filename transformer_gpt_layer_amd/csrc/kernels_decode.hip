@@ -243,7 +243,7 @@ hipError_t launch_gemv(Dt wdt, Dt adt, GemvKind kind, const GemvArgs& a, hipStre
 // Region 2: for one (row, head) and one chunk of cached positions, q.K/sqrt(d) scores, a
 // wave-reduced max and sum, and the exp-weighted V sum; the last chunk workgroup to finish merges
 // the chunk partials (log-sum-exp) into ctx. grid = (nchunk, heads, rows).
-template <typename AT, int D, int C>
+template <typename AT, int D, int C, bool QH = false>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
   constexpr int EK = 16 / (int)sizeof(AT);  // elements per 16-byte load
   constexpr int LPK = D / EK;               // lanes per key
@@ -270,7 +270,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
   const float qs = 1.4426950408889634f / sqrtf((float)D);
   float qv[EK];
 #pragma unroll
-  for (int e = 0; e < EK; ++e) qv[e] = a.q[(size_t)rr * H + j * D + e0 + e] * qs;
+  for (int e = 0; e < EK; ++e) {
+    const size_t qi = (size_t)rr * H + j * D + e0 + e;
+    if constexpr (QH) qv[e] = (float)a.q16[qi] * qs;
+    else qv[e] = a.q[qi] * qs;
+  }
 
   const size_t head_base = (((size_t)seq * a.heads + j) * a.cap) * D;
   const AT* Kp = reinterpret_cast<const AT*>(a.k_cache) + head_base;
@@ -356,33 +360,41 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
   float f[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) f[w] = s_l[w] > 0.f ? exp2f(s_m[w] - M) : 0.f;
-  if (tid < D) part[2 + tid] = f[0] * s_acc[0][tid] + f[1] * s_acc[1][tid] + f[2] * s_acc[2][tid] + f[3] * s_acc[3][tid];
+  // Partials are stored at device scope (written through past this XCD's L2) and every store is
+  // acknowledged before the arrival count moves, so the merging workgroup, reading them at device
+  // scope, sees them without an L2 write-back or invalidation of the whole cache.
+  if (tid < D)
+    __hip_atomic_store(part + 2 + tid, f[0] * s_acc[0][tid] + f[1] * s_acc[1][tid] + f[2] * s_acc[2][tid] + f[3] * s_acc[3][tid],
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (tid == 0) {
-    part[0] = M;
-    part[1] = f[0] * s_l[0] + f[1] * s_l[1] + f[2] * s_l[2] + f[3] * s_l[3];
+    __hip_atomic_store(part, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(part + 1, f[0] * s_l[0] + f[1] * s_l[1] + f[2] * s_l[2] + f[3] * s_l[3], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are acknowledged
   __syncthreads();
   uint32_t* cnt = a.counters + (size_t)rr * a.heads + j;
-  if (tid == 0) s_last = (atomicAdd(cnt, 1u) == (uint32_t)(nvalid - 1));
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nvalid - 1);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   // last workgroup of this (row, head): log-sum-exp merge of the nvalid chunk partials
   const float* p0 = a.part + ((size_t)rr * a.heads + j) * a.nchunk * (D + 2);
   if (tid < D) {
     float MM = kNeg;
-    for (int cc = 0; cc < nvalid; ++cc) MM = fmaxf(MM, __builtin_nontemporal_load(p0 + (size_t)cc * (D + 2)));
+    auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    for (int cc = 0; cc < nvalid; ++cc) MM = fmaxf(MM, ld(p0 + (size_t)cc * (D + 2)));
     float L = 0.f, A = 0.f;
     for (int cc = 0; cc < nvalid; ++cc) {
       const float* pc = p0 + (size_t)cc * (D + 2);
-      const float lc = __builtin_nontemporal_load(pc + 1);
-      const float w = lc > 0.f ? exp2f(__builtin_nontemporal_load(pc) - MM) : 0.f;
+      const float lc = ld(pc + 1);
+      const float w = lc > 0.f ? exp2f(ld(pc) - MM) : 0.f;
       L += w * lc;
-      A += w * __builtin_nontemporal_load(pc + 2 + tid);
+      A += w * ld(pc + 2 + tid);
     }
-    a.ctx[(size_t)rr * H + j * D + tid] = A / L;
+    if constexpr (QH) a.ctx16[(size_t)rr * H + j * D + tid] = (half_t)(A / L);
+    else a.ctx[(size_t)rr * H + j * D + tid] = A / L;
   }
   if (tid == 0) *cnt = 0u;
 }
@@ -400,6 +412,18 @@ template <typename AT, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.nchunk, a.heads, a.rows);
   hipLaunchKernelGGL((attn_decode_kernel<AT, D, kAttnChunk>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode_f16(const AttnArgs& a, hipStream_t st) {
+  if (a.chunk != kAttnChunk) return hipErrorInvalidValue;
+  dim3 grid(a.nchunk, a.heads, a.rows);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL((attn_decode_kernel<half_t, 64, kAttnChunk, true>), grid, dim3(256), 0, st, a);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL((attn_decode_kernel<half_t, 128, kAttnChunk, true>), grid, dim3(256), 0, st, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

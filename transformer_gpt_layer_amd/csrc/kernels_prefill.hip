@@ -147,6 +147,64 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(const IT* __restrict__ x, 
   }
 }
 
+// A few rows (a decode step): one 256-thread workgroup per row holds the whole row in registers
+// (up to NR 16-byte vectors per thread), so the statistics take one pass and one round trip: sums
+// of d = x - x[0] and d^2 give the mean and the biased variance (shifting by an element of the row
+// keeps the subtraction well conditioned).
+template <typename IT, int NR>
+__global__ __launch_bounds__(256) void ln_row_wg_kernel(const IT* __restrict__ x, const half_t* __restrict__ g,
+                                                       const half_t* __restrict__ beta, half_t* __restrict__ out, int H,
+                                                       float eps) {
+  constexpr int V = 16 / (int)sizeof(IT);
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x, row = blockIdx.x;
+  const IT* xr = x + (size_t)row * H;
+  const int nv = H / V;
+  float v[NR][V], gv[NR][V], bv[NR][V];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int i = tid + j * 256;
+    if (i < nv) {
+      ld_row<V>(xr + i * V, v[j]);
+      ld_halves<V>(g + i * V, gv[j]);
+      ld_halves<V>(beta + i * V, bv[j]);
+    }
+  }
+  const float c0 = (float)xr[0];
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+    if (tid + j * 256 < nv)
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float d = v[j][e] - c0;
+        s1 += d;
+        s2 += d * d;
+      }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = s1;
+    red[1][tid >> 6] = s2;
+  }
+  __syncthreads();
+  const float t1 = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  const float t2 = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const float dm = t1 / (float)H;
+  const float mean = c0 + dm;
+  const float rstd = rsqrtf(fmaxf(t2 / (float)H - dm * dm, 0.f) + eps);
+  half_t* o = out + (size_t)row * H;
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int i = tid + j * 256;
+    if (i < nv) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[j][e] = (v[j][e] - mean) * rstd * gv[j][e] + bv[j][e];
+      st_halves<V>(o + i * V, v[j]);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ GEMM
 constexpr int kBM = 128, kBK = 64, kGemmThreads = 256;
 #ifndef DS_GEMM_STAGES
@@ -464,6 +522,147 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
     for (int r = 0; r < 4; ++r) cr[16 * f + 4 * grp + r] = (half_t)(o[f][r] * inv);
 }
 
+
+// ------------------------------------------------------------------ skinny GEMM (M <= 16 rows)
+// A decode step of a few rows is bound by streaming the weights, so each weight row is read once
+// and the rows of the step ride along on MFMA: a workgroup owns 16 output columns (16 rows of W)
+// and its KS waves split K. Per 32-wide k step the 16 W rows are the B operand (lane l: row l%16,
+// k chunk l/16, one 16-byte load) and the activation rows the A operand (rows past M read as
+// zeros); v_mfma_f32_16x16x32_f16 leaves C[4(l/16)+i][l%16] in lane l. int8 weights: a lane's
+// 16-byte load is 16 codes (k 16j..16j+15, j = l/16) of a 64-k block (one quantization group);
+// the block's two MFMAs take k 16j..16j+7 and then 16j+8..16j+15 in lane group j (the sum over k
+// does not depend on that order), the activations are loaded in the same order, the codes become
+// fp16 exactly, and the block's product is scaled by the row's group scale before accumulating.
+__device__ __forceinline__ half8_t i8x8_to_half8(uint32_t lo, uint32_t hi) {
+  const uint32_t flip = 0x80808080u;  // q + 128 for every byte
+  lo ^= flip;
+  hi ^= flip;
+  const half2_t p0 = i8pair_to_half2(lo, false), p1 = i8pair_to_half2(lo, true);
+  const half2_t p2 = i8pair_to_half2(hi, false), p3 = i8pair_to_half2(hi, true);
+  half8_t h;
+  h[0] = p0.x; h[1] = p0.y; h[2] = p1.x; h[3] = p1.y;
+  h[4] = p2.x; h[5] = p2.y; h[6] = p3.x; h[7] = p3.y;
+  return h;
+}
+
+#ifndef DS_SKINNY_KS
+#define DS_SKINNY_KS 8
+#endif
+#ifndef DS_SKINNY_U16
+#define DS_SKINNY_U16 4
+#endif
+constexpr int kSkinnyMaxWaves = DS_SKINNY_KS;  // waves (K splits) per workgroup at most
+
+template <bool I8, int EPI>
+__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(const GemmArgs g) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, KS = blockDim.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  if (EPI == EPI_QKV && blockIdx.x == 0 && g.attn_counters)
+    for (int i = threadIdx.x; i < g.n_counters; i += blockDim.x) g.attn_counters[i] = 0u;
+  const int K = g.K, kq = K / KS, kb = w * kq, ke = kb + kq;
+  const int n = min(n0 + r, g.N - 1);  // columns past N re-read a valid row; their outputs are dropped
+  const bool arow = r < g.M;
+  const half_t* ap = g.a + (size_t)(arow ? r : 0) * K;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!I8) {
+    // software pipeline over blocks of U k-steps: the next block's loads are in flight while the
+    // current block is multiplied; steps past the wave's range are skipped (no load, no MFMA)
+    const half_t* wp = g.w + (size_t)n * K + kb + 8 * grp;
+    ap += kb + 8 * grp;
+    constexpr int U = DS_SKINNY_U16;
+    const int steps = kq / 32, nblk = (steps + U - 1) / U;
+    u32x4 wv[2][U], av[2][U];
+    auto load = [&](int blk, u32x4 (&w_)[U], u32x4 (&a_)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int st = blk * U + u;
+        if (st < steps) {
+          w_[u] = ld16(wp + 32 * st);  // cached: the two halves of a 128-byte line come from adjacent steps
+          a_[u] = arow ? ld16(ap + 32 * st) : zero;
+        }
+      }
+    };
+    auto mul = [&](int blk, const u32x4 (&w_)[U], const u32x4 (&a_)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (blk * U + u < steps)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a_[u]), __builtin_bit_cast(half8_t, w_[u]),
+                                                       acc, 0, 0, 0);
+    };
+    load(0, wv[0], av[0]);
+    for (int blk = 0; blk < nblk; blk += 2) {
+      if (blk + 1 < nblk) load(blk + 1, wv[1], av[1]);
+      mul(blk, wv[0], av[0]);
+      if (blk + 1 >= nblk) break;
+      if (blk + 2 < nblk) load(blk + 2, wv[0], av[0]);
+      mul(blk + 1, wv[1], av[1]);
+    }
+  } else {
+    const int8_t* wp = g.wq + (size_t)n * K + kb + 16 * grp;
+    const half_t* sp = g.wscale + (size_t)n * (K / 64) + kb / 64;
+    ap += kb + 16 * grp;
+    constexpr int U = 3;
+    const int steps = kq / 64, nblk = (steps + U - 1) / U;
+    u32x4 wv[2][U], a0[2][U], a1[2][U];
+    float sc[2][U];
+    auto load = [&](int blk, u32x4 (&w_)[U], u32x4 (&x0)[U], u32x4 (&x1)[U], float (&s_)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int st = blk * U + u;
+        if (st < steps) {
+          w_[u] = ld16(wp + 64 * st);  // cached: the two halves of a 128-byte line come from adjacent blocks
+          x0[u] = arow ? ld16(ap + 64 * st) : zero;
+          x1[u] = arow ? ld16(ap + 64 * st + 8) : zero;
+          s_[u] = (float)sp[st];
+        }
+      }
+    };
+    auto mul = [&](int blk, const u32x4 (&w_)[U], const u32x4 (&x0)[U], const u32x4 (&x1)[U], const float (&s_)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (blk * U + u < steps) {
+          float4_t t = {0.f, 0.f, 0.f, 0.f};
+          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x0[u]), i8x8_to_half8(w_[u].x, w_[u].y), t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x1[u]), i8x8_to_half8(w_[u].z, w_[u].w), t, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = fmaf(t[i], s_[u], acc[i]);
+        }
+    };
+    load(0, wv[0], a0[0], a1[0], sc[0]);
+    for (int blk = 0; blk < nblk; blk += 2) {
+      if (blk + 1 < nblk) load(blk + 1, wv[1], a0[1], a1[1], sc[1]);
+      mul(blk, wv[0], a0[0], a1[0], sc[0]);
+      if (blk + 1 >= nblk) break;
+      if (blk + 2 < nblk) load(blk + 2, wv[0], a0[0], a1[0], sc[0]);
+      mul(blk + 1, wv[1], a0[1], a1[1], sc[1]);
+    }
+  }
+  // sum the waves' K ranges, then the epilogue of C[4 grp + i][n0 + r]
+  __shared__ float4_t red[kSkinnyMaxWaves][kWave];
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+  for (int v = 1; v < KS; ++v) {
+    const float4_t o = red[v][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += o[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) epilogue_store<EPI>(g, 4 * grp + i, n0 + r, acc[i]);
+}
+
+template <bool I8, int EPI>
+hipError_t launch_skinny_t(const GemmArgs& a, hipStream_t st) {
+  const int kq = I8 ? 64 : 32;  // k per MFMA block
+  int ks = kSkinnyMaxWaves;
+  while (ks > 1 && a.K % (ks * kq) != 0) ks >>= 1;
+  if (a.K % (ks * kq) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((skinny_kernel<I8, EPI>), dim3((a.N + 15) / 16), dim3(64 * ks), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int BN, int EPI>
 hipError_t launch_gemm_bn(const GemmArgs& a0, int cus, hipStream_t st) {
   GemmArgs a = a0;
@@ -501,6 +700,22 @@ int gemm_pick_bn(int M, int N, int cus) {
   return 160;
 }
 
+hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.M > kSkinnyMaxRows) return hipErrorInvalidValue;
+#define DS_SK(E)                                                                                   \
+  case E:                                                                                          \
+    return int8_weights ? launch_skinny_t<true, E>(a, st) : launch_skinny_t<false, E>(a, st);
+  switch (epi) {
+    DS_SK(EPI_QKV)
+    DS_SK(EPI_OPROJ)
+    DS_SK(EPI_FF1)
+    DS_SK(EPI_FF2)
+  }
+#undef DS_SK
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int bn, int cus, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   switch (epi) {
@@ -515,6 +730,14 @@ hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int bn, int cus, hipStrea
 hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const half_t* b, half_t* out, int rows, int H,
                           float eps, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  constexpr int kNR = 8;  // 16-byte vectors per thread of the workgroup-per-row kernel
+  if (rows < 64 && H <= 256 * kNR * (in_f32 ? 4 : 8)) {
+    if (in_f32)
+      hipLaunchKernelGGL((ln_row_wg_kernel<float, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const float*>(x), g, b, out, H, eps);
+    else
+      hipLaunchKernelGGL((ln_row_wg_kernel<half_t, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const half_t*>(x), g, b, out, H, eps);
+    return hipGetLastError();
+  }
   const dim3 grid((rows + 3) / 4);
   if (in_f32)
     hipLaunchKernelGGL(ln_rows_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), g, b, out, rows, H, eps);

@@ -103,8 +103,17 @@ bool use_mfma(const ds_layer_desc& d, int rows) {
   return (int64_t)rows * kmax * 2 < lim && (int64_t)d.ffn * d.hidden * 2 < lim && 3 * (int64_t)d.hidden * d.hidden * 2 < lim;
 }
 
+// Steps of a few rows (fewer than the MFMA tile path takes) with fp16 activations and fp16 or int8
+// weights run the same LayerNorm / attention kernels with the skinny GEMM, which streams every
+// weight row once whatever the row count.
+bool use_skinny(const ds_layer_desc& d, int rows) {
+  if (d.act_dtype != DS_F16 || rows < 1 || rows > ds::kSkinnyMaxRows) return false;
+  if (d.weight_dtype == DS_F16) return rows < kMfmaMinRows;
+  return d.weight_dtype == DS_I8 && d.quant_group == 64;
+}
+
 int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int batch, int ntok, char* base,
-                 const WsLayout& W, hipStream_t st) {
+                 const WsLayout& W, bool skinny, hipStream_t st) {
   const ds_layer_desc& d = L->desc;
   const int rows = batch * ntok, H = d.hidden, F = d.ffn;
   int dev = 0, cus = 0;
@@ -128,37 +137,66 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   g.k_cache = static_cast<ds::half_t*>(kv->k);
   g.v_cache = static_cast<ds::half_t*>(kv->v);
   g.M = rows;
+  const bool i8 = d.weight_dtype == DS_I8;
+  g.group = d.quant_group;
+  // one weight matrix (fp16, or int8 codes with their scales) and its product
+  auto gemm = [&](ds::GemmEpi epi, ds::GemmArgs& a, const void* w, const void* s) -> hipError_t {
+    if (i8) {
+      a.wq = static_cast<const int8_t*>(w);
+      a.wscale = static_cast<const ds::half_t*>(s);
+    } else {
+      a.w = static_cast<const ds::half_t*>(w);
+    }
+    if (skinny) return ds::launch_skinny(epi, i8, a, st);
+    return ds::launch_gemm(epi, a, ds::gemm_pick_bn(a.M, a.N, cus), cus, st);
+  };
 
   // 1: h = LN1(x); [q | k | v] = h Wqkv^T + bqkv, k and v into the cache rows d_len[b] + t
   if (hipError_t e = ds::launch_ln_rows(false, x, hp(L->w.ln1_g), hp(L->w.ln1_b), h, rows, H, d.ln_eps, st))
     return hip_fail(e, "ln1 launch");
   ds::GemmArgs a = g;
-  a.a = h; a.w = hp(L->w.w_qkv); a.bias = hp(L->w.b_qkv); a.out = q; a.N = 3 * H; a.K = H;
-  if (hipError_t e = ds::launch_gemm(ds::EPI_QKV, a, ds::gemm_pick_bn(rows, a.N, cus), cus, st)) return hip_fail(e, "qkv gemm launch");
+  a.a = h; a.bias = hp(L->w.b_qkv); a.out = q; a.N = 3 * H; a.K = H;
+  const bool chunked_attn = skinny && ntok == 1;  // decode: chunked attention with an in-kernel merge
+  if (chunked_attn) {
+    a.attn_counters = reinterpret_cast<uint32_t*>(base + W.cnt);
+    a.n_counters = rows * d.heads;
+  }
+  if (hipError_t e = gemm(ds::EPI_QKV, a, L->w.w_qkv, L->w.s_qkv)) return hip_fail(e, "qkv gemm launch");
 
   // 2: attention of the new rows over the cache
   ds::AttnPrefillArgs at{};
   at.q = q; at.k_cache = g.k_cache; at.v_cache = g.v_cache; at.d_len = kv->d_len; at.ctx = ctx;
   at.batch = batch; at.tokens = ntok; at.heads = d.heads; at.head_dim = d.head_dim; at.cap = kv->capacity;
   at.causal = d.triangular_masking; at.scale = 1.f / std::sqrt((float)d.head_dim);
-  if (hipError_t e = ds::launch_attn_prefill(at, st)) return hip_fail(e, "attention launch");
+  if (chunked_attn) {
+    ds::AttnArgs ad{};
+    ad.q16 = q; ad.ctx16 = ctx;
+    ad.k_cache = kv->k; ad.v_cache = kv->v; ad.d_len = kv->d_len;
+    ad.part = reinterpret_cast<float*>(base + W.part);
+    ad.counters = reinterpret_cast<uint32_t*>(base + W.cnt);
+    ad.rows = rows; ad.tokens = ntok; ad.heads = d.heads; ad.head_dim = d.head_dim;
+    ad.cap = kv->capacity; ad.chunk = W.chunk; ad.nchunk = W.nchunk; ad.causal = d.triangular_masking;
+    if (hipError_t e = ds::launch_attn_decode_f16(ad, st)) return hip_fail(e, "attention launch");
+  } else if (hipError_t e = ds::launch_attn_prefill(at, st)) {
+    return hip_fail(e, "attention launch");
+  }
 
   // 3: x2 = x + ctx Wo^T + bo
   a = g;
-  a.a = ctx; a.w = hp(L->w.w_o); a.bias = hp(L->w.b_o); a.out = x2; a.resid = x; a.N = H; a.K = H;
-  if (hipError_t e = ds::launch_gemm(ds::EPI_OPROJ, a, ds::gemm_pick_bn(rows, a.N, cus), cus, st)) return hip_fail(e, "o gemm launch");
+  a.a = ctx; a.bias = hp(L->w.b_o); a.out = x2; a.resid = x; a.N = H; a.K = H;
+  if (hipError_t e = gemm(ds::EPI_OPROJ, a, L->w.w_o, L->w.s_o)) return hip_fail(e, "o gemm launch");
 
   // 4: f = GeLU(LN2(x2) W1^T + b1)
   if (hipError_t e = ds::launch_ln_rows(true, x2, hp(L->w.ln2_g), hp(L->w.ln2_b), h, rows, H, d.ln_eps, st))
     return hip_fail(e, "ln2 launch");
   a = g;
-  a.a = h; a.w = hp(L->w.w_ff1); a.bias = hp(L->w.b_ff1); a.out = f; a.N = F; a.K = H;
-  if (hipError_t e = ds::launch_gemm(ds::EPI_FF1, a, ds::gemm_pick_bn(rows, a.N, cus), cus, st)) return hip_fail(e, "ff1 gemm launch");
+  a.a = h; a.bias = hp(L->w.b_ff1); a.out = f; a.N = F; a.K = H;
+  if (hipError_t e = gemm(ds::EPI_FF1, a, L->w.w_ff1, L->w.s_ff1)) return hip_fail(e, "ff1 gemm launch");
 
   // 5: y = x2 + f W2^T + b2, then d_len += ntok
   a = g;
-  a.a = f; a.w = hp(L->w.w_ff2); a.bias = hp(L->w.b_ff2); a.out = y; a.resid = x2; a.N = H; a.K = F;
-  if (hipError_t e = ds::launch_gemm(ds::EPI_FF2, a, ds::gemm_pick_bn(rows, a.N, cus), cus, st)) return hip_fail(e, "ff2 gemm launch");
+  a.a = f; a.bias = hp(L->w.b_ff2); a.out = y; a.resid = x2; a.N = H; a.K = F;
+  if (hipError_t e = gemm(ds::EPI_FF2, a, L->w.w_ff2, L->w.s_ff2)) return hip_fail(e, "ff2 gemm launch");
   if (hipError_t e = ds::launch_len_advance(kv->d_len, batch, ntok, kv->capacity, st)) return hip_fail(e, "len advance launch");
   if (kv->h_len)
     for (int b = 0; b < batch; ++b) kv->h_len[b] += ntok;
@@ -179,7 +217,8 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  if (use_mfma(L->desc, rows)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, st);
+  if (use_mfma(L->desc, rows)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, false, st);
+  if (use_skinny(L->desc, rows)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, true, st);
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
   const int H = d.hidden, F = d.ffn;
 
