@@ -51,9 +51,9 @@ struct AttnPrefillArgs {
   float scale;            // 1/sqrt(head_dim)
 };
 
-// BN (columns per workgroup tile) that best fills `cus` compute units for an M x N output.
-int gemm_pick_bn(int M, int N, int cus);
-hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int bn, int cus, hipStream_t st);
+// Tile configuration for an M x N x K product on `cus` compute units.
+int gemm_pick(int M, int N, int K, int cus);
+hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int cfg, hipStream_t st);
 // LayerNorm of `rows` rows of H elements (fp32 or fp16 input) into fp16.
 hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const half_t* b, half_t* out, int rows, int H,
                           float eps, hipStream_t st);

@@ -48,26 +48,16 @@ __device__ __forceinline__ lds_void* lds_ptr(const void* p) {
 template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-__device__ __forceinline__ void wait_vm_dyn(int n) {
-  switch (n) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<1>(); break;
-    case 2: wait_vm<2>(); break;
-    case 3: wait_vm<3>(); break;
-    case 4: wait_vm<4>(); break;
-    case 5: wait_vm<5>(); break;
-    case 6: wait_vm<6>(); break;
-    case 7: wait_vm<7>(); break;
-    case 8: wait_vm<8>(); break;
-    case 9: wait_vm<9>(); break;
-    case 10: wait_vm<10>(); break;
-    case 11: wait_vm<11>(); break;
-    case 12: wait_vm<12>(); break;
-    case 13: wait_vm<13>(); break;
-    case 14: wait_vm<14>(); break;
-    default: wait_vm<15>(); break;
+template <int N> __device__ __forceinline__ void wait_vm_upto(int n) {
+  if constexpr (N == 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= N) wait_vm<N>();
+    else wait_vm_upto<N - 1>(n);
   }
 }
+// s_waitcnt vmcnt(n) for a wave-uniform n (n above 47 waits for 47).
+__device__ __forceinline__ void wait_vm_dyn(int n) { wait_vm_upto<47>(n); }
 
 // Workgroup barrier that waits only for this wave's LDS operations, not for its outstanding global
 // loads (a __syncthreads() would also drain the prefetched stages of the GEMM ring).
@@ -206,24 +196,25 @@ __global__ __launch_bounds__(256) void ln_row_wg_kernel(const IT* __restrict__ x
 }
 
 // ------------------------------------------------------------------ GEMM
-constexpr int kBM = 128, kBK = 64, kGemmThreads = 256;
-#ifndef DS_GEMM_STAGES
-#define DS_GEMM_STAGES 2
-#endif
-constexpr int kStages = DS_GEMM_STAGES;
+// Workgroup tile BM x BN, four waves in a 2 x 2 grid (each a (BM/2) x (BN/2) quarter of 16 x 16
+// MFMA blocks), k-steps of 64 staged through an ST-deep LDS ring by direct-to-LDS buffer loads.
+// Each k-step is two halves of 32: the operand reads of one half are issued between the products
+// of the other, and one barrier per k-step both publishes the next stage and frees the last one.
+constexpr int kBK = 64, kGemmThreads = 256;
 
-template <int BN> struct GemmShape {
-  static constexpr int WN = BN / 2;               // columns of one wave's quarter
-  static constexpr int FM = 4, FN = WN / 16;      // 16x16 MFMA blocks per wave
-  static constexpr int A_BYTES = kBM * kBK * 2;   // 16 KB
-  static constexpr int B_BYTES = BN * kBK * 2;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LOADS = (kBM + BN) / 8;    // 1 KB wave loads (8 rows x 128 B) per stage
-  static constexpr int NJ = (LOADS + 3) / 4;      // per wave, at most
-  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
+// KG = 2 splits every k-step between two groups of four waves (one 32-wide half each) and adds
+// the two partial tiles through LDS at the end: two waves per SIMD with one workgroup per CU.
+template <int BM, int BN, int ST, int KG> struct GemmShape {
+  static constexpr int THREADS = kGemmThreads * KG;
+  static constexpr int WM = BM / 2, WN = BN / 2;  // one wave's quarter
+  static constexpr int FM = WM / 16, FN = WN / 16;  // 16x16 MFMA blocks per wave
+  static constexpr int A_BYTES = BM * kBK * 2;
+  static constexpr int STAGE = (BM + BN) * kBK * 2;
+  static constexpr int LDS = ST * STAGE;
+  static_assert(BM % 64 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(ST >= 2, "the ring needs two stages");
+  static_assert(KG == 1 || (KG == 2 && LDS >= 4 * FM * FN * 1024), "the partial tiles must fit the ring");
 };
-
-template <int BN> constexpr size_t gemm_lds_bytes() { return (size_t)kStages * GemmShape<BN>::STAGE; }
 
 // Swizzled byte offset of (row, 16-byte chunk) in a 128-byte-row LDS tile: chunk c of row r sits
 // at position c ^ (r % 8), so 16 consecutive rows read at one chunk spread over all banks.
@@ -231,33 +222,65 @@ __device__ __forceinline__ uint32_t swz(int row, int chunk) {
   return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
 }
 
-// This wave's share of one stage: wave loads u < n, each a per-lane global byte offset at k = 0
-// (kOutOfRange for rows past the matrix), its LDS byte offset in the stage, and its operand.
-constexpr int kMaxLoadsPerWave = 16;
-template <int NJ> struct LoadPlan {
-  static_assert(NJ <= kMaxLoadsPerWave, "too many wave loads per stage");
-  uint32_t voff[kMaxLoadsPerWave];
-  uint32_t ldso[kMaxLoadsPerWave];
-  bool isa[kMaxLoadsPerWave];
-  int n;
-};
-
-// Issue this wave's loads of k-step kt into its ring stage. Buffer descriptors are built here from
-// plain pointers: the host compiler rejects the descriptor type as a parameter (and, inside a
-// lambda, silently drops the kernel's launch stub).
-__device__ __forceinline__ void issue_stage(unsigned char* smem, int stage_bytes, int kt, const GemmArgs& g,
-                                            const uint32_t* voff, const uint32_t* ldso, const bool* isa, int n) {
+// This wave's loads of one stage. Wave load j of the workgroup (j = wave + 4u) fills bytes
+// [1024 j, 1024 j + 1024) of the stage with 8 rows of 128 bytes: A rows m0 + 8j + 0..7 for
+// j < BM/8, then W rows n0 + 8(j - BM/8) + 0..7. Lane L carries row L/8, logical chunk
+// (L%8) ^ (L/8), which lands at physical chunk L%8, as swz() expects; va / vw are the lane's byte
+// offsets for u = 0 at k = 0. Rows past the matrix lie past the descriptor's size and load zeros.
+// A k-step past the end (valid false) is requested out of range: it loads zeros into a stage that
+// is never read, and keeps the number of loads per step fixed.
+// With two wave groups, group 0 loads the A rows and group 1 the W rows (wave is then the index
+// within the group).
+template <int BM, int BN, bool DO_A, bool DO_W>
+__device__ __forceinline__ void issue_stage(unsigned char* stage, int wave, uint32_t koff, bool valid,
+                                            const GemmArgs& g, uint32_t va, uint32_t vw, uint32_t row_step) {
   const rsrc_t ra = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.K * 2));
   const rsrc_t rw = make_rsrc(g.w, (uint32_t)((size_t)g.N * g.K * 2));
-  unsigned char* base = smem + (kt % kStages) * stage_bytes;
-  const uint32_t koff = (uint32_t)(kt * kBK * 2);
+  if constexpr (DO_A) {
 #pragma unroll
-  for (int u = 0; u < kMaxLoadsPerWave; ++u) {
-    if (u < n) {
-      const uint32_t off = voff[u] == kOutOfRange ? kOutOfRange : voff[u] + koff;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isa[u] ? ra : rw, lds_ptr(base + ldso[u]), 16, off, 0, 0, 0);
-    }
+    for (int u = 0; u < BM / 32; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(stage + (wave + 4 * u) * 1024), 16,
+                                               valid ? va + u * row_step + koff : kOutOfRange, 0, 0, 0);
   }
+  if constexpr (DO_W) {
+#pragma unroll
+    for (int u = 0; u < BN / 32; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(stage + BM * 128 + (wave + 4 * u) * 1024), 16,
+                                               valid ? vw + u * row_step + koff : kOutOfRange, 0, 0, 0);
+  }
+}
+
+// One wave's operands of one 32-wide half (ks) of a stage: FM A blocks and FN W blocks of 16 rows;
+// lane l takes row l%16, k-chunk l/16 (8 halves), the MFMA operand layout.
+template <typename S>
+__device__ __forceinline__ void read_half(const unsigned char* stage, int ks, int arow, int brow, int fch,
+                                          half8_t (&af)[S::FM], half8_t (&bf)[S::FN]) {
+#pragma unroll
+  for (int a = 0; a < S::FM; ++a)
+    af[a] = *reinterpret_cast<const half8_t*>(stage + swz(arow + 16 * a, 4 * ks + fch));
+#pragma unroll
+  for (int b = 0; b < S::FN; ++b)
+    bf[b] = *reinterpret_cast<const half8_t*>(stage + S::A_BYTES + swz(brow + 16 * b, 4 * ks + fch));
+}
+
+// The products of one half, with the FM + FN operand reads issued just before (for the other half)
+// spread between them: one read after every second product.
+template <typename S>
+__device__ __forceinline__ void mfma_half(float4_t (&acc)[S::FM][S::FN], const half8_t (&af)[S::FM],
+                                          const half8_t (&bf)[S::FN]) {
+#pragma unroll
+  for (int a = 0; a < S::FM; ++a)
+#pragma unroll
+    for (int b = 0; b < S::FN; ++b)
+      acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < S::FM + S::FN; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  constexpr int rest = S::FM * S::FN - 2 * (S::FM + S::FN);
+  static_assert(rest >= 0, "too few products per half to cover its reads");
+  if constexpr (rest > 0) __builtin_amdgcn_sched_group_barrier(0x008, rest, 0);
 }
 
 template <int EPI>
@@ -289,49 +312,111 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& g, int m, int n, 
   }
 }
 
-template <int BN, int EPI>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
-  typedef GemmShape<BN> S;
+// Epilogue of one wave's FM x FN blocks of 16 x 16 at rows mb.., columns nb..: lane l holds
+// C[16a + 4(l/16) + r][16b + l%16]. Column terms (bias, destination) are computed once per column
+// and row terms once per row.
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, int mb, int nb, const float4_t (&acc)[FM][FN], int lane) {
+  const int frow = lane & 15, fch = lane >> 4;
+  float bias[FN];
+  size_t col[FN];  // EPI_QKV: offset within the q row or within a sequence's head-major cache block
+  int kind[FN];  // EPI_QKV: 0 q, 1 k cache, 2 v cache; all: -1 past N
+#pragma unroll
+  for (int b = 0; b < FN; ++b) {
+    const int n = nb + 16 * b + frow;
+    kind[b] = -1;
+    col[b] = n;
+    bias[b] = 0.f;
+    if (n < g.N) {
+      bias[b] = (float)g.bias[n];
+      kind[b] = 0;
+      if constexpr (EPI == EPI_QKV) {
+        const int H = g.hidden;
+        if (n >= H) {
+          int nn = n - H;
+          kind[b] = nn < H ? 1 : 2;
+          nn = nn < H ? nn : nn - H;
+          const int j = nn / g.head_dim;
+          col[b] = (size_t)j * g.cap * g.head_dim + (nn - j * g.head_dim);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mb + 16 * a + 4 * fch + r;
+      if (m >= g.M) continue;
+      if constexpr (EPI == EPI_QKV) {
+        const int H = g.hidden;
+        const int bb = m / g.tokens, t = m - bb * g.tokens;
+        const int pos = g.d_len[bb] + t;
+        // the host rejects a full cache; a bad device length writes no cache row
+        const bool okc = pos >= 0 && pos < g.cap;
+        const size_t rc = ((size_t)bb * g.heads * g.cap + (okc ? pos : 0)) * g.head_dim;
+        half_t* q = static_cast<half_t*>(g.out) + (size_t)m * H;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+          const half_t z = (half_t)(acc[a][b][r] + bias[b]);
+          if (kind[b] == 0) q[col[b]] = z;
+          else if (kind[b] > 0 && okc) (kind[b] == 1 ? g.k_cache : g.v_cache)[rc + col[b]] = z;
+        }
+      } else {
+        const size_t row = (size_t)m * g.N;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+          if (kind[b] < 0) continue;
+          const float z = acc[a][b][r] + bias[b];
+          const size_t i = row + col[b];
+          if constexpr (EPI == EPI_OPROJ) {
+            static_cast<float*>(g.out)[i] = (float)static_cast<const half_t*>(g.resid)[i] + z;
+          } else if constexpr (EPI == EPI_FF1) {
+            static_cast<half_t*>(g.out)[i] = (half_t)gelu(z, g.gelu_tanh != 0);
+          } else {
+            static_cast<half_t*>(g.out)[i] = (half_t)(static_cast<const float*>(g.resid)[i] + z);
+          }
+        }
+      }
+    }
+}
+
+// Loads of one stage by this wave (both operands, or its group's operand with two groups).
+template <int BM, int BN, int KG>
+__device__ __forceinline__ void issue_mine(unsigned char* stage, int q, int grp, int j, int nk, const GemmArgs& g,
+                                           uint32_t va, uint32_t vw, uint32_t row_step) {
+  const uint32_t koff = (uint32_t)(j * kBK * 2);
+  if constexpr (KG == 1) {
+    issue_stage<BM, BN, true, true>(stage, q, koff, j < nk, g, va, vw, row_step);
+  } else {
+    if (grp == 0) issue_stage<BM, BN, true, false>(stage, q, koff, j < nk, g, va, vw, row_step);
+    else issue_stage<BM, BN, false, true>(stage, q, koff, j < nk, g, va, vw, row_step);
+  }
+}
+
+template <int BM, int BN, int ST, int KG, int EPI>
+__global__ __launch_bounds__(kGemmThreads * KG) void gemm_kernel(const GemmArgs g) {
+  typedef GemmShape<BM, BN, ST, KG> S;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load set-up stays scalar
-  const int wm = wave & 1, wn = wave >> 1;
+  const int q = wave & 3, grp = wave >> 2;  // quadrant; k-group (KG = 2)
+  const int wm = q & 1, wn = q >> 1;
 
   // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a contiguous tile range.
   const int T = g.tiles_m * g.tiles_n, i = blockIdx.x;
   const int x = i & 7, per = T >> 3, rem = T & 7;
   const int t = x * per + min(x, rem) + (i >> 3);
   const int tm = t % g.tiles_m, tn = t / g.tiles_m;
-  const int m0 = tm * kBM, n0 = tn * BN;
-  const int M = g.M, N = g.N, K = g.K;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int K = g.K;
 
-  // This wave's wave loads j = wave + 4u: 8 rows of the A tile (j < 16) or of the W tile. Lane L
-  // fills LDS bytes 16L..16L+15 of the load's 1 KB: row L/8, physical chunk L%8, which holds the
-  // logical chunk (L%8) ^ row; eight lanes read one whole 128-byte line of a row.
-  const int lr = lane >> 3;
-  const int lc = (lane & 7) ^ lr;
-  LoadPlan<S::NJ> plan;
-  plan.n = 0;
-#pragma unroll
-  for (int u = 0; u < S::NJ; ++u) {
-    const int j = wave + 4 * u;
-    plan.voff[u] = kOutOfRange;
-    plan.ldso[u] = 0;
-    plan.isa[u] = true;
-    if (j < S::LOADS) {
-      ++plan.n;
-      if (j < kBM / 8) {
-        const int r = m0 + 8 * j + lr;
-        plan.voff[u] = r < M ? (uint32_t)(((size_t)r * K + lc * 8) * 2) : kOutOfRange;
-        plan.ldso[u] = (uint32_t)(j * 1024);
-      } else {
-        const int r = n0 + 8 * (j - kBM / 8) + lr;
-        plan.voff[u] = r < N ? (uint32_t)(((size_t)r * K + lc * 8) * 2) : kOutOfRange;
-        plan.ldso[u] = (uint32_t)(S::A_BYTES + (j - kBM / 8) * 1024);
-        plan.isa[u] = false;
-      }
-    }
-  }
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+  const uint32_t row_step = (uint32_t)(32 * K * 2);  // 4 wave loads = 32 rows
+  const uint32_t va = (uint32_t)(((size_t)(m0 + 8 * q + lr) * K + lc * 8) * 2);
+  const uint32_t vw = (uint32_t)(((size_t)(n0 + 8 * q + lr) * K + lc * 8) * 2);
+  // this wave's wave loads per stage
+  const int nl = KG == 1 ? (BM + BN) / 32 : (grp == 0 ? BM / 32 : BN / 32);
   const int nk = K / kBK;
   float4_t acc[S::FM][S::FN];
 #pragma unroll
@@ -339,48 +424,75 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
     for (int b = 0; b < S::FN; ++b) acc[a][b] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+  // k-step j lives in stage j % ST. Every step requests exactly one stage (out of range past the
+  // end), so when step kt+1's stage must be complete, the loads allowed in flight are always the
+  // ST - 2 stages requested after it.
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < nk) issue_stage(smem, S::STAGE, s, g, plan.voff, plan.ldso, plan.isa, plan.n);
+  for (int s = 0; s < ST; ++s) issue_mine<BM, BN, KG>(smem + s * S::STAGE, q, grp, s, nk, g, va, vw, row_step);
 
-  const int frow = lane & 15, fch = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    // stages kt+1 .. min(kt+kStages-2, nk-1) may stay in flight
-    const int ahead = min(kStages - 2, nk - 1 - kt);
-    wait_vm_dyn(ahead * plan.n);
-    lds_barrier();
-    if (kt + kStages - 1 < nk) issue_stage(smem, S::STAGE, kt + kStages - 1, g, plan.voff, plan.ldso, plan.isa, plan.n);
-    const unsigned char* As = smem + (kt % kStages) * S::STAGE;
-    const unsigned char* Bs = As + S::A_BYTES;
-    // two k-substeps of 32 per stage; all operand reads first, so the MFMAs of the first substep
-    // overlap the reads of the second
-    half8_t af[2][S::FM], bf[2][S::FN];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int a = 0; a < S::FM; ++a)
-        af[ks][a] = *reinterpret_cast<const half8_t*>(As + swz(wm * 64 + 16 * a + frow, 4 * ks + fch));
-#pragma unroll
-      for (int b = 0; b < S::FN; ++b)
-        bf[ks][b] = *reinterpret_cast<const half8_t*>(Bs + swz(wn * S::WN + 16 * b + frow, 4 * ks + fch));
+  const int fch = lane >> 4;
+  const int arow = wm * S::WM + (lane & 15), brow = wn * S::WN + (lane & 15);
+  half8_t a0[S::FM], b0[S::FN], a1[S::FM], b1[S::FN];
+  wait_vm_dyn((ST - 1) * nl);
+  lds_barrier();
+  if constexpr (KG == 1) {
+    read_half<S>(smem, 0, arow, brow, fch, a0, b0);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      unsigned char* cur = smem + (kt % ST) * S::STAGE;
+      read_half<S>(cur, 1, arow, brow, fch, a1, b1);
+      mfma_half<S>(acc, a0, b0);
+      // step kt+1's stage is in LDS and every wave has finished reading step kt's
+      wait_vm_dyn((ST - 2) * nl);
+      lds_barrier();
+      issue_mine<BM, BN, KG>(cur, q, grp, kt + ST, nk, g, va, vw, row_step);
+      read_half<S>(smem + ((kt + 1) % ST) * S::STAGE, 0, arow, brow, fch, a0, b0);
+      mfma_half<S>(acc, a1, b1);
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    read_half<S>(smem + ((nk - 1) % ST) * S::STAGE, 1, arow, brow, fch, a1, b1);
+    mfma_half<S>(acc, a0, b0);
+    mfma_half<S>(acc, a1, b1);
+  } else {
+    // this group's half of step kt+1 is read under the products of step kt
+    auto step = [&](int kt, half8_t (&xa)[S::FM], half8_t (&xb)[S::FN], half8_t (&ya)[S::FM], half8_t (&yb)[S::FN]) {
+      wait_vm_dyn((ST - 2) * nl);
+      lds_barrier();
+      issue_mine<BM, BN, KG>(smem + (kt % ST) * S::STAGE, q, grp, kt + ST, nk, g, va, vw, row_step);
+      read_half<S>(smem + ((kt + 1) % ST) * S::STAGE, grp, arow, brow, fch, ya, yb);
+      mfma_half<S>(acc, xa, xb);
+    };
+    read_half<S>(smem, grp, arow, brow, fch, a0, b0);
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+      step(kt, a0, b0, a1, b1);
+      step(kt + 1, a1, b1, a0, b0);
+    }
+    if (kt + 1 < nk) {
+      step(kt, a0, b0, a1, b1);
+      mfma_half<S>(acc, a1, b1);
+    } else {
+      mfma_half<S>(acc, a0, b0);
+    }
+  }
+  wait_vm<0>();  // the out-of-range requests past the end
+
+  if constexpr (KG == 2) {
+    // group 1 hands its partial tile to group 0 through the (now idle) ring
+    float4_t* red = reinterpret_cast<float4_t*>(smem) + q * (S::FM * S::FN * 64) + lane;
+    lds_barrier();
+    if (grp == 1) {
 #pragma unroll
       for (int a = 0; a < S::FM; ++a)
 #pragma unroll
-        for (int b = 0; b < S::FN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ks][a], bf[ks][b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < S::FN; ++b) red[(a * S::FN + b) * 64] = acc[a][b];
+    }
+    lds_barrier();
+    if (grp == 1) return;
+#pragma unroll
+    for (int a = 0; a < S::FM; ++a)
+#pragma unroll
+      for (int b = 0; b < S::FN; ++b) acc[a][b] += red[(a * S::FN + b) * 64];
   }
-
-  // lane l holds C[4(l/16) + r][l%16] of each 16x16 block
-#pragma unroll
-  for (int a = 0; a < S::FM; ++a)
-#pragma unroll
-    for (int b = 0; b < S::FN; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        epilogue_store<EPI>(g, m0 + wm * 64 + 16 * a + 4 * fch + r, n0 + wn * S::WN + 16 * b + frow, acc[a][b][r]);
+  epilogue<EPI, S::FM, S::FN>(g, m0 + wm * S::WM, n0 + wn * S::WN, acc, lane);
 }
 
 // ------------------------------------------------------------------ attention over the cache
@@ -663,25 +775,31 @@ hipError_t launch_skinny_t(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BN, int EPI>
-hipError_t launch_gemm_bn(const GemmArgs& a0, int cus, hipStream_t st) {
+template <int BM, int BN, int ST, int KG, int EPI>
+hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t st) {
+  typedef GemmShape<BM, BN, ST, KG> S;
   GemmArgs a = a0;
-  a.tiles_m = (a.M + kBM - 1) / kBM;
+  a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
-  (void)cus;
-  const size_t lds = gemm_lds_bytes<BN>();
   // above the default 64 KB of dynamic LDS; set on every launch (cheap, and per device)
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BN, EPI>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, ST, KG, EPI>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_kernel<BN, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(kGemmThreads), lds, st, a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, ST, KG, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(S::THREADS), S::LDS, st, a);
   return hipGetLastError();
 }
 
+// The two tile configurations (128 x 160 tiles either way; the rows, columns and k-step count of a
+// workgroup are those of the ring above):
+//   0: two-stage ring, four waves, two workgroups per CU, for products with at least two tiles
+//      per CU (the next tiles' loads overlap the current ones' products);
+//   1: three-stage ring, two groups of four waves splitting each k-step, one workgroup per CU, for
+//      products with at most one tile per CU (deeper prefetch, two waves per SIMD).
 template <int EPI>
-hipError_t launch_gemm_epi(const GemmArgs& a, int bn, int cus, hipStream_t st) {
-  switch (bn) {
-    case 160: return launch_gemm_bn<160, EPI>(a, cus, st);
+hipError_t launch_gemm_epi(const GemmArgs& a, int cfg, hipStream_t st) {
+  switch (cfg) {
+    case 0: return launch_gemm_t<128, 160, 2, 1, EPI>(a, st);
+    case 1: return launch_gemm_t<128, 160, 3, 2, EPI>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -690,14 +808,12 @@ hipError_t launch_gemm_epi(const GemmArgs& a, int bn, int cus, hipStream_t st) {
 
 using namespace prefill;
 
-// 128 x 160 tiles with a two-stage ring (72 KB of LDS) let two workgroups share a CU, which hides
-// more load latency than wider tiles with one workgroup per CU (measured: 256- and 320-column tiles
-// ran 1.3x-1.7x slower on the GPT-Neo-2.7B prefill GEMMs).
-int gemm_pick_bn(int M, int N, int cus) {
-  (void)M;
-  (void)N;
-  (void)cus;
-  return 160;
+// Measured on the GPT-Neo-2.7B prefill products (2048 rows): configuration 0 runs the 768- and
+// 1024-tile products 1.1x-1.4x faster than 1, and 1 the 256-tile ones 1.2x-1.3x faster than 0.
+int gemm_pick(int M, int N, int K, int cus) {
+  (void)K;
+  const long tiles = (long)((M + 127) / 128) * ((N + 159) / 160);
+  return tiles <= cus ? 1 : 0;
 }
 
 hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, hipStream_t st) {
@@ -716,13 +832,14 @@ hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, hipS
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int bn, int cus, hipStream_t st) {
+hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int cfg, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.K < kBK || a.K % kBK) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(a, bn, cus, st);
-    case EPI_OPROJ: return launch_gemm_epi<EPI_OPROJ>(a, bn, cus, st);
-    case EPI_FF1: return launch_gemm_epi<EPI_FF1>(a, bn, cus, st);
-    case EPI_FF2: return launch_gemm_epi<EPI_FF2>(a, bn, cus, st);
+    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(a, cfg, st);
+    case EPI_OPROJ: return launch_gemm_epi<EPI_OPROJ>(a, cfg, st);
+    case EPI_FF1: return launch_gemm_epi<EPI_FF1>(a, cfg, st);
+    case EPI_FF2: return launch_gemm_epi<EPI_FF2>(a, cfg, st);
   }
   return hipErrorInvalidValue;
 }

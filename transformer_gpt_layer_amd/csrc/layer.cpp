@@ -148,7 +148,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
       a.w = static_cast<const ds::half_t*>(w);
     }
     if (skinny) return ds::launch_skinny(epi, i8, a, st);
-    return ds::launch_gemm(epi, a, ds::gemm_pick_bn(a.M, a.N, cus), cus, st);
+    return ds::launch_gemm(epi, a, ds::gemm_pick(a.M, a.N, a.K, cus), st);
   };
 
   // 1: h = LN1(x); [q | k | v] = h Wqkv^T + bqkv, k and v into the cache rows d_len[b] + t
