@@ -163,10 +163,12 @@ int ds_dequantize_i8(const int8_t* q, const void* s, float* w, int32_t n, int32_
  * Persistent multi-layer decode. A stack binds n_layers layers that share one description (same
  * shapes and dtypes) to their caches (caches[l] for layers[l], all of one capacity and at least
  * max_batch sequences) and runs a whole decode step -- regions 1-4 of [KP] section 三 3.2 for every
- * layer in turn -- as one cooperative launch whose workgroups all stay resident; the phase
- * boundaries of [KP] section 三 3.1 become grid-wide barriers. The cache structs are copied: their
- * k, v, d_len and h_len pointers must stay valid for the stack's life. The library allocates two
- * small device buffers per stack (layer table, barrier counters), freed by ds_stack_destroy.
+ * layer in turn -- as one cooperative launch whose workgroups all stay resident; at the phase
+ * boundaries of [KP] section 三 3.1 each workgroup waits for exactly the values of the previous
+ * phase it reads (stored with tags naming launch, layer and phase). The cache structs are copied:
+ * their k, v, d_len and h_len pointers must stay valid for the stack's life. The library allocates
+ * two small device buffers per stack (layer table; launch counter, exit count and error flag),
+ * freed by ds_stack_destroy.
  * Requirements: max_batch 1..4; hidden <= 8192; hidden and ffn multiples of 256 (fp32 weights),
  * 512 (fp16) or 1024 (int8); each cache under 2 GiB. Errors: DS_ERR_NULL, DS_ERR_SHAPE,
  * DS_ERR_ALIGN, DS_ERR_UNSUPPORTED, DS_ERR_HIP.
@@ -186,15 +188,15 @@ int32_t ds_stack_groups(const ds_stack_t* stack);
 /* One decode step through all layers: x, y [batch][hidden] in act_dtype (y may alias x). Writes
  * each layer's new K/V row at its d_len[b], attends over rows 0..d_len[b], and after the last
  * layer advances every layer's d_len[b] (and h_len[b] when given) by one. Enqueued on stream.
- * Calls on one stack must not overlap in time (they share its barrier counters). */
+ * Calls on one stack must not overlap in time (they share its counters). */
 int ds_stack_forward_decode(ds_stack_t* stack, const void* x, void* y, int32_t batch,
                             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Synchronizes the device and reports whether a step of this stack hit its grid-barrier timeout
- * (DS_ERR_HIP, with the barrier state reset so the stack can run again) or not (DS_OK). */
+/* Synchronizes the device and reports whether a step of this stack hit its wait timeout
+ * (DS_ERR_HIP, with the counters reset so the stack can run again) or not (DS_OK). */
 int ds_stack_check(ds_stack_t* stack);
 
-/* Per-barrier wait limit of the persistent kernel (default 2 s); on expiry the kernel raises an
+/* Limit of each wait of the persistent kernel (default 2 s); on expiry the kernel raises an
  * error flag and every workgroup leaves the launch. */
 int ds_stack_set_timeout_us(ds_stack_t* stack, int64_t microseconds);
 

@@ -279,7 +279,7 @@ class Stack:
         return y
 
     def check(self):
-        """Synchronize; raise if a step hit the grid-barrier timeout (the state is then reset)."""
+        """Synchronize; raise if a step hit the wait timeout (the state is then reset)."""
         check(lib().ds_stack_check(self._h), "ds_stack_check")
 
     def set_timeout_us(self, us: int):

@@ -35,8 +35,8 @@ __host__ __device__ inline uint32_t stack_tag(uint32_t launch, int l, int ph) {
 }
 enum { TAG_Q = 0, TAG_PART = 1, TAG_CTX = 2, TAG_X2 = 3, TAG_F = 4, TAG_Y = 5 };
 
-// Workgroup shape: kStackSyncWaves waves stage activations, reduce, run the epilogues, attention
-// and the grid barriers; kStackWorkers waves stream the weights and compute the row dot products.
+// Workgroup shape: kStackSyncWaves waves stage activations, reduce, run the epilogues and attention
+// and exchange tagged values; kStackWorkers waves stream the weights and compute the row dot products.
 constexpr int kStackSyncWaves = 4;
 constexpr int kStackWorkers = 12;
 constexpr int kStackWaves = kStackSyncWaves + kStackWorkers;

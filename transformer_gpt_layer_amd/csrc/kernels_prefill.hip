@@ -672,7 +672,7 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(const Gemm
   const int n0 = blockIdx.x * 16;
   if (EPI == EPI_QKV && blockIdx.x == 0 && g.attn_counters)
     for (int i = threadIdx.x; i < g.n_counters; i += blockDim.x) g.attn_counters[i] = 0u;
-  const int K = g.K, kq = K / KS, kb = w * kq, ke = kb + kq;
+  const int K = g.K, kq = K / KS, kb = w * kq;
   const int n = min(n0 + r, g.N - 1);  // columns past N re-read a valid row; their outputs are dropped
   const bool arow = r < g.M;
   const half_t* ap = g.a + (size_t)(arow ? r : 0) * K;

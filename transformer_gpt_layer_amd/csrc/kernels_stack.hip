@@ -5,7 +5,7 @@
 // bias; attention over the cache with the head transform folded into its addressing; the output
 // GeMM with bias and residual; LN + FF1 + bias + GELU; FF2 + bias + residual). Section 三 3.1 puts the
 // fusion boundaries where partial results must meet (the all-reduce points); here those are the
-// grid-wide barriers between phases.
+// points where a phase waits for the values of the previous one, produced by other workgroups.
 //
 // gfx950 design. One cooperative launch keeps one 16-wave workgroup per CU resident for the whole
 // step. Each projection is cut into per-workgroup row tiles; a tile is one contiguous range of the
@@ -19,13 +19,15 @@
 //    Workers issue nothing but these loads, so their in-order load counter only ever waits for
 //    the oldest slice; row partial sums go to LDS.
 //  - 4 sync waves stage each phase's activation (LayerNorm included), reduce the workers' partial
-//    sums, run the epilogues (bias, residual, GeLU, the q/k/v scatter), compute attention over
-//    the cache and take the grid barriers.
-// So weight streaming continues straight through the barriers, the activation staging and the
-// epilogues. Activations that cross workgroups are written and read with sc1 buffer operations
-// (at the device coherence point, past the per-XCD L2 copies); barrier arrivals are agent-scope
-// atomics spread over 16 counters. Every wait, in LDS or on the grid, is bounded by a wall-clock
-// timeout that raises the error flag, after which every wave leaves the kernel.
+//    sums, run the epilogues (bias, residual, GeLU, the q/k/v scatter) and compute attention over
+//    the cache.
+// So weight streaming continues straight through the waits between phases, the activation
+// staging and the epilogues. A value that crosses workgroups is stored as a (value, tag) pair,
+// the tag naming the launch, layer and phase that produced it, with sc1 buffer operations (at the
+// device coherence point, past the per-XCD L2 copies); a consumer polls exactly the pairs it
+// reads until their tags are current, so the grid never meets at a barrier. Every wait, in LDS or
+// on other workgroups' values, is bounded by a wall-clock timeout that raises the error flag,
+// after which every wave leaves the kernel.
 #include "ds_device.hpp"
 #include "ds_stack.hpp"
 
@@ -59,22 +61,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ u32x4 coh_load16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxCoherent);
 }
-__device__ __forceinline__ uint32_t coh_load4(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kAuxCoherent);
-}
 __device__ __forceinline__ void coh_store4(rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kAuxCoherent);
 }
 
-// coherent scalar access in the activation type
-template <typename AT> __device__ __forceinline__ float coh_ld_act(rsrc_t r, uint32_t idx);
-template <> __device__ __forceinline__ float coh_ld_act<float>(rsrc_t r, uint32_t idx) {
-  return as_f32(coh_load4(r, idx * 4));
-}
-template <> __device__ __forceinline__ float coh_ld_act<half_t>(rsrc_t r, uint32_t idx) {
-  const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(r, idx * 2, 0, kAuxCoherent);
-  return (float)__builtin_bit_cast(half_t, h);
-}
+// coherent scalar store in the activation type
 template <typename AT> __device__ __forceinline__ void coh_st_act(rsrc_t r, uint32_t idx, float v);
 template <> __device__ __forceinline__ void coh_st_act<float>(rsrc_t r, uint32_t idx, float v) {
   coh_store4(r, idx * 4, __builtin_bit_cast(uint32_t, v));
@@ -314,9 +305,6 @@ __device__ __forceinline__ Geo phase_geo(const StackArgs& a, int SL, int g, int 
 
 __device__ __forceinline__ const void* phase_w(const StackLayer& L, int ph) {
   return ph == 0 ? L.w_qkv : ph == 1 ? L.w_o : ph == 2 ? L.w_ff1 : L.w_ff2;
-}
-__device__ __forceinline__ const void* phase_s(const StackLayer& L, int ph) {
-  return ph == 0 ? L.s_qkv : ph == 1 ? L.s_o : ph == 2 ? L.s_ff1 : L.s_ff2;
 }
 
 // ------------------------------------------------------------------ worker waves

@@ -3,7 +3,7 @@
 // A stack binds L layers that share one description to their L KV caches and runs a whole decode
 // step -- every fusion region of every layer ("DeepSpeed Inference 内核优化深度解析", section 三 3.2)
 // -- in one cooperative launch. The library owns two small device buffers per stack: the table of
-// layer pointers and the grid-barrier / attention-merge counters (zero at rest).
+// layer pointers and the sync block (launch counter, exit count, error flag).
 #include <hip/hip_runtime.h>
 
 #include <cstring>
