@@ -34,9 +34,14 @@ struct GemmArgs {
   const int8_t* wq;
   const half_t* wscale;
   int group;
-  // skinny QKV launch: zeroes these attention merge counters first
+  // skinny QKV launch: zeroes these attention merge counters (and the split counters below) first
   uint32_t* attn_counters;
   int n_counters;
+  // skinny launches with K split over workgroups: per-column-block partial tiles and arrival
+  // counters (zero at rest: the last arriver of a block resets its counter)
+  float* sk_part;
+  uint32_t* sk_cnt;
+  int n_sk_cnt;
 };
 
 // Attention of `tokens` new rows per sequence over keys 0..d_len[b]+tokens-1 of the cache (the new
@@ -60,7 +65,11 @@ hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const hal
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t st);
 // The same product and epilogues for M <= 16 rows (decode of a few sequences): every weight row is
 // streamed once, with fp16 weights (w) or int8 codes and group-64 scales (wq, wscale, group).
-hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, hipStream_t st);
+hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, int cus, hipStream_t st);
 constexpr int kSkinnyMaxRows = 16;
+constexpr int kSkinnyMaxSplit = 8;  // K splits over workgroups at most
+// Workspace of the split skinny launches for products of up to n_max columns.
+inline size_t skinny_part_bytes(int n_max) { return (size_t)((n_max + 15) / 16) * kSkinnyMaxSplit * 64 * 16; }
+inline size_t skinny_cnt_bytes(int n_max) { return (size_t)((n_max + 15) / 16) * 4; }
 
 }  // namespace ds

@@ -638,13 +638,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
 // ------------------------------------------------------------------ skinny GEMM (M <= 16 rows)
 // A decode step of a few rows is bound by streaming the weights, so each weight row is read once
 // and the rows of the step ride along on MFMA: a workgroup owns 16 output columns (16 rows of W)
-// and its KS waves split K. Per 32-wide k step the 16 W rows are the B operand (lane l: row l%16,
-// k chunk l/16, one 16-byte load) and the activation rows the A operand (rows past M read as
-// zeros); v_mfma_f32_16x16x32_f16 leaves C[4(l/16)+i][l%16] in lane l. int8 weights: a lane's
-// 16-byte load is 16 codes (k 16j..16j+15, j = l/16) of a 64-k block (one quantization group);
-// the block's two MFMAs take k 16j..16j+7 and then 16j+8..16j+15 in lane group j (the sum over k
-// does not depend on that order), the activations are loaded in the same order, the codes become
-// fp16 exactly, and the block's product is scaled by the row's group scale before accumulating.
+// and its waves split K. Per 32-wide k step the 16 W rows are the B operand (lane l: row l%16,
+// k chunk l/16) and the activation rows the A operand (rows past M are zeros);
+// v_mfma_f32_16x16x32_f16 leaves C[4(l/16)+i][l%16] in lane l. int8 weights: a lane takes 16 codes
+// (k 16j..16j+15, j = l/16) of a 64-k block (one quantization group); the block's two MFMAs take
+// k 16j..16j+7 and then 16j+8..16j+15 in lane group j (the sum over k does not depend on that
+// order), the activations are loaded in the same order, the codes become fp16 exactly, and the
+// block's product is scaled by the row's group scale before accumulating.
 __device__ __forceinline__ half8_t i8x8_to_half8(uint32_t lo, uint32_t hi) {
   const uint32_t flip = 0x80808080u;  // q + 128 for every byte
   lo ^= flip;
@@ -657,121 +657,179 @@ __device__ __forceinline__ half8_t i8x8_to_half8(uint32_t lo, uint32_t hi) {
   return h;
 }
 
-#ifndef DS_SKINNY_KS
-#define DS_SKINNY_KS 8
-#endif
-#ifndef DS_SKINNY_U16
-#define DS_SKINNY_U16 4
-#endif
-constexpr int kSkinnyMaxWaves = DS_SKINNY_KS;  // waves (K splits) per workgroup at most
+constexpr int kSkinnyMaxWaves = 8;  // waves (K splits) per workgroup at most
+
+// The weight rows reach LDS as whole 128-byte lines through direct-to-LDS loads (8 rows x 128 B per
+// wave load, the XOR-swizzled layout of the tiled GEMM) and the B operands are read back from LDS:
+// loading them in the operand layout directly would fetch 64-byte halves of 16 rows per load.
+// Each wave owns a private ring of kSkR stages (16 rows x 128 B of W each: 64 k for fp16, 128 k
+// for int8) and the matching activation loads in registers; every load is a buffer load, so rows
+// past N and stages past the wave's range read zeros (activation rows past M are not loaded at
+// all), and each stage issues the same number of loads, which keeps the in-order load counter
+// arithmetic fixed. Products with few column blocks also split K over workgroups.
+constexpr int kSkR = 2;          // stages in flight per wave (more waves beat deeper rings: measured)
+constexpr int kSkMinStages = 8;  // stages per wave worth a wave of its own
 
 template <bool I8, int EPI>
-__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_kernel(const GemmArgs g) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, KS = blockDim.x >> 6;
-  const int r = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  if (EPI == EPI_QKV && blockIdx.x == 0 && g.attn_counters)
-    for (int i = threadIdx.x; i < g.n_counters; i += blockDim.x) g.attn_counters[i] = 0u;
-  const int K = g.K, kq = K / KS, kb = w * kq;
-  const int n = min(n0 + r, g.N - 1);  // columns past N re-read a valid row; their outputs are dropped
+__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ float4_t red[kSkinnyMaxWaves][kWave];
+  const int lane = threadIdx.x & 63, KS = blockDim.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, j = lane >> 4;
+  // workgroup = (column block cb, K part sp); its waves split the part
+  const int split = g.n_sk_cnt > 0 ? max(1, g.tiles_n) : 1;
+  const int cb = blockIdx.x / split, sp = blockIdx.x - cb * split;
+  const int n0 = cb * 16;
+  if (EPI == EPI_QKV && blockIdx.x == 0) {
+    if (g.attn_counters)
+      for (int i = threadIdx.x; i < g.n_counters; i += blockDim.x) g.attn_counters[i] = 0u;
+    if (g.sk_cnt)
+      for (int i = threadIdx.x; i < g.n_sk_cnt; i += blockDim.x) g.sk_cnt[i] = 0u;
+  }
+  const int K = g.K;
+  constexpr int SK = I8 ? 128 : 64;               // k per stage
+  constexpr int LPS = I8 ? 8 : 4;                 // loads per stage: 2 W lines-sets, A, scales
+  const int kq = K / split / KS, kb = sp * (K / split) + w * kq, ns = kq / SK;
+  const uint32_t wrow = (uint32_t)(I8 ? K : 2 * K);  // bytes per weight row
+  const rsrc_t rw = make_rsrc(I8 ? (const void*)g.wq : (const void*)g.w, (uint32_t)((size_t)g.N * wrow));
+  const rsrc_t ra = make_rsrc(g.a, (uint32_t)((size_t)g.M * K * 2));
+  const rsrc_t rs = make_rsrc(g.wscale, I8 ? (uint32_t)((size_t)g.N * (K / 64) * 2) : 0u);
+  unsigned char* ring = smem + w * (kSkR * 2048);
+  // W: wave load u of a stage covers rows n0 + 8u + L/8, logical chunk (L%8) ^ (L/8)
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+  const uint32_t w_off = (uint32_t)(n0 + lr) * wrow + (uint32_t)(I8 ? kb : 2 * kb) + lc * 16;
+  // A: row r; fp16 step s of a stage takes k 32s + 8j .. +8; int8 group g takes 64g + 16j .. +16
+  const uint32_t a_off = (uint32_t)((r * K + kb) * 2) + (uint32_t)(I8 ? 32 * j : 16 * j);
+  const uint32_t s_off = (uint32_t)((n0 + r) * (K / 64) + kb / 64) * 2;
+  u32x4 av[kSkR][I8 ? 4 : 2];
+  float sc[kSkR][2];
+  // lanes of rows past M issue no activation loads (their operand rows are zeros)
   const bool arow = r < g.M;
-  const half_t* ap = g.a + (size_t)(arow ? r : 0) * K;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (!I8) {
-    // software pipeline over blocks of U k-steps: the next block's loads are in flight while the
-    // current block is multiplied; steps past the wave's range are skipped (no load, no MFMA)
-    const half_t* wp = g.w + (size_t)n * K + kb + 8 * grp;
-    ap += kb + 8 * grp;
-    constexpr int U = DS_SKINNY_U16;
-    const int steps = kq / 32, nblk = (steps + U - 1) / U;
-    u32x4 wv[2][U], av[2][U];
-    auto load = [&](int blk, u32x4 (&w_)[U], u32x4 (&a_)[U]) {
+  auto issue = [&](int i, int slot) {
+    const bool ok = i < ns;
+    const uint32_t wk = (uint32_t)i * 128u;  // W bytes per row per stage: 128 for fp16 and int8
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int st = blk * U + u;
-        if (st < steps) {
-          w_[u] = ld16(wp + 32 * st);  // cached: the two halves of a 128-byte line come from adjacent steps
-          a_[u] = arow ? ld16(ap + 32 * st) : zero;
-        }
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(ring + slot * 2048 + u * 1024), 16,
+                                               ok ? w_off + (uint32_t)(8 * u) * wrow + wk : kOutOfRange, 0, 0, 0);
+    const uint32_t ak = (uint32_t)(i * SK * 2);
+    if constexpr (!I8) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        av[slot][t] = u32x4{0u, 0u, 0u, 0u};
+        if (arow) av[slot][t] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ak + 64 * t : kOutOfRange, 0, 0);
       }
-    };
-    auto mul = [&](int blk, const u32x4 (&w_)[U], const u32x4 (&a_)[U]) {
+    } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (blk * U + u < steps)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a_[u]), __builtin_bit_cast(half8_t, w_[u]),
-                                                       acc, 0, 0, 0);
-    };
-    load(0, wv[0], av[0]);
-    for (int blk = 0; blk < nblk; blk += 2) {
-      if (blk + 1 < nblk) load(blk + 1, wv[1], av[1]);
-      mul(blk, wv[0], av[0]);
-      if (blk + 1 >= nblk) break;
-      if (blk + 2 < nblk) load(blk + 2, wv[0], av[0]);
-      mul(blk + 1, wv[1], av[1]);
+      for (int t = 0; t < 2; ++t) {
+        av[slot][2 * t] = u32x4{0u, 0u, 0u, 0u};
+        av[slot][2 * t + 1] = u32x4{0u, 0u, 0u, 0u};
+        if (arow) {
+          av[slot][2 * t] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ak + 128 * t : kOutOfRange, 0, 0);
+          av[slot][2 * t + 1] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ak + 128 * t + 16 : kOutOfRange, 0, 0);
+        }
+        const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? s_off + (uint32_t)(2 * i + t) * 2 : kOutOfRange, 0, 0);
+        sc[slot][t] = (float)__builtin_bit_cast(half_t, h);
+      }
     }
-  } else {
-    const int8_t* wp = g.wq + (size_t)n * K + kb + 16 * grp;
-    const half_t* sp = g.wscale + (size_t)n * (K / 64) + kb / 64;
-    ap += kb + 16 * grp;
-    constexpr int U = 3;
-    const int steps = kq / 64, nblk = (steps + U - 1) / U;
-    u32x4 wv[2][U], a0[2][U], a1[2][U];
-    float sc[2][U];
-    auto load = [&](int blk, u32x4 (&w_)[U], u32x4 (&x0)[U], u32x4 (&x1)[U], float (&s_)[U]) {
+  };
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int st = blk * U + u;
-        if (st < steps) {
-          w_[u] = ld16(wp + 64 * st);  // cached: the two halves of a 128-byte line come from adjacent blocks
-          x0[u] = arow ? ld16(ap + 64 * st) : zero;
-          x1[u] = arow ? ld16(ap + 64 * st + 8) : zero;
-          s_[u] = (float)sp[st];
+  for (int i = 0; i < kSkR; ++i) issue(i, i);
+  for (int i = 0; i < ns; i += kSkR) {
+#pragma unroll
+    for (int q = 0; q < kSkR; ++q) {
+      // stage i + q complete; the kSkR - 1 stages requested after it may stay in flight
+      wait_vm<(kSkR - 1) * LPS>();
+      const unsigned char* st = ring + q * 2048;
+      if (i + q < ns) {
+        if constexpr (!I8) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const half8_t b = *reinterpret_cast<const half8_t*>(st + swz(r, 4 * t + j));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av[q][t]), b, acc, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const u32x4 c = *reinterpret_cast<const u32x4*>(st + swz(r, 4 * t + j));
+            float4_t p = {0.f, 0.f, 0.f, 0.f};
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av[q][2 * t]), i8x8_to_half8(c.x, c.y), p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av[q][2 * t + 1]), i8x8_to_half8(c.z, c.w), p, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(p[e], sc[q][t], acc[e]);
+          }
         }
       }
-    };
-    auto mul = [&](int blk, const u32x4 (&w_)[U], const u32x4 (&x0)[U], const u32x4 (&x1)[U], const float (&s_)[U]) {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (blk * U + u < steps) {
-          float4_t t = {0.f, 0.f, 0.f, 0.f};
-          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x0[u]), i8x8_to_half8(w_[u].x, w_[u].y), t, 0, 0, 0);
-          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x1[u]), i8x8_to_half8(w_[u].z, w_[u].w), t, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = fmaf(t[i], s_[u], acc[i]);
-        }
-    };
-    load(0, wv[0], a0[0], a1[0], sc[0]);
-    for (int blk = 0; blk < nblk; blk += 2) {
-      if (blk + 1 < nblk) load(blk + 1, wv[1], a0[1], a1[1], sc[1]);
-      mul(blk, wv[0], a0[0], a1[0], sc[0]);
-      if (blk + 1 >= nblk) break;
-      if (blk + 2 < nblk) load(blk + 2, wv[0], a0[0], a1[0], sc[0]);
-      mul(blk + 1, wv[1], a0[1], a1[1], sc[1]);
+      // the slot's operands are in registers before its refill is requested
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      issue(i + q + kSkR, q);
     }
   }
-  // sum the waves' K ranges, then the epilogue of C[4 grp + i][n0 + r]
-  __shared__ float4_t red[kSkinnyMaxWaves][kWave];
+  wait_vm<0>();  // the out-of-range requests past the end
+  // sum the waves' K ranges, then the epilogue of C[4 j + e][n0 + r]
   red[w][lane] = acc;
   __syncthreads();
   if (w != 0) return;
   for (int v = 1; v < KS; ++v) {
     const float4_t o = red[v][lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += o[i];
+    for (int e = 0; e < 4; ++e) acc[e] += o[e];
+  }
+  if (split > 1) {
+    // K split over workgroups: publish this part's tile (device-scope stores, complete before the
+    // arrival is counted); the last of the block's parts to arrive adds all parts in part order,
+    // so the sum does not depend on arrival order, resets the counter and runs the epilogue
+    // the block's parts: split x 1 KB, 16 bytes per lane, written and read at the device coherence
+    // point (sc1), past the per-XCD L2s
+    const rsrc_t rp = make_rsrc(g.sk_part + (size_t)cb * split * 256, (uint32_t)(split * 1024));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), rp, (uint32_t)(sp * 1024 + lane * 16), 0, 16);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the stores have completed
+    __shared__ uint32_t arrived;
+    if (lane == 0) arrived = __hip_atomic_fetch_add(g.sk_cnt + cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (*(volatile uint32_t*)&arrived != (uint32_t)(split - 1)) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = 0.f;
+    for (int q = 0; q < split; ++q) {
+      const float4_t o = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)(q * 1024 + lane * 16), 0, 16));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += o[e];
+    }
+    if (lane == 0) __hip_atomic_store(g.sk_cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) epilogue_store<EPI>(g, 4 * grp + i, n0 + r, acc[i]);
+  for (int e = 0; e < 4; ++e) epilogue_store<EPI>(g, 4 * j + e, n0 + r, acc[e]);
 }
 
 template <bool I8, int EPI>
-hipError_t launch_skinny_t(const GemmArgs& a, hipStream_t st) {
-  const int kq = I8 ? 64 : 32;  // k per MFMA block
+hipError_t launch_skinny_t(const GemmArgs& a, int cus, hipStream_t st) {
+  // as many waves as divide K evenly while each still streams at least kSkMinStages stages
+  const int kq = I8 ? 128 : 64;  // k per stage
+  const int nblk = (a.N + 15) / 16;
+  // Few column blocks (fewer than four workgroups per CU) split K over workgroups as well, as far
+  // as every part keeps kSkMinStages stages; never the QKV product, whose first workgroup clears
+  // the split counters.
+  int split = 1;
+  if (EPI != EPI_QKV && a.sk_part && a.sk_cnt && nblk <= a.n_sk_cnt)
+    while (2 * split <= kSkinnyMaxSplit && nblk * split < 4 * cus && a.K % (2 * split * kq) == 0 &&
+           a.K / (2 * split) >= kq * kSkMinStages)
+      split *= 2;
+  const int kp = a.K / split;
+  // as many waves as divide the part evenly while each still streams at least kSkMinStages stages
   int ks = kSkinnyMaxWaves;
-  while (ks > 1 && a.K % (ks * kq) != 0) ks >>= 1;
-  if (a.K % (ks * kq) != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((skinny_kernel<I8, EPI>), dim3((a.N + 15) / 16), dim3(64 * ks), 0, st, a);
+  while (ks > 1 && (kp % (ks * kq) != 0 || kp / (ks * kq) < kSkMinStages)) ks >>= 1;
+  if (kp % (ks * kq) != 0) return hipErrorInvalidValue;
+  GemmArgs g = a;
+  g.tiles_n = split;
+  if (split == 1 && EPI != EPI_QKV) g.n_sk_cnt = 0;
+  const size_t lds = (size_t)ks * kSkR * 2048;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_dma_kernel<I8, EPI>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((skinny_dma_kernel<I8, EPI>), dim3(nblk * split), dim3(64 * ks), lds, st, g);
   return hipGetLastError();
 }
 
@@ -816,12 +874,12 @@ int gemm_pick(int M, int N, int K, int cus) {
   return tiles <= cus ? 1 : 0;
 }
 
-hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, hipStream_t st) {
+hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, int cus, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.M > kSkinnyMaxRows) return hipErrorInvalidValue;
 #define DS_SK(E)                                                                                   \
   case E:                                                                                          \
-    return int8_weights ? launch_skinny_t<true, E>(a, st) : launch_skinny_t<false, E>(a, st);
+    return int8_weights ? launch_skinny_t<true, E>(a, cus, st) : launch_skinny_t<false, E>(a, cus, st);
   switch (epi) {
     DS_SK(EPI_QKV)
     DS_SK(EPI_OPROJ)

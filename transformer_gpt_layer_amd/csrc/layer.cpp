@@ -56,8 +56,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct WsLayout {
-  size_t q, part, cnt, ctx, x2, f, h, total;
-  int chunk, nchunk;
+  size_t q, part, cnt, ctx, x2, f, h, sk_part, sk_cnt, total;
+  int chunk, nchunk, n_sk_cnt;
 };
 
 WsLayout ws_layout(const ds_layer_desc& d, int rows, int cap) {
@@ -73,6 +73,11 @@ WsLayout ws_layout(const ds_layer_desc& d, int rows, int cap) {
   L.x2 = take((size_t)rows * d.hidden * 4);
   L.f = take((size_t)rows * d.ffn * 4);
   L.h = take((size_t)rows * d.hidden * 2);  // fp16 LayerNorm rows of the MFMA path
+  // partial tiles and counters of the skinny products that split K over workgroups
+  const int n_max = d.hidden > d.ffn ? d.hidden : d.ffn;
+  L.sk_part = take(ds::skinny_part_bytes(n_max));
+  L.sk_cnt = take(ds::skinny_cnt_bytes(n_max));
+  L.n_sk_cnt = (n_max + 15) / 16;
   L.total = off;
   return L;
 }
@@ -137,6 +142,11 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   g.k_cache = static_cast<ds::half_t*>(kv->k);
   g.v_cache = static_cast<ds::half_t*>(kv->v);
   g.M = rows;
+  if (skinny) {
+    g.sk_part = reinterpret_cast<float*>(base + W.sk_part);
+    g.sk_cnt = reinterpret_cast<uint32_t*>(base + W.sk_cnt);
+    g.n_sk_cnt = W.n_sk_cnt;
+  }
   const bool i8 = d.weight_dtype == DS_I8;
   g.group = d.quant_group;
   // one weight matrix (fp16, or int8 codes with their scales) and its product
@@ -147,7 +157,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     } else {
       a.w = static_cast<const ds::half_t*>(w);
     }
-    if (skinny) return ds::launch_skinny(epi, i8, a, st);
+    if (skinny) return ds::launch_skinny(epi, i8, a, cus, st);
     return ds::launch_gemm(epi, a, ds::gemm_pick(a.M, a.N, a.K, cus), st);
   };
 
