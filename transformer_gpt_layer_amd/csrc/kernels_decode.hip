@@ -280,14 +280,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
   const AT* Kp = reinterpret_cast<const AT*>(a.k_cache) + head_base;
   const AT* Vp = reinterpret_cast<const AT*>(a.v_cache) + head_base;
 
+  // the chunk's K and V rows are requested together: one memory round trip per workgroup
   float sc[NIT];
   bool valid[NIT];
-  u32x4 raw[NIT];
+  u32x4 raw[NIT], rawv[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int key = kb + (it * 4 + wave) * KPI + lane / LPK;
     valid[it] = key < ke;
     raw[it] = valid[it] ? ld16(Kp + (size_t)key * D + e0) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int key = kb + (it * 4 + wave) * KPI + lane / LPK;
+    rawv[it] = valid[it] ? ld16(Vp + (size_t)key * D + e0) : u32x4{0, 0, 0, 0};
   }
   float m = kNeg;
 #pragma unroll
@@ -310,11 +316,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
   }
   m = wave_max(m);
 
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int key = kb + (it * 4 + wave) * KPI + lane / LPK;
-    raw[it] = valid[it] ? ld16(Vp + (size_t)key * D + e0) : u32x4{0, 0, 0, 0};
-  }
   float l = 0.f, acc[EK];
 #pragma unroll
   for (int e = 0; e < EK; ++e) acc[e] = 0.f;
@@ -323,12 +324,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
     const float p = valid[it] ? exp2f(sc[it] - m) : 0.f;
     l += p;
     if constexpr (sizeof(AT) == 4) {
-      acc[0] += p * as_f32(raw[it].x);
-      acc[1] += p * as_f32(raw[it].y);
-      acc[2] += p * as_f32(raw[it].z);
-      acc[3] += p * as_f32(raw[it].w);
+      acc[0] += p * as_f32(rawv[it].x);
+      acc[1] += p * as_f32(rawv[it].y);
+      acc[2] += p * as_f32(rawv[it].z);
+      acc[3] += p * as_f32(rawv[it].w);
     } else {
-      const uint32_t wv[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+      const uint32_t wv[4] = {rawv[it].x, rawv[it].y, rawv[it].z, rawv[it].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const half2_t vv = as_half2(wv[h]);
@@ -399,40 +400,37 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
   if (tid == 0) *cnt = 0u;
 }
 
-constexpr int kAttnChunk = 64;
+constexpr int kAttnChunk = 64;       // positions per workgroup for few (row, head) pairs
+constexpr int kAttnChunkWide = 256;  // and for many: fewer workgroups and partials to merge
 
 int attn_chunk_for(int rows, int heads, int cap) {
-  (void)rows;
-  (void)heads;
   (void)cap;
-  return kAttnChunk;
+  return (long)rows * heads >= 256 ? kAttnChunkWide : kAttnChunk;
 }
 
-template <typename AT, int D>
+template <typename AT, int D, int C, bool QH>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.nchunk, a.heads, a.rows);
-  hipLaunchKernelGGL((attn_decode_kernel<AT, D, kAttnChunk>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_decode_kernel<AT, D, C, QH>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_decode_f16(const AttnArgs& a, hipStream_t st) {
-  if (a.chunk != kAttnChunk) return hipErrorInvalidValue;
-  dim3 grid(a.nchunk, a.heads, a.rows);
+template <typename AT, bool QH>
+static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t st) {
+  const bool wide = a.chunk == kAttnChunkWide;
+  if (!wide && a.chunk != kAttnChunk) return hipErrorInvalidValue;
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((attn_decode_kernel<half_t, 64, kAttnChunk, true>), grid, dim3(256), 0, st, a);
-  else if (a.head_dim == 128)
-    hipLaunchKernelGGL((attn_decode_kernel<half_t, 128, kAttnChunk, true>), grid, dim3(256), 0, st, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+    return wide ? launch_attn_t<AT, 64, kAttnChunkWide, QH>(a, st) : launch_attn_t<AT, 64, kAttnChunk, QH>(a, st);
+  if (a.head_dim == 128)
+    return wide ? launch_attn_t<AT, 128, kAttnChunkWide, QH>(a, st) : launch_attn_t<AT, 128, kAttnChunk, QH>(a, st);
+  return hipErrorInvalidValue;
 }
+
+hipError_t launch_attn_decode_f16(const AttnArgs& a, hipStream_t st) { return launch_attn_d<half_t, true>(a, st); }
 
 hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st) {
-  if (a.chunk != kAttnChunk) return hipErrorInvalidValue;
-  if (adt == F32 && a.head_dim == 64) return launch_attn_t<float, 64>(a, st);
-  if (adt == F32 && a.head_dim == 128) return launch_attn_t<float, 128>(a, st);
-  if (adt == F16 && a.head_dim == 64) return launch_attn_t<half_t, 64>(a, st);
-  if (adt == F16 && a.head_dim == 128) return launch_attn_t<half_t, 128>(a, st);
+  if (adt == F32) return launch_attn_d<float, false>(a, st);
+  if (adt == F16) return launch_attn_d<half_t, false>(a, st);
   return hipErrorInvalidValue;
 }
 
