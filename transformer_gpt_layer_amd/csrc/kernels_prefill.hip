@@ -499,17 +499,28 @@ __global__ __launch_bounds__(kGemmThreads * KG) void gemm_kernel(const GemmArgs 
 // One workgroup per (sequence b, head j, 64 consecutive new rows); wave w owns rows 16w..16w+15.
 // Computed transposed so that MFMA results feed the next MFMA without a layout change:
 //   S^T[key][row] = K Q^T    (A = K rows from LDS, B = q rows from registers)
-//   O^T[d][row]  += V^T P^T  (A = V^T from LDS, B = the probabilities, already in B layout)
+//   O^T[d][row]  += V^T P^T  (A = V^T, B = the probabilities, already in B layout)
 // In S^T's accumulator layout a lane holds four keys of one row (column), and O^T's accumulators
-// in a lane also all belong to that row, so the online-softmax rescale is per lane.
+// in a lane also all belong to that row, so the online-softmax rescale is per lane. V stays
+// row-major in LDS; its transposed operand comes from ds_read_b64_tr_b16, which hands lane i of a
+// 16-lane group element i%4 of the 8 bytes addressed by lane 4e + i/4 as its element e (checked
+// on the device with an in-bounds probe).
 constexpr int kAttnRows = 64, kAttnKeys = 64;
 
 template <int D> struct AttnShape {
   static constexpr int KROW = D * 2;                     // bytes of one K row in LDS
-  static constexpr int VTROW = kAttnKeys * 2 + 8;        // bytes of one V^T row (padded)
+  static constexpr int VROW = D * 2 + 32;                // bytes of one V row (padded: the four
+                                                         // keys of a transposed read hit distinct banks)
   static constexpr int K_BYTES = kAttnKeys * KROW;
-  static constexpr int LDS = K_BYTES + D * VTROW;
+  static constexpr int LDS = K_BYTES + kAttnKeys * VROW;
 };
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+__device__ __forceinline__ short4_t lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(reinterpret_cast<uintptr_t>(p)));
+}
 
 template <int D> constexpr size_t attn_lds_bytes() { return (size_t)AttnShape<D>::LDS; }
 
@@ -519,10 +530,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
   constexpr int NCH = D / 8;  // 16-byte chunks per K row
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* Ks = smem;
-  unsigned char* Vt = smem + S::K_BYTES;
+  unsigned char* Vs = smem + S::K_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qtiles = (g.tokens + kAttnRows - 1) / kAttnRows;
-  const int qt = blockIdx.x % qtiles, bj = blockIdx.x / qtiles;
+  // causal tiles further down see more keys: launch them first so that the long ones do not
+  // start last
+  const int qt = qtiles - 1 - (int)(blockIdx.x % qtiles), bj = blockIdx.x / qtiles;
   const int j = bj % g.heads, b = bj / g.heads;
   const int H = g.heads * D;
   const int len = min(max(g.d_len[b], 0), g.cap);  // rows already in the cache before this call
@@ -553,22 +566,35 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
 
   const half_t* kbase = g.k_cache + ((size_t)b * g.heads + j) * g.cap * D;
   const half_t* vbase = g.v_cache + ((size_t)b * g.heads + j) * g.cap * D;
+  // each thread carries NT 16-byte pieces of K and of V of a key tile; the next tile's pieces
+  // are requested before the current tile's products, so their latency hides behind them
+  constexpr int NT = kAttnKeys * NCH / 256;
+  static_assert(NT * 256 == kAttnKeys * NCH, "whole pieces per thread");
+  u32x4 kpre[NT], vpre[NT];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int c = tid + 256 * i, kr = c / NCH, ch = c - kr * NCH, key = k0 + kr;
+      kpre[i] = u32x4{0u, 0u, 0u, 0u};
+      vpre[i] = u32x4{0u, 0u, 0u, 0u};
+      if (key < kend) {
+        kpre[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + ch * 8);
+        vpre[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * D + ch * 8);
+      }
+    }
+  };
+  if (kmax > 0) fetch(0);
   for (int k0 = 0; k0 < kmax; k0 += kAttnKeys) {
     __syncthreads();  // the previous tile is no longer read
-    // stage K [key][d] (chunk-swizzled) and V^T [d][key]; keys at or past kend are zeros
-    for (int c = tid; c < kAttnKeys * NCH; c += 256) {
-      const int kr = c / NCH, ch = c - kr * NCH, key = k0 + kr;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < kend) {
-        kv = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + ch * 8);
-        vv = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * D + ch * 8);
-      }
-      *reinterpret_cast<u32x4*>(Ks + kr * S::KROW + ((ch ^ (kr & 7)) << 4)) = kv;
-      const half8_t vh = __builtin_bit_cast(half8_t, vv);
+    // stage K [key][d] (chunk-swizzled) and V [key][d] (padded rows); keys at or past kend are zeros
 #pragma unroll
-      for (int e = 0; e < 8; ++e) *reinterpret_cast<half_t*>(Vt + (ch * 8 + e) * S::VTROW + kr * 2) = vh[e];
+    for (int i = 0; i < NT; ++i) {
+      const int c = tid + 256 * i, kr = c / NCH, ch = c - kr * NCH;
+      *reinterpret_cast<u32x4*>(Ks + kr * S::KROW + ((ch ^ (kr & 7)) << 4)) = kpre[i];
+      *reinterpret_cast<u32x4*>(Vs + kr * S::VROW + ch * 16) = vpre[i];
     }
     __syncthreads();
+    if (k0 + kAttnKeys < kmax) fetch(k0 + kAttnKeys);
 
     // S^T for 64 keys: four 16-key blocks; lane holds keys 16 f + 4 grp + r of its row
     float4_t st[4];
@@ -613,15 +639,17 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
 #pragma unroll
     for (int f = 0; f < D / 16; ++f) o[f] *= corr;
     // O^T += V^T P^T: B element e of lane group grp is key 32 s + 4 grp + e (e < 4) or
-    // 32 s + 16 + 4 grp + (e - 4), matching the st layout; A (V^T) takes the same keys.
+    // 32 s + 16 + 4 grp + (e - 4), matching the st layout; A (V^T, d = 16 f + lane % 16) takes
+    // the same keys: in each transposed read, lane frow of the group addresses key
+    // 32 s + 16 h + 4 grp + frow / 4 at d = 16 f + 4 (frow % 4), h = 0 for e < 4, 1 for e >= 4.
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int f = 0; f < D / 16; ++f) {
-        const unsigned char* vr = Vt + (16 * f + frow) * S::VTROW;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + (32 * s + 4 * grp) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + (32 * s + 16 + 4 * grp) * 2);
-        const u32x4 vv = {lo.x, lo.y, hi.x, hi.y};
+        const unsigned char* va = Vs + (32 * s + 4 * grp + (frow >> 2)) * S::VROW + (16 * f + 4 * (frow & 3)) * 2;
+        const short4_t lo = lds_read_tr16(va);
+        const short4_t hi = lds_read_tr16(va + 16 * S::VROW);
+        const short8_t vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         o[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, vv), pf[s], o[f], 0, 0, 0);
       }
   }
