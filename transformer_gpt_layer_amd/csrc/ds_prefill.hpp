@@ -59,9 +59,11 @@ struct AttnPrefillArgs {
 // Tile configuration for an M x N x K product on `cus` compute units.
 int gemm_pick(int M, int N, int K, int cus);
 hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int cfg, hipStream_t st);
-// LayerNorm of `rows` rows of H elements (fp32 or fp16 input) into fp16.
+// LayerNorm of `rows` rows of H elements (fp32 or fp16 input) into fp16. With d_len, the same
+// launch also advances the cache lengths (d_len[b] += ntok for b < batch, unless that would pass
+// cap): for a LayerNorm that runs after every reader of the lengths in the step.
 hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const half_t* b, half_t* out, int rows, int H,
-                          float eps, hipStream_t st);
+                          float eps, hipStream_t st, int32_t* d_len = nullptr, int batch = 0, int ntok = 0, int cap = 0);
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t st);
 // The same product and epilogues for M <= 16 rows (decode of a few sequences): every weight row is
 // streamed once, with fp16 weights (w) or int8 codes and group-64 scales (wq, wscale, group).

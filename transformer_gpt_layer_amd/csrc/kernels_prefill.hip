@@ -25,6 +25,7 @@
 // operand reads (16 rows, one chunk) hit distinct banks. Tiles are numbered so that the workgroups the dispatcher sends to
 // one XCD (every 8th) hold consecutive tiles, which share their weight columns in that XCD's L2.
 #include "ds_device.hpp"
+#include "ds_launch.hpp"
 #include "ds_prefill.hpp"
 
 namespace ds {
@@ -141,11 +142,71 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(const IT* __restrict__ x, 
 // (up to NR 16-byte vectors per thread), so the statistics take one pass and one round trip: sums
 // of d = x - x[0] and d^2 give the mean and the biased variance (shifting by an element of the row
 // keeps the subtraction well conditioned).
+// Optional length advance folded into a LayerNorm launch that runs after every reader of the
+// lengths in this step: d_len[b] += ntok for b < batch, unless that would pass cap.
+struct LenAdvance {
+  int32_t* d_len;
+  int batch, ntok, cap;
+};
+__device__ __forceinline__ void len_advance(const LenAdvance& la) {
+  if (la.d_len && blockIdx.x == 0)
+    for (int b = threadIdx.x; b < la.batch; b += blockDim.x)
+      if (la.d_len[b] + la.ntok <= la.cap) la.d_len[b] += la.ntok;
+}
+
+// One wave per row with the whole row in registers (NR 16-byte pieces per lane): one pass over
+// memory, exact two-pass statistics on the registers.
+template <typename IT, int NR>
+__global__ __launch_bounds__(256) void ln_rows_reg_kernel(const IT* __restrict__ x, const half_t* __restrict__ g,
+                                                          const half_t* __restrict__ beta, half_t* __restrict__ out,
+                                                          int rows, int H, float eps, const LenAdvance la) {
+  constexpr int V = 16 / (int)sizeof(IT);
+  len_advance(la);
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const IT* xr = x + (size_t)row * H;
+  const int nv = H / V;
+  float v[NR][V];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int i = lane + j * kWave;
+    if (i < nv) ld_row<V>(xr + i * V, v[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+    if (lane + j * kWave < nv)
+#pragma unroll
+      for (int e = 0; e < V; ++e) s += v[j][e];
+  const float mean = wave_sum(s) / (float)H;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+    if (lane + j * kWave < nv)
+#pragma unroll
+      for (int e = 0; e < V; ++e) q += (v[j][e] - mean) * (v[j][e] - mean);
+  const float rstd = rsqrtf(wave_sum(q) / (float)H + eps);
+  half_t* o = out + (size_t)row * H;
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int i = lane + j * kWave;
+    if (i < nv) {
+      float gv[V], bv[V];
+      ld_halves<V>(g + i * V, gv);
+      ld_halves<V>(beta + i * V, bv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[j][e] = (v[j][e] - mean) * rstd * gv[e] + bv[e];
+      st_halves<V>(o + i * V, v[j]);
+    }
+  }
+}
+
 template <typename IT, int NR>
 __global__ __launch_bounds__(256) void ln_row_wg_kernel(const IT* __restrict__ x, const half_t* __restrict__ g,
                                                        const half_t* __restrict__ beta, half_t* __restrict__ out, int H,
-                                                       float eps) {
+                                                       float eps, const LenAdvance la) {
   constexpr int V = 16 / (int)sizeof(IT);
+  len_advance(la);
   __shared__ float red[2][4];
   const int tid = threadIdx.x, row = blockIdx.x;
   const IT* xr = x + (size_t)row * H;
@@ -931,22 +992,45 @@ hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int cfg, hipStream_t st) 
 }
 
 hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const half_t* b, half_t* out, int rows, int H,
-                          float eps, hipStream_t st) {
+                          float eps, hipStream_t st, int32_t* d_len, int batch, int ntok, int cap) {
   if (rows <= 0) return hipSuccess;
+  const LenAdvance la{d_len, batch, ntok, cap};
   constexpr int kNR = 8;  // 16-byte vectors per thread of the workgroup-per-row kernel
   if (rows < 64 && H <= 256 * kNR * (in_f32 ? 4 : 8)) {
     if (in_f32)
-      hipLaunchKernelGGL((ln_row_wg_kernel<float, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const float*>(x), g, b, out, H, eps);
+      hipLaunchKernelGGL((ln_row_wg_kernel<float, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const float*>(x), g, b, out, H, eps, la);
     else
-      hipLaunchKernelGGL((ln_row_wg_kernel<half_t, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const half_t*>(x), g, b, out, H, eps);
+      hipLaunchKernelGGL((ln_row_wg_kernel<half_t, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const half_t*>(x), g, b, out, H, eps, la);
     return hipGetLastError();
   }
   const dim3 grid((rows + 3) / 4);
+  // register-resident wave-per-row kernel: 16-byte pieces per lane, the fewest of 4, 8, 12, 16
+  // that hold the row
+  const int pieces = (H / (in_f32 ? 4 : 8) + kWave - 1) / kWave;
+  if (pieces <= 16) {
+#define DS_LNR(NR)                                                                                                   \
+  if (pieces <= NR) {                                                                                                \
+    if (in_f32)                                                                                                      \
+      hipLaunchKernelGGL((ln_rows_reg_kernel<float, NR>), grid, dim3(256), 0, st, static_cast<const float*>(x), g, b, \
+                         out, rows, H, eps, la);                                                                     \
+    else                                                                                                             \
+      hipLaunchKernelGGL((ln_rows_reg_kernel<half_t, NR>), grid, dim3(256), 0, st, static_cast<const half_t*>(x), g, \
+                         b, out, rows, H, eps, la);                                                                  \
+    return hipGetLastError();                                                                                        \
+  }
+    DS_LNR(4)
+    DS_LNR(8)
+    DS_LNR(12)
+    DS_LNR(16)
+#undef DS_LNR
+  }
   if (in_f32)
     hipLaunchKernelGGL(ln_rows_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), g, b, out, rows, H, eps);
   else
     hipLaunchKernelGGL(ln_rows_kernel<half_t>, grid, dim3(256), 0, st, static_cast<const half_t*>(x), g, b, out, rows, H, eps);
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return e;
+  if (d_len) return launch_len_advance(d_len, batch, ntok, cap, st);
+  return hipSuccess;
 }
 
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t st) {

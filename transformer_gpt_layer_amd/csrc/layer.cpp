@@ -196,18 +196,19 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   a.a = ctx; a.bias = hp(L->w.b_o); a.out = x2; a.resid = x; a.N = H; a.K = H;
   if (hipError_t e = gemm(ds::EPI_OPROJ, a, L->w.w_o, L->w.s_o)) return hip_fail(e, "o gemm launch");
 
-  // 4: f = GeLU(LN2(x2) W1^T + b1)
-  if (hipError_t e = ds::launch_ln_rows(true, x2, hp(L->w.ln2_g), hp(L->w.ln2_b), h, rows, H, d.ln_eps, st))
+  // 4: f = GeLU(LN2(x2) W1^T + b1); the LN2 launch also advances d_len by ntok (the QKV epilogue
+  // and attention, its only readers in this step, have run)
+  if (hipError_t e = ds::launch_ln_rows(true, x2, hp(L->w.ln2_g), hp(L->w.ln2_b), h, rows, H, d.ln_eps, st, kv->d_len,
+                                        batch, ntok, kv->capacity))
     return hip_fail(e, "ln2 launch");
   a = g;
   a.a = h; a.bias = hp(L->w.b_ff1); a.out = f; a.N = F; a.K = H;
   if (hipError_t e = gemm(ds::EPI_FF1, a, L->w.w_ff1, L->w.s_ff1)) return hip_fail(e, "ff1 gemm launch");
 
-  // 5: y = x2 + f W2^T + b2, then d_len += ntok
+  // 5: y = x2 + f W2^T + b2
   a = g;
   a.a = f; a.bias = hp(L->w.b_ff2); a.out = y; a.resid = x2; a.N = H; a.K = F;
   if (hipError_t e = gemm(ds::EPI_FF2, a, L->w.w_ff2, L->w.s_ff2)) return hip_fail(e, "ff2 gemm launch");
-  if (hipError_t e = ds::launch_len_advance(kv->d_len, batch, ntok, kv->capacity, st)) return hip_fail(e, "len advance launch");
   if (kv->h_len)
     for (int b = 0; b < batch; ++b) kv->h_len[b] += ntok;
   return DS_OK;
