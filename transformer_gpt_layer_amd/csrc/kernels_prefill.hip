@@ -261,20 +261,23 @@ __global__ __launch_bounds__(256) void ln_row_wg_kernel(const IT* __restrict__ x
 // MFMA blocks), k-steps of 64 staged through an ST-deep LDS ring by direct-to-LDS buffer loads.
 // Each k-step is two halves of 32: the operand reads of one half are issued between the products
 // of the other, and one barrier per k-step both publishes the next stage and frees the last one.
-constexpr int kBK = 64, kGemmThreads = 256;
+constexpr int kBK = 64;
 
 // KG = 2 splits every k-step between two groups of four waves (one 32-wide half each) and adds
 // the two partial tiles through LDS at the end: two waves per SIMD with one workgroup per CU.
-template <int BM, int BN, int ST, int KG> struct GemmShape {
-  static constexpr int THREADS = kGemmThreads * KG;
-  static constexpr int WM = BM / 2, WN = BN / 2;  // one wave's quarter
+constexpr int gemm_threads(int kg, int nwn) { return kWave * 2 * nwn * kg; }
+
+template <int BM, int BN, int ST, int KG, int NWN = 2> struct GemmShape {
+  static constexpr int NWM = 2, NQ = NWM * NWN;    // waves of one k-group: NWM x NWN grid
+  static constexpr int THREADS = gemm_threads(KG, NWN);
+  static constexpr int WM = BM / NWM, WN = BN / NWN;  // one wave's part
   static constexpr int FM = WM / 16, FN = WN / 16;  // 16x16 MFMA blocks per wave
   static constexpr int A_BYTES = BM * kBK * 2;
   static constexpr int STAGE = (BM + BN) * kBK * 2;
   static constexpr int LDS = ST * STAGE;
-  static_assert(BM % 64 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(BM % (8 * NQ) == 0 && BN % (8 * NQ) == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
   static_assert(ST >= 2, "the ring needs two stages");
-  static_assert(KG == 1 || (KG == 2 && LDS >= 4 * FM * FN * 1024), "the partial tiles must fit the ring");
+  static_assert(KG == 1 || (KG == 2 && LDS >= NQ * FM * FN * 1024), "the partial tiles must fit the ring");
 };
 
 // Swizzled byte offset of (row, 16-byte chunk) in a 128-byte-row LDS tile: chunk c of row r sits
@@ -292,21 +295,21 @@ __device__ __forceinline__ uint32_t swz(int row, int chunk) {
 // is never read, and keeps the number of loads per step fixed.
 // With two wave groups, group 0 loads the A rows and group 1 the W rows (wave is then the index
 // within the group).
-template <int BM, int BN, bool DO_A, bool DO_W>
+template <int BM, int BN, bool DO_A, bool DO_W, int NQ>
 __device__ __forceinline__ void issue_stage(unsigned char* stage, int wave, uint32_t koff, bool valid,
                                             const GemmArgs& g, uint32_t va, uint32_t vw, uint32_t row_step) {
   const rsrc_t ra = make_rsrc(g.a, (uint32_t)((size_t)g.M * g.K * 2));
   const rsrc_t rw = make_rsrc(g.w, (uint32_t)((size_t)g.N * g.K * 2));
   if constexpr (DO_A) {
 #pragma unroll
-    for (int u = 0; u < BM / 32; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(stage + (wave + 4 * u) * 1024), 16,
+    for (int u = 0; u < BM / (8 * NQ); ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(stage + (wave + NQ * u) * 1024), 16,
                                                valid ? va + u * row_step + koff : kOutOfRange, 0, 0, 0);
   }
   if constexpr (DO_W) {
 #pragma unroll
-    for (int u = 0; u < BN / 32; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(stage + BM * 128 + (wave + 4 * u) * 1024), 16,
+    for (int u = 0; u < BN / (8 * NQ); ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(stage + BM * 128 + (wave + NQ * u) * 1024), 16,
                                                valid ? vw + u * row_step + koff : kOutOfRange, 0, 0, 0);
   }
 }
@@ -443,26 +446,26 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, int mb, int nb, cons
 }
 
 // Loads of one stage by this wave (both operands, or its group's operand with two groups).
-template <int BM, int BN, int KG>
+template <int BM, int BN, int KG, int NQ>
 __device__ __forceinline__ void issue_mine(unsigned char* stage, int q, int grp, int j, int nk, const GemmArgs& g,
                                            uint32_t va, uint32_t vw, uint32_t row_step) {
   const uint32_t koff = (uint32_t)(j * kBK * 2);
   if constexpr (KG == 1) {
-    issue_stage<BM, BN, true, true>(stage, q, koff, j < nk, g, va, vw, row_step);
+    issue_stage<BM, BN, true, true, NQ>(stage, q, koff, j < nk, g, va, vw, row_step);
   } else {
-    if (grp == 0) issue_stage<BM, BN, true, false>(stage, q, koff, j < nk, g, va, vw, row_step);
-    else issue_stage<BM, BN, false, true>(stage, q, koff, j < nk, g, va, vw, row_step);
+    if (grp == 0) issue_stage<BM, BN, true, false, NQ>(stage, q, koff, j < nk, g, va, vw, row_step);
+    else issue_stage<BM, BN, false, true, NQ>(stage, q, koff, j < nk, g, va, vw, row_step);
   }
 }
 
-template <int BM, int BN, int ST, int KG, int EPI>
-__global__ __launch_bounds__(kGemmThreads * KG) void gemm_kernel(const GemmArgs g) {
-  typedef GemmShape<BM, BN, ST, KG> S;
+template <int BM, int BN, int ST, int KG, int NWN, int EPI>
+__global__ __launch_bounds__(gemm_threads(KG, NWN)) void gemm_kernel(const GemmArgs g) {
+  typedef GemmShape<BM, BN, ST, KG, NWN> S;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load set-up stays scalar
-  const int q = wave & 3, grp = wave >> 2;  // quadrant; k-group (KG = 2)
-  const int wm = q & 1, wn = q >> 1;
+  const int q = wave % S::NQ, grp = wave / S::NQ;  // wave of the k-group; k-group (KG = 2)
+  const int wm = q % S::NWM, wn = q / S::NWM;
 
   // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a contiguous tile range.
   const int T = g.tiles_m * g.tiles_n, i = blockIdx.x;
@@ -473,11 +476,11 @@ __global__ __launch_bounds__(kGemmThreads * KG) void gemm_kernel(const GemmArgs 
   const int K = g.K;
 
   const int lr = lane >> 3, lc = (lane & 7) ^ lr;
-  const uint32_t row_step = (uint32_t)(32 * K * 2);  // 4 wave loads = 32 rows
+  const uint32_t row_step = (uint32_t)(8 * S::NQ * K * 2);  // NQ wave loads = 8 NQ rows
   const uint32_t va = (uint32_t)(((size_t)(m0 + 8 * q + lr) * K + lc * 8) * 2);
   const uint32_t vw = (uint32_t)(((size_t)(n0 + 8 * q + lr) * K + lc * 8) * 2);
   // this wave's wave loads per stage
-  const int nl = KG == 1 ? (BM + BN) / 32 : (grp == 0 ? BM / 32 : BN / 32);
+  const int nl = KG == 1 ? (BM + BN) / (8 * S::NQ) : (grp == 0 ? BM / (8 * S::NQ) : BN / (8 * S::NQ));
   const int nk = K / kBK;
   float4_t acc[S::FM][S::FN];
 #pragma unroll
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(kGemmThreads * KG) void gemm_kernel(const GemmArgs 
   // end), so when step kt+1's stage must be complete, the loads allowed in flight are always the
   // ST - 2 stages requested after it.
 #pragma unroll
-  for (int s = 0; s < ST; ++s) issue_mine<BM, BN, KG>(smem + s * S::STAGE, q, grp, s, nk, g, va, vw, row_step);
+  for (int s = 0; s < ST; ++s) issue_mine<BM, BN, KG, S::NQ>(smem + s * S::STAGE, q, grp, s, nk, g, va, vw, row_step);
 
   const int fch = lane >> 4;
   const int arow = wm * S::WM + (lane & 15), brow = wn * S::WN + (lane & 15);
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(kGemmThreads * KG) void gemm_kernel(const GemmArgs 
       // step kt+1's stage is in LDS and every wave has finished reading step kt's
       wait_vm_dyn((ST - 2) * nl);
       lds_barrier();
-      issue_mine<BM, BN, KG>(cur, q, grp, kt + ST, nk, g, va, vw, row_step);
+      issue_mine<BM, BN, KG, S::NQ>(cur, q, grp, kt + ST, nk, g, va, vw, row_step);
       read_half<S>(smem + ((kt + 1) % ST) * S::STAGE, 0, arow, brow, fch, a0, b0);
       mfma_half<S>(acc, a1, b1);
     }
@@ -517,7 +520,7 @@ __global__ __launch_bounds__(kGemmThreads * KG) void gemm_kernel(const GemmArgs 
     auto step = [&](int kt, half8_t (&xa)[S::FM], half8_t (&xb)[S::FN], half8_t (&ya)[S::FM], half8_t (&yb)[S::FN]) {
       wait_vm_dyn((ST - 2) * nl);
       lds_barrier();
-      issue_mine<BM, BN, KG>(smem + (kt % ST) * S::STAGE, q, grp, kt + ST, nk, g, va, vw, row_step);
+      issue_mine<BM, BN, KG, S::NQ>(smem + (kt % ST) * S::STAGE, q, grp, kt + ST, nk, g, va, vw, row_step);
       read_half<S>(smem + ((kt + 1) % ST) * S::STAGE, grp, arow, brow, fch, ya, yb);
       mfma_half<S>(acc, xa, xb);
     };
@@ -922,31 +925,34 @@ hipError_t launch_skinny_t(const GemmArgs& a, int cus, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int ST, int KG, int EPI>
+template <int BM, int BN, int ST, int KG, int NWN, int EPI>
 hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t st) {
-  typedef GemmShape<BM, BN, ST, KG> S;
+  typedef GemmShape<BM, BN, ST, KG, NWN> S;
   GemmArgs a = a0;
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
   // above the default 64 KB of dynamic LDS; set on every launch (cheap, and per device)
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, ST, KG, EPI>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, ST, KG, NWN, EPI>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, ST, KG, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(S::THREADS), S::LDS, st, a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, ST, KG, NWN, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(S::THREADS), S::LDS, st, a);
   return hipGetLastError();
 }
 
-// The two tile configurations (128 x 160 tiles either way; the rows, columns and k-step count of a
-// workgroup are those of the ring above):
-//   0: two-stage ring, four waves, two workgroups per CU, for products with at least two tiles
-//      per CU (the next tiles' loads overlap the current ones' products);
-//   1: three-stage ring, two groups of four waves splitting each k-step, one workgroup per CU, for
-//      products with at most one tile per CU (deeper prefetch, two waves per SIMD).
+// The tile configurations:
+//   0: 128 x 160, two-stage ring, four waves, two workgroups per CU, for products with at least
+//      two such tiles per CU (the next tiles' loads overlap the current ones' products);
+//   1: 128 x 160, three-stage ring, two groups of four waves splitting each k-step, one workgroup
+//      per CU, for products with at most one such tile per CU (deeper prefetch, two waves per SIMD);
+//   2: 256 x 256, two-stage ring, eight waves of 128 x 64, one workgroup per CU: half the bytes
+//      loaded per FLOP of 128 x 160 (the ring's loads set the pace), for products that come out
+//      at 85-100 % of one such tile per CU.
 template <int EPI>
 hipError_t launch_gemm_epi(const GemmArgs& a, int cfg, hipStream_t st) {
   switch (cfg) {
-    case 0: return launch_gemm_t<128, 160, 2, 1, EPI>(a, st);
-    case 1: return launch_gemm_t<128, 160, 3, 2, EPI>(a, st);
+    case 0: return launch_gemm_t<128, 160, 2, 1, 2, EPI>(a, st);
+    case 1: return launch_gemm_t<128, 160, 3, 2, 2, EPI>(a, st);
+    case 2: return launch_gemm_t<256, 256, 2, 1, 4, EPI>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -956,9 +962,13 @@ hipError_t launch_gemm_epi(const GemmArgs& a, int cfg, hipStream_t st) {
 using namespace prefill;
 
 // Measured on the GPT-Neo-2.7B prefill products (2048 rows): configuration 0 runs the 768- and
-// 1024-tile products 1.1x-1.4x faster than 1, and 1 the 256-tile ones 1.2x-1.3x faster than 0.
+// 1024-tile products 1.1x-1.4x faster than 1, and 1 the 256-tile ones 1.2x-1.3x faster than 0;
+// configuration 2 runs QKV (240 tiles of 256 x 256) 1.33x faster than 0, and FF1 (320 such
+// tiles, a second round for 64) 1.3x slower.
 int gemm_pick(int M, int N, int K, int cus) {
   (void)K;
+  const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+  if (M % 256 == 0 && N % 256 == 0 && t256 <= cus && 20 * t256 >= 17 * (long)cus) return 2;
   const long tiles = (long)((M + 127) / 128) * ((N + 159) / 160);
   return tiles <= cus ? 1 : 0;
 }
