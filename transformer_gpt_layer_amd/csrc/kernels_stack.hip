@@ -199,7 +199,7 @@ __device__ __forceinline__ bool grid_error(const StackArgs& a) {
   return __hip_atomic_load(a.sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
 
-constexpr int kPollUnroll = 4;  // 16-byte loads (two tagged values each) a thread keeps in flight
+constexpr int kPollUnroll = 8;  // 16-byte loads (two tagged values each) a thread keeps in flight
 
 // Wait until the tagged values [0, n) at src all carry `tag`, handing each one once to put(i, v).
 // Threads st, st+NT, ... of the sync waves share the work.
