@@ -45,6 +45,12 @@ SMALL = {
                       group=64, batch=5, past=65, cfg_id=104),
     "i8-d64-b1-k256": _wl("c1", hidden=256, heads=4, head_dim=64, ffn=512, weight_dtype="i8", act_dtype="f16",
                           group=64, batch=1, past=3, cfg_id=105),
+    # wide enough that the few-row products split K over workgroups (O by 4, FF2 by 8 for fp16)
+    # and that attention takes 256-position chunks (15 rows x 32 heads)
+    "f16-d64-b15-h2048": _wl("c1", hidden=2048, heads=32, head_dim=64, ffn=4096, weight_dtype="f16", act_dtype="f16",
+                             batch=15, past=300, cfg_id=106),
+    "i8-d64-b15-h2048": _wl("c1", hidden=2048, heads=32, head_dim=64, ffn=8192, weight_dtype="i8", act_dtype="f16",
+                            group=64, batch=15, past=301, cfg_id=107),
 }
 
 
