@@ -48,6 +48,33 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
+def read_probe_gbs(torch, tg, gib=2, reps=5):
+    """HBM read bandwidth this device reaches: the library's streaming read of a 2 GiB buffer,
+    best of a few launches timed with events on the current stream."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tg.read_probe(buf, out)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tg.read_probe(buf, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del buf
+    return (gib << 30) / (best * 1e-3) / 1e9
+
+
+def step_stats(times_ms):
+    """Median, p10 and p90 of per-step times (ms)."""
+    t = sorted(times_ms)
+    pick = lambda q: t[min(len(t) - 1, max(0, int(round(q * (len(t) - 1)))))]
+    return {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4)}
+
+
 def copy_calibration(torch, gib: int = 1):
     """Three plain device-to-device copies of `gib` GiB (torch's copy kernel): the reference whose
     FETCH_SIZE / WRITE_SIZE counters scale the kernels' counters to bytes."""
@@ -191,13 +218,16 @@ def run_prefill(args, wl, torch, tg, syn):
             g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     with torch.cuda.stream(stream):
         e0.record(stream)
-        for _ in range(args.steps):
+        for i in range(args.steps):
             g.replay()
+            marks[i].record(stream)
         e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    per_step = [(e0 if i == 0 else marks[i - 1]).elapsed_time(marks[i]) for i in range(args.steps)]
     out = bufs[layers % 2]
     assert torch.isfinite(out.float()).all(), "non-finite prefill output"
     fl = prefill_flops_per_layer(wl)
@@ -214,6 +244,7 @@ def run_prefill(args, wl, torch, tg, syn):
                    "hidden": wl.hidden, "heads": wl.heads, "ffn": wl.ffn,
                    "launch": "per-layer kernels (LN, 4 MFMA GEMMs, flash attention), hip-graph"},
         "flops_per_layer": fl,
+        "step_ms": step_stats(per_step),
         "roofline": {"bound": "mfma", "kernel": "whole prefill step (weight GEMMs + attention)",
                      "achieved": round(tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
@@ -265,6 +296,8 @@ def main():
     ap.add_argument("--mode", choices=["auto", "stack", "layers"], default="auto",
                     help="stack: one persistent launch per step; layers: six kernels per layer")
     ap.add_argument("--no-graph", action="store_true", help="layers mode: launch eagerly instead of a HIP graph")
+    ap.add_argument("--no-read-probe", dest="read_probe", action="store_false",
+                    help="skip the streaming-read measurement of the HBM bandwidth this device reaches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three 1 GiB device copies (the reference for HBM traffic counters)")
     args = ap.parse_args()
@@ -327,7 +360,8 @@ def main():
         torch.cuda.synchronize()
         st.check()
         ms = e0.elapsed_time(e1) / args.steps
-        kernel_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
+        per_step = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+        kernel_ms = sum(per_step) / args.steps
         launch_desc = f"persistent stack kernel, {st.groups} workgroups"
     else:
         def step():
@@ -350,13 +384,16 @@ def main():
                 run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         with torch.cuda.stream(stream):
             e0.record(stream)
-            for _ in range(args.steps):
+            for i in range(args.steps):
                 run()
+                marks[i].record(stream)
             e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
+        per_step = [(e0 if i == 0 else marks[i - 1]).elapsed_time(marks[i]) for i in range(args.steps)]
         out = bufs[layers % 2]
         launch_desc = "per-layer kernels, " + ("eager" if args.no_graph else "hip-graph")
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
@@ -395,8 +432,14 @@ def main():
         "hbm_gbs_per_layer_step": round(gbs, 1),
         "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
         "bytes_per_layer_step": per,
+        "step_ms": step_stats(per_step),
         "roofline": roofline,
     }
+    if args.read_probe:
+        probe = read_probe_gbs(torch, tg)
+        result["read_probe_gbs"] = round(probe, 1)
+        # the roofline kernel's achieved rate over what a plain streaming read reaches here
+        result["hbm_frac_of_read_probe"] = round(roofline["achieved"] / probe, 4)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(wl, stack, kvs, args.cpu_seconds)
     print(json.dumps(result))

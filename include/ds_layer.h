@@ -159,6 +159,15 @@ int ds_quantize_i8(const float* w, int8_t* q, void* s, int32_t n, int32_t k, int
 int ds_dequantize_i8(const int8_t* q, const void* s, float* w, int32_t n, int32_t k, int32_t group,
                      void* stream);
 
+/* Measurement aid, no layer operation (no passage of the pages defines it; it serves callers that
+ * quote decode bandwidth against what the device reaches, beside the vendor peak): reads the
+ * `bytes` bytes of the device buffer `buf` once with 16-byte streaming loads spread over the whole
+ * device and XORs a 32-bit digest of the data into the device word *out, so that the reads cannot
+ * be elided; the launch time gives the achievable HBM read bandwidth. buf must be 16-byte aligned
+ * and bytes a multiple of 16; the caller owns both buffers. Enqueued on stream; DS_ERR_NULL,
+ * DS_ERR_ALIGN or DS_ERR_HIP on failure. */
+int ds_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Persistent multi-layer decode. A stack binds n_layers layers that share one description (same
  * shapes and dtypes) to their caches (caches[l] for layers[l], all of one capacity and at least

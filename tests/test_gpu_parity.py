@@ -143,6 +143,21 @@ def test_kv_full_raises_before_launch():
     assert kv.lengths() == [wl.capacity] * wl.batch
 
 
+def test_read_probe_reads_every_word():
+    """The bandwidth probe's digest is the XOR of every 32-bit word of the buffer: two full passes
+    of its grid (2048 workgroups x 2048 16-byte pieces), then five whole workgroup spans and a
+    ragged tail of 3 x 256 + 37 pieces."""
+    import transformer_gpt_layer_amd as tg
+    g = torch.Generator().manual_seed(11)
+    words = 4 * (2 * 2048 * 2048 + 5 * 2048 + 3 * 256 + 37)
+    host = torch.randint(-2**31, 2**31 - 1, (words,), dtype=torch.int32, generator=g)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tg.read_probe(host.cuda(), out)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert int(out.cpu().numpy().view(np.uint32)[0]) == int(want)
+
+
 @pytest.mark.parametrize("name,S,P0", [("f16-d128-b3", 7, 5), ("f32-d128-b3", 5, 0), ("i8-d128-b5", 4, 9)])
 def test_prefill_matches_oracle(name, S, P0):
     wl = SMALL[name]

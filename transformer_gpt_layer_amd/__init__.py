@@ -286,6 +286,17 @@ class Stack:
         check(lib().ds_stack_set_timeout_us(self._h, int(us)), "ds_stack_set_timeout_us")
 
 
+def read_probe(buf: torch.Tensor, out: torch.Tensor, stream=None):
+    """Stream-read every byte of the device tensor buf once; out (int32, 1 element) receives a
+    digest. The launch time gives the HBM read bandwidth the device reaches."""
+    if not buf.is_cuda or not buf.is_contiguous() or (buf.numel() * buf.element_size()) % 16:
+        raise ValueError("buf must be a contiguous device tensor of a multiple of 16 bytes")
+    if out.dtype != torch.int32 or out.numel() < 1 or not out.is_cuda:
+        raise ValueError("out must be a device int32 tensor")
+    check(lib().ds_read_probe(ptr(buf), buf.numel() * buf.element_size(), ptr(out), stream_handle(stream)),
+          "ds_read_probe")
+
+
 def quantize_i8(w: torch.Tensor, group: int = 64, stream=None):
     """Group-wise symmetric int8 quantization on the GPU: w float32 [n, k] ->
     (q int8 [n, k], s float16 [n, k/group])."""

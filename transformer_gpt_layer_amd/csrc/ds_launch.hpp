@@ -55,6 +55,8 @@ hipError_t launch_kv_append(Dt adt, const void* k_new, const void* v_new, void* 
                             int cap, hipStream_t st);
 // d_len[b] += ntok for b < batch, unless that would pass cap
 hipError_t launch_len_advance(int32_t* d_len, int batch, int ntok, int cap, hipStream_t st);
+// Reads bytes (a multiple of 16) from buf with streaming loads; *out ^= a digest of the data.
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t st);
 hipError_t launch_quantize_i8(const float* w, int8_t* q, uint16_t* s, int n, int k, int group,
                               hipStream_t st);
 hipError_t launch_dequantize_i8(const int8_t* q, const uint16_t* s, float* w, int n, int k,

@@ -54,6 +54,45 @@ hipError_t launch_kv_append(Dt adt, const void* k_new, const void* v_new, void* 
   return hipGetLastError();
 }
 
+// Streaming read of a whole buffer: each workgroup reads a contiguous 32 KB span per pass (every
+// thread eight nontemporal 16-byte loads in flight, 4 KB apart), folds what it read into one word,
+// and each workgroup folds its words into *out with one atomic XOR, so the loads cannot be dropped.
+// 2048 workgroups of 256 threads cover all CUs.
+constexpr int kProbeGroups = 2048, kProbeThreads = 256, kProbeUnroll = 8;
+__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* __restrict__ p, size_t n16, uint32_t* out) {
+  constexpr size_t span = (size_t)kProbeThreads * kProbeUnroll;
+  const size_t stride = (size_t)gridDim.x * span;
+  size_t i = (size_t)blockIdx.x * span + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kProbeUnroll - 1) * kProbeThreads < n16; i += stride) {
+    u32x4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kProbeThreads);
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  // the last, partial span: its pieces below n16
+  for (int u = 0; u < kProbeUnroll; ++u) {
+    const size_t j = i + (size_t)u * kProbeThreads;
+    if (i < n16 && j < n16) {
+      const u32x4 v = __builtin_nontemporal_load(p + j);
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  __shared__ uint32_t wg;
+  if (threadIdx.x == 0) wg = 0u;
+  __syncthreads();
+  __hip_atomic_fetch_xor(&wg, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_xor(out, wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(kProbeGroups), dim3(kProbeThreads), 0, st, static_cast<const u32x4*>(buf),
+                     bytes / 16, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_len_advance(int32_t* d_len, int batch, int ntok, int cap, hipStream_t st) {
   hipLaunchKernelGGL(len_advance_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, d_len, batch, ntok, cap);
   return hipGetLastError();

@@ -394,6 +394,14 @@ int ds_quantize_i8(const float* w, int8_t* q, void* s, int32_t n, int32_t k, int
   return DS_OK;
 }
 
+int ds_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+  if (!buf || !out) return fail(DS_ERR_NULL, "buf or out is NULL");
+  if (!aligned16(buf) || bytes % 16) return fail(DS_ERR_ALIGN, "buf must be 16-byte aligned and bytes a multiple of 16");
+  if (hipError_t e = ds::launch_read_probe(buf, bytes, out, reinterpret_cast<hipStream_t>(stream)))
+    return hip_fail(e, "read probe launch");
+  return DS_OK;
+}
+
 int ds_dequantize_i8(const int8_t* q, const void* s, float* w, int32_t n, int32_t k, int32_t group, void* stream) {
   if (!w || !q || !s) return fail(DS_ERR_NULL, "q, s or w is NULL");
   if (n < 0 || k < 0 || group < 16 || group % 16 || k % group) return fail(DS_ERR_SHAPE, "need n, k >= 0, group a multiple of 16 dividing k");
