@@ -754,18 +754,19 @@ constexpr int kSkinnyMaxWaves = 8;  // waves (K splits) per workgroup at most
 // The weight rows reach LDS as whole 128-byte lines through direct-to-LDS loads (8 rows x 128 B per
 // wave load, the XOR-swizzled layout of the tiled GEMM) and the B operands are read back from LDS:
 // loading them in the operand layout directly would fetch 64-byte halves of 16 rows per load.
-// Each wave owns a private ring of kSkR stages (16 rows x 128 B of W each: 64 k for fp16, 128 k
-// for int8) and the matching activation loads in registers; every load is a buffer load, so rows
-// past N and stages past the wave's range read zeros (activation rows past M are not loaded at
-// all), and each stage issues the same number of loads, which keeps the in-order load counter
-// arithmetic fixed. Products with few column blocks also split K over workgroups.
-constexpr int kSkR = 2;          // stages in flight per wave (more waves beat deeper rings: measured)
+// Each wave owns a private ring of R stages (16 rows x 128 B of W each: 64 k for fp16, 128 k for
+// int8) and the matching activation loads in registers; every load is a buffer load, so rows past
+// N and stages past the wave's range read zeros (activation rows past M are not loaded at all),
+// and each stage issues the same number of loads, which keeps the in-order load counter arithmetic
+// fixed. Products with few column blocks also split K over workgroups. The launcher picks the
+// split and the waves per workgroup so that every workgroup of the launch is resident at once and
+// the CUs carry equal shares.
+constexpr int kSkR = 2;          // stages in flight per wave: deeper rings (3, 4, 6) measured slower
 constexpr int kSkMinStages = 8;  // stages per wave worth a wave of its own
 
-template <bool I8, int EPI>
+template <bool I8, int EPI, int R = kSkR>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ float4_t red[kSkinnyMaxWaves][kWave];
   const int lane = threadIdx.x & 63, KS = blockDim.x >> 6;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, j = lane >> 4;
@@ -787,15 +788,15 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
   const rsrc_t rw = make_rsrc(I8 ? (const void*)g.wq : (const void*)g.w, (uint32_t)((size_t)g.N * wrow));
   const rsrc_t ra = make_rsrc(g.a, (uint32_t)((size_t)g.M * K * 2));
   const rsrc_t rs = make_rsrc(g.wscale, I8 ? (uint32_t)((size_t)g.N * (K / 64) * 2) : 0u);
-  unsigned char* ring = smem + w * (kSkR * 2048);
+  unsigned char* ring = smem + w * (R * 2048);
   // W: wave load u of a stage covers rows n0 + 8u + L/8, logical chunk (L%8) ^ (L/8)
   const int lr = lane >> 3, lc = (lane & 7) ^ lr;
   const uint32_t w_off = (uint32_t)(n0 + lr) * wrow + (uint32_t)(I8 ? kb : 2 * kb) + lc * 16;
   // A: row r; fp16 step s of a stage takes k 32s + 8j .. +8; int8 group g takes 64g + 16j .. +16
   const uint32_t a_off = (uint32_t)((r * K + kb) * 2) + (uint32_t)(I8 ? 32 * j : 16 * j);
   const uint32_t s_off = (uint32_t)((n0 + r) * (K / 64) + kb / 64) * 2;
-  u32x4 av[kSkR][I8 ? 4 : 2];
-  float sc[kSkR][2];
+  u32x4 av[R][I8 ? 4 : 2];
+  float sc[R][2];
   // lanes of rows past M issue no activation loads (their operand rows are zeros)
   const bool arow = r < g.M;
   auto issue = [&](int i, int slot) {
@@ -828,12 +829,12 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
   };
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < kSkR; ++i) issue(i, i);
-  for (int i = 0; i < ns; i += kSkR) {
+  for (int i = 0; i < R; ++i) issue(i, i);
+  for (int i = 0; i < ns; i += R) {
 #pragma unroll
-    for (int q = 0; q < kSkR; ++q) {
-      // stage i + q complete; the kSkR - 1 stages requested after it may stay in flight
-      wait_vm<(kSkR - 1) * LPS>();
+    for (int q = 0; q < R; ++q) {
+      // stage i + q complete; the R - 1 stages requested after it may stay in flight
+      wait_vm<(R - 1) * LPS>();
       const unsigned char* st = ring + q * 2048;
       if (i + q < ns) {
         if constexpr (!I8) {
@@ -856,16 +857,17 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
       }
       // the slot's operands are in registers before its refill is requested
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      issue(i + q + kSkR, q);
+      issue(i + q + R, q);
     }
   }
   wait_vm<0>();  // the out-of-range requests past the end
-  // sum the waves' K ranges, then the epilogue of C[4 j + e][n0 + r]
-  red[w][lane] = acc;
+  // sum the waves' K ranges (each wave's partial tile in the first 1 KB of its own ring, which
+  // nothing else touches once its loads have landed), then the epilogue of C[4 j + e][n0 + r]
+  reinterpret_cast<float4_t*>(ring)[lane] = acc;
   __syncthreads();
   if (w != 0) return;
   for (int v = 1; v < KS; ++v) {
-    const float4_t o = red[v][lane];
+    const float4_t o = reinterpret_cast<const float4_t*>(smem + v * (R * 2048))[lane];
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += o[e];
   }
@@ -896,32 +898,68 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
   for (int e = 0; e < 4; ++e) epilogue_store<EPI>(g, 4 * j + e, n0 + r, acc[e]);
 }
 
+// Resident workgroups per CU of a skinny variant with `waves` waves (the runtime's occupancy
+// figure: registers, LDS and wave slots), cached per variant and wave count.
 template <bool I8, int EPI>
-hipError_t launch_skinny_t(const GemmArgs& a, int cus, hipStream_t st) {
-  // as many waves as divide K evenly while each still streams at least kSkMinStages stages
+int skinny_slots(int waves) {
+  static int cache[kSkinnyMaxWaves + 1] = {};
+  int& c = cache[waves];
+  if (c == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&skinny_dma_kernel<I8, EPI>),
+                                                     64 * waves, (size_t)waves * kSkR * 2048) != hipSuccess)
+      n = 0;
+    c = n > 0 ? n : -1;
+  }
+  return c;
+}
+
+// Split and waves per workgroup of a skinny launch, best first by: the largest per-CU count of
+// workgroups relative to their number (every workgroup resident at once, so no CU runs a second
+// round while the others idle), fewer K splits, more waves. Measured on the 13B FF2 product (320
+// column blocks, K 20480): 1280 workgroups of four waves, all resident, 45 us; of eight waves (four
+// resident per CU, a second round for one per CU) 50 us.
+struct SkPlan {
+  int split = 0, ks = 0, per_cu = 0;
+};
+template <bool I8, int EPI>
+SkPlan skinny_plan(const GemmArgs& a, int cus) {
   const int kq = I8 ? 128 : 64;  // k per stage
   const int nblk = (a.N + 15) / 16;
-  // Few column blocks (fewer than four workgroups per CU) split K over workgroups as well, as far
-  // as every part keeps kSkMinStages stages; never the QKV product, whose first workgroup clears
-  // the split counters.
-  int split = 1;
-  if (EPI != EPI_QKV && a.sk_part && a.sk_cnt && nblk <= a.n_sk_cnt)
-    while (2 * split <= kSkinnyMaxSplit && nblk * split < 4 * cus && a.K % (2 * split * kq) == 0 &&
-           a.K / (2 * split) >= kq * kSkMinStages)
-      split *= 2;
-  const int kp = a.K / split;
-  // as many waves as divide the part evenly while each still streams at least kSkMinStages stages
-  int ks = kSkinnyMaxWaves;
-  while (ks > 1 && (kp % (ks * kq) != 0 || kp / (ks * kq) < kSkMinStages)) ks >>= 1;
-  if (kp % (ks * kq) != 0) return hipErrorInvalidValue;
+  // never split the QKV product, whose first workgroup clears the split counters
+  const bool can_split = EPI != EPI_QKV && a.sk_part && a.sk_cnt && nblk <= a.n_sk_cnt;
+  SkPlan best;
+  for (int split = 1; split <= (can_split ? kSkinnyMaxSplit : 1); split *= 2) {
+    if (a.K % (split * kq) != 0) continue;
+    const int kp = a.K / split, nwg = nblk * split, per_cu = (nwg + cus - 1) / cus;
+    for (int ks = kSkinnyMaxWaves; ks >= 1; ks >>= 1) {
+      if (kp % (ks * kq) != 0 || kp / (ks * kq) < kSkMinStages || skinny_slots<I8, EPI>(ks) < per_cu) continue;
+      const bool better = best.split == 0 || (long)per_cu * best.split < (long)best.per_cu * split;
+      if (better) best = SkPlan{split, ks, per_cu};
+      break;  // the most waves that fit this split
+    }
+  }
+  if (best.split == 0) {  // nothing fits one round: the most waves that divide K
+    int ks = kSkinnyMaxWaves;
+    while (ks > 1 && (a.K % (ks * kq) != 0 || a.K / (ks * kq) < kSkMinStages)) ks >>= 1;
+    if (a.K % (ks * kq) == 0) best = SkPlan{1, ks, 0};
+  }
+  return best;
+}
+
+template <bool I8, int EPI>
+hipError_t launch_skinny_t(const GemmArgs& a, int cus, hipStream_t st) {
+  const SkPlan p = skinny_plan<I8, EPI>(a, cus);
+  if (p.split == 0) return hipErrorInvalidValue;
+  const int nblk = (a.N + 15) / 16;
   GemmArgs g = a;
-  g.tiles_n = split;
-  if (split == 1 && EPI != EPI_QKV) g.n_sk_cnt = 0;
-  const size_t lds = (size_t)ks * kSkR * 2048;
+  g.tiles_n = p.split;
+  if (p.split == 1 && EPI != EPI_QKV) g.n_sk_cnt = 0;
+  const size_t lds = (size_t)p.ks * kSkR * 2048;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_dma_kernel<I8, EPI>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((skinny_dma_kernel<I8, EPI>), dim3(nblk * split), dim3(64 * ks), lds, st, g);
+  hipLaunchKernelGGL((skinny_dma_kernel<I8, EPI>), dim3(nblk * p.split), dim3(64 * p.ks), lds, st, g);
   return hipGetLastError();
 }
 
