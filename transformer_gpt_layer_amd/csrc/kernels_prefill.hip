@@ -764,7 +764,10 @@ constexpr int kSkinnyMaxWaves = 8;  // waves (K splits) per workgroup at most
 constexpr int kSkR = 2;          // stages in flight per wave: deeper rings (3, 4, 6) measured slower
 constexpr int kSkMinStages = 8;  // stages per wave worth a wave of its own
 
-template <bool I8, int EPI, int R = kSkR>
+// A1: at most 8 activation rows, so one activation load per 64 k (fp16) or two per 128 k (int8)
+// fill the operands of both MFMA halves of a stage: lanes of rows 8-15 (whose products are
+// discarded) load the second half of rows 0-7, which a row rotate by 8 lanes hands to rows 0-7.
+template <bool I8, int EPI, bool A1, int R = kSkR>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63, KS = blockDim.x >> 6;
@@ -782,7 +785,8 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
   }
   const int K = g.K;
   constexpr int SK = I8 ? 128 : 64;               // k per stage
-  constexpr int LPS = I8 ? 8 : 4;                 // loads per stage: 2 W lines-sets, A, scales
+  // loads per stage: 2 W line-sets, the activation loads, one scale load (int8)
+  constexpr int LPS = I8 ? (A1 ? 5 : 7) : (A1 ? 3 : 4);
   const int kq = K / split / KS, kb = sp * (K / split) + w * kq, ns = kq / SK;
   const uint32_t wrow = (uint32_t)(I8 ? K : 2 * K);  // bytes per weight row
   const rsrc_t rw = make_rsrc(I8 ? (const void*)g.wq : (const void*)g.w, (uint32_t)((size_t)g.N * wrow));
@@ -792,13 +796,19 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
   // W: wave load u of a stage covers rows n0 + 8u + L/8, logical chunk (L%8) ^ (L/8)
   const int lr = lane >> 3, lc = (lane & 7) ^ lr;
   const uint32_t w_off = (uint32_t)(n0 + lr) * wrow + (uint32_t)(I8 ? kb : 2 * kb) + lc * 16;
-  // A: row r; fp16 step s of a stage takes k 32s + 8j .. +8; int8 group g takes 64g + 16j .. +16
-  const uint32_t a_off = (uint32_t)((r * K + kb) * 2) + (uint32_t)(I8 ? 32 * j : 16 * j);
+  // A: row r; fp16 step s of a stage takes k 32s + 8j .. +8; int8 group g takes 64g + 16j .. +16.
+  // With A1, lanes of rows 8-15 take the second step (group) of row r - 8.
+  const int ar = A1 ? (r & 7) : r;
+  const uint32_t a_off = (uint32_t)((ar * K + kb) * 2) + (uint32_t)(I8 ? 32 * j : 16 * j) +
+                         (A1 && r >= 8 ? (I8 ? 128u : 64u) : 0u);
+  // int8: the scales of the stage's two 64-k groups, adjacent fp16 values (4-byte aligned: K/64
+  // and kb/64 are even)
   const uint32_t s_off = (uint32_t)((n0 + r) * (K / 64) + kb / 64) * 2;
-  u32x4 av[R][I8 ? 4 : 2];
-  float sc[R][2];
+  constexpr int NA = I8 ? (A1 ? 2 : 4) : (A1 ? 1 : 2);  // activation loads per stage
+  u32x4 av[R][NA];
+  uint32_t sc[R];
   // lanes of rows past M issue no activation loads (their operand rows are zeros)
-  const bool arow = r < g.M;
+  const bool arow = ar < g.M;
   auto issue = [&](int i, int slot) {
     const bool ok = i < ns;
     const uint32_t wk = (uint32_t)i * 128u;  // W bytes per row per stage: 128 for fp16 and int8
@@ -807,25 +817,14 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(ring + slot * 2048 + u * 1024), 16,
                                                ok ? w_off + (uint32_t)(8 * u) * wrow + wk : kOutOfRange, 0, 0, 0);
     const uint32_t ak = (uint32_t)(i * SK * 2);
-    if constexpr (!I8) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        av[slot][t] = u32x4{0u, 0u, 0u, 0u};
-        if (arow) av[slot][t] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ak + 64 * t : kOutOfRange, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        av[slot][2 * t] = u32x4{0u, 0u, 0u, 0u};
-        av[slot][2 * t + 1] = u32x4{0u, 0u, 0u, 0u};
-        if (arow) {
-          av[slot][2 * t] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ak + 128 * t : kOutOfRange, 0, 0);
-          av[slot][2 * t + 1] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ak + 128 * t + 16 : kOutOfRange, 0, 0);
-        }
-        const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? s_off + (uint32_t)(2 * i + t) * 2 : kOutOfRange, 0, 0);
-        sc[slot][t] = (float)__builtin_bit_cast(half_t, h);
-      }
+    for (int t = 0; t < NA; ++t) {
+      // fp16: step t at +64 t; int8: group t / 2 at +128 (t / 2), its second 16 bytes at +16
+      const uint32_t at = I8 ? (uint32_t)(128 * (t >> 1) + 16 * (t & 1)) : (uint32_t)(64 * t);
+      av[slot][t] = u32x4{0u, 0u, 0u, 0u};
+      if (arow) av[slot][t] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? a_off + ak + at : kOutOfRange, 0, 0);
     }
+    if constexpr (I8) sc[slot] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? s_off + (uint32_t)i * 4u : kOutOfRange, 0, 0);
   };
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -837,21 +836,37 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
       wait_vm<(R - 1) * LPS>();
       const unsigned char* st = ring + q * 2048;
       if (i + q < ns) {
+        // the activation operands of the stage's two halves (fp16 steps, int8 groups)
+        u32x4 op[I8 ? 4 : 2];
+        if constexpr (A1) {
+#pragma unroll
+          for (int t = 0; t < NA; ++t) {
+            op[t] = av[q][t];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)  // row_ror:8
+              op[NA + t][e] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)av[q][t][e], 0x128, 0xf, 0xf, false);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < NA; ++t) op[t] = av[q][t];
+        }
         if constexpr (!I8) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const half8_t b = *reinterpret_cast<const half8_t*>(st + swz(r, 4 * t + j));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av[q][t]), b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, op[t]), b, acc, 0, 0, 0);
           }
         } else {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const u32x4 c = *reinterpret_cast<const u32x4*>(st + swz(r, 4 * t + j));
             float4_t p = {0.f, 0.f, 0.f, 0.f};
-            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av[q][2 * t]), i8x8_to_half8(c.x, c.y), p, 0, 0, 0);
-            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av[q][2 * t + 1]), i8x8_to_half8(c.z, c.w), p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, op[2 * t]), i8x8_to_half8(c.x, c.y), p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, op[2 * t + 1]), i8x8_to_half8(c.z, c.w), p, 0, 0, 0);
+            const half2_t sp2 = as_half2(sc[q]);
+            const float scale = (float)(t == 0 ? sp2.x : sp2.y);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = fmaf(p[e], sc[q][t], acc[e]);
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(p[e], scale, acc[e]);
           }
         }
       }
@@ -900,13 +915,13 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
 
 // Resident workgroups per CU of a skinny variant with `waves` waves (the runtime's occupancy
 // figure: registers, LDS and wave slots), cached per variant and wave count.
-template <bool I8, int EPI>
+template <bool I8, int EPI, bool A1>
 int skinny_slots(int waves) {
   static int cache[kSkinnyMaxWaves + 1] = {};
   int& c = cache[waves];
   if (c == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&skinny_dma_kernel<I8, EPI>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&skinny_dma_kernel<I8, EPI, A1>),
                                                      64 * waves, (size_t)waves * kSkR * 2048) != hipSuccess)
       n = 0;
     c = n > 0 ? n : -1;
@@ -922,7 +937,7 @@ int skinny_slots(int waves) {
 struct SkPlan {
   int split = 0, ks = 0, per_cu = 0;
 };
-template <bool I8, int EPI>
+template <bool I8, int EPI, bool A1>
 SkPlan skinny_plan(const GemmArgs& a, int cus) {
   const int kq = I8 ? 128 : 64;  // k per stage
   const int nblk = (a.N + 15) / 16;
@@ -933,7 +948,7 @@ SkPlan skinny_plan(const GemmArgs& a, int cus) {
     if (a.K % (split * kq) != 0) continue;
     const int kp = a.K / split, nwg = nblk * split, per_cu = (nwg + cus - 1) / cus;
     for (int ks = kSkinnyMaxWaves; ks >= 1; ks >>= 1) {
-      if (kp % (ks * kq) != 0 || kp / (ks * kq) < kSkMinStages || skinny_slots<I8, EPI>(ks) < per_cu) continue;
+      if (kp % (ks * kq) != 0 || kp / (ks * kq) < kSkMinStages || skinny_slots<I8, EPI, A1>(ks) < per_cu) continue;
       const bool better = best.split == 0 || (long)per_cu * best.split < (long)best.per_cu * split;
       if (better) best = SkPlan{split, ks, per_cu};
       break;  // the most waves that fit this split
@@ -947,19 +962,19 @@ SkPlan skinny_plan(const GemmArgs& a, int cus) {
   return best;
 }
 
-template <bool I8, int EPI>
+template <bool I8, int EPI, bool A1>
 hipError_t launch_skinny_t(const GemmArgs& a, int cus, hipStream_t st) {
-  const SkPlan p = skinny_plan<I8, EPI>(a, cus);
+  const SkPlan p = skinny_plan<I8, EPI, A1>(a, cus);
   if (p.split == 0) return hipErrorInvalidValue;
   const int nblk = (a.N + 15) / 16;
   GemmArgs g = a;
   g.tiles_n = p.split;
   if (p.split == 1 && EPI != EPI_QKV) g.n_sk_cnt = 0;
   const size_t lds = (size_t)p.ks * kSkR * 2048;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_dma_kernel<I8, EPI>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_dma_kernel<I8, EPI, A1>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((skinny_dma_kernel<I8, EPI>), dim3(nblk * p.split), dim3(64 * p.ks), lds, st, g);
+  hipLaunchKernelGGL((skinny_dma_kernel<I8, EPI, A1>), dim3(nblk * p.split), dim3(64 * p.ks), lds, st, g);
   return hipGetLastError();
 }
 
@@ -1011,19 +1026,22 @@ int gemm_pick(int M, int N, int K, int cus) {
   return tiles <= cus ? 1 : 0;
 }
 
+template <int E>
+hipError_t launch_skinny_e(bool i8, const GemmArgs& a, int cus, hipStream_t st) {
+  const bool a1 = a.M <= 8;  // one activation load serves both halves of a stage
+  if (i8) return a1 ? launch_skinny_t<true, E, true>(a, cus, st) : launch_skinny_t<true, E, false>(a, cus, st);
+  return a1 ? launch_skinny_t<false, E, true>(a, cus, st) : launch_skinny_t<false, E, false>(a, cus, st);
+}
+
 hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, int cus, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.M > kSkinnyMaxRows) return hipErrorInvalidValue;
-#define DS_SK(E)                                                                                   \
-  case E:                                                                                          \
-    return int8_weights ? launch_skinny_t<true, E>(a, cus, st) : launch_skinny_t<false, E>(a, cus, st);
   switch (epi) {
-    DS_SK(EPI_QKV)
-    DS_SK(EPI_OPROJ)
-    DS_SK(EPI_FF1)
-    DS_SK(EPI_FF2)
+    case EPI_QKV: return launch_skinny_e<EPI_QKV>(int8_weights, a, cus, st);
+    case EPI_OPROJ: return launch_skinny_e<EPI_OPROJ>(int8_weights, a, cus, st);
+    case EPI_FF1: return launch_skinny_e<EPI_FF1>(int8_weights, a, cus, st);
+    case EPI_FF2: return launch_skinny_e<EPI_FF2>(int8_weights, a, cus, st);
   }
-#undef DS_SK
   return hipErrorInvalidValue;
 }
 
