@@ -248,7 +248,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
   constexpr int EK = 16 / (int)sizeof(AT);  // elements per 16-byte load
   constexpr int LPK = D / EK;               // lanes per key
   constexpr int KPI = kWave / LPK;          // keys per wave per load
-  constexpr int NIT = (C + 4 * KPI - 1) / (4 * KPI);
+  constexpr int KPS = 4 * KPI;              // keys per workgroup step
+  constexpr int PF = 4;                     // steps whose K and V loads a wave keeps in flight
+  static_assert(C % KPS == 0, "chunk of whole steps");
   const float kNeg = -1e30f;
   __shared__ float s_m[4], s_l[4];
   __shared__ float s_acc[4][D];
@@ -260,9 +262,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
   const int len0 = a.d_len[seq];
   int nkeys = a.causal ? len0 + t + 1 : len0 + a.tokens;
   if (nkeys > a.cap) nkeys = a.cap;
-  const int nvalid = (nkeys + C - 1) / C;
+  // ceil(nkeys / C) chunks of equal length (whole steps, at most C), so that no workgroup is left
+  // with a sliver of the keys
+  const int nch = (nkeys + C - 1) / C;
+  const int cs = ((nkeys + nch - 1) / nch + KPS - 1) / KPS * KPS;
+  const int nvalid = (nkeys + cs - 1) / cs;
   if (c >= nvalid) return;
-  const int kb = c * C, ke = min(kb + C, nkeys);
+  const int kb = c * cs, ke = min(kb + cs, nkeys);
+  const int nsteps = (ke - kb + KPS - 1) / KPS;
   const int H = a.heads * D;
 
   // q slice of this lane, scaled by log2(e)/sqrt(d) so that scores feed exp2 directly
@@ -276,69 +283,79 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
     else qv[e] = a.q[qi] * qs;
   }
 
+  // K and V rows of this (sequence, head) as buffers ending at the last key: loads past it, and
+  // the out-of-chunk requests of the last steps, read zeros
   const size_t head_base = (((size_t)seq * a.heads + j) * a.cap) * D;
-  const AT* Kp = reinterpret_cast<const AT*>(a.k_cache) + head_base;
-  const AT* Vp = reinterpret_cast<const AT*>(a.v_cache) + head_base;
+  const uint32_t hbytes = (uint32_t)((size_t)nkeys * D * sizeof(AT));
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<AT*>(reinterpret_cast<const AT*>(a.k_cache) + head_base), (short)0, (int)hbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<AT*>(reinterpret_cast<const AT*>(a.v_cache) + head_base), (short)0, (int)hbytes, 0x00020000);
+  const int kl = wave * KPI + lane / LPK;  // this lane's key within a step
+  u32x4 kr[PF], vr[PF];
+  auto issue = [&](int step, int slot) {
+    const int key = kb + step * KPS + kl;
+    const uint32_t off = step < nsteps && key < ke ? (uint32_t)(((size_t)key * D + e0) * sizeof(AT)) : 0x80000000u;
+    kr[slot] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    vr[slot] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+  };
+#pragma unroll
+  for (int q = 0; q < PF; ++q) issue(q, q);
 
-  // the chunk's K and V rows are requested together: one memory round trip per workgroup
-  float sc[NIT];
-  bool valid[NIT];
-  u32x4 raw[NIT], rawv[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int key = kb + (it * 4 + wave) * KPI + lane / LPK;
-    valid[it] = key < ke;
-    raw[it] = valid[it] ? ld16(Kp + (size_t)key * D + e0) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int key = kb + (it * 4 + wave) * KPI + lane / LPK;
-    rawv[it] = valid[it] ? ld16(Vp + (size_t)key * D + e0) : u32x4{0, 0, 0, 0};
-  }
-  float m = kNeg;
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    float p = 0.f;
-    if constexpr (sizeof(AT) == 4) {
-      p = qv[0] * as_f32(raw[it].x) + qv[1] * as_f32(raw[it].y) + qv[2] * as_f32(raw[it].z) +
-          qv[3] * as_f32(raw[it].w);
-    } else {
-      const uint32_t wv[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const half2_t kk = as_half2(wv[h]);
-        p += qv[2 * h] * (float)kk.x + qv[2 * h + 1] * (float)kk.y;
-      }
-    }
-    p = group_sum<LPK>(p);
-    sc[it] = valid[it] ? p : kNeg;
-    m = fmaxf(m, sc[it]);
-  }
-  m = wave_max(m);
-
-  float l = 0.f, acc[EK];
+  // online softmax over this lane's keys: running max m, weight sum l, weighted V sum acc
+  float m = kNeg, l = 0.f, acc[EK];
 #pragma unroll
   for (int e = 0; e < EK; ++e) acc[e] = 0.f;
+  for (int i = 0; i < nsteps; i += PF) {
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const float p = valid[it] ? exp2f(sc[it] - m) : 0.f;
-    l += p;
-    if constexpr (sizeof(AT) == 4) {
-      acc[0] += p * as_f32(rawv[it].x);
-      acc[1] += p * as_f32(rawv[it].y);
-      acc[2] += p * as_f32(rawv[it].z);
-      acc[3] += p * as_f32(rawv[it].w);
-    } else {
-      const uint32_t wv[4] = {rawv[it].x, rawv[it].y, rawv[it].z, rawv[it].w};
+    for (int q = 0; q < PF; ++q) {
+      if (i + q < nsteps) {
+        const int key = kb + (i + q) * KPS + kl;
+        float p = 0.f;
+        if constexpr (sizeof(AT) == 4) {
+          p = qv[0] * as_f32(kr[q].x) + qv[1] * as_f32(kr[q].y) + qv[2] * as_f32(kr[q].z) + qv[3] * as_f32(kr[q].w);
+        } else {
+          const uint32_t wv[4] = {kr[q].x, kr[q].y, kr[q].z, kr[q].w};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const half2_t vv = as_half2(wv[h]);
-        acc[2 * h] += p * (float)vv.x;
-        acc[2 * h + 1] += p * (float)vv.y;
+          for (int h = 0; h < 4; ++h) {
+            const half2_t kk = as_half2(wv[h]);
+            p += qv[2 * h] * (float)kk.x + qv[2 * h + 1] * (float)kk.y;
+          }
+        }
+        p = group_sum<LPK>(p);
+        if (key < ke) {
+          const float mn = fmaxf(m, p);
+          const float cf = exp2f(m - mn), w = exp2f(p - mn);
+          m = mn;
+          l = l * cf + w;
+          if constexpr (sizeof(AT) == 4) {
+            acc[0] = acc[0] * cf + w * as_f32(vr[q].x);
+            acc[1] = acc[1] * cf + w * as_f32(vr[q].y);
+            acc[2] = acc[2] * cf + w * as_f32(vr[q].z);
+            acc[3] = acc[3] * cf + w * as_f32(vr[q].w);
+          } else {
+            const uint32_t wv[4] = {vr[q].x, vr[q].y, vr[q].z, vr[q].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const half2_t vv = as_half2(wv[h]);
+              acc[2 * h] = acc[2 * h] * cf + w * (float)vv.x;
+              acc[2 * h + 1] = acc[2 * h + 1] * cf + w * (float)vv.y;
+            }
+          }
+        }
       }
+      issue(i + q + PF, q);
     }
   }
-  // reduce over the key slots of the wave (lanes with equal lane % LPK)
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the requests past the end
+  // rescale every key slot to the wave's max, then reduce over the slots (lanes with equal
+  // lane % LPK)
+  const float mw = wave_max(m);
+  const float sw = exp2f(m - mw);
+  l *= sw;
+#pragma unroll
+  for (int e = 0; e < EK; ++e) acc[e] *= sw;
+  m = mw;
 #pragma unroll
   for (int off = LPK; off < kWave; off <<= 1) {
     l += __shfl_xor(l, off, kWave);
