@@ -25,7 +25,8 @@ PEAK_HBM_GBS = 8000.0
 # the SHA-256 of the kernel's source file; the figure is reported only while that source is
 # unchanged.
 TRAFFIC_RECORDS = {
-    "stack_decode_kernel": ("profiles/stack_decode_kernel_c2_f16_b1.md", "transformer_gpt_layer_amd/csrc/kernels_stack.hip"),
+    "stack_decode_kernel": ("profiles/stack_decode_kernel_c2_f16_b1.md",
+                            ("transformer_gpt_layer_amd/csrc/kernels_stack.hip", "transformer_gpt_layer_amd/csrc/ds_stack.hpp")),
 }
 
 
@@ -35,10 +36,13 @@ def measured_traffic(kernel: str, workload: str):
 
     if kernel not in TRAFFIC_RECORDS:
         return None
-    summary, source = (os.path.join(ROOT, p) for p in TRAFFIC_RECORDS[kernel])
-    if not (os.path.exists(summary) and os.path.exists(source)):
+    summary, sources = TRAFFIC_RECORDS[kernel]
+    summary = os.path.join(ROOT, summary)
+    sources = [os.path.join(ROOT, p) for p in sources]
+    if not (os.path.exists(summary) and all(os.path.exists(p) for p in sources)):
         return None
-    digest = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    # the record holds for exactly these kernel sources (the files concatenated, in this order)
+    digest = hashlib.sha256(b"".join(open(p, "rb").read() for p in sources)).hexdigest()
     for line in open(summary):
         m = re.match(r"traffic-record: (\{.*\})\s*$", line.strip())
         if m:

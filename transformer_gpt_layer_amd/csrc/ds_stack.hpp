@@ -38,7 +38,7 @@ enum { TAG_Q = 0, TAG_PART = 1, TAG_CTX = 2, TAG_X2 = 3, TAG_F = 4, TAG_Y = 5 };
 // Workgroup shape: kStackSyncWaves waves stage activations, reduce, run the epilogues and attention
 // and exchange tagged values; kStackWorkers waves stream the weights and compute the row dot products.
 constexpr int kStackSyncWaves = 4;
-constexpr int kStackWorkers = 12;
+constexpr int kStackWorkers = 8;
 constexpr int kStackWaves = kStackSyncWaves + kStackWorkers;
 constexpr int kStackThreads = 64 * kStackWaves;  // one workgroup per CU
 constexpr int kStackChunk = 64;                  // cache rows per attention work item

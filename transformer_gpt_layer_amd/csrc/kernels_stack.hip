@@ -7,12 +7,12 @@
 // fusion boundaries where partial results must meet (the all-reduce points); here those are the
 // points where a phase waits for the values of the previous one, produced by other workgroups.
 //
-// gfx950 design. One cooperative launch keeps one 16-wave workgroup per CU resident for the whole
+// gfx950 design. One cooperative launch keeps one 12-wave workgroup per CU resident for the whole
 // step. Each projection is cut into per-workgroup row tiles; a tile is one contiguous range of the
 // row-major matrix, cut into 1 KB "slices" (one 16-byte load per lane of a wave64).
 //
 // The waves are specialized so that HBM never waits for the step's serial parts:
-//  - 12 worker waves own contiguous blocks of each tile and walk the fixed sequence of all their
+//  - 8 worker waves own contiguous blocks of each tile and walk the fixed sequence of all their
 //    slices of all layers. Each keeps kRing slices in flight in a rotating set of registers: a
 //    slice is multiplied with the staged activation (LDS) the moment it is consumed, and its
 //    registers at once load the slice kRing places further on, whatever phase or layer that is.
@@ -38,8 +38,11 @@ constexpr int NS = kStackSyncWaves;
 constexpr int NT = NS * kWave;             // sync threads
 constexpr int NWK = kStackWorkers;
 // Weight slices a worker keeps in flight: 24 for fp16 weights and one batch row (24 KB per wave,
-// 288 KB per CU), 16 for fp32; variants with four batch rows or int8 weights (two 16-byte
-// activation reads per row) keep 12 so that a 128-VGPR wave still holds everything.
+// 192 KB per CU), 16 for fp32; variants with four batch rows or int8 weights (two 16-byte
+// activation reads per row) keep 12. Twelve waves per workgroup (three per SIMD) leave every wave
+// up to 168 VGPRs: the sync waves' attention and staging then run without register spills, whose
+// reloads from scratch memory (queued behind the weight stream) cost 9 % of the step at sixteen
+// waves and 128 VGPRs. 288 KB in flight per CU streamed no faster than 192 KB.
 template <typename WT, int BM> struct Ring { static constexpr int value = (sizeof(WT) == 1 || BM == 4) ? 12 : (sizeof(WT) == 2 ? 24 : 16); };
 constexpr int kAuxCoherent = 16;           // sc1
 constexpr int kAuxStream = 2;              // nt
