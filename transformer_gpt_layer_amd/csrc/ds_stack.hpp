@@ -44,6 +44,14 @@ constexpr int kStackThreads = 64 * kStackWaves;  // one workgroup per CU
 constexpr int kStackChunk = 64;                  // cache rows per attention work item
 constexpr int kStackLdsMax = 160 * 1024;
 
+// Rows of an N-row projection per workgroup tile. FF1's tiles hold an even number of rows, so
+// that the fp16 stacks can exchange its outputs as packed pairs (both rows of a pair are produced
+// by one workgroup).
+__host__ __device__ inline int stack_tile_rows(int N, int G, bool even) {
+  const int r = (N + G - 1) / G;
+  return even ? (r + 1) & ~1 : r;
+}
+
 // Dynamic LDS layout of one workgroup (byte offsets; the activation rows start at 0). Identical on
 // the host and the device.
 struct StackLds {

@@ -198,6 +198,13 @@ __device__ __forceinline__ void tstore(rsrc_t r, uint32_t idx, float v, uint32_t
   __builtin_amdgcn_raw_buffer_store_b64(pv, r, idx * 8u, 0, kAuxCoherent);
 }
 
+// Two fp16 values packed in the value word of one tagged 8-byte store (element 2i low, 2i+1 high).
+__device__ __forceinline__ void tstore_pair(rsrc_t r, uint32_t pair, half_t lo, half_t hi, uint32_t tag) {
+  const uint32_t v = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  const u32x2 pv = {v, tag};
+  __builtin_amdgcn_raw_buffer_store_b64(pv, r, pair * 8u, 0, kAuxCoherent);
+}
+
 __device__ __forceinline__ bool grid_error(const StackArgs& a) {
   return __hip_atomic_load(a.sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
@@ -296,7 +303,7 @@ __device__ __forceinline__ Geo phase_geo(const StackArgs& a, int SL, int g, int 
   Geo p;
   p.N = ph == 0 ? 3 * H : (ph == 2 ? F : H);
   p.K = ph == 3 ? F : H;
-  const int rows = (p.N + G - 1) / G;
+  const int rows = stack_tile_rows(p.N, G, ph == 2);
   p.r0 = min(p.N, g * rows);
   p.nr = min(p.N, p.r0 + rows) - p.r0;
   const int T = p.nr * (p.K / SL);
@@ -831,7 +838,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
   const int nitems = B * a.nh * a.nchunk;
 
   // per-workgroup row tiles of each projection (the same split the workers use)
-  const int rq = (3 * H + G - 1) / G, ro = (H + G - 1) / G, r1 = (F + G - 1) / G;
+  const int rq = stack_tile_rows(3 * H, G, false), ro = stack_tile_rows(H, G, false), r1 = stack_tile_rows(F, G, true);
   const int q0 = min(3 * H, g * rq), nq = min(3 * H, q0 + rq) - q0;
   const int o0 = min(H, g * ro), no = min(H, o0 + ro) - o0;
   const int f0 = min(F, g * r1), nf = min(F, f0 + r1) - f0;
@@ -956,10 +963,21 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     if (!hand_over(seq0 + 2u)) return;
     {
       const rsrc_t rf = make_rsrc(a.f, (uint32_t)(B * F * 8));
-      for (int t = st; t < nf * B; t += NT) {
-        const int rl = t / B, b = t - rl * B, n = f0 + rl;
-        const float z = row_sum(rl, b) + ldp<AT>(L.b_ff1, n);
-        tstore(rf, (uint32_t)(b * F + n), (float)(AT)gelu(z, a.gelu_tanh != 0), t_f);
+      if constexpr (sizeof(AT) == 2) {
+        // fp16 f: pairs of rows (f0 and nf are even) in one tagged store each, half the bytes the
+        // FF2 staging polls
+        for (int t = st; t < (nf / 2) * B; t += NT) {
+          const int pl = t / B, b = t - pl * B, rl = 2 * pl, n = f0 + rl;
+          const half_t g0 = (half_t)gelu(row_sum(rl, b) + ldp<AT>(L.b_ff1, n), a.gelu_tanh != 0);
+          const half_t g1 = (half_t)gelu(row_sum(rl + 1, b) + ldp<AT>(L.b_ff1, n + 1), a.gelu_tanh != 0);
+          tstore_pair(rf, (uint32_t)((b * F + n) / 2), g0, g1, t_f);
+        }
+      } else {
+        for (int t = st; t < nf * B; t += NT) {
+          const int rl = t / B, b = t - rl * B, n = f0 + rl;
+          const float z = row_sum(rl, b) + ldp<AT>(L.b_ff1, n);
+          tstore(rf, (uint32_t)(b * F + n), (float)(AT)gelu(z, a.gelu_tanh != 0), t_f);
+        }
       }
     }
 
@@ -969,7 +987,17 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     clear_slots(ny);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff2, y0, ny, F, a.group, scl, st);
     zero_rows(F);
-    if (!poll_range(c, a, a.f, B * F, t_f, st, [&](int i, float v) { act[i] = (LT)v; })) return;
+    if constexpr (sizeof(AT) == 2) {
+      // pair i holds f elements 2i and 2i + 1 of the [B][F] rows
+      if (!poll_range(c, a, a.f, B * F / 2, t_f, st, [&](int i, float v) {
+            const uint32_t u = __builtin_bit_cast(uint32_t, v);
+            act[2 * i] = (LT)__builtin_bit_cast(half_t, (uint16_t)(u & 0xffffu));
+            act[2 * i + 1] = (LT)__builtin_bit_cast(half_t, (uint16_t)(u >> 16));
+          }))
+        return;
+    } else if (!poll_range(c, a, a.f, B * F, t_f, st, [&](int i, float v) { act[i] = (LT)v; })) {
+      return;
+    }
     if (!hand_over(seq0 + 3u)) return;
     {
       const rsrc_t ryt = make_rsrc(a.ybuf, (uint32_t)(B * H * 8));
@@ -1041,7 +1069,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
 int stack_rows_per_wg(int H, int F, int G) {
   int r = (3 * H + G - 1) / G;
   r = max(r, (H + G - 1) / G);
-  r = max(r, (F + G - 1) / G);
+  r = max(r, stack_tile_rows(F, G, true));
   return r;
 }
 
