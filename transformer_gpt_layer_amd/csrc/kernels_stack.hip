@@ -851,6 +851,10 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     for (int w = 0; w < NWK; ++w) s += p[w * BM];
     return s;
   };
+  // Epilogue operands of this thread's first row are requested when its phase begins, so that
+  // their memory latency (long while the workers stream) passes during the staging and the
+  // workers' products instead of after them; later rows (t >= NT) load in the loop.
+  auto pre_ld = [&](const void* bias, int r0, int nr) { return st < nr * B ? ldp<AT>(bias, r0 + st / B) : 0.f; };
   auto clear_slots = [&](int nr) {
     for (int i = st; i < nr * NWK * BM; i += NT) slots[i] = 0.f;
   };
@@ -881,6 +885,8 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 
     // ---- region 1: LN1 + QKV + bias; q, k, v tagged; k, v also into the cache row d_len[b]
     fresh();
+    const float pre_q = pre_ld(L.b_qkv, q0, nq);
+    const int pre_pos = L.d_len[st % B];
     if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nq);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_qkv, q0, nq, H, a.group, scl, st);
@@ -907,14 +913,14 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
       const rsrc_t rk = make_rsrc(L.k, cache_bytes), rv = make_rsrc(L.v, cache_bytes);
       for (int t = st; t < nq * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = q0 + rl;
-        const float z = row_sum(rl, b) + ldp<AT>(L.b_qkv, n);
+        const float z = row_sum(rl, b) + (t == st ? pre_q : ldp<AT>(L.b_qkv, n));
         if (n < H) {
           tstore(rqo, (uint32_t)(b * H + n), z, t_q);
         } else {
           const int m = n < 2 * H ? n - H : n - 2 * H, j = m / D, e = m - j * D;
           const float zr = (float)(AT)z;  // the value the cache holds
           tstore(n < 2 * H ? rkn : rvn, (uint32_t)(b * H + m), zr, t_q);
-          const int pos = L.d_len[b];
+          const int pos = t == st ? pre_pos : L.d_len[b];
           if (pos >= 0 && pos < a.cap)
             coh_st_act<AT>(n < 2 * H ? rk : rv, (uint32_t)((((size_t)b * a.nh + j) * a.cap + pos) * D + e), z);
         }
@@ -933,6 +939,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 
     // ---- output projection + bias + residual: x2 = x + Wo ctx + bo
     fresh();
+    const float pre_o = pre_ld(L.b_o, o0, no);
     if (!sync_bar(c, a, sb, st)) return;  // the attention scratch (same LDS) and the slots are free
     clear_slots(no);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_o, o0, no, H, a.group, scl, st);
@@ -943,7 +950,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
       const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 8));
       for (int t = st; t < no * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = o0 + rl;
-        const float z = row_sum(rl, b) + ldp<AT>(L.b_o, n);
+        const float z = row_sum(rl, b) + (t == st ? pre_o : ldp<AT>(L.b_o, n));
         const float xr = l == 0 ? ldp<AT>(a.x, b * H + n) : res_y[t];
         const float v = xr + z;
         res_x2[t] = v;
@@ -953,6 +960,10 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 
     // ---- region 3: LN2 + FF1 + bias + GeLU
     fresh();
+    // fp16: this thread's first pair of rows; otherwise its first row
+    const float pre_f0 = sizeof(AT) == 2 ? (st < (nf / 2) * B ? ldp<AT>(L.b_ff1, f0 + 2 * (st / B)) : 0.f)
+                                         : pre_ld(L.b_ff1, f0, nf);
+    const float pre_f1 = sizeof(AT) == 2 && st < (nf / 2) * B ? ldp<AT>(L.b_ff1, f0 + 2 * (st / B) + 1) : 0.f;
     if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nf);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff1, f0, nf, H, a.group, scl, st);
@@ -968,14 +979,15 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
         // FF2 staging polls
         for (int t = st; t < (nf / 2) * B; t += NT) {
           const int pl = t / B, b = t - pl * B, rl = 2 * pl, n = f0 + rl;
-          const half_t g0 = (half_t)gelu(row_sum(rl, b) + ldp<AT>(L.b_ff1, n), a.gelu_tanh != 0);
-          const half_t g1 = (half_t)gelu(row_sum(rl + 1, b) + ldp<AT>(L.b_ff1, n + 1), a.gelu_tanh != 0);
+          const float b0 = t == st ? pre_f0 : ldp<AT>(L.b_ff1, n), b1 = t == st ? pre_f1 : ldp<AT>(L.b_ff1, n + 1);
+          const half_t g0 = (half_t)gelu(row_sum(rl, b) + b0, a.gelu_tanh != 0);
+          const half_t g1 = (half_t)gelu(row_sum(rl + 1, b) + b1, a.gelu_tanh != 0);
           tstore_pair(rf, (uint32_t)((b * F + n) / 2), g0, g1, t_f);
         }
       } else {
         for (int t = st; t < nf * B; t += NT) {
           const int rl = t / B, b = t - rl * B, n = f0 + rl;
-          const float z = row_sum(rl, b) + ldp<AT>(L.b_ff1, n);
+          const float z = row_sum(rl, b) + (t == st ? pre_f0 : ldp<AT>(L.b_ff1, n));
           tstore(rf, (uint32_t)(b * F + n), (float)(AT)gelu(z, a.gelu_tanh != 0), t_f);
         }
       }
@@ -983,6 +995,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 
     // ---- region 4: FF2 + bias + residual: y = x2 + W2 f + b2
     fresh();
+    const float pre_y = pre_ld(L.b_ff2, y0, ny);
     if (!sync_bar(c, a, sb, st)) return;  // the LayerNorm rows (same LDS) and the slots are free
     clear_slots(ny);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff2, y0, ny, F, a.group, scl, st);
@@ -1004,7 +1017,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
       const rsrc_t ry = make_rsrc(a.y, (uint32_t)(B * H * sizeof(AT)));
       for (int t = st; t < ny * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = y0 + rl;
-        const float z = row_sum(rl, b) + ldp<AT>(L.b_ff2, n);
+        const float z = row_sum(rl, b) + (t == st ? pre_y : ldp<AT>(L.b_ff2, n));
         const float v = (float)(AT)(res_x2[t] + z);
         res_y[t] = v;
         if (last)
