@@ -174,7 +174,7 @@ def _oracle_weights(layer, wl):
     return w
 
 
-def cpu_baseline_prefill(wl, stack, target_rows: int = 64):
+def cpu_baseline_prefill(wl, stack, target_rows: int = 256):
     """The oracle (plain C, double, one thread) on a bounded sample: the first target_rows prompt
     rows of one sequence through layer 0, scaled to prompt tokens/s of the full L-layer stack."""
     import numpy as np
