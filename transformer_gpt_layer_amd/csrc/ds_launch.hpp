@@ -49,6 +49,8 @@ hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st);
 // The same attention with fp16 q and ctx (q16, ctx16) and an fp16 cache.
 hipError_t launch_attn_decode_f16(const AttnArgs& a, hipStream_t st);
 int attn_chunk_for(int rows, int heads, int cap);
+// Chunks per (row, head) for one launch, at most nmax (see the definition).
+int attn_chunks_for(int rows, int heads, int cap, int chunk, int nmax, int cus);
 
 hipError_t launch_kv_append(Dt adt, const void* k_new, const void* v_new, void* kc, void* vc,
                             const int32_t* d_len, int batch, int ntok, int heads, int head_dim,

@@ -262,9 +262,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
   const int len0 = a.d_len[seq];
   int nkeys = a.causal ? len0 + t + 1 : len0 + a.tokens;
   if (nkeys > a.cap) nkeys = a.cap;
-  // ceil(nkeys / C) chunks of equal length (whole steps, at most C), so that no workgroup is left
-  // with a sliver of the keys
-  const int nch = (nkeys + C - 1) / C;
+  // chunks of equal length (whole steps), so that no workgroup is left with a sliver of the keys:
+  // the launch's count, fewer when there are under 64 keys per chunk
+  const int nch = min(a.nchunk, (nkeys + 63) / 64);
   const int cs = ((nkeys + nch - 1) / nch + KPS - 1) / KPS * KPS;
   const int nvalid = (nkeys + cs - 1) / cs;
   if (c >= nvalid) return;
@@ -419,6 +419,26 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
 
 constexpr int kAttnChunk = 64;       // positions per workgroup for few (row, head) pairs
 constexpr int kAttnChunkWide = 256;  // and for many: fewer workgroups and partials to merge
+
+// Chunks per (row, head) for a launch. With 64-position chunks (few pairs), as many as the
+// capacity has. With wide chunks, between ceil(cap / 512) and nmax (the workspace's slots) the count
+// whose workgroups spread most evenly over the CUs, the fewest among equals: the 13B batch-8
+// step (320 pairs, capacity 1088) runs 4 chunks (1280 workgroups, 5 per CU) instead of 5 (6.25).
+int attn_chunks_for(int rows, int heads, int cap, int chunk, int nmax, int cus) {
+  if (chunk != kAttnChunkWide || cus <= 0) return nmax;
+  const long pairs = (long)rows * heads;
+  int best = nmax;
+  long best_num = 0, best_den = 1;  // imbalance ceil(pairs n / cus) cus / (pairs n)
+  for (int n = max(1, (cap + 511) / 512); n <= nmax; ++n) {
+    const long wg = pairs * n, num = (wg + cus - 1) / cus * cus;
+    if (best_num == 0 || num * best_den < best_num * wg) {
+      best = n;
+      best_num = num;
+      best_den = wg;
+    }
+  }
+  return best;
+}
 
 int attn_chunk_for(int rows, int heads, int cap) {
   (void)cap;

@@ -185,7 +185,8 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     ad.part = reinterpret_cast<float*>(base + W.part);
     ad.counters = reinterpret_cast<uint32_t*>(base + W.cnt);
     ad.rows = rows; ad.tokens = ntok; ad.heads = d.heads; ad.head_dim = d.head_dim;
-    ad.cap = kv->capacity; ad.chunk = W.chunk; ad.nchunk = W.nchunk; ad.causal = d.triangular_masking;
+    ad.cap = kv->capacity; ad.chunk = W.chunk; ad.causal = d.triangular_masking;
+    ad.nchunk = ds::attn_chunks_for(rows, d.heads, kv->capacity, W.chunk, W.nchunk, cus);
     if (hipError_t e = ds::launch_attn_decode_f16(ad, st)) return hip_fail(e, "attention launch");
   } else if (hipError_t e = ds::launch_attn_prefill(at, st)) {
     return hip_fail(e, "attention launch");
