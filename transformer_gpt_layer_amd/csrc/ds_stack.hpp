@@ -59,6 +59,8 @@ struct StackLds {
   uint32_t slots;   // per-(row, worker, batch row) partial sums
   uint32_t scales;  // int8 scales of the current row tile
   uint32_t wtab;    // the four weight-matrix pointers of every layer (8 bytes each)
+  uint32_t layers;  // a copy of every layer's StackLayer (the sync waves' parameters)
+  uint32_t lens;    // every layer's cache lengths at launch, 4 per layer (constant during the launch)
   uint32_t res;     // this workgroup's rows of x2, then of the layer output (fp32, res_n each)
   uint32_t res_n;
   uint32_t total;
@@ -84,7 +86,9 @@ __host__ __device__ inline StackLds stack_lds_layout(int wsize, int bm, int H, i
   L.scales = stack_align(L.slots + (uint32_t)rows_per_wg * kStackWorkers * bm * 4u);
   const uint32_t sc = wsize == 1 ? (uint32_t)rows_per_wg * (kmax / (uint32_t)group) * 2u : 0u;
   L.wtab = stack_align(L.scales + sc);
-  L.res = stack_align(L.wtab + (uint32_t)n_layers * 4u * 8u);
+  L.layers = stack_align(L.wtab + (uint32_t)n_layers * 4u * 8u);
+  L.lens = stack_align(L.layers + (uint32_t)n_layers * (uint32_t)sizeof(StackLayer));
+  L.res = stack_align(L.lens + (uint32_t)n_layers * 4u * 4u);
   L.res_n = (uint32_t)rows_per_wg * (uint32_t)bm;
   L.total = stack_align(L.res + 2u * L.res_n * 4u);
   return L;

@@ -631,7 +631,8 @@ template <typename AT, int D> struct AttnShape {
 // row at position len from this launch's tagged K/V), wave-reduced max and sum, the exp-weighted V
 // sum; (max, sum, acc[D]) is stored tagged for the workgroup that merges the (sequence, head).
 template <typename AT, int D>
-__device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_t& sb, const StackLayer& L, int item,
+__device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_t& sb, const StackLayer& L,
+                                             const int32_t* lens, int item,
                                              uint32_t tag_q, uint32_t tag_part, float* s_acc, int st) {
   typedef AttnShape<AT, D> S;
   constexpr int EK = S::EK, LPK = S::LPK, KPI = S::KPI, NIT = S::NIT;
@@ -639,7 +640,7 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
   const int cc = item % a.nchunk;
   const int j = (item / a.nchunk) % a.nh;
   const int b = item / (a.nchunk * a.nh);
-  const int len = L.d_len[b];
+  const int len = lens[b];
   int nkeys = len + 1;
   if (nkeys > a.cap) nkeys = a.cap;
   const int nvalid = (nkeys + kStackChunk - 1) / kStackChunk;
@@ -782,10 +783,10 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
 // Merge of one (sequence b, head j): every chunk's partial (log-sum-exp) into ctx, rounded to AT
 // as the per-layer path stores it.
 template <typename AT, int D>
-__device__ __forceinline__ bool attn_merge(Ctl& c, const StackArgs& a, uint32_t& sb, const StackLayer& L, int b, int j,
+__device__ __forceinline__ bool attn_merge(Ctl& c, const StackArgs& a, uint32_t& sb, const int32_t* lens, int b, int j,
                                            uint32_t tag_part, uint32_t tag_ctx, float* s_part, int st) {
   const float kNeg = -1e30f;
-  int nkeys = L.d_len[b] + 1;
+  int nkeys = lens[b] + 1;
   if (nkeys > a.cap) nkeys = a.cap;
   const int nvalid = (nkeys + kStackChunk - 1) / kStackChunk;
   const int H = a.nh * D;
@@ -876,7 +877,8 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
   };
 
   for (int l = 0; l < a.n_layers; ++l) {
-    const StackLayer& L = a.layers[l];
+    const StackLayer& L = reinterpret_cast<const StackLayer*>(smem + a.lds.layers)[l];
+    const int32_t* lens = reinterpret_cast<const int32_t*>(smem + a.lds.lens) + l * 4;  // d_len[b] at launch
     const bool last = l == a.n_layers - 1;
     const uint32_t seq0 = (uint32_t)l * 4u;
     const uint32_t t_q = stack_tag(launch, l, TAG_Q), t_part = stack_tag(launch, l, TAG_PART);
@@ -886,7 +888,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     // ---- region 1: LN1 + QKV + bias; q, k, v tagged; k, v also into the cache row d_len[b]
     fresh();
     const float pre_q = pre_ld(L.b_qkv, q0, nq);
-    const int pre_pos = L.d_len[st % B];
+    const int pre_pos = lens[st % B];
     if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nq);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_qkv, q0, nq, H, a.group, scl, st);
@@ -920,7 +922,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
           const int m = n < 2 * H ? n - H : n - 2 * H, j = m / D, e = m - j * D;
           const float zr = (float)(AT)z;  // the value the cache holds
           tstore(n < 2 * H ? rkn : rvn, (uint32_t)(b * H + m), zr, t_q);
-          const int pos = t == st ? pre_pos : L.d_len[b];
+          const int pos = t == st ? pre_pos : lens[b];
           if (pos >= 0 && pos < a.cap)
             coh_st_act<AT>(n < 2 * H ? rk : rv, (uint32_t)((((size_t)b * a.nh + j) * a.cap + pos) * D + e), z);
         }
@@ -931,10 +933,10 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     // merges it owns (chunk 0 of a head), so that no merge waits on a partial queued behind it
     fresh();
     for (int item = g; item < nitems; item += G)
-      if (!attn_partial<AT, D>(c, a, sb, L, item, t_q, t_part, s_acc, st)) return;
+      if (!attn_partial<AT, D>(c, a, sb, L, lens, item, t_q, t_part, s_acc, st)) return;
     for (int item = g; item < nitems; item += G)
       if (item % a.nchunk == 0 &&
-          !attn_merge<AT, D>(c, a, sb, L, item / (a.nchunk * a.nh), (item / a.nchunk) % a.nh, t_part, t_ctx, s_part, st))
+          !attn_merge<AT, D>(c, a, sb, lens, item / (a.nchunk * a.nh), (item / a.nchunk) % a.nh, t_part, t_ctx, s_part, st))
         return;
 
     // ---- output projection + bias + residual: x2 = x + Wo ctx + bo
@@ -1057,6 +1059,18 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
   uint64_t* wtab = reinterpret_cast<uint64_t*>(smem + a.lds.wtab);
   for (int i = threadIdx.x; i < a.n_layers * 4; i += kStackThreads)
     wtab[i] = reinterpret_cast<uint64_t>(phase_w(a.layers[i >> 2], i & 3));
+  // The layer table and the cache lengths in LDS: the sync waves read them inside their chain,
+  // where a global load would wait behind the CU's queue of weight loads.
+  static_assert(sizeof(StackLayer) % 4 == 0, "layer table in words");
+  {
+    constexpr int kWords = (int)(sizeof(StackLayer) / 4);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(smem + a.lds.layers);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.layers);
+    for (int i = threadIdx.x; i < a.n_layers * kWords; i += kStackThreads) dst[i] = src[i];
+    int32_t* lens = reinterpret_cast<int32_t*>(smem + a.lds.lens);
+    for (int i = threadIdx.x; i < a.n_layers * 4; i += kStackThreads)
+      lens[i] = (i & 3) < a.B ? a.layers[i >> 2].d_len[i & 3] : 0;
+  }
   if (threadIdx.x == 0) {
     c.act_ready = 0u;
     for (int w = 0; w < NWK; ++w) c.done[w] = 0u;
