@@ -123,6 +123,11 @@ __device__ __forceinline__ void raise_abort(Ctl& c, uint32_t* sync) {
   __hip_atomic_store(sync + kSyncError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The grid error flag is a global load, which waits behind the CU's queue of weight loads: a
+// waiting loop reads it once every kErrorEvery rounds, so that it does not delay the loop's
+// reaction to the value it waits for (the wall-clock timeout is checked every round).
+constexpr uint32_t kErrorEvery = 64;
+
 // Spin until pred() holds; false on this workgroup's abort, the grid error flag or a timeout
 // (which raises both). Only lane 0 of the wave polls (the other lanes would only add LDS traffic
 // that the workers' activation reads queue behind); the outcome is broadcast to the wave.
@@ -131,7 +136,7 @@ __device__ __forceinline__ bool spin_until(Ctl& c, const StackArgs& a, Pred pred
   int ok = 1;
   if (__lane_id() == 0 && !pred()) {
     const uint64_t t0 = wall_clock64();
-    for (;;) {
+    for (uint32_t it = 1;; ++it) {
       __builtin_amdgcn_s_sleep(2);
       if (pred()) break;
       if (lds_ld(&c.abort) != 0u) {
@@ -139,7 +144,8 @@ __device__ __forceinline__ bool spin_until(Ctl& c, const StackArgs& a, Pred pred
         break;
       }
       if (wall_clock64() - t0 > a.timeout_ticks ||
-          __hip_atomic_load(a.sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+          (it % kErrorEvery == 0 &&
+           __hip_atomic_load(a.sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
         raise_abort(c, a.sync);
         ok = 0;
         break;
@@ -244,7 +250,8 @@ __device__ __forceinline__ bool poll_range(Ctl& c, const StackArgs& a, const uin
       if (!stale) break;
       if (round == 0) {
         t0 = wall_clock64();
-      } else if (wall_clock64() - t0 > a.timeout_ticks || lds_ld(&c.abort) != 0u || grid_error(a)) {
+      } else if (wall_clock64() - t0 > a.timeout_ticks || lds_ld(&c.abort) != 0u ||
+                 ((uint32_t)round % kErrorEvery == 0 && grid_error(a))) {
         raise_abort(c, a.sync);
         return false;
       }
@@ -282,7 +289,8 @@ __device__ __forceinline__ bool poll_lane(Ctl& c, const StackArgs& a, rsrc_t r, 
     if (!stale) return true;
     if (round == 0) {
       t0 = wall_clock64();
-    } else if (wall_clock64() - t0 > a.timeout_ticks || lds_ld(&c.abort) != 0u || grid_error(a)) {
+    } else if (wall_clock64() - t0 > a.timeout_ticks || lds_ld(&c.abort) != 0u ||
+               ((uint32_t)round % kErrorEvery == 0 && grid_error(a))) {
       raise_abort(c, a.sync);
       return false;
     }
