@@ -115,7 +115,7 @@ def build_stack(wl, torch, tg, syn, layers):
     act = torch.float32 if wl.act_dtype == "f32" else torch.float16
     cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
                          dtype={"f32": "fp32", "f16": "fp16", "i8": "int8"}[wl.weight_dtype],
-                         quantization_setting=(wl.group, False) if wl.weight_dtype == "i8" else None)
+                         quant_group=wl.group if wl.weight_dtype == "i8" else None)
     stack, kvs = [], []
     lens = torch.zeros((layers, wl.batch), dtype=torch.int32, device=dev)
     for l in range(layers):
@@ -366,10 +366,12 @@ def main():
             e1.record(stream)
         torch.cuda.synchronize()
         st.check()
+        groups = st.groups
+        st.close()  # release the handle now, not during interpreter shutdown
         ms = e0.elapsed_time(e1) / args.steps
         per_step = [a.elapsed_time(b) for a, b in zip(starts, ends)]
         kernel_ms = sum(per_step) / args.steps
-        launch_desc = f"persistent stack kernel, {st.groups} workgroups"
+        launch_desc = f"persistent stack kernel, {groups} workgroups"
     else:
         def step():
             lens.fill_(wl.past)

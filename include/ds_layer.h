@@ -32,7 +32,8 @@
  *    it. Weights and caches must outlive every call that uses them. A ds_layer_t is a small host
  *    object owned by the library, released by ds_layer_destroy.
  *  - Matrices are [N][K] row-major (K contiguous): W_qkv [3H][H], W_o [H][H], W_ff1 [F][H],
- *    W_ff2 [H][F]. int8 scales are fp16 [N][K/quant_group]: element (n,k) = q[n][k] * s[n][k/group].
+ *    W_ff2 [H][F]. int8 scales are fp16 [N][K/group]: element (n,k) = q[n][k] * s[n][k/group], with
+ *    group = quant_group for W_qkv and W_o and the MLP group for W_ff1 and W_ff2.
  *    Every weight, scale, bias, LayerNorm, cache and activation pointer must be 16-byte aligned.
  *  - Enqueueing calls put their work on `stream` (a hipStream_t; NULL is the null stream) and
  *    return without waiting. They allocate nothing and never synchronize, so they can be captured
@@ -75,7 +76,14 @@ typedef struct {
   int32_t weight_dtype;       /* ds_dtype of W_qkv, W_o, W_ff1, W_ff2                           */
   int32_t act_dtype;          /* ds_dtype of x, y, the caches, biases and LayerNorm parameters  */
                               /* supported pairs: (F32,F32) (F16,F16) (I8,F16)                  */
-  int32_t quant_group;        /* 64 when weight_dtype is DS_I8, else 0                          */
+  int32_t quant_group;        /* int8: elements per scale along the reduction dimension of      */
+                              /* W_qkv and W_o (and of W_ff1, W_ff2 when quant_group_mlp is 0);  */
+                              /* 0 for other weight dtypes                                       */
+  int32_t quant_group_mlp;    /* int8: elements per scale of W_ff1 and W_ff2 (0: quant_group)    */
+                              /* ([KP] section 五 5.2: quantize_groups and mlp_extra_grouping,   */
+                              /* finer groups for the MLP matrices); 0 for other weight dtypes.  */
+                              /* Supported: quant_group 64 with quant_group_mlp 0 or 64; other   */
+                              /* int8 group sizes return DS_ERR_UNSUPPORTED.                     */
   float ln_eps;               /* LayerNorm epsilon, > 0 (1e-5 by default)                       */
   int32_t gelu_tanh;          /* 0: u*Phi(u) with erf (default); 1: tanh approximation          */
   int32_t triangular_masking; /* 1 (default): a row at position p sees keys 0..p; 0: all keys   */
@@ -175,20 +183,31 @@ int ds_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
  * layer in turn -- as one cooperative launch whose workgroups all stay resident; at the phase
  * boundaries of [KP] section 三 3.1 each workgroup waits for exactly the values of the previous
  * phase it reads (stored with tags naming launch, layer and phase). The cache structs are copied:
- * their k, v, d_len and h_len pointers must stay valid for the stack's life. The library allocates
- * two small device buffers per stack (layer table; launch counter, exit count and error flag),
- * freed by ds_stack_destroy.
- * Requirements: max_batch 1..4; hidden <= 8192; hidden and ffn multiples of 256 (fp32 weights),
- * 512 (fp16) or 1024 (int8); each cache under 2 GiB. Errors: DS_ERR_NULL, DS_ERR_SHAPE,
- * DS_ERR_ALIGN, DS_ERR_UNSUPPORTED, DS_ERR_HIP.
+ * their k, v, d_len and h_len pointers must stay valid for the stack's life.
+ * The stack's persistent device state (the layer table, a launch counter, an exit count and an
+ * error flag) lives in a caller-owned device buffer of ds_stack_state_bytes(n_layers) bytes,
+ * 16-byte aligned, which ds_stack_create initializes (synchronously) and which must stay valid and
+ * untouched for the stack's life; the library allocates no device memory.
+ * Requirements: 1 <= n_layers <= 511; max_batch 1..4; hidden <= 8192; hidden and ffn multiples of
+ * 256 (fp32 weights), 512 (fp16) or 1024 (int8); each cache under 2 GiB. Errors: DS_ERR_NULL,
+ * DS_ERR_SHAPE, DS_ERR_ALIGN, DS_ERR_UNSUPPORTED (n_layers above 511 included), DS_ERR_WORKSPACE
+ * (state buffer too small), DS_ERR_HIP.
  * ------------------------------------------------------------------------------------------- */
 typedef struct ds_stack ds_stack_t;
 
+/* Bytes of the caller-owned state buffer of a stack of n_layers layers (0 if n_layers < 1). */
+size_t ds_stack_state_bytes(int32_t n_layers);
+
 int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, int32_t n_layers,
-                    int32_t max_batch, ds_stack_t** out);
+                    int32_t max_batch, void* state, size_t state_bytes, ds_stack_t** out);
+/* Releases the host handle (no device memory is freed; the state buffer is the caller's). */
 int ds_stack_destroy(ds_stack_t* stack);
 
-/* Workspace bytes for a step of `batch` sequences (0 if batch is outside 1..max_batch). */
+/* Workspace bytes for a step of `batch` sequences (0 if batch is outside 1..max_batch). The
+ * workspace holds the tagged values of one launch; the library clears it (with a fill kernel on
+ * the call's stream) the first time a stack uses it after another stack did, and again after every
+ * 2^19 - 64 launches of one stack, so that no stale value can carry a current tag. Between calls
+ * nothing but the stacks may write it. */
 size_t ds_stack_workspace_bytes(const ds_stack_t* stack, int32_t batch);
 
 /* Number of workgroups the persistent launch uses (all co-resident on the device). */
@@ -202,7 +221,10 @@ int ds_stack_forward_decode(ds_stack_t* stack, const void* x, void* y, int32_t b
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronizes the device and reports whether a step of this stack hit its wait timeout
- * (DS_ERR_HIP, with the counters reset so the stack can run again) or not (DS_OK). */
+ * (DS_ERR_HIP) or not (DS_OK). After a timeout every later launch of the stack leaves at once,
+ * before any store, until this call resets the counters; it also copies every layer's device
+ * lengths back into the host mirrors (h_len), which were advanced at enqueue time for steps that
+ * then did not run, so the stack can run again from the lengths the device holds. */
 int ds_stack_check(ds_stack_t* stack);
 
 /* Limit of each wait of the persistent kernel (default 2 s); on expiry the kernel raises an

@@ -35,6 +35,9 @@ def lib():
         L.ora_attend.argtypes = [_D, _D, _D, C.c_int, C.c_int, _D]
         L.ora_layer_forward.argtypes = [C.c_void_p, C.c_void_p, _D, _D, C.c_int,
                                         C.POINTER(C.c_int), _D, _D, C.c_int, C.c_int, C.c_void_p]
+        L.ora_lm_head.argtypes = [_D, C.c_int, _D, _D, C.c_double, _D, C.c_int, _D]
+        L.ora_argmax.argtypes = [_D, C.c_int]
+        L.ora_argmax.restype = C.c_int
         L.ora_fp16_from_double.argtypes = [C.c_double]
         L.ora_fp16_from_double.restype = C.c_uint16
         L.ora_fp16_to_double.argtypes = [C.c_uint16]
@@ -92,6 +95,24 @@ def attend(q, keys, vals):
     out = np.empty(d)
     lib().ora_attend(_p(q), _p(keys), _p(vals), n, d, _p(out))
     return out
+
+
+# ---------------------------------------------------------------- the ends of a generation step
+def lm_head(y, g, b, w_vocab, eps=1e-5):
+    """logits [V] = W_vocab LN(y; g, b) for one row y [H]."""
+    y, g, b, w = _f64(y), _f64(g), _f64(b), _f64(w_vocab)
+    V, H = w.shape
+    out = np.empty(V)
+    lib().ora_lm_head(_p(y), H, _p(g), _p(b), eps, _p(w), V, _p(out))
+    return out
+
+
+def argmax(v):
+    """Greedy choice over a 1-D array: first index of the largest value."""
+    v = _f64(v)
+    if v.ndim != 1 or v.size < 1:
+        raise ValueError("argmax needs a non-empty 1-D array")
+    return int(lib().ora_argmax(_p(v), v.size))
 
 
 # ---------------------------------------------------------------- fp16 and int8

@@ -165,6 +165,24 @@ int ora_layer_forward(const ora_desc* dsc, const ora_weights* w, double* k_cache
   return 0;
 }
 
+/* The end of a generation step ([KP] section 二, the GPT-Neo-2.7B text-generation example): the
+ * final LayerNorm of the last layer's output, then the LM head, logits[v] = sum_k w[v][k] h[k]. */
+void ora_lm_head(const double* y, int H, const double* g, const double* b, double eps,
+                 const double* w_vocab, int V, double* logits) {
+  double* h = (double*)malloc(sizeof(double) * (size_t)H);
+  ora_layernorm(y, H, g, b, eps, h);
+  ora_linear(w_vocab, NULL, h, V, H, logits);
+  free(h);
+}
+
+/* Greedy decoding: scan left to right and keep the first position holding the largest value. */
+int ora_argmax(const double* v, int n) {
+  int best = 0;
+  for (int i = 1; i < n; ++i)
+    if (v[i] > v[best]) best = i;
+  return best;
+}
+
 /* IEEE 754 binary16 from a double, rounding to nearest with ties to even.
  * Normal numbers have an 11-bit significand and exponents -14..15; below 2^-14 the spacing is
  * the fixed 2^-24 (subnormals); a rounded magnitude of 2^16 or more becomes infinity. */

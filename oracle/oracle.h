@@ -73,6 +73,15 @@ int ora_layer_forward(const ora_desc* desc, const ora_weights* w, double* k_cach
                       int cap, int* lens, const double* x, double* y, int batch, int ntok,
                       ora_stages* stages);
 
+/* ---- the ends of a generation step (the text-generation example of [KP] section 二) ----
+ * After the last layer: a final LayerNorm and the LM head, logits = W_vocab LN(y; g, b) with
+ * w_vocab [V][H] (no bias), then greedy decoding. */
+void ora_lm_head(const double* y, int H, const double* g, const double* b, double eps,
+                 const double* w_vocab, int V, double* logits);
+/* Greedy choice: the index of the largest of n values; among equal largest values, the smallest
+ * index. n >= 1; the values are finite. */
+int  ora_argmax(const double* v, int n);
+
 /* ---- IEEE binary16 ---- */
 uint16_t ora_fp16_from_double(double v); /* round to nearest, ties to even; overflow -> inf */
 double   ora_fp16_to_double(uint16_t h);

@@ -6,8 +6,11 @@ inputs from here.
 
 Recipe (the pages' workloads are trained GPT-2 / GPT-Neo / Turing-NLG / GPT-3-like models whose
 weights are not available; seeded draws of the same shapes stand in for them):
-  weights ~ N(0, 0.02), biases ~ N(0, 0.01), LayerNorm gamma = 1, beta = 0,
-  activations x ~ N(0, 1), past K/V cache rows ~ N(0, 1).
+  weights ~ N(0, 0.02), biases ~ N(0, bias_std) (0.01 by default), LayerNorm gamma = 1 and
+  beta = 0 by default, activations x ~ N(0, 1), past K/V cache rows ~ N(0, 1).
+Parity cases that must see the LayerNorm affine map set ln_std > 0: gamma ~ 1 + N(0, ln_std) and
+beta ~ N(0, ln_std), drawn per layer (the seed includes the layer), so that a kernel which ignores
+gamma/beta, or reads another layer's or the other LayerNorm's, gives a visibly different result.
 Draws are float32 from torch's generator on the requested device, seeded from
 (config id, layer, tensor id) through numpy's SeedSequence; the caller rounds them to the
 target dtype (round to nearest even). A given key always yields the same tensor on a given
@@ -42,6 +45,8 @@ class Workload:
     past: int          # filled cache rows before the step (decode) or P0 (prefill)
     seq: int = 1       # new rows per sequence: 1 for decode, S for prefill
     group: int = 0     # int8 group size along the reduction dimension
+    ln_std: float = 0.0     # > 0: LayerNorm gamma ~ 1 + N(0, ln_std), beta ~ N(0, ln_std)
+    bias_std: float = 0.01  # biases ~ N(0, bias_std)
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -81,18 +86,29 @@ def normal(shape, std: float, cfg_id: int, layer: int, tensor_id: int, device="c
 
 def layer_weights_f32(wl: Workload, layer: int, device="cpu") -> dict:
     """The twelve float32 parameter tensors of one layer (weights [N,K] row-major)."""
-    H, F, c = wl.hidden, wl.ffn, wl.cfg_id
+    H, F, c, bs = wl.hidden, wl.ffn, wl.cfg_id, wl.bias_std
+
+    def gamma(tid):
+        if wl.ln_std <= 0:
+            return torch.ones(H, device=device)
+        return normal((H,), wl.ln_std, c, layer, tid, device).add_(1.0)
+
+    def beta(tid):
+        if wl.ln_std <= 0:
+            return torch.zeros(H, device=device)
+        return normal((H,), wl.ln_std, c, layer, tid, device)
+
     return {
-        "ln1_g": torch.ones(H, device=device), "ln1_b": torch.zeros(H, device=device),
+        "ln1_g": gamma(LN1_G), "ln1_b": beta(LN1_B),
         "w_qkv": normal((3 * H, H), 0.02, c, layer, W_QKV, device),
-        "b_qkv": normal((3 * H,), 0.01, c, layer, B_QKV, device),
+        "b_qkv": normal((3 * H,), bs, c, layer, B_QKV, device),
         "w_o": normal((H, H), 0.02, c, layer, W_O, device),
-        "b_o": normal((H,), 0.01, c, layer, B_O, device),
-        "ln2_g": torch.ones(H, device=device), "ln2_b": torch.zeros(H, device=device),
+        "b_o": normal((H,), bs, c, layer, B_O, device),
+        "ln2_g": gamma(LN2_G), "ln2_b": beta(LN2_B),
         "w_ff1": normal((F, H), 0.02, c, layer, W_FF1, device),
-        "b_ff1": normal((F,), 0.01, c, layer, B_FF1, device),
+        "b_ff1": normal((F,), bs, c, layer, B_FF1, device),
         "w_ff2": normal((H, F), 0.02, c, layer, W_FF2, device),
-        "b_ff2": normal((H,), 0.01, c, layer, B_FF2, device),
+        "b_ff2": normal((H,), bs, c, layer, B_FF2, device),
     }
 
 

@@ -29,7 +29,7 @@ def gpu_layer_and_oracle_weights(wl: syn.Workload, layer: int, device="cuda", ch
     act = TORCH[wl.act_dtype]
     cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
                          dtype={"f32": "fp32", "f16": "fp16", "i8": "int8"}[wl.weight_dtype],
-                         quantization_setting=(wl.group, False) if wl.weight_dtype == "i8" else None, **cfg_kw)
+                         quant_group=wl.group if wl.weight_dtype == "i8" else None, **cfg_kw)
     gw, ow = {}, {}
     for name, t in w32.items():
         if name.startswith("w_"):

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def _desc(**kw):
     d = dict(hidden=256, heads=2, head_dim=128, ffn=512, weight_dtype=1, act_dtype=1, quant_group=0,
-             ln_eps=1e-5, gelu_tanh=0, triangular_masking=1)
+             quant_group_mlp=0, ln_eps=1e-5, gelu_tanh=0, triangular_masking=1)
     d.update(kw)
     return _lib.LayerDescC(**d)
 
@@ -60,8 +60,13 @@ def _create(desc, w):
     (dict(ffn=100), _lib.DS_ERR_SHAPE),
     (dict(weight_dtype=2, act_dtype=2), _lib.DS_ERR_DTYPE),
     (dict(weight_dtype=0, act_dtype=1), _lib.DS_ERR_DTYPE),
-    (dict(weight_dtype=2, act_dtype=1, quant_group=24), _lib.DS_ERR_DTYPE),
     (dict(quant_group=64), _lib.DS_ERR_DTYPE),
+    (dict(quant_group_mlp=32), _lib.DS_ERR_DTYPE),
+    # int8 group sizes other than 64 have no GPU-tested kernels: refused, not silently mishandled
+    (dict(weight_dtype=2, act_dtype=1, quant_group=24), _lib.DS_ERR_UNSUPPORTED),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=32), _lib.DS_ERR_UNSUPPORTED),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=128), _lib.DS_ERR_UNSUPPORTED),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=64, quant_group_mlp=32), _lib.DS_ERR_UNSUPPORTED),
     (dict(ln_eps=0.0), _lib.DS_ERR_SHAPE),
     (dict(triangular_masking=2), _lib.DS_ERR_SHAPE),
 ])
@@ -77,6 +82,9 @@ def test_create_rejects_null_and_misaligned_pointers():
     assert _create(_desc(), _weights(w_ff1=FAKE + 8))[0] == _lib.DS_ERR_ALIGN
     assert _create(_desc(), _weights(s_o=FAKE))[0] == _lib.DS_ERR_DTYPE       # scales on fp16 weights
     assert _create(_desc(weight_dtype=2, quant_group=64), _weights(int8=True, s_ff2=None))[0] == _lib.DS_ERR_NULL
+    rc, h = _create(_desc(weight_dtype=2, quant_group=64, quant_group_mlp=64), _weights(int8=True))
+    assert rc == 0, _lib.lib().ds_last_error()
+    _lib.lib().ds_layer_destroy(h)
     h = C.c_void_p()
     assert _lib.lib().ds_layer_create(None, C.byref(_weights()), C.byref(h)) == _lib.DS_ERR_NULL
 
@@ -134,10 +142,60 @@ def test_config_merge_rules():
     cfg = tg.make_config({"hidden": 256, "heads": 2, "ffn": 512}, dtype="int8")
     assert cfg.dtype == _lib.DS_I8 and cfg.quant_group == 64 and cfg.triangular_masking and cfg.max_out_tokens == 1024
     assert tg.make_config('{"hidden": 256, "heads": 4, "ffn": 512}').dtype == _lib.DS_F16   # fp16 default
-    assert tg.make_config(hidden=256, heads=2, ffn=512, dtype="int8", quantization_setting=(32, True)).quant_group == 32
+    assert tg.make_config(hidden=256, heads=2, ffn=512, dtype="int8", quant_group=64).quant_group == 64
     with pytest.raises(ValueError, match="Conflicting"):
         tg.make_config({"hidden": 256, "heads": 2, "ffn": 512, "dtype": "fp16"}, dtype="fp32")
     with pytest.raises(ValueError):
         tg.make_config(hidden=256, heads=2, ffn=512, quant_group=64)          # group on fp16 weights
     with pytest.raises(ValueError):
         tg.make_config(hidden=256, heads=2, ffn=512, bogus=1)
+
+
+def test_quantization_setting_is_a_group_count():
+    """quantization_setting=(quantize_groups, mlp_extra_grouping): quantize_groups is a number of
+    groups per hidden-width weight row, so the group size is hidden / quantize_groups."""
+    cfg = tg.make_config(hidden=5120, heads=40, ffn=20480, dtype="int8", quantization_setting=(80, False))
+    assert cfg.quant_group == 64 and cfg.quant_group_mlp == 0
+    assert tg.make_config(hidden=2560, heads=20, ffn=10240, dtype="int8", quantization_setting=40).quant_group == 64
+    with pytest.raises(ValueError, match="dividing hidden"):
+        tg.make_config(hidden=2560, heads=20, ffn=10240, dtype="int8", quantization_setting=(48, False))
+    with pytest.raises(ValueError, match="disagree"):
+        tg.make_config(hidden=2560, heads=20, ffn=10240, dtype="int8", quantization_setting=(40, False), quant_group=32)
+    # extra MLP grouping halves the MLP group size; refused until the kernels support it
+    with pytest.raises(NotImplementedError):
+        tg.make_config(hidden=5120, heads=40, ffn=20480, dtype="int8", quantization_setting=(80, True))
+    with pytest.raises(ValueError, match="int8"):
+        tg.make_config(hidden=256, heads=2, ffn=512, dtype="fp16", quantization_setting=(4, False))
+
+
+def test_stack_create_rejects_before_device_work():
+    """ds_stack_create refuses bad layer counts and state buffers before any HIP call."""
+    L, h = _lib.lib(), _layer()
+    hl = np.zeros(1, dtype=np.int32)
+    n = 600
+    handles = (C.c_void_p * n)(*([h.value] * n))
+    caches = (_lib.KVCacheC * n)(*[_lib.KVCacheC(FAKE, FAKE, FAKE, hl.ctypes.data_as(C.POINTER(C.c_int32)), 1, 64)
+                                   for _ in range(n)])
+    out = C.c_void_p()
+    need = L.ds_stack_state_bytes(2)
+    assert need > 0 and L.ds_stack_state_bytes(0) == 0
+    # the tag packs layer * 8 + phase into 12 bits: 511 layers at most
+    assert L.ds_stack_create(handles, caches, 512, 1, C.c_void_p(FAKE), 1 << 30, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
+    assert L.ds_stack_create(handles, caches, n, 1, C.c_void_p(FAKE), 1 << 30, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
+    assert "511" in L.ds_last_error().decode()
+    assert L.ds_stack_create(handles, caches, 0, 1, C.c_void_p(FAKE), 1 << 30, C.byref(out)) == _lib.DS_ERR_SHAPE
+    assert L.ds_stack_create(handles, caches, 2, 1, None, need, C.byref(out)) == _lib.DS_ERR_NULL
+    assert L.ds_stack_create(handles, caches, 2, 1, C.c_void_p(FAKE + 8), need, C.byref(out)) == _lib.DS_ERR_ALIGN
+    assert L.ds_stack_create(handles, caches, 2, 1, C.c_void_p(FAKE), need - 1, C.byref(out)) == _lib.DS_ERR_WORKSPACE
+    assert L.ds_stack_create(handles, caches, 2, 5, C.c_void_p(FAKE), need, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
+    assert not out.value
+    L.ds_layer_destroy(h)
+
+
+def test_layer_close_is_idempotent():
+    cfg = tg.make_config(hidden=256, heads=2, ffn=512, dtype="fp16")
+    rc, h = _create(_desc(), _weights())
+    assert rc == 0
+    _lib.lib().ds_layer_destroy(h)
+    assert _lib.lib().ds_layer_destroy(None) == 0
+    assert cfg.quant_group_mlp == 0

@@ -30,7 +30,7 @@ _DT = {"f16": "fp16", "i8": "int8", "f32": "fp32"}
 
 def _config(wl):
     return tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn, dtype=_DT[wl.weight_dtype],
-                          quantization_setting=(wl.group, False) if wl.weight_dtype == "i8" else None)
+                          quant_group=wl.group if wl.weight_dtype == "i8" else None)
 
 
 def _gpu_layer(wl, layer, cfg):
@@ -88,6 +88,7 @@ def test_c2_full_stack_32_layers_matches_oracle():
     x = syn.normal((1, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").half()
     y = st.decode(x)
     st.check()
+    st.close()
     desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
     h = x.double().cpu().numpy()[:, None, :]
     for l in range(wl.layers):
@@ -123,9 +124,9 @@ def test_13b_full_shape_layer_matches_oracle(name):
     ok, ov = _oracle_cache(kv, wl.past)
     x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").half()
     if use_stack:
-        st = tg.Stack([gl], [kv], max_batch=wl.batch)
-        y = st.decode(x)
-        st.check()
+        with tg.Stack([gl], [kv], max_batch=wl.batch) as st:
+            y = st.decode(x)
+            st.check()
     else:
         y = gl.decode(kv, x)
     torch.cuda.synchronize()
@@ -175,3 +176,68 @@ def test_c5_full_shape_prefill_layer_sampled_rows():
         err = rel_l2(y[b, :rows].double().cpu().numpy(), yo)
         print(f"  sequence {b}, rows 0..{rows - 1}: rel L2 {err:.3e}", flush=True)
         assert err <= TOL["f16"], (b, err)
+
+
+def test_c5_full_shape_prefill_last_rows_match_oracle():
+    """The last 16 prompt rows of one sequence at the full prefill shape (4 x 512, causal): rows
+    496..511 attend over 497..512 keys spread over all eight 64-key tiles, and sit in the last row
+    tile of every GEMM. The oracle computes the K/V rows 0..495 of that sequence (LN1 and the K, V
+    rows of the QKV projection), then the layer for rows 496..511 on top of them."""
+    wl = syn.WORKLOADS["c5"]
+    cfg = _config(wl)
+    gl = _gpu_layer(wl, 0, cfg)
+    kv = tg.KVCache(wl.batch, wl.heads, wl.capacity, wl.head_dim, torch.float16, "cuda")
+    x = syn.stack_input_f32(wl, "cuda").half().contiguous()
+    y = gl.prefill(kv, x)
+    torch.cuda.synchronize()
+    ow = _oracle_weights(gl, wl)
+    H, nh, d, S = wl.hidden, wl.heads, wl.head_dim, wl.seq
+    b, t0 = 2, S - 16
+    xd = x[b].double().cpu().numpy()
+    ok = np.zeros((1, nh, wl.capacity, d))
+    ov = np.zeros_like(ok)
+    for t in range(t0):
+        h = oracle.layernorm(xd[t], ow["ln1_g"], ow["ln1_b"])
+        z = oracle.linear(ow["w_qkv"][H:], ow["b_qkv"][H:], h)
+        ok[0, :, t] = z[:H].reshape(nh, d)
+        ov[0, :, t] = z[H:].reshape(nh, d)
+    lens = np.full(1, t0, dtype=np.int32)
+    desc = oracle.Desc(H, nh, d, wl.ffn)
+    yo = oracle.layer_forward(desc, ow, ok, ov, lens, xd[None, t0:])[0]
+    yg = y[b, t0:].double().cpu().numpy()
+    err, err_d = rel_l2(yg, yo), rel_l2(yg - xd[t0:], yo - xd[t0:])
+    print(f"  sequence {b}, rows {t0}..{S - 1}: rel L2 {err:.3e}, of y - x {err_d:.3e}", flush=True)
+    assert err <= TOL["f16"] and err_d <= TOL["f16"], (err, err_d)
+    kg = kv.k[b, :, t0:S].double().cpu().numpy()
+    assert rel_l2(kg, ok[0, :, t0:S]) <= TOL["f16"]
+
+
+def test_c5_full_shape_gemm_configurations_agree(monkeypatch):
+    """At the full prefill shape the automatic choice runs QKV on the 256 x 256 configuration (2),
+    O and FF2 on 1 and FF1 on 0. Forcing configuration 0 on every product must give the same outputs
+    on every row (GPU against GPU, within the fp16 bar), so configurations 1 and 2 are checked on all
+    rows, not only on the rows the oracle samples."""
+    wl = syn.WORKLOADS["c5"]
+    cfg = _config(wl)
+    x = syn.stack_input_f32(wl, "cuda").half().contiguous()
+    outs, caches = [], []
+    for forced in (None, "0"):
+        if forced is None:
+            monkeypatch.delenv("DS_GEMM_CONFIG", raising=False)
+        else:
+            monkeypatch.setenv("DS_GEMM_CONFIG", forced)
+        gl = _gpu_layer(wl, 0, cfg)
+        kv = tg.KVCache(wl.batch, wl.heads, wl.capacity, wl.head_dim, torch.float16, "cuda")
+        outs.append(gl.prefill(kv, x))
+        caches.append(kv)
+        torch.cuda.synchronize()
+    a, b = outs[0].double().cpu().numpy(), outs[1].double().cpu().numpy()
+    xd = x.double().cpu().numpy()
+    err = rel_l2(a - xd, b - xd)
+    print(f"  automatic vs configuration 0, all rows: rel L2 of y - x {err:.3e}", flush=True)
+    assert err <= 1e-3, err
+    for b_ in range(wl.batch):
+        e = rel_l2((outs[0][b_] - x[b_]).double().cpu().numpy(), (outs[1][b_] - x[b_]).double().cpu().numpy())
+        assert e <= 1e-3, (b_, e)
+    assert torch.equal(caches[0].k, caches[1].k) or rel_l2(caches[0].k.double().cpu().numpy(),
+                                                           caches[1].k.double().cpu().numpy()) <= 1e-3

@@ -37,6 +37,9 @@ CASES = {
 }
 
 
+AFFINE = dict(ln_std=0.2, bias_std=0.1)
+
+
 def _prefill_case(wl, S, P0, **cfg_kw):
     wl = dataclasses.replace(wl, past=P0, seq=S)
     cap = ((P0 + S + 1 + 63) // 64) * 64
@@ -46,14 +49,51 @@ def _prefill_case(wl, S, P0, **cfg_kw):
     return wl, gl, ow, kv, ok, ov, lens, x
 
 
+# per-layer LayerNorm affine and larger biases, with both GeLU forms
+CASES.update({
+    "d128-b2-s100-affine-tanh": (_wl(cfg_id=209, **AFFINE), 100, 0),
+    "d64-b3-s70-p33-affine": (_wl(hidden=320, heads=5, head_dim=64, ffn=640, batch=3, cfg_id=210, **AFFINE), 70, 33),
+})
+TANH = {"d128-b2-s100-affine-tanh"}
+
+
+def _check_prefill(name, wl, S, P0, tanh):
+    wl, gl, ow, kv, ok, ov, lens, x = _prefill_case(wl, S, P0, gelu_tanh=tanh)
+    print(f"case {name}: B={wl.batch} S={S} P0={P0} H={wl.hidden} F={wl.ffn} d={wl.head_dim} tanh={tanh}", flush=True)
+    y = gl.prefill(kv, x)
+    torch.cuda.synchronize()
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn, gelu_tanh=tanh)
+    yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy())
+    yd, xd = y.double().cpu().numpy(), x.double().cpu().numpy()
+    err, err_d = rel_l2(yd, yo), rel_l2(yd - xd, yo - xd)
+    print(f"  rel L2 {err:.3e}, of y - x {err_d:.3e}", flush=True)
+    assert err <= TOL["f16"] and err_d <= TOL["f16"], (err, err_d)
+    n = P0 + S
+    assert rel_l2(kv.k.double().cpu().numpy()[:, :, :n], ok[:, :, :n]) <= TOL["f16"]
+    assert rel_l2(kv.v.double().cpu().numpy()[:, :, :n], ov[:, :, :n]) <= TOL["f16"]
+    assert kv.lengths() == [n] * wl.batch
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("name", ["d128-b2-s256", "d64-b3-s70-p33-affine", "d128-b2-s100-affine-tanh"])
+def test_prefill_each_gemm_configuration_matches_oracle(name, cfg, monkeypatch):
+    """Every GEMM tile configuration (0: 128 x 160 two-stage, 1: 128 x 160 three-stage with two wave
+    groups, 2: 256 x 256 eight waves) forced on all four products of small shapes, whose automatic
+    choice would not take it, against the oracle; ragged row and column tiles included."""
+    monkeypatch.setenv("DS_GEMM_CONFIG", str(cfg))
+    wl, S, P0 = CASES[name]
+    _check_prefill(f"{name} config {cfg}", wl, S, P0, name in TANH)
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_prefill_mfma_matches_oracle(name):
     wl, S, P0 = CASES[name]
-    wl, gl, ow, kv, ok, ov, lens, x = _prefill_case(wl, S, P0)
+    tanh = name in TANH
+    wl, gl, ow, kv, ok, ov, lens, x = _prefill_case(wl, S, P0, gelu_tanh=tanh)
     print(f"case {name}: B={wl.batch} S={S} P0={P0} H={wl.hidden} F={wl.ffn} d={wl.head_dim}", flush=True)
     y = gl.prefill(kv, x)
     torch.cuda.synchronize()
-    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn, gelu_tanh=tanh)
     yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy())
     err = rel_l2(y.double().cpu().numpy(), yo)
     assert err <= TOL["f16"], err

@@ -46,6 +46,7 @@ class LayerConfig:
     ffn: int
     dtype: int = DS_F16            # weight dtype; activations are fp32 for fp32 weights, else fp16
     quant_group: int = 0           # int8 only: elements per scale along the reduction dimension
+    quant_group_mlp: int = 0       # int8 only: elements per scale of the MLP matrices (0: quant_group)
     ln_eps: float = 1e-5
     gelu_tanh: bool = False
     triangular_masking: bool = True
@@ -65,11 +66,11 @@ class LayerConfig:
 
     def c_desc(self) -> _lib.LayerDescC:
         return _lib.LayerDescC(self.hidden, self.heads, self.head_dim, self.ffn, self.dtype,
-                               self.act_dtype, self.quant_group, self.ln_eps, int(self.gelu_tanh),
-                               int(self.triangular_masking))
+                               self.act_dtype, self.quant_group, self.quant_group_mlp, self.ln_eps,
+                               int(self.gelu_tanh), int(self.triangular_masking))
 
 
-_CONFIG_KEYS = {"hidden", "heads", "ffn", "dtype", "quant_group", "ln_eps", "gelu_tanh",
+_CONFIG_KEYS = {"hidden", "heads", "ffn", "dtype", "quant_group", "quant_group_mlp", "ln_eps", "gelu_tanh",
                 "triangular_masking", "max_out_tokens", "quantization_setting"}
 
 
@@ -77,8 +78,16 @@ def make_config(config=None, **kwargs) -> LayerConfig:
     """Merge a config (dict, JSON text or JSON file path) with keyword arguments.
 
     Keyword arguments add to the config; a key present in both with different values raises
-    ValueError. `quantization_setting` may give the int8 group size as an int or as a
-    (group, mlp_extra_grouping) pair; with int8 and no setting the group is 64.
+    ValueError.
+
+    int8 grouping. `quant_group` gives the group size directly (elements per fp16 scale along the
+    reduction dimension; 64 when int8 is chosen without a setting). `quantization_setting` follows
+    the page "DeepSpeed Inference 内核优化深度解析", section 五 5.2: (quantize_groups,
+    mlp_extra_grouping), where quantize_groups is a number of groups. Read here as the number of
+    groups each weight row of the hidden-width reduction (K = hidden) is cut into, so the group size
+    is hidden / quantize_groups, which must divide evenly; mlp_extra_grouping=True asks for twice as
+    many groups (half the group size) in the MLP matrices. A bare int is taken the same way as
+    quantize_groups. Extra MLP grouping raises NotImplementedError until the library supports it.
     """
     base = {}
     if config is not None:
@@ -95,18 +104,34 @@ def make_config(config=None, **kwargs) -> LayerConfig:
     dt = _dtype_code(base.pop("dtype", "fp16"))
     qs = base.pop("quantization_setting", None)
     group = base.pop("quant_group", None)
+    group_mlp = base.pop("quant_group_mlp", None)
     if qs is not None:
-        g = qs[0] if isinstance(qs, (tuple, list)) else qs
-        if group is not None and group != g:
-            raise ValueError("quant_group and quantization_setting disagree")
+        count, extra = (qs[0], bool(qs[1]) if len(qs) > 1 else False) if isinstance(qs, (tuple, list)) else (qs, False)
+        count = int(count)
+        hidden = int(base.get("hidden", 0))
+        if count < 1 or hidden < 1 or hidden % count:
+            raise ValueError(f"quantize_groups {count} must be a positive number of groups dividing hidden {hidden}")
+        g = hidden // count
+        if group is not None and int(group) != g:
+            raise ValueError(f"quant_group {group} and quantization_setting ({count} groups -> {g}) disagree")
         group = g
+        if extra:
+            if g % 2:
+                raise ValueError(f"mlp_extra_grouping needs an even group size, got {g}")
+            if group_mlp is not None and int(group_mlp) != g // 2:
+                raise ValueError("quant_group_mlp and mlp_extra_grouping disagree")
+            group_mlp = g // 2
     if dt == DS_I8:
         group = 64 if group is None else int(group)
-    elif group not in (None, 0):
-        raise ValueError("quant_group applies to int8 weights only")
+        group_mlp = 0 if group_mlp is None or int(group_mlp) == group else int(group_mlp)
+        if group_mlp:
+            raise NotImplementedError(f"int8 MLP groups of {group_mlp} (extra MLP grouping) are not supported by "
+                                      f"this build; the MLP matrices use the attention group size {group}")
+    elif group not in (None, 0) or group_mlp not in (None, 0):
+        raise ValueError("quant_group and quantization_setting apply to int8 weights only")
     else:
-        group = 0
-    return LayerConfig(dtype=dt, quant_group=group, **base)
+        group, group_mlp = 0, 0
+    return LayerConfig(dtype=dt, quant_group=group, quant_group_mlp=group_mlp, **base)
 
 
 class KVCache:
@@ -173,18 +198,34 @@ class Layer:
         check(lib().ds_layer_create(C.byref(cfg.c_desc()), C.byref(cw), C.byref(h)), "ds_layer_create")
         self._h = h
 
+    def close(self):
+        """Release the library handle (the weight tensors stay the caller's). Idempotent."""
+        h, self._h = getattr(self, "_h", None), None
+        if h is not None and h.value:
+            lib().ds_layer_destroy(h)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
     def __del__(self):
-        h = getattr(self, "_h", None)
-        if h is not None and h.value and _lib._LIB is not None:
-            _lib._LIB.ds_layer_destroy(h)
-            self._h = None
+        # at interpreter shutdown the modules this needs may already be gone: then the process
+        # ends anyway and the small host handle goes with it
+        try:
+            self.close()
+        except Exception:
+            pass
 
     @property
     def handle(self):
+        if self._h is None:
+            raise ValueError("layer is closed")
         return self._h
 
     def workspace_bytes(self, batch, tokens, capacity) -> int:
-        return int(lib().ds_layer_workspace_bytes(self._h, batch, tokens, capacity))
+        return int(lib().ds_layer_workspace_bytes(self.handle, batch, tokens, capacity))
 
     def workspace(self, batch, tokens, capacity, device="cuda") -> torch.Tensor:
         return torch.empty(self.workspace_bytes(batch, tokens, capacity), dtype=torch.uint8, device=device)
@@ -204,7 +245,7 @@ class Layer:
         y = self._io(x, y, (B, self.cfg.hidden))
         if workspace is None:
             workspace = self.workspace(B, 1, kv.capacity, x.device)
-        check(lib().ds_layer_forward_decode(self._h, C.byref(kv.c_struct()), ptr(x), ptr(y), B,
+        check(lib().ds_layer_forward_decode(self.handle, C.byref(kv.c_struct()), ptr(x), ptr(y), B,
                                             ptr(workspace), workspace.numel(), stream_handle(stream)),
               "ds_layer_forward_decode")
         return y
@@ -215,7 +256,7 @@ class Layer:
         y = self._io(x, y, (B, S, self.cfg.hidden))
         if workspace is None:
             workspace = self.workspace(B, S, kv.capacity, x.device)
-        check(lib().ds_layer_forward_prefill(self._h, C.byref(kv.c_struct()), ptr(x), ptr(y), B, S,
+        check(lib().ds_layer_forward_prefill(self.handle, C.byref(kv.c_struct()), ptr(x), ptr(y), B, S,
                                              ptr(workspace), workspace.numel(), stream_handle(stream)),
               "ds_layer_forward_prefill")
         return y
@@ -226,39 +267,62 @@ class Layer:
         for t in (k_new, v_new):
             if tuple(t.shape) != (B, T, self.cfg.hidden) or t.dtype != self.cfg.torch_act_dtype or not t.is_contiguous():
                 raise ValueError("k_new, v_new must be contiguous [batch, ntok, hidden] in the activation dtype")
-        check(lib().ds_kv_append(self._h, C.byref(kv.c_struct()), ptr(k_new), ptr(v_new), B, T,
+        check(lib().ds_kv_append(self.handle, C.byref(kv.c_struct()), ptr(k_new), ptr(v_new), B, T,
                                  stream_handle(stream)), "ds_kv_append")
 
 
 class Stack:
     """Persistent decode of a whole stack: layers[l] bound to caches[l]; one launch per step.
 
-    The layers (and their weight tensors) and the caches must outlive the stack.
+    The layers (and their weight tensors) and the caches must outlive the stack. The stack's device
+    state (layer table, launch counter, error flag) is a tensor this object owns. Call close() (or
+    use the stack as a context manager) when done: it releases the library handle at a point the
+    program chooses rather than during interpreter shutdown.
     """
 
-    def __init__(self, layers, caches, max_batch: int = 1):
+    def __init__(self, layers, caches, max_batch: int = 1, device="cuda"):
         if len(layers) != len(caches) or not layers:
             raise ValueError("need one cache per layer")
         self.layers, self.caches, self.max_batch = list(layers), list(caches), max_batch
         handles = (C.c_void_p * len(layers))(*[l.handle.value for l in layers])
         self._cstructs = (_lib.KVCacheC * len(caches))(*[c.c_struct() for c in caches])
+        nbytes = int(lib().ds_stack_state_bytes(len(layers)))
+        self._state = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
         h = C.c_void_p()
-        check(lib().ds_stack_create(handles, self._cstructs, len(layers), max_batch, C.byref(h)), "ds_stack_create")
+        check(lib().ds_stack_create(handles, self._cstructs, len(layers), max_batch, ptr(self._state),
+                                    self._state.numel(), C.byref(h)), "ds_stack_create")
         self._h = h
         self.cfg = layers[0].cfg
 
+    def close(self):
+        """Release the library handle; the state tensor is freed with this object. Idempotent."""
+        h, self._h = getattr(self, "_h", None), None
+        if h is not None and h.value:
+            lib().ds_stack_destroy(h)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
     def __del__(self):
-        h = getattr(self, "_h", None)
-        if h is not None and h.value and _lib._LIB is not None:
-            _lib._LIB.ds_stack_destroy(h)
-            self._h = None
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _handle(self):
+        if self._h is None:
+            raise ValueError("stack is closed")
+        return self._h
 
     @property
     def groups(self) -> int:
-        return int(lib().ds_stack_groups(self._h))
+        return int(lib().ds_stack_groups(self._handle()))
 
     def workspace_bytes(self, batch) -> int:
-        return int(lib().ds_stack_workspace_bytes(self._h, batch))
+        return int(lib().ds_stack_workspace_bytes(self._handle(), batch))
 
     def workspace(self, batch, device="cuda") -> torch.Tensor:
         n = self.workspace_bytes(batch)
@@ -274,16 +338,16 @@ class Stack:
         y = torch.empty_like(x) if y is None else y
         if workspace is None:
             workspace = self.workspace(B, x.device)
-        check(lib().ds_stack_forward_decode(self._h, ptr(x), ptr(y), B, ptr(workspace), workspace.numel(),
+        check(lib().ds_stack_forward_decode(self._handle(), ptr(x), ptr(y), B, ptr(workspace), workspace.numel(),
                                             stream_handle(stream)), "ds_stack_forward_decode")
         return y
 
     def check(self):
         """Synchronize; raise if a step hit the wait timeout (the state is then reset)."""
-        check(lib().ds_stack_check(self._h), "ds_stack_check")
+        check(lib().ds_stack_check(self._handle()), "ds_stack_check")
 
     def set_timeout_us(self, us: int):
-        check(lib().ds_stack_set_timeout_us(self._h, int(us)), "ds_stack_set_timeout_us")
+        check(lib().ds_stack_set_timeout_us(self._handle(), int(us)), "ds_stack_set_timeout_us")
 
 
 def read_probe(buf: torch.Tensor, out: torch.Tensor, stream=None):

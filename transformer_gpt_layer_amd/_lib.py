@@ -22,13 +22,13 @@ EXPORTS = ("ds_layer_create", "ds_layer_destroy", "ds_layer_workspace_bytes", "d
            "ds_layer_forward_decode", "ds_layer_forward_prefill", "ds_quantize_i8",
            "ds_dequantize_i8", "ds_last_error", "ds_stack_create", "ds_stack_destroy",
            "ds_stack_workspace_bytes", "ds_stack_groups", "ds_stack_forward_decode",
-           "ds_stack_check", "ds_stack_set_timeout_us", "ds_read_probe")
+           "ds_stack_check", "ds_stack_set_timeout_us", "ds_read_probe", "ds_stack_state_bytes")
 
 
 class LayerDescC(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn", C.c_int32), ("weight_dtype", C.c_int32), ("act_dtype", C.c_int32),
-                ("quant_group", C.c_int32), ("ln_eps", C.c_float), ("gelu_tanh", C.c_int32),
+                ("quant_group", C.c_int32), ("quant_group_mlp", C.c_int32), ("ln_eps", C.c_float), ("gelu_tanh", C.c_int32),
                 ("triangular_masking", C.c_int32)]
 
 
@@ -67,7 +67,9 @@ def lib():
         L.ds_quantize_i8.argtypes = [vp, vp, vp, i32, i32, i32, vp]
         L.ds_dequantize_i8.argtypes = [vp, vp, vp, i32, i32, i32, vp]
         L.ds_last_error.restype = C.c_char_p
-        L.ds_stack_create.argtypes = [C.POINTER(vp), C.POINTER(KVCacheC), i32, i32, C.POINTER(vp)]
+        L.ds_stack_state_bytes.argtypes = [i32]
+        L.ds_stack_state_bytes.restype = C.c_size_t
+        L.ds_stack_create.argtypes = [C.POINTER(vp), C.POINTER(KVCacheC), i32, i32, vp, C.c_size_t, C.POINTER(vp)]
         L.ds_stack_destroy.argtypes = [vp]
         L.ds_stack_workspace_bytes.argtypes = [vp, i32]
         L.ds_stack_workspace_bytes.restype = C.c_size_t

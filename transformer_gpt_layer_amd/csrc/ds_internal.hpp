@@ -7,6 +7,10 @@
 struct ds_layer {
   ds_layer_desc desc;
   ds_layer_weights w;
+  // MFMA tile configuration forced for every GEMM of this layer (-1: chosen per product). Read from
+  // the DS_GEMM_CONFIG environment variable at create time; for tests that must run each
+  // configuration on shapes where the automatic choice would not take it.
+  int gemm_cfg = -1;
 };
 
 namespace ds {

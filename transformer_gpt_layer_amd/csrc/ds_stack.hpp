@@ -16,11 +16,12 @@ struct StackLayer {
   int32_t* d_len;
 };
 
-// sync[] layout in 32-bit words (library-owned). Workgroups never wait for each other at a
-// barrier: every value that crosses workgroups is stored together with a tag naming the launch,
-// the layer and the phase that produced it, and a consumer polls until the tags it needs are
-// current. kSyncLaunch holds the launch counter (seeded per stack, advanced by the last workgroup
-// out); kSyncExit counts finished workgroups; kSyncError is raised by any wait that timed out.
+// sync[] layout in 32-bit words, at the start of the caller-owned state buffer. Workgroups never
+// wait for each other at a barrier: every value that crosses workgroups is stored together with a
+// tag naming the launch, the layer and the phase that produced it, and a consumer polls until the
+// tags it needs are current. kSyncLaunch holds the launch counter (seeded per stack, advanced by the
+// last workgroup out, kLaunchBits wide); kSyncExit counts finished workgroups; kSyncError is raised
+// by any wait that timed out, and a launch that finds it raised leaves before any store.
 constexpr int kSyncLine = 64;
 enum {
   kSyncLaunch = 0,
@@ -28,10 +29,16 @@ enum {
   kSyncError = 2 * kSyncLine,
   kSyncWords = 3 * kSyncLine,
 };
+constexpr uint32_t kSyncBytes = kSyncWords * 4;  // the layer table follows (256-byte aligned)
+constexpr int kLaunchBits = 19;
+constexpr uint32_t kLaunchMask = (1u << kLaunchBits) - 1u;
+constexpr int kStackMaxLayers = 511;  // layer * 8 + phase fits the tag's 12 low bits
 
-// Tag of values produced in layer l by phase ph of launch `launch` (layer < 512, ph < 8).
+// Tag of values produced in layer l (< 512) by phase ph (< 8) of launch `launch`. The top bit is
+// always set, so zero-filled memory never holds a current tag; within any 2^19 consecutive launches
+// of one stack no two tags are equal (the host clears the workspace before the counter comes round).
 __host__ __device__ inline uint32_t stack_tag(uint32_t launch, int l, int ph) {
-  return (launch << 12) | (uint32_t)(l * 8 + ph);
+  return 0x80000000u | ((launch & kLaunchMask) << 12) | (uint32_t)(l * 8 + ph);
 }
 enum { TAG_Q = 0, TAG_PART = 1, TAG_CTX = 2, TAG_X2 = 3, TAG_F = 4, TAG_Y = 5 };
 

@@ -32,6 +32,22 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AT* __restrict__ k
   *reinterpret_cast<u32x4*>(vc + at) = ld16(vn + el);
 }
 
+// Zero fill of a 16-byte aligned buffer whose size is a multiple of 16 bytes (a kernel rather than a
+// memset node, so that it replays correctly inside captured graphs).
+__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
+
 __global__ void len_advance_kernel(int32_t* d_len, int batch, int ntok, int cap) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < batch && d_len[b] + ntok <= cap) d_len[b] += ntok;

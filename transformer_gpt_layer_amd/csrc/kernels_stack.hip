@@ -1052,7 +1052,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
           if (v + 1 <= a.cap) __hip_atomic_store(dl, v + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       __hip_atomic_store(a.sync + kSyncExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.sync + kSyncLaunch, launch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.sync + kSyncLaunch, (launch + 1u) & kLaunchMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1083,10 +1083,13 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
     c.act_ready = 0u;
     for (int w = 0; w < NWK; ++w) c.done[w] = 0u;
     c.sbar = 0u;
-    c.abort = 0u;
     c.launch = __hip_atomic_load(a.sync + kSyncLaunch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // an earlier launch of this stack timed out and the state has not been reset yet: this launch
+    // would run under that launch's number, so it leaves before storing anything
+    c.abort = __hip_atomic_load(a.sync + kSyncError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ? 1u : 0u;
   }
   __syncthreads();
+  if (c.abort != 0u) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   if (wave < NS) {

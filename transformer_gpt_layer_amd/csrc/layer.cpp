@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -158,7 +159,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
       a.w = static_cast<const ds::half_t*>(w);
     }
     if (skinny) return ds::launch_skinny(epi, i8, a, cus, st);
-    return ds::launch_gemm(epi, a, ds::gemm_pick(a.M, a.N, a.K, cus), st);
+    return ds::launch_gemm(epi, a, L->gemm_cfg >= 0 ? L->gemm_cfg : ds::gemm_pick(a.M, a.N, a.K, cus), st);
   };
 
   // 1: h = LN1(x); [q | k | v] = h Wqkv^T + bqkv, k and v into the cache rows d_len[b] + t
@@ -315,10 +316,14 @@ int ds_layer_create(const ds_layer_desc* desc, const ds_layer_weights* w, ds_lay
                        (d.weight_dtype == DS_I8 && d.act_dtype == DS_F16);
   if (!pair_ok) return fail(DS_ERR_DTYPE, "unsupported (weight, activation) dtype pair (%d, %d)", d.weight_dtype, d.act_dtype);
   if (d.weight_dtype == DS_I8) {
-    if (d.quant_group < 16 || d.quant_group % 16 || d.hidden % d.quant_group || d.ffn % d.quant_group)
-      return fail(DS_ERR_DTYPE, "quant_group %d must be a multiple of 16 dividing hidden and ffn", d.quant_group);
-  } else if (d.quant_group != 0) {
-    return fail(DS_ERR_DTYPE, "quant_group %d must be 0 for non-int8 weights", d.quant_group);
+    // the int8 kernels are built and parity-tested for groups of 64 elements along K
+    const int gm = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
+    if (d.quant_group != 64 || gm != 64)
+      return fail(DS_ERR_UNSUPPORTED, "int8 group sizes %d (attention) and %d (MLP): this build supports 64 and 64",
+                  d.quant_group, gm);
+  } else if (d.quant_group != 0 || d.quant_group_mlp != 0) {
+    return fail(DS_ERR_DTYPE, "quant_group %d and quant_group_mlp %d must be 0 for non-int8 weights", d.quant_group,
+                d.quant_group_mlp);
   }
   if (!(d.ln_eps > 0.f) || !std::isfinite(d.ln_eps)) return fail(DS_ERR_SHAPE, "ln_eps must be finite and > 0");
   if ((d.gelu_tanh != 0 && d.gelu_tanh != 1) || (d.triangular_masking != 0 && d.triangular_masking != 1))
@@ -343,6 +348,11 @@ int ds_layer_create(const ds_layer_desc* desc, const ds_layer_weights* w, ds_lay
   if (!L) return fail(DS_ERR_NULL, "out of host memory");
   L->desc = d;
   L->w = *w;
+  if (const char* env = std::getenv("DS_GEMM_CONFIG")) {
+    char* end = nullptr;
+    const long v = std::strtol(env, &end, 10);
+    if (end != env && *end == '\0' && v >= 0 && v <= 2) L->gemm_cfg = (int)v;
+  }
   *out = L;
   return DS_OK;
 }

@@ -2,13 +2,17 @@
 //
 // A stack binds L layers that share one description to their L KV caches and runs a whole decode
 // step -- every fusion region of every layer ("DeepSpeed Inference 内核优化深度解析", section 三 3.2)
-// -- in one cooperative launch. The library owns two small device buffers per stack: the table of
-// layer pointers and the sync block (launch counter, exit count, error flag).
+// -- in one cooperative launch. Its persistent device state (the sync block: launch counter, exit
+// count, error flag; then the table of layer pointers) lives in a caller-owned buffer; the library
+// allocates no device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <random>
+#include <unordered_map>
 #include <vector>
 
 #include "ds_internal.hpp"
@@ -18,13 +22,39 @@ struct ds_stack {
   ds_layer_desc desc;
   std::vector<ds_kv_cache> caches;
   int n_layers = 0, max_batch = 0, G = 0, nchunk = 0, device = 0;
-  ds::StackLayer* d_layers = nullptr;
-  uint32_t* d_sync = nullptr;
+  uint64_t uid = 0;  // never reused: names this stack in the workspace registry
+  ds::StackLayer* d_layers = nullptr;  // inside the caller's state buffer
+  uint32_t* d_sync = nullptr;          // the state buffer's first kSyncBytes
   size_t sync_words = 0;
   uint64_t timeout_ticks = 200000000ull;  // 2 s at the 100 MHz wall clock
 };
 
 namespace {
+
+constexpr size_t kStateTable = 1024;  // byte offset of the layer table in the state buffer
+static_assert(kStateTable >= ds::kSyncBytes, "sync block fits before the table");
+
+// Launches of one stack on one workspace between two clears: the tags of 2^19 consecutive launches
+// are distinct, and the margin covers the counter steps of failed launches that ds_stack_check
+// skips.
+constexpr uint32_t kClearEvery = (1u << ds::kLaunchBits) - 64u;
+
+// Which stack last used each workspace (by device address), how many of its launches ran since the
+// workspace was last cleared, and how many bytes that clear covered.
+struct WsUse {
+  uint64_t uid = 0;
+  uint32_t launches = 0;
+  size_t bytes = 0;
+};
+std::mutex& ws_mutex() {
+  static std::mutex m;
+  return m;
+}
+std::unordered_map<uintptr_t, WsUse>& ws_registry() {
+  static std::unordered_map<uintptr_t, WsUse> r;
+  return r;
+}
+std::atomic<uint64_t> g_next_uid{1};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
@@ -57,15 +87,43 @@ int hip_err(hipError_t e, const char* where) {
   return ds::set_error(DS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+// Before a launch of stack S on the workspace ws (bytes used by this launch): clear it when another
+// stack used it last, when this launch uses bytes the last clear did not cover, or when the launch
+// counter could come round to a tag the workspace still holds.
+int prepare_workspace(const ds_stack& S, void* ws, size_t bytes, hipStream_t st) {
+  bool clear;
+  {
+    std::lock_guard<std::mutex> g(ws_mutex());
+    WsUse& u = ws_registry()[reinterpret_cast<uintptr_t>(ws)];
+    clear = u.uid != S.uid || u.launches >= kClearEvery || u.bytes < bytes;
+    if (clear) u = WsUse{S.uid, 0u, bytes > u.bytes || u.uid != S.uid ? bytes : u.bytes};
+    ++u.launches;
+  }
+  if (clear)
+    if (hipError_t e = ds::launch_fill_zero(ws, bytes, st)) return hip_err(e, "workspace clear launch");
+  return DS_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
+size_t ds_stack_state_bytes(int32_t n_layers) {
+  if (n_layers < 1) return 0;
+  return up256(kStateTable + sizeof(ds::StackLayer) * (size_t)n_layers);
+}
+
 int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, int32_t n_layers,
-                    int32_t max_batch, ds_stack_t** out) {
+                    int32_t max_batch, void* state, size_t state_bytes, ds_stack_t** out) {
   if (!layers || !caches || !out) return ds::set_error(DS_ERR_NULL, "layers, caches or out is NULL");
   *out = nullptr;
   if (n_layers < 1) return ds::set_error(DS_ERR_SHAPE, "n_layers %d < 1", n_layers);
+  if (n_layers > ds::kStackMaxLayers)
+    return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode handles at most %d layers, got %d", ds::kStackMaxLayers, n_layers);
+  if (!state) return ds::set_error(DS_ERR_NULL, "state buffer is NULL");
+  if (!aligned16(state)) return ds::set_error(DS_ERR_ALIGN, "state buffer is not 16-byte aligned");
+  if (state_bytes < ds_stack_state_bytes(n_layers))
+    return ds::set_error(DS_ERR_WORKSPACE, "state buffer %zu bytes < %zu needed", state_bytes, ds_stack_state_bytes(n_layers));
   if (max_batch < 1 || max_batch > 4)
     return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode handles batch 1..4, got %d", max_batch);
   if (layers[0] && layers[0]->desc.weight_dtype == DS_F32 && max_batch > 1)
@@ -131,20 +189,19 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
                               caches[l].k, caches[l].v, caches[l].d_len};
   }
   S->sync_words = ds::kSyncWords;
-  e = hipMalloc(reinterpret_cast<void**>(&S->d_layers), sizeof(ds::StackLayer) * n_layers);
-  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&S->d_sync), S->sync_words * 4);
-  if (e == hipSuccess) e = hipMemcpy(S->d_layers, table.data(), sizeof(ds::StackLayer) * n_layers, hipMemcpyHostToDevice);
+  S->uid = g_next_uid.fetch_add(1);
+  S->d_sync = static_cast<uint32_t*>(state);
+  S->d_layers = reinterpret_cast<ds::StackLayer*>(static_cast<char*>(state) + kStateTable);
+  e = hipMemcpy(S->d_layers, table.data(), sizeof(ds::StackLayer) * n_layers, hipMemcpyHostToDevice);
   if (e == hipSuccess) {
-    // the launch counter starts at a random value, so that tags of this stack never match values
-    // some earlier stack left in a reused workspace
+    // the launch counter starts at a random value: a second line of defence, besides the clear on
+    // a change of owner, against values some other stack left in a shared workspace
     std::vector<uint32_t> init(S->sync_words, 0u);
-    init[ds::kSyncLaunch] = std::random_device{}() & 0xfffffu;
+    init[ds::kSyncLaunch] = std::random_device{}() & ds::kLaunchMask;
     e = hipMemcpy(S->d_sync, init.data(), S->sync_words * 4, hipMemcpyHostToDevice);
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    (void)hipFree(S->d_layers);
-    (void)hipFree(S->d_sync);
     delete S;
     return hip_err(e, "stack device state");
   }
@@ -154,8 +211,12 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
 
 int ds_stack_destroy(ds_stack_t* S) {
   if (!S) return DS_OK;
-  (void)hipFree(S->d_layers);
-  (void)hipFree(S->d_sync);
+  {
+    std::lock_guard<std::mutex> g(ws_mutex());
+    auto& reg = ws_registry();
+    for (auto it = reg.begin(); it != reg.end();)
+      it = it->second.uid == S->uid ? reg.erase(it) : std::next(it);
+  }
   delete S;
   return DS_OK;
 }
@@ -215,7 +276,9 @@ int ds_stack_forward_decode(ds_stack_t* S, const void* x, void* y, int32_t batch
   const int wsz_i = d.weight_dtype == DS_F32 ? 4 : (d.weight_dtype == DS_F16 ? 2 : 1);
   a.lds = ds::stack_lds_layout(wsz_i, batch <= 1 ? 1 : 4, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->G),
                                S->nchunk, d.head_dim, d.quant_group, S->n_layers);
-  if (hipError_t e = ds::launch_stack_decode(wdt, adt, a, reinterpret_cast<hipStream_t>(stream)))
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (int rc = prepare_workspace(*S, ws, W.total, st)) return rc;
+  if (hipError_t e = ds::launch_stack_decode(wdt, adt, a, st))
     return hip_err(e, "persistent decode launch");
   for (int l = 0; l < S->n_layers; ++l)
     if (int32_t* hl = S->caches[l].h_len)
@@ -235,8 +298,12 @@ int ds_stack_check(ds_stack_t* S) {
     // no value that launch stored carries a tag the next one waits for
     words[ds::kSyncError] = 0u;
     words[ds::kSyncExit] = 0u;
-    words[ds::kSyncLaunch] = (words[ds::kSyncLaunch] + 1u) & 0xfffffu;
+    words[ds::kSyncLaunch] = (words[ds::kSyncLaunch] + 1u) & ds::kLaunchMask;
     (void)hipMemcpy(S->d_sync, words.data(), S->sync_words * 4, hipMemcpyHostToDevice);
+    // the host mirrors were advanced when the failed steps were enqueued; the device lengths were
+    // not (only a completed launch advances them): take the device's
+    for (const ds_kv_cache& c : S->caches)
+      if (c.h_len) (void)hipMemcpy(c.h_len, c.d_len, sizeof(int32_t) * (size_t)S->max_batch, hipMemcpyDeviceToHost);
     (void)hipDeviceSynchronize();
     return ds::set_error(DS_ERR_HIP, "persistent decode: a wait timed out (error flag %u, %u of %d workgroups "
                          "finished); state reset, outputs of the failed step are invalid", err, exits, S->G);
