@@ -317,3 +317,57 @@ def test_layer_rejects_overflow():
     k, v, lens = _cache(1, nh, 8, H // nh, 8, 2)
     with pytest.raises(ValueError):
         oracle.layer_forward(oracle.Desc(H, nh, H // nh, F), w, k, v, lens, np.zeros((1, 1, H)))
+
+
+# ------------------------------------------------------------------ the ends of a generation step
+def test_argmax_golden_cases():
+    gold = json.load(open(os.path.join(GOLD, "argmax_examples.json")))
+    for case in gold["cases"]:
+        assert oracle.argmax(np.array(case["values"])) == case["index"], case["note"]
+
+
+def test_argmax_matches_numpy_and_takes_the_first_tie():
+    # numpy's argmax returns the first position of the maximum, the same rule
+    for n in (1, 2, 7, 64, 50257):
+        v = rng.normal(size=n)
+        assert oracle.argmax(v) == int(np.argmax(v))
+        w = v.copy()
+        i, j = sorted(rng.choice(n, size=2, replace=False)) if n > 1 else (0, 0)
+        w[i] = w[j] = v.max() + 1.0   # an exact tie at the top
+        assert oracle.argmax(w) == i
+
+
+def _alternating(H, a):
+    """y = [a, -a, a, -a, ...]: mean 0, biased variance a^2, so LN(y) = y / sqrt(a^2 + eps)."""
+    y = np.empty(H)
+    y[0::2], y[1::2] = a, -a
+    return y
+
+
+def test_lm_head_closed_form_with_small_integer_weights():
+    H, V, a, eps = 8, 5, 1.5, 1e-5
+    w = rng.integers(-3, 4, size=(V, H)).astype(np.float64)
+    y = _alternating(H, a)
+    logits = oracle.lm_head(y, np.ones(H), np.zeros(H), w, eps)
+    sign = np.array([1.0, -1.0] * (H // 2))
+    expect = (a / math.sqrt(a * a + eps)) * (w @ sign)   # integer sums, one scale
+    assert np.max(np.abs(logits - expect)) < 1e-13
+    # gamma = 0: the normalized row drops out and the logits are W beta, exactly (small integers)
+    beta = rng.integers(-2, 3, size=H).astype(np.float64)
+    assert np.array_equal(oracle.lm_head(y, np.zeros(H), beta, w, eps), w @ beta)
+    # a transposed or shifted weight would break the per-row one-hot picks
+    eye = np.zeros((H, H))
+    eye[np.arange(H), (np.arange(H) + 3) % H] = 2.0
+    picked = oracle.lm_head(y, np.ones(H), np.zeros(H), eye, eps)
+    assert np.max(np.abs(picked - 2.0 * np.roll(y, -3) / math.sqrt(a * a + eps))) < 1e-13
+
+
+def test_lm_head_matches_torch_float64_and_greedy_choice():
+    H, V = 64, 300
+    y = rng.normal(size=H)
+    g, b = 1.0 + 0.2 * rng.normal(size=H), 0.2 * rng.normal(size=H)
+    w = 0.02 * rng.normal(size=(V, H))
+    ref = torch.from_numpy(w) @ Fn.layer_norm(torch.from_numpy(y), (H,), torch.from_numpy(g), torch.from_numpy(b), 1e-5)
+    logits = oracle.lm_head(y, g, b, w)
+    assert np.max(np.abs(logits - ref.numpy())) < 1e-13
+    assert oracle.argmax(logits) == int(torch.argmax(ref))
