@@ -220,6 +220,18 @@ int32_t ds_stack_groups(const ds_stack_t* stack);
 int ds_stack_forward_decode(ds_stack_t* stack, const void* x, void* y, int32_t batch,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation): the same step as ds_stack_forward_decode, with
+ * the workspace taken from a static device array inside the library (DS_STACK_STATIC_SCRATCH_BYTES,
+ * 16 MiB, held on each GPU the library runs on until the process ends) instead of a caller buffer.
+ * The call allocates nothing. A step whose workspace (ds_stack_workspace_bytes) exceeds the array
+ * returns DS_ERR_WORKSPACE before anything is enqueued. Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents (the library clears it when a different stack used
+ * it last): calls that overlap in time on one GPU, from any stacks or streams, race and give
+ * undefined results. Same other arguments, outputs and errors as ds_stack_forward_decode. */
+#define DS_STACK_STATIC_SCRATCH_BYTES (16u << 20)
+int ds_stack_forward_decode_static(ds_stack_t* stack, const void* x, void* y, int32_t batch, void* stream);
+
 /* Synchronizes the device and reports whether a step of this stack hit its wait timeout
  * (DS_ERR_HIP) or not (DS_OK). After a timeout every later launch of the stack leaves at once,
  * before any store, until this call resets the counters; it also copies every layer's device

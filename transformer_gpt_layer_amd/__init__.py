@@ -342,6 +342,18 @@ class Stack:
                                             stream_handle(stream)), "ds_stack_forward_decode")
         return y
 
+    def decode_static(self, x, y=None, stream=None):
+        """The same step with the library's static device scratch as workspace: allocates nothing
+        (for callers that cannot allocate). Calls that overlap on one GPU race."""
+        B = x.shape[0]
+        if tuple(x.shape) != (B, self.cfg.hidden) or x.dtype != self.cfg.torch_act_dtype or not x.is_contiguous():
+            raise ValueError("x must be contiguous [batch, hidden] in the activation dtype")
+        if y is None:
+            raise ValueError("decode_static writes into a caller-provided y (it allocates nothing)")
+        check(lib().ds_stack_forward_decode_static(self._handle(), ptr(x), ptr(y), B, stream_handle(stream)),
+              "ds_stack_forward_decode_static")
+        return y
+
     def check(self):
         """Synchronize; raise if a step hit the wait timeout (the state is then reset)."""
         check(lib().ds_stack_check(self._handle()), "ds_stack_check")

@@ -22,7 +22,8 @@ EXPORTS = ("ds_layer_create", "ds_layer_destroy", "ds_layer_workspace_bytes", "d
            "ds_layer_forward_decode", "ds_layer_forward_prefill", "ds_quantize_i8",
            "ds_dequantize_i8", "ds_last_error", "ds_stack_create", "ds_stack_destroy",
            "ds_stack_workspace_bytes", "ds_stack_groups", "ds_stack_forward_decode",
-           "ds_stack_check", "ds_stack_set_timeout_us", "ds_read_probe", "ds_stack_state_bytes")
+           "ds_stack_check", "ds_stack_set_timeout_us", "ds_read_probe", "ds_stack_state_bytes",
+           "ds_stack_forward_decode_static")
 
 
 class LayerDescC(C.Structure):
@@ -76,6 +77,8 @@ def lib():
         L.ds_stack_groups.argtypes = [vp]
         L.ds_stack_groups.restype = i32
         L.ds_stack_forward_decode.argtypes = [vp, vp, vp, i32, vp, C.c_size_t, vp]
+        L.ds_stack_forward_decode_static.argtypes = [vp, vp, vp, i32, vp]
+        L.ds_stack_forward_decode_static.restype = C.c_int
         L.ds_stack_check.argtypes = [vp]
         L.ds_stack_set_timeout_us.argtypes = [vp, C.c_int64]
         L.ds_read_probe.argtypes = [vp, C.c_size_t, vp, vp]

@@ -56,6 +56,38 @@ std::unordered_map<uintptr_t, WsUse>& ws_registry() {
 }
 std::atomic<uint64_t> g_next_uid{1};
 
+// The workspace of ds_stack_forward_decode_static: a file-scope device array, one copy per GPU.
+// Host code never passes the array's name to a kernel (on the host it is only a stand-in symbol);
+// it passes the device address hipGetSymbolAddress returns for the current device, looked up once
+// per device and kept.
+constexpr size_t kStaticScratch = DS_STACK_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratch];
+constexpr int kMaxDevices = 64;
+std::mutex& scratch_mutex() {
+  static std::mutex m;
+  return m;
+}
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int hip_err(hipError_t e, const char* where);
+
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_err(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return ds::set_error(DS_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(scratch_mutex());
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return hip_err(e, "static scratch address");
+    if (!p) return ds::set_error(DS_ERR_HIP, "static scratch address is NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DS_OK;
+}
+
+int stack_forward(ds_stack_t* S, const void* x, void* y, int32_t batch, void* ws, size_t ws_bytes, void* stream);
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 int slice_elems(int wdt) { return wdt == DS_F32 ? 256 : (wdt == DS_F16 ? 512 : 1024); }
@@ -230,6 +262,26 @@ int32_t ds_stack_groups(const ds_stack_t* S) { return S ? S->G : 0; }
 
 int ds_stack_forward_decode(ds_stack_t* S, const void* x, void* y, int32_t batch, void* ws, size_t ws_bytes,
                             void* stream) {
+  return stack_forward(S, x, y, batch, ws, ws_bytes, stream);
+}
+
+int ds_stack_forward_decode_static(ds_stack_t* S, const void* x, void* y, int32_t batch, void* stream) {
+  if (!S) return ds::set_error(DS_ERR_NULL, "stack is NULL");
+  if (batch < 1 || batch > S->max_batch) return ds::set_error(DS_ERR_SHAPE, "batch %d outside [1, %d]", batch, S->max_batch);
+  const size_t need = stack_ws(*S, batch).total;
+  if (need > kStaticScratch)
+    return ds::set_error(DS_ERR_WORKSPACE, "step needs %zu bytes of workspace; the static scratch holds %zu", need,
+                         kStaticScratch);
+  void* ws = nullptr;
+  if (int rc = static_scratch(&ws)) return rc;
+  return stack_forward(S, x, y, batch, ws, kStaticScratch, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int stack_forward(ds_stack_t* S, const void* x, void* y, int32_t batch, void* ws, size_t ws_bytes, void* stream) {
   if (!S) return ds::set_error(DS_ERR_NULL, "stack is NULL");
   if (batch < 1 || batch > S->max_batch) return ds::set_error(DS_ERR_SHAPE, "batch %d outside [1, %d]", batch, S->max_batch);
   if (!x || !y || !ws) return ds::set_error(DS_ERR_NULL, "x, y or workspace is NULL");
@@ -285,6 +337,10 @@ int ds_stack_forward_decode(ds_stack_t* S, const void* x, void* y, int32_t batch
       for (int b = 0; b < batch; ++b) hl[b] += 1;
   return DS_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int ds_stack_check(ds_stack_t* S) {
   if (!S) return ds::set_error(DS_ERR_NULL, "stack is NULL");
