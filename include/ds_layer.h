@@ -195,11 +195,28 @@ int ds_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
  * ------------------------------------------------------------------------------------------- */
 typedef struct ds_stack ds_stack_t;
 
+/* The ends of a generation step (the GPT-Neo-2.7B text-generation example of [KP] section 二):
+ * after the last layer, a final LayerNorm and the LM head, logits = W_vocab LN(y; ln_g, ln_b) (no
+ * bias), then greedy decoding: the token is the position of the largest logit, the smallest such
+ * position on ties. (The example samples; the logits are returned for callers that do.) Borrowed
+ * device pointers: ln_g, ln_b [hidden] in act_dtype; w [vocab][hidden] in weight_dtype; s the fp16
+ * scales [vocab][hidden/quant_group] when the weights are int8, else NULL. */
+typedef struct {
+  const void* ln_g;
+  const void* ln_b;
+  const void* w;
+  const void* s;
+  int32_t vocab;  /* >= 1; vocab * hidden weight bytes under 2 GiB */
+} ds_lm_head;
+
 /* Bytes of the caller-owned state buffer of a stack of n_layers layers (0 if n_layers < 1). */
 size_t ds_stack_state_bytes(int32_t n_layers);
 
+/* head: NULL for a stack without the LM head (ds_stack_forward_generate then fails with
+ * DS_ERR_UNSUPPORTED), else copied (its pointers must stay valid for the stack's life). */
 int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, int32_t n_layers,
-                    int32_t max_batch, void* state, size_t state_bytes, ds_stack_t** out);
+                    int32_t max_batch, const ds_lm_head* head, void* state, size_t state_bytes,
+                    ds_stack_t** out);
 /* Releases the host handle (no device memory is freed; the state buffer is the caller's). */
 int ds_stack_destroy(ds_stack_t* stack);
 
@@ -219,6 +236,13 @@ int32_t ds_stack_groups(const ds_stack_t* stack);
  * Calls on one stack must not overlap in time (they share its counters). */
 int ds_stack_forward_decode(ds_stack_t* stack, const void* x, void* y, int32_t batch,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* One whole generation step: ds_stack_forward_decode through every layer (y receives the last
+ * layer's output), then the LM head in the same launch. logits: device fp32 [batch][vocab], or NULL
+ * to skip storing them; tokens: device int32 [batch], the greedy choice of each sequence. NaN logits
+ * give an unspecified token. Same workspace and errors as ds_stack_forward_decode. */
+int ds_stack_forward_generate(ds_stack_t* stack, const void* x, void* y, float* logits, int32_t* tokens,
+                              int32_t batch, void* workspace, size_t workspace_bytes, void* stream);
 
 /* For callers that cannot allocate device memory (code being captured into a HIP graph, tight
  * serving loops, harnesses that forbid allocation): the same step as ds_stack_forward_decode, with

@@ -24,7 +24,10 @@ import torch
 
 # tensor ids
 LN1_G, LN1_B, W_QKV, B_QKV, W_O, B_O, LN2_G, LN2_B, W_FF1, B_FF1, W_FF2, B_FF2, K_PAST, V_PAST = range(14)
-X_LAYER = 65535  # layer slot used for the stack input x
+LNF_G, LNF_B, W_VOCAB = 14, 15, 16
+X_LAYER = 65535     # layer slot used for the stack input x
+HEAD_LAYER = 65534  # layer slot of the final LayerNorm and the LM head
+GPT_NEO_VOCAB = 50257  # the GPT-2 BPE vocabulary of the GPT-Neo-2.7B example
 
 WEIGHT_NAMES = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
                 "ln2_g", "ln2_b", "w_ff1", "b_ff1", "w_ff2", "b_ff2")
@@ -122,3 +125,15 @@ def past_kv_f32(wl: Workload, layer: int, device="cpu"):
 def stack_input_f32(wl: Workload, device="cpu", step: int = 0) -> torch.Tensor:
     """float32 [B, T, H] N(0,1) input rows of the stack."""
     return normal((wl.batch, wl.seq, wl.hidden), 1.0, wl.cfg_id, X_LAYER, step, device)
+
+
+def lm_head_f32(wl: Workload, vocab: int, device="cpu") -> dict:
+    """float32 final LayerNorm (gamma, beta as for the layers of this workload) and LM head weight
+    [vocab, hidden] ~ N(0, 0.02)."""
+    H, c = wl.hidden, wl.cfg_id
+    if wl.ln_std > 0:
+        g = normal((H,), wl.ln_std, c, HEAD_LAYER, LNF_G, device).add_(1.0)
+        b = normal((H,), wl.ln_std, c, HEAD_LAYER, LNF_B, device)
+    else:
+        g, b = torch.ones(H, device=device), torch.zeros(H, device=device)
+    return {"ln_g": g, "ln_b": b, "w": normal((vocab, H), 0.02, c, HEAD_LAYER, W_VOCAB, device)}

@@ -180,16 +180,29 @@ def test_stack_create_rejects_before_device_work():
     need = L.ds_stack_state_bytes(2)
     assert need > 0 and L.ds_stack_state_bytes(0) == 0
     # the tag packs layer * 8 + phase into 12 bits: 511 layers at most
-    assert L.ds_stack_create(handles, caches, 512, 1, C.c_void_p(FAKE), 1 << 30, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
-    assert L.ds_stack_create(handles, caches, n, 1, C.c_void_p(FAKE), 1 << 30, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
+    assert L.ds_stack_create(handles, caches, 512, 1, None, C.c_void_p(FAKE), 1 << 30, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
+    assert L.ds_stack_create(handles, caches, n, 1, None, C.c_void_p(FAKE), 1 << 30, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
     assert "511" in L.ds_last_error().decode()
-    assert L.ds_stack_create(handles, caches, 0, 1, C.c_void_p(FAKE), 1 << 30, C.byref(out)) == _lib.DS_ERR_SHAPE
-    assert L.ds_stack_create(handles, caches, 2, 1, None, need, C.byref(out)) == _lib.DS_ERR_NULL
-    assert L.ds_stack_create(handles, caches, 2, 1, C.c_void_p(FAKE + 8), need, C.byref(out)) == _lib.DS_ERR_ALIGN
-    assert L.ds_stack_create(handles, caches, 2, 1, C.c_void_p(FAKE), need - 1, C.byref(out)) == _lib.DS_ERR_WORKSPACE
-    assert L.ds_stack_create(handles, caches, 2, 5, C.c_void_p(FAKE), need, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
+    assert L.ds_stack_create(handles, caches, 0, 1, None, C.c_void_p(FAKE), 1 << 30, C.byref(out)) == _lib.DS_ERR_SHAPE
+    assert L.ds_stack_create(handles, caches, 2, 1, None, None, need, C.byref(out)) == _lib.DS_ERR_NULL
+    assert L.ds_stack_create(handles, caches, 2, 1, None, C.c_void_p(FAKE + 8), need, C.byref(out)) == _lib.DS_ERR_ALIGN
+    assert L.ds_stack_create(handles, caches, 2, 1, None, C.c_void_p(FAKE), need - 1, C.byref(out)) == _lib.DS_ERR_WORKSPACE
+    assert L.ds_stack_create(handles, caches, 2, 5, None, C.c_void_p(FAKE), need, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
     assert not out.value
     L.ds_layer_destroy(h)
+    # LM head descriptions are checked before any device work too (on a stack-compatible layer)
+    rc, h2 = _create(_desc(hidden=512, heads=4, ffn=1024), _weights())
+    assert rc == 0
+    handles = (C.c_void_p * 2)(h2.value, h2.value)
+    bad = [_lib.LmHeadC(FAKE, FAKE, None, None, 100), _lib.LmHeadC(FAKE, FAKE, FAKE + 8, None, 100),
+           _lib.LmHeadC(FAKE, FAKE, FAKE, FAKE, 100), _lib.LmHeadC(FAKE, FAKE, FAKE, None, 0),
+           _lib.LmHeadC(FAKE, FAKE, FAKE, None, 1 << 21)]
+    codes = [_lib.DS_ERR_NULL, _lib.DS_ERR_ALIGN, _lib.DS_ERR_DTYPE, _lib.DS_ERR_SHAPE, _lib.DS_ERR_SHAPE]
+    for head, code in zip(bad, codes):
+        rc = L.ds_stack_create(handles, caches, 2, 1, C.byref(head), C.c_void_p(FAKE), need, C.byref(out))
+        assert rc == code, (rc, L.ds_last_error())
+    assert not out.value
+    L.ds_layer_destroy(h2)
 
 
 def test_layer_close_is_idempotent():

@@ -1,8 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configurations the benchmark times.
 
 - GPT-Neo-2.7B shapes (hidden 2560, 20 heads, FF 10240, fp16, batch 1, 512 past rows): the whole
-  32-layer persistent decode step, every output element and every new cache row checked against
-  the oracle run layer after layer.
+  32-layer persistent generation step with the final LayerNorm and the LM head over the GPT-Neo
+  vocabulary (50257), every output element, every new cache row, the logits and the greedy token
+  checked against the oracle run layer after layer.
 - 13B shapes (hidden 5120, 40 heads, FF 20480, batch 8, 1024 past rows), fp16 and int8 (group 64):
   one full-size layer through the per-layer kernels the benchmark uses at batch 8, and the int8
   batch-1 layer through the persistent kernel. The kernels and their grids depend on the shapes,
@@ -83,10 +84,14 @@ def test_c2_full_stack_32_layers_matches_oracle():
     kvs = [_filled_cache(wl, l, layers[l], torch.float16) for l in range(wl.layers)]
     # the oracle's copies of the past rows, taken before the step writes row P
     past = [_oracle_cache(kv, wl.past) for kv in kvs]
-    st = tg.Stack(layers, kvs, max_batch=1)
+    # the generation step's ends: final LayerNorm and the LM head over the GPT-Neo vocabulary
+    h32 = syn.lm_head_f32(wl, syn.GPT_NEO_VOCAB, "cuda")
+    head = {k: v.half().contiguous() for k, v in h32.items()}
+    del h32
+    st = tg.Stack(layers, kvs, max_batch=1, head=head)
     print(f"  workgroups {st.groups}", flush=True)
     x = syn.normal((1, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").half()
-    y = st.decode(x)
+    y, logits, tokens = st.generate(x)
     st.check()
     st.close()
     desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
@@ -103,6 +108,20 @@ def test_c2_full_stack_32_layers_matches_oracle():
     err = rel_l2(y.double().cpu().numpy(), h[:, 0])
     print(f"  32-layer output rel L2 {err:.3e}", flush=True)
     assert err <= TOL["f16"], err
+    lo = oracle.lm_head(h[0, 0], head["ln_g"].double().cpu().numpy(), head["ln_b"].double().cpu().numpy(),
+                        head["w"].double().cpu().numpy())
+    lg = logits[0].double().cpu().numpy()
+    err_l = rel_l2(lg, lo)
+    top2 = np.sort(lo)[-2:]
+    print(f"  logits rel L2 {err_l:.3e}; token {int(tokens[0])}, oracle {oracle.argmax(lo)} "
+          f"(oracle top-2 gap {top2[1] - top2[0]:.3e}, largest logit error {np.abs(lg - lo).max():.3e})", flush=True)
+    assert err_l <= TOL["f16"], err_l
+    assert int(tokens[0]) == int(np.flatnonzero(lg == lg.max())[0])
+    margin = 2 * float(np.abs(lg - lo).max())
+    if top2[1] - top2[0] > margin:
+        assert int(tokens[0]) == oracle.argmax(lo)
+    else:
+        assert lo[int(tokens[0])] >= lo.max() - margin
 
 
 @pytest.mark.parametrize("name", ["c3", "c4b8", "c4b1"])

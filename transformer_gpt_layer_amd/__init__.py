@@ -280,16 +280,35 @@ class Stack:
     program chooses rather than during interpreter shutdown.
     """
 
-    def __init__(self, layers, caches, max_batch: int = 1, device="cuda"):
+    def __init__(self, layers, caches, max_batch: int = 1, device="cuda", head=None):
+        """head: optional LM head, a dict with ln_g, ln_b [hidden] (activation dtype), w [vocab,
+        hidden] (weight dtype) and, for int8 weights, s [vocab, hidden / group] fp16 scales; the
+        tensors are borrowed and must outlive the stack."""
         if len(layers) != len(caches) or not layers:
             raise ValueError("need one cache per layer")
         self.layers, self.caches, self.max_batch = list(layers), list(caches), max_batch
+        cfg = layers[0].cfg
+        self._head = None
+        chead = None
+        if head is not None:
+            w = head["w"]
+            if w.dim() != 2 or w.shape[1] != cfg.hidden or not w.is_contiguous() or w.dtype != _TORCH_DT[cfg.dtype]:
+                raise ValueError(f"head w must be a contiguous [vocab, {cfg.hidden}] {_TORCH_DT[cfg.dtype]} tensor")
+            for n in ("ln_g", "ln_b"):
+                t = head[n]
+                if tuple(t.shape) != (cfg.hidden,) or t.dtype != cfg.torch_act_dtype or not t.is_contiguous():
+                    raise ValueError(f"head {n} must be a contiguous [{cfg.hidden}] {cfg.torch_act_dtype} tensor")
+            s = head.get("s")
+            self._head = dict(head)
+            self.vocab = int(w.shape[0])
+            chead = C.byref(_lib.LmHeadC(head["ln_g"].data_ptr(), head["ln_b"].data_ptr(), w.data_ptr(),
+                                         s.data_ptr() if s is not None else None, self.vocab))
         handles = (C.c_void_p * len(layers))(*[l.handle.value for l in layers])
         self._cstructs = (_lib.KVCacheC * len(caches))(*[c.c_struct() for c in caches])
         nbytes = int(lib().ds_stack_state_bytes(len(layers)))
         self._state = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
         h = C.c_void_p()
-        check(lib().ds_stack_create(handles, self._cstructs, len(layers), max_batch, ptr(self._state),
+        check(lib().ds_stack_create(handles, self._cstructs, len(layers), max_batch, chead, ptr(self._state),
                                     self._state.numel(), C.byref(h)), "ds_stack_create")
         self._h = h
         self.cfg = layers[0].cfg
@@ -341,6 +360,25 @@ class Stack:
         check(lib().ds_stack_forward_decode(self._handle(), ptr(x), ptr(y), B, ptr(workspace), workspace.numel(),
                                             stream_handle(stream)), "ds_stack_forward_decode")
         return y
+
+    def generate(self, x, y=None, logits=None, tokens=None, workspace=None, stream=None):
+        """One generation step: every layer, then the LM head and the greedy choice, in one launch.
+        Returns (y, logits, tokens); pass logits=False to skip storing the logits."""
+        B = x.shape[0]
+        if tuple(x.shape) != (B, self.cfg.hidden) or x.dtype != self.cfg.torch_act_dtype or not x.is_contiguous():
+            raise ValueError("x must be contiguous [batch, hidden] in the activation dtype")
+        if self._head is None:
+            raise ValueError("this stack has no LM head")
+        y = torch.empty_like(x) if y is None else y
+        if logits is None:
+            logits = torch.empty((B, self.vocab), dtype=torch.float32, device=x.device)
+        tokens = torch.empty(max(B, 4), dtype=torch.int32, device=x.device) if tokens is None else tokens
+        if workspace is None:
+            workspace = self.workspace(B, x.device)
+        check(lib().ds_stack_forward_generate(self._handle(), ptr(x), ptr(y), ptr(logits) if logits is not False else None,
+                                              ptr(tokens), B, ptr(workspace), workspace.numel(), stream_handle(stream)),
+              "ds_stack_forward_generate")
+        return y, (logits if logits is not False else None), tokens[:B]
 
     def decode_static(self, x, y=None, stream=None):
         """The same step with the library's static device scratch as workspace: allocates nothing

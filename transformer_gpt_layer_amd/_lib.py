@@ -23,7 +23,7 @@ EXPORTS = ("ds_layer_create", "ds_layer_destroy", "ds_layer_workspace_bytes", "d
            "ds_dequantize_i8", "ds_last_error", "ds_stack_create", "ds_stack_destroy",
            "ds_stack_workspace_bytes", "ds_stack_groups", "ds_stack_forward_decode",
            "ds_stack_check", "ds_stack_set_timeout_us", "ds_read_probe", "ds_stack_state_bytes",
-           "ds_stack_forward_decode_static")
+           "ds_stack_forward_decode_static", "ds_stack_forward_generate")
 
 
 class LayerDescC(C.Structure):
@@ -39,6 +39,11 @@ WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "s_qkv", "w_o", "b_o", "s_o
 
 class LayerWeightsC(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class LmHeadC(C.Structure):
+    _fields_ = [("ln_g", C.c_void_p), ("ln_b", C.c_void_p), ("w", C.c_void_p), ("s", C.c_void_p),
+                ("vocab", C.c_int32)]
 
 
 class KVCacheC(C.Structure):
@@ -70,7 +75,10 @@ def lib():
         L.ds_last_error.restype = C.c_char_p
         L.ds_stack_state_bytes.argtypes = [i32]
         L.ds_stack_state_bytes.restype = C.c_size_t
-        L.ds_stack_create.argtypes = [C.POINTER(vp), C.POINTER(KVCacheC), i32, i32, vp, C.c_size_t, C.POINTER(vp)]
+        L.ds_stack_create.argtypes = [C.POINTER(vp), C.POINTER(KVCacheC), i32, i32, C.POINTER(LmHeadC), vp,
+                                      C.c_size_t, C.POINTER(vp)]
+        L.ds_stack_forward_generate.argtypes = [vp, vp, vp, vp, vp, i32, vp, C.c_size_t, vp]
+        L.ds_stack_forward_generate.restype = C.c_int
         L.ds_stack_destroy.argtypes = [vp]
         L.ds_stack_workspace_bytes.argtypes = [vp, i32]
         L.ds_stack_workspace_bytes.restype = C.c_size_t

@@ -7,6 +7,12 @@
 
 namespace ds {
 
+// The LM head at the end of a stack: final LayerNorm parameters and the [V][H] weight (borrowed).
+struct StackHead {
+  const void *ln_g, *ln_b, *w, *s;
+  int V;
+};
+
 // One layer as the persistent kernel sees it: weights (borrowed) and its bound KV cache.
 struct StackLayer {
   const void *ln1_g, *ln1_b, *w_qkv, *b_qkv, *s_qkv, *w_o, *b_o, *s_o;
@@ -22,12 +28,17 @@ struct StackLayer {
 // tags it needs are current. kSyncLaunch holds the launch counter (seeded per stack, advanced by the
 // last workgroup out, kLaunchBits wide); kSyncExit counts finished workgroups; kSyncError is raised
 // by any wait that timed out, and a launch that finds it raised leaves before any store.
+// kSyncArgmax holds the greedy-decoding keys of the LM head: two slots (launch parity) of
+// kStackMaxBatch 64-bit keys; a launch takes the slot of its counter's parity and clears the other
+// for the next launch.
 constexpr int kSyncLine = 64;
+constexpr int kStackMaxBatch = 4;
 enum {
   kSyncLaunch = 0,
   kSyncExit = kSyncLine,
   kSyncError = 2 * kSyncLine,
-  kSyncWords = 3 * kSyncLine,
+  kSyncArgmax = 3 * kSyncLine,
+  kSyncWords = 4 * kSyncLine,
 };
 constexpr uint32_t kSyncBytes = kSyncWords * 4;  // the layer table follows (256-byte aligned)
 constexpr int kLaunchBits = 19;
@@ -80,6 +91,7 @@ __host__ __device__ inline uint32_t stack_align(uint32_t v) { return (v + 255u) 
 // of the merge), which is never live at the same time as staged activations.
 __host__ __device__ inline StackLds stack_lds_layout(int wsize, int bm, int H, int F, int rows_per_wg, int nchunk,
                                                      int D, int group, int n_layers) {
+  // the weight table holds 4 entries per layer and one for the LM head
   StackLds L{};
   const uint32_t lt = wsize == 4 ? 4u : 2u;
   const uint32_t kmax = (uint32_t)(H > F ? H : F);
@@ -93,7 +105,7 @@ __host__ __device__ inline StackLds stack_lds_layout(int wsize, int bm, int H, i
   L.scales = stack_align(L.slots + (uint32_t)rows_per_wg * kStackWorkers * bm * 4u);
   const uint32_t sc = wsize == 1 ? (uint32_t)rows_per_wg * (kmax / (uint32_t)group) * 2u : 0u;
   L.wtab = stack_align(L.scales + sc);
-  L.layers = stack_align(L.wtab + (uint32_t)n_layers * 4u * 8u);
+  L.layers = stack_align(L.wtab + ((uint32_t)n_layers * 4u + 1u) * 8u);
   L.lens = stack_align(L.layers + (uint32_t)n_layers * (uint32_t)sizeof(StackLayer));
   L.res = stack_align(L.lens + (uint32_t)n_layers * 4u * 4u);
   L.res_n = (uint32_t)rows_per_wg * (uint32_t)bm;
@@ -118,16 +130,22 @@ struct StackArgs {
   uint2* ctx;      // [B][H]
   uint2* x2;       // [B][H]
   uint2* f;        // [B][F]
-  uint2* ybuf;     // [B][H] layer outputs except the last
+  uint2* ybuf;     // [B][H] layer outputs (the last one only when the LM head runs)
   uint32_t* sync;  // kSync* words
+  // the LM head (V == 0: none); head != 0: this launch runs it after the last layer
+  int head, V;
+  const void *head_g, *head_b, *head_w, *head_s;
+  float* logits;    // [B][V] fp32, or null
+  int32_t* tokens;  // [B] greedy choices
   int G;           // workgroups (all co-resident)
   int nchunk;      // attention chunks of kStackChunk rows over the capacity
   StackLds lds;
   uint64_t timeout_ticks;  // per wait, in 100 MHz wall-clock ticks
 };
 
-// The largest per-workgroup row tile among the four projections for a grid of G workgroups.
-int stack_rows_per_wg(int H, int F, int G);
+// The largest per-workgroup row tile among the four projections (and the LM head's V rows) for a
+// grid of G workgroups.
+int stack_rows_per_wg(int H, int F, int V, int G);
 hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups);
 hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, hipStream_t st);
 

@@ -105,7 +105,8 @@ struct Ctl {
   uint32_t launch;       // launch counter (tags of this launch)
   float red[NS][8];      // LayerNorm sums: (sum, sum of squares) for up to 4 rows, per wave
   float m[NS], l[NS];    // attention: per-wave max and sum
-  int tab[NWK][4][8];    // per worker and phase: the block geometry (see worker_table)
+  int tab[NWK][5][8];    // per worker and phase (4: the LM head): the block geometry (see worker_table)
+  uint64_t best[kStackMaxBatch];  // LM head: this workgroup's largest argmax key per sequence
 };
 
 // Fields of a worker's phase-table entry.
@@ -299,9 +300,9 @@ __device__ __forceinline__ bool poll_lane(Ctl& c, const StackArgs& a, rsrc_t r, 
 }
 
 // ------------------------------------------------------------------ row tiles
-// Phase ph (0 QKV, 1 O, 2 FF1, 3 FF2) of workgroup g: rows [r0, r0+nr) of the [N][K] matrix, one
-// contiguous range of nr*K elements cut into slices of SL elements (K is a multiple of SL), so
-// slice s lies in tile row s / (K/SL). Worker w owns the contiguous block [s0, s0+cnt).
+// Phase ph (0 QKV, 1 O, 2 FF1, 3 FF2, 4 the LM head) of workgroup g: rows [r0, r0+nr) of the [N][K]
+// matrix, one contiguous range of nr*K elements cut into slices of SL elements (K is a multiple of
+// SL), so slice s lies in tile row s / (K/SL). Worker w owns the contiguous block [s0, s0+cnt).
 struct Geo {
   int N, K, r0, nr, s0, cnt;
 };
@@ -309,7 +310,7 @@ struct Geo {
 __device__ __forceinline__ Geo phase_geo(const StackArgs& a, int SL, int g, int w, int ph) {
   const int H = a.H, F = a.F, G = a.G;
   Geo p;
-  p.N = ph == 0 ? 3 * H : (ph == 2 ? F : H);
+  p.N = ph == 0 ? 3 * H : (ph == 2 ? F : (ph == 4 ? a.V : H));
   p.K = ph == 3 ? F : H;
   const int rows = stack_tile_rows(p.N, G, ph == 2);
   p.r0 = min(p.N, g * rows);
@@ -336,12 +337,12 @@ __device__ __forceinline__ void flush_rows(float (&acc)[BM], float* slots, int r
   }
 }
 
-// Lane p (0..3) of worker w fills the table entry of phase p: slice count, byte offset of the
+// Lane p (0..4) of worker w fills the table entry of phase p: slice count, byte offset of the
 // block's first slice in the matrix, matrix bytes, K, slices per row, first row and slice-in-row.
 template <typename WT>
 __device__ __forceinline__ void worker_table(const StackArgs& a, Ctl& c, int g, int w, int lane) {
   constexpr int SL = kWave * WTraits<WT>::E;
-  if (lane < 4) {
+  if (lane < 5) {
     const Geo p = phase_geo(a, SL, g, w, lane);
     int* t = c.tab[w][lane];
     const int sper = p.K / SL;
@@ -360,9 +361,10 @@ __device__ __forceinline__ int tab_ld(const Ctl& c, int w, int ph, int f) {
   return __builtin_amdgcn_readfirstlane(c.tab[w][ph][f]);
 }
 
-// Weight-matrix pointer of (layer, phase) from the LDS table, made wave-uniform.
-__device__ __forceinline__ const void* wtab_ld(const uint64_t* wtab, int l, int ph) {
-  const uint64_t u = wtab[l * 4 + ph];
+// Weight-matrix pointer of step p (layer p / 4, phase p % 4; p = 4 L is the LM head) from the LDS
+// table, made wave-uniform.
+__device__ __forceinline__ const void* wtab_ld(const uint64_t* wtab, int p) {
+  const uint64_t u = wtab[p];
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
   return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
@@ -375,48 +377,46 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
   constexpr int E = WTraits<WT>::E, SL = kWave * E;
   constexpr int kRing = Ring<WT, BM>::value;
   constexpr uint32_t SLB = (uint32_t)(SL * sizeof(WT));  // bytes of one slice
+  // The worker's steps: p = 4 l + ph for the four projections of layer l, then p = 4 L for the LM
+  // head when this launch runs it; gi(p) names the step's entry in the phase table.
   const int L = a.n_layers;
+  const int P = 4 * L + (a.head ? 1 : 0);
+  auto gi = [&](int p) { return p < 4 * L ? (p & 3) : 4; };
   worker_table<WT>(a, c, g, w, lane);
   const int per_layer = tab_ld(c, w, 0, T_CNT) + tab_ld(c, w, 1, T_CNT) + tab_ld(c, w, 2, T_CNT) + tab_ld(c, w, 3, T_CNT);
-  const int total = L * per_layer;
+  const int total = L * per_layer + (a.head ? tab_ld(c, w, 4, T_CNT) : 0);
 
-  // issue cursor: the next slice to load (layer il, phase iph, slice is of icnt)
-  int il = 0, iph = 0, is = 0, icnt = tab_ld(c, w, 0, T_CNT);
-  while (il < L && icnt == 0) {
-    if (++iph == 4) {
-      iph = 0;
-      ++il;
-    }
-    icnt = tab_ld(c, w, iph, T_CNT);
+  // issue cursor: the next slice to load (step ip, slice is of icnt)
+  int ip = 0, is = 0, icnt = tab_ld(c, w, 0, T_CNT);
+  while (ip < P && icnt == 0) {
+    ++ip;
+    icnt = ip < P ? tab_ld(c, w, gi(ip), T_CNT) : 0;
   }
-  const void* iw = wtab_ld(wtab, il < L ? il : 0, il < L ? iph : 0);
-  uint32_t ibytes = (uint32_t)tab_ld(c, w, iph, T_BYTES);
-  uint32_t ioff = (uint32_t)tab_ld(c, w, iph, T_BASE);
+  const void* iw = wtab_ld(wtab, ip < P ? ip : 0);
+  uint32_t ibytes = (uint32_t)tab_ld(c, w, ip < P ? gi(ip) : 0, T_BYTES);
+  uint32_t ioff = (uint32_t)tab_ld(c, w, ip < P ? gi(ip) : 0, T_BASE);
   const uint32_t voff = (uint32_t)(lane * 16);
 
-  // consume cursor: the next slice to multiply (layer cl, phase cph, slice cs of ccnt)
-  int cl = 0, cph = 0, cs = 0, ccnt = tab_ld(c, w, 0, T_CNT);
+  // consume cursor: the next slice to multiply (step cp, slice cs of ccnt)
+  int cp = 0, cs = 0, ccnt = tab_ld(c, w, 0, T_CNT);
   int K = tab_ld(c, w, 0, T_K), Sper = tab_ld(c, w, 0, T_SPER);
   int rl = tab_ld(c, w, 0, T_RL0), ks = tab_ld(c, w, 0, T_KS0);
   bool wait_act = true;
-  // leave phase (cl, cph) [finished or empty], publishing it, and move to the next non-empty one
+  // leave step cp [finished or empty], publishing it, and move to the next non-empty one
   auto c_advance = [&]() {
     for (;;) {
       wait_lgkm0();  // this wave's slot writes are in LDS before the flag says so
-      if (lane == 0) lds_st(&c.done[w], (uint32_t)(cl * 4 + cph + 1));
-      if (++cph == 4) {
-        cph = 0;
-        ++cl;
-      }
-      if (cl >= L) return;
-      ccnt = tab_ld(c, w, cph, T_CNT);
+      if (lane == 0) lds_st(&c.done[w], (uint32_t)(cp + 1));
+      if (++cp >= P) return;
+      ccnt = tab_ld(c, w, gi(cp), T_CNT);
       if (ccnt > 0) break;
     }
+    const int t = gi(cp);
     cs = 0;
-    K = tab_ld(c, w, cph, T_K);
-    Sper = tab_ld(c, w, cph, T_SPER);
-    rl = tab_ld(c, w, cph, T_RL0);
-    ks = tab_ld(c, w, cph, T_KS0);
+    K = tab_ld(c, w, t, T_K);
+    Sper = tab_ld(c, w, t, T_SPER);
+    rl = tab_ld(c, w, t, T_RL0);
+    ks = tab_ld(c, w, t, T_KS0);
     wait_act = true;
   };
   if (ccnt == 0) c_advance();
@@ -428,23 +428,20 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
   // issue one load: the next slice, or an out-of-range load (reads nothing) past the end
 #define DS_ISSUE(dst)                                                                            \
   {                                                                                              \
-    const bool live = il < L;                                                                    \
+    const bool live = ip < P;                                                                    \
     const rsrc_t r = make_rsrc(iw, ibytes);                                                      \
     dst = __builtin_amdgcn_raw_buffer_load_b128(r, voff, live ? ioff : kOutOfRange, kAuxStream); \
     ioff += SLB;                                                                                 \
     if (live && ++is >= icnt) {                                                                  \
       is = 0;                                                                                    \
       do {                                                                                       \
-        if (++iph == 4) {                                                                        \
-          iph = 0;                                                                               \
-          ++il;                                                                                  \
-        }                                                                                        \
-        icnt = tab_ld(c, w, iph, T_CNT);                                                         \
-      } while (il < L && icnt == 0);                                                             \
-      if (il < L) {                                                                              \
-        iw = wtab_ld(wtab, il, iph);                                                             \
-        ibytes = (uint32_t)tab_ld(c, w, iph, T_BYTES);                                           \
-        ioff = (uint32_t)tab_ld(c, w, iph, T_BASE);                                              \
+        ++ip;                                                                                    \
+        icnt = ip < P ? tab_ld(c, w, gi(ip), T_CNT) : 0;                                         \
+      } while (ip < P && icnt == 0);                                                             \
+      if (ip < P) {                                                                              \
+        iw = wtab_ld(wtab, ip);                                                                  \
+        ibytes = (uint32_t)tab_ld(c, w, gi(ip), T_BYTES);                                        \
+        ioff = (uint32_t)tab_ld(c, w, gi(ip), T_BASE);                                           \
       }                                                                                          \
     }                                                                                            \
   }
@@ -464,7 +461,7 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
         cs = __builtin_amdgcn_readfirstlane(cs);
         wait_vm_at_most<kRing - 1>();  // exactly kRing loads are in flight: the oldest has landed
         if (wait_act) {
-          const uint32_t need = (uint32_t)(cl * 4 + cph + 1);
+          const uint32_t need = (uint32_t)(cp + 1);
           ok = worker_spin(c, a, [&] { return lds_ld(&c.act_ready) >= need; });
           wait_act = false;
         }
@@ -1030,21 +1027,68 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
         const float z = row_sum(rl, b) + (t == st ? pre_y : ldp<AT>(L.b_ff2, n));
         const float v = (float)(AT)(res_x2[t] + z);
         res_y[t] = v;
-        if (last)
-          coh_st_act<AT>(ry, (uint32_t)(b * H + n), v);
-        else
-          tstore(ryt, (uint32_t)(b * H + n), v, t_y);
+        if (last) coh_st_act<AT>(ry, (uint32_t)(b * H + n), v);
+        if (!last || a.head) tstore(ryt, (uint32_t)(b * H + n), v, t_y);
       }
     }
   }
 
+  // ---- the LM head: final LayerNorm of the last layer's output, logits = W_vocab h, greedy choice
+  uint64_t* keys = reinterpret_cast<uint64_t*>(a.sync + kSyncArgmax) + (launch & 1u) * kStackMaxBatch;
+  if (a.head) {
+    fresh();
+    const int rv = stack_tile_rows(a.V, G, false);
+    const int v0 = min(a.V, g * rv), nv = min(a.V, v0 + rv) - v0;
+    if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
+    clear_slots(nv);
+    if constexpr (sizeof(WT) == 1) stage_scales(a.head_s, v0, nv, H, a.group, scl, st);
+    const uint32_t t_last = stack_tag(launch, a.n_layers - 1, TAG_Y);
+    if (!stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)a.head_g, (const AT*)a.head_b, act, raw, gb, st, [&]() {
+          return poll_range(c, a, a.ybuf, B * H, t_last, st, [&](int i, float v) { raw[i] = v; });
+        }))
+      return;
+    if (!hand_over(4u * (uint32_t)a.n_layers)) return;
+    // each logit as a 64-bit key that orders like (value, -index): the order-preserving bits of the
+    // float above the inverted row index, so the largest key is the largest logit at its smallest
+    // index (both zeros count as +0)
+    uint64_t best[BM];
+#pragma unroll
+    for (int b = 0; b < BM; ++b) best[b] = 0ull;
+    for (int t = st; t < nv * B; t += NT) {
+      const int rl = t / B, b = t - rl * B, n = v0 + rl;
+      const float z = row_sum(rl, b);
+      if (a.logits) a.logits[(size_t)b * a.V + n] = z;
+      const uint32_t u = z == 0.f ? 0u : __builtin_bit_cast(uint32_t, z);
+      const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      const uint64_t key = ((uint64_t)ord << 32) | (uint64_t)(0xffffffffu - (uint32_t)n);
+#pragma unroll
+      for (int bb = 0; bb < BM; ++bb)
+        if (bb == b && key > best[bb]) best[bb] = key;
+    }
+    // the workgroup's largest key per sequence (LDS atomics), then one device atomic per sequence
+    if (st < BM) c.best[st] = 0ull;
+    if (!sync_bar(c, a, sb, st)) return;
+#pragma unroll
+    for (int b = 0; b < BM; ++b)
+      if (b < B && best[b] != 0ull) __hip_atomic_fetch_max(&c.best[b], best[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (!sync_bar(c, a, sb, st)) return;
+    if (st < B && nv > 0)
+      (void)__hip_atomic_fetch_max(keys + st, c.best[st], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
   // every store of this workgroup is complete; the last workgroup out advances the cache lengths
-  // (every other one has finished reading them) and the launch counter
+  // (every other one has finished reading them) and the launch counter, and hands out the greedy
+  // choices (every workgroup's argmax key is in, each added before its workgroup counted itself out)
   wait_vm_at_most<0>();
   if (!sync_bar(c, a, sb, st)) return;
   if (st == 0) {
     const uint32_t out = __hip_atomic_fetch_add(a.sync + kSyncExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (out == (uint32_t)G - 1) {
+      if (a.head)
+        for (int b = 0; b < B; ++b) {
+          const uint64_t key = __hip_atomic_load(keys + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          a.tokens[b] = (int32_t)(0xffffffffu - (uint32_t)key);
+        }
       for (int l = 0; l < a.n_layers; ++l)
         for (int b = 0; b < B; ++b) {
           int32_t* dl = a.layers[l].d_len + b;
@@ -1067,6 +1111,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
   uint64_t* wtab = reinterpret_cast<uint64_t*>(smem + a.lds.wtab);
   for (int i = threadIdx.x; i < a.n_layers * 4; i += kStackThreads)
     wtab[i] = reinterpret_cast<uint64_t>(phase_w(a.layers[i >> 2], i & 3));
+  if (threadIdx.x == 0) wtab[a.n_layers * 4] = reinterpret_cast<uint64_t>(a.head_w);
   // The layer table and the cache lengths in LDS: the sync waves read them inside their chain,
   // where a global load would wait behind the CU's queue of weight loads.
   static_assert(sizeof(StackLayer) % 4 == 0, "layer table in words");
@@ -1090,6 +1135,12 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
   }
   __syncthreads();
   if (c.abort != 0u) return;
+  // the argmax keys of the next launch (the other parity) start at zero; no workgroup of this
+  // launch touches them
+  if (blockIdx.x == 0 && threadIdx.x < kStackMaxBatch) {
+    uint64_t* next = reinterpret_cast<uint64_t*>(a.sync + kSyncArgmax) + ((c.launch + 1u) & 1u) * kStackMaxBatch;
+    __hip_atomic_store(next + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   if (wave < NS) {
@@ -1104,10 +1155,11 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
 }
 
 // ------------------------------------------------------------------ host-side launch helpers
-int stack_rows_per_wg(int H, int F, int G) {
+int stack_rows_per_wg(int H, int F, int V, int G) {
   int r = (3 * H + G - 1) / G;
   r = max(r, (H + G - 1) / G);
   r = max(r, stack_tile_rows(F, G, true));
+  r = max(r, stack_tile_rows(V, G, false));
   return r;
 }
 

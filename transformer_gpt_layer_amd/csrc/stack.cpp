@@ -23,6 +23,7 @@ struct ds_stack {
   std::vector<ds_kv_cache> caches;
   int n_layers = 0, max_batch = 0, G = 0, nchunk = 0, device = 0;
   uint64_t uid = 0;  // never reused: names this stack in the workspace registry
+  ds::StackHead head{};                 // V == 0: no LM head
   ds::StackLayer* d_layers = nullptr;  // inside the caller's state buffer
   uint32_t* d_sync = nullptr;          // the state buffer's first kSyncBytes
   size_t sync_words = 0;
@@ -86,7 +87,8 @@ int static_scratch(void** out) {
   return DS_OK;
 }
 
-int stack_forward(ds_stack_t* S, const void* x, void* y, int32_t batch, void* ws, size_t ws_bytes, void* stream);
+int stack_forward(ds_stack_t* S, const void* x, void* y, float* logits, int32_t* tokens, bool head, int32_t batch,
+                  void* ws, size_t ws_bytes, void* stream);
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
@@ -146,7 +148,8 @@ size_t ds_stack_state_bytes(int32_t n_layers) {
 }
 
 int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, int32_t n_layers,
-                    int32_t max_batch, void* state, size_t state_bytes, ds_stack_t** out) {
+                    int32_t max_batch, const ds_lm_head* head, void* state, size_t state_bytes,
+                    ds_stack_t** out) {
   if (!layers || !caches || !out) return ds::set_error(DS_ERR_NULL, "layers, caches or out is NULL");
   *out = nullptr;
   if (n_layers < 1) return ds::set_error(DS_ERR_SHAPE, "n_layers %d < 1", n_layers);
@@ -182,6 +185,15 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
       return ds::set_error(DS_ERR_UNSUPPORTED, "cache %d is 2 GiB or larger", l);
   }
 
+  if (head) {
+    if (!head->ln_g || !head->ln_b || !head->w) return ds::set_error(DS_ERR_NULL, "LM head ln_g, ln_b or w is NULL");
+    if (!aligned16(head->ln_g) || !aligned16(head->ln_b) || !aligned16(head->w))
+      return ds::set_error(DS_ERR_ALIGN, "an LM head pointer is not 16-byte aligned");
+    if ((d.weight_dtype == DS_I8) != (head->s != nullptr) || (head->s && !aligned16(head->s)))
+      return ds::set_error(DS_ERR_DTYPE, "LM head scales: required (16-byte aligned) for int8 weights, NULL otherwise");
+    if (head->vocab < 1 || (size_t)head->vocab * d.hidden * wsz >= (1ull << 31))
+      return ds::set_error(DS_ERR_SHAPE, "LM head vocab %d must be >= 1 with its weights under 2 GiB", head->vocab);
+  }
   ds_stack* S = new (std::nothrow) ds_stack;
   if (!S) return ds::set_error(DS_ERR_NULL, "out of host memory");
   S->desc = d;
@@ -189,6 +201,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
   S->n_layers = n_layers;
   S->max_batch = max_batch;
   S->nchunk = (caches[0].capacity + ds::kStackChunk - 1) / ds::kStackChunk;
+  if (head) S->head = ds::StackHead{head->ln_g, head->ln_b, head->w, head->s, head->vocab};
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
   hipError_t e = hipGetDevice(&S->device);
   int cus = 0;
@@ -197,7 +210,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
   const int bm = max_batch <= 1 ? 1 : 4;
   int G = cus;  // one workgroup of kStackThreads per CU
   for (int iter = 0; e == hipSuccess && iter < 3; ++iter) {
-    const ds::StackLds lay = ds::stack_lds_layout(wsz_i, bm, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, G),
+    const ds::StackLds lay = ds::stack_lds_layout(wsz_i, bm, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->head.V, G),
                                                   S->nchunk, d.head_dim, d.quant_group, n_layers);
     if (lay.total > (uint32_t)ds::kStackLdsMax - 4096u) {  // the static control block takes the rest
       delete S;
@@ -262,7 +275,17 @@ int32_t ds_stack_groups(const ds_stack_t* S) { return S ? S->G : 0; }
 
 int ds_stack_forward_decode(ds_stack_t* S, const void* x, void* y, int32_t batch, void* ws, size_t ws_bytes,
                             void* stream) {
-  return stack_forward(S, x, y, batch, ws, ws_bytes, stream);
+  return stack_forward(S, x, y, nullptr, nullptr, false, batch, ws, ws_bytes, stream);
+}
+
+int ds_stack_forward_generate(ds_stack_t* S, const void* x, void* y, float* logits, int32_t* tokens, int32_t batch,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (!S) return ds::set_error(DS_ERR_NULL, "stack is NULL");
+  if (S->head.V < 1) return ds::set_error(DS_ERR_UNSUPPORTED, "this stack was created without an LM head");
+  if (!tokens) return ds::set_error(DS_ERR_NULL, "tokens is NULL");
+  if (!aligned16(tokens) || (logits && !aligned16(logits)))
+    return ds::set_error(DS_ERR_ALIGN, "tokens or logits is not 16-byte aligned");
+  return stack_forward(S, x, y, logits, tokens, true, batch, ws, ws_bytes, stream);
 }
 
 int ds_stack_forward_decode_static(ds_stack_t* S, const void* x, void* y, int32_t batch, void* stream) {
@@ -274,14 +297,15 @@ int ds_stack_forward_decode_static(ds_stack_t* S, const void* x, void* y, int32_
                          kStaticScratch);
   void* ws = nullptr;
   if (int rc = static_scratch(&ws)) return rc;
-  return stack_forward(S, x, y, batch, ws, kStaticScratch, stream);
+  return stack_forward(S, x, y, nullptr, nullptr, false, batch, ws, kStaticScratch, stream);
 }
 
 }  // extern "C"
 
 namespace {
 
-int stack_forward(ds_stack_t* S, const void* x, void* y, int32_t batch, void* ws, size_t ws_bytes, void* stream) {
+int stack_forward(ds_stack_t* S, const void* x, void* y, float* logits, int32_t* tokens, bool head, int32_t batch,
+                  void* ws, size_t ws_bytes, void* stream) {
   if (!S) return ds::set_error(DS_ERR_NULL, "stack is NULL");
   if (batch < 1 || batch > S->max_batch) return ds::set_error(DS_ERR_SHAPE, "batch %d outside [1, %d]", batch, S->max_batch);
   if (!x || !y || !ws) return ds::set_error(DS_ERR_NULL, "x, y or workspace is NULL");
@@ -324,9 +348,17 @@ int stack_forward(ds_stack_t* S, const void* x, void* y, int32_t batch, void* ws
   a.G = S->G;
   a.nchunk = S->nchunk;
   a.timeout_ticks = S->timeout_ticks;
+  a.head = head ? 1 : 0;
+  a.V = S->head.V;
+  a.head_g = S->head.ln_g;
+  a.head_b = S->head.ln_b;
+  a.head_w = S->head.w;
+  a.head_s = S->head.s;
+  a.logits = logits;
+  a.tokens = tokens;
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
   const int wsz_i = d.weight_dtype == DS_F32 ? 4 : (d.weight_dtype == DS_F16 ? 2 : 1);
-  a.lds = ds::stack_lds_layout(wsz_i, batch <= 1 ? 1 : 4, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->G),
+  a.lds = ds::stack_lds_layout(wsz_i, batch <= 1 ? 1 : 4, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->head.V, S->G),
                                S->nchunk, d.head_dim, d.quant_group, S->n_layers);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (int rc = prepare_workspace(*S, ws, W.total, st)) return rc;
@@ -355,6 +387,7 @@ int ds_stack_check(ds_stack_t* S) {
     words[ds::kSyncError] = 0u;
     words[ds::kSyncExit] = 0u;
     words[ds::kSyncLaunch] = (words[ds::kSyncLaunch] + 1u) & ds::kLaunchMask;
+    for (int i = 0; i < 4 * ds::kStackMaxBatch; ++i) words[ds::kSyncArgmax + i] = 0u;  // both key slots
     (void)hipMemcpy(S->d_sync, words.data(), S->sync_words * 4, hipMemcpyHostToDevice);
     // the host mirrors were advanced when the failed steps were enqueued; the device lengths were
     // not (only a completed launch advances them): take the device's
