@@ -1,17 +1,22 @@
-"""Decode throughput of the fused GPT-layer stack on one MI355X (and, with --config c5, prefill).
+"""Decode throughput of the fused GPT-layer stack on one MI355X, with nested records for the other
+workloads of the metric (batch 8 fp16 and int8, int8 batch 1, the generation step with the LM head,
+and prefill).
 
-One step = one decode token for every sequence of the batch through all L layers of the stack
+One decode step = one new token for every sequence of the batch through all L layers of the stack
 (LN1+QKV, attention over the KV cache, output projection, LN2+FF1+GeLU, FF2), starting from the
 same cache lengths each step. Weights and caches are seeded synthetic tensors resident in HBM
 (distinct per layer, so weights stream from HBM rather than the 256 MB last-level cache).
 
-Prints one JSON line: decode tokens/s and the achieved HBM GB/s per layer step (against the
-8 TB/s peak), the roofline entry of the dominant kernel, and the CPU oracle's throughput on a
-bounded sample of the same workload.
+Prints one JSON line. Its top level is the headline workload (GPT-Neo-2.7B shapes, fp16, batch 1,
+512 past rows, 32 layers): decode tokens/s, achieved HBM GB/s per layer step, the roofline entry of
+the dominant kernel (timed with HIP events on the stream it runs on), and the oracle's throughput on
+a bounded sample of the same workload, on one host thread and on all host cores. `records` holds the
+same fields for the other workloads.
 """
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -19,11 +24,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0
+METRIC = "decode tokens/s at batch 1/8 + achieved HBM GB/s (% of peak) per layer step"
 
 # HBM traffic of a kernel as counted by rocprofv3 (FETCH_SIZE and WRITE_SIZE, each scaled by what
 # the same counter reads for a copy of known size) is recorded in a profile summary together with
-# the SHA-256 of the kernel's source file; the figure is reported only while that source is
-# unchanged.
+# the SHA-256 of the kernel's source files; the figure is reported only while they are unchanged.
 TRAFFIC_RECORDS = {
     "stack_decode_kernel": ("profiles/stack_decode_kernel_c2_f16_b1.md",
                             ("transformer_gpt_layer_amd/csrc/kernels_stack.hip", "transformer_gpt_layer_amd/csrc/ds_stack.hpp")),
@@ -41,7 +47,6 @@ def measured_traffic(kernel: str, workload: str):
     sources = [os.path.join(ROOT, p) for p in sources]
     if not (os.path.exists(summary) and all(os.path.exists(p) for p in sources)):
         return None
-    # the record holds for exactly these kernel sources (the files concatenated, in this order)
     digest = hashlib.sha256(b"".join(open(p, "rb").read() for p in sources)).hexdigest()
     for line in open(summary):
         m = re.match(r"traffic-record: (\{.*\})\s*$", line.strip())
@@ -91,26 +96,61 @@ def copy_calibration(torch, gib: int = 1):
     print(json.dumps({"copy_calibration_bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4, "copies": 3}))
 
 
-def algorithmic_bytes_per_layer(wl) -> dict:
-    """Bytes one layer step must move at least once (weights and scales, biases and LayerNorm
-    vectors, the past K/V rows read, the new K/V rows written, x read and y written)."""
-    H, F, B, P, T = wl.hidden, wl.ffn, wl.batch, wl.past, wl.seq
+# ------------------------------------------------------------------ algorithmic work
+def _sizes(wl):
     a = 4 if wl.act_dtype == "f32" else 2
-    nw = 3 * H * H + H * H + 2 * H * F
-    if wl.weight_dtype == "i8":
-        wbytes = nw + (nw // wl.group) * 2
-    else:
-        wbytes = nw * (4 if wl.weight_dtype == "f32" else 2)
+
+    def wbytes(n, k):
+        if wl.weight_dtype == "i8":
+            return n * k + (n * k // wl.group) * 2
+        return n * k * (4 if wl.weight_dtype == "f32" else 2)
+    return a, wbytes
+
+
+def part_bytes(wl) -> dict:
+    """Bytes each kernel of one decode layer step must move at least once: its weights (and scales),
+    biases and LayerNorm vectors, the past K/V rows it reads, the new K/V rows it writes, x read by
+    the first and y written by the last. Intermediates between kernels are not counted."""
+    H, F, B, P, T = wl.hidden, wl.ffn, wl.batch, wl.past, wl.seq
+    a, wb = _sizes(wl)
+    return {"ln1": B * T * H * a + 2 * H * a, "qkv": wb(3 * H, H) + 3 * H * a + 2 * B * T * H * a,
+            "attn": 2 * B * P * H * a, "o": wb(H, H) + H * a, "ln2": 2 * H * a, "ff1": wb(F, H) + F * a,
+            "ff2": wb(H, F) + H * a + B * T * H * a, "len": 0}
+
+
+def algorithmic_bytes_per_layer(wl) -> dict:
+    """Bytes one layer step must move at least once (the sum over its kernels of part_bytes)."""
+    H, F, B, P, T = wl.hidden, wl.ffn, wl.batch, wl.past, wl.seq
+    a, wb = _sizes(wl)
+    weights = wb(3 * H, H) + wb(H, H) + wb(F, H) + wb(H, F)
     small = (3 * H + H + F + H + 4 * H) * a
-    kv_read = 2 * B * P * H * a
-    kv_write = 2 * B * T * H * a
-    xy = 2 * B * T * H * a
-    return {"weights": wbytes, "small": small, "kv_read": kv_read, "kv_write": kv_write, "xy": xy,
-            "total": wbytes + small + kv_read + kv_write + xy}
+    kv_read, kv_write, xy = 2 * B * P * H * a, 2 * B * T * H * a, 2 * B * T * H * a
+    total = weights + small + kv_read + kv_write + xy
+    assert total == sum(part_bytes(wl).values())
+    return {"weights": weights, "small": small, "kv_read": kv_read, "kv_write": kv_write, "xy": xy, "total": total}
 
 
+def head_bytes(wl, vocab) -> int:
+    """The LM head's bytes per generation step: its weight (and scales), the final LayerNorm
+    vectors, the last layer's output read and the fp32 logits written."""
+    a, wb = _sizes(wl)
+    return wb(vocab, wl.hidden) + 2 * wl.hidden * a + wl.batch * wl.hidden * a + wl.batch * vocab * 4
+
+
+def prefill_flops(wl) -> dict:
+    """Algorithmic FLOPs of one prefill layer step: the four weight GEMMs (2 M N K each, M = B S)
+    and causal attention (QK^T and PV over the visible keys only: S (S+1) / 2 per sequence and
+    head, 2 d FLOPs each for the two products)."""
+    H, F, B, S, nh, d = wl.hidden, wl.ffn, wl.batch, wl.seq, wl.heads, wl.head_dim
+    M = B * S
+    g = {"qkv": 2 * M * 3 * H * H, "o": 2 * M * H * H, "ff1": 2 * M * F * H, "ff2": 2 * M * H * F}
+    attn = 2 * 2 * d * nh * B * (S * (S + 1) // 2)
+    return {**g, "attn": attn, "gemm_total": sum(g.values()), "total": sum(g.values()) + attn}
+
+
+# ------------------------------------------------------------------ building a stack
 def build_stack(wl, torch, tg, syn, layers):
-    """Device weights, caches (P seeded rows each) and one shared workspace."""
+    """Device weights and caches (P seeded rows each) for every layer, one [L, B] length tensor."""
     dev = "cuda"
     act = torch.float32 if wl.act_dtype == "f32" else torch.float16
     cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
@@ -139,68 +179,270 @@ def build_stack(wl, torch, tg, syn, layers):
         stack.append(layer)
         kvs.append(kv)
     torch.cuda.synchronize()
-    ws = stack[0].workspace(wl.batch, 1, wl.capacity)
-    return stack, kvs, lens, ws, act
+    return stack, kvs, lens, act
 
 
-PEAK_F16_TFLOPS = 2500.0
+def gpu_head(wl, vocab, torch, tg, syn):
+    act = torch.float32 if wl.act_dtype == "f32" else torch.float16
+    h32 = syn.lm_head_f32(wl, vocab, "cuda")
+    head = {"ln_g": h32["ln_g"].to(act).contiguous(), "ln_b": h32["ln_b"].to(act).contiguous()}
+    if wl.weight_dtype == "i8":
+        head["w"], head["s"] = tg.quantize_i8(h32["w"].contiguous(), wl.group)
+    else:
+        head["w"] = h32["w"].to(act).contiguous()
+    return head
 
 
-def prefill_flops_per_layer(wl) -> dict:
-    """Algorithmic FLOPs of one prefill layer step: the four weight GEMMs (2 M N K each, M = B S)
-    and causal attention (QK^T and PV over the visible keys only: S (S+1) / 2 per sequence and
-    head, 2 d FLOPs each for the two products)."""
-    H, F, B, S, nh, d = wl.hidden, wl.ffn, wl.batch, wl.seq, wl.heads, wl.head_dim
-    M = B * S
-    g = {"qkv": 2 * M * 3 * H * H, "o": 2 * M * H * H, "ff1": 2 * M * F * H, "ff2": 2 * M * H * F}
-    attn = 2 * 2 * d * nh * B * (S * (S + 1) // 2)
-    return {**g, "attention": attn, "gemm_total": sum(g.values()), "total": sum(g.values()) + attn}
+# ------------------------------------------------------------------ timing
+def time_launches(torch, stream, launch, reset, steps, warmup):
+    """Run launch() warmup + steps times on `stream` (reset() before each), with an event pair
+    around every launch: (mean ms over the timed region, per-launch ms)."""
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            reset()
+            launch()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(steps):
+            reset()
+            starts[i].record(stream)
+            launch()
+            ends[i].record(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, [a.elapsed_time(b) for a, b in zip(starts, ends)]
 
 
-def _oracle_weights(layer, wl):
+def time_graph(torch, stream, step, steps, warmup):
+    """Capture step() in a HIP graph and replay it: (mean ms over the timed region, per-step ms)."""
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(steps):
+            g.replay()
+            marks[i].record(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return ms, [(e0 if i == 0 else marks[i - 1]).elapsed_time(marks[i]) for i in range(steps)]
+
+
+def kernel_times(torch, stream, stack, kvs, lens, wl, x, reset, ws=None, reps=3):
+    """Per-kernel durations of the per-layer path: one layer step at a time with events between its
+    kernel launches (the library's ds_layer_time_kernels, on `stream`), on three layers spread over
+    the stack, `reps` times each; the median per kernel kind, in ms."""
+    L = len(stack)
+    got = {}
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            for l in sorted({0, L // 2, L - 1}):
+                reset()
+                for part, ms in stack[l].time_kernels(kvs[l], x, workspace=ws, stream=stream):
+                    got.setdefault(part, []).append(ms)
+    torch.cuda.synchronize()
+    return {k: statistics.median(v) for k, v in got.items()}
+
+
+# ------------------------------------------------------------------ the oracle on the host
+def _cpu_share():
+    """Host threads this run may use: the OMP_NUM_THREADS the box sets, else the CPU count (at
+    most 16, the share of one GPU)."""
+    n = int(os.environ.get("OMP_NUM_THREADS") or 0) or (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
+def _oracle_worker(job):
+    """One host process's share of the CPU baseline: oracle layer steps on the arrays in job (files
+    under /dev/shm, memory-mapped read-only) until target_s seconds of oracle time have run."""
+    import numpy as np
+
+    import oracle
+
+    w = {n: np.load(p, mmap_mode="r") for n, p in job["weights"].items()}
+    k = np.array(np.load(job["k"], mmap_mode="r"))
+    v = np.array(np.load(job["v"], mmap_mode="r"))
+    desc = oracle.Desc(*job["desc"])
+    rng = np.random.default_rng(job["seed"])
+    x = rng.standard_normal(tuple(job["x_shape"]))
+    done, spent = 0, 0.0
+    while spent < job["target_s"]:
+        lens = np.full(x.shape[0], job["past"], dtype=np.int32)
+        t0 = time.perf_counter()
+        # the layer overwrites rows past.. and advances a fresh copy of the lengths, so every step
+        # starts from the same cache
+        oracle.layer_forward(desc, w, k, v, lens, x)
+        spent += time.perf_counter() - t0
+        done += 1
+    return done, spent
+
+
+def cpu_baselines(wl, layer, kv, target_s: float, rows=None):
+    """The oracle (plain C, double, single-threaded) timed on a bounded sample of this workload:
+    whole layer steps of layer 0's weights and cache (decode: one new row per sequence; prefill:
+    `rows` prompt rows of one sequence), on one host thread and on every host thread of this run
+    (one process each, same sample), scaled to the full L-layer stack."""
+    import multiprocessing as mp
+
     import numpy as np
     import torch
 
     import oracle
 
-    w = {}
-    for n in ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b", "w_ff1", "b_ff1", "w_ff2", "b_ff2"):
-        t = layer._weights[n]
-        if n.startswith("w_") and wl.weight_dtype == "i8":
-            s = layer._weights["s" + n[1:]]
-            w[n] = oracle.dequantize_i8(t.cpu().numpy(), s.cpu().view(torch.int16).numpy().view(np.uint16), wl.group)
+    tag = f"/dev/shm/ds_bench_{os.getpid()}"
+    paths = {"weights": {}}
+    try:
+        for n in ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b", "w_ff1", "b_ff1", "w_ff2", "b_ff2"):
+            t = layer._weights[n]
+            if n.startswith("w_") and wl.weight_dtype == "i8":
+                s = layer._weights["s" + n[1:]].cpu().view(torch.int16).numpy().view(np.uint16)
+                arr = oracle.dequantize_i8(t.cpu().numpy(), s, wl.group)
+            else:
+                arr = t.double().cpu().numpy()
+            paths["weights"][n] = f"{tag}_{n}.npy"
+            np.save(paths["weights"][n], arr)
+            del arr
+        prefill = rows is not None
+        B = 1 if prefill else wl.batch
+        past = 0 if prefill else wl.past
+        shape = (B, wl.heads, wl.capacity, wl.head_dim)
+        k = np.zeros(shape)
+        v = np.zeros(shape)
+        if past:
+            k[:, :, :past] = kv.k[:B, :, :past].double().cpu().numpy()
+            v[:, :, :past] = kv.v[:B, :, :past].double().cpu().numpy()
+        paths["k"], paths["v"] = f"{tag}_k.npy", f"{tag}_v.npy"
+        np.save(paths["k"], k)
+        np.save(paths["v"], v)
+        del k, v
+        job = dict(paths, desc=(wl.hidden, wl.heads, wl.head_dim, wl.ffn), past=past, target_s=target_s,
+                   x_shape=(B, rows if prefill else 1, wl.hidden), seed=0)
+        done1, spent1 = _oracle_worker(job)
+        n = _cpu_share()
+        t0 = time.perf_counter()
+        with mp.get_context("spawn").Pool(n) as pool:
+            res = pool.map(_oracle_worker, [dict(job, seed=i) for i in range(n)])
+        wall = time.perf_counter() - t0
+    finally:
+        for p in list(paths["weights"].values()) + [paths.get("k"), paths.get("v")]:
+            if p and os.path.exists(p):
+                os.remove(p)
+    per_step_tokens = rows if prefill else wl.batch
+    unit = "prompt tokens/s" if prefill else "tokens/s"
+    what = (f"{rows} prompt rows of one sequence" if prefill else
+            f"one decode step of {wl.batch} sequences against {wl.past} past rows")
+    one = per_step_tokens * done1 / (spent1 * wl.layers)
+    steps_all = sum(d for d, _ in res)
+    longest = max(s for _, s in res)
+    allc = per_step_tokens * steps_all / (longest * wl.layers)
+    return ({"value": round(one, 4), "unit": unit, "cores": 1, "kind": "oracle",
+             "sample": f"{done1} oracle layer steps ({what}, layer 0 of {wl.name}) in {spent1:.1f} s on one host "
+                       f"thread, scaled to the {wl.layers}-layer stack"},
+            {"value": round(allc, 4), "unit": unit, "cores": n, "kind": "oracle",
+             "sample": f"{steps_all} oracle layer steps of the same sample in {n} single-threaded processes "
+                       f"({wall:.1f} s wall), scaled to the {wl.layers}-layer stack"})
+
+
+# ------------------------------------------------------------------ records
+def _base(wl, layers, ms, steps, warmup, value, unit, dtype, launch):
+    return {"metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": dtype, "data": "synthetic (seeded N(0,0.02) weights, N(0,1) inputs and past K/V)",
+            "config": {"workload": wl.name, "layers": layers, "batch": wl.batch, "past_kv": wl.past,
+                       "hidden": wl.hidden, "heads": wl.heads, "ffn": wl.ffn, "launch": launch}}
+
+
+def decode_record(args, wl, torch, tg, syn, layers, mode="auto", cpu_s=0.0, vocab=0):
+    """One decode workload. The persistent stack (one launch per step) serves batches up to 4; larger
+    batches run the per-layer kernels under a HIP graph. With vocab > 0 the step is a whole
+    generation step: the stack runs the LM head and the greedy choice after the last layer."""
+    stack, kvs, lens, act = build_stack(wl, torch, tg, syn, layers)
+    x0 = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").to(act)
+    stream = torch.cuda.Stream()
+    per = algorithmic_bytes_per_layer(wl)
+    step_bytes = per["total"] * layers
+    use_stack = mode == "stack" or (mode == "auto" and wl.batch <= 4)
+    dtype = {"f32": "f32", "f16": "f16", "i8": "i8w-f16"}[wl.weight_dtype]
+    reset = lambda: lens.fill_(wl.past)
+    extra = {}
+    if use_stack:
+        head = gpu_head(wl, vocab, torch, tg, syn) if vocab else None
+        st = tg.Stack(stack, kvs, max_batch=wl.batch, head=head)
+        sws = st.workspace(wl.batch)
+        out = torch.empty_like(x0)
+        if vocab:
+            logits = torch.empty((wl.batch, vocab), dtype=torch.float32, device="cuda")
+            tokens = torch.empty(4, dtype=torch.int32, device="cuda")
+            launch = lambda: st.generate(x0, out, logits, tokens, sws, stream=stream)
+            step_bytes += head_bytes(wl, vocab)
         else:
-            w[n] = t.double().cpu().numpy()
-    return w
+            launch = lambda: st.decode(x0, out, sws, stream=stream)
+        ms, per_step = time_launches(torch, stream, launch, reset, args.steps, args.warmup)
+        st.check()
+        groups = st.groups
+        st.close()
+        kernel_ms = statistics.mean(per_step)
+        kgbs = step_bytes / (kernel_ms * 1e-3) / 1e9
+        name = "stack_decode_kernel (all layers" + (" and the LM head" if vocab else "") + " of one step)"
+        roofline = {"bound": "hbm", "kernel": name, "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                    "traffic": measured_traffic("stack_decode_kernel", wl.name)
+                    if (layers == wl.layers and not vocab) else None,
+                    "kernel_ms": round(kernel_ms, 4), "bytes_per_launch": step_bytes}
+        launch_desc = f"persistent stack kernel, {groups} workgroups" + (f", LM head over {vocab} rows" if vocab else "")
+        if vocab:
+            extra = {"vocab": vocab, "head_bytes": head_bytes(wl, vocab), "tokens": tokens[:wl.batch].tolist()}
+    else:
+        ws = stack[0].workspace(wl.batch, 1, wl.capacity)
+        bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+
+        def step():
+            lens.fill_(wl.past)
+            for l in range(layers):
+                stack[l].decode(kvs[l], x0 if l == 0 else bufs[l % 2], bufs[(l + 1) % 2], ws)
+
+        ms, per_step = time_graph(torch, stream, step, args.steps, args.warmup)
+        out = bufs[layers % 2]
+        kt = kernel_times(torch, stream, stack, kvs, lens, wl, x0, reset, ws)
+        pb = part_bytes(wl)
+        kernels = {p: {"ms": round(t, 4), "bytes": pb[p], "gbs": round(pb[p] / (t * 1e-3) / 1e9, 1)}
+                   for p, t in kt.items()}
+        dom = max(kt, key=kt.get)
+        gbs_dom = pb[dom] / (kt[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": f"{dom} (per-layer kernel; the longest of the layer step)",
+                    "achieved": round(gbs_dom, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs_dom / PEAK_HBM_GBS, 4), "traffic": None, "kernel_ms": round(kt[dom], 4),
+                    "bytes_per_launch": pb[dom], "kernels": kernels}
+        launch_desc = "per-layer kernels under a HIP graph (LN, skinny GEMMs, chunked attention)"
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    rec = _base(wl, layers, ms, args.steps, args.warmup, wl.batch / (ms * 1e-3), "tokens/s", dtype, launch_desc)
+    rec.update({"hbm_gbs_per_layer_step": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                "bytes_per_layer_step": per, "step_ms": step_stats(per_step), "roofline": roofline, **extra})
+    if cpu_s > 0:
+        rec["cpu_baseline"], rec["cpu_baseline_all_cores"] = cpu_baselines(wl, stack[0], kvs[0], cpu_s)
+    return rec
 
 
-def cpu_baseline_prefill(wl, stack, target_rows: int = 256):
-    """The oracle (plain C, double, one thread) on a bounded sample: the first target_rows prompt
-    rows of one sequence through layer 0, scaled to prompt tokens/s of the full L-layer stack."""
-    import numpy as np
-
-    import oracle
-
-    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
-    w = _oracle_weights(stack[0], wl)
-    S = min(target_rows, wl.seq)
-    x = np.random.default_rng(0).standard_normal((1, S, wl.hidden))
-    k = np.zeros((1, wl.heads, wl.capacity, wl.head_dim))
-    v = np.zeros_like(k)
-    lens = np.zeros(1, dtype=np.int32)
-    t0 = time.perf_counter()
-    oracle.layer_forward(desc, w, k, v, lens, x)
-    spent = time.perf_counter() - t0
-    return {"value": S / (spent * wl.layers), "unit": "prompt tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the first {S} prompt rows of one sequence of {wl.name} through one layer in {spent:.1f} s "
-                      f"on one host thread, scaled to the {wl.layers}-layer stack"}
-
-
-def run_prefill(args, wl, torch, tg, syn):
-    """C5-style workload: one step = the B x S prompt through all L layers (cache lengths reset to
-    0 each step), captured once in a HIP graph and replayed."""
-    layers = args.layers or wl.layers
-    stack, kvs, lens, _, act = build_stack(wl, torch, tg, syn, layers)
+def prefill_record(args, wl, torch, tg, syn, layers, cpu_s=0.0):
+    """Prefill: one step = the B x S prompt through all L layers (lengths reset to 0 each step),
+    captured once in a HIP graph and replayed. The roofline entry is the longest MFMA GEMM of the
+    layer step, timed per kernel."""
+    stack, kvs, lens, act = build_stack(wl, torch, tg, syn, layers)
     ws = stack[0].workspace(wl.batch, wl.seq, wl.capacity)
     x0 = syn.normal((wl.batch, wl.seq, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").to(act)
     bufs = [torch.empty_like(x0), torch.empty_like(x0)]
@@ -211,85 +453,37 @@ def run_prefill(args, wl, torch, tg, syn):
             stack[l].prefill(kvs[l], x0 if l == 0 else bufs[l % 2], bufs[(l + 1) % 2], ws)
 
     stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        step()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        step()
-    with torch.cuda.stream(stream):
-        for _ in range(max(1, args.warmup)):
-            g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for i in range(args.steps):
-            g.replay()
-            marks[i].record(stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    per_step = [(e0 if i == 0 else marks[i - 1]).elapsed_time(marks[i]) for i in range(args.steps)]
+    ms, per_step = time_graph(torch, stream, step, args.steps, args.warmup)
     out = bufs[layers % 2]
     assert torch.isfinite(out.float()).all(), "non-finite prefill output"
-    fl = prefill_flops_per_layer(wl)
+    fl = prefill_flops(wl)
+    kt = kernel_times(torch, stream, stack, kvs, lens, wl, x0, lambda: lens.zero_(), ws)
+    kernels = {p: {"ms": round(t, 4), **({"tflops": round(fl[p] / (t * 1e-3) / 1e12, 1)} if p in fl else {})}
+               for p, t in kt.items()}
+    gemms = [p for p in ("qkv", "o", "ff1", "ff2") if p in kt]
+    dom = max(gemms, key=kt.get)
+    tf_dom = fl[dom] / (kt[dom] * 1e-3) / 1e12
     tflops = fl["total"] * layers / (ms * 1e-3) / 1e12
-    gemm_tflops = fl["gemm_total"] * layers / (ms * 1e-3) / 1e12
-    result = {
-        "metric": "prefill prompt tokens/s + MFMA utilization (weight-GEMM FLOPs / step time / 2.5 PF)",
-        "value": round(wl.batch * wl.seq / (ms * 1e-3), 1),
-        "unit": "prompt tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prompt rows)",
-        "config": {"workload": wl.name, "layers": layers, "batch": wl.batch, "seq": wl.seq,
-                   "hidden": wl.hidden, "heads": wl.heads, "ffn": wl.ffn,
-                   "launch": "per-layer kernels (LN, 4 MFMA GEMMs, flash attention), hip-graph"},
-        "flops_per_layer": fl,
-        "step_ms": step_stats(per_step),
-        "roofline": {"bound": "mfma", "kernel": "whole prefill step (weight GEMMs + attention)",
-                     "achieved": round(tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
-                     "gemm_flops_over_step_tflops": round(gemm_tflops, 1)},
-    }
-    if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline_prefill(wl, stack)
-    print(json.dumps(result))
+    rec = _base(wl, layers, ms, args.steps, args.warmup, wl.batch * wl.seq / (ms * 1e-3), "prompt tokens/s", "f16",
+                "per-layer kernels (LN, 4 MFMA GEMMs, flash attention) under a HIP graph")
+    rec["metric"] = "prefill prompt tokens/s + MFMA utilization of the prefill GEMMs"
+    rec["config"].update({"seq": wl.seq})
+    rec.update({"flops_per_layer": fl, "step_ms": step_stats(per_step),
+                "step_tflops": round(tflops, 1), "step_frac_of_peak": round(tflops / PEAK_F16_TFLOPS, 4),
+                "roofline": {"bound": "mfma", "kernel": f"{dom} GEMM (the longest GEMM of the layer step)",
+                             "achieved": round(tf_dom, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tf_dom / PEAK_F16_TFLOPS, 4), "traffic": None,
+                             "kernel_ms": round(kt[dom], 4), "flops_per_launch": fl[dom], "kernels": kernels}})
+    if cpu_s > 0:
+        rec["cpu_baseline"], rec["cpu_baseline_all_cores"] = cpu_baselines(wl, stack[0], kvs[0], cpu_s, rows=32)
+    return rec
 
 
-def cpu_baseline(wl, stack, kvs, target_s: float):
-    """The oracle (plain C, double, one thread) on a bounded sample: whole decode layer steps of
-    this workload, every layer once and then the last layer's weights again, until about target_s
-    seconds of oracle time have run; scaled to tokens/s of the full L-layer stack."""
-    import numpy as np
-    import torch
-
-    import oracle
-
-    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
-    x = np.random.default_rng(0).standard_normal((wl.batch, 1, wl.hidden))
-    done, spent, w, k, v = 0, 0.0, None, None, None
-    lens = np.full(wl.batch, wl.past, dtype=np.int32)
-    while spent < target_s:
-        if done < len(stack):
-            layer, kv = stack[done], kvs[done]
-            w = _oracle_weights(layer, wl)
-            k = np.zeros((wl.batch, wl.heads, wl.capacity, wl.head_dim))
-            v = np.zeros_like(k)
-            k[:, :, :wl.past] = kv.k[:, :, :wl.past].double().cpu().numpy()
-            v[:, :, :wl.past] = kv.v[:, :, :wl.past].double().cpu().numpy()
-        t0 = time.perf_counter()
-        # the cache and the lengths are advanced in place: every step starts from the same past
-        x = oracle.layer_forward(desc, w, k.copy(), v.copy(), lens.copy(), x)
-        spent += time.perf_counter() - t0
-        done += 1
-    per_layer = spent / done
-    return {"value": wl.batch / (per_layer * wl.layers), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} decode layer steps of {wl.name} (batch {wl.batch}, {wl.past} past rows; each of the "
-                      f"{min(done, len(stack))} layers once, then the last layer's weights again) in {spent:.1f} s "
-                      f"on one host thread, scaled to the {wl.layers}-layer stack"}
+def _free(torch):
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -297,12 +491,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", help="workload key in synthetic.WORKLOADS (c5: prefill)")
-    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: the workload's)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 disables)")
+    ap.add_argument("--config", default="c2", help="headline workload key in synthetic.WORKLOADS (c5: prefill)")
+    ap.add_argument("--layers", type=int, default=0, help="override the headline's layer count (0: the workload's)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle sample per leg (one thread, all threads) for the headline (0 disables)")
+    ap.add_argument("--record-cpu-seconds", type=float, default=4.0, help="the same for each nested record")
+    ap.add_argument("--records", default="c2gen,c3,c4b8,c4b1,c5",
+                    help="nested records after the c2 headline (comma list; empty for none): c2gen (the "
+                         "generation step with the LM head), c3, c4b8, c4b1, c5")
     ap.add_argument("--mode", choices=["auto", "stack", "layers"], default="auto",
-                    help="stack: one persistent launch per step; layers: six kernels per layer")
-    ap.add_argument("--no-graph", action="store_true", help="layers mode: launch eagerly instead of a HIP graph")
+                    help="stack: one persistent launch per step; layers: the per-layer kernels")
     ap.add_argument("--no-read-probe", dest="read_probe", action="store_false",
                     help="skip the streaming-read measurement of the HBM bandwidth this device reaches")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -319,138 +517,38 @@ def main():
     import synthetic as syn
     import transformer_gpt_layer_amd as tg
 
+    torch.cuda.set_device(0)
     if args.copy_calibration:
-        torch.cuda.set_device(0)
         return copy_calibration(torch)
     wl = syn.WORKLOADS[args.config]
-    torch.cuda.set_device(0)
-    if wl.seq != 1:
-        return run_prefill(args, wl, torch, tg, syn)
     layers = args.layers or wl.layers
-    torch.cuda.set_device(0)
-    stack, kvs, lens, ws, act = build_stack(wl, torch, tg, syn, layers)
-    x0 = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").to(act)
-    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
-
-    def step():
-        lens.fill_(wl.past)
-        for l in range(layers):
-            stack[l].decode(kvs[l], x0 if l == 0 else bufs[l % 2], bufs[(l + 1) % 2], ws)
-
-    stream = torch.cuda.Stream()
-    use_stack = args.mode == "stack" or (args.mode == "auto" and wl.batch <= 4)
-    kernel_ms = None
-    if use_stack:
-        st = tg.Stack(stack, kvs, max_batch=wl.batch)
-        sws = st.workspace(wl.batch)
-        out = torch.empty_like(x0)
-
-        def launch():
-            st.decode(x0, out, sws)
-
-        with torch.cuda.stream(stream):
-            for _ in range(max(1, args.warmup)):
-                lens.fill_(wl.past)
-                launch()
-        st.check()
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for i in range(args.steps):
-                lens.fill_(wl.past)
-                starts[i].record(stream)
-                launch()
-                ends[i].record(stream)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        st.check()
-        groups = st.groups
-        st.close()  # release the handle now, not during interpreter shutdown
-        ms = e0.elapsed_time(e1) / args.steps
-        per_step = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-        kernel_ms = sum(per_step) / args.steps
-        launch_desc = f"persistent stack kernel, {groups} workgroups"
+    if wl.seq != 1:
+        result = prefill_record(args, wl, torch, tg, syn, layers, args.cpu_seconds)
     else:
-        def step():
-            lens.fill_(wl.past)
-            for l in range(layers):
-                stack[l].decode(kvs[l], x0 if l == 0 else bufs[l % 2], bufs[(l + 1) % 2], ws)
-
-        with torch.cuda.stream(stream):
-            step()
-        torch.cuda.synchronize()
-        if args.no_graph:
-            run = step
-        else:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                step()
-            run = g.replay
-        with torch.cuda.stream(stream):
-            for _ in range(args.warmup):
-                run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for i in range(args.steps):
-                run()
-                marks[i].record(stream)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
-        per_step = [(e0 if i == 0 else marks[i - 1]).elapsed_time(marks[i]) for i in range(args.steps)]
-        out = bufs[layers % 2]
-        launch_desc = "per-layer kernels, " + ("eager" if args.no_graph else "hip-graph")
-    assert torch.isfinite(out.float()).all(), "non-finite decode output"
-
-    per = algorithmic_bytes_per_layer(wl)
-    step_bytes = per["total"] * layers
-    gbs = step_bytes / (ms * 1e-3) / 1e9
-    tok_s = wl.batch / (ms * 1e-3)
-    if kernel_ms is not None:
-        kgbs = step_bytes / (kernel_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": "stack_decode_kernel (all layers of one step)",
-                    "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                    "traffic": measured_traffic("stack_decode_kernel", wl.name) if layers == wl.layers else None,
-                    "kernel_ms": round(kernel_ms, 4), "bytes_per_launch": step_bytes}
-    else:
-        roofline = {"bound": "hbm", "kernel": "whole decode step (per-layer kernels)",
-                    "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
-    result = {
-        "metric": "decode tokens/s at batch 1/8 + achieved HBM GB/s (% of peak) per layer step",
-        "value": round(tok_s, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {"f32": "f32", "f16": "f16", "i8": "i8w-f16"}[wl.weight_dtype],
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) inputs and past K/V)",
-        "config": {"workload": wl.name, "layers": layers, "batch": wl.batch, "past_kv": wl.past,
-                   "hidden": wl.hidden, "heads": wl.heads, "ffn": wl.ffn,
-                   "launch": launch_desc},
-        "hbm_gbs_per_layer_step": round(gbs, 1),
-        "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-        "bytes_per_layer_step": per,
-        "step_ms": step_stats(per_step),
-        "roofline": roofline,
-    }
+        result = decode_record(args, wl, torch, tg, syn, layers, args.mode, args.cpu_seconds)
+    _free(torch)
     if args.read_probe:
         probe = read_probe_gbs(torch, tg)
         result["read_probe_gbs"] = round(probe, 1)
-        # the roofline kernel's achieved rate over what a plain streaming read reaches here
-        result["hbm_frac_of_read_probe"] = round(roofline["achieved"] / probe, 4)
-    if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(wl, stack, kvs, args.cpu_seconds)
+        if result["roofline"]["unit"] == "GB/s":
+            # the roofline kernel's achieved rate over what a plain streaming read reaches here
+            result["hbm_frac_of_read_probe"] = round(result["roofline"]["achieved"] / probe, 4)
+    names = [r for r in args.records.split(",") if r] if args.config == "c2" else []
+    if names:
+        result["records"] = {}
+    for name in names:
+        print(f"[bench] record {name}", file=sys.stderr, flush=True)
+        cs = args.record_cpu_seconds
+        if name == "c2gen":
+            w2 = syn.WORKLOADS["c2"]
+            rec = decode_record(args, w2, torch, tg, syn, w2.layers, "stack", 0.0, vocab=syn.GPT_NEO_VOCAB)
+            rec["metric"] = "generation-step tokens/s (32 layers + final LayerNorm + LM head + greedy choice)"
+        elif syn.WORKLOADS[name].seq != 1:
+            rec = prefill_record(args, syn.WORKLOADS[name], torch, tg, syn, syn.WORKLOADS[name].layers, cs)
+        else:
+            rec = decode_record(args, syn.WORKLOADS[name], torch, tg, syn, syn.WORKLOADS[name].layers, "auto", cs)
+        result["records"][name] = rec
+        _free(torch)
     print(json.dumps(result))
 
 

@@ -167,6 +167,29 @@ int ds_quantize_i8(const float* w, int8_t* q, void* s, int32_t n, int32_t k, int
 int ds_dequantize_i8(const int8_t* q, const void* s, float* w, int32_t n, int32_t k, int32_t group,
                      void* stream);
 
+/* The kernel launches of one layer step, in order, as ds_layer_time_kernels names them. */
+typedef enum {
+  DS_PART_LN1 = 0,   /* LayerNorm of the input rows (MFMA and skinny paths)                   */
+  DS_PART_QKV = 1,   /* region 1: QKV product + bias, k/v into the cache (fp32 path: with LN1) */
+  DS_PART_ATTN = 2,  /* region 2: attention over the cache                                    */
+  DS_PART_O = 3,     /* output projection + bias + residual                                   */
+  DS_PART_LN2 = 4,   /* LayerNorm of x2 (MFMA and skinny paths; advances the lengths)         */
+  DS_PART_FF1 = 5,   /* region 3: FF1 + bias + GeLU (fp32 path: with LN2)                      */
+  DS_PART_FF2 = 6,   /* region 4: FF2 + bias + residual                                       */
+  DS_PART_LEN = 7    /* the length advance (fp32 path)                                        */
+} ds_part;
+
+/* Measurement aid, no layer operation (it serves callers that report each kernel's time against
+ * its roofline): runs one step of ds_layer_forward_decode (ntok == 1) or ds_layer_forward_prefill
+ * (same arguments and effects) with HIP events recorded on `stream` between its kernel launches,
+ * after a GPU-side wait of about 200 us so that the host enqueues the whole step before it starts;
+ * then waits for the stream and writes each launch's duration ms[i] and its ds_part kinds[i], in
+ * launch order. Returns the number of launches (at most max), or a negative ds_status. Not for
+ * graph capture (it synchronizes). */
+int ds_layer_time_kernels(const ds_layer_t* layer, ds_kv_cache* kv, const void* x, void* y, int32_t batch,
+                          int32_t ntok, void* workspace, size_t workspace_bytes, void* stream, float* ms,
+                          int32_t* kinds, int32_t max);
+
 /* Measurement aid, no layer operation (no passage of the pages defines it; it serves callers that
  * quote decode bandwidth against what the device reaches, beside the vendor peak): reads the
  * `bytes` bytes of the device buffer `buf` once with 16-byte streaming loads spread over the whole

@@ -231,3 +231,25 @@ def test_prefill_matches_oracle(name, S, P0, tanh):
     assert rel_l2(kg[:, :, :P0 + S], ok[:, :, :P0 + S]) <= TOL[wl.act_dtype]
     assert rel_l2(vg[:, :, :P0 + S], ov[:, :, :P0 + S]) <= TOL[wl.act_dtype]
     assert kv.lengths() == [P0 + S] * wl.batch
+
+
+@pytest.mark.parametrize("name,parts", [
+    ("f16-d64-b9", ["ln1", "qkv", "attn", "o", "ln2", "ff1", "ff2"]),
+    ("c1", ["qkv", "attn", "o", "ff1", "ff2", "len"]),
+])
+def test_time_kernels_runs_the_same_step(name, parts):
+    """The timing aid runs exactly the decode step (same outputs, same cache rows, same lengths) and
+    names its kernel launches in order."""
+    wl = SMALL[name]
+    gl, _ = gpu_layer_and_oracle_weights(wl, 0)
+    x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").to(gl.cfg.torch_act_dtype)
+    kv1, *_ = filled_caches(wl, 0, gl)
+    y1 = gl.decode(kv1, x)
+    kv2, *_ = filled_caches(wl, 0, gl)
+    y2 = torch.empty_like(y1)
+    timed = gl.time_kernels(kv2, x, y2)
+    torch.cuda.synchronize()
+    assert [p for p, _ in timed] == parts
+    assert all(ms > 0 for _, ms in timed)
+    assert torch.equal(y1, y2) and torch.equal(kv1.k, kv2.k) and torch.equal(kv1.v, kv2.v)
+    assert kv1.lengths() == kv2.lengths()

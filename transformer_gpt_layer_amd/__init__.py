@@ -261,6 +261,21 @@ class Layer:
               "ds_layer_forward_prefill")
         return y
 
+    def time_kernels(self, kv: KVCache, x, y=None, workspace=None, stream=None):
+        """One decode ([batch, hidden]) or prefill ([batch, seq, hidden]) step with an event between
+        kernel launches: returns [(part name, milliseconds)] in launch order. Synchronizes."""
+        B = x.shape[0]
+        T = 1 if x.dim() == 2 else x.shape[1]
+        y = self._io(x, y, tuple(x.shape))
+        if workspace is None:
+            workspace = self.workspace(B, T, kv.capacity, x.device)
+        ms = (C.c_float * 16)()
+        kinds = (C.c_int32 * 16)()
+        n = lib().ds_layer_time_kernels(self.handle, C.byref(kv.c_struct()), ptr(x), ptr(y), B, T, ptr(workspace),
+                                        workspace.numel(), stream_handle(stream), ms, kinds, 16)
+        check(min(n, 0), "ds_layer_time_kernels")
+        return [(_lib.PARTS[kinds[i]], float(ms[i])) for i in range(n)]
+
     def kv_append(self, kv: KVCache, k_new, v_new, stream=None):
         """Copy k_new, v_new [batch, ntok, hidden] into the cache after the filled rows."""
         B, T = k_new.shape[0], k_new.shape[1]

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libdslayer.so")
 DS_F32, DS_F16, DS_I8 = 0, 1, 2
 DS_OK, DS_ERR_NULL, DS_ERR_SHAPE, DS_ERR_DTYPE, DS_ERR_ALIGN = 0, -1, -2, -3, -4
 DS_ERR_KV_FULL, DS_ERR_UNSUPPORTED, DS_ERR_HIP, DS_ERR_WORKSPACE = -5, -6, -7, -8
+PARTS = ("ln1", "qkv", "attn", "o", "ln2", "ff1", "ff2", "len")  # ds_part names, in enum order
 
 # every symbol the header declares
 EXPORTS = ("ds_layer_create", "ds_layer_destroy", "ds_layer_workspace_bytes", "ds_kv_append",
@@ -23,7 +24,7 @@ EXPORTS = ("ds_layer_create", "ds_layer_destroy", "ds_layer_workspace_bytes", "d
            "ds_dequantize_i8", "ds_last_error", "ds_stack_create", "ds_stack_destroy",
            "ds_stack_workspace_bytes", "ds_stack_groups", "ds_stack_forward_decode",
            "ds_stack_check", "ds_stack_set_timeout_us", "ds_read_probe", "ds_stack_state_bytes",
-           "ds_stack_forward_decode_static", "ds_stack_forward_generate")
+           "ds_stack_forward_decode_static", "ds_stack_forward_generate", "ds_layer_time_kernels")
 
 
 class LayerDescC(C.Structure):
@@ -79,6 +80,9 @@ def lib():
                                       C.c_size_t, C.POINTER(vp)]
         L.ds_stack_forward_generate.argtypes = [vp, vp, vp, vp, vp, i32, vp, C.c_size_t, vp]
         L.ds_stack_forward_generate.restype = C.c_int
+        L.ds_layer_time_kernels.argtypes = [vp, C.POINTER(KVCacheC), vp, vp, i32, i32, vp, C.c_size_t, vp,
+                                            C.POINTER(C.c_float), C.POINTER(C.c_int32), i32]
+        L.ds_layer_time_kernels.restype = C.c_int
         L.ds_stack_destroy.argtypes = [vp]
         L.ds_stack_workspace_bytes.argtypes = [vp, i32]
         L.ds_stack_workspace_bytes.restype = C.c_size_t

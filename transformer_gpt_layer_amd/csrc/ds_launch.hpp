@@ -55,6 +55,8 @@ int attn_chunks_for(int rows, int heads, int cap, int chunk, int nmax, int cus);
 hipError_t launch_kv_append(Dt adt, const void* k_new, const void* v_new, void* kc, void* vc,
                             const int32_t* d_len, int batch, int ntok, int heads, int head_dim,
                             int cap, hipStream_t st);
+// A GPU-side wait of about `microseconds` (the wall clock of the device, one thread).
+hipError_t launch_delay(uint32_t microseconds, hipStream_t st);
 // Zeroes `bytes` bytes at p (16-byte aligned; the size is rounded down to whole 16-byte pieces).
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // d_len[b] += ntok for b < batch, unless that would pass cap

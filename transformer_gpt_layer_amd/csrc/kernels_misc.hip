@@ -48,6 +48,17 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
+// A bounded GPU-side wait of `ticks` periods of the 100 MHz wall clock (one thread).
+__global__ void delay_kernel(uint64_t ticks) {
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
+
+hipError_t launch_delay(uint32_t microseconds, hipStream_t st) {
+  hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(1), 0, st, (uint64_t)microseconds * 100u);
+  return hipGetLastError();
+}
+
 __global__ void len_advance_kernel(int32_t* d_len, int batch, int ntok, int cap) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < batch && d_len[b] + ntok <= cap) d_len[b] += ntok;

@@ -56,6 +56,27 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 
+// ds_layer_time_kernels: events recorded after each kernel launch of one step (the calling thread's
+// timer; null outside that call).
+constexpr int kMaxMarks = 16;
+struct KernelTimer {
+  hipEvent_t ev[kMaxMarks + 1] = {};
+  int kinds[kMaxMarks] = {};
+  int n = 0;
+  bool failed = false;
+};
+thread_local KernelTimer* g_timer = nullptr;
+
+void mark(hipStream_t st, int kind) {
+  KernelTimer* t = g_timer;
+  if (!t || t->failed) return;
+  if (t->n >= kMaxMarks || hipEventRecord(t->ev[t->n + 1], st) != hipSuccess) {
+    t->failed = true;
+    return;
+  }
+  t->kinds[t->n++] = kind;
+}
+
 struct WsLayout {
   size_t q, part, cnt, ctx, x2, f, h, sk_part, sk_cnt, total;
   int chunk, nchunk, n_sk_cnt;
@@ -165,6 +186,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   // 1: h = LN1(x); [q | k | v] = h Wqkv^T + bqkv, k and v into the cache rows d_len[b] + t
   if (hipError_t e = ds::launch_ln_rows(false, x, hp(L->w.ln1_g), hp(L->w.ln1_b), h, rows, H, d.ln_eps, st))
     return hip_fail(e, "ln1 launch");
+  mark(st, DS_PART_LN1);
   ds::GemmArgs a = g;
   a.a = h; a.bias = hp(L->w.b_qkv); a.out = q; a.N = 3 * H; a.K = H;
   const bool chunked_attn = skinny && ntok == 1;  // decode: chunked attention with an in-kernel merge
@@ -173,6 +195,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     a.n_counters = rows * d.heads;
   }
   if (hipError_t e = gemm(ds::EPI_QKV, a, L->w.w_qkv, L->w.s_qkv)) return hip_fail(e, "qkv gemm launch");
+  mark(st, DS_PART_QKV);
 
   // 2: attention of the new rows over the cache
   ds::AttnPrefillArgs at{};
@@ -192,25 +215,30 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   } else if (hipError_t e = ds::launch_attn_prefill(at, st)) {
     return hip_fail(e, "attention launch");
   }
+  mark(st, DS_PART_ATTN);
 
   // 3: x2 = x + ctx Wo^T + bo
   a = g;
   a.a = ctx; a.bias = hp(L->w.b_o); a.out = x2; a.resid = x; a.N = H; a.K = H;
   if (hipError_t e = gemm(ds::EPI_OPROJ, a, L->w.w_o, L->w.s_o)) return hip_fail(e, "o gemm launch");
+  mark(st, DS_PART_O);
 
   // 4: f = GeLU(LN2(x2) W1^T + b1); the LN2 launch also advances d_len by ntok (the QKV epilogue
   // and attention, its only readers in this step, have run)
   if (hipError_t e = ds::launch_ln_rows(true, x2, hp(L->w.ln2_g), hp(L->w.ln2_b), h, rows, H, d.ln_eps, st, kv->d_len,
                                         batch, ntok, kv->capacity))
     return hip_fail(e, "ln2 launch");
+  mark(st, DS_PART_LN2);
   a = g;
   a.a = h; a.bias = hp(L->w.b_ff1); a.out = f; a.N = F; a.K = H;
   if (hipError_t e = gemm(ds::EPI_FF1, a, L->w.w_ff1, L->w.s_ff1)) return hip_fail(e, "ff1 gemm launch");
+  mark(st, DS_PART_FF1);
 
   // 5: y = x2 + f W2^T + b2
   a = g;
   a.a = f; a.bias = hp(L->w.b_ff2); a.out = y; a.resid = x2; a.N = H; a.K = F;
   if (hipError_t e = gemm(ds::EPI_FF2, a, L->w.w_ff2, L->w.s_ff2)) return hip_fail(e, "ff2 gemm launch");
+  mark(st, DS_PART_FF2);
   if (kv->h_len)
     for (int b = 0; b < batch; ++b) kv->h_len[b] += ntok;
   return DS_OK;
@@ -256,6 +284,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   a.k_cache = kv->k; a.v_cache = kv->v;
   a.attn_counters = reinterpret_cast<uint32_t*>(base + W.cnt);
   if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_QKV, a, st)) return hip_fail(e, "ln_qkv launch");
+  mark(st, DS_PART_QKV);
 
   // 2: attention over the cache
   ds::AttnArgs at{};
@@ -267,6 +296,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   at.rows = rows; at.tokens = ntok; at.heads = d.heads; at.head_dim = d.head_dim;
   at.cap = kv->capacity; at.chunk = W.chunk; at.nchunk = W.nchunk; at.causal = d.triangular_masking;
   if (hipError_t e = ds::launch_attn_decode(adt, at, st)) return hip_fail(e, "attention launch");
+  mark(st, DS_PART_ATTN);
 
   // 3: x2 = x + Wo ctx + bo
   a = g;
@@ -274,6 +304,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   a.in = base + W.ctx; a.resid = x; a.out = base + W.x2;
   a.n = H; a.k = H;
   if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_OPROJ, a, st)) return hip_fail(e, "o_proj launch");
+  mark(st, DS_PART_O);
 
   // 4: f = GeLU(W1 LN2(x2) + b1)
   a = g;
@@ -281,6 +312,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   a.in = base + W.x2; a.ln_g = L->w.ln2_g; a.ln_b = L->w.ln2_b; a.out = base + W.f;
   a.n = F; a.k = H;
   if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_FF1, a, st)) return hip_fail(e, "ln_ff1 launch");
+  mark(st, DS_PART_FF1);
 
   // 5: y = x2 + W2 f + b2, then d_len += ntok
   a = g;
@@ -288,7 +320,9 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   a.in = base + W.f; a.resid = base + W.x2; a.out = y;
   a.n = H; a.k = F;
   if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_FF2, a, st)) return hip_fail(e, "ff2 launch");
+  mark(st, DS_PART_FF2);
   if (hipError_t e = ds::launch_len_advance(kv->d_len, batch, ntok, kv->capacity, st)) return hip_fail(e, "len advance launch");
+  mark(st, DS_PART_LEN);
 
   if (kv->h_len)
     for (int b = 0; b < batch; ++b) kv->h_len[b] += ntok;
@@ -394,6 +428,39 @@ int ds_layer_forward_prefill(const ds_layer_t* layer, ds_kv_cache* kv, const voi
                              int32_t seq, void* workspace, size_t workspace_bytes, void* stream) {
   if (seq < 0) return fail(DS_ERR_SHAPE, "seq %d < 0", seq);
   return forward_rows(layer, kv, x, y, batch, seq, workspace, workspace_bytes, stream);
+}
+
+int ds_layer_time_kernels(const ds_layer_t* layer, ds_kv_cache* kv, const void* x, void* y, int32_t batch,
+                          int32_t ntok, void* workspace, size_t workspace_bytes, void* stream, float* ms,
+                          int32_t* kinds, int32_t max) {
+  if (!ms || !kinds) return fail(DS_ERR_NULL, "ms or kinds is NULL");
+  if (max < 1 || ntok < 1) return fail(DS_ERR_SHAPE, "max %d and ntok %d must be >= 1", max, ntok);
+  KernelTimer t;
+  int made = 0;
+  hipError_t e = hipSuccess;
+  for (; made <= kMaxMarks && e == hipSuccess; ++made) e = hipEventCreate(&t.ev[made]);
+  if (e != hipSuccess) --made;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int rc = DS_OK;
+  if (e == hipSuccess) e = ds::launch_delay(200, st);
+  if (e == hipSuccess) e = hipEventRecord(t.ev[0], st);
+  if (e != hipSuccess) {
+    rc = hip_fail(e, "timer set-up");
+  } else {
+    g_timer = &t;
+    rc = forward_rows(layer, kv, x, y, batch, ntok, workspace, workspace_bytes, stream);
+    g_timer = nullptr;
+    if (rc == DS_OK && t.failed) rc = fail(DS_ERR_HIP, "recording the kernel events failed");
+    if (rc == DS_OK) {
+      if ((e = hipEventSynchronize(t.ev[t.n])) != hipSuccess) rc = hip_fail(e, "timer wait");
+      for (int i = 0; i < t.n && i < max && rc == DS_OK; ++i) {
+        if ((e = hipEventElapsedTime(&ms[i], t.ev[i], t.ev[i + 1])) != hipSuccess) rc = hip_fail(e, "event time");
+        kinds[i] = t.kinds[i];
+      }
+    }
+  }
+  for (int i = 0; i < made; ++i) (void)hipEventDestroy(t.ev[i]);
+  return rc == DS_OK ? (t.n < max ? t.n : max) : rc;
 }
 
 int ds_quantize_i8(const float* w, int8_t* q, void* s, int32_t n, int32_t k, int32_t group, void* stream) {
