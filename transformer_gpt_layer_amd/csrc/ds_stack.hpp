@@ -146,7 +146,9 @@ struct StackArgs {
 // The largest per-workgroup row tile among the four projections (and the LM head's V rows) for a
 // grid of G workgroups.
 int stack_rows_per_wg(int H, int F, int V, int G);
-hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups);
+// Slices per worker group of the persistent kernel for these widths (1 or 5).
+int stack_group_slices(Dt wdt, int H, int F);
+hipError_t stack_max_groups(Dt wdt, Dt adt, int B, int GS, size_t lds, int* groups);
 hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, hipStream_t st);
 
 }  // namespace ds

@@ -302,12 +302,13 @@ __device__ __forceinline__ bool poll_lane(Ctl& c, const StackArgs& a, rsrc_t r, 
 // ------------------------------------------------------------------ row tiles
 // Phase ph (0 QKV, 1 O, 2 FF1, 3 FF2, 4 the LM head) of workgroup g: rows [r0, r0+nr) of the [N][K]
 // matrix, one contiguous range of nr*K elements cut into slices of SL elements (K is a multiple of
-// SL), so slice s lies in tile row s / (K/SL). Worker w owns the contiguous block [s0, s0+cnt).
+// SL), so slice s lies in tile row s / (K/SL). Worker w owns the contiguous block [s0, s0+cnt), whose
+// ends are multiples of GS slices (GS divides K/SL: a group of GS slices never straddles a row).
 struct Geo {
   int N, K, r0, nr, s0, cnt;
 };
 
-__device__ __forceinline__ Geo phase_geo(const StackArgs& a, int SL, int g, int w, int ph) {
+__device__ __forceinline__ Geo phase_geo(const StackArgs& a, int SL, int GS, int g, int w, int ph) {
   const int H = a.H, F = a.F, G = a.G;
   Geo p;
   p.N = ph == 0 ? 3 * H : (ph == 2 ? F : (ph == 4 ? a.V : H));
@@ -316,7 +317,7 @@ __device__ __forceinline__ Geo phase_geo(const StackArgs& a, int SL, int g, int 
   p.r0 = min(p.N, g * rows);
   p.nr = min(p.N, p.r0 + rows) - p.r0;
   const int T = p.nr * (p.K / SL);
-  const int M = (T + NWK - 1) / NWK;
+  const int M = ((T + NWK - 1) / NWK + GS - 1) / GS * GS;
   p.s0 = min(T, w * M);
   p.cnt = min(T, p.s0 + M) - p.s0;
   return p;
@@ -337,22 +338,23 @@ __device__ __forceinline__ void flush_rows(float (&acc)[BM], float* slots, int r
   }
 }
 
-// Lane p (0..4) of worker w fills the table entry of phase p: slice count, byte offset of the
-// block's first slice in the matrix, matrix bytes, K, slices per row, first row and slice-in-row.
-template <typename WT>
+// Lane p (0..4) of worker w fills the table entry of phase p, counting in groups of GS slices: group
+// count, byte offset of the block's first slice in the matrix, matrix bytes, K, groups per row, first
+// row and group-in-row.
+template <typename WT, int GS>
 __device__ __forceinline__ void worker_table(const StackArgs& a, Ctl& c, int g, int w, int lane) {
   constexpr int SL = kWave * WTraits<WT>::E;
   if (lane < 5) {
-    const Geo p = phase_geo(a, SL, g, w, lane);
+    const Geo p = phase_geo(a, SL, GS, g, w, lane);
     int* t = c.tab[w][lane];
     const int sper = p.K / SL;
-    t[T_CNT] = p.cnt;
+    t[T_CNT] = p.cnt / GS;
     t[T_BASE] = (int)(((size_t)p.r0 * p.K + (size_t)p.s0 * SL) * sizeof(WT));
     t[T_BYTES] = (int)((size_t)p.N * p.K * sizeof(WT));
     t[T_K] = p.K;
-    t[T_SPER] = sper;
+    t[T_SPER] = sper / GS;
     t[T_RL0] = p.s0 / sper;
-    t[T_KS0] = p.s0 - (p.s0 / sper) * sper;
+    t[T_KS0] = (p.s0 - (p.s0 / sper) * sper) / GS;
   }
   wait_lgkm0();
 }
@@ -370,23 +372,30 @@ __device__ __forceinline__ const void* wtab_ld(const uint64_t* wtab, int p) {
   return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
 
-template <typename WT, int BM>
+// A worker walks its sequence of groups (GS consecutive 1 KB slices of one row) with a ring of RG
+// groups in flight: each group is multiplied with the staged activation as soon as all its slices
+// have landed (GS LDS reads, then GS products, back to back), and only then are the group's
+// registers refilled with the group RG places further on, whatever phase or layer that is. The
+// bookkeeping runs once per group, which is what bounds a worker's pace through slices that have
+// already landed (the first groups of a phase were loaded during the exchange before it).
+template <typename WT, int BM, int GS>
 __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typename WTraits<WT>::LT* act, float* slots,
                                        const half_t* scl, const uint64_t* wtab, int g, int w, int lane) {
   typedef typename WTraits<WT>::LT LT;
   constexpr int E = WTraits<WT>::E, SL = kWave * E;
-  constexpr int kRing = Ring<WT, BM>::value;
+  constexpr int RG = Ring<WT, BM>::value / GS > 0 ? Ring<WT, BM>::value / GS : 1;  // groups in flight
   constexpr uint32_t SLB = (uint32_t)(SL * sizeof(WT));  // bytes of one slice
+  constexpr uint32_t GB = SLB * GS;                     // bytes of one group
   // The worker's steps: p = 4 l + ph for the four projections of layer l, then p = 4 L for the LM
   // head when this launch runs it; gi(p) names the step's entry in the phase table.
   const int L = a.n_layers;
   const int P = 4 * L + (a.head ? 1 : 0);
   auto gi = [&](int p) { return p < 4 * L ? (p & 3) : 4; };
-  worker_table<WT>(a, c, g, w, lane);
+  worker_table<WT, GS>(a, c, g, w, lane);
   const int per_layer = tab_ld(c, w, 0, T_CNT) + tab_ld(c, w, 1, T_CNT) + tab_ld(c, w, 2, T_CNT) + tab_ld(c, w, 3, T_CNT);
-  const int total = L * per_layer + (a.head ? tab_ld(c, w, 4, T_CNT) : 0);
+  const int total = L * per_layer + (a.head ? tab_ld(c, w, 4, T_CNT) : 0);  // groups
 
-  // issue cursor: the next slice to load (step ip, slice is of icnt)
+  // issue cursor: the next group to load (step ip, group is of icnt)
   int ip = 0, is = 0, icnt = tab_ld(c, w, 0, T_CNT);
   while (ip < P && icnt == 0) {
     ++ip;
@@ -397,7 +406,7 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
   uint32_t ioff = (uint32_t)tab_ld(c, w, ip < P ? gi(ip) : 0, T_BASE);
   const uint32_t voff = (uint32_t)(lane * 16);
 
-  // consume cursor: the next slice to multiply (step cp, slice cs of ccnt)
+  // consume cursor: the next group to multiply (step cp, group cs of ccnt; row rl, group ks of Sper)
   int cp = 0, cs = 0, ccnt = tab_ld(c, w, 0, T_CNT);
   int K = tab_ld(c, w, 0, T_K), Sper = tab_ld(c, w, 0, T_SPER);
   int rl = tab_ld(c, w, 0, T_RL0), ks = tab_ld(c, w, 0, T_KS0);
@@ -425,60 +434,66 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
 #pragma unroll
   for (int b = 0; b < BM; ++b) acc[b] = 0.f;
 
-  // issue one load: the next slice, or an out-of-range load (reads nothing) past the end
-#define DS_ISSUE(dst)                                                                            \
-  {                                                                                              \
-    const bool live = ip < P;                                                                    \
-    const rsrc_t r = make_rsrc(iw, ibytes);                                                      \
-    dst = __builtin_amdgcn_raw_buffer_load_b128(r, voff, live ? ioff : kOutOfRange, kAuxStream); \
-    ioff += SLB;                                                                                 \
-    if (live && ++is >= icnt) {                                                                  \
-      is = 0;                                                                                    \
-      do {                                                                                       \
-        ++ip;                                                                                    \
-        icnt = ip < P ? tab_ld(c, w, gi(ip), T_CNT) : 0;                                         \
-      } while (ip < P && icnt == 0);                                                             \
-      if (ip < P) {                                                                              \
-        iw = wtab_ld(wtab, ip);                                                                  \
-        ibytes = (uint32_t)tab_ld(c, w, gi(ip), T_BYTES);                                        \
-        ioff = (uint32_t)tab_ld(c, w, gi(ip), T_BASE);                                           \
-      }                                                                                          \
-    }                                                                                            \
+  // issue one group: GS loads of the next group, or out-of-range loads (read nothing) past the end
+#define DS_ISSUE(dst)                                                                                \
+  {                                                                                                  \
+    const bool live = ip < P;                                                                        \
+    const rsrc_t r = make_rsrc(iw, ibytes);                                                          \
+    _Pragma("unroll") for (int k = 0; k < GS; ++k) dst[k] =                                          \
+        __builtin_amdgcn_raw_buffer_load_b128(r, voff, live ? ioff + (uint32_t)k * SLB : kOutOfRange, kAuxStream); \
+    ioff += GB;                                                                                      \
+    if (live && ++is >= icnt) {                                                                      \
+      is = 0;                                                                                        \
+      do {                                                                                           \
+        ++ip;                                                                                        \
+        icnt = ip < P ? tab_ld(c, w, gi(ip), T_CNT) : 0;                                             \
+      } while (ip < P && icnt == 0);                                                                 \
+      if (ip < P) {                                                                                  \
+        iw = wtab_ld(wtab, ip);                                                                      \
+        ibytes = (uint32_t)tab_ld(c, w, gi(ip), T_BYTES);                                            \
+        ioff = (uint32_t)tab_ld(c, w, gi(ip), T_BASE);                                               \
+      }                                                                                              \
+    }                                                                                                \
   }
 
-  u32x4 ring[kRing];
+  u32x4 ring[RG][GS];
 #pragma unroll
-  for (int u = 0; u < kRing; ++u) DS_ISSUE(ring[u])
+  for (int u = 0; u < RG; ++u) DS_ISSUE(ring[u])
 
   bool ok = true;
   for (int pos = 0; pos < total && ok;) {
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) {
+    for (int u = 0; u < RG; ++u) {
       if (pos < total && ok) {
         // the cursor is wave-uniform; say so, so that its bookkeeping stays in scalar registers
         ks = __builtin_amdgcn_readfirstlane(ks);
         rl = __builtin_amdgcn_readfirstlane(rl);
         cs = __builtin_amdgcn_readfirstlane(cs);
-        wait_vm_at_most<kRing - 1>();  // exactly kRing loads are in flight: the oldest has landed
+        wait_vm_at_most<(RG - 1) * GS>();  // exactly RG groups are in flight: the oldest has landed
         if (wait_act) {
           const uint32_t need = (uint32_t)(cp + 1);
           ok = worker_spin(c, a, [&] { return lds_ld(&c.act_ready) >= need; });
           wait_act = false;
         }
         if (ok) {
-          const LT* ap = act + ks * SL + lane * E;
-          float sc = 1.f;
-          if constexpr (sizeof(WT) == 1) sc = (float)scl[rl * (K / a.group) + (ks * SL + lane * E) / a.group];
+          const LT* ap = act + ks * (GS * SL) + lane * E;
 #pragma unroll
-          for (int b = 0; b < BM; ++b) {
-            if constexpr (sizeof(WT) == 4) {
-              acc[b] = dot4_f32(ring[u], *reinterpret_cast<const float4_t*>(ap + b * K), acc[b]);
-            } else if constexpr (sizeof(WT) == 2) {
-              acc[b] = dot8_f16(ring[u], *reinterpret_cast<const u32x4*>(ap + b * K), acc[b]);
-            } else {
-              acc[b] = fmaf(dot16_i8(ring[u], *reinterpret_cast<const u32x4*>(ap + b * K),
-                                     *reinterpret_cast<const u32x4*>(ap + b * K + 8)),
-                            sc, acc[b]);
+          for (int k = 0; k < GS; ++k) {
+            float sc = 1.f;
+            if constexpr (sizeof(WT) == 1)
+              sc = (float)scl[rl * (K / a.group) + ((ks * GS + k) * SL + lane * E) / a.group];
+#pragma unroll
+            for (int b = 0; b < BM; ++b) {
+              const LT* apk = ap + k * SL + b * K;
+              if constexpr (sizeof(WT) == 4) {
+                acc[b] = dot4_f32(ring[u][k], *reinterpret_cast<const float4_t*>(apk), acc[b]);
+              } else if constexpr (sizeof(WT) == 2) {
+                acc[b] = dot8_f16(ring[u][k], *reinterpret_cast<const u32x4*>(apk), acc[b]);
+              } else {
+                acc[b] = fmaf(dot16_i8(ring[u][k], *reinterpret_cast<const u32x4*>(apk),
+                                       *reinterpret_cast<const u32x4*>(apk + 8)),
+                              sc, acc[b]);
+              }
             }
           }
           if (++ks == Sper) {
@@ -1103,7 +1118,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 }  // namespace
 
 // ------------------------------------------------------------------ the persistent kernel
-template <typename WT, typename AT, int BM, int D>
+template <typename WT, typename AT, int BM, int D, int GS>
 __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const StackArgs a) {
   typedef typename WTraits<WT>::LT LT;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1149,7 +1164,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
     if (lds_ld(&c.abort) == 0u) return;
     raise_abort(c, a.sync);  // a failed sync wave releases the workers
   } else {
-    worker<WT, BM>(a, c, reinterpret_cast<const LT*>(smem), reinterpret_cast<float*>(smem + a.lds.slots),
+    worker<WT, BM, GS>(a, c, reinterpret_cast<const LT*>(smem), reinterpret_cast<float*>(smem + a.lds.slots),
                    reinterpret_cast<const half_t*>(smem + a.lds.scales), wtab, blockIdx.x, wave - NS, lane);
   }
 }
@@ -1163,32 +1178,46 @@ int stack_rows_per_wg(int H, int F, int V, int G) {
   return r;
 }
 
-template <typename WT, typename AT, int BM, int D>
+template <typename WT, typename AT, int BM, int D, int GS>
 static const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&stack_decode_kernel<WT, AT, BM, D>);
+  return reinterpret_cast<const void*>(&stack_decode_kernel<WT, AT, BM, D, GS>);
 }
 
-// Instantiated variants: batch tiles of 1 or 4 rows (2..4 sequences use the 4-row tile).
-static const void* pick(Dt wdt, Dt adt, int B, int D) {
+// Slices per worker group: 5 when every row of the stack's products (K = hidden or ffn) holds a
+// multiple of 5 slices (the GPT-Neo-2.7B and 13B widths), else 1.
+int stack_group_slices(Dt wdt, int H, int F) {
+  const int sl = wdt == F32 ? 256 : (wdt == F16 ? 512 : 1024);
+  return (H / sl) % 5 == 0 && (F / sl) % 5 == 0 ? 5 : 1;
+}
+
+// Instantiated variants: batch tiles of 1 or 4 rows (2..4 sequences use the 4-row tile), head_dim 64
+// or 128, groups of 1 or 5 slices.
+static const void* pick(Dt wdt, Dt adt, int B, int D, int GS) {
   const bool one = B <= 1;
-#define DS_PICK(WT_, AT_)                                                                       \
-  {                                                                                              \
-    if (D == 64) return one ? kernel_ptr<WT_, AT_, 1, 64>() : kernel_ptr<WT_, AT_, 4, 64>();     \
-    return one ? kernel_ptr<WT_, AT_, 1, 128>() : kernel_ptr<WT_, AT_, 4, 128>();               \
+#define DS_PICK_G(WT_, AT_, G_)                                                                        \
+  {                                                                                                     \
+    if (D == 64) return one ? kernel_ptr<WT_, AT_, 1, 64, G_>() : kernel_ptr<WT_, AT_, 4, 64, G_>();    \
+    return one ? kernel_ptr<WT_, AT_, 1, 128, G_>() : kernel_ptr<WT_, AT_, 4, 128, G_>();              \
+  }
+#define DS_PICK(WT_, AT_)                \
+  {                                      \
+    if (GS == 5) DS_PICK_G(WT_, AT_, 5)  \
+    DS_PICK_G(WT_, AT_, 1)               \
   }
   if (wdt == F16 && adt == F16) DS_PICK(half_t, half_t)
   if (wdt == I8 && adt == F16) DS_PICK(int8_t, half_t)
   if (wdt == F32 && adt == F32 && one) {
-    if (D == 64) return kernel_ptr<float, float, 1, 64>();
-    return kernel_ptr<float, float, 1, 128>();
+    if (GS == 5) return D == 64 ? kernel_ptr<float, float, 1, 64, 5>() : kernel_ptr<float, float, 1, 128, 5>();
+    return D == 64 ? kernel_ptr<float, float, 1, 64, 1>() : kernel_ptr<float, float, 1, 128, 1>();
   }
 #undef DS_PICK
+#undef DS_PICK_G
   return nullptr;
 }
 
-hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups) {
+hipError_t stack_max_groups(Dt wdt, Dt adt, int B, int GS, size_t lds, int* groups) {
   // head_dim does not change the register or LDS footprint enough to matter: query d = 128
-  const void* k = pick(wdt, adt, B, 128);
+  const void* k = pick(wdt, adt, B, 128, GS);
   if (!k) return hipErrorInvalidValue;
   int per_cu = 0, dev = 0;
   hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1204,7 +1233,7 @@ hipError_t stack_max_groups(Dt wdt, Dt adt, int B, size_t lds, int* groups) {
 }
 
 hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, hipStream_t st) {
-  const void* k = pick(wdt, adt, a.B, a.d);
+  const void* k = pick(wdt, adt, a.B, a.d, stack_group_slices(wdt, a.H, a.F));
   if (!k) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)a.lds.total);
   if (e != hipSuccess) return e;

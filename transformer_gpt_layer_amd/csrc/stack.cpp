@@ -217,7 +217,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
       return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode: %u bytes of LDS per workgroup needed", lay.total);
     }
     int fit = 0;
-    e = ds::stack_max_groups(wdt, adt, max_batch, lay.total, &fit);
+    e = ds::stack_max_groups(wdt, adt, max_batch, ds::stack_group_slices(wdt, d.hidden, d.ffn), lay.total, &fit);
     if (e == hipSuccess) G = G < fit ? G : fit;
   }
   if (e != hipSuccess || G < 1) {
