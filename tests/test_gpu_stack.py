@@ -21,12 +21,12 @@ def _wl(base, **kw):
     return dataclasses.replace(syn.WORKLOADS[base] if isinstance(base, str) else base, **kw)
 
 
-def build(wl, layers, past=None, batch=None, gelu_tanh=False):
+def build(wl, layers, past=None, batch=None, gelu_tanh=False, cap=None):
     B = wl.batch if batch is None else batch
     gls, ows, kvs, oks, ovs, lens = [], [], [], [], [], []
     for l in range(layers):
         gl, ow = gpu_layer_and_oracle_weights(wl, l, gelu_tanh=gelu_tanh)
-        kv, ok, ov, ln = filled_caches(wl, l, gl, past=past, batch=B)
+        kv, ok, ov, ln = filled_caches(wl, l, gl, past=past, batch=B, cap=cap)
         gls.append(gl); ows.append(ow); kvs.append(kv); oks.append(ok); ovs.append(ov); lens.append(ln)
     return gls, ows, kvs, oks, ovs, lens
 
@@ -95,6 +95,33 @@ def test_stack_decode_matches_oracle(name):
                 P = wl.past + step
                 assert rel_l2(kvs[l].k.double().cpu().numpy()[:, :, P], oks[l][:, :, P]) <= TOL[wl.act_dtype]
                 assert rel_l2(kvs[l].v.double().cpu().numpy()[:, :, P], ovs[l][:, :, P]) <= TOL[wl.act_dtype]
+
+
+def test_stack_ragged_lengths_in_a_large_cache():
+    """Sequences of lengths 150, 40 and 1 in caches of 2048 rows: the attention items cover the
+    chunks that hold keys of the longest sequence only, and the shorter sequences skip the chunks
+    past their own keys."""
+    wl = _wl("c1", hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="f16", act_dtype="f16", batch=3,
+             past=150, cfg_id=221, **AFFINE)
+    L, want = 2, [150, 40, 1]
+    gls, ows, kvs, oks, ovs, lens = build(wl, L, cap=2048)
+    for kv, ln in zip(kvs, lens):
+        kv.set_lengths(want)
+        ln[:] = want
+    with tg.Stack(gls, kvs, max_batch=wl.batch) as st:
+        ws = st.workspace(wl.batch)
+        for step in range(2):
+            x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, step, "cuda").half()
+            y = st.decode(x, workspace=ws)
+            st.check()
+            yo = oracle_step(wl, ows, oks, ovs, lens, x.double().cpu().numpy())
+            yd = y.double().cpu().numpy()
+            for b in range(wl.batch):
+                err = rel_l2(yd[b], yo[b])
+                print(f"  step {step} sequence {b} (length {want[b] + step}): rel L2 {err:.3e}", flush=True)
+                assert err <= TOL["f16"], (step, b, err)
+            for l in range(L):
+                assert kvs[l].lengths() == [n + step + 1 for n in want]
 
 
 @pytest.mark.parametrize("dt,batch", [("f16", 1), ("f16", 3), ("f32", 1)])

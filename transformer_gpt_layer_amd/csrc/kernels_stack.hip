@@ -81,6 +81,19 @@ template <typename T> __device__ __forceinline__ float ldp(const void* p, int i)
   return (float)reinterpret_cast<const T*>(p)[i];
 }
 
+// Element i of a T array as raw bits, converted later by cvraw. A wave waits for a load at the
+// first use of its value, and that wait also covers every earlier store of the wave (on this ISA
+// one counter tracks both): converting at the use point keeps an early-issued load from making the
+// wave wait for the acknowledgements of the tagged stores it has just made.
+template <typename T> __device__ __forceinline__ uint32_t ldraw(const void* p, int i) {
+  if constexpr (sizeof(T) == 2) return (uint32_t)reinterpret_cast<const uint16_t*>(p)[i];
+  else return reinterpret_cast<const uint32_t*>(p)[i];
+}
+template <typename T> __device__ __forceinline__ float cvraw(uint32_t u) {
+  if constexpr (sizeof(T) == 2) return (float)__builtin_bit_cast(half_t, (uint16_t)u);
+  else return __builtin_bit_cast(float, u);
+}
+
 // s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding: vmcnt in bits
 // [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima).
 template <int N> __device__ __forceinline__ void wait_vm_at_most() {
@@ -103,7 +116,7 @@ struct Ctl {
   uint32_t sbar;         // sync-wave barrier arrivals
   uint32_t abort;        // set when any wait of this workgroup failed
   uint32_t launch;       // launch counter (tags of this launch)
-  float red[NS][8];      // LayerNorm sums: (sum, sum of squares) for up to 4 rows, per wave
+  float red[NS][12];     // LayerNorm per wave and row (up to 4): two sums, or count, mean, deviations
   float m[NS], l[NS];    // attention: per-wave max and sum
   int tab[NWK][5][8];    // per worker and phase (4: the LM head): the block geometry (see worker_table)
   uint64_t best[kStackMaxBatch];  // LM head: this workgroup's largest argmax key per sequence
@@ -630,6 +643,196 @@ __device__ __forceinline__ void load_rows_plain(const void* in, int B, int K, fl
   }
 }
 
+// ------------------------------------------------------------------ sync waves: LayerNorm in registers
+// When the B rows fit kLnPairs pairs per sync thread, each thread keeps the pairs it fetched in
+// registers (pair j = st + u NT holds elements 2j, 2j + 1 of the flattened [B][K] rows), reduces
+// them, and writes its normalized pairs: one barrier and no round trip of the rows through LDS.
+constexpr int kLnPairs = 5;  // 2560 elements: more would spill the sync waves' registers
+
+// Pairwise update of (count, mean, sum of squared deviations) (Chan, Golub and LeVeque).
+__device__ __forceinline__ void chan_merge(float& n, float& m, float& q, float n2, float m2, float q2) {
+  const float nn = n + n2;
+  if (nn > 0.f) {
+    const float d = m2 - m, f = n2 / nn;
+    q += q2 + d * d * n * f;
+    m += d * f;
+    n = nn;
+  }
+}
+
+// The tagged pairs of [0, n) (n even) owned by thread st into x, polled until current.
+template <int PU>
+__device__ __forceinline__ bool poll_regs(Ctl& c, const StackArgs& a, const uint2* src, int n, uint32_t tag, int st,
+                                          float (&x)[PU][2]) {
+  const rsrc_t r = make_rsrc(src, (uint32_t)n * 8u);
+  const int nv = n >> 1;
+  bool need[PU];
+#pragma unroll
+  for (int u = 0; u < PU; ++u) need[u] = st + u * NT < nv;
+  uint64_t t0 = 0;
+  for (int round = 0;; ++round) {
+    u32x4 v[PU];
+#pragma unroll
+    for (int u = 0; u < PU; ++u) v[u] = coh_load16(r, need[u] ? (uint32_t)((st + u * NT) * 16) : kOutOfRange);
+    bool stale = false;
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      if (!need[u]) continue;
+      if (v[u].y == tag && v[u].w == tag) {
+        x[u][0] = as_f32(v[u].x);
+        x[u][1] = as_f32(v[u].z);
+        need[u] = false;
+      } else {
+        stale = true;
+      }
+    }
+    if (!stale) break;
+    if (round == 0) {
+      t0 = wall_clock64();
+    } else if (wall_clock64() - t0 > a.timeout_ticks || lds_ld(&c.abort) != 0u ||
+               ((uint32_t)round % kErrorEvery == 0 && grid_error(a))) {
+      raise_abort(c, a.sync);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// The caller's rows (AT, written before the launch): thread st's pairs of [0, n) into x.
+template <typename AT, int PU>
+__device__ __forceinline__ void load_regs_plain(const void* in, int n, int st, float (&x)[PU][2]) {
+  const rsrc_t r = make_rsrc(in, (uint32_t)(n * sizeof(AT)));
+  const int nv = n >> 1;
+#pragma unroll
+  for (int u = 0; u < PU; ++u) {
+    const int j = st + u * NT;
+    const uint32_t off = j < nv ? (uint32_t)(j * 2 * sizeof(AT)) : kOutOfRange;
+    if constexpr (sizeof(AT) == 2) {
+      const half2_t h = as_half2(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+      x[u][0] = (float)h.x;
+      x[u][1] = (float)h.y;
+    } else {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+      x[u][0] = as_f32(w.x);
+      x[u][1] = as_f32(w.y);
+    }
+  }
+}
+
+// LayerNorm (biased variance) of B rows of K elements held as pairs in registers, into act as LT;
+// the rows come from `plain` (the caller's input) when it is given, else from the tagged values at
+// `tagged`. gamma and beta of the thread's pairs are issued first and converted only when used.
+template <typename LT, typename AT, int BM, int PU>
+__device__ __forceinline__ bool stage_ln_regs(Ctl& c, const StackArgs& a, uint32_t& sb, int B, int K,
+                                              const AT* __restrict__ gam, const AT* __restrict__ beta, LT* act,
+                                              int st, const void* plain, const uint2* tagged, uint32_t tag) {
+  const int n = B * K, nv = n >> 1;
+  const rsrc_t rg = make_rsrc(gam, (uint32_t)(K * sizeof(AT))), rb = make_rsrc(beta, (uint32_t)(K * sizeof(AT)));
+  u32x2 gw[PU], bw[PU];  // fp16: the pair in .x; fp32: the two values
+#pragma unroll
+  for (int u = 0; u < PU; ++u) {
+    const int j = st + u * NT;
+    const uint32_t off = j < nv ? (uint32_t)((2 * j % K) * sizeof(AT)) : kOutOfRange;
+    if constexpr (sizeof(AT) == 2) {
+      gw[u].x = __builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0);
+      bw[u].x = __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0);
+    } else {
+      gw[u] = __builtin_amdgcn_raw_buffer_load_b64(rg, off, 0, 0);
+      bw[u] = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
+    }
+  }
+  float x[PU][2];
+  if (plain)
+    load_regs_plain<AT, PU>(plain, n, st, x);
+  else if (!poll_regs<PU>(c, a, tagged, n, tag, st, x))
+    return false;
+  // per thread and row: count, mean and squared deviations of its values (two passes in registers),
+  // then merged across the wave
+  float sn[BM], sm[BM], sq[BM];
+#pragma unroll
+  for (int b = 0; b < BM; ++b) {
+    float s = 0.f, cnt = 0.f;
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      const int j = st + u * NT;
+      if (j < nv && (BM == 1 || 2 * j / K == b)) {
+        s += x[u][0] + x[u][1];
+        cnt += 2.f;
+      }
+    }
+    const float m = cnt > 0.f ? s / cnt : 0.f;
+    float q = 0.f;
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      const int j = st + u * NT;
+      if (j < nv && (BM == 1 || 2 * j / K == b)) {
+        const float d0 = x[u][0] - m, d1 = x[u][1] - m;
+        q += d0 * d0 + d1 * d1;
+      }
+    }
+    sn[b] = cnt;
+    sm[b] = m;
+    sq[b] = q;
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1)
+#pragma unroll
+    for (int b = 0; b < BM; ++b) {
+      const float n2 = __shfl_xor(sn[b], off, kWave), m2 = __shfl_xor(sm[b], off, kWave);
+      const float q2 = __shfl_xor(sq[b], off, kWave);
+      chan_merge(sn[b], sm[b], sq[b], n2, m2, q2);
+    }
+  if ((st & 63) == 0) {
+#pragma unroll
+    for (int b = 0; b < BM; ++b) {
+      c.red[st >> 6][3 * b] = sn[b];
+      c.red[st >> 6][3 * b + 1] = sm[b];
+      c.red[st >> 6][3 * b + 2] = sq[b];
+    }
+  }
+  if (!sync_bar(c, a, sb, st)) return false;
+  float mean[BM], rstd[BM];
+#pragma unroll
+  for (int b = 0; b < BM; ++b) {
+    float tn = 0.f, tm = 0.f, tq = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NS; ++wv) chan_merge(tn, tm, tq, c.red[wv][3 * b], c.red[wv][3 * b + 1], c.red[wv][3 * b + 2]);
+    mean[b] = tm;
+    rstd[b] = rsqrtf(fmaxf(tq / (float)K, 0.f) + a.eps);
+  }
+#pragma unroll
+  for (int u = 0; u < PU; ++u) {
+    const int j = st + u * NT;
+    if (j >= nv) continue;
+    const int b = BM == 1 ? 0 : 2 * j / K;
+    float g0, g1, b0, b1;
+    if constexpr (sizeof(AT) == 2) {
+      const half2_t gh = as_half2(gw[u].x), bh = as_half2(bw[u].x);
+      g0 = (float)gh.x;
+      g1 = (float)gh.y;
+      b0 = (float)bh.x;
+      b1 = (float)bh.y;
+    } else {
+      g0 = as_f32(gw[u].x);
+      g1 = as_f32(gw[u].y);
+      b0 = as_f32(bw[u].x);
+      b1 = as_f32(bw[u].y);
+    }
+    float mb = mean[0], rb_ = rstd[0];
+#pragma unroll
+    for (int bb = 1; bb < BM; ++bb)
+      if (bb == b) {
+        mb = mean[bb];
+        rb_ = rstd[bb];
+      }
+    act[2 * j] = (LT)((x[u][0] - mb) * rb_ * g0 + b0);
+    act[2 * j + 1] = (LT)((x[u][1] - mb) * rb_ * g1 + b1);
+  }
+  for (int i = n + st; i < BM * K; i += NT) act[i] = (LT)0.f;  // activation rows past B
+  return true;
+}
+
 // int8: the fp16 scales of the phase's row tile, [nr][K/group], into LDS.
 __device__ __forceinline__ void stage_scales(const void* s, int r0, int nr, int K, int group, half_t* scl, int st) {
   const int n = nr * (K / group);
@@ -647,40 +850,65 @@ template <typename AT, int D> struct AttnShape {
   static constexpr int NIT = (kStackChunk + NS * KPI - 1) / (NS * KPI);
 };
 
-// One item's partial: scores of q against the chunk's rows (the past rows from the cache, the new
-// row at position len from this launch's tagged K/V), wave-reduced max and sum, the exp-weighted V
-// sum; (max, sum, acc[D]) is stored tagged for the workgroup that merges the (sequence, head).
-template <typename AT, int D>
-__device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_t& sb, const StackLayer& L,
-                                             const int32_t* lens, int item,
-                                             uint32_t tag_q, uint32_t tag_part, float* s_acc, int st) {
-  typedef AttnShape<AT, D> S;
-  constexpr int EK = S::EK, LPK = S::LPK, KPI = S::KPI, NIT = S::NIT;
-  const float kNeg = -1e30f;
-  const int cc = item % a.nchunk;
-  const int j = (item / a.nchunk) % a.nh;
-  const int b = item / (a.nchunk * a.nh);
-  const int len = lens[b];
+// The attention items of one layer: (sequence b, head j, chunk cc) for the chunks that hold keys,
+// numbered densely over the longest sequence's chunk count so that workgroups get at most one
+// item each whenever there are fewer items than workgroups, whatever the cache capacity.
+struct AttnItem {
+  int b, j, cc;
+  bool valid;
+};
+__device__ __forceinline__ int attn_nvalid(const StackArgs& a, int len) {
   int nkeys = len + 1;
   if (nkeys > a.cap) nkeys = a.cap;
-  const int nvalid = (nkeys + kStackChunk - 1) / kStackChunk;
-  if (cc >= nvalid) return true;
+  return (nkeys + kStackChunk - 1) / kStackChunk;
+}
+__device__ __forceinline__ AttnItem attn_item(const StackArgs& a, const int32_t* lens, int nvmax, int item) {
+  AttnItem it;
+  it.cc = item % nvmax;
+  it.j = (item / nvmax) % a.nh;
+  it.b = item / (nvmax * a.nh);
+  it.valid = it.cc < attn_nvalid(a, lens[it.b]);
+  return it;
+}
+
+// Loads of an item's past rows (written by earlier launches) straight from the cache into kr, vr.
+template <typename AT, int D>
+__device__ __forceinline__ void attn_load(const StackArgs& a, const StackLayer& L, int len, const AttnItem& it, int st,
+                                          u32x4 (&kr)[AttnShape<AT, D>::NIT], u32x4 (&vr)[AttnShape<AT, D>::NIT]) {
+  typedef AttnShape<AT, D> S;
+  constexpr int EK = S::EK, LPK = S::LPK, KPI = S::KPI, NIT = S::NIT;
   const int wave = st >> 6, lane = st & 63;
-  const int H = a.nh * D;
-  const size_t head = (((size_t)b * a.nh + j) * a.cap) * D;
+  const size_t head = (((size_t)it.b * a.nh + it.j) * a.cap) * D;
   const uint32_t bytes = (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(AT));
   const rsrc_t rk = make_rsrc(L.k, bytes), rv = make_rsrc(L.v, bytes);
   const int e0 = (lane % LPK) * EK;
-  // past rows (written by earlier launches) straight from the cache
-  u32x4 kr[NIT], vr[NIT];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int key = cc * kStackChunk + (it * NS + wave) * KPI + lane / LPK;
-    const bool past = key < len && key < a.cap && key < (cc + 1) * kStackChunk;
+  for (int i = 0; i < NIT; ++i) {
+    const int key = it.cc * kStackChunk + (i * NS + wave) * KPI + lane / LPK;
+    const bool past = key < len && key < a.cap && key < (it.cc + 1) * kStackChunk;
     const uint32_t off = past ? (uint32_t)((head + (size_t)key * D + e0) * sizeof(AT)) : kOutOfRange;
-    kr[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-    vr[it] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
   }
+}
+
+// One item's partial: scores of q against the chunk's rows (the past rows in kr, vr from
+// attn_load, the new row at position len from this launch's tagged K/V), wave-reduced max and sum,
+// the exp-weighted V sum; (max, sum, acc[D]) is stored tagged for the workgroup that merges the
+// (sequence, head).
+template <typename AT, int D>
+__device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_t& sb, int len, const AttnItem& ai,
+                                             uint32_t tag_q, uint32_t tag_part, float* s_acc, int st,
+                                             u32x4 (&kr)[AttnShape<AT, D>::NIT], u32x4 (&vr)[AttnShape<AT, D>::NIT]) {
+  typedef AttnShape<AT, D> S;
+  constexpr int EK = S::EK, LPK = S::LPK, KPI = S::KPI, NIT = S::NIT;
+  const float kNeg = -1e30f;
+  const int cc = ai.cc, j = ai.j, b = ai.b;
+  int nkeys = len + 1;
+  if (nkeys > a.cap) nkeys = a.cap;
+  const int wave = st >> 6, lane = st & 63;
+  const int H = a.nh * D;
+  const int e0 = (lane % LPK) * EK;
   // q of this head, this lane's EK elements
   const rsrc_t rq = make_rsrc(a.q, (uint32_t)(a.B * H * 8));
   float qv[EK];
@@ -856,7 +1084,24 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     st = t;
   };
   uint32_t sb = 0;
-  const int nitems = B * a.nh * a.nchunk;
+  typedef AttnShape<AT, D> AS;
+  u32x4 kr[AS::NIT], vr[AS::NIT];  // the past rows of the current attention item
+
+  // LayerNorm of the B rows of H into act, from `plain` (the caller's input) when given, else from
+  // the tagged values at `tagged`: in registers when the rows fit, else through LDS
+  auto layer_norm = [&](const void* gam, const void* beta, const void* plain, const uint2* tagged,
+                        uint32_t tag) __attribute__((always_inline)) -> bool {
+    if (B * H <= 2 * NT * kLnPairs)
+      return stage_ln_regs<LT, AT, BM, kLnPairs>(c, a, sb, B, H, (const AT*)gam, (const AT*)beta, act, st, plain,
+                                                 tagged, tag);
+    return stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)gam, (const AT*)beta, act, raw, gb, st, [&]() {
+      if (plain) {
+        load_rows_plain<AT>(plain, B, H, raw, st);
+        return true;
+      }
+      return poll_range(c, a, tagged, B * H, tag, st, [&](int i, float v) { raw[i] = v; });
+    });
+  };
 
   // per-workgroup row tiles of each projection (the same split the workers use)
   const int rq = stack_tile_rows(3 * H, G, false), ro = stack_tile_rows(H, G, false), r1 = stack_tile_rows(F, G, true);
@@ -875,7 +1120,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
   // Epilogue operands of this thread's first row are requested when its phase begins, so that
   // their memory latency (long while the workers stream) passes during the staging and the
   // workers' products instead of after them; later rows (t >= NT) load in the loop.
-  auto pre_ld = [&](const void* bias, int r0, int nr) { return st < nr * B ? ldp<AT>(bias, r0 + st / B) : 0.f; };
+  auto pre_ld = [&](const void* bias, int r0, int nr) { return st < nr * B ? ldraw<AT>(bias, r0 + st / B) : 0u; };
   auto clear_slots = [&](int nr) {
     for (int i = st; i < nr * NWK * BM; i += NT) slots[i] = 0.f;
   };
@@ -905,28 +1150,20 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     const uint32_t t_ctx = stack_tag(launch, l, TAG_CTX), t_x2 = stack_tag(launch, l, TAG_X2);
     const uint32_t t_f = stack_tag(launch, l, TAG_F), t_y = stack_tag(launch, l, TAG_Y);
 
+    // attention items of this layer (chunks with keys, over the longest sequence)
+    int nvmax = 1;
+    for (int b = 0; b < B; ++b) nvmax = max(nvmax, attn_nvalid(a, lens[b]));
+    const int nitems = B * a.nh * nvmax;
+
     // ---- region 1: LN1 + QKV + bias; q, k, v tagged; k, v also into the cache row d_len[b]
     fresh();
-    const float pre_q = pre_ld(L.b_qkv, q0, nq);
+    const uint32_t pre_q = pre_ld(L.b_qkv, q0, nq);
     const int pre_pos = lens[st % B];
     if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nq);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_qkv, q0, nq, H, a.group, scl, st);
-    {
-      bool ok;
-      if (l == 0) {
-        ok = stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)L.ln1_g, (const AT*)L.ln1_b, act, raw, gb, st, [&]() {
-          load_rows_plain<AT>(a.x, B, H, raw, st);
-          return true;
-        });
-      } else {
-        const uint32_t t_prev = stack_tag(launch, l - 1, TAG_Y);
-        ok = stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)L.ln1_g, (const AT*)L.ln1_b, act, raw, gb, st, [&]() {
-          return poll_range(c, a, a.ybuf, B * H, t_prev, st, [&](int i, float v) { raw[i] = v; });
-        });
-      }
-      if (!ok) return;
-    }
+    if (!layer_norm(L.ln1_g, L.ln1_b, l == 0 ? a.x : nullptr, a.ybuf, l == 0 ? 0u : stack_tag(launch, l - 1, TAG_Y)))
+      return;
     if (!hand_over(seq0)) return;
     {
       const rsrc_t rqo = make_rsrc(a.q, (uint32_t)(B * H * 8));
@@ -935,7 +1172,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
       const rsrc_t rk = make_rsrc(L.k, cache_bytes), rv = make_rsrc(L.v, cache_bytes);
       for (int t = st; t < nq * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = q0 + rl;
-        const float z = row_sum(rl, b) + (t == st ? pre_q : ldp<AT>(L.b_qkv, n));
+        const float z = row_sum(rl, b) + (t == st ? cvraw<AT>(pre_q) : ldp<AT>(L.b_qkv, n));
         if (n < H) {
           tstore(rqo, (uint32_t)(b * H + n), z, t_q);
         } else {
@@ -952,16 +1189,20 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     // ---- region 2: attention over the cache; first every partial of this workgroup, then the
     // merges it owns (chunk 0 of a head), so that no merge waits on a partial queued behind it
     fresh();
-    for (int item = g; item < nitems; item += G)
-      if (!attn_partial<AT, D>(c, a, sb, L, lens, item, t_q, t_part, s_acc, st)) return;
-    for (int item = g; item < nitems; item += G)
-      if (item % a.nchunk == 0 &&
-          !attn_merge<AT, D>(c, a, sb, lens, item / (a.nchunk * a.nh), (item / a.nchunk) % a.nh, t_part, t_ctx, s_part, st))
-        return;
+    for (int item = g; item < nitems; item += G) {
+      const AttnItem it = attn_item(a, lens, nvmax, item);
+      if (!it.valid) continue;
+      attn_load<AT, D>(a, L, lens[it.b], it, st, kr, vr);
+      if (!attn_partial<AT, D>(c, a, sb, lens[it.b], it, t_q, t_part, s_acc, st, kr, vr)) return;
+    }
+    for (int item = g; item < nitems; item += G) {
+      const AttnItem it = attn_item(a, lens, nvmax, item);
+      if (it.valid && it.cc == 0 && !attn_merge<AT, D>(c, a, sb, lens, it.b, it.j, t_part, t_ctx, s_part, st)) return;
+    }
 
     // ---- output projection + bias + residual: x2 = x + Wo ctx + bo
     fresh();
-    const float pre_o = pre_ld(L.b_o, o0, no);
+    const uint32_t pre_o = pre_ld(L.b_o, o0, no);
     if (!sync_bar(c, a, sb, st)) return;  // the attention scratch (same LDS) and the slots are free
     clear_slots(no);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_o, o0, no, H, a.group, scl, st);
@@ -972,7 +1213,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
       const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 8));
       for (int t = st; t < no * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = o0 + rl;
-        const float z = row_sum(rl, b) + (t == st ? pre_o : ldp<AT>(L.b_o, n));
+        const float z = row_sum(rl, b) + (t == st ? cvraw<AT>(pre_o) : ldp<AT>(L.b_o, n));
         const float xr = l == 0 ? ldp<AT>(a.x, b * H + n) : res_y[t];
         const float v = xr + z;
         res_x2[t] = v;
@@ -983,16 +1224,13 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     // ---- region 3: LN2 + FF1 + bias + GeLU
     fresh();
     // fp16: this thread's first pair of rows; otherwise its first row
-    const float pre_f0 = sizeof(AT) == 2 ? (st < (nf / 2) * B ? ldp<AT>(L.b_ff1, f0 + 2 * (st / B)) : 0.f)
-                                         : pre_ld(L.b_ff1, f0, nf);
-    const float pre_f1 = sizeof(AT) == 2 && st < (nf / 2) * B ? ldp<AT>(L.b_ff1, f0 + 2 * (st / B) + 1) : 0.f;
+    const uint32_t pre_f0 = sizeof(AT) == 2 ? (st < (nf / 2) * B ? ldraw<AT>(L.b_ff1, f0 + 2 * (st / B)) : 0u)
+                                            : pre_ld(L.b_ff1, f0, nf);
+    const uint32_t pre_f1 = sizeof(AT) == 2 && st < (nf / 2) * B ? ldraw<AT>(L.b_ff1, f0 + 2 * (st / B) + 1) : 0u;
     if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nf);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff1, f0, nf, H, a.group, scl, st);
-    if (!stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)L.ln2_g, (const AT*)L.ln2_b, act, raw, gb, st, [&]() {
-          return poll_range(c, a, a.x2, B * H, t_x2, st, [&](int i, float v) { raw[i] = v; });
-        }))
-      return;
+    if (!layer_norm(L.ln2_g, L.ln2_b, nullptr, a.x2, t_x2)) return;
     if (!hand_over(seq0 + 2u)) return;
     {
       const rsrc_t rf = make_rsrc(a.f, (uint32_t)(B * F * 8));
@@ -1001,7 +1239,8 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
         // FF2 staging polls
         for (int t = st; t < (nf / 2) * B; t += NT) {
           const int pl = t / B, b = t - pl * B, rl = 2 * pl, n = f0 + rl;
-          const float b0 = t == st ? pre_f0 : ldp<AT>(L.b_ff1, n), b1 = t == st ? pre_f1 : ldp<AT>(L.b_ff1, n + 1);
+          const float b0 = t == st ? cvraw<AT>(pre_f0) : ldp<AT>(L.b_ff1, n);
+          const float b1 = t == st ? cvraw<AT>(pre_f1) : ldp<AT>(L.b_ff1, n + 1);
           const half_t g0 = (half_t)gelu(row_sum(rl, b) + b0, a.gelu_tanh != 0);
           const half_t g1 = (half_t)gelu(row_sum(rl + 1, b) + b1, a.gelu_tanh != 0);
           tstore_pair(rf, (uint32_t)((b * F + n) / 2), g0, g1, t_f);
@@ -1009,7 +1248,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
       } else {
         for (int t = st; t < nf * B; t += NT) {
           const int rl = t / B, b = t - rl * B, n = f0 + rl;
-          const float z = row_sum(rl, b) + (t == st ? pre_f0 : ldp<AT>(L.b_ff1, n));
+          const float z = row_sum(rl, b) + (t == st ? cvraw<AT>(pre_f0) : ldp<AT>(L.b_ff1, n));
           tstore(rf, (uint32_t)(b * F + n), (float)(AT)gelu(z, a.gelu_tanh != 0), t_f);
         }
       }
@@ -1017,7 +1256,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 
     // ---- region 4: FF2 + bias + residual: y = x2 + W2 f + b2
     fresh();
-    const float pre_y = pre_ld(L.b_ff2, y0, ny);
+    const uint32_t pre_y = pre_ld(L.b_ff2, y0, ny);
     if (!sync_bar(c, a, sb, st)) return;  // the LayerNorm rows (same LDS) and the slots are free
     clear_slots(ny);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff2, y0, ny, F, a.group, scl, st);
@@ -1039,7 +1278,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
       const rsrc_t ry = make_rsrc(a.y, (uint32_t)(B * H * sizeof(AT)));
       for (int t = st; t < ny * B; t += NT) {
         const int rl = t / B, b = t - rl * B, n = y0 + rl;
-        const float z = row_sum(rl, b) + (t == st ? pre_y : ldp<AT>(L.b_ff2, n));
+        const float z = row_sum(rl, b) + (t == st ? cvraw<AT>(pre_y) : ldp<AT>(L.b_ff2, n));
         const float v = (float)(AT)(res_x2[t] + z);
         res_y[t] = v;
         if (last) coh_st_act<AT>(ry, (uint32_t)(b * H + n), v);
@@ -1058,10 +1297,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     clear_slots(nv);
     if constexpr (sizeof(WT) == 1) stage_scales(a.head_s, v0, nv, H, a.group, scl, st);
     const uint32_t t_last = stack_tag(launch, a.n_layers - 1, TAG_Y);
-    if (!stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)a.head_g, (const AT*)a.head_b, act, raw, gb, st, [&]() {
-          return poll_range(c, a, a.ybuf, B * H, t_last, st, [&](int i, float v) { raw[i] = v; });
-        }))
-      return;
+    if (!layer_norm(a.head_g, a.head_b, nullptr, a.ybuf, t_last)) return;
     if (!hand_over(4u * (uint32_t)a.n_layers)) return;
     // each logit as a 64-bit key that orders like (value, -index): the order-preserving bits of the
     // float above the inverted row index, so the largest key is the largest logit at its smallest
