@@ -82,8 +82,8 @@ typedef struct {
   int32_t quant_group_mlp;    /* int8: elements per scale of W_ff1 and W_ff2 (0: quant_group)    */
                               /* ([KP] section 五 5.2: quantize_groups and mlp_extra_grouping,   */
                               /* finer groups for the MLP matrices); 0 for other weight dtypes.  */
-                              /* Supported: quant_group 64 with quant_group_mlp 0 or 64; other   */
-                              /* int8 group sizes return DS_ERR_UNSUPPORTED.                     */
+                              /* Both must be multiples of 16 dividing their matrices' K (hidden */
+                              /* for W_qkv, W_o, W_ff1; ffn for W_ff2), else DS_ERR_SHAPE.        */
   float ln_eps;               /* LayerNorm epsilon, > 0 (1e-5 by default)                       */
   int32_t gelu_tanh;          /* 0: u*Phi(u) with erf (default); 1: tanh approximation          */
   int32_t triangular_masking; /* 1 (default): a row at position p sees keys 0..p; 0: all keys   */

@@ -48,6 +48,7 @@ class Workload:
     past: int          # filled cache rows before the step (decode) or P0 (prefill)
     seq: int = 1       # new rows per sequence: 1 for decode, S for prefill
     group: int = 0     # int8 group size along the reduction dimension
+    group_mlp: int = 0  # int8 group size of the MLP matrices (0: group)
     ln_std: float = 0.0     # > 0: LayerNorm gamma ~ 1 + N(0, ln_std), beta ~ N(0, ln_std)
     bias_std: float = 0.01  # biases ~ N(0, bias_std)
     extra: dict = field(default_factory=dict, compare=False, hash=False)

@@ -27,23 +27,26 @@ def gpu_layer_and_oracle_weights(wl: syn.Workload, layer: int, device="cuda", ch
 
     w32 = syn.layer_weights_f32(wl, layer, device)
     act = TORCH[wl.act_dtype]
+    i8 = wl.weight_dtype == "i8"
     cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
                          dtype={"f32": "fp32", "f16": "fp16", "i8": "int8"}[wl.weight_dtype],
-                         quant_group=wl.group if wl.weight_dtype == "i8" else None, **cfg_kw)
+                         quant_group=wl.group if i8 else None,
+                         quant_group_mlp=wl.group_mlp if i8 and wl.group_mlp else None, **cfg_kw)
     gw, ow = {}, {}
     for name, t in w32.items():
         if name.startswith("w_"):
-            if wl.weight_dtype == "i8":
-                q, s = tg.quantize_i8(t.contiguous(), wl.group)
+            if i8:
+                G = wl.group_mlp if wl.group_mlp and name in ("w_ff1", "w_ff2") else wl.group
+                q, s = tg.quantize_i8(t.contiguous(), G)
                 gw[name], gw["s" + name[1:]] = q, s
                 if check_quant:
-                    oq, os_ = oracle.quantize_i8(t.cpu().numpy(), wl.group)
+                    oq, os_ = oracle.quantize_i8(t.cpu().numpy(), G)
                     assert np.array_equal(q.cpu().numpy(), oq), f"int8 codes of {name} differ from the oracle"
                     assert np.array_equal(s.cpu().view(torch.int16).numpy().view(np.uint16), os_), \
                         f"fp16 scales of {name} differ from the oracle"
-                    ow[name] = oracle.dequantize_i8(oq, os_, wl.group)
+                    ow[name] = oracle.dequantize_i8(oq, os_, G)
                 else:
-                    ow[name] = oracle.dequantize_i8(q.cpu().numpy(), s.cpu().view(torch.int16).numpy().view(np.uint16), wl.group)
+                    ow[name] = oracle.dequantize_i8(q.cpu().numpy(), s.cpu().view(torch.int16).numpy().view(np.uint16), G)
             else:
                 gw[name] = t.to(act).contiguous()
                 ow[name] = gw[name].double().cpu().numpy()

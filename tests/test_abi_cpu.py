@@ -62,11 +62,14 @@ def _create(desc, w):
     (dict(weight_dtype=0, act_dtype=1), _lib.DS_ERR_DTYPE),
     (dict(quant_group=64), _lib.DS_ERR_DTYPE),
     (dict(quant_group_mlp=32), _lib.DS_ERR_DTYPE),
-    # int8 group sizes other than 64 have no GPU-tested kernels: refused, not silently mishandled
-    (dict(weight_dtype=2, act_dtype=1, quant_group=24), _lib.DS_ERR_UNSUPPORTED),
-    (dict(weight_dtype=2, act_dtype=1, quant_group=32), _lib.DS_ERR_UNSUPPORTED),
-    (dict(weight_dtype=2, act_dtype=1, quant_group=128), _lib.DS_ERR_UNSUPPORTED),
-    (dict(weight_dtype=2, act_dtype=1, quant_group=64, quant_group_mlp=32), _lib.DS_ERR_UNSUPPORTED),
+    # int8 groups: multiples of 16 that divide the reduction width of their matrices
+    (dict(weight_dtype=2, act_dtype=1, quant_group=24), _lib.DS_ERR_SHAPE),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=0), _lib.DS_ERR_SHAPE),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=48), _lib.DS_ERR_SHAPE),      # 48 does not divide 256
+    (dict(weight_dtype=2, act_dtype=1, quant_group=512), _lib.DS_ERR_SHAPE),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=64, quant_group_mlp=24), _lib.DS_ERR_SHAPE),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=64, quant_group_mlp=-32), _lib.DS_ERR_SHAPE),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=64, quant_group_mlp=96), _lib.DS_ERR_SHAPE),
     (dict(ln_eps=0.0), _lib.DS_ERR_SHAPE),
     (dict(triangular_masking=2), _lib.DS_ERR_SHAPE),
 ])
@@ -82,9 +85,10 @@ def test_create_rejects_null_and_misaligned_pointers():
     assert _create(_desc(), _weights(w_ff1=FAKE + 8))[0] == _lib.DS_ERR_ALIGN
     assert _create(_desc(), _weights(s_o=FAKE))[0] == _lib.DS_ERR_DTYPE       # scales on fp16 weights
     assert _create(_desc(weight_dtype=2, quant_group=64), _weights(int8=True, s_ff2=None))[0] == _lib.DS_ERR_NULL
-    rc, h = _create(_desc(weight_dtype=2, quant_group=64, quant_group_mlp=64), _weights(int8=True))
-    assert rc == 0, _lib.lib().ds_last_error()
-    _lib.lib().ds_layer_destroy(h)
+    for ga, gm in ((64, 64), (64, 32), (32, 0), (128, 64), (16, 256)):
+        rc, h = _create(_desc(weight_dtype=2, quant_group=ga, quant_group_mlp=gm), _weights(int8=True))
+        assert rc == 0, (ga, gm, _lib.lib().ds_last_error())
+        _lib.lib().ds_layer_destroy(h)
     h = C.c_void_p()
     assert _lib.lib().ds_layer_create(None, C.byref(_weights()), C.byref(h)) == _lib.DS_ERR_NULL
 
@@ -161,9 +165,12 @@ def test_quantization_setting_is_a_group_count():
         tg.make_config(hidden=2560, heads=20, ffn=10240, dtype="int8", quantization_setting=(48, False))
     with pytest.raises(ValueError, match="disagree"):
         tg.make_config(hidden=2560, heads=20, ffn=10240, dtype="int8", quantization_setting=(40, False), quant_group=32)
-    # extra MLP grouping halves the MLP group size; refused until the kernels support it
-    with pytest.raises(NotImplementedError):
-        tg.make_config(hidden=5120, heads=40, ffn=20480, dtype="int8", quantization_setting=(80, True))
+    # extra MLP grouping halves the MLP group size
+    cfg = tg.make_config(hidden=5120, heads=40, ffn=20480, dtype="int8", quantization_setting=(80, True))
+    assert cfg.quant_group == 64 and cfg.quant_group_mlp == 32
+    with pytest.raises(ValueError, match="disagree"):
+        tg.make_config(hidden=5120, heads=40, ffn=20480, dtype="int8", quantization_setting=(80, True),
+                       quant_group_mlp=64)
     with pytest.raises(ValueError, match="int8"):
         tg.make_config(hidden=256, heads=2, ffn=512, dtype="fp16", quantization_setting=(4, False))
 

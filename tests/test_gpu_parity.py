@@ -68,6 +68,14 @@ CASES.update({
     "i8-affine-tanh-b5": (_wl(SMALL["i8-d128-b5"], cfg_id=126, **AFFINE), True),
     "i8-affine-b1": (_wl(SMALL["i8-d64-b1-k256"], cfg_id=127, **AFFINE), False),
     "i8-affine-tanh-b15": (_wl(SMALL["i8-d64-b15-h2048"], cfg_id=128, **AFFINE), True),
+    # finer int8 groups (mlp_extra_grouping halves the MLP group; other group sizes): the per-row
+    # GEMV path with a scale group per matrix, at one and at several activation rows
+    "i8-g64-mlp32-b1": (_wl(SMALL["i8-d128-b5"], group_mlp=32, batch=1, cfg_id=129, **AFFINE), False),
+    "i8-g32-b8": (_wl(SMALL["i8-d128-b5"], group=32, ffn=1536, batch=8, cfg_id=130, **AFFINE), True),
+    "i8-g128-mlp64-b3": (_wl("c1", hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="i8", act_dtype="f16",
+                             group=128, group_mlp=64, batch=3, past=40, cfg_id=131, **AFFINE), False),
+    "i8-g16-mlp48-b2": (_wl("c1", hidden=768, heads=12, head_dim=64, ffn=1536, weight_dtype="i8", act_dtype="f16",
+                            group=16, group_mlp=48, batch=2, past=21, cfg_id=132, **AFFINE), True),
 })
 
 

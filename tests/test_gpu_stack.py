@@ -60,6 +60,12 @@ CASES = {
     "i8-d128-b3-L3-affine": (_wl("c1", hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="i8",
                                  act_dtype="f16", group=64, batch=3, past=65, cfg_id=214, **AFFINE), 3, False),
     "f32-d64-b1-L3-affine-tanh": (_wl("c1", cfg_id=215, **AFFINE), 3, True),
+    # int8 with a finer MLP group (mlp_extra_grouping) and with groups of 32 throughout
+    "i8-d128-b1-L2-g64-mlp32": (_wl("c1", hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="i8",
+                                    act_dtype="f16", group=64, group_mlp=32, batch=1, past=50, cfg_id=222, **AFFINE),
+                                2, False),
+    "i8-d128-b3-L2-g32": (_wl("c1", hidden=1024, heads=8, head_dim=128, ffn=3072, weight_dtype="i8",
+                              act_dtype="f16", group=32, batch=3, past=20, cfg_id=223, **AFFINE), 2, True),
     # widths whose rows hold a multiple of 5 slices: the workers consume groups of 5 slices
     "f16-d128-b2-L3-g5": (_wl("c1", hidden=2560, heads=20, head_dim=128, ffn=5120, weight_dtype="f16",
                               act_dtype="f16", batch=2, past=70, cfg_id=217, **AFFINE), 3, True),

@@ -163,24 +163,43 @@ def test_quantizer_golden_examples():
         assert not q[0, len(c["q_head"]):].any()
 
 
-def test_quantizer_bounds_and_idempotence():
+@pytest.mark.parametrize("G", [64, 32, 16])
+def test_quantizer_bounds_and_idempotence(G):
     w = (rng.normal(0, 0.02, (48, 256))).astype(np.float32)
-    w[3, 64:128] = 0.0                      # one all-zero group
+    w[3, 64:128] = 0.0                      # one all-zero group (whole groups at every G here)
     w[5, 7] = 0.9                           # one outlier
-    q, s = oracle.quantize_i8(w, 64)
+    q, s = oracle.quantize_i8(w, G)
+    assert s.shape == (48, 256 // G)
     sv = oracle.fp16_to_double(s)
-    deq = oracle.dequantize_i8(q, s, 64)
-    per = np.repeat(sv, 64, axis=1)
+    deq = oracle.dequantize_i8(q, s, G)
+    per = np.repeat(sv, G, axis=1)
     assert np.all(np.abs(w.astype(np.float64) - deq) <= per / 2 * (1 + 1e-12))   # |w - q s| <= s/2
     assert np.all(np.abs(q.astype(int)) <= 127)
-    amax = np.abs(w.reshape(48, 4, 64)).max(-1)
-    qmax = np.abs(q.astype(int).reshape(48, 4, 64)).max(-1)
+    amax = np.abs(w.reshape(48, 256 // G, G)).max(-1)
+    qmax = np.abs(q.astype(int).reshape(48, 256 // G, G)).max(-1)
     assert np.all(qmax[amax > 0] == 127) and np.all(qmax[amax == 0] == 0)
-    assert sv[3, 1] == 0.0
+    assert np.all(sv[3, 64 // G:128 // G] == 0.0)
     # dequantized values are exact in float32, and quantizing them again returns (q, s)
     assert np.array_equal(deq.astype(np.float32).astype(np.float64), deq)
-    q2, s2 = oracle.quantize_i8(deq.astype(np.float32), 64)
+    q2, s2 = oracle.quantize_i8(deq.astype(np.float32), G)
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def test_quantizer_group_32_boundaries():
+    """Groups of 32 along K (the finer MLP groups): each half of a 64-wide row gets its own scale.
+    amax = f32(0.127) gives the scale 1049 * 2^-20 (fp16 bits 0x1419, the golden 'rounded scale'
+    case); amax = f32(0.254), exactly twice that, gives exactly twice the scale (0x1819: one binade
+    up, same significand). So 0.127 codes as 127 in the first group and as round(63.47) = 63 in the
+    second, and as 63 under a single group of 64."""
+    w = np.zeros((1, 64), np.float32)
+    w[0, 0], w[0, 32], w[0, 33] = 0.127, 0.254, 0.127
+    q, s = oracle.quantize_i8(w, 32)
+    assert [int(v) for v in s[0]] == [0x1419, 0x1819]
+    assert (int(q[0, 0]), int(q[0, 32]), int(q[0, 33])) == (127, 127, 63)
+    assert np.count_nonzero(q) == 3
+    q64, s64 = oracle.quantize_i8(w, 64)
+    assert [int(v) for v in s64[0]] == [0x1819]
+    assert (int(q64[0, 0]), int(q64[0, 32]), int(q64[0, 33])) == (63, 127, 63)
 
 
 # ------------------------------------------------------------------ the whole layer

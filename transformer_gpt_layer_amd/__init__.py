@@ -87,7 +87,7 @@ def make_config(config=None, **kwargs) -> LayerConfig:
     groups each weight row of the hidden-width reduction (K = hidden) is cut into, so the group size
     is hidden / quantize_groups, which must divide evenly; mlp_extra_grouping=True asks for twice as
     many groups (half the group size) in the MLP matrices. A bare int is taken the same way as
-    quantize_groups. Extra MLP grouping raises NotImplementedError until the library supports it.
+    quantize_groups. Group sizes must be multiples of 16 dividing the matrices' reduction widths.
     """
     base = {}
     if config is not None:
@@ -124,9 +124,6 @@ def make_config(config=None, **kwargs) -> LayerConfig:
     if dt == DS_I8:
         group = 64 if group is None else int(group)
         group_mlp = 0 if group_mlp is None or int(group_mlp) == group else int(group_mlp)
-        if group_mlp:
-            raise NotImplementedError(f"int8 MLP groups of {group_mlp} (extra MLP grouping) are not supported by "
-                                      f"this build; the MLP matrices use the attention group size {group}")
     elif group not in (None, 0) or group_mlp not in (None, 0):
         raise ValueError("quant_group and quantization_setting apply to int8 weights only")
     else:

@@ -86,7 +86,8 @@ struct StackLds {
 
 __host__ __device__ inline uint32_t stack_align(uint32_t v) { return (v + 255u) & ~255u; }
 
-// wsize: weight element bytes (4, 2, 1); bm: batch rows of the kernel variant (1 or 4). The
+// wsize: weight element bytes (4, 2, 1); bm: batch rows of the kernel variant (1 or 4); group: the
+// smallest int8 scale group of the stack's matrices (sizes the staged scales). The
 // activation region also holds the attention scratch (per-wave partials, then the chunk partials
 // of the merge), which is never live at the same time as staged activations.
 __host__ __device__ inline StackLds stack_lds_layout(int wsize, int bm, int H, int F, int rows_per_wg, int nchunk,
@@ -119,7 +120,7 @@ struct StackArgs {
   int n_layers;
   const void* x;   // [B][H] stack input (activation type)
   void* y;         // [B][H] stack output (activation type)
-  int B, H, nh, d, F, cap, group;
+  int B, H, nh, d, F, cap, group, group_mlp;  // int8 scale groups: W_qkv, W_o, LM head; W_ff1, W_ff2
   float eps;
   int gelu_tanh;
   // workspace: tagged values (8 bytes each)

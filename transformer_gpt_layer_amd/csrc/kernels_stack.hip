@@ -123,7 +123,7 @@ struct Ctl {
 };
 
 // Fields of a worker's phase-table entry.
-enum { T_CNT = 0, T_BASE = 1, T_BYTES = 2, T_K = 3, T_SPER = 4, T_RL0 = 5, T_KS0 = 6 };
+enum { T_CNT = 0, T_BASE = 1, T_BYTES = 2, T_K = 3, T_SPER = 4, T_RL0 = 5, T_KS0 = 6, T_GRP = 7 };
 
 __device__ __forceinline__ uint32_t lds_ld(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -368,6 +368,7 @@ __device__ __forceinline__ void worker_table(const StackArgs& a, Ctl& c, int g, 
     t[T_SPER] = sper / GS;
     t[T_RL0] = p.s0 / sper;
     t[T_KS0] = (p.s0 - (p.s0 / sper) * sper) / GS;
+    t[T_GRP] = lane == 2 || lane == 3 ? a.group_mlp : a.group;  // int8 scale group of the phase's matrix
   }
   wait_lgkm0();
 }
@@ -423,6 +424,7 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
   int cp = 0, cs = 0, ccnt = tab_ld(c, w, 0, T_CNT);
   int K = tab_ld(c, w, 0, T_K), Sper = tab_ld(c, w, 0, T_SPER);
   int rl = tab_ld(c, w, 0, T_RL0), ks = tab_ld(c, w, 0, T_KS0);
+  int grp = tab_ld(c, w, 0, T_GRP), spr = K / grp;  // int8: scale group and scales per row
   bool wait_act = true;
   // leave step cp [finished or empty], publishing it, and move to the next non-empty one
   auto c_advance = [&]() {
@@ -439,6 +441,8 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
     Sper = tab_ld(c, w, t, T_SPER);
     rl = tab_ld(c, w, t, T_RL0);
     ks = tab_ld(c, w, t, T_KS0);
+    grp = tab_ld(c, w, t, T_GRP);
+    spr = K / grp;
     wait_act = true;
   };
   if (ccnt == 0) c_advance();
@@ -494,7 +498,7 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
           for (int k = 0; k < GS; ++k) {
             float sc = 1.f;
             if constexpr (sizeof(WT) == 1)
-              sc = (float)scl[rl * (K / a.group) + ((ks * GS + k) * SL + lane * E) / a.group];
+              sc = (float)scl[rl * spr + ((ks * GS + k) * SL + lane * E) / grp];
 #pragma unroll
             for (int b = 0; b < BM; ++b) {
               const LT* apk = ap + k * SL + b * K;
@@ -1229,7 +1233,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     const uint32_t pre_f1 = sizeof(AT) == 2 && st < (nf / 2) * B ? ldraw<AT>(L.b_ff1, f0 + 2 * (st / B) + 1) : 0u;
     if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nf);
-    if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff1, f0, nf, H, a.group, scl, st);
+    if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff1, f0, nf, H, a.group_mlp, scl, st);
     if (!layer_norm(L.ln2_g, L.ln2_b, nullptr, a.x2, t_x2)) return;
     if (!hand_over(seq0 + 2u)) return;
     {
@@ -1259,7 +1263,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     const uint32_t pre_y = pre_ld(L.b_ff2, y0, ny);
     if (!sync_bar(c, a, sb, st)) return;  // the LayerNorm rows (same LDS) and the slots are free
     clear_slots(ny);
-    if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff2, y0, ny, F, a.group, scl, st);
+    if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff2, y0, ny, F, a.group_mlp, scl, st);
     zero_rows(F);
     if constexpr (sizeof(AT) == 2) {
       // pair i holds f elements 2i and 2i + 1 of the [B][F] rows

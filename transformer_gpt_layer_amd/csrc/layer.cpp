@@ -136,7 +136,8 @@ bool use_mfma(const ds_layer_desc& d, int rows) {
 bool use_skinny(const ds_layer_desc& d, int rows) {
   if (d.act_dtype != DS_F16 || rows < 1 || rows > ds::kSkinnyMaxRows) return false;
   if (d.weight_dtype == DS_F16) return rows < kMfmaMinRows;
-  return d.weight_dtype == DS_I8 && d.quant_group == 64;
+  // the int8 skinny kernel applies one scale per 64-element block of K
+  return d.weight_dtype == DS_I8 && d.quant_group == 64 && (d.quant_group_mlp == 0 || d.quant_group_mlp == 64);
 }
 
 int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int batch, int ntok, char* base,
@@ -264,6 +265,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   const int H = d.hidden, F = d.ffn;
 
   ds::GemvArgs g{};
+  const int group_mlp = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
   g.group = d.quant_group;
   g.rows = rows;
   g.tokens = ntok;
@@ -310,7 +312,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   a = g;
   a.w = L->w.w_ff1; a.s = L->w.s_ff1; a.bias = L->w.b_ff1;
   a.in = base + W.x2; a.ln_g = L->w.ln2_g; a.ln_b = L->w.ln2_b; a.out = base + W.f;
-  a.n = F; a.k = H;
+  a.n = F; a.k = H; a.group = group_mlp;
   if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_FF1, a, st)) return hip_fail(e, "ln_ff1 launch");
   mark(st, DS_PART_FF1);
 
@@ -318,7 +320,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   a = g;
   a.w = L->w.w_ff2; a.s = L->w.s_ff2; a.bias = L->w.b_ff2;
   a.in = base + W.f; a.resid = base + W.x2; a.out = y;
-  a.n = H; a.k = F;
+  a.n = H; a.k = F; a.group = group_mlp;
   if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_FF2, a, st)) return hip_fail(e, "ff2 launch");
   mark(st, DS_PART_FF2);
   if (hipError_t e = ds::launch_len_advance(kv->d_len, batch, ntok, kv->capacity, st)) return hip_fail(e, "len advance launch");
@@ -350,11 +352,14 @@ int ds_layer_create(const ds_layer_desc* desc, const ds_layer_weights* w, ds_lay
                        (d.weight_dtype == DS_I8 && d.act_dtype == DS_F16);
   if (!pair_ok) return fail(DS_ERR_DTYPE, "unsupported (weight, activation) dtype pair (%d, %d)", d.weight_dtype, d.act_dtype);
   if (d.weight_dtype == DS_I8) {
-    // the int8 kernels are built and parity-tested for groups of 64 elements along K
+    // a lane's 16 consecutive codes share one scale: groups are multiples of 16 dividing the
+    // reduction dimension of their matrices (hidden for W_qkv, W_o, W_ff1; ffn for W_ff2)
     const int gm = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
-    if (d.quant_group != 64 || gm != 64)
-      return fail(DS_ERR_UNSUPPORTED, "int8 group sizes %d (attention) and %d (MLP): this build supports 64 and 64",
-                  d.quant_group, gm);
+    if (d.quant_group < 16 || d.quant_group % 16 || d.hidden % d.quant_group)
+      return fail(DS_ERR_SHAPE, "int8 quant_group %d must be a multiple of 16 dividing hidden %d", d.quant_group, d.hidden);
+    if (d.quant_group_mlp < 0 || gm < 16 || gm % 16 || d.hidden % gm || d.ffn % gm)
+      return fail(DS_ERR_SHAPE, "int8 MLP group %d must be a multiple of 16 dividing hidden %d and ffn %d", gm, d.hidden,
+                  d.ffn);
   } else if (d.quant_group != 0 || d.quant_group_mlp != 0) {
     return fail(DS_ERR_DTYPE, "quant_group %d and quant_group_mlp %d must be 0 for non-int8 weights", d.quant_group,
                 d.quant_group_mlp);

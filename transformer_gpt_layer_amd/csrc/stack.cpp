@@ -95,6 +95,13 @@ size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 int slice_elems(int wdt) { return wdt == DS_F32 ? 256 : (wdt == DS_F16 ? 512 : 1024); }
 size_t act_bytes(int adt) { return adt == DS_F32 ? 4 : 2; }
 
+// The smallest int8 scale group among the stack's matrices (1 for other weight dtypes).
+int min_group(const ds_layer_desc& d) {
+  if (d.weight_dtype != DS_I8) return 1;
+  const int gm = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
+  return gm < d.quant_group ? gm : d.quant_group;
+}
+
 struct StackWs {
   size_t q, knew, vnew, part, ctx, x2, f, y, total;
 };
@@ -211,7 +218,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
   int G = cus;  // one workgroup of kStackThreads per CU
   for (int iter = 0; e == hipSuccess && iter < 3; ++iter) {
     const ds::StackLds lay = ds::stack_lds_layout(wsz_i, bm, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->head.V, G),
-                                                  S->nchunk, d.head_dim, d.quant_group, n_layers);
+                                                  S->nchunk, d.head_dim, min_group(d), n_layers);
     if (lay.total > (uint32_t)ds::kStackLdsMax - 4096u) {  // the static control block takes the rest
       delete S;
       return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode: %u bytes of LDS per workgroup needed", lay.total);
@@ -334,6 +341,7 @@ int stack_forward(ds_stack_t* S, const void* x, void* y, float* logits, int32_t*
   a.F = d.ffn;
   a.cap = cap;
   a.group = d.quant_group;
+  a.group_mlp = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
   a.eps = d.ln_eps;
   a.gelu_tanh = d.gelu_tanh;
   a.q = reinterpret_cast<uint2*>(base + W.q);
@@ -359,7 +367,7 @@ int stack_forward(ds_stack_t* S, const void* x, void* y, float* logits, int32_t*
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
   const int wsz_i = d.weight_dtype == DS_F32 ? 4 : (d.weight_dtype == DS_F16 ? 2 : 1);
   a.lds = ds::stack_lds_layout(wsz_i, batch <= 1 ? 1 : 4, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->head.V, S->G),
-                               S->nchunk, d.head_dim, d.quant_group, S->n_layers);
+                               S->nchunk, d.head_dim, min_group(d), S->n_layers);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (int rc = prepare_workspace(*S, ws, W.total, st)) return rc;
   if (hipError_t e = ds::launch_stack_decode(wdt, adt, a, st))
