@@ -53,7 +53,11 @@
 extern "C" {
 #endif
 
-typedef enum { DS_F32 = 0, DS_F16 = 1, DS_I8 = 2 } ds_dtype;
+/* DS_BF16: bfloat16 (8-bit significand). A model dtype beside fp16, fp32 and int8 in the config
+ * table of "DeepSpeed MoE 大规模稀疏模型推理实战指南" (the dtype row), and the init_inference dtype
+ * of "解密DeepSpeed推理引擎：如何让大模型在消费级GPU上跑得更快" section 5.1 (mixed precision: bf16
+ * where the device supports it, else fp16). */
+typedef enum { DS_F32 = 0, DS_F16 = 1, DS_I8 = 2, DS_BF16 = 3 } ds_dtype;
 
 typedef enum {
   DS_OK = 0,
@@ -75,7 +79,7 @@ typedef struct {
   int32_t ffn;                /* F: intermediate width, a multiple of 64                        */
   int32_t weight_dtype;       /* ds_dtype of W_qkv, W_o, W_ff1, W_ff2                           */
   int32_t act_dtype;          /* ds_dtype of x, y, the caches, biases and LayerNorm parameters  */
-                              /* supported pairs: (F32,F32) (F16,F16) (I8,F16)                  */
+                              /* supported pairs: (F32,F32) (F16,F16) (I8,F16) (BF16,BF16)      */
   int32_t quant_group;        /* int8: elements per scale along the reduction dimension of      */
                               /* W_qkv and W_o (and of W_ff1, W_ff2 when quant_group_mlp is 0);  */
                               /* 0 for other weight dtypes                                       */

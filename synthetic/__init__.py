@@ -42,8 +42,8 @@ class Workload:
     head_dim: int
     ffn: int
     layers: int
-    weight_dtype: str  # "f32" | "f16" | "i8"
-    act_dtype: str     # "f32" | "f16"
+    weight_dtype: str  # "f32" | "f16" | "i8" | "bf16"
+    act_dtype: str     # "f32" | "f16" | "bf16"
     batch: int
     past: int          # filled cache rows before the step (decode) or P0 (prefill)
     seq: int = 1       # new rows per sequence: 1 for decode, S for prefill

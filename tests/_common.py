@@ -8,8 +8,9 @@ import torch
 
 import synthetic as syn
 
-TOL = {"f32": 1e-4, "f16": 1e-2}  # relative L2 bars: fp32 configs, fp16-activation configs
-TORCH = {"f32": torch.float32, "f16": torch.float16}
+# relative L2 bars: fp32 configs, fp16-activation configs, bf16 configs
+TOL = {"f32": 1e-4, "f16": 1e-2, "bf16": 4e-2}
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
 def rel_l2(a, b) -> float:
@@ -29,7 +30,7 @@ def gpu_layer_and_oracle_weights(wl: syn.Workload, layer: int, device="cuda", ch
     act = TORCH[wl.act_dtype]
     i8 = wl.weight_dtype == "i8"
     cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
-                         dtype={"f32": "fp32", "f16": "fp16", "i8": "int8"}[wl.weight_dtype],
+                         dtype={"f32": "fp32", "f16": "fp16", "i8": "int8", "bf16": "bf16"}[wl.weight_dtype],
                          quant_group=wl.group if i8 else None,
                          quant_group_mlp=wl.group_mlp if i8 and wl.group_mlp else None, **cfg_kw)
     gw, ow = {}, {}

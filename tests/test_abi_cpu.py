@@ -6,6 +6,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import transformer_gpt_layer_amd as tg
 from transformer_gpt_layer_amd import _lib
@@ -60,6 +61,11 @@ def _create(desc, w):
     (dict(ffn=100), _lib.DS_ERR_SHAPE),
     (dict(weight_dtype=2, act_dtype=2), _lib.DS_ERR_DTYPE),
     (dict(weight_dtype=0, act_dtype=1), _lib.DS_ERR_DTYPE),
+    (dict(weight_dtype=3, act_dtype=1), _lib.DS_ERR_DTYPE),      # bf16 weights need bf16 activations
+    (dict(weight_dtype=1, act_dtype=3), _lib.DS_ERR_DTYPE),
+    (dict(weight_dtype=2, act_dtype=3, quant_group=64), _lib.DS_ERR_DTYPE),
+    (dict(weight_dtype=4, act_dtype=4), _lib.DS_ERR_DTYPE),
+    (dict(weight_dtype=3, act_dtype=3, quant_group=64), _lib.DS_ERR_DTYPE),
     (dict(quant_group=64), _lib.DS_ERR_DTYPE),
     (dict(quant_group_mlp=32), _lib.DS_ERR_DTYPE),
     # int8 groups: multiples of 16 that divide the reduction width of their matrices
@@ -153,6 +159,18 @@ def test_config_merge_rules():
         tg.make_config(hidden=256, heads=2, ffn=512, quant_group=64)          # group on fp16 weights
     with pytest.raises(ValueError):
         tg.make_config(hidden=256, heads=2, ffn=512, bogus=1)
+
+
+def test_bf16_is_a_weight_and_activation_dtype():
+    """dtype bf16 (torch.bfloat16): bf16 weights with bf16 activations, caches and parameters."""
+    for v in ("bf16", "bfloat16", torch.bfloat16, "torch.bfloat16"):
+        cfg = tg.make_config(hidden=256, heads=2, ffn=512, dtype=v)
+        assert cfg.dtype == _lib.DS_BF16 and cfg.act_dtype == _lib.DS_BF16 and cfg.torch_act_dtype == torch.bfloat16
+    rc, h = _create(_desc(weight_dtype=3, act_dtype=3), _weights())
+    assert rc == 0, _lib.lib().ds_last_error()
+    _lib.lib().ds_layer_destroy(h)
+    with pytest.raises(ValueError, match="int8"):
+        tg.make_config(hidden=256, heads=2, ffn=512, dtype="bf16", quant_group=64)
 
 
 def test_quantization_setting_is_a_group_count():

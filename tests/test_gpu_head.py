@@ -72,6 +72,8 @@ CASES = {
     "i8-d128-b4-L2-v300": (_wl(hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="i8", act_dtype="f16",
                                group=64, batch=4, past=70, cfg_id=404, ln_std=0.2), 2, 300, True),
     "f32-d64-b1-L2-v129": (_wl(cfg_id=405, ln_std=0.2, bias_std=0.1), 2, 129, False),
+    "bf16-d128-b1-L2-v1000": (_wl(hidden=512, heads=4, head_dim=128, ffn=1024, weight_dtype="bf16", act_dtype="bf16",
+                                  batch=1, past=40, cfg_id=408, ln_std=0.2, bias_std=0.1), 2, 1000, True),
     # finer MLP groups: the LM head keeps the attention group
     "i8-d128-b2-L2-v500-mlp32": (_wl(hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="i8", act_dtype="f16",
                                      group=64, group_mlp=32, batch=2, past=30, cfg_id=407, ln_std=0.2), 2, 500, False),

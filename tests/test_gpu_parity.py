@@ -51,6 +51,11 @@ SMALL = {
                              batch=15, past=300, cfg_id=106),
     "i8-d64-b15-h2048": _wl("c1", hidden=2048, heads=32, head_dim=64, ffn=8192, weight_dtype="i8", act_dtype="f16",
                             group=64, batch=15, past=301, cfg_id=107),
+    # bf16 weights and activations (the per-row GEMV path at every batch)
+    "bf16-d128-b3": _wl("c1", hidden=256, heads=2, head_dim=128, ffn=768, weight_dtype="bf16", act_dtype="bf16",
+                        batch=3, past=70, cfg_id=140),
+    "bf16-d64-b9": _wl("c1", hidden=320, heads=5, head_dim=64, ffn=640, weight_dtype="bf16", act_dtype="bf16",
+                       batch=9, past=129, cfg_id=141),
 }
 
 # Per-layer LayerNorm gamma ~ 1 + N(0, 0.2), beta ~ N(0, 0.2) and biases ~ N(0, 0.1), on every
@@ -74,6 +79,9 @@ CASES.update({
     "i8-g32-b8": (_wl(SMALL["i8-d128-b5"], group=32, ffn=1536, batch=8, cfg_id=130, **AFFINE), True),
     "i8-g128-mlp64-b3": (_wl("c1", hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="i8", act_dtype="f16",
                              group=128, group_mlp=64, batch=3, past=40, cfg_id=131, **AFFINE), False),
+    "bf16-affine-tanh-b1": (_wl(SMALL["bf16-d128-b3"], batch=1, cfg_id=142, **AFFINE), True),
+    "bf16-affine-b4-h1024": (_wl("c1", hidden=1024, heads=8, head_dim=128, ffn=4096, weight_dtype="bf16",
+                                 act_dtype="bf16", batch=4, past=300, cfg_id=143, **AFFINE), False),
     "i8-g16-mlp48-b2": (_wl("c1", hidden=768, heads=12, head_dim=64, ffn=1536, weight_dtype="i8", act_dtype="f16",
                             group=16, group_mlp=48, batch=2, past=21, cfg_id=132, **AFFINE), True),
 })
@@ -222,7 +230,8 @@ def test_read_probe_reads_every_word():
 
 @pytest.mark.parametrize("name,S,P0,tanh", [("f16-d128-b3", 7, 5, False), ("f32-d128-b3", 5, 0, False),
                                              ("i8-d128-b5", 4, 9, False), ("f16-affine-b3", 5, 3, True),
-                                             ("f32-affine-tanh", 6, 2, True), ("i8-affine-tanh-b5", 3, 4, True)])
+                                             ("f32-affine-tanh", 6, 2, True), ("i8-affine-tanh-b5", 3, 4, True),
+                                             ("bf16-d128-b3", 6, 4, False), ("bf16-affine-tanh-b1", 5, 2, True)])
 def test_prefill_matches_oracle(name, S, P0, tanh):
     wl = CASES[name][0]
     gl, ow = gpu_layer_and_oracle_weights(wl, 0, gelu_tanh=tanh)

@@ -60,6 +60,14 @@ CASES = {
     "i8-d128-b3-L3-affine": (_wl("c1", hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="i8",
                                  act_dtype="f16", group=64, batch=3, past=65, cfg_id=214, **AFFINE), 3, False),
     "f32-d64-b1-L3-affine-tanh": (_wl("c1", cfg_id=215, **AFFINE), 3, True),
+    # bf16 weights and activations: one batch row with the LayerNorm in registers, two rows
+    # through LDS with groups of five slices, and the four-row tile at head_dim 64
+    "bf16-d128-b1-L3-affine-tanh": (_wl("c1", hidden=512, heads=4, head_dim=128, ffn=2048, weight_dtype="bf16",
+                                        act_dtype="bf16", batch=1, past=45, cfg_id=224, **AFFINE), 3, True),
+    "bf16-d128-b2-L2-g5": (_wl("c1", hidden=2560, heads=20, head_dim=128, ffn=5120, weight_dtype="bf16",
+                               act_dtype="bf16", batch=2, past=70, cfg_id=225, **AFFINE), 2, False),
+    "bf16-d64-b4-L2": (_wl("c1", hidden=1024, heads=16, head_dim=64, ffn=1536, weight_dtype="bf16",
+                           act_dtype="bf16", batch=4, past=33, cfg_id=226, **AFFINE), 2, False),
     # int8 with a finer MLP group (mlp_extra_grouping) and with groups of 32 throughout
     "i8-d128-b1-L2-g64-mlp32": (_wl("c1", hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="i8",
                                     act_dtype="f16", group=64, group_mlp=32, batch=1, past=50, cfg_id=222, **AFFINE),

@@ -18,24 +18,24 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import DS_F16, DS_F32, DS_I8, check, lib, ptr, stream_handle
+from ._lib import DS_BF16, DS_F16, DS_F32, DS_I8, check, lib, ptr, stream_handle
 
 __all__ = ["LayerConfig", "make_config", "Layer", "KVCache", "Stack", "quantize_i8", "dequantize_i8"]
 
 _DTYPE_NAMES = {"fp32": DS_F32, "float32": DS_F32, "float": DS_F32, "f32": DS_F32,
                 "fp16": DS_F16, "float16": DS_F16, "half": DS_F16, "f16": DS_F16,
-                "int8": DS_I8, "i8": DS_I8}
-_TORCH_DT = {DS_F32: torch.float32, DS_F16: torch.float16, DS_I8: torch.int8}
+                "int8": DS_I8, "i8": DS_I8, "bf16": DS_BF16, "bfloat16": DS_BF16}
+_TORCH_DT = {DS_F32: torch.float32, DS_F16: torch.float16, DS_I8: torch.int8, DS_BF16: torch.bfloat16}
 
 
 def _dtype_code(v) -> int:
     if isinstance(v, torch.dtype):
-        v = {torch.float32: "fp32", torch.float16: "fp16", torch.int8: "int8"}.get(v, str(v))
-    if isinstance(v, int) and v in (DS_F32, DS_F16, DS_I8):
+        v = {torch.float32: "fp32", torch.float16: "fp16", torch.int8: "int8", torch.bfloat16: "bf16"}.get(v, str(v))
+    if isinstance(v, int) and v in (DS_F32, DS_F16, DS_I8, DS_BF16):
         return v
     key = str(v).lower().replace("torch.", "")
     if key not in _DTYPE_NAMES:
-        raise ValueError(f"unsupported dtype {v!r}: fp32, fp16 or int8")
+        raise ValueError(f"unsupported dtype {v!r}: fp32, fp16, bf16 or int8")
     return _DTYPE_NAMES[key]
 
 
@@ -44,7 +44,7 @@ class LayerConfig:
     hidden: int
     heads: int
     ffn: int
-    dtype: int = DS_F16            # weight dtype; activations are fp32 for fp32 weights, else fp16
+    dtype: int = DS_F16            # weight dtype; activations: fp32 for fp32, bf16 for bf16, else fp16
     quant_group: int = 0           # int8 only: elements per scale along the reduction dimension
     quant_group_mlp: int = 0       # int8 only: elements per scale of the MLP matrices (0: quant_group)
     ln_eps: float = 1e-5
@@ -58,7 +58,7 @@ class LayerConfig:
 
     @property
     def act_dtype(self) -> int:
-        return DS_F32 if self.dtype == DS_F32 else DS_F16
+        return self.dtype if self.dtype in (DS_F32, DS_BF16) else DS_F16
 
     @property
     def torch_act_dtype(self) -> torch.dtype:

@@ -13,7 +13,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdslayer.so")
 
-DS_F32, DS_F16, DS_I8 = 0, 1, 2
+DS_F32, DS_F16, DS_I8, DS_BF16 = 0, 1, 2, 3
 DS_OK, DS_ERR_NULL, DS_ERR_SHAPE, DS_ERR_DTYPE, DS_ERR_ALIGN = 0, -1, -2, -3, -4
 DS_ERR_KV_FULL, DS_ERR_UNSUPPORTED, DS_ERR_HIP, DS_ERR_WORKSPACE = -5, -6, -7, -8
 PARTS = ("ln1", "qkv", "attn", "o", "ln2", "ff1", "ff2", "len")  # ds_part names, in enum order

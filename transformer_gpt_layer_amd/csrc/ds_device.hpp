@@ -1,5 +1,5 @@
 // ds_device.hpp -- device helpers shared by the gfx950 kernels of libdslayer.so:
-// 16-byte vector loads, wave64 reductions, fp16 packing, int8 -> fp16 conversion, GeLU.
+// 16-byte vector loads, wave64 reductions, fp16 and bf16 packing, int8 -> fp16 conversion, GeLU.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -8,6 +8,8 @@ namespace ds {
 
 typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16_t;
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -76,6 +78,37 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 
+__device__ __forceinline__ bf162_t as_bf162(uint32_t u) { return __builtin_bit_cast(bf162_t, u); }
+
+// Two packed 16-bit values (element 0 in the low half) of type T as floats, and back (RNE).
+// bf16 widens exactly by a 16-bit shift.
+template <typename T> __device__ __forceinline__ float lo16(uint32_t u) {
+  if constexpr (__is_same(T, half_t)) return (float)as_half2(u).x;
+  else return as_f32(u << 16);
+}
+template <typename T> __device__ __forceinline__ float hi16(uint32_t u) {
+  if constexpr (__is_same(T, half_t)) return (float)as_half2(u).y;
+  else return as_f32(u & 0xffff0000u);
+}
+template <typename T> __device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  if constexpr (__is_same(T, half_t)) {
+    const half2_t h = {(half_t)lo, (half_t)hi};
+    return __builtin_bit_cast(uint32_t, h);
+  } else {
+    const bf162_t h = {(bf16_t)lo, (bf16_t)hi};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+}
+
+// dot of 8 bf16 weights (one 16-byte load) with 8 bf16 activations, accumulated in fp32
+__device__ __forceinline__ float dot8_bf16(u32x4 w, u32x4 a, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(w.x), as_bf162(a.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(w.y), as_bf162(a.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(w.z), as_bf162(a.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(w.w), as_bf162(a.w), acc, false);
+  return acc;
+}
+
 // dot of 8 fp16 weights (one 16-byte load) with 8 fp16 activations, accumulated in fp32
 __device__ __forceinline__ float dot8_f16(u32x4 w, u32x4 a, float acc) {
   acc = __builtin_amdgcn_fdot2(as_half2(w.x), as_half2(a.x), acc, false);
@@ -84,6 +117,11 @@ __device__ __forceinline__ float dot8_f16(u32x4 w, u32x4 a, float acc) {
   acc = __builtin_amdgcn_fdot2(as_half2(w.w), as_half2(a.w), acc, false);
   return acc;
 }
+
+// dot of 8 16-bit weights with 8 activations of the same type (fp16 or bf16)
+template <typename T> __device__ __forceinline__ float dot8(u32x4 w, u32x4 a, float acc);
+template <> __device__ __forceinline__ float dot8<half_t>(u32x4 w, u32x4 a, float acc) { return dot8_f16(w, a, acc); }
+template <> __device__ __forceinline__ float dot8<bf16_t>(u32x4 w, u32x4 a, float acc) { return dot8_bf16(w, a, acc); }
 
 // int8 -> fp16, exactly: with the byte offset to unsigned u = q + 128, the fp16 bit pattern
 // 0x6400 | u encodes 1024 + u (in [1024, 2048) the fp16 spacing is 1), so subtracting
@@ -138,11 +176,13 @@ __device__ __forceinline__ float gelu(float u, bool tanh_form) {
 template <typename WT> struct WTraits;
 template <> struct WTraits<float> { static constexpr int E = 4; typedef float LT; };
 template <> struct WTraits<half_t> { static constexpr int E = 8; typedef half_t LT; };
+template <> struct WTraits<bf16_t> { static constexpr int E = 8; typedef bf16_t LT; };
 template <> struct WTraits<int8_t> { static constexpr int E = 16; typedef half_t LT; };
 
 // ---------------------------------------------------------------- stores in the activation type
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ half_t from_f32<half_t>(float v) { return (half_t)v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return (bf16_t)v; }
 
 }  // namespace ds

@@ -6,7 +6,7 @@
 
 namespace ds {
 
-enum Dt { F32 = 0, F16 = 1, I8 = 2 };
+enum Dt { F32 = 0, F16 = 1, I8 = 2, BF16 = 3 };
 enum GemvKind { KIND_QKV = 0, KIND_OPROJ = 1, KIND_FF1 = 2, KIND_FF2 = 3 };
 
 // Arguments of one fused GEMV launch over `rows` activation rows (rows = batch * tokens).

@@ -47,7 +47,7 @@ __device__ __forceinline__ void gemv_rows(const WT* __restrict__ W, const half_t
       } else if constexpr (sizeof(WT) == 2) {
         const u32x4 a8 = *reinterpret_cast<const u32x4*>(ap);
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r][b] = dot8_f16(w[r], a8, acc[r][b]);
+        for (int r = 0; r < R; ++r) acc[r][b] = dot8<WT>(w[r], a8, acc[r][b]);
       } else {
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 8);
@@ -236,6 +236,7 @@ hipError_t launch_gemv(Dt wdt, Dt adt, GemvKind kind, const GemvArgs& a, hipStre
   if (wdt == F32 && adt == F32) return launch_gemv_t<float, float>(kind, a, st);
   if (wdt == F16 && adt == F16) return launch_gemv_t<half_t, half_t>(kind, a, st);
   if (wdt == I8 && adt == F16) return launch_gemv_t<int8_t, half_t>(kind, a, st);
+  if (wdt == BF16 && adt == BF16) return launch_gemv_t<bf16_t, bf16_t>(kind, a, st);
   return hipErrorInvalidValue;
 }
 
@@ -317,10 +318,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
         } else {
           const uint32_t wv[4] = {kr[q].x, kr[q].y, kr[q].z, kr[q].w};
 #pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const half2_t kk = as_half2(wv[h]);
-            p += qv[2 * h] * (float)kk.x + qv[2 * h + 1] * (float)kk.y;
-          }
+          for (int h = 0; h < 4; ++h) p += qv[2 * h] * lo16<AT>(wv[h]) + qv[2 * h + 1] * hi16<AT>(wv[h]);
         }
         p = group_sum<LPK>(p);
         if (key < ke) {
@@ -337,9 +335,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
             const uint32_t wv[4] = {vr[q].x, vr[q].y, vr[q].z, vr[q].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-              const half2_t vv = as_half2(wv[h]);
-              acc[2 * h] = acc[2 * h] * cf + w * (float)vv.x;
-              acc[2 * h + 1] = acc[2 * h + 1] * cf + w * (float)vv.y;
+              acc[2 * h] = acc[2 * h] * cf + w * lo16<AT>(wv[h]);
+              acc[2 * h + 1] = acc[2 * h + 1] * cf + w * hi16<AT>(wv[h]);
             }
           }
         }
@@ -468,6 +465,7 @@ hipError_t launch_attn_decode_f16(const AttnArgs& a, hipStream_t st) { return la
 hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st) {
   if (adt == F32) return launch_attn_d<float, false>(a, st);
   if (adt == F16) return launch_attn_d<half_t, false>(a, st);
+  if (adt == BF16) return launch_attn_d<bf16_t, false>(a, st);
   return hipErrorInvalidValue;
 }
 

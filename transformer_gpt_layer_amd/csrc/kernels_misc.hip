@@ -75,7 +75,7 @@ hipError_t launch_kv_append(Dt adt, const void* k_new, const void* v_new, void* 
   if (adt == F32)
     hipLaunchKernelGGL(kv_append_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)k_new,
                        (const float*)v_new, (float*)kc, (float*)vc, d_len, batch, ntok, heads, head_dim, cap);
-  else
+  else  // fp16 and bf16: a copy of 16-bit elements
     hipLaunchKernelGGL(kv_append_kernel<half_t>, dim3(blocks), dim3(256), 0, st, (const half_t*)k_new,
                        (const half_t*)v_new, (half_t*)kc, (half_t*)vc, d_len, batch, ntok, heads, head_dim, cap);
   return hipGetLastError();

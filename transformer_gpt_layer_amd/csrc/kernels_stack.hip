@@ -76,6 +76,9 @@ template <> __device__ __forceinline__ void coh_st_act<float>(rsrc_t r, uint32_t
 template <> __device__ __forceinline__ void coh_st_act<half_t>(rsrc_t r, uint32_t idx, float v) {
   __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (half_t)v), r, idx * 2, 0, kAuxCoherent);
 }
+template <> __device__ __forceinline__ void coh_st_act<bf16_t>(rsrc_t r, uint32_t idx, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16_t)v), r, idx * 2, 0, kAuxCoherent);
+}
 
 template <typename T> __device__ __forceinline__ float ldp(const void* p, int i) {
   return (float)reinterpret_cast<const T*>(p)[i];
@@ -90,7 +93,7 @@ template <typename T> __device__ __forceinline__ uint32_t ldraw(const void* p, i
   else return reinterpret_cast<const uint32_t*>(p)[i];
 }
 template <typename T> __device__ __forceinline__ float cvraw(uint32_t u) {
-  if constexpr (sizeof(T) == 2) return (float)__builtin_bit_cast(half_t, (uint16_t)u);
+  if constexpr (sizeof(T) == 2) return lo16<T>(u);
   else return __builtin_bit_cast(float, u);
 }
 
@@ -218,10 +221,11 @@ __device__ __forceinline__ void tstore(rsrc_t r, uint32_t idx, float v, uint32_t
   __builtin_amdgcn_raw_buffer_store_b64(pv, r, idx * 8u, 0, kAuxCoherent);
 }
 
-// Two fp16 values packed in the value word of one tagged 8-byte store (element 2i low, 2i+1 high).
-__device__ __forceinline__ void tstore_pair(rsrc_t r, uint32_t pair, half_t lo, half_t hi, uint32_t tag) {
-  const uint32_t v = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-  const u32x2 pv = {v, tag};
+// Two 16-bit values (fp16 or bf16, rounded from fp32) packed in the value word of one tagged 8-byte
+// store (element 2i low, 2i+1 high).
+template <typename AT>
+__device__ __forceinline__ void tstore_pair(rsrc_t r, uint32_t pair, float lo, float hi, uint32_t tag) {
+  const u32x2 pv = {pack16<AT>(lo, hi), tag};
   __builtin_amdgcn_raw_buffer_store_b64(pv, r, pair * 8u, 0, kAuxCoherent);
 }
 
@@ -505,7 +509,7 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
               if constexpr (sizeof(WT) == 4) {
                 acc[b] = dot4_f32(ring[u][k], *reinterpret_cast<const float4_t*>(apk), acc[b]);
               } else if constexpr (sizeof(WT) == 2) {
-                acc[b] = dot8_f16(ring[u][k], *reinterpret_cast<const u32x4*>(apk), acc[b]);
+                acc[b] = dot8<WT>(ring[u][k], *reinterpret_cast<const u32x4*>(apk), acc[b]);
               } else {
                 acc[b] = fmaf(dot16_i8(ring[u][k], *reinterpret_cast<const u32x4*>(apk),
                                        *reinterpret_cast<const u32x4*>(apk + 8)),
@@ -638,9 +642,8 @@ __device__ __forceinline__ void load_rows_plain(const void* in, int B, int K, fl
         const uint32_t ww[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          const half2_t p = as_half2(ww[h]);
-          raw[j * V + 2 * h] = (float)p.x;
-          raw[j * V + 2 * h + 1] = (float)p.y;
+          raw[j * V + 2 * h] = lo16<AT>(ww[h]);
+          raw[j * V + 2 * h + 1] = hi16<AT>(ww[h]);
         }
       }
     }
@@ -713,9 +716,9 @@ __device__ __forceinline__ void load_regs_plain(const void* in, int n, int st, f
     const int j = st + u * NT;
     const uint32_t off = j < nv ? (uint32_t)(j * 2 * sizeof(AT)) : kOutOfRange;
     if constexpr (sizeof(AT) == 2) {
-      const half2_t h = as_half2(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-      x[u][0] = (float)h.x;
-      x[u][1] = (float)h.y;
+      const uint32_t h = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+      x[u][0] = lo16<AT>(h);
+      x[u][1] = hi16<AT>(h);
     } else {
       const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
       x[u][0] = as_f32(w.x);
@@ -812,11 +815,10 @@ __device__ __forceinline__ bool stage_ln_regs(Ctl& c, const StackArgs& a, uint32
     const int b = BM == 1 ? 0 : 2 * j / K;
     float g0, g1, b0, b1;
     if constexpr (sizeof(AT) == 2) {
-      const half2_t gh = as_half2(gw[u].x), bh = as_half2(bw[u].x);
-      g0 = (float)gh.x;
-      g1 = (float)gh.y;
-      b0 = (float)bh.x;
-      b1 = (float)bh.y;
+      g0 = lo16<AT>(gw[u].x);
+      g1 = hi16<AT>(gw[u].x);
+      b0 = lo16<AT>(bw[u].x);
+      b1 = hi16<AT>(bw[u].x);
     } else {
       g0 = as_f32(gw[u].x);
       g1 = as_f32(gw[u].y);
@@ -935,14 +937,10 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
         vr[it] = u32x4{__builtin_bit_cast(uint32_t, vn[0]), __builtin_bit_cast(uint32_t, vn[1]),
                        __builtin_bit_cast(uint32_t, vn[2]), __builtin_bit_cast(uint32_t, vn[3])};
       } else {
-        half8_t kh, vh;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kh[e] = (half_t)kn[e];
-          vh[e] = (half_t)vn[e];
-        }
-        kr[it] = __builtin_bit_cast(u32x4, kh);
-        vr[it] = __builtin_bit_cast(u32x4, vh);
+        kr[it] = u32x4{pack16<AT>(kn[0], kn[1]), pack16<AT>(kn[2], kn[3]), pack16<AT>(kn[4], kn[5]),
+                       pack16<AT>(kn[6], kn[7])};
+        vr[it] = u32x4{pack16<AT>(vn[0], vn[1]), pack16<AT>(vn[2], vn[3]), pack16<AT>(vn[4], vn[5]),
+                       pack16<AT>(vn[6], vn[7])};
       }
     }
   }
@@ -960,10 +958,7 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
     } else {
       const uint32_t wv[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const half2_t kk = as_half2(wv[h]);
-        p += qv[2 * h] * (float)kk.x + qv[2 * h + 1] * (float)kk.y;
-      }
+      for (int h = 0; h < 4; ++h) p += qv[2 * h] * lo16<AT>(wv[h]) + qv[2 * h + 1] * hi16<AT>(wv[h]);
     }
     p = group_sum<LPK>(p);
     sc[it] = valid[it] ? p : kNeg;
@@ -986,9 +981,8 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
       const uint32_t wv[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const half2_t vv = as_half2(wv[h]);
-        acc[2 * h] += p * (float)vv.x;
-        acc[2 * h + 1] += p * (float)vv.y;
+        acc[2 * h] += p * lo16<AT>(wv[h]);
+        acc[2 * h + 1] += p * hi16<AT>(wv[h]);
       }
     }
   }
@@ -1239,15 +1233,14 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     {
       const rsrc_t rf = make_rsrc(a.f, (uint32_t)(B * F * 8));
       if constexpr (sizeof(AT) == 2) {
-        // fp16 f: pairs of rows (f0 and nf are even) in one tagged store each, half the bytes the
+        // 16-bit f: pairs of rows (f0 and nf are even) in one tagged store each, half the bytes the
         // FF2 staging polls
         for (int t = st; t < (nf / 2) * B; t += NT) {
           const int pl = t / B, b = t - pl * B, rl = 2 * pl, n = f0 + rl;
           const float b0 = t == st ? cvraw<AT>(pre_f0) : ldp<AT>(L.b_ff1, n);
           const float b1 = t == st ? cvraw<AT>(pre_f1) : ldp<AT>(L.b_ff1, n + 1);
-          const half_t g0 = (half_t)gelu(row_sum(rl, b) + b0, a.gelu_tanh != 0);
-          const half_t g1 = (half_t)gelu(row_sum(rl + 1, b) + b1, a.gelu_tanh != 0);
-          tstore_pair(rf, (uint32_t)((b * F + n) / 2), g0, g1, t_f);
+          tstore_pair<AT>(rf, (uint32_t)((b * F + n) / 2), gelu(row_sum(rl, b) + b0, a.gelu_tanh != 0),
+                          gelu(row_sum(rl + 1, b) + b1, a.gelu_tanh != 0), t_f);
         }
       } else {
         for (int t = st; t < nf * B; t += NT) {
@@ -1266,11 +1259,10 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff2, y0, ny, F, a.group_mlp, scl, st);
     zero_rows(F);
     if constexpr (sizeof(AT) == 2) {
-      // pair i holds f elements 2i and 2i + 1 of the [B][F] rows
+      // pair i holds f elements 2i and 2i + 1 of the [B][F] rows, already in the staged type
+      static_assert(__is_same(LT, AT), "16-bit activations are staged in their own type");
       if (!poll_range(c, a, a.f, B * F / 2, t_f, st, [&](int i, float v) {
-            const uint32_t u = __builtin_bit_cast(uint32_t, v);
-            act[2 * i] = (LT)__builtin_bit_cast(half_t, (uint16_t)(u & 0xffffu));
-            act[2 * i + 1] = (LT)__builtin_bit_cast(half_t, (uint16_t)(u >> 16));
+            reinterpret_cast<uint32_t*>(act)[i] = __builtin_bit_cast(uint32_t, v);
           }))
         return;
     } else if (!poll_range(c, a, a.f, B * F, t_f, st, [&](int i, float v) { act[i] = (LT)v; })) {
@@ -1426,7 +1418,7 @@ static const void* kernel_ptr() {
 // Slices per worker group: 5 when every row of the stack's products (K = hidden or ffn) holds a
 // multiple of 5 slices (the GPT-Neo-2.7B and 13B widths), else 1.
 int stack_group_slices(Dt wdt, int H, int F) {
-  const int sl = wdt == F32 ? 256 : (wdt == F16 ? 512 : 1024);
+  const int sl = wdt == F32 ? 256 : (wdt == I8 ? 1024 : 512);
   return (H / sl) % 5 == 0 && (F / sl) % 5 == 0 ? 5 : 1;
 }
 
@@ -1446,6 +1438,7 @@ static const void* pick(Dt wdt, Dt adt, int B, int D, int GS) {
   }
   if (wdt == F16 && adt == F16) DS_PICK(half_t, half_t)
   if (wdt == I8 && adt == F16) DS_PICK(int8_t, half_t)
+  if (wdt == BF16 && adt == BF16) DS_PICK(bf16_t, bf16_t)
   if (wdt == F32 && adt == F32 && one) {
     if (GS == 5) return D == 64 ? kernel_ptr<float, float, 1, 64, 5>() : kernel_ptr<float, float, 1, 128, 5>();
     return D == 64 ? kernel_ptr<float, float, 1, 64, 1>() : kernel_ptr<float, float, 1, 128, 1>();

@@ -349,7 +349,8 @@ int ds_layer_create(const ds_layer_desc* desc, const ds_layer_weights* w, ds_lay
     return fail(DS_ERR_SHAPE, "hidden %d and ffn %d must be positive multiples of 64 (hidden <= 65536, ffn <= 262144)", d.hidden, d.ffn);
   const bool pair_ok = (d.weight_dtype == DS_F32 && d.act_dtype == DS_F32) ||
                        (d.weight_dtype == DS_F16 && d.act_dtype == DS_F16) ||
-                       (d.weight_dtype == DS_I8 && d.act_dtype == DS_F16);
+                       (d.weight_dtype == DS_I8 && d.act_dtype == DS_F16) ||
+                       (d.weight_dtype == DS_BF16 && d.act_dtype == DS_BF16);
   if (!pair_ok) return fail(DS_ERR_DTYPE, "unsupported (weight, activation) dtype pair (%d, %d)", d.weight_dtype, d.act_dtype);
   if (d.weight_dtype == DS_I8) {
     // a lane's 16 consecutive codes share one scale: groups are multiples of 16 dividing the

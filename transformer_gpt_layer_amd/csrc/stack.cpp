@@ -92,7 +92,8 @@ int stack_forward(ds_stack_t* S, const void* x, void* y, float* logits, int32_t*
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
-int slice_elems(int wdt) { return wdt == DS_F32 ? 256 : (wdt == DS_F16 ? 512 : 1024); }
+int slice_elems(int wdt) { return wdt == DS_F32 ? 256 : (wdt == DS_I8 ? 1024 : 512); }
+int weight_bytes(int wdt) { return wdt == DS_F32 ? 4 : (wdt == DS_I8 ? 1 : 2); }
 size_t act_bytes(int adt) { return adt == DS_F32 ? 4 : 2; }
 
 // The smallest int8 scale group among the stack's matrices (1 for other weight dtypes).
@@ -177,7 +178,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
     if (std::memcmp(&layers[l]->desc, &d, sizeof d) != 0)
       return ds::set_error(DS_ERR_SHAPE, "layer %d has a different description from layer 0", l);
   const int sl = slice_elems(d.weight_dtype);
-  const size_t wsz = d.weight_dtype == DS_F32 ? 4 : (d.weight_dtype == DS_F16 ? 2 : 1);
+  const size_t wsz = (size_t)weight_bytes(d.weight_dtype);
   if ((size_t)d.hidden * d.ffn * wsz >= (1ull << 31) || (size_t)3 * d.hidden * d.hidden * wsz >= (1ull << 31))
     return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode needs every weight matrix under 2 GiB");
   if (d.hidden % sl || d.ffn % sl || d.hidden > 8192)
@@ -213,7 +214,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
   hipError_t e = hipGetDevice(&S->device);
   int cus = 0;
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, S->device);
-  const int wsz_i = d.weight_dtype == DS_F32 ? 4 : (d.weight_dtype == DS_F16 ? 2 : 1);
+  const int wsz_i = weight_bytes(d.weight_dtype);
   const int bm = max_batch <= 1 ? 1 : 4;
   int G = cus;  // one workgroup of kStackThreads per CU
   for (int iter = 0; e == hipSuccess && iter < 3; ++iter) {
@@ -365,7 +366,7 @@ int stack_forward(ds_stack_t* S, const void* x, void* y, float* logits, int32_t*
   a.logits = logits;
   a.tokens = tokens;
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
-  const int wsz_i = d.weight_dtype == DS_F32 ? 4 : (d.weight_dtype == DS_F16 ? 2 : 1);
+  const int wsz_i = weight_bytes(d.weight_dtype);
   a.lds = ds::stack_lds_layout(wsz_i, batch <= 1 ? 1 : 4, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->head.V, S->G),
                                S->nchunk, d.head_dim, min_group(d), S->n_layers);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
