@@ -44,6 +44,8 @@ def lib():
         L.ora_fp16_to_double.restype = C.c_double
         L.ora_quantize_i8.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         L.ora_dequantize_i8.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, _D]
+        L.ora_moe_forward.argtypes = [C.c_void_p, C.c_void_p, _D, C.c_int, C.c_void_p, _D, C.c_void_p, _D]
+        L.ora_moe_forward.restype = C.c_int
         _LIB = L
     return _LIB
 
@@ -113,6 +115,44 @@ def argmax(v):
     if v.ndim != 1 or v.size < 1:
         raise ValueError("argmax needs a non-empty 1-D array")
     return int(lib().ora_argmax(_p(v), v.size))
+
+
+# ---------------------------------------------------------------- the MoE expert FF
+class _MoeDesc(C.Structure):
+    _fields_ = [("hidden", C.c_int), ("ffn", C.c_int), ("experts", C.c_int), ("top_k", C.c_int),
+                ("ln_eps", C.c_double), ("gelu_tanh", C.c_int), ("residual", C.c_int), ("combine", C.c_int)]
+
+
+class _MoeWeights(C.Structure):
+    _fields_ = [(n, _D) for n in ("ln_g", "ln_b", "w_gate", "w1", "b1", "w2", "b2", "r_w1", "r_b1", "r_w2", "r_b2")]
+
+
+def moe_forward(w, x2, top_k=1, eps=1e-5, gelu_tanh=False, combine=0, force_sel=None):
+    """The MoE expert FF ("DeepSpeed MoE 大规模稀疏模型推理实战指南", the MoE sections; the gate and
+    combine readings are in oracle.h). w: dict with ln_g, ln_b [H], w_gate [E,H], w1 [E,F,H],
+    b1 [E,F], w2 [E,H,F], b2 [E,H], and r_w1, r_b1, r_w2, r_b2 for the 'residual' type (else
+    absent). x2: [T,H]. force_sel: [T,top_k] experts to use instead of the top-k. Returns
+    (y [T,H], sel [T,top_k] int32, wgt [T,top_k])."""
+    arr = {k: _f64(v) for k, v in w.items() if v is not None}
+    E, F, H = arr["w1"].shape
+    x2 = _f64(x2)
+    T = x2.shape[0]
+    residual = "r_w1" in arr
+    d = _MoeDesc(H, F, E, top_k, eps, int(gelu_tanh), int(residual), int(combine))
+    cw = _MoeWeights(*[(_p(arr[n]) if n in arr else None) for n, _ in _MoeWeights._fields_])
+    y = np.empty((T, H))
+    sel = np.empty((T, top_k), dtype=np.int32)
+    wgt = np.empty((T, top_k))
+    fs = None
+    if force_sel is not None:
+        fs = np.ascontiguousarray(force_sel, dtype=np.int32)
+        if fs.shape != (T, top_k):
+            raise ValueError("force_sel must be [tokens, top_k]")
+    rc = lib().ora_moe_forward(C.byref(d), C.byref(cw), _p(x2), T, fs.ctypes.data if fs is not None else None,
+                               _p(y), sel.ctypes.data, _p(wgt))
+    if rc != 0:
+        raise ValueError("moe_forward: inconsistent shapes or a forced expert out of range")
+    return y, sel, wgt
 
 
 # ---------------------------------------------------------------- fp16 and int8

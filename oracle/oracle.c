@@ -183,6 +183,67 @@ int ora_argmax(const double* v, int n) {
   return best;
 }
 
+/* One expert (or the residual MLP): out = W2 GeLU(W1 h + b1) + b2. */
+static void moe_expert(const double* w1, const double* b1, const double* w2, const double* b2, const double* h,
+                       int H, int F, int tanh_form, double* u, double* out) {
+  ora_linear(w1, b1, h, F, H, u);
+  for (int i = 0; i < F; ++i) u[i] = ora_gelu(u[i], tanh_form);
+  ora_linear(w2, b2, u, H, F, out);
+}
+
+/* The MoE expert FF ([MP], MoE sections; readings in oracle.h). */
+int ora_moe_forward(const ora_moe_desc* d, const ora_moe_weights* w, const double* x2, int tokens,
+                    const int* force_sel, double* y, int* sel, double* wgt) {
+  const int H = d->hidden, F = d->ffn, E = d->experts, K = d->top_k;
+  if (H < 1 || F < 1 || E < 1 || K < 1 || K > E || tokens < 0) return -1;
+  if (d->residual && !(w->r_w1 && w->r_b1 && w->r_w2 && w->r_b2)) return -1;
+  double* h = (double*)malloc(sizeof(double) * (size_t)H);
+  double* logit = (double*)malloc(sizeof(double) * (size_t)E);
+  double* p = (double*)malloc(sizeof(double) * (size_t)E);
+  double* q = (double*)malloc(sizeof(double) * (size_t)E);
+  double* u = (double*)malloc(sizeof(double) * (size_t)F);
+  double* o = (double*)malloc(sizeof(double) * (size_t)H);
+  int* chosen = (int*)malloc(sizeof(int) * (size_t)K);
+  int rc = 0;
+  for (int t = 0; t < tokens && rc == 0; ++t) {
+    const double* xt = x2 + (size_t)t * H;
+    double* yt = y + (size_t)t * H;
+    ora_layernorm(xt, H, w->ln_g, w->ln_b, d->ln_eps, h);
+    ora_linear(w->w_gate, NULL, h, E, H, logit);
+    ora_softmax(logit, E, p);
+    /* the k largest probabilities, one at a time: argmax over the experts not yet taken */
+    for (int e = 0; e < E; ++e) q[e] = p[e];
+    for (int i = 0; i < K; ++i) {
+      if (force_sel) {
+        chosen[i] = force_sel[(size_t)t * K + i];
+        if (chosen[i] < 0 || chosen[i] >= E) rc = -1;
+      } else {
+        chosen[i] = ora_argmax(q, E);
+        q[chosen[i]] = -1.0; /* below every probability */
+      }
+    }
+    if (rc) break;
+    double psum = 0.0;
+    for (int i = 0; i < K; ++i) psum += p[chosen[i]];
+    for (int c = 0; c < H; ++c) yt[c] = xt[c];
+    for (int i = 0; i < K; ++i) {
+      const int e = chosen[i];
+      const double wi = d->combine ? p[e] : p[e] / psum;
+      moe_expert(w->w1 + (size_t)e * F * H, w->b1 + (size_t)e * F, w->w2 + (size_t)e * H * F, w->b2 + (size_t)e * H, h,
+                 H, F, d->gelu_tanh, u, o);
+      for (int c = 0; c < H; ++c) yt[c] += wi * o[c];
+      if (sel) sel[(size_t)t * K + i] = e;
+      if (wgt) wgt[(size_t)t * K + i] = wi;
+    }
+    if (d->residual) {
+      moe_expert(w->r_w1, w->r_b1, w->r_w2, w->r_b2, h, H, F, d->gelu_tanh, u, o);
+      for (int c = 0; c < H; ++c) yt[c] += o[c];
+    }
+  }
+  free(h); free(logit); free(p); free(q); free(u); free(o); free(chosen);
+  return rc;
+}
+
 /* IEEE 754 binary16 from a double, rounding to nearest with ties to even.
  * Normal numbers have an 11-bit significand and exponents -14..15; below 2^-14 the spacing is
  * the fixed 2^-24 (subnormals); a rounded magnitude of 2^16 or more becomes infinity. */

@@ -13,7 +13,8 @@
  *         3.3: the mechanisms), section 五 (5.2: int8 inference with quantize_groups), section 四
  *         (4.2: dtype fp32/fp16/int8, max_out_tokens).
  *   [MP]  "DeepSpeed MoE 大规模稀疏模型推理实战指南" (blog.gitcode.com) -- the inference-config table,
- *         row triangular_masking (default True: the attention score mask type).
+ *         row triangular_masking (default True: the attention score mask type); the MoE sections:
+ *         a number of experts per MoE layer, MoE types 'standard' and 'residual' (PR-MoE).
  *
  * Where the pages are silent the oracle takes these readings (each is listed in the design doc):
  *   LayerNorm uses the biased variance and eps = 1e-5 unless the caller passes another eps;
@@ -21,7 +22,8 @@
  *   Q, K, V are rows [0,H), [H,2H), [2H,3H) of the fused projection, head j owning [j*d,(j+1)*d);
  *   the order inside region 3 is Wo -> +bo -> +x -> LN2 -> W1 -> +b1 -> GeLU, then W2 -> +b2 -> +x2;
  *   keys past a row's own position are excluded from its softmax (not added as -inf);
- *   int8 groups are 64 consecutive elements along the reduction dimension of one weight row,
+ *   int8 groups are consecutive elements along the reduction dimension of one weight row (64 in
+ *   the configs; the caller passes the size, finer for the MLP matrices with mlp_extra_grouping),
  *   scale = fp16_RNE(amax/127), code = clamp(round_half_even(w/scale), -127, 127), amax = 0 -> 0.
  *
  * Layouts: every matrix is [N][K] row-major (K contiguous); activations are [B][T][width];
@@ -81,6 +83,35 @@ void ora_lm_head(const double* y, int H, const double* g, const double* b, doubl
 /* Greedy choice: the index of the largest of n values; among equal largest values, the smallest
  * index. n >= 1; the values are finite. */
 int  ora_argmax(const double* v, int n);
+
+/* ---- the MoE expert FF ([MP]: num_experts per layer, type standard | residual) ----
+ * The pages name the experts and the two types but not the gate. Readings (listed in the design doc):
+ * h = LN(x2; ln_g, ln_b); gate logits = W_gate h (no bias); p = softmax over the E experts; the
+ * top_k experts are the k largest p, taken one at a time, the smallest index first among equal
+ * values; an expert is the dense FF, FF_e(h) = W2_e GeLU(W1_e h + b1_e) + b2_e; the combine
+ * weights are the chosen p renormalized to sum 1 (combine 0) or the p themselves (combine 1);
+ * 'residual' adds a dense MLP of the same form: y = x2 + sum_i w_i FF_{e_i}(h) [+ FF_r(h)]. */
+typedef struct {
+  int hidden, ffn, experts, top_k;
+  double ln_eps;
+  int gelu_tanh;
+  int residual;  /* 1: PR-MoE, a dense MLP added to the experts' output */
+  int combine;   /* 0: chosen probabilities renormalized; 1: the softmax probabilities */
+} ora_moe_desc;
+
+typedef struct {
+  const double *ln_g, *ln_b;                /* [H]                                   */
+  const double *w_gate;                     /* [E][H]                                */
+  const double *w1, *b1;                    /* [E][F][H], [E][F]                     */
+  const double *w2, *b2;                    /* [E][H][F], [E][H]                     */
+  const double *r_w1, *r_b1, *r_w2, *r_b2;  /* the residual MLP, or NULL (standard) */
+} ora_moe_weights;
+
+/* x2, y: [T][H]. sel, wgt: [T][top_k] outputs (may be NULL). force_sel: [T][top_k] experts to use
+ * in place of the top-k (their weights still come from p), or NULL. Returns 0, or -1 on a bad
+ * shape or a forced expert out of range. */
+int ora_moe_forward(const ora_moe_desc* d, const ora_moe_weights* w, const double* x2, int tokens,
+                    const int* force_sel, double* y, int* sel, double* wgt);
 
 /* ---- IEEE binary16 ---- */
 uint16_t ora_fp16_from_double(double v); /* round to nearest, ties to even; overflow -> inf */

@@ -390,3 +390,135 @@ def test_lm_head_matches_torch_float64_and_greedy_choice():
     logits = oracle.lm_head(y, g, b, w)
     assert np.max(np.abs(logits - ref.numpy())) < 1e-13
     assert oracle.argmax(logits) == int(torch.argmax(ref))
+
+
+# ------------------------------------------------------------------ the MoE expert FF
+def _rand_moe(H, F, E, seed, residual=False):
+    r = np.random.default_rng(seed)
+    w = {"ln_g": r.normal(1, 0.1, H), "ln_b": r.normal(0, 0.1, H), "w_gate": r.normal(0, 0.3, (E, H)),
+         "w1": r.normal(0, 0.05, (E, F, H)), "b1": r.normal(0, 0.1, (E, F)),
+         "w2": r.normal(0, 0.05, (E, H, F)), "b2": r.normal(0, 0.1, (E, H))}
+    if residual:
+        w.update({"r_w1": r.normal(0, 0.05, (F, H)), "r_b1": r.normal(0, 0.1, F),
+                  "r_w2": r.normal(0, 0.05, (H, F)), "r_b2": r.normal(0, 0.1, H)})
+    return w
+
+
+def _dense_ffn_via_layer(x2, ln_g, ln_b, w1, b1, w2, b2, tanh=False):
+    """x2 + W2 GeLU(W1 LN(x2) + b1) + b2 through the (separately pinned) layer oracle: with
+    W_o = 0 and b_o = 0 the attention adds nothing, so x2 = x and the layer's region 3 and 4 are
+    exactly the dense FF of x2."""
+    T, H = x2.shape
+    F = w1.shape[0]
+    lw = _rand_layer(H, 2, F, 99, zero=("w_o", "b_o"))
+    lw.update({"ln2_g": ln_g, "ln2_b": ln_b, "w_ff1": w1, "b_ff1": b1, "w_ff2": w2, "b_ff2": b2})
+    kc, vc = np.zeros((T, 2, 4, H // 2)), np.zeros((T, 2, 4, H // 2))
+    lens = np.zeros(T, dtype=np.int32)
+    return oracle.layer_forward(oracle.Desc(H, 2, H // 2, F, gelu_tanh=tanh), lw, kc, vc, lens, x2[:, None, :])[:, 0]
+
+
+@pytest.mark.parametrize("tanh", [False, True])
+def test_moe_single_expert_is_the_dense_ffn(tanh):
+    H, F = 16, 24
+    w = _rand_moe(H, F, 1, 31)
+    x2 = rng.normal(0, 1, (3, H))
+    y, sel, wgt = oracle.moe_forward(w, x2, top_k=1, gelu_tanh=tanh)
+    ref = _dense_ffn_via_layer(x2, w["ln_g"], w["ln_b"], w["w1"][0], w["b1"][0], w["w2"][0], w["b2"][0], tanh)
+    assert np.all(sel == 0) and np.all(wgt == 1.0)
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-13)
+
+
+def test_moe_identical_experts_reduce_to_the_dense_ffn():
+    # the combine weights sum to 1 whichever experts are chosen: renormalized top-2, or every
+    # expert with its softmax probability
+    H, F, E = 16, 20, 4
+    one = _rand_moe(H, F, 1, 32)
+    w = dict(one, w_gate=rng.normal(0, 1, (E, H)))
+    for n in ("w1", "b1", "w2", "b2"):
+        w[n] = np.repeat(one[n], E, axis=0)
+    x2 = rng.normal(0, 1, (5, H))
+    ref = _dense_ffn_via_layer(x2, w["ln_g"], w["ln_b"], one["w1"][0], one["b1"][0], one["w2"][0], one["b2"][0])
+    y2, _, wgt2 = oracle.moe_forward(w, x2, top_k=2, combine=0)
+    yall, _, wgta = oracle.moe_forward(w, x2, top_k=E, combine=1)
+    np.testing.assert_allclose(wgt2.sum(1), 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(wgta.sum(1), 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(y2, ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(yall, ref, rtol=0, atol=1e-13)
+
+
+def test_moe_permuting_the_experts_permutes_the_choice_only():
+    H, F, E, k = 12, 16, 6, 2
+    w = _rand_moe(H, F, E, 33)
+    x2 = rng.normal(0, 1, (7, H))
+    y, sel, wgt = oracle.moe_forward(w, x2, top_k=k)
+    perm = np.array([3, 0, 5, 1, 4, 2])         # new expert i is old expert perm[i]
+    wp = dict(w)
+    for n in ("w_gate", "w1", "b1", "w2", "b2"):
+        wp[n] = w[n][perm]
+    yp, selp, wgtp = oracle.moe_forward(wp, x2, top_k=k)
+    assert np.array_equal(perm[selp], sel)
+    # equal up to the order of the softmax denominator's sum
+    np.testing.assert_allclose(wgtp, wgt, rtol=1e-14)
+    np.testing.assert_allclose(yp, y, rtol=0, atol=1e-14)
+    # the chosen experts are the k most probable, most probable first
+    for t in range(x2.shape[0]):
+        h = oracle.layernorm(x2[t], w["ln_g"], w["ln_b"])
+        p = oracle.softmax(w["w_gate"] @ h)
+        order = sorted(range(E), key=lambda e: (-p[e], e))
+        assert list(sel[t]) == order[:k]
+
+
+def test_moe_gate_by_hand():
+    """H = 4, x2 = (1, -1, 1, -1): LN gives h = x2 / sqrt(1 + eps) (mean 0, variance 1). Gate row e
+    is c_e (1, -1, 1, -1) / 4, so logit_e = c_e / sqrt(1 + eps) with c = (0, 2, 1, 2, -1). The two
+    largest are the tied experts 1 and 3, taken in index order, each with renormalized weight 1/2.
+    Every expert has W1 = W2 = 0 and b1 = 0 (GeLU(0) = 0), so FF_e(h) = b2_e, the e-th basis
+    vector times (e + 1): y = x2 + (2 e_1 + 4 e_3) / 2 = (1, 0, 1, 1)."""
+    H, F, E = 4, 3, 5
+    c = np.array([0.0, 2.0, 1.0, 2.0, -1.0])
+    s = np.array([1.0, -1.0, 1.0, -1.0])
+    b2 = np.zeros((E, H))
+    for e in range(E):
+        b2[e, e % H] = e + 1
+    w = {"ln_g": np.ones(H), "ln_b": np.zeros(H), "w_gate": np.outer(c, s) / 4,
+         "w1": np.zeros((E, F, H)), "b1": np.zeros((E, F)), "w2": np.zeros((E, H, F)), "b2": b2}
+    x2 = s[None, :]
+    y, sel, wgt = oracle.moe_forward(w, x2, top_k=2, combine=0)
+    assert list(sel[0]) == [1, 3] and list(wgt[0]) == [0.5, 0.5]
+    np.testing.assert_allclose(y[0], [1.0, 0.0, 1.0, 1.0], rtol=0, atol=1e-15)
+    # combine 1: the softmax probabilities themselves, exp(2a) / sum_e exp(c_e a), a = 1/sqrt(1+eps)
+    a = 1 / math.sqrt(1 + 1e-5)
+    p1 = math.exp(2 * a) / (1 + 2 * math.exp(2 * a) + math.exp(a) + math.exp(-a))
+    y1, sel1, wgt1 = oracle.moe_forward(w, x2, top_k=2, combine=1)
+    assert list(sel1[0]) == [1, 3]
+    np.testing.assert_allclose(wgt1[0], [p1, p1], rtol=1e-14)
+    np.testing.assert_allclose(y1[0], s + p1 * (2 * np.eye(H)[1] + 4 * np.eye(H)[3]), rtol=0, atol=1e-14)
+    # top-1 with the tie: the smaller index
+    _, selt, _ = oracle.moe_forward(w, x2, top_k=1)
+    assert int(selt[0, 0]) == 1
+
+
+def test_moe_residual_type_adds_the_dense_mlp():
+    H, F, E = 16, 24, 3
+    w = _rand_moe(H, F, E, 34, residual=True)
+    x2 = rng.normal(0, 1, (4, H))
+    y_res, sel, wgt = oracle.moe_forward(w, x2, top_k=2)
+    std = {k: v for k, v in w.items() if not k.startswith("r_")}
+    y_std, sel2, _ = oracle.moe_forward(std, x2, top_k=2)
+    assert np.array_equal(sel, sel2)
+    dense = _dense_ffn_via_layer(x2, w["ln_g"], w["ln_b"], w["r_w1"], w["r_b1"], w["r_w2"], w["r_b2"])
+    np.testing.assert_allclose(y_res - y_std, dense - x2, rtol=0, atol=1e-13)
+
+
+def test_moe_forced_selection():
+    H, F, E = 8, 8, 4
+    w = _rand_moe(H, F, E, 35)
+    x2 = rng.normal(0, 1, (3, H))
+    y, sel, wgt = oracle.moe_forward(w, x2, top_k=2)
+    yf, self_, wgtf = oracle.moe_forward(w, x2, top_k=2, force_sel=sel)
+    assert np.array_equal(y, yf) and np.array_equal(sel, self_) and np.array_equal(wgt, wgtf)
+    other = (sel + 1) % E
+    yo, selo, _ = oracle.moe_forward(w, x2, top_k=2, force_sel=other)
+    assert np.array_equal(selo, other) and not np.allclose(yo, y)
+    with pytest.raises(ValueError):
+        oracle.moe_forward(w, x2, top_k=2, force_sel=np.full((3, 2), E))
