@@ -294,6 +294,68 @@ int ds_stack_check(ds_stack_t* stack);
  * error flag and every workgroup leaves the launch. */
 int ds_stack_set_timeout_us(ds_stack_t* stack, int64_t microseconds);
 
+/* ---------------------------------------------------------------- the MoE expert FF
+ * The expert feed-forward block of an MoE layer ("DeepSpeed MoE 大规模稀疏模型推理实战指南", the MoE
+ * sections: a number of experts per MoE layer, the layer types 'standard' and 'residual'
+ * (PR-MoE)). It takes the residual stream after attention, x2, and returns y for T tokens:
+ *   h = LN(x2; ln_g, ln_b);  p = softmax over the experts of W_gate h (no bias);
+ *   the top_k experts are the k largest p (the smallest index first among equal values);
+ *   w_i = p_i / sum of the chosen p (combine 0), or p_i itself (combine 1);
+ *   y = x2 + sum_i w_i FF_{e_i}(h)  [+ FF_r(h) for the residual type],
+ *   FF(h) = W2 GeLU(W1 h + b1) + b2 (erf GeLU, or tanh with gelu_tanh).
+ * The pages name the experts and the types but not the gate: the gate and the combine weights
+ * above are this library's reading. The gate decides in fp32 from h rounded to the activation
+ * type (the rows the experts see); a near tie may be decided differently in another precision. */
+typedef struct {
+  int32_t hidden, ffn;        /* H (multiple of 64), F (multiple of 64)                          */
+  int32_t experts, top_k;     /* 1..1023 experts; 1..8 chosen per token, top_k <= experts        */
+  int32_t weight_dtype;       /* ds_dtype of W1, W2 (experts and residual MLP)                   */
+  int32_t act_dtype;          /* ds_dtype of x2, y, W_gate, biases, LN parameters; pairs as for  */
+                              /* a layer: (F32,F32) (F16,F16) (I8,F16) (BF16,BF16)               */
+  int32_t quant_group;        /* int8: elements per fp16 scale along K of W1 and W2 (a multiple  */
+                              /* of 16 dividing hidden and ffn); 0 otherwise                     */
+  float ln_eps;               /* > 0                                                             */
+  int32_t gelu_tanh;          /* 0: u*Phi(u) with erf; 1: tanh approximation                     */
+  int32_t residual;           /* 0: 'standard'; 1: 'residual' (PR-MoE: a dense MLP added)         */
+  int32_t combine;            /* 0: chosen p renormalized to sum 1; 1: the softmax p             */
+} ds_moe_desc;
+
+/* Borrowed device pointers, all 16-byte aligned. Experts are stacked: W1 [E][F][H], b1 [E][F],
+ * W2 [E][H][F], b2 [E][H]; int8 scales s1 [E][F][H/group], s2 [E][H][F/group] (NULL otherwise).
+ * W_gate [E][H], ln_g, ln_b [H] are in the activation dtype. r_* are the residual MLP's (one
+ * expert's shapes), required for the residual type and NULL for the standard type. */
+typedef struct {
+  const void *ln_g, *ln_b, *w_gate;
+  const void *w1, *b1, *s1, *w2, *b2, *s2;
+  const void *r_w1, *r_b1, *r_s1, *r_w2, *r_b2, *r_s2;
+} ds_moe_weights;
+
+typedef struct ds_moe ds_moe_t;
+
+/* Validates and keeps the description and pointers (nothing is read from the device). Errors:
+ * DS_ERR_NULL, DS_ERR_ALIGN, DS_ERR_SHAPE, DS_ERR_DTYPE. */
+int ds_moe_create(const ds_moe_desc* desc, const ds_moe_weights* w, ds_moe_t** out);
+int ds_moe_destroy(ds_moe_t* moe);
+
+/* Workspace bytes for steps of up to max_tokens tokens (0 if max_tokens is out of range: tokens
+ * times (top_k + residual) may not exceed 4096). */
+size_t ds_moe_workspace_bytes(const ds_moe_t* moe, int32_t max_tokens);
+
+/* One step on `tokens` rows of x2 [tokens][H] into y [tokens][H] (y may alias x2). sel_out
+ * (int32 [tokens][top_k]) and wgt_out (fp32 [tokens][top_k]) receive the chosen experts and their
+ * combine weights when not NULL. Enqueues five kernels on `stream` (gate, routing, the experts'
+ * two products, combination); allocates nothing and never synchronizes. Every chosen expert's
+ * weights are read once per step, however many tokens chose it. Errors before any enqueue:
+ * DS_ERR_NULL, DS_ERR_ALIGN, DS_ERR_SHAPE (tokens < 1 or too many pairs), DS_ERR_WORKSPACE. */
+int ds_moe_forward(const ds_moe_t* moe, const void* x2, void* y, int32_t tokens, int32_t* sel_out, float* wgt_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same step with a HIP event after each of the five launches; ms[i] (host, max entries)
+ * receives their durations in launch order (0 gate, 1 routing, 2 FF1, 3 FF2, 4 combination).
+ * Synchronizes the stream. Returns the number of launches or a negative status. */
+int ds_moe_time_kernels(const ds_moe_t* moe, const void* x2, void* y, int32_t tokens, void* workspace,
+                        size_t workspace_bytes, void* stream, float* ms, int32_t max);
+
 /* Message describing the last non-zero status returned on the calling thread. */
 const char* ds_last_error(void);
 

@@ -138,3 +138,63 @@ def lm_head_f32(wl: Workload, vocab: int, device="cpu") -> dict:
     else:
         g, b = torch.ones(H, device=device), torch.zeros(H, device=device)
     return {"ln_g": g, "ln_b": b, "w": normal((vocab, H), 0.02, c, HEAD_LAYER, W_VOCAB, device)}
+
+
+# ---------------------------------------------------------------- the MoE expert FF
+# tensor ids of the MoE block (layer slot = the block's index)
+MOE_LN_G, MOE_LN_B, W_GATE, W_EXP1, B_EXP1, W_EXP2, B_EXP2, W_RES1, B_RES1, W_RES2, B_RES2, X2_IN = range(20, 32)
+
+
+@dataclass(frozen=True)
+class MoeWorkload:
+    """One MoE expert-FF block ("DeepSpeed MoE 大规模稀疏模型推理实战指南": experts per MoE layer,
+    types standard / residual). Gate weights ~ N(0, gate_std^2), gate_std = 1/sqrt(hidden) by
+    default so that the gate logits of a LayerNorm-ed row are about N(0, 1); expert and residual
+    weights ~ N(0, 0.02), biases ~ N(0, bias_std); x2 ~ N(0, 1)."""
+    name: str
+    cfg_id: int
+    hidden: int
+    ffn: int
+    experts: int
+    top_k: int
+    tokens: int
+    weight_dtype: str   # "f32" | "f16" | "i8" | "bf16"
+    act_dtype: str      # "f32" | "f16" | "bf16"
+    group: int = 0
+    residual: bool = False
+    combine: int = 0
+    ln_std: float = 0.0
+    bias_std: float = 0.01
+    gate_std: float = 0.0   # 0: 1/sqrt(hidden)
+
+
+MOE_WORKLOADS = {
+    # the MoE page's 52B model: a 1.3B dense backbone (24 layers, hidden 2048) with 128 experts per
+    # MoE layer; expert FF width 4 x hidden (the GPT convention; the page gives no width); top-1
+    "moe-1.3b-e128": MoeWorkload("moe-1.3b-e128-f16-top1-t8", 30, 2048, 8192, 128, 1, 8, "f16", "f16"),
+    "moe-1.3b-e128-t1": MoeWorkload("moe-1.3b-e128-f16-top1-t1", 30, 2048, 8192, 128, 1, 1, "f16", "f16"),
+}
+
+
+def moe_weights_f32(mw: MoeWorkload, device="cpu", block: int = 0) -> dict:
+    """float32 tensors of one MoE block: ln_g, ln_b [H], w_gate [E,H], w1 [E,F,H], b1 [E,F],
+    w2 [E,H,F], b2 [E,H], and r_w1 [F,H], r_b1 [F], r_w2 [H,F], r_b2 [H] for the residual type."""
+    H, F, E, c, bs = mw.hidden, mw.ffn, mw.experts, mw.cfg_id, mw.bias_std
+    gs = mw.gate_std if mw.gate_std > 0 else 1.0 / float(np.sqrt(H))
+    if mw.ln_std > 0:
+        g = normal((H,), mw.ln_std, c, block, MOE_LN_G, device).add_(1.0)
+        b = normal((H,), mw.ln_std, c, block, MOE_LN_B, device)
+    else:
+        g, b = torch.ones(H, device=device), torch.zeros(H, device=device)
+    w = {"ln_g": g, "ln_b": b, "w_gate": normal((E, H), gs, c, block, W_GATE, device),
+         "w1": normal((E, F, H), 0.02, c, block, W_EXP1, device), "b1": normal((E, F), bs, c, block, B_EXP1, device),
+         "w2": normal((E, H, F), 0.02, c, block, W_EXP2, device), "b2": normal((E, H), bs, c, block, B_EXP2, device)}
+    if mw.residual:
+        w.update({"r_w1": normal((F, H), 0.02, c, block, W_RES1, device), "r_b1": normal((F,), bs, c, block, B_RES1, device),
+                  "r_w2": normal((H, F), 0.02, c, block, W_RES2, device), "r_b2": normal((H,), bs, c, block, B_RES2, device)})
+    return w
+
+
+def moe_input_f32(mw: MoeWorkload, device="cpu", step: int = 0) -> torch.Tensor:
+    """float32 [T, H] N(0, 1) rows of the residual stream entering the block."""
+    return normal((mw.tokens, mw.hidden), 1.0, mw.cfg_id, X_LAYER, X2_IN + 64 * step, device)

@@ -237,3 +237,79 @@ def test_layer_close_is_idempotent():
     _lib.lib().ds_layer_destroy(h)
     assert _lib.lib().ds_layer_destroy(None) == 0
     assert cfg.quant_group_mlp == 0
+
+
+# ------------------------------------------------------------------ the MoE expert FF (host checks)
+def _moe_desc(**kw):
+    d = dict(hidden=256, ffn=512, experts=8, top_k=2, weight_dtype=1, act_dtype=1, quant_group=0, ln_eps=1e-5,
+             gelu_tanh=0, residual=0, combine=0)
+    d.update(kw)
+    return _lib.MoeDescC(**d)
+
+
+def _moe_weights(int8=False, residual=False, **over):
+    w = {n: FAKE for n in ("ln_g", "ln_b", "w_gate", "w1", "b1", "w2", "b2")}
+    if int8:
+        w.update(s1=FAKE, s2=FAKE)
+    if residual:
+        w.update(r_w1=FAKE, r_b1=FAKE, r_w2=FAKE, r_b2=FAKE)
+        if int8:
+            w.update(r_s1=FAKE, r_s2=FAKE)
+    w.update(over)
+    return _lib.MoeWeightsC(*[w.get(n) for n in _lib.MOE_WEIGHT_FIELDS])
+
+
+def _moe_create(desc, weights):
+    h = C.c_void_p()
+    rc = _lib.lib().ds_moe_create(C.byref(desc), C.byref(weights), C.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=200), _lib.DS_ERR_SHAPE),
+    (dict(ffn=0), _lib.DS_ERR_SHAPE),
+    (dict(experts=0), _lib.DS_ERR_SHAPE),
+    (dict(experts=1024), _lib.DS_ERR_SHAPE),
+    (dict(top_k=0), _lib.DS_ERR_SHAPE),
+    (dict(top_k=9, experts=16), _lib.DS_ERR_SHAPE),
+    (dict(top_k=3, experts=2), _lib.DS_ERR_SHAPE),
+    (dict(weight_dtype=1, act_dtype=3), _lib.DS_ERR_DTYPE),
+    (dict(weight_dtype=0, act_dtype=1), _lib.DS_ERR_DTYPE),
+    (dict(quant_group=64), _lib.DS_ERR_DTYPE),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=24), _lib.DS_ERR_SHAPE),
+    (dict(weight_dtype=2, act_dtype=1, quant_group=0), _lib.DS_ERR_SHAPE),
+    (dict(ln_eps=0.0), _lib.DS_ERR_SHAPE),
+    (dict(combine=2), _lib.DS_ERR_SHAPE),
+    (dict(residual=1), _lib.DS_ERR_NULL),      # the residual type without its MLP
+])
+def test_moe_create_rejects_bad_descriptions(kw, code):
+    rc, h = _moe_create(_moe_desc(**kw), _moe_weights(int8=kw.get("weight_dtype") == 2))
+    assert rc == code, (rc, _lib.lib().ds_last_error())
+    assert not h.value
+
+
+def test_moe_create_checks_pointers_and_accepts_valid_blocks():
+    assert _moe_create(_moe_desc(), _moe_weights(w1=None))[0] == _lib.DS_ERR_NULL
+    assert _moe_create(_moe_desc(), _moe_weights(w2=FAKE + 4))[0] == _lib.DS_ERR_ALIGN
+    assert _moe_create(_moe_desc(), _moe_weights(s1=FAKE))[0] == _lib.DS_ERR_DTYPE          # scales on fp16
+    assert _moe_create(_moe_desc(), _moe_weights(residual=True))[0] == _lib.DS_ERR_SHAPE    # MLP on a standard MoE
+    assert _moe_create(_moe_desc(weight_dtype=2, quant_group=64), _moe_weights(int8=True, s2=None))[0] == _lib.DS_ERR_NULL
+    for d, w in ((_moe_desc(), _moe_weights()),
+                 (_moe_desc(residual=1, combine=1, gelu_tanh=1), _moe_weights(residual=True)),
+                 (_moe_desc(weight_dtype=2, quant_group=32, residual=1), _moe_weights(int8=True, residual=True)),
+                 (_moe_desc(weight_dtype=3, act_dtype=3, experts=1023, top_k=8), _moe_weights()),
+                 (_moe_desc(weight_dtype=0, act_dtype=0, experts=1, top_k=1), _moe_weights())):
+        rc, h = _moe_create(d, w)
+        assert rc == 0, _lib.lib().ds_last_error()
+        L = _lib.lib()
+        assert L.ds_moe_workspace_bytes(h, 1) > 0 and L.ds_moe_workspace_bytes(h, 0) == 0
+        slots = d.top_k + d.residual
+        assert L.ds_moe_workspace_bytes(h, 4096 // slots) > 0 and L.ds_moe_workspace_bytes(h, 4096 // slots + 1) == 0
+        # forward: argument errors before anything is enqueued
+        ws = L.ds_moe_workspace_bytes(h, 2)
+        assert L.ds_moe_forward(h, FAKE, FAKE, 0, None, None, FAKE, ws, None) == _lib.DS_ERR_SHAPE
+        assert L.ds_moe_forward(h, FAKE, FAKE, 4096 // slots + 1, None, None, FAKE, ws, None) == _lib.DS_ERR_SHAPE
+        assert L.ds_moe_forward(h, None, FAKE, 2, None, None, FAKE, ws, None) == _lib.DS_ERR_NULL
+        assert L.ds_moe_forward(h, FAKE + 2, FAKE, 2, None, None, FAKE, ws, None) == _lib.DS_ERR_ALIGN
+        assert L.ds_moe_forward(h, FAKE, FAKE, 2, None, None, FAKE, ws - 1, None) == _lib.DS_ERR_WORKSPACE
+        L.ds_moe_destroy(h)

@@ -20,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import DS_BF16, DS_F16, DS_F32, DS_I8, check, lib, ptr, stream_handle
 
-__all__ = ["LayerConfig", "make_config", "Layer", "KVCache", "Stack", "quantize_i8", "dequantize_i8"]
+__all__ = ["LayerConfig", "make_config", "Layer", "KVCache", "Stack", "MoE", "quantize_i8", "dequantize_i8"]
 
 _DTYPE_NAMES = {"fp32": DS_F32, "float32": DS_F32, "float": DS_F32, "f32": DS_F32,
                 "fp16": DS_F16, "float16": DS_F16, "half": DS_F16, "f16": DS_F16,
@@ -421,6 +421,106 @@ def read_probe(buf: torch.Tensor, out: torch.Tensor, stream=None):
         raise ValueError("out must be a device int32 tensor")
     check(lib().ds_read_probe(ptr(buf), buf.numel() * buf.element_size(), ptr(out), stream_handle(stream)),
           "ds_read_probe")
+
+
+class MoE:
+    """The MoE expert FF of one layer (ds_moe_* in include/ds_layer.h): y = x2 + the gated top-k
+    experts' FF of LN(x2), plus a dense MLP for the residual (PR-MoE) type; the gate reading is the
+    one stated with ds_moe_desc. Weights (device tensors, contiguous): ln_g, ln_b [H] and w_gate
+    [E,H] in the activation dtype; w1 [E,F,H], b1 [E,F], w2 [E,H,F], b2 [E,H] (weights in the weight
+    dtype, biases in the activation dtype; int8 also s1 [E,F,H/g], s2 [E,H,F/g] fp16); for the
+    residual type r_w1 [F,H], r_b1 [F], r_w2 [H,F], r_b2 [H] (and r_s1, r_s2 for int8)."""
+
+    def __init__(self, hidden: int, ffn: int, experts: int, top_k: int, weights: dict, dtype="fp16",
+                 quant_group=None, ln_eps: float = 1e-5, gelu_tanh: bool = False, combine: int = 0):
+        dt = _dtype_code(dtype)
+        adt = dt if dt in (DS_F32, DS_BF16) else DS_F16
+        self.dtype, self.act_dtype = dt, adt
+        self.hidden, self.ffn, self.experts, self.top_k = hidden, ffn, experts, top_k
+        self.residual = weights.get("r_w1") is not None
+        group = (64 if quant_group is None else int(quant_group)) if dt == DS_I8 else 0
+        if dt != DS_I8 and quant_group not in (None, 0):
+            raise ValueError("quant_group applies to int8 weights only")
+        H, F, E = hidden, ffn, experts
+        wdt, atd = _TORCH_DT[dt], _TORCH_DT[adt]
+        shapes = {"ln_g": ((H,), atd), "ln_b": ((H,), atd), "w_gate": ((E, H), atd),
+                  "w1": ((E, F, H), wdt), "b1": ((E, F), atd), "w2": ((E, H, F), wdt), "b2": ((E, H), atd)}
+        if dt == DS_I8:
+            shapes.update({"s1": ((E, F, H // group), torch.float16), "s2": ((E, H, F // group), torch.float16)})
+        if self.residual:
+            shapes.update({"r_w1": ((F, H), wdt), "r_b1": ((F,), atd), "r_w2": ((H, F), wdt), "r_b2": ((H,), atd)})
+            if dt == DS_I8:
+                shapes.update({"r_s1": ((F, H // group), torch.float16), "r_s2": ((H, F // group), torch.float16)})
+        for name, (shp, dty) in shapes.items():
+            t = weights.get(name)
+            if t is None:
+                raise ValueError(f"missing MoE weight {name}")
+            if tuple(t.shape) != shp or t.dtype != dty or not t.is_contiguous():
+                raise ValueError(f"{name}: need a contiguous {shp} {dty} tensor, got {tuple(t.shape)} {t.dtype}")
+        extra = set(k for k, v in weights.items() if v is not None) - set(shapes)
+        if extra:
+            raise ValueError(f"unexpected MoE weights {sorted(extra)}")
+        self._weights = dict(weights)
+        self._desc = _lib.MoeDescC(H, F, E, top_k, dt, adt, group, ln_eps, int(gelu_tanh), int(self.residual), int(combine))
+        cw = _lib.MoeWeightsC(*[ptr(self._weights.get(n)) for n in _lib.MOE_WEIGHT_FIELDS])
+        h = C.c_void_p()
+        check(lib().ds_moe_create(C.byref(self._desc), C.byref(cw), C.byref(h)), "ds_moe_create")
+        self._h = h
+        self.device = weights["w1"].device
+
+    def close(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h is not None and h.value:
+            lib().ds_moe_destroy(h)
+
+    def __del__(self):
+        self.close()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _handle(self):
+        if self._h is None:
+            raise ValueError("MoE is closed")
+        return self._h
+
+    def workspace(self, tokens: int) -> torch.Tensor:
+        n = lib().ds_moe_workspace_bytes(self._handle(), tokens)
+        if n == 0:
+            raise ValueError(f"tokens {tokens} out of range")
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def _check_x(self, x2):
+        if x2.dim() != 2 or x2.shape[1] != self.hidden or x2.dtype != _TORCH_DT[self.act_dtype] or not x2.is_contiguous():
+            raise ValueError(f"x2 must be a contiguous [tokens, {self.hidden}] {_TORCH_DT[self.act_dtype]} tensor")
+
+    def forward(self, x2: torch.Tensor, y=None, workspace=None, stream=None, routing: bool = False):
+        """y [T,H] for x2 [T,H]; with routing=True also the chosen experts (int32 [T,k]) and their
+        combine weights (fp32 [T,k])."""
+        self._check_x(x2)
+        T = x2.shape[0]
+        y = torch.empty_like(x2) if y is None else y
+        ws = self.workspace(T) if workspace is None else workspace
+        sel = torch.empty((T, self.top_k), dtype=torch.int32, device=x2.device) if routing else None
+        wgt = torch.empty((T, self.top_k), dtype=torch.float32, device=x2.device) if routing else None
+        check(lib().ds_moe_forward(self._handle(), ptr(x2), ptr(y), T, ptr(sel), ptr(wgt), ptr(ws), ws.numel(),
+                                   stream_handle(stream)), "ds_moe_forward")
+        return (y, sel, wgt) if routing else y
+
+    def time_kernels(self, x2: torch.Tensor, y=None, workspace=None, stream=None):
+        """Per-launch milliseconds of one step: a dict over MOE_PARTS (synchronizes)."""
+        self._check_x(x2)
+        T = x2.shape[0]
+        y = torch.empty_like(x2) if y is None else y
+        ws = self.workspace(T) if workspace is None else workspace
+        ms = (C.c_float * 8)()
+        n = lib().ds_moe_time_kernels(self._handle(), ptr(x2), ptr(y), T, ptr(ws), ws.numel(), stream_handle(stream), ms, 8)
+        if n < 0:
+            check(n, "ds_moe_time_kernels")
+        return {_lib.MOE_PARTS[i]: ms[i] for i in range(n)}
 
 
 def quantize_i8(w: torch.Tensor, group: int = 64, stream=None):

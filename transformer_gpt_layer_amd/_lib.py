@@ -24,7 +24,10 @@ EXPORTS = ("ds_layer_create", "ds_layer_destroy", "ds_layer_workspace_bytes", "d
            "ds_dequantize_i8", "ds_last_error", "ds_stack_create", "ds_stack_destroy",
            "ds_stack_workspace_bytes", "ds_stack_groups", "ds_stack_forward_decode",
            "ds_stack_check", "ds_stack_set_timeout_us", "ds_read_probe", "ds_stack_state_bytes",
-           "ds_stack_forward_decode_static", "ds_stack_forward_generate", "ds_layer_time_kernels")
+           "ds_stack_forward_decode_static", "ds_stack_forward_generate", "ds_layer_time_kernels",
+           "ds_moe_create", "ds_moe_destroy", "ds_moe_workspace_bytes", "ds_moe_forward",
+           "ds_moe_time_kernels")
+MOE_PARTS = ("gate", "route", "ff1", "ff2", "combine")  # ds_moe_time_kernels launch order
 
 
 class LayerDescC(C.Structure):
@@ -45,6 +48,20 @@ class LayerWeightsC(C.Structure):
 class LmHeadC(C.Structure):
     _fields_ = [("ln_g", C.c_void_p), ("ln_b", C.c_void_p), ("w", C.c_void_p), ("s", C.c_void_p),
                 ("vocab", C.c_int32)]
+
+
+class MoeDescC(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("ffn", C.c_int32), ("experts", C.c_int32), ("top_k", C.c_int32),
+                ("weight_dtype", C.c_int32), ("act_dtype", C.c_int32), ("quant_group", C.c_int32),
+                ("ln_eps", C.c_float), ("gelu_tanh", C.c_int32), ("residual", C.c_int32), ("combine", C.c_int32)]
+
+
+MOE_WEIGHT_FIELDS = ("ln_g", "ln_b", "w_gate", "w1", "b1", "s1", "w2", "b2", "s2",
+                     "r_w1", "r_b1", "r_s1", "r_w2", "r_b2", "r_s2")
+
+
+class MoeWeightsC(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in MOE_WEIGHT_FIELDS]
 
 
 class KVCacheC(C.Structure):
@@ -94,6 +111,14 @@ def lib():
         L.ds_stack_check.argtypes = [vp]
         L.ds_stack_set_timeout_us.argtypes = [vp, C.c_int64]
         L.ds_read_probe.argtypes = [vp, C.c_size_t, vp, vp]
+        L.ds_moe_create.argtypes = [C.POINTER(MoeDescC), C.POINTER(MoeWeightsC), C.POINTER(vp)]
+        L.ds_moe_destroy.argtypes = [vp]
+        L.ds_moe_workspace_bytes.argtypes = [vp, i32]
+        L.ds_moe_workspace_bytes.restype = C.c_size_t
+        L.ds_moe_forward.argtypes = [vp, vp, vp, i32, vp, vp, vp, C.c_size_t, vp]
+        L.ds_moe_time_kernels.argtypes = [vp, vp, vp, i32, vp, C.c_size_t, vp, C.POINTER(C.c_float), i32]
+        for name in ("ds_moe_create", "ds_moe_destroy", "ds_moe_forward", "ds_moe_time_kernels"):
+            getattr(L, name).restype = C.c_int
         for name in ("ds_layer_create", "ds_layer_destroy", "ds_kv_append", "ds_layer_forward_decode",
                      "ds_layer_forward_prefill", "ds_quantize_i8", "ds_dequantize_i8", "ds_stack_create",
                      "ds_stack_destroy", "ds_stack_forward_decode", "ds_stack_check",

@@ -44,6 +44,32 @@ struct AttnArgs {
   _Float16* ctx16;
 };
 
+// The MoE expert FF of one step (kernels_moe.hip). T tokens, each with k chosen experts plus, for
+// the residual type, the residual MLP as slot k: KS = k + residual slots per token.
+constexpr int kMoeMaxK = 8;          // experts per token at most
+constexpr int kMoeMaxExperts = 1023; // experts per layer at most (the residual MLP is one more)
+constexpr int kMoeMaxPairs = 4096;   // tokens x slots at most per step
+struct MoeArgs {
+  const void* x2;      // [T][H] activation type
+  void* y;             // [T][H] activation type
+  const void *ln_g, *ln_b, *w_gate;                     // [H], [H], [E][H] activation type
+  const void *w1, *b1, *s1, *w2, *b2, *s2;              // experts [E][F][H], [E][F], ..., [E][H][F], [E][H]
+  const void *r_w1, *r_b1, *r_s1, *r_w2, *r_b2, *r_s2;  // the residual MLP, or null
+  void* h;             // [T][H] LayerNorm output in the staged type
+  int32_t* sel;        // [T][KS] expert of each slot (E: the residual MLP)
+  float* wgt;          // [T][KS] combine weight of each slot
+  int32_t* route;      // 1 + 3 umax + T KS ints (kernels_moe.hip, Route)
+  float* f;            // [T KS][F] GeLU(W1 h + b1) per slot
+  float* z;            // [T KS][H] W2 f + b2 per slot
+  int32_t* sel_out;    // optional [T][k]
+  float* wgt_out;      // optional [T][k]
+  int T, H, F, E, k, KS, umax, group, residual, combine, gelu_tanh;
+  float eps;
+};
+// Called after each of the five launches (part 0 gate, 1 route, 2 FF1, 3 FF2, 4 combine) when set.
+typedef void (*MoeKernelHook)(void* ctx, hipStream_t st, int part);
+hipError_t launch_moe(Dt wdt, Dt adt, const MoeArgs& a, hipStream_t st, MoeKernelHook hook, void* hook_ctx);
+
 hipError_t launch_gemv(Dt wdt, Dt adt, GemvKind kind, const GemvArgs& a, hipStream_t st);
 hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st);
 // The same attention with fp16 q and ctx (q16, ctx16) and an fp16 cache.
