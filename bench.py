@@ -479,6 +479,81 @@ def prefill_record(args, wl, torch, tg, syn, layers, cpu_s=0.0):
     return rec
 
 
+def moe_record(args, mw, torch, tg, syn, cpu_s=0.0):
+    """The MoE expert FF block of the MoE page's 1.3B + MoE-128 model: one step = the tokens through
+    the gate, the routing, the chosen experts' two products and the combination, captured in a HIP
+    graph. Algorithmic bytes: the LayerNorm and gate weights, each chosen expert's weights and
+    biases once, x2 read and y written. The roofline entry is the longer of the two expert
+    products, timed per kernel (ds_moe_time_kernels), over the bytes of the experts it streams."""
+    import numpy as np
+
+    import oracle
+
+    H, F, E, T, k = mw.hidden, mw.ffn, mw.experts, mw.tokens, mw.top_k
+    w32 = syn.moe_weights_f32(mw, "cuda")
+    gw = {n: t.half().contiguous() for n, t in w32.items()}
+    del w32
+    _free(torch)
+    moe = tg.MoE(H, F, E, k, gw, dtype="fp16")
+    x = syn.moe_input_f32(mw, "cuda").half()
+    y = torch.empty_like(x)
+    ws = moe.workspace(T)
+    _, sel, _ = moe.forward(x, routing=True)
+    torch.cuda.synchronize()
+    used = sorted(set(int(e) for e in sel.cpu().numpy().ravel()))
+    U = len(used)
+    stream = torch.cuda.Stream()
+    ms, per_step = time_graph(torch, stream, lambda: moe.forward(x, y, ws, stream=stream), args.steps, args.warmup)
+    assert torch.isfinite(y.float()).all(), "non-finite MoE output"
+    reps = [moe.time_kernels(x, y, ws, stream=stream) for _ in range(5)]
+    kt = {p: statistics.median(r[p] for r in reps) for p in reps[0]}
+    b_ff1 = U * (F * H * 2 + F * 2)
+    b_ff2 = U * (H * F * 2 + H * 2)
+    b_gate = E * H * 2 + 2 * H * 2
+    step_bytes = b_gate + b_ff1 + b_ff2 + 2 * T * H * 2
+    pb = {"gate": b_gate, "ff1": b_ff1, "ff2": b_ff2}
+    kernels = {p: {"ms": round(t, 4), **({"bytes": pb[p], "gbs": round(pb[p] / (t * 1e-3) / 1e9, 1)} if p in pb else {})}
+               for p, t in kt.items()}
+    dom = "ff1" if kt["ff1"] >= kt["ff2"] else "ff2"
+    gbs_dom = pb[dom] / (kt[dom] * 1e-3) / 1e9
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    rec = {"metric": "MoE expert-FF tokens/s (gate, top-k routing, chosen experts, combination) + HBM roofline",
+           "value": round(T / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic (seeded N(0,0.02) expert weights, N(0,1/H) gate, N(0,1) inputs)",
+           "config": {"workload": mw.name, "hidden": H, "ffn": F, "experts": E, "top_k": k, "tokens": T,
+                      "experts_chosen": U, "launch": "5 kernels (gate, routing, grouped FF1, grouped FF2, "
+                                                     "combination) under a HIP graph"},
+           "hbm_gbs": round(gbs, 1), "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_step": step_bytes,
+           "step_ms": step_stats(per_step),
+           "roofline": {"bound": "hbm", "kernel": f"moe {dom} (grouped expert GEMV)", "achieved": round(gbs_dom, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs_dom / PEAK_HBM_GBS, 4),
+                        "traffic": None, "kernel_ms": round(kt[dom], 4), "bytes_per_launch": pb[dom],
+                        "kernels": kernels}}
+    if cpu_s > 0:
+        # the oracle on the chosen experts only (a compact copy: the full 128 experts would not fit
+        # the host as float64), one token at a time, on one host thread
+        idx = torch.tensor(used, device="cuda")
+        ow = {"ln_g": gw["ln_g"].double().cpu().numpy(), "ln_b": gw["ln_b"].double().cpu().numpy(),
+              "w_gate": gw["w_gate"].index_select(0, idx).double().cpu().numpy()}
+        for n in ("w1", "b1", "w2", "b2"):
+            ow[n] = gw[n].index_select(0, idx).double().cpu().numpy()
+        xd = x.double().cpu().numpy()
+        local = np.searchsorted(np.array(used), sel.cpu().numpy())
+        t0, done = time.perf_counter(), 0
+        while done < T and (done == 0 or time.perf_counter() - t0 < cpu_s):
+            oracle.moe_forward(ow, xd[done:done + 1], top_k=k, force_sel=local[done:done + 1])
+            done += 1
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(done / el, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{done} tokens through the oracle's MoE block on the chosen experts in "
+                                         f"{el:.1f} s on one host thread"}
+    moe.close()
+    del gw
+    return rec
+
+
 def _free(torch):
     import gc
     gc.collect()
@@ -496,9 +571,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle sample per leg (one thread, all threads) for the headline (0 disables)")
     ap.add_argument("--record-cpu-seconds", type=float, default=4.0, help="the same for each nested record")
-    ap.add_argument("--records", default="c2gen,c3,c4b8,c4b1,c5",
+    ap.add_argument("--records", default="c2gen,c3,c4b8,c4b1,c5,moe,moe1",
                     help="nested records after the c2 headline (comma list; empty for none): c2gen (the "
-                         "generation step with the LM head), c3, c4b8, c4b1, c5")
+                         "generation step with the LM head), c3, c4b8, c4b1, c5, moe (the MoE expert FF "
+                         "of the 1.3B + MoE-128 model, 8 tokens), moe1 (the same, 1 token)")
     ap.add_argument("--mode", choices=["auto", "stack", "layers"], default="auto",
                     help="stack: one persistent launch per step; layers: the per-layer kernels")
     ap.add_argument("--no-read-probe", dest="read_probe", action="store_false",
@@ -539,7 +615,10 @@ def main():
     for name in names:
         print(f"[bench] record {name}", file=sys.stderr, flush=True)
         cs = args.record_cpu_seconds
-        if name == "c2gen":
+        if name in ("moe", "moe1"):
+            mw = syn.MOE_WORKLOADS["moe-1.3b-e128" if name == "moe" else "moe-1.3b-e128-t1"]
+            rec = moe_record(args, mw, torch, tg, syn, cs)
+        elif name == "c2gen":
             w2 = syn.WORKLOADS["c2"]
             rec = decode_record(args, w2, torch, tg, syn, w2.layers, "stack", 0.0, vocab=syn.GPT_NEO_VOCAB)
             rec["metric"] = "generation-step tokens/s (32 layers + final LayerNorm + LM head + greedy choice)"

@@ -56,14 +56,16 @@ struct MoeArgs {
   const void *w1, *b1, *s1, *w2, *b2, *s2;              // experts [E][F][H], [E][F], ..., [E][H][F], [E][H]
   const void *r_w1, *r_b1, *r_s1, *r_w2, *r_b2, *r_s2;  // the residual MLP, or null
   void* h;             // [T][H] LayerNorm output in the staged type
+  float* logits;       // [T][E] gate logits
   int32_t* sel;        // [T][KS] expert of each slot (E: the residual MLP)
   float* wgt;          // [T][KS] combine weight of each slot
   int32_t* route;      // 1 + 3 umax + T KS ints (kernels_moe.hip, Route)
-  float* f;            // [T KS][F] GeLU(W1 h + b1) per slot
+  void* f;             // [T KS][F] GeLU(W1 h + b1) per slot, in the staged type
   float* z;            // [T KS][H] W2 f + b2 per slot
   int32_t* sel_out;    // optional [T][k]
   float* wgt_out;      // optional [T][k]
   int T, H, F, E, k, KS, umax, group, residual, combine, gelu_tanh;
+  int lds_act;         // activation staging bytes of an expert workgroup (set by the launcher)
   float eps;
 };
 // Called after each of the five launches (part 0 gate, 1 route, 2 FF1, 3 FF2, 4 combine) when set.

@@ -27,7 +27,7 @@ size_t staged_size(int wdt) { return wdt == DS_F32 ? 4 : 2; }
 int slots(const ds_moe_desc& d) { return d.top_k + (d.residual ? 1 : 0); }
 
 struct MoeWs {
-  size_t h, sel, wgt, route, f, z, total;
+  size_t h, logits, sel, wgt, route, f, z, total;
   int umax;
 };
 
@@ -39,10 +39,11 @@ MoeWs moe_ws(const ds_moe_desc& d, int T) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += up256(bytes); return at; };
   L.h = take((size_t)T * d.hidden * staged_size(d.weight_dtype));
+  L.logits = take((size_t)T * d.experts * 4);
   L.sel = take((size_t)P * 4);
   L.wgt = take((size_t)P * 4);
   L.route = take((size_t)(1 + 3 * L.umax + P) * 4);
-  L.f = take((size_t)P * d.ffn * 4);
+  L.f = take((size_t)P * d.ffn * staged_size(d.weight_dtype));
   L.z = take((size_t)P * d.hidden * 4);
   L.total = off;
   return L;
@@ -67,10 +68,11 @@ int enqueue(const ds_moe* M, const void* x2, void* y, int tokens, int32_t* sel_o
   a.r_w1 = M->w.r_w1; a.r_b1 = M->w.r_b1; a.r_s1 = M->w.r_s1;
   a.r_w2 = M->w.r_w2; a.r_b2 = M->w.r_b2; a.r_s2 = M->w.r_s2;
   a.h = base + L.h;
+  a.logits = reinterpret_cast<float*>(base + L.logits);
   a.sel = reinterpret_cast<int32_t*>(base + L.sel);
   a.wgt = reinterpret_cast<float*>(base + L.wgt);
   a.route = reinterpret_cast<int32_t*>(base + L.route);
-  a.f = reinterpret_cast<float*>(base + L.f);
+  a.f = base + L.f;
   a.z = reinterpret_cast<float*>(base + L.z);
   a.sel_out = sel_out;
   a.wgt_out = wgt_out;
