@@ -46,6 +46,7 @@ def lib():
         L.ora_dequantize_i8.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, _D]
         L.ora_moe_forward.argtypes = [C.c_void_p, C.c_void_p, _D, C.c_int, C.c_void_p, _D, C.c_void_p, _D]
         L.ora_moe_forward.restype = C.c_int
+        L.ora_quantize_row_i8.argtypes = [_D, C.c_int, C.c_void_p, C.c_void_p]
         _LIB = L
     return _LIB
 
@@ -115,6 +116,20 @@ def argmax(v):
     if v.ndim != 1 or v.size < 1:
         raise ValueError("argmax needs a non-empty 1-D array")
     return int(lib().ora_argmax(_p(v), v.size))
+
+
+def quantize_rows_i8(x):
+    """The int8 KV-cache reading: each row of x [..., n] (float64) as int8 codes [..., n] and one fp16
+    scale (uint16 bits) [...] per row, scale = fp16(amax/127), code = clamp(RNE(x/scale), -127, 127)."""
+    x = _f64(x)
+    n = x.shape[-1]
+    rows = x.reshape(-1, n)
+    q = np.empty(rows.shape, dtype=np.int8)
+    s = np.empty(rows.shape[0], dtype=np.uint16)
+    for i in range(rows.shape[0]):
+        r = np.ascontiguousarray(rows[i])
+        lib().ora_quantize_row_i8(_p(r), n, q[i:].ctypes.data, s[i:].ctypes.data)
+    return q.reshape(x.shape), s.reshape(x.shape[:-1])
 
 
 # ---------------------------------------------------------------- the MoE expert FF
@@ -194,7 +209,8 @@ def dequantize_i8(q, s, group=64):
 # ---------------------------------------------------------------- the layer
 class _Desc(C.Structure):
     _fields_ = [("hidden", C.c_int), ("heads", C.c_int), ("head_dim", C.c_int), ("ffn", C.c_int),
-                ("ln_eps", C.c_double), ("gelu_tanh", C.c_int), ("triangular_masking", C.c_int)]
+                ("ln_eps", C.c_double), ("gelu_tanh", C.c_int), ("triangular_masking", C.c_int),
+                ("kv_int8", C.c_int)]
 
 
 _WNAMES = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
@@ -221,6 +237,7 @@ class Desc:
     ln_eps: float = 1e-5
     gelu_tanh: bool = False
     triangular_masking: bool = True
+    kv_int8: bool = False  # the int8 KV cache reading (ora_quantize_row_i8 per appended head row)
 
 
 def layer_forward(desc: Desc, weights: dict, k_cache, v_cache, lens, x, stages=False):
@@ -239,7 +256,7 @@ def layer_forward(desc: Desc, weights: dict, k_cache, v_cache, lens, x, stages=F
     ws = {n: _f64(weights[n]) for n in _WNAMES}
     cw = _Weights(*[_p(ws[n]) for n in _WNAMES])
     cd = _Desc(desc.hidden, desc.heads, desc.head_dim, desc.ffn, desc.ln_eps,
-               int(desc.gelu_tanh), int(desc.triangular_masking))
+               int(desc.gelu_tanh), int(desc.triangular_masking), int(desc.kv_int8))
     xx = _f64(x)
     y = np.empty((B, T, H))
     st_arrays = None

@@ -113,18 +113,32 @@ int ora_layer_forward(const ora_desc* dsc, const ora_weights* w, double* k_cache
       put(stage_row(st ? st->qkv : NULL, b, t, ntok, 3 * H), z, 3 * H);
     }
 
-  /* Append: K[b][j][p] = k_j and V[b][j][p] = v_j at p = lens[b] + t. */
+  /* Append: K[b][j][p] = k_j and V[b][j][p] = v_j at p = lens[b] + t; with an int8 cache each
+   * head row is stored quantized, and attention below reads the dequantized row. */
+  int8_t* codes = (int8_t*)malloc((size_t)d);
   for (int b = 0; b < batch; ++b)
     for (int t = 0; t < ntok; ++t) {
       const double* z = qkv + ((size_t)b * ntok + t) * 3 * H;
       const int p = lens[b] + t;
-      for (int j = 0; j < nh; ++j)
+      for (int j = 0; j < nh; ++j) {
+        double* kr = k_cache + (((size_t)b * nh + j) * cap + p) * d;
+        double* vr = v_cache + (((size_t)b * nh + j) * cap + p) * d;
         for (int e = 0; e < d; ++e) {
-          size_t at = (((size_t)b * nh + j) * cap + p) * d + e;
-          k_cache[at] = z[H + j * d + e];
-          v_cache[at] = z[2 * H + j * d + e];
+          kr[e] = z[H + j * d + e];
+          vr[e] = z[2 * H + j * d + e];
         }
+        if (dsc->kv_int8) {
+          double* rows[2] = {kr, vr};
+          for (int m = 0; m < 2; ++m) {
+            uint16_t sb;
+            ora_quantize_row_i8(rows[m], d, codes, &sb);
+            const double sv = ora_fp16_to_double(sb);
+            for (int e = 0; e < d; ++e) rows[m][e] = (double)codes[e] * sv;
+          }
+        }
+      }
     }
+  free(codes);
 
   for (int b = 0; b < batch; ++b)
     for (int t = 0; t < ntok; ++t) {
@@ -302,6 +316,21 @@ int ora_quantize_i8(const float* w, int n, int k, int group, int8_t* q, uint16_t
       }
     }
   return 0;
+}
+
+void ora_quantize_row_i8(const double* x, int n, int8_t* q, uint16_t* s) {
+  double amax = 0.0;
+  for (int i = 0; i < n; ++i)
+    if (fabs(x[i]) > amax) amax = fabs(x[i]);
+  const uint16_t sb = ora_fp16_from_double(amax / 127.0);
+  *s = sb;
+  const double sv = ora_fp16_to_double(sb);
+  for (int i = 0; i < n; ++i) {
+    double c = (sv == 0.0) ? 0.0 : nearbyint(x[i] / sv);
+    if (c > 127.0) c = 127.0;
+    if (c < -127.0) c = -127.0;
+    q[i] = (int8_t)c;
+  }
 }
 
 int ora_dequantize_i8(const int8_t* q, const uint16_t* s, int n, int k, int group, double* w) {

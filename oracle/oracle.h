@@ -42,6 +42,9 @@ typedef struct {
   double ln_eps;
   int gelu_tanh;           /* 0: u*Phi(u) with erf; 1: the tanh approximation            */
   int triangular_masking;  /* 1: row at position p sees keys 0..p; 0: sees every key     */
+  int kv_int8;             /* 1: the cache holds each appended K and V row of one head as  */
+                           /*    int8 codes with one fp16 scale (ora_quantize_row_i8); the */
+                           /*    cache arrays here receive the dequantized values q*s      */
 } ora_desc;
 
 typedef struct {
@@ -112,6 +115,11 @@ typedef struct {
  * shape or a forced expert out of range. */
 int ora_moe_forward(const ora_moe_desc* d, const ora_moe_weights* w, const double* x2, int tokens,
                     const int* force_sel, double* y, int* sel, double* wgt);
+
+/* The int8 KV cache reading (the pages do not quantize the cache; this follows their group-wise
+ * weight quantizer with one group per cached row of one head): scale = fp16_RNE(amax/127),
+ * code = clamp(round_half_even(x/scale), -127, 127); amax = 0 -> scale 0, codes 0. x: n doubles. */
+void ora_quantize_row_i8(const double* x, int n, int8_t* q, uint16_t* s);
 
 /* ---- IEEE binary16 ---- */
 uint16_t ora_fp16_from_double(double v); /* round to nearest, ties to even; overflow -> inf */

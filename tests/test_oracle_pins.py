@@ -522,3 +522,66 @@ def test_moe_forced_selection():
     assert np.array_equal(selo, other) and not np.allclose(yo, y)
     with pytest.raises(ValueError):
         oracle.moe_forward(w, x2, top_k=2, force_sel=np.full((3, 2), E))
+
+
+# ------------------------------------------------------------------ the int8 KV cache reading
+def test_kv_row_quantizer_matches_the_weight_quantizer():
+    # on float32 rows the per-row quantizer is the (pinned) group quantizer with one group per row
+    x = rng.normal(0, 1.3, (9, 128)).astype(np.float32)
+    x[4] = 0.0
+    q, s = oracle.quantize_rows_i8(x.astype(np.float64))
+    qw, sw = oracle.quantize_i8(x, 128)
+    assert np.array_equal(q, qw) and np.array_equal(s, sw[:, 0])
+    assert s[4] == 0 and not q[4].any()
+
+
+def test_kv_row_quantizer_by_hand():
+    """amax 1.0: scale = fp16(1/127) = (1 + 8/1024) 2^-7 = 0.00787353515625 (bits 0x2008: 1/127
+    lies 8.06 steps of 2^-17 above 2^-7). Codes: 1.0 / s = 127.008 -> 127, 0.3 / s = 38.10 -> 38,
+    -0.5 / s = -63.504 -> -64, 0.125 / s = 15.876 -> 16."""
+    q, s = oracle.quantize_rows_i8(np.array([[1.0, 0.3, -0.5, 0.125, 0.0, 0.0, 0.0, 0.0]]))
+    assert int(s[0]) == 0x2008
+    assert list(q[0, :5]) == [127, 38, -64, 16, 0]
+
+
+def _kv_layer_case(H=64, nh=2, F=96, B=2, P=5, seed=40):
+    w = _rand_layer(H, nh, F, seed)
+    d = H // nh
+    kc, vc, _ = _cache(B, nh, P + 3, d, P, seed + 1)
+    x = rng.normal(0, 1, (B, 1, H))
+    return w, kc, vc, x, d
+
+
+def test_layer_int8_kv_with_exactly_representable_rows_is_the_fp_layer():
+    # new K/V rows from the bias alone (W_qkv's K and V rows zero), each row holding 127 * 2^-4
+    # and other multiples of 2^-4: the scale is 2^-4 exactly and every code exact, so the int8
+    # cache holds the same values and the layer gives the same output bit for bit
+    H, nh, F, B, P = 64, 2, 96, 2, 5
+    w, kc, vc, x, d = _kv_layer_case(H, nh, F, B, P)
+    w["w_qkv"][H:] = 0.0
+    codes = rng.integers(-127, 128, 2 * H)
+    codes[::d] = 127
+    w["b_qkv"][H:] = codes * 2.0 ** -4
+    out = []
+    for kv8 in (False, True):
+        k2, v2, lens = kc.copy(), vc.copy(), np.full(B, P, dtype=np.int32)
+        y = oracle.layer_forward(oracle.Desc(H, nh, d, F, kv_int8=kv8), w, k2, v2, lens, x)
+        out.append((y, k2, v2))
+    assert np.array_equal(out[0][0], out[1][0])
+    assert np.array_equal(out[0][1], out[1][1]) and np.array_equal(out[0][2], out[1][2])
+
+
+def test_layer_int8_kv_cache_holds_the_quantized_rows():
+    H, nh, F, B, P = 64, 2, 96, 2, 5
+    w, kc, vc, x, d = _kv_layer_case(H, nh, F, B, P, seed=41)
+    k_fp, v_fp, lens = kc.copy(), vc.copy(), np.full(B, P, dtype=np.int32)
+    y_fp = oracle.layer_forward(oracle.Desc(H, nh, d, F), w, k_fp, v_fp, lens, x)
+    k8, v8, lens = kc.copy(), vc.copy(), np.full(B, P, dtype=np.int32)
+    y8 = oracle.layer_forward(oracle.Desc(H, nh, d, F, kv_int8=True), w, k8, v8, lens, x)
+    for fp, c8 in ((k_fp, k8), (v_fp, v8)):
+        q, s = oracle.quantize_rows_i8(fp[:, :, P])
+        want = q.astype(np.float64) * oracle.fp16_to_double(s)[..., None]
+        assert np.array_equal(c8[:, :, P], want)                  # the new row: q * s
+        assert np.array_equal(c8[:, :, :P], fp[:, :, :P])          # the past rows untouched
+    # the attention sees the quantized rows: close to the fp layer, not equal
+    assert not np.array_equal(y8, y_fp) and np.allclose(y8, y_fp, rtol=0, atol=5e-2)
