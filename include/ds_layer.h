@@ -91,6 +91,13 @@ typedef struct {
   float ln_eps;               /* LayerNorm epsilon, > 0 (1e-5 by default)                       */
   int32_t gelu_tanh;          /* 0: u*Phi(u) with erf (default); 1: tanh approximation          */
   int32_t triangular_masking; /* 1 (default): a row at position p sees keys 0..p; 0: all keys   */
+  int32_t kv_dtype;           /* 0 (default): the cache holds K and V in act_dtype; DS_I8: int8  */
+                              /* codes with one fp16 scale per cached row of one head (k_scale, */
+                              /* v_scale of ds_kv_cache), for fp16 or bf16 activations. The     */
+                              /* pages do not quantize the cache: this applies their group-wise */
+                              /* weight quantizer ([KP] section 五 5.2) with one group per row: */
+                              /* scale = fp16_RNE(amax/127), code = clamp(RNE(x/scale), +-127); */
+                              /* attention reads q*s, the new rows included.                    */
 } ds_layer_desc;
 
 /* Borrowed device pointers to one layer's parameters. s_* are the fp16 group scales of the int8
@@ -106,7 +113,8 @@ typedef struct {
 } ds_layer_weights;
 
 /* A caller-owned KV cache for one layer. k and v are [batch][heads][capacity][head_dim] in
- * act_dtype. d_len is a device int32[batch] holding the number of filled rows of each sequence;
+ * act_dtype, or int8 codes when the layer's kv_dtype is DS_I8; k_scale and v_scale are then
+ * [batch][heads][capacity] fp16 row scales (NULL otherwise). d_len is a device int32[batch] holding the number of filled rows of each sequence;
  * decode and prefill write the new rows at d_len[b].. and then add the number of new rows to it.
  * h_len is an optional HOST int32[batch] mirror of d_len: when it is not NULL the library checks
  * capacity against it before enqueueing and advances it at enqueue time (a graph replay does not
@@ -119,6 +127,8 @@ typedef struct {
   int32_t* h_len;
   int32_t batch;
   int32_t capacity;
+  void* k_scale;
+  void* v_scale;
 } ds_kv_cache;
 
 typedef struct ds_layer ds_layer_t;

@@ -1,0 +1,125 @@
+"""The int8 KV cache (kv_dtype DS_I8: int8 codes with one fp16 scale per cached row of one head)
+against the oracle's kv_int8 reading, on the per-layer decode and prefill paths.
+
+Appended rows come from fp16/bf16 values both sides see exactly, so their codes and scales are
+compared bit for bit with the oracle's row quantizer. The rows a step writes come from the step's
+own K/V projection (fp32 on the GPU, double in the oracle): a code may differ by one where the
+quantizer's rounding is a near tie, so those rows are compared as dequantized values.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+import transformer_gpt_layer_amd as tg
+from tests._common import TOL, TORCH, gpu_layer_and_oracle_weights, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(**kw):
+    return dataclasses.replace(syn.WORKLOADS["c1"], **kw)
+
+
+def kv8_caches(wl, layer, gl, past=None, cap=None, batch=None):
+    """A GPU int8 KV cache holding `past` seeded rows (appended through ds_kv_append, which
+    quantizes them) and the oracle's float64 cache of the dequantized rows; the GPU's codes and
+    scales are checked bit for bit against the oracle's row quantizer on the same values."""
+    B = wl.batch if batch is None else batch
+    P = wl.past if past is None else past
+    cap = wl.capacity if cap is None else cap
+    act = TORCH[wl.act_dtype]
+    kv = tg.KVCache(B, wl.heads, cap, wl.head_dim, torch.int8, "cuda")
+    ok = np.zeros((B, wl.heads, cap, wl.head_dim))
+    ov = np.zeros_like(ok)
+    if P > 0:
+        kp = syn.normal((B, P, wl.hidden), 1.0, wl.cfg_id, layer, syn.K_PAST, "cuda").to(act)
+        vp = syn.normal((B, P, wl.hidden), 1.0, wl.cfg_id, layer, syn.V_PAST, "cuda").to(act)
+        gl.kv_append(kv, kp.contiguous(), vp.contiguous())
+        torch.cuda.synchronize()
+        for src, codes, scales, dst in ((kp, kv.k, kv.k_scale, ok), (vp, kv.v, kv.v_scale, ov)):
+            rows = src.double().cpu().numpy().reshape(B, P, wl.heads, wl.head_dim).transpose(0, 2, 1, 3)
+            q, s = oracle.quantize_rows_i8(rows)
+            assert np.array_equal(codes[:, :, :P].cpu().numpy(), q), "appended int8 codes differ from the oracle"
+            sb = scales[:, :, :P].cpu().view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(sb, s), "appended fp16 row scales differ from the oracle"
+            dst[:, :, :P] = q.astype(np.float64) * oracle.fp16_to_double(s)[..., None]
+    lens = np.full(B, P, dtype=np.int32)
+    return kv, ok, ov, lens
+
+
+CASES = {
+    "f16-d128-b1": _wl(hidden=256, heads=2, head_dim=128, ffn=768, weight_dtype="f16", act_dtype="f16", batch=1,
+                       past=70, cfg_id=601),
+    "f16-d64-b3-affine": _wl(hidden=512, heads=8, head_dim=64, ffn=1024, weight_dtype="f16", act_dtype="f16", batch=3,
+                             past=129, cfg_id=602, ln_std=0.2, bias_std=0.1),
+    "i8w-d128-b9": _wl(hidden=512, heads=4, head_dim=128, ffn=1024, weight_dtype="i8", act_dtype="f16", group=64,
+                       batch=9, past=300, cfg_id=603),
+    "bf16-d128-b2-affine": _wl(hidden=512, heads=4, head_dim=128, ffn=2048, weight_dtype="bf16", act_dtype="bf16",
+                               batch=2, past=45, cfg_id=604, ln_std=0.2, bias_std=0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_with_int8_kv_matches_oracle(name):
+    wl = CASES[name]
+    tanh = "affine" in name
+    print(f"[kv8 decode] {name}: {wl}", flush=True)
+    gl, ow = gpu_layer_and_oracle_weights(wl, 0, gelu_tanh=tanh, kv_dtype="int8")
+    kv, ok, ov, lens = kv8_caches(wl, 0, gl)
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn, gelu_tanh=tanh, kv_int8=True)
+    act = TORCH[wl.act_dtype]
+    for step in range(2):
+        x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, step, "cuda").to(act)
+        y = gl.decode(kv, x)
+        torch.cuda.synchronize()
+        xd = x.double().cpu().numpy()
+        P = int(lens[0])
+        yo = oracle.layer_forward(desc, ow, ok, ov, lens, xd[:, None])[:, 0]
+        yd = y.double().cpu().numpy()
+        err, err_d = rel_l2(yd, yo), rel_l2(yd - xd, yo - xd)
+        kd, vd = kv.dequantized()
+        ek = rel_l2(kd[:, :, P].double().cpu().numpy(), ok[:, :, P])
+        ev = rel_l2(vd[:, :, P].double().cpu().numpy(), ov[:, :, P])
+        print(f"  step {step}: rel L2 {err:.3e}, of y - x {err_d:.3e}; new rows K {ek:.3e} V {ev:.3e}", flush=True)
+        tol = TOL[wl.act_dtype]
+        assert err <= tol and err_d <= tol and ek <= tol and ev <= tol
+        # the new rows are int8 codes with one scale per row: max |code| is 127 where amax > 0
+        codes = kv.k[:, :, P].cpu().numpy().astype(int)
+        assert np.all(np.abs(codes).max(-1) == 127)
+        assert kv.lengths() == [P + 1] * wl.batch
+
+
+@pytest.mark.parametrize("name,S,P0", [("f16-d128-b1", 6, 5), ("f16-d64-b3-affine", 4, 0)])
+def test_prefill_with_int8_kv_matches_oracle(name, S, P0):
+    wl = CASES[name]
+    gl, ow = gpu_layer_and_oracle_weights(wl, 0, kv_dtype="int8")
+    kv, ok, ov, lens = kv8_caches(wl, 0, gl, past=P0)
+    x = syn.normal((wl.batch, S, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 7, "cuda").to(TORCH[wl.act_dtype])
+    y = gl.prefill(kv, x)
+    torch.cuda.synchronize()
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn, kv_int8=True)
+    yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy())
+    yd, xd = y.double().cpu().numpy(), x.double().cpu().numpy()
+    err, err_d = rel_l2(yd, yo), rel_l2(yd - xd, yo - xd)
+    kd, vd = kv.dequantized()
+    ek = rel_l2(kd[:, :, :P0 + S].double().cpu().numpy(), ok[:, :, :P0 + S])
+    print(f"  prefill {name} S={S} P0={P0}: rel L2 {err:.3e}, of y - x {err_d:.3e}, cache K {ek:.3e}", flush=True)
+    assert err <= TOL["f16"] and err_d <= TOL["f16"] and ek <= TOL["f16"]
+    assert kv.lengths() == [P0 + S] * wl.batch
+
+
+def test_int8_kv_scale_pointers_are_checked():
+    wl = CASES["f16-d128-b1"]
+    gl, _ = gpu_layer_and_oracle_weights(wl, 0, kv_dtype="int8")
+    kv = tg.KVCache(1, wl.heads, 64, wl.head_dim, torch.int8, "cuda")
+    kv.k_scale = None
+    with pytest.raises(ValueError, match="k_scale"):
+        gl.decode(kv, torch.zeros((1, wl.hidden), dtype=torch.float16, device="cuda"))
+    gl16, _ = gpu_layer_and_oracle_weights(wl, 0)
+    kv8 = tg.KVCache(1, wl.heads, 64, wl.head_dim, torch.int8, "cuda")
+    with pytest.raises(ValueError, match="not int8"):
+        gl16.decode(kv8, torch.zeros((1, wl.hidden), dtype=torch.float16, device="cuda"))

@@ -51,6 +51,7 @@ class LayerConfig:
     gelu_tanh: bool = False
     triangular_masking: bool = True
     max_out_tokens: int = 1024
+    kv_dtype: int = 0              # 0: the cache in the activation dtype; DS_I8: int8 rows, fp16 scales
 
     @property
     def head_dim(self) -> int:
@@ -67,11 +68,15 @@ class LayerConfig:
     def c_desc(self) -> _lib.LayerDescC:
         return _lib.LayerDescC(self.hidden, self.heads, self.head_dim, self.ffn, self.dtype,
                                self.act_dtype, self.quant_group, self.quant_group_mlp, self.ln_eps,
-                               int(self.gelu_tanh), int(self.triangular_masking))
+                               int(self.gelu_tanh), int(self.triangular_masking), int(self.kv_dtype))
+
+    @property
+    def torch_cache_dtype(self) -> torch.dtype:
+        return torch.int8 if self.kv_dtype == DS_I8 else self.torch_act_dtype
 
 
 _CONFIG_KEYS = {"hidden", "heads", "ffn", "dtype", "quant_group", "quant_group_mlp", "ln_eps", "gelu_tanh",
-                "triangular_masking", "max_out_tokens", "quantization_setting"}
+                "triangular_masking", "max_out_tokens", "quantization_setting", "kv_dtype"}
 
 
 def make_config(config=None, **kwargs) -> LayerConfig:
@@ -102,6 +107,15 @@ def make_config(config=None, **kwargs) -> LayerConfig:
     if unknown:
         raise ValueError(f"unknown config keys: {sorted(unknown)}")
     dt = _dtype_code(base.pop("dtype", "fp16"))
+    kvd = base.pop("kv_dtype", None)
+    if kvd in (None, 0, "auto"):
+        kvd = 0
+    else:
+        kvd = _dtype_code(kvd)
+        if kvd != DS_I8 and kvd != (dt if dt in (DS_F32, DS_BF16) else DS_F16):
+            raise ValueError("kv_dtype is the activation dtype (the default) or int8")
+        kvd = DS_I8 if kvd == DS_I8 else 0
+    base["kv_dtype"] = kvd
     qs = base.pop("quantization_setting", None)
     group = base.pop("quant_group", None)
     group_mlp = base.pop("quant_group_mlp", None)
@@ -133,12 +147,18 @@ def make_config(config=None, **kwargs) -> LayerConfig:
 
 class KVCache:
     """Caller-owned K/V cache of one layer: k, v [batch][heads][capacity][head_dim] in the
-    activation dtype, device lengths d_len int32[batch] and an optional host mirror."""
+    activation dtype (or int8 codes with fp16 row scales k_scale, v_scale [batch][heads][capacity]
+    for a layer whose kv_dtype is int8), device lengths d_len int32[batch] and an optional host
+    mirror."""
 
     def __init__(self, batch, heads, capacity, head_dim, dtype, device="cuda", track_host=True):
         self.batch, self.heads, self.capacity, self.head_dim = batch, heads, capacity, head_dim
         self.k = torch.zeros((batch, heads, capacity, head_dim), dtype=dtype, device=device)
         self.v = torch.zeros_like(self.k)
+        self.k_scale = self.v_scale = None
+        if dtype == torch.int8:
+            self.k_scale = torch.zeros((batch, heads, capacity), dtype=torch.float16, device=device)
+            self.v_scale = torch.zeros_like(self.k_scale)
         self.d_len = torch.zeros(batch, dtype=torch.int32, device=device)
         self.h_len = _lib.host_lengths([0] * batch) if track_host else None
         self._c = None
@@ -146,8 +166,14 @@ class KVCache:
     def c_struct(self) -> _lib.KVCacheC:
         hl = self.h_len.ctypes.data_as(C.POINTER(C.c_int32)) if self.h_len is not None else None
         self._c = _lib.KVCacheC(self.k.data_ptr(), self.v.data_ptr(), self.d_len.data_ptr(), hl,
-                                self.batch, self.capacity)
+                                self.batch, self.capacity, ptr(self.k_scale), ptr(self.v_scale))
         return self._c
+
+    def dequantized(self):
+        """(k, v) as float32: the stored values, q * s for an int8 cache."""
+        if self.k_scale is None:
+            return self.k.float(), self.v.float()
+        return self.k.float() * self.k_scale.float()[..., None], self.v.float() * self.v_scale.float()[..., None]
 
     def set_lengths(self, lengths):
         vals = [int(v) for v in lengths]

@@ -34,7 +34,7 @@ class LayerDescC(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn", C.c_int32), ("weight_dtype", C.c_int32), ("act_dtype", C.c_int32),
                 ("quant_group", C.c_int32), ("quant_group_mlp", C.c_int32), ("ln_eps", C.c_float), ("gelu_tanh", C.c_int32),
-                ("triangular_masking", C.c_int32)]
+                ("triangular_masking", C.c_int32), ("kv_dtype", C.c_int32)]
 
 
 WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "s_qkv", "w_o", "b_o", "s_o",
@@ -66,7 +66,8 @@ class MoeWeightsC(C.Structure):
 
 class KVCacheC(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("d_len", C.c_void_p),
-                ("h_len", C.POINTER(C.c_int32)), ("batch", C.c_int32), ("capacity", C.c_int32)]
+                ("h_len", C.POINTER(C.c_int32)), ("batch", C.c_int32), ("capacity", C.c_int32),
+                ("k_scale", C.c_void_p), ("v_scale", C.c_void_p)]
 
 
 _LIB = None

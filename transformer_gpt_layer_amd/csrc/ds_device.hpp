@@ -160,6 +160,44 @@ __device__ __forceinline__ float dot4_f32(u32x4 w, float4_t a, float acc) {
   return acc;
 }
 
+// ---------------------------------------------------------------- int8 quantization
+// IEEE 754 binary16 bits of a double, round to nearest, ties to even, built directly on the
+// double's bit fields: keep 10 fraction bits below the leading one (fewer in the subnormal range
+// below 2^-14), round on the discarded bits, and let a carry ripple into the exponent field.
+__device__ inline uint16_t f64_to_f16_bits_rne(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  const uint64_t mag = u & 0x7fffffffffffffffull;
+  if (mag >= 0x7ff0000000000000ull) return sign | (mag > 0x7ff0000000000000ull ? 0x7e00u : 0x7c00u);
+  if (mag == 0) return sign;
+  const int e = (int)(mag >> 52) - 1023;
+  if (e > 15) return sign | 0x7c00u;
+  if (e < -25) return sign;  // below 2^-25, half the smallest subnormal: rounds to zero
+  const uint64_t m = (mag & ((1ull << 52) - 1)) | (1ull << 52);  // doubles this small are normal
+  const int shift = (e >= -14) ? 42 : 42 + (-14 - e);
+  uint64_t q = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1), halfway = 1ull << (shift - 1);
+  if (rem > halfway || (rem == halfway && (q & 1))) ++q;
+  uint32_t bits = (e >= -14) ? (uint32_t)(((e + 14) << 10) + q) : (uint32_t)q;
+  if (bits >= 0x7c00u) bits = 0x7c00u;
+  return sign | (uint16_t)bits;
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
+  return (double)(float)__builtin_bit_cast(half_t, h);
+}
+
+// Byte i (0..3) of w as a signed int8 value.
+__device__ __forceinline__ float i8_at(uint32_t w, int i) { return (float)(int)(int8_t)(uint8_t)(w >> (8 * i)); }
+
+// One value's int8 code under the fp16 scale sv (as a double): clamp(rint(x / sv), -127, 127),
+// 0 for a zero scale. With amax in double and sv = fp16_RNE(amax / 127) this is the group-wise
+// weight quantizer's rule; the KV cache uses it with one group per cached row of one head.
+__device__ __forceinline__ int32_t i8_code(double x, double sv) {
+  const double c = sv == 0.0 ? 0.0 : rint(x / sv);
+  return (int32_t)fmin(127.0, fmax(-127.0, c));
+}
+
 // ---------------------------------------------------------------- GeLU
 // u * Phi(u) = u/2 (1 + erf(u / sqrt 2)), or the tanh approximation
 // u/2 (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))); erf and tanh come from the ROCm device library.

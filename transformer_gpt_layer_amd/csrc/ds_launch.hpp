@@ -25,6 +25,7 @@ struct GemvArgs {
   void* v_cache;
   const int32_t* d_len;
   uint32_t* attn_counters;  // zeroed by the KIND_QKV launch: rows * heads counters
+  float* kv_new;            // KIND_QKV with an int8 cache: k and v as fp32 [rows][2H] instead of the cache
   int n, k, group, rows, tokens, cap, heads, head_dim, hidden;
   float eps;
   int gelu_tanh;
@@ -42,6 +43,9 @@ struct AttnArgs {
   // fp16 q and ctx in place of q and ctx (launch_attn_decode_f16)
   const _Float16* q16;
   _Float16* ctx16;
+  // an int8 cache: fp16 row scales [batch][heads][cap] (null for a cache in the activation type)
+  const void* k_scale;
+  const void* v_scale;
 };
 
 // The MoE expert FF of one step (kernels_moe.hip). T tokens, each with k chosen experts plus, for
@@ -83,6 +87,12 @@ int attn_chunks_for(int rows, int heads, int cap, int chunk, int nmax, int cus);
 hipError_t launch_kv_append(Dt adt, const void* k_new, const void* v_new, void* kc, void* vc,
                             const int32_t* d_len, int batch, int ntok, int heads, int head_dim,
                             int cap, hipStream_t st);
+// An int8 cache (fp16 row scales ks, vs): the rows [batch][ntok] of k and v, each `stride` elements
+// apart (type IT: F32 for fp32 rows from a projection, or the activation type), quantized per
+// (row, head) into the cache rows d_len[b] + t and their scales.
+hipError_t launch_kv_store_i8(Dt it, const void* ksrc, const void* vsrc, int stride, void* kc, void* vc, void* ks,
+                              void* vs, const int32_t* d_len, int batch, int ntok, int heads, int head_dim, int cap,
+                              hipStream_t st);
 // A GPU-side wait of about `microseconds` (the wall clock of the device, one thread).
 hipError_t launch_delay(uint32_t microseconds, hipStream_t st);
 // Zeroes `bytes` bytes at p (16-byte aligned; the size is rounded down to whole 16-byte pieces).

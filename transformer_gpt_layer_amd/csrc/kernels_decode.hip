@@ -113,6 +113,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
         const int H = a.hidden, d = a.head_dim;
         if (n < H) {
           a.q_out[(size_t)rr * H + n] = z;
+        } else if (a.kv_new) {
+          a.kv_new[(size_t)rr * 2 * H + (n - H)] = z;  // quantized into the int8 cache by kv_store_i8
         } else {
           const int seq = rr / a.tokens, t = rr - seq * a.tokens;
           const int pos = a.d_len[seq] + t;
@@ -229,11 +231,19 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
       const_cast<AT*>(reinterpret_cast<const AT*>(a.v_cache) + head_base), (short)0, (int)hbytes, 0x00020000);
   const int kl = wave * KPI + lane / LPK;  // this lane's key within a step
   u32x4 kr[PF], vr[PF];
+  float ksc[PF], vsc[PF];  // an int8 cache: the keys' fp16 row scales
+  const uint16_t* ksp = static_cast<const uint16_t*>(a.k_scale) + ((size_t)seq * a.heads + j) * a.cap;
+  const uint16_t* vsp = static_cast<const uint16_t*>(a.v_scale) + ((size_t)seq * a.heads + j) * a.cap;
   auto issue = [&](int step, int slot) {
     const int key = kb + step * KPS + kl;
-    const uint32_t off = step < nsteps && key < ke ? (uint32_t)(((size_t)key * D + e0) * sizeof(AT)) : 0x80000000u;
+    const bool live = step < nsteps && key < ke;
+    const uint32_t off = live ? (uint32_t)(((size_t)key * D + e0) * sizeof(AT)) : 0x80000000u;
     kr[slot] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
     vr[slot] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    if constexpr (sizeof(AT) == 1) {
+      ksc[slot] = live ? (float)__builtin_bit_cast(half_t, ksp[key]) : 0.f;
+      vsc[slot] = live ? (float)__builtin_bit_cast(half_t, vsp[key]) : 0.f;
+    }
   };
 #pragma unroll
   for (int q = 0; q < PF; ++q) issue(q, q);
@@ -250,10 +260,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
         float p = 0.f;
         if constexpr (sizeof(AT) == 4) {
           p = qv[0] * as_f32(kr[q].x) + qv[1] * as_f32(kr[q].y) + qv[2] * as_f32(kr[q].z) + qv[3] * as_f32(kr[q].w);
-        } else {
+        } else if constexpr (sizeof(AT) == 2) {
           const uint32_t wv[4] = {kr[q].x, kr[q].y, kr[q].z, kr[q].w};
 #pragma unroll
           for (int h = 0; h < 4; ++h) p += qv[2 * h] * lo16<AT>(wv[h]) + qv[2 * h + 1] * hi16<AT>(wv[h]);
+        } else {
+          const uint32_t wv[4] = {kr[q].x, kr[q].y, kr[q].z, kr[q].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) p += qv[4 * h + b] * i8_at(wv[h], b);
+          p *= ksc[q];
         }
         p = group_sum<LPK>(p);
         if (key < ke) {
@@ -266,13 +283,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
             acc[1] = acc[1] * cf + w * as_f32(vr[q].y);
             acc[2] = acc[2] * cf + w * as_f32(vr[q].z);
             acc[3] = acc[3] * cf + w * as_f32(vr[q].w);
-          } else {
+          } else if constexpr (sizeof(AT) == 2) {
             const uint32_t wv[4] = {vr[q].x, vr[q].y, vr[q].z, vr[q].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
               acc[2 * h] = acc[2 * h] * cf + w * lo16<AT>(wv[h]);
               acc[2 * h + 1] = acc[2 * h + 1] * cf + w * hi16<AT>(wv[h]);
             }
+          } else {
+            const uint32_t wv[4] = {vr[q].x, vr[q].y, vr[q].z, vr[q].w};
+            const float ws = w * vsc[q];
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+              for (int b = 0; b < 4; ++b) acc[4 * h + b] = acc[4 * h + b] * cf + ws * i8_at(wv[h], b);
           }
         }
       }
@@ -398,6 +422,7 @@ static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t st) {
 hipError_t launch_attn_decode_f16(const AttnArgs& a, hipStream_t st) { return launch_attn_d<half_t, true>(a, st); }
 
 hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st) {
+  if (a.k_scale) return adt == F16 || adt == BF16 ? launch_attn_d<int8_t, false>(a, st) : hipErrorInvalidValue;
   if (adt == F32) return launch_attn_d<float, false>(a, st);
   if (adt == F16) return launch_attn_d<half_t, false>(a, st);
   if (adt == BF16) return launch_attn_d<bf16_t, false>(a, st);

@@ -32,6 +32,62 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AT* __restrict__ k
   *reinterpret_cast<u32x4*>(vc + at) = ld16(vn + el);
 }
 
+// ------------------------------------------------------------------ int8 KV rows
+// One wave per (row r = b * ntok + t, head j, K or V): the head's d values of the new row (IT:
+// fp32 from a projection epilogue, or the activation type for an append), their amax (exact in
+// float), the row's fp16 scale and int8 codes (i8_code: the group-wise quantizer's rule with one
+// group per row), into the cache row d_len[b] + t and its scale. Rows at or past capacity are
+// skipped. d is 64 or 128: a lane holds one or two values.
+template <typename IT>
+__global__ __launch_bounds__(256) void kv_store_i8_kernel(const IT* __restrict__ ksrc, const IT* __restrict__ vsrc,
+                                                          int stride, int8_t* kc, int8_t* vc, uint16_t* ks, uint16_t* vs,
+                                                          const int32_t* d_len, int batch, int ntok, int heads, int d,
+                                                          int cap) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t item = (size_t)blockIdx.x * 4 + wave;  // (r * heads + j) * 2 + m
+  if (item >= (size_t)batch * ntok * heads * 2) return;
+  const int m = (int)(item & 1u);
+  const size_t rj = item >> 1;
+  const int j = (int)(rj % heads);
+  const size_t r = rj / heads;
+  const int b = (int)(r / ntok), t = (int)(r - (size_t)b * ntok);
+  const int pos = d_len[b] + t;
+  if (pos < 0 || pos >= cap) return;
+  const IT* src = (m ? vsrc : ksrc) + r * stride + (size_t)j * d;
+  const float x0 = lane < d ? to_f32(src[lane]) : 0.f;
+  const float x1 = lane + 64 < d ? to_f32(src[lane + 64]) : 0.f;
+  const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+  const uint16_t sb = f64_to_f16_bits_rne((double)amax / 127.0);
+  const double sv = f16_bits_to_f64(sb);
+  const size_t row = ((size_t)b * heads + j) * cap + pos;
+  int8_t* dst = (m ? vc : kc) + row * d;
+  if (lane < d) dst[lane] = (int8_t)i8_code((double)x0, sv);
+  if (lane + 64 < d) dst[lane + 64] = (int8_t)i8_code((double)x1, sv);
+  if (lane == 0) (m ? vs : ks)[row] = sb;
+}
+
+hipError_t launch_kv_store_i8(Dt it, const void* ksrc, const void* vsrc, int stride, void* kc, void* vc, void* ks,
+                              void* vs, const int32_t* d_len, int batch, int ntok, int heads, int head_dim, int cap,
+                              hipStream_t st) {
+  const size_t items = (size_t)batch * ntok * heads * 2;
+  if (items == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((items + 3) / 4);
+  int8_t *k8 = static_cast<int8_t*>(kc), *v8 = static_cast<int8_t*>(vc);
+  uint16_t *ks16 = static_cast<uint16_t*>(ks), *vs16 = static_cast<uint16_t*>(vs);
+  if (it == F32)
+    hipLaunchKernelGGL(kv_store_i8_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)ksrc, (const float*)vsrc,
+                       stride, k8, v8, ks16, vs16, d_len, batch, ntok, heads, head_dim, cap);
+  else if (it == F16)
+    hipLaunchKernelGGL(kv_store_i8_kernel<half_t>, dim3(blocks), dim3(256), 0, st, (const half_t*)ksrc,
+                       (const half_t*)vsrc, stride, k8, v8, ks16, vs16, d_len, batch, ntok, heads, head_dim, cap);
+  else if (it == BF16)
+    hipLaunchKernelGGL(kv_store_i8_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)ksrc,
+                       (const bf16_t*)vsrc, stride, k8, v8, ks16, vs16, d_len, batch, ntok, heads, head_dim, cap);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 // Zero fill of a 16-byte aligned buffer whose size is a multiple of 16 bytes (a kernel rather than a
 // memset node, so that it replays correctly inside captured graphs).
 __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* p, size_t n16) {
@@ -126,32 +182,6 @@ hipError_t launch_len_advance(int32_t* d_len, int batch, int ntok, int cap, hipS
 }
 
 // ------------------------------------------------------------------ int8 quantizer
-// IEEE 754 binary16 bits of a double, round to nearest, ties to even, built directly on the
-// double's bit fields: keep 10 fraction bits below the leading one (fewer in the subnormal range
-// below 2^-14), round on the discarded bits, and let a carry ripple into the exponent field.
-__device__ uint16_t f64_to_f16_bits_rne(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
-  const uint64_t mag = u & 0x7fffffffffffffffull;
-  if (mag >= 0x7ff0000000000000ull) return sign | (mag > 0x7ff0000000000000ull ? 0x7e00u : 0x7c00u);
-  if (mag == 0) return sign;
-  const int e = (int)(mag >> 52) - 1023;
-  if (e > 15) return sign | 0x7c00u;
-  if (e < -25) return sign;  // below 2^-25, half the smallest subnormal: rounds to zero
-  const uint64_t m = (mag & ((1ull << 52) - 1)) | (1ull << 52);  // doubles this small are normal
-  const int shift = (e >= -14) ? 42 : 42 + (-14 - e);
-  uint64_t q = m >> shift;
-  const uint64_t rem = m & ((1ull << shift) - 1), halfway = 1ull << (shift - 1);
-  if (rem > halfway || (rem == halfway && (q & 1))) ++q;
-  uint32_t bits = (e >= -14) ? (uint32_t)(((e + 14) << 10) + q) : (uint32_t)q;
-  if (bits >= 0x7c00u) bits = 0x7c00u;
-  return sign | (uint16_t)bits;
-}
-
-__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
-  return (double)(float)__builtin_bit_cast(half_t, h);
-}
-
 // One thread per (row, group): amax in double, scale = fp16_RNE(amax/127), codes = clamp(rint(w/s)).
 __global__ __launch_bounds__(256) void quantize_i8_kernel(const float* __restrict__ w, int8_t* __restrict__ q,
                                                           uint16_t* __restrict__ s, int n, int k, int group) {

@@ -56,6 +56,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 
+// the layer's cache holds int8 rows with fp16 scales
+bool kv_int8(const ds_layer_desc& d) { return d.kv_dtype == DS_I8; }
+
 // ds_layer_time_kernels: events recorded after each kernel launch of one step (the calling thread's
 // timer; null outside that call).
 constexpr int kMaxMarks = 16;
@@ -78,7 +81,7 @@ void mark(hipStream_t st, int kind) {
 }
 
 struct WsLayout {
-  size_t q, part, cnt, ctx, x2, f, h, sk_part, sk_cnt, total;
+  size_t q, part, cnt, ctx, x2, f, h, sk_part, sk_cnt, kvn, total;
   int chunk, nchunk, n_sk_cnt;
 };
 
@@ -100,6 +103,8 @@ WsLayout ws_layout(const ds_layer_desc& d, int rows, int cap) {
   L.sk_part = take(ds::skinny_part_bytes(n_max));
   L.sk_cnt = take(ds::skinny_cnt_bytes(n_max));
   L.n_sk_cnt = (n_max + 15) / 16;
+  // an int8 cache: the new k and v rows (fp32) between the QKV product and their quantization
+  L.kvn = kv_int8(d) ? take((size_t)rows * 2 * d.hidden * 4) : 0;
   L.total = off;
   return L;
 }
@@ -111,11 +116,16 @@ int check_kv(const ds_layer* L, const ds_kv_cache* kv, int batch, int ntok) {
   if (kv->batch < 1 || kv->capacity < 1) return fail(DS_ERR_SHAPE, "kv cache batch %d / capacity %d must be >= 1", kv->batch, kv->capacity);
   if (batch < 0 || batch > kv->batch) return fail(DS_ERR_SHAPE, "batch %d outside [0, %d]", batch, kv->batch);
   if (ntok < 0) return fail(DS_ERR_SHAPE, "token count %d < 0", ntok);
+  if (L->desc.kv_dtype == DS_I8) {
+    if (!kv->k_scale || !kv->v_scale) return fail(DS_ERR_NULL, "an int8 kv cache needs k_scale and v_scale");
+    if (!aligned16(kv->k_scale) || !aligned16(kv->v_scale)) return fail(DS_ERR_ALIGN, "kv scales are not 16-byte aligned");
+  } else if (kv->k_scale || kv->v_scale) {
+    return fail(DS_ERR_DTYPE, "kv scales are set but the layer's cache is not int8");
+  }
   if (kv->h_len)
     for (int b = 0; b < batch; ++b)
       if (kv->h_len[b] < 0 || (int64_t)kv->h_len[b] + ntok > kv->capacity)
         return fail(DS_ERR_KV_FULL, "sequence %d: %d rows + %d new > capacity %d", b, kv->h_len[b], ntok, kv->capacity);
-  (void)L;
   return DS_OK;
 }
 
@@ -124,7 +134,7 @@ constexpr int kMfmaMinRows = 16;
 // The MFMA path takes fp16 weights and activations, at least kMfmaMinRows rows, and operands whose
 // byte sizes stay inside one buffer descriptor's 31-bit range.
 bool use_mfma(const ds_layer_desc& d, int rows) {
-  if (d.weight_dtype != DS_F16 || d.act_dtype != DS_F16 || rows < kMfmaMinRows) return false;
+  if (d.weight_dtype != DS_F16 || d.act_dtype != DS_F16 || rows < kMfmaMinRows || kv_int8(d)) return false;
   const int64_t kmax = d.hidden > d.ffn ? d.hidden : d.ffn;
   const int64_t lim = int64_t(1) << 31;
   return (int64_t)rows * kmax * 2 < lim && (int64_t)d.ffn * d.hidden * 2 < lim && 3 * (int64_t)d.hidden * d.hidden * 2 < lim;
@@ -134,7 +144,7 @@ bool use_mfma(const ds_layer_desc& d, int rows) {
 // weights run the same LayerNorm / attention kernels with the skinny GEMM, which streams every
 // weight row once whatever the row count.
 bool use_skinny(const ds_layer_desc& d, int rows) {
-  if (d.act_dtype != DS_F16 || rows < 1 || rows > ds::kSkinnyMaxRows) return false;
+  if (d.act_dtype != DS_F16 || rows < 1 || rows > ds::kSkinnyMaxRows || kv_int8(d)) return false;
   if (d.weight_dtype == DS_F16) return rows < kMfmaMinRows;
   // the int8 skinny kernel applies one scale per 64-element block of K
   return d.weight_dtype == DS_I8 && d.quant_group == 64 && (d.quant_group_mlp == 0 || d.quant_group_mlp == 64);
@@ -285,7 +295,14 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   a.q_out = reinterpret_cast<float*>(base + W.q);
   a.k_cache = kv->k; a.v_cache = kv->v;
   a.attn_counters = reinterpret_cast<uint32_t*>(base + W.cnt);
+  if (kv_int8(d)) a.kv_new = reinterpret_cast<float*>(base + W.kvn);
   if (hipError_t e = ds::launch_gemv(wdt, adt, ds::KIND_QKV, a, st)) return hip_fail(e, "ln_qkv launch");
+  if (kv_int8(d)) {
+    const float* kvn = reinterpret_cast<const float*>(base + W.kvn);
+    if (hipError_t e = ds::launch_kv_store_i8(ds::F32, kvn, kvn + H, 2 * H, kv->k, kv->v, kv->k_scale, kv->v_scale,
+                                              kv->d_len, batch, ntok, d.heads, d.head_dim, kv->capacity, st))
+      return hip_fail(e, "int8 kv store launch");
+  }
   mark(st, DS_PART_QKV);
 
   // 2: attention over the cache
@@ -297,6 +314,8 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   at.ctx = reinterpret_cast<float*>(base + W.ctx);
   at.rows = rows; at.tokens = ntok; at.heads = d.heads; at.head_dim = d.head_dim;
   at.cap = kv->capacity; at.chunk = W.chunk; at.nchunk = W.nchunk; at.causal = d.triangular_masking;
+  at.k_scale = kv_int8(d) ? kv->k_scale : nullptr;
+  at.v_scale = kv_int8(d) ? kv->v_scale : nullptr;
   if (hipError_t e = ds::launch_attn_decode(adt, at, st)) return hip_fail(e, "attention launch");
   mark(st, DS_PART_ATTN);
 
@@ -366,6 +385,9 @@ int ds_layer_create(const ds_layer_desc* desc, const ds_layer_weights* w, ds_lay
                 d.quant_group_mlp);
   }
   if (!(d.ln_eps > 0.f) || !std::isfinite(d.ln_eps)) return fail(DS_ERR_SHAPE, "ln_eps must be finite and > 0");
+  if (d.kv_dtype != 0 && d.kv_dtype != DS_I8) return fail(DS_ERR_DTYPE, "kv_dtype %d must be 0 or DS_I8", d.kv_dtype);
+  if (d.kv_dtype == DS_I8 && d.act_dtype != DS_F16 && d.act_dtype != DS_BF16)
+    return fail(DS_ERR_DTYPE, "an int8 kv cache needs fp16 or bf16 activations");
   if ((d.gelu_tanh != 0 && d.gelu_tanh != 1) || (d.triangular_masking != 0 && d.triangular_masking != 1))
     return fail(DS_ERR_SHAPE, "gelu_tanh and triangular_masking must be 0 or 1");
 
@@ -416,9 +438,12 @@ int ds_kv_append(const ds_layer_t* layer, ds_kv_cache* kv, const void* k_new, co
   if (!aligned16(k_new) || !aligned16(v_new)) return fail(DS_ERR_ALIGN, "k_new or v_new is not 16-byte aligned");
   const ds_layer_desc& d = layer->desc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (hipError_t e = ds::launch_kv_append(static_cast<ds::Dt>(d.act_dtype), k_new, v_new, kv->k, kv->v, kv->d_len,
-                                          batch, ntok, d.heads, d.head_dim, kv->capacity, st))
-    return hip_fail(e, "kv_append launch");
+  hipError_t e = kv_int8(d) ? ds::launch_kv_store_i8(static_cast<ds::Dt>(d.act_dtype), k_new, v_new, d.hidden, kv->k,
+                                                     kv->v, kv->k_scale, kv->v_scale, kv->d_len, batch, ntok, d.heads,
+                                                     d.head_dim, kv->capacity, st)
+                            : ds::launch_kv_append(static_cast<ds::Dt>(d.act_dtype), k_new, v_new, kv->k, kv->v,
+                                                   kv->d_len, batch, ntok, d.heads, d.head_dim, kv->capacity, st);
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
   if (hipError_t e = ds::launch_len_advance(kv->d_len, batch, ntok, kv->capacity, st)) return hip_fail(e, "len advance launch");
   if (kv->h_len)
     for (int b = 0; b < batch; ++b) kv->h_len[b] += ntok;

@@ -174,6 +174,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
   for (int l = 0; l < n_layers; ++l)
     if (!layers[l]) return ds::set_error(DS_ERR_NULL, "layer %d is NULL", l);
   const ds_layer_desc d = layers[0]->desc;
+  if (d.kv_dtype != 0) return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode with an int8 kv cache is not built");
   for (int l = 1; l < n_layers; ++l)
     if (std::memcmp(&layers[l]->desc, &d, sizeof d) != 0)
       return ds::set_error(DS_ERR_SHAPE, "layer %d has a different description from layer 0", l);
