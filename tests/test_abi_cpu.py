@@ -227,6 +227,24 @@ def test_stack_create_rejects_before_device_work():
         rc = L.ds_stack_create(handles, caches, 2, 1, C.byref(head), C.c_void_p(FAKE), need, C.byref(out))
         assert rc == code, (rc, L.ds_last_error())
     assert not out.value
+    # an int8 kv cache: the stack needs its row scales, and fp16 activations
+    rc, h8 = _create(_desc(hidden=512, heads=4, ffn=1024, kv_dtype=_lib.DS_I8), _weights())
+    assert rc == 0, L.ds_last_error()
+    handles8 = (C.c_void_p * 2)(h8.value, h8.value)
+    assert L.ds_stack_create(handles8, caches, 2, 1, None, C.c_void_p(FAKE), need, C.byref(out)) == _lib.DS_ERR_NULL
+    assert "k_scale" in L.ds_last_error().decode()
+    scaled = (_lib.KVCacheC * 2)(*[_lib.KVCacheC(FAKE, FAKE, FAKE, hl.ctypes.data_as(C.POINTER(C.c_int32)), 1, 64,
+                                                 FAKE + 8, FAKE) for _ in range(2)])
+    assert L.ds_stack_create(handles8, scaled, 2, 1, None, C.c_void_p(FAKE), need, C.byref(out)) == _lib.DS_ERR_ALIGN
+    # scales on the caches of layers whose cache is not int8
+    assert L.ds_stack_create(handles, scaled, 2, 1, None, C.c_void_p(FAKE), need, C.byref(out)) == _lib.DS_ERR_DTYPE
+    L.ds_layer_destroy(h8)
+    rc, hb = _create(_desc(hidden=512, heads=4, ffn=1024, weight_dtype=3, act_dtype=3, kv_dtype=_lib.DS_I8), _weights())
+    assert rc == 0, L.ds_last_error()
+    handlesb = (C.c_void_p * 2)(hb.value, hb.value)
+    assert L.ds_stack_create(handlesb, scaled, 2, 1, None, C.c_void_p(FAKE), need, C.byref(out)) == _lib.DS_ERR_UNSUPPORTED
+    assert not out.value
+    L.ds_layer_destroy(hb)
     L.ds_layer_destroy(h2)
 
 

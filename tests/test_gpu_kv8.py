@@ -15,40 +15,13 @@ import torch
 import oracle
 import synthetic as syn
 import transformer_gpt_layer_amd as tg
-from tests._common import TOL, TORCH, gpu_layer_and_oracle_weights, rel_l2
+from tests._common import TOL, TORCH, gpu_layer_and_oracle_weights, kv8_caches, rel_l2
 
 pytestmark = pytest.mark.gpu
 
 
 def _wl(**kw):
     return dataclasses.replace(syn.WORKLOADS["c1"], **kw)
-
-
-def kv8_caches(wl, layer, gl, past=None, cap=None, batch=None):
-    """A GPU int8 KV cache holding `past` seeded rows (appended through ds_kv_append, which
-    quantizes them) and the oracle's float64 cache of the dequantized rows; the GPU's codes and
-    scales are checked bit for bit against the oracle's row quantizer on the same values."""
-    B = wl.batch if batch is None else batch
-    P = wl.past if past is None else past
-    cap = wl.capacity if cap is None else cap
-    act = TORCH[wl.act_dtype]
-    kv = tg.KVCache(B, wl.heads, cap, wl.head_dim, torch.int8, "cuda")
-    ok = np.zeros((B, wl.heads, cap, wl.head_dim))
-    ov = np.zeros_like(ok)
-    if P > 0:
-        kp = syn.normal((B, P, wl.hidden), 1.0, wl.cfg_id, layer, syn.K_PAST, "cuda").to(act)
-        vp = syn.normal((B, P, wl.hidden), 1.0, wl.cfg_id, layer, syn.V_PAST, "cuda").to(act)
-        gl.kv_append(kv, kp.contiguous(), vp.contiguous())
-        torch.cuda.synchronize()
-        for src, codes, scales, dst in ((kp, kv.k, kv.k_scale, ok), (vp, kv.v, kv.v_scale, ov)):
-            rows = src.double().cpu().numpy().reshape(B, P, wl.heads, wl.head_dim).transpose(0, 2, 1, 3)
-            q, s = oracle.quantize_rows_i8(rows)
-            assert np.array_equal(codes[:, :, :P].cpu().numpy(), q), "appended int8 codes differ from the oracle"
-            sb = scales[:, :, :P].cpu().view(torch.int16).numpy().view(np.uint16)
-            assert np.array_equal(sb, s), "appended fp16 row scales differ from the oracle"
-            dst[:, :, :P] = q.astype(np.float64) * oracle.fp16_to_double(s)[..., None]
-    lens = np.full(B, P, dtype=np.int32)
-    return kv, ok, ov, lens
 
 
 CASES = {

@@ -12,7 +12,7 @@ import torch
 import oracle
 import synthetic as syn
 import transformer_gpt_layer_amd as tg
-from tests._common import TOL, filled_caches, gpu_layer_and_oracle_weights, rel_l2
+from tests._common import TOL, filled_caches, gpu_layer_and_oracle_weights, kv8_caches, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -21,18 +21,22 @@ def _wl(base, **kw):
     return dataclasses.replace(syn.WORKLOADS[base] if isinstance(base, str) else base, **kw)
 
 
-def build(wl, layers, past=None, batch=None, gelu_tanh=False, cap=None):
+def build(wl, layers, past=None, batch=None, gelu_tanh=False, cap=None, kv8=False):
     B = wl.batch if batch is None else batch
     gls, ows, kvs, oks, ovs, lens = [], [], [], [], [], []
     for l in range(layers):
-        gl, ow = gpu_layer_and_oracle_weights(wl, l, gelu_tanh=gelu_tanh)
-        kv, ok, ov, ln = filled_caches(wl, l, gl, past=past, batch=B, cap=cap)
+        if kv8:
+            gl, ow = gpu_layer_and_oracle_weights(wl, l, gelu_tanh=gelu_tanh, kv_dtype="int8")
+            kv, ok, ov, ln = kv8_caches(wl, l, gl, past=past, batch=B, cap=cap)
+        else:
+            gl, ow = gpu_layer_and_oracle_weights(wl, l, gelu_tanh=gelu_tanh)
+            kv, ok, ov, ln = filled_caches(wl, l, gl, past=past, batch=B, cap=cap)
         gls.append(gl); ows.append(ow); kvs.append(kv); oks.append(ok); ovs.append(ov); lens.append(ln)
     return gls, ows, kvs, oks, ovs, lens
 
 
-def oracle_step(wl, ows, oks, ovs, lens, x, gelu_tanh=False):
-    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn, gelu_tanh=gelu_tanh)
+def oracle_step(wl, ows, oks, ovs, lens, x, gelu_tanh=False, kv8=False):
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn, gelu_tanh=gelu_tanh, kv_int8=kv8)
     h = x[:, None, :]
     for l in range(len(ows)):
         h = oracle.layer_forward(desc, ows[l], oks[l], ovs[l], lens[l], h)
@@ -109,6 +113,75 @@ def test_stack_decode_matches_oracle(name):
                 P = wl.past + step
                 assert rel_l2(kvs[l].k.double().cpu().numpy()[:, :, P], oks[l][:, :, P]) <= TOL[wl.act_dtype]
                 assert rel_l2(kvs[l].v.double().cpu().numpy()[:, :, P], ovs[l][:, :, P]) <= TOL[wl.act_dtype]
+
+
+# int8 KV caches (one fp16 scale per cached row of one head): the attention item that holds a
+# sequence's new row quantizes it and writes the cache. Past lengths 63 and 127 put the new rows
+# of consecutive steps on both sides of a chunk boundary.
+KV8_CASES = {
+    "f16-d128-b1-L3-affine-kv8": (_wl("c1", hidden=512, heads=4, head_dim=128, ffn=2048, weight_dtype="f16",
+                                      act_dtype="f16", batch=1, past=63, cfg_id=231, **AFFINE), 3, False),
+    "i8-d64-b3-L2-tanh-kv8": (_wl("c1", hidden=1024, heads=16, head_dim=64, ffn=2048, weight_dtype="i8",
+                                  act_dtype="f16", group=64, batch=3, past=70, cfg_id=232, **AFFINE), 2, True),
+    "f16-d128-b2-L2-g5-kv8": (_wl("c1", hidden=2560, heads=20, head_dim=128, ffn=5120, weight_dtype="f16",
+                                  act_dtype="f16", batch=2, past=127, cfg_id=233, **AFFINE), 2, False),
+    "i8-d128-b1-L2-g5-kv8": (_wl("c1", hidden=5120, heads=40, head_dim=128, ffn=5120, weight_dtype="i8",
+                                 act_dtype="f16", group=64, batch=1, past=5, cfg_id=234, **AFFINE), 2, False),
+}
+
+
+@pytest.mark.parametrize("name", list(KV8_CASES))
+def test_stack_decode_with_int8_kv_matches_oracle(name):
+    wl, L, tanh = KV8_CASES[name]
+    print(f"[stack int8 kv parity] {name}: {wl} layers={L} gelu_tanh={tanh}", flush=True)
+    gls, ows, kvs, oks, ovs, lens = build(wl, L, gelu_tanh=tanh, kv8=True)
+    with tg.Stack(gls, kvs, max_batch=wl.batch) as st:
+        ws = st.workspace(wl.batch)
+        for step in range(3):
+            x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, step, "cuda").half()
+            y = st.decode(x, workspace=ws)
+            st.check()
+            xd = x.double().cpu().numpy()
+            yo = oracle_step(wl, ows, oks, ovs, lens, xd, gelu_tanh=tanh, kv8=True)
+            yd = y.double().cpu().numpy()
+            err, err_d = rel_l2(yd, yo), rel_l2(yd - xd, yo - xd)
+            P = wl.past + step
+            news = []
+            for l in range(L):
+                assert kvs[l].lengths() == [P + 1] * wl.batch
+                kd, vd = kvs[l].dequantized()
+                news.append(rel_l2(kd[:, :, P].double().cpu().numpy(), oks[l][:, :, P]))
+                news.append(rel_l2(vd[:, :, P].double().cpu().numpy(), ovs[l][:, :, P]))
+                codes = torch.cat([kvs[l].k[:, :, P], kvs[l].v[:, :, P]], 1).cpu().numpy().astype(int)
+                assert np.all(np.abs(codes).max(-1) == 127), "a new row's codes do not reach 127"
+            print(f"  step {step}: rel L2 {err:.3e}, of y - x {err_d:.3e}; new rows worst {max(news):.3e}", flush=True)
+            assert err <= TOL["f16"] and err_d <= TOL["f16"] and max(news) <= TOL["f16"], (step, err, err_d, news)
+
+
+def test_stack_with_int8_kv_matches_the_per_layer_path():
+    """The stack and the per-layer path on the same int8 caches: the same codes for rows whose
+    quantization is not a near tie, and outputs within the activation type's rounding."""
+    wl = _wl("c1", hidden=1024, heads=8, head_dim=128, ffn=2048, weight_dtype="f16", act_dtype="f16", batch=2,
+             past=40, cfg_id=235, **AFFINE)
+    L = 2
+    gls, ows, kvs, oks, ovs, lens = build(wl, L, kv8=True)
+    _, _, kvs2, _, _, _ = build(wl, L, kv8=True)
+    x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").half()
+    with tg.Stack(gls, kvs, max_batch=wl.batch) as st:
+        y = st.decode(x)
+        st.check()
+    h = x
+    for l in range(L):
+        h = gls[l].decode(kvs2[l], h)
+    torch.cuda.synchronize()
+    err = rel_l2(y.double().cpu().numpy(), h.double().cpu().numpy())
+    print(f"  stack vs per-layer: rel L2 {err:.3e}", flush=True)
+    assert err <= 2e-3
+    for l in range(L):
+        for a, b in ((kvs[l].k, kvs2[l].k), (kvs[l].v, kvs2[l].v)):
+            d = (a[:, :, wl.past].int() - b[:, :, wl.past].int()).abs()
+            assert int(d.max()) <= 1 and float((d > 0).float().mean()) < 0.05
+        assert torch.equal(kvs[l].k[:, :, :wl.past], kvs2[l].k[:, :, :wl.past])
 
 
 def test_stack_ragged_lengths_in_a_large_cache():

@@ -20,6 +20,8 @@ struct StackLayer {
   void* k;
   void* v;
   int32_t* d_len;
+  void* ks;  // an int8 cache: fp16 row scales of K and V [batch][heads][cap]; null otherwise
+  void* vs;
 };
 
 // sync[] layout in 32-bit words, at the start of the caller-owned state buffer. Workgroups never
@@ -121,6 +123,7 @@ struct StackArgs {
   const void* x;   // [B][H] stack input (activation type)
   void* y;         // [B][H] stack output (activation type)
   int B, H, nh, d, F, cap, group, group_mlp;  // int8 scale groups: W_qkv, W_o, LM head; W_ff1, W_ff2
+  int kv8;         // the caches hold int8 codes with fp16 row scales (StackLayer ks, vs)
   float eps;
   int gelu_tanh;
   // workspace: tagged values (8 bytes each)
@@ -149,7 +152,7 @@ struct StackArgs {
 int stack_rows_per_wg(int H, int F, int V, int G);
 // Slices per worker group of the persistent kernel for these widths (1 or 5).
 int stack_group_slices(Dt wdt, int H, int F);
-hipError_t stack_max_groups(Dt wdt, Dt adt, int B, int GS, size_t lds, int* groups);
+hipError_t stack_max_groups(Dt wdt, Dt adt, bool kv8, int B, int GS, size_t lds, int* groups);
 hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, hipStream_t st);
 
 }  // namespace ds

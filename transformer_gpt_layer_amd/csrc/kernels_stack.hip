@@ -28,6 +28,8 @@
 // reads until their tags are current, so the grid never meets at a barrier. Every wait, in LDS or
 // on other workgroups' values, is bounded by a wall-clock timeout that raises the error flag,
 // after which every wave leaves the kernel.
+#include <type_traits>
+
 #include "ds_device.hpp"
 #include "ds_stack.hpp"
 
@@ -877,36 +879,57 @@ __device__ __forceinline__ AttnItem attn_item(const StackArgs& a, const int32_t*
   return it;
 }
 
-// Loads of an item's past rows (written by earlier launches) straight from the cache into kr, vr.
-template <typename AT, int D>
+// Loads of an item's past rows (written by earlier launches) straight from the cache into kr, vr;
+// KT is the cache's element type (the activation type, or int8 with the rows' fp16 scales, which
+// land in ksc, vsc).
+template <typename KT, int D>
 __device__ __forceinline__ void attn_load(const StackArgs& a, const StackLayer& L, int len, const AttnItem& it, int st,
-                                          u32x4 (&kr)[AttnShape<AT, D>::NIT], u32x4 (&vr)[AttnShape<AT, D>::NIT]) {
-  typedef AttnShape<AT, D> S;
+                                          u32x4 (&kr)[AttnShape<KT, D>::NIT], u32x4 (&vr)[AttnShape<KT, D>::NIT],
+                                          float (&ksc)[AttnShape<KT, D>::NIT], float (&vsc)[AttnShape<KT, D>::NIT]) {
+  typedef AttnShape<KT, D> S;
   constexpr int EK = S::EK, LPK = S::LPK, KPI = S::KPI, NIT = S::NIT;
   const int wave = st >> 6, lane = st & 63;
-  const size_t head = (((size_t)it.b * a.nh + it.j) * a.cap) * D;
-  const uint32_t bytes = (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(AT));
+  const size_t hrow = ((size_t)it.b * a.nh + it.j) * a.cap;  // the head's first cache row
+  const size_t head = hrow * D;
+  const uint32_t bytes = (uint32_t)((size_t)a.B * a.nh * a.cap * D * sizeof(KT));
   const rsrc_t rk = make_rsrc(L.k, bytes), rv = make_rsrc(L.v, bytes);
   const int e0 = (lane % LPK) * EK;
 #pragma unroll
   for (int i = 0; i < NIT; ++i) {
     const int key = it.cc * kStackChunk + (i * NS + wave) * KPI + lane / LPK;
     const bool past = key < len && key < a.cap && key < (it.cc + 1) * kStackChunk;
-    const uint32_t off = past ? (uint32_t)((head + (size_t)key * D + e0) * sizeof(AT)) : kOutOfRange;
+    const uint32_t off = past ? (uint32_t)((head + (size_t)key * D + e0) * sizeof(KT)) : kOutOfRange;
     kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
     vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    ksc[i] = vsc[i] = 0.f;
+    if constexpr (sizeof(KT) == 1) {
+      if (past) {
+        ksc[i] = (float)__builtin_bit_cast(half_t, static_cast<const uint16_t*>(L.ks)[hrow + key]);
+        vsc[i] = (float)__builtin_bit_cast(half_t, static_cast<const uint16_t*>(L.vs)[hrow + key]);
+      }
+    }
   }
+}
+
+// Largest value over aligned groups of G lanes; every lane gets its group's maximum.
+template <int G> __device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
 }
 
 // One item's partial: scores of q against the chunk's rows (the past rows in kr, vr from
 // attn_load, the new row at position len from this launch's tagged K/V), wave-reduced max and sum,
 // the exp-weighted V sum; (max, sum, acc[D]) is stored tagged for the workgroup that merges the
-// (sequence, head).
-template <typename AT, int D>
-__device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_t& sb, int len, const AttnItem& ai,
-                                             uint32_t tag_q, uint32_t tag_part, float* s_acc, int st,
-                                             u32x4 (&kr)[AttnShape<AT, D>::NIT], u32x4 (&vr)[AttnShape<AT, D>::NIT]) {
-  typedef AttnShape<AT, D> S;
+// (sequence, head). With an int8 cache (KT int8) the item that holds the new row quantizes it
+// (one fp16 scale per row: the row's amax over its lanes, the quantizer rule of i8_code), stores
+// the codes and scales into the cache for later launches, and attends over the dequantized row.
+template <typename KT, int D>
+__device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_t& sb, const StackLayer& L, int len,
+                                             const AttnItem& ai, uint32_t tag_q, uint32_t tag_part, float* s_acc, int st,
+                                             u32x4 (&kr)[AttnShape<KT, D>::NIT], u32x4 (&vr)[AttnShape<KT, D>::NIT],
+                                             float (&ksc)[AttnShape<KT, D>::NIT], float (&vsc)[AttnShape<KT, D>::NIT]) {
+  typedef AttnShape<KT, D> S;
   constexpr int EK = S::EK, LPK = S::LPK, KPI = S::KPI, NIT = S::NIT;
   const float kNeg = -1e30f;
   const int cc = ai.cc, j = ai.j, b = ai.b;
@@ -927,20 +950,49 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
   for (int it = 0; it < NIT; ++it) {
     const int key = cc * kStackChunk + (it * NS + wave) * KPI + lane / LPK;
     if (key == len && key < a.cap) {
-      float kn[EK], vn[EK];
       const rsrc_t rkn = make_rsrc(a.knew, (uint32_t)(a.B * H * 8)), rvn = make_rsrc(a.vnew, (uint32_t)(a.B * H * 8));
-      if (!poll_lane<EK>(c, a, rkn, (uint32_t)(b * H + j * D + e0), tag_q, kn)) return false;
-      if (!poll_lane<EK>(c, a, rvn, (uint32_t)(b * H + j * D + e0), tag_q, vn)) return false;
-      if constexpr (sizeof(AT) == 4) {
-        kr[it] = u32x4{__builtin_bit_cast(uint32_t, kn[0]), __builtin_bit_cast(uint32_t, kn[1]),
-                       __builtin_bit_cast(uint32_t, kn[2]), __builtin_bit_cast(uint32_t, kn[3])};
-        vr[it] = u32x4{__builtin_bit_cast(uint32_t, vn[0]), __builtin_bit_cast(uint32_t, vn[1]),
-                       __builtin_bit_cast(uint32_t, vn[2]), __builtin_bit_cast(uint32_t, vn[3])};
+      if constexpr (sizeof(KT) == 1) {
+        // the key's LPK lanes hold its D values: amax over them, the row scale, the codes; K, then V
+        const size_t row = ((size_t)b * a.nh + j) * a.cap + key;
+        auto quantize = [&](rsrc_t src, void* cache, void* scales, u32x4& codes, float& scale) -> bool {
+          float xn[EK];
+          if (!poll_lane<EK>(c, a, src, (uint32_t)(b * H + j * D + e0), tag_q, xn)) return false;
+          float am = 0.f;
+#pragma unroll
+          for (int e = 0; e < EK; ++e) am = fmaxf(am, fabsf(xn[e]));
+          am = group_max<LPK>(am);
+          const uint16_t bits = f64_to_f16_bits_rne((double)am / 127.0);
+          const double sv = f16_bits_to_f64(bits);
+          uint32_t w[4];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            w[h] = 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[h] |= ((uint32_t)i8_code((double)xn[4 * h + q], sv) & 0xffu) << (8 * q);
+          }
+          codes = u32x4{w[0], w[1], w[2], w[3]};
+          scale = (float)sv;
+          *reinterpret_cast<u32x4*>(static_cast<int8_t*>(cache) + row * D + e0) = codes;
+          if (lane % LPK == 0) static_cast<uint16_t*>(scales)[row] = bits;
+          return true;
+        };
+        if (!quantize(rkn, L.k, L.ks, kr[it], ksc[it])) return false;
+        if (!quantize(rvn, L.v, L.vs, vr[it], vsc[it])) return false;
       } else {
-        kr[it] = u32x4{pack16<AT>(kn[0], kn[1]), pack16<AT>(kn[2], kn[3]), pack16<AT>(kn[4], kn[5]),
-                       pack16<AT>(kn[6], kn[7])};
-        vr[it] = u32x4{pack16<AT>(vn[0], vn[1]), pack16<AT>(vn[2], vn[3]), pack16<AT>(vn[4], vn[5]),
-                       pack16<AT>(vn[6], vn[7])};
+        float kn[EK], vn[EK];
+        if (!poll_lane<EK>(c, a, rkn, (uint32_t)(b * H + j * D + e0), tag_q, kn)) return false;
+        if (!poll_lane<EK>(c, a, rvn, (uint32_t)(b * H + j * D + e0), tag_q, vn)) return false;
+        if constexpr (sizeof(KT) == 4) {
+          kr[it] = u32x4{__builtin_bit_cast(uint32_t, kn[0]), __builtin_bit_cast(uint32_t, kn[1]),
+                         __builtin_bit_cast(uint32_t, kn[2]), __builtin_bit_cast(uint32_t, kn[3])};
+          vr[it] = u32x4{__builtin_bit_cast(uint32_t, vn[0]), __builtin_bit_cast(uint32_t, vn[1]),
+                         __builtin_bit_cast(uint32_t, vn[2]), __builtin_bit_cast(uint32_t, vn[3])};
+        } else {
+          kr[it] = u32x4{pack16<KT>(kn[0], kn[1]), pack16<KT>(kn[2], kn[3]), pack16<KT>(kn[4], kn[5]),
+                         pack16<KT>(kn[6], kn[7])};
+          vr[it] = u32x4{pack16<KT>(vn[0], vn[1]), pack16<KT>(vn[2], vn[3]), pack16<KT>(vn[4], vn[5]),
+                         pack16<KT>(vn[6], vn[7])};
+        }
       }
     }
   }
@@ -953,12 +1005,19 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
     const int key = cc * kStackChunk + (it * NS + wave) * KPI + lane / LPK;
     valid[it] = key < nkeys && key < (cc + 1) * kStackChunk;
     float p = 0.f;
-    if constexpr (sizeof(AT) == 4) {
+    if constexpr (sizeof(KT) == 4) {
       p = qv[0] * as_f32(kr[it].x) + qv[1] * as_f32(kr[it].y) + qv[2] * as_f32(kr[it].z) + qv[3] * as_f32(kr[it].w);
+    } else if constexpr (sizeof(KT) == 2) {
+      const uint32_t wv[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) p += qv[2 * h] * lo16<KT>(wv[h]) + qv[2 * h + 1] * hi16<KT>(wv[h]);
     } else {
       const uint32_t wv[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) p += qv[2 * h] * lo16<AT>(wv[h]) + qv[2 * h + 1] * hi16<AT>(wv[h]);
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p += qv[4 * h + q] * i8_at(wv[h], q);
+      p *= ksc[it];
     }
     p = group_sum<LPK>(p);
     sc[it] = valid[it] ? p : kNeg;
@@ -972,18 +1031,25 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
   for (int it = 0; it < NIT; ++it) {
     const float p = valid[it] ? exp2f(sc[it] - m) : 0.f;
     l += p;
-    if constexpr (sizeof(AT) == 4) {
+    if constexpr (sizeof(KT) == 4) {
       acc[0] += p * as_f32(vr[it].x);
       acc[1] += p * as_f32(vr[it].y);
       acc[2] += p * as_f32(vr[it].z);
       acc[3] += p * as_f32(vr[it].w);
-    } else {
+    } else if constexpr (sizeof(KT) == 2) {
       const uint32_t wv[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        acc[2 * h] += p * lo16<AT>(wv[h]);
-        acc[2 * h + 1] += p * hi16<AT>(wv[h]);
+        acc[2 * h] += p * lo16<KT>(wv[h]);
+        acc[2 * h + 1] += p * hi16<KT>(wv[h]);
       }
+    } else {
+      const float pv = p * vsc[it];
+      const uint32_t wv[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[4 * h + q] += pv * i8_at(wv[h], q);
     }
   }
 #pragma unroll
@@ -1059,7 +1125,7 @@ __device__ __forceinline__ bool attn_merge(Ctl& c, const StackArgs& a, uint32_t&
 }
 
 // ------------------------------------------------------------------ sync waves: the phase loop
-template <typename WT, typename AT, int BM, int D>
+template <typename WT, typename AT, int BM, int D, bool KV8>
 __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned char* smem, int g, int st_in,
                                           uint32_t launch) {
   typedef typename WTraits<WT>::LT LT;
@@ -1082,8 +1148,10 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     st = t;
   };
   uint32_t sb = 0;
-  typedef AttnShape<AT, D> AS;
-  u32x4 kr[AS::NIT], vr[AS::NIT];  // the past rows of the current attention item
+  typedef typename std::conditional<KV8, int8_t, AT>::type KT;  // the cache's element type
+  typedef AttnShape<KT, D> AS;
+  u32x4 kr[AS::NIT], vr[AS::NIT];    // the past rows of the current attention item
+  float ksc[AS::NIT], vsc[AS::NIT];  // and their row scales (an int8 cache)
 
   // LayerNorm of the B rows of H into act, from `plain` (the caller's input) when given, else from
   // the tagged values at `tagged`: in registers when the rows fit, else through LDS
@@ -1175,11 +1243,16 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
           tstore(rqo, (uint32_t)(b * H + n), z, t_q);
         } else {
           const int m = n < 2 * H ? n - H : n - 2 * H, j = m / D, e = m - j * D;
-          const float zr = (float)(AT)z;  // the value the cache holds
-          tstore(n < 2 * H ? rkn : rvn, (uint32_t)(b * H + m), zr, t_q);
-          const int pos = t == st ? pre_pos : lens[b];
-          if (pos >= 0 && pos < a.cap)
-            coh_st_act<AT>(n < 2 * H ? rk : rv, (uint32_t)((((size_t)b * a.nh + j) * a.cap + pos) * D + e), z);
+          if constexpr (KV8) {
+            // the attention item of the new row quantizes it and writes the cache
+            tstore(n < 2 * H ? rkn : rvn, (uint32_t)(b * H + m), z, t_q);
+          } else {
+            const float zr = (float)(AT)z;  // the value the cache holds
+            tstore(n < 2 * H ? rkn : rvn, (uint32_t)(b * H + m), zr, t_q);
+            const int pos = t == st ? pre_pos : lens[b];
+            if (pos >= 0 && pos < a.cap)
+              coh_st_act<AT>(n < 2 * H ? rk : rv, (uint32_t)((((size_t)b * a.nh + j) * a.cap + pos) * D + e), z);
+          }
         }
       }
     }
@@ -1190,8 +1263,8 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     for (int item = g; item < nitems; item += G) {
       const AttnItem it = attn_item(a, lens, nvmax, item);
       if (!it.valid) continue;
-      attn_load<AT, D>(a, L, lens[it.b], it, st, kr, vr);
-      if (!attn_partial<AT, D>(c, a, sb, lens[it.b], it, t_q, t_part, s_acc, st, kr, vr)) return;
+      attn_load<KT, D>(a, L, lens[it.b], it, st, kr, vr, ksc, vsc);
+      if (!attn_partial<KT, D>(c, a, sb, L, lens[it.b], it, t_q, t_part, s_acc, st, kr, vr, ksc, vsc)) return;
     }
     for (int item = g; item < nitems; item += G) {
       const AttnItem it = attn_item(a, lens, nvmax, item);
@@ -1350,7 +1423,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 }  // namespace
 
 // ------------------------------------------------------------------ the persistent kernel
-template <typename WT, typename AT, int BM, int D, int GS>
+template <typename WT, typename AT, int BM, int D, int GS, bool KV8>
 __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const StackArgs a) {
   typedef typename WTraits<WT>::LT LT;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1392,7 +1465,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void stack_decode_kernel(const St
   const int lane = threadIdx.x & 63;
   if (wave < NS) {
     const uint32_t launch = __builtin_amdgcn_readfirstlane(c.launch);
-    sync_side<WT, AT, BM, D>(a, c, smem, blockIdx.x, (int)threadIdx.x, launch);
+    sync_side<WT, AT, BM, D, KV8>(a, c, smem, blockIdx.x, (int)threadIdx.x, launch);
     if (lds_ld(&c.abort) == 0u) return;
     raise_abort(c, a.sync);  // a failed sync wave releases the workers
   } else {
@@ -1410,9 +1483,9 @@ int stack_rows_per_wg(int H, int F, int V, int G) {
   return r;
 }
 
-template <typename WT, typename AT, int BM, int D, int GS>
+template <typename WT, typename AT, int BM, int D, int GS, bool KV8 = false>
 static const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&stack_decode_kernel<WT, AT, BM, D, GS>);
+  return reinterpret_cast<const void*>(&stack_decode_kernel<WT, AT, BM, D, GS, KV8>);
 }
 
 // Slices per worker group: 5 when every row of the stack's products (K = hidden or ffn) holds a
@@ -1423,34 +1496,41 @@ int stack_group_slices(Dt wdt, int H, int F) {
 }
 
 // Instantiated variants: batch tiles of 1 or 4 rows (2..4 sequences use the 4-row tile), head_dim 64
-// or 128, groups of 1 or 5 slices.
-static const void* pick(Dt wdt, Dt adt, int B, int D, int GS) {
+// or 128, groups of 1 or 5 slices; an int8 cache with fp16 activations.
+static const void* pick(Dt wdt, Dt adt, bool kv8, int B, int D, int GS) {
   const bool one = B <= 1;
-#define DS_PICK_G(WT_, AT_, G_)                                                                        \
-  {                                                                                                     \
-    if (D == 64) return one ? kernel_ptr<WT_, AT_, 1, 64, G_>() : kernel_ptr<WT_, AT_, 4, 64, G_>();    \
-    return one ? kernel_ptr<WT_, AT_, 1, 128, G_>() : kernel_ptr<WT_, AT_, 4, 128, G_>();              \
+#define DS_PICK_G(WT_, AT_, G_, K_)                                                                           \
+  {                                                                                                            \
+    if (D == 64) return one ? kernel_ptr<WT_, AT_, 1, 64, G_, K_>() : kernel_ptr<WT_, AT_, 4, 64, G_, K_>();   \
+    return one ? kernel_ptr<WT_, AT_, 1, 128, G_, K_>() : kernel_ptr<WT_, AT_, 4, 128, G_, K_>();             \
   }
-#define DS_PICK(WT_, AT_)                \
-  {                                      \
-    if (GS == 5) DS_PICK_G(WT_, AT_, 5)  \
-    DS_PICK_G(WT_, AT_, 1)               \
+#define DS_PICK_K(WT_, AT_, K_)              \
+  {                                          \
+    if (GS == 5) DS_PICK_G(WT_, AT_, 5, K_)  \
+    DS_PICK_G(WT_, AT_, 1, K_)               \
   }
+#define DS_PICK(WT_, AT_)                         \
+  {                                               \
+    if (kv8) DS_PICK_K(WT_, AT_, true)            \
+    DS_PICK_K(WT_, AT_, false)                    \
+  }
+  if (kv8 && adt != F16) return nullptr;
   if (wdt == F16 && adt == F16) DS_PICK(half_t, half_t)
   if (wdt == I8 && adt == F16) DS_PICK(int8_t, half_t)
-  if (wdt == BF16 && adt == BF16) DS_PICK(bf16_t, bf16_t)
+  if (wdt == BF16 && adt == BF16) DS_PICK_K(bf16_t, bf16_t, false)
   if (wdt == F32 && adt == F32 && one) {
     if (GS == 5) return D == 64 ? kernel_ptr<float, float, 1, 64, 5>() : kernel_ptr<float, float, 1, 128, 5>();
     return D == 64 ? kernel_ptr<float, float, 1, 64, 1>() : kernel_ptr<float, float, 1, 128, 1>();
   }
 #undef DS_PICK
+#undef DS_PICK_K
 #undef DS_PICK_G
   return nullptr;
 }
 
-hipError_t stack_max_groups(Dt wdt, Dt adt, int B, int GS, size_t lds, int* groups) {
+hipError_t stack_max_groups(Dt wdt, Dt adt, bool kv8, int B, int GS, size_t lds, int* groups) {
   // head_dim does not change the register or LDS footprint enough to matter: query d = 128
-  const void* k = pick(wdt, adt, B, 128, GS);
+  const void* k = pick(wdt, adt, kv8, B, 128, GS);
   if (!k) return hipErrorInvalidValue;
   int per_cu = 0, dev = 0;
   hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1466,7 +1546,7 @@ hipError_t stack_max_groups(Dt wdt, Dt adt, int B, int GS, size_t lds, int* grou
 }
 
 hipError_t launch_stack_decode(Dt wdt, Dt adt, const StackArgs& a, hipStream_t st) {
-  const void* k = pick(wdt, adt, a.B, a.d, stack_group_slices(wdt, a.H, a.F));
+  const void* k = pick(wdt, adt, a.kv8 != 0, a.B, a.d, stack_group_slices(wdt, a.H, a.F));
   if (!k) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)a.lds.total);
   if (e != hipSuccess) return e;

@@ -174,7 +174,9 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
   for (int l = 0; l < n_layers; ++l)
     if (!layers[l]) return ds::set_error(DS_ERR_NULL, "layer %d is NULL", l);
   const ds_layer_desc d = layers[0]->desc;
-  if (d.kv_dtype != 0) return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode with an int8 kv cache is not built");
+  const bool kv8 = d.kv_dtype == DS_I8;
+  if (kv8 && d.act_dtype != DS_F16)
+    return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode with an int8 kv cache needs fp16 activations");
   for (int l = 1; l < n_layers; ++l)
     if (std::memcmp(&layers[l]->desc, &d, sizeof d) != 0)
       return ds::set_error(DS_ERR_SHAPE, "layer %d has a different description from layer 0", l);
@@ -188,9 +190,15 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
     const ds_kv_cache& c = caches[l];
     if (!c.k || !c.v || !c.d_len) return ds::set_error(DS_ERR_NULL, "cache %d: k, v or d_len is NULL", l);
     if (!aligned16(c.k) || !aligned16(c.v)) return ds::set_error(DS_ERR_ALIGN, "cache %d is not 16-byte aligned", l);
+    if (kv8 && (!c.k_scale || !c.v_scale))
+      return ds::set_error(DS_ERR_NULL, "cache %d: an int8 kv cache needs k_scale and v_scale", l);
+    if (kv8 && (!aligned16(c.k_scale) || !aligned16(c.v_scale)))
+      return ds::set_error(DS_ERR_ALIGN, "cache %d: kv scales are not 16-byte aligned", l);
+    if (!kv8 && (c.k_scale || c.v_scale))
+      return ds::set_error(DS_ERR_DTYPE, "cache %d has scales but the layers' kv cache is not int8", l);
     if (c.batch < max_batch || c.capacity < 1 || c.capacity != caches[0].capacity)
       return ds::set_error(DS_ERR_SHAPE, "cache %d: batch %d < %d or capacity differs from cache 0", l, c.batch, max_batch);
-    if ((size_t)c.batch * d.heads * c.capacity * d.head_dim * act_bytes(d.act_dtype) >= (1ull << 31))
+    if ((size_t)c.batch * d.heads * c.capacity * d.head_dim * (kv8 ? 1 : act_bytes(d.act_dtype)) >= (1ull << 31))
       return ds::set_error(DS_ERR_UNSUPPORTED, "cache %d is 2 GiB or larger", l);
   }
 
@@ -226,7 +234,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
       return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode: %u bytes of LDS per workgroup needed", lay.total);
     }
     int fit = 0;
-    e = ds::stack_max_groups(wdt, adt, max_batch, ds::stack_group_slices(wdt, d.hidden, d.ffn), lay.total, &fit);
+    e = ds::stack_max_groups(wdt, adt, kv8, max_batch, ds::stack_group_slices(wdt, d.hidden, d.ffn), lay.total, &fit);
     if (e == hipSuccess) G = G < fit ? G : fit;
   }
   if (e != hipSuccess || G < 1) {
@@ -240,7 +248,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
     const ds_layer_weights& w = layers[l]->w;
     table[l] = ds::StackLayer{w.ln1_g, w.ln1_b, w.w_qkv, w.b_qkv, w.s_qkv, w.w_o, w.b_o, w.s_o,
                               w.ln2_g, w.ln2_b, w.w_ff1, w.b_ff1, w.s_ff1, w.w_ff2, w.b_ff2, w.s_ff2,
-                              caches[l].k, caches[l].v, caches[l].d_len};
+                              caches[l].k, caches[l].v, caches[l].d_len, caches[l].k_scale, caches[l].v_scale};
   }
   S->sync_words = ds::kSyncWords;
   S->uid = g_next_uid.fetch_add(1);
@@ -344,6 +352,7 @@ int stack_forward(ds_stack_t* S, const void* x, void* y, float* logits, int32_t*
   a.cap = cap;
   a.group = d.quant_group;
   a.group_mlp = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
+  a.kv8 = d.kv_dtype == DS_I8 ? 1 : 0;
   a.eps = d.ln_eps;
   a.gelu_tanh = d.gelu_tanh;
   a.q = reinterpret_cast<uint2*>(base + W.q);
