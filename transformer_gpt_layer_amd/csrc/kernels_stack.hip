@@ -548,7 +548,7 @@ __device__ __forceinline__ bool stage_ln(Ctl& c, const StackArgs& a, uint32_t& s
                                          const AT* __restrict__ gam, const AT* __restrict__ beta, LT* act, float* raw,
                                          AT* gb, int st, Fill fill) {
   constexpr int VG = 16 / (int)sizeof(AT);
-  constexpr int kGB = 2;  // gamma/beta vectors per thread issued ahead of the rows
+  constexpr int kGB = 3;  // gamma/beta vectors per thread issued ahead of the rows (K <= 6144 at 16 bits)
   const int ngv = K / VG;
   const rsrc_t rg = make_rsrc(gam, (uint32_t)(K * sizeof(AT))), rb = make_rsrc(beta, (uint32_t)(K * sizeof(AT)));
   u32x4 gv[kGB], bv[kGB];
@@ -844,8 +844,31 @@ __device__ __forceinline__ bool stage_ln_regs(Ctl& c, const StackArgs& a, uint32
 // int8: the fp16 scales of the phase's row tile, [nr][K/group], into LDS.
 __device__ __forceinline__ void stage_scales(const void* s, int r0, int nr, int K, int group, half_t* scl, int st) {
   const int n = nr * (K / group);
-  const half_t* src = static_cast<const half_t*>(s) + (size_t)r0 * (K / group);
-  for (int i = st; i < n; i += NT) scl[i] = src[i];
+  const size_t e0 = (size_t)r0 * (K / group);
+  const half_t* src = static_cast<const half_t*>(s) + e0;
+  int done = 0;
+  if ((e0 & 7) == 0) {
+    // 16-byte loads, kScaleVec per thread issued before any is written: one memory round trip
+    // per kScaleVec * NT vectors (a round trip is long while the workers stream)
+    constexpr int kScaleVec = 4;
+    const int nv = n >> 3;
+    const rsrc_t r = make_rsrc(src, (uint32_t)n * 2u);
+    for (int j0 = 0; j0 < nv; j0 += kScaleVec * NT) {
+      u32x4 v[kScaleVec];
+#pragma unroll
+      for (int u = 0; u < kScaleVec; ++u) {
+        const int j = j0 + st + u * NT;
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, j < nv ? (uint32_t)(j * 16) : kOutOfRange, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kScaleVec; ++u) {
+        const int j = j0 + st + u * NT;
+        if (j < nv) *reinterpret_cast<u32x4*>(scl + j * 8) = v[u];
+      }
+    }
+    done = nv * 8;
+  }
+  for (int i = done + st; i < n; i += NT) scl[i] = src[i];
 }
 
 // ------------------------------------------------------------------ sync waves: attention
