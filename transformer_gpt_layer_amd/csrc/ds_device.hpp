@@ -126,10 +126,11 @@ template <> __device__ __forceinline__ float dot8<bf16_t>(u32x4 w, u32x4 a, floa
 // int8 -> fp16, exactly: with the byte offset to unsigned u = q + 128, the fp16 bit pattern
 // 0x6400 | u encodes 1024 + u (in [1024, 2048) the fp16 spacing is 1), so subtracting
 // 1152 = 1024 + 128 leaves q exactly. Two bytes of `w` (selected by `hi`) become one half2.
+// One v_perm_b32 builds both halves: over the byte string {0x64 x 4 (bytes 4-7), w (bytes 0-3)}
+// it picks bytes (u0, 0x64, u1, 0x64) from the low (selector 0x04010400) or high (0x04030402)
+// pair of w.
 __device__ __forceinline__ half2_t i8pair_to_half2(uint32_t w_biased, bool hi) {
-  uint32_t b0 = hi ? (w_biased >> 16) & 0xffu : w_biased & 0xffu;
-  uint32_t b1 = hi ? (w_biased >> 24) : (w_biased >> 8) & 0xffu;
-  uint32_t bits = 0x64006400u | b0 | (b1 << 16);
+  const uint32_t bits = __builtin_amdgcn_perm(0x64646464u, w_biased, hi ? 0x04030402u : 0x04010400u);
   const half2_t off = {(half_t)1152.0f, (half_t)1152.0f};
   return as_half2(bits) - off;
 }

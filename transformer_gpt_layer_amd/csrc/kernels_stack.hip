@@ -431,6 +431,9 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
   int K = tab_ld(c, w, 0, T_K), Sper = tab_ld(c, w, 0, T_SPER);
   int rl = tab_ld(c, w, 0, T_RL0), ks = tab_ld(c, w, 0, T_KS0);
   int grp = tab_ld(c, w, 0, T_GRP), spr = K / grp;  // int8: scale group and scales per row
+  // int8: the group of element x of a row is x / grp = mulhi(x, ceil(2^32 / grp)), exact while
+  // x * grp < 2^32 (stack creation checks row length x group against that bound)
+  uint32_t ginv = (uint32_t)(((1ull << 32) + (uint64_t)grp - 1) / (uint64_t)grp);
   bool wait_act = true;
   // leave step cp [finished or empty], publishing it, and move to the next non-empty one
   auto c_advance = [&]() {
@@ -449,6 +452,7 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
     ks = tab_ld(c, w, t, T_KS0);
     grp = tab_ld(c, w, t, T_GRP);
     spr = K / grp;
+    ginv = (uint32_t)(((1ull << 32) + (uint64_t)grp - 1) / (uint64_t)grp);
     wait_act = true;
   };
   if (ccnt == 0) c_advance();
@@ -504,7 +508,7 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
           for (int k = 0; k < GS; ++k) {
             float sc = 1.f;
             if constexpr (sizeof(WT) == 1)
-              sc = (float)scl[rl * spr + ((ks * GS + k) * SL + lane * E) / grp];
+              sc = (float)scl[rl * spr + __umulhi((uint32_t)((ks * GS + k) * SL + lane * E), ginv)];
 #pragma unroll
             for (int b = 0; b < BM; ++b) {
               const LT* apk = ap + k * SL + b * K;

@@ -102,6 +102,11 @@ int min_group(const ds_layer_desc& d) {
   const int gm = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
   return gm < d.quant_group ? gm : d.quant_group;
 }
+int max_group(const ds_layer_desc& d) {
+  if (d.weight_dtype != DS_I8) return 1;
+  const int gm = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
+  return gm > d.quant_group ? gm : d.quant_group;
+}
 
 struct StackWs {
   size_t q, knew, vnew, part, ctx, x2, f, y, total;
@@ -186,6 +191,8 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
     return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode needs every weight matrix under 2 GiB");
   if (d.hidden % sl || d.ffn % sl || d.hidden > 8192)
     return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode needs hidden and ffn multiples of %d and hidden <= 8192", sl);
+  if (d.weight_dtype == DS_I8 && (size_t)(d.hidden > d.ffn ? d.hidden : d.ffn) * (size_t)max_group(d) >= (1ull << 32))
+    return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode needs row length x int8 group below 2^32");
   for (int l = 0; l < n_layers; ++l) {
     const ds_kv_cache& c = caches[l];
     if (!c.k || !c.v || !c.d_len) return ds::set_error(DS_ERR_NULL, "cache %d: k, v or d_len is NULL", l);
