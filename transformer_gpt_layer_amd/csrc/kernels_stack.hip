@@ -236,26 +236,28 @@ __device__ __forceinline__ bool grid_error(const StackArgs& a) {
 }
 
 constexpr int kPollUnroll = 8;  // 16-byte loads (two tagged values each) a thread keeps in flight
+constexpr int kPollWide = 10;   // the same for the LayerNorm rows past the register path and for f:
+                                // one round for 5120 values (hidden 5120, or ffn 10240 as pairs)
 
 // Wait until the tagged values [0, n) at src all carry `tag`, handing each one once to put(i, v).
 // Threads st, st+NT, ... of the sync waves share the work.
-template <typename Put>
+template <int U = kPollUnroll, typename Put>
 __device__ __forceinline__ bool poll_range(Ctl& c, const StackArgs& a, const uint2* src, int n, uint32_t tag, int st,
                                            Put put) {
   const rsrc_t r = make_rsrc(src, (uint32_t)n * 8u);
   const int nv = (n + 1) >> 1;
-  for (int j0 = st; j0 < nv; j0 += NT * kPollUnroll) {
-    bool need[kPollUnroll];
+  for (int j0 = st; j0 < nv; j0 += NT * U) {
+    bool need[U];
 #pragma unroll
-    for (int u = 0; u < kPollUnroll; ++u) need[u] = j0 + u * NT < nv;
+    for (int u = 0; u < U; ++u) need[u] = j0 + u * NT < nv;
     uint64_t t0 = 0;
     for (int round = 0;; ++round) {
-      u32x4 v[kPollUnroll];
+      u32x4 v[U];
 #pragma unroll
-      for (int u = 0; u < kPollUnroll; ++u) v[u] = coh_load16(r, need[u] ? (uint32_t)((j0 + u * NT) * 16) : kOutOfRange);
+      for (int u = 0; u < U; ++u) v[u] = coh_load16(r, need[u] ? (uint32_t)((j0 + u * NT) * 16) : kOutOfRange);
       bool stale = false;
 #pragma unroll
-      for (int u = 0; u < kPollUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         if (!need[u]) continue;
         const int i = 2 * (j0 + u * NT);
         const bool second = i + 1 < n;
@@ -1192,7 +1194,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
         load_rows_plain<AT>(plain, B, H, raw, st);
         return true;
       }
-      return poll_range(c, a, tagged, B * H, tag, st, [&](int i, float v) { raw[i] = v; });
+      return poll_range<kPollWide>(c, a, tagged, B * H, tag, st, [&](int i, float v) { raw[i] = v; });
     });
   };
 
@@ -1361,7 +1363,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     if constexpr (sizeof(AT) == 2) {
       // pair i holds f elements 2i and 2i + 1 of the [B][F] rows, already in the staged type
       static_assert(__is_same(LT, AT), "16-bit activations are staged in their own type");
-      if (!poll_range(c, a, a.f, B * F / 2, t_f, st, [&](int i, float v) {
+      if (!poll_range<kPollWide>(c, a, a.f, B * F / 2, t_f, st, [&](int i, float v) {
             reinterpret_cast<uint32_t*>(act)[i] = __builtin_bit_cast(uint32_t, v);
           }))
         return;
