@@ -123,6 +123,13 @@ template <typename T> __device__ __forceinline__ float dot8(u32x4 w, u32x4 a, fl
 template <> __device__ __forceinline__ float dot8<half_t>(u32x4 w, u32x4 a, float acc) { return dot8_f16(w, a, acc); }
 template <> __device__ __forceinline__ float dot8<bf16_t>(u32x4 w, u32x4 a, float acc) { return dot8_bf16(w, a, acc); }
 
+// An LDS address for the direct-to-LDS buffer loads (the generic pointer of a __shared__ object
+// carries its LDS offset in the low 32 bits).
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void* lds_ptr(const void* p) {
+  return reinterpret_cast<lds_void*>(reinterpret_cast<uintptr_t>(p));
+}
+
 // int8 -> fp16, exactly: with the byte offset to unsigned u = q + 128, the fp16 bit pattern
 // 0x6400 | u encodes 1024 + u (in [1024, 2048) the fp16 spacing is 1), so subtracting
 // 1152 = 1024 + 128 leaves q exactly. Two bytes of `w` (selected by `hi`) become one half2.

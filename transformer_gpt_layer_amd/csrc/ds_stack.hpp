@@ -83,6 +83,7 @@ struct StackLds {
   uint32_t lens;    // every layer's cache lengths at launch, 4 per layer (constant during the launch)
   uint32_t res;     // this workgroup's rows of x2, then of the layer output (fp32, res_n each)
   uint32_t res_n;
+  uint32_t lnp;     // LayerNorm gamma and beta, prefetched: LN1 (or the LM head's) area, then LN2's
   uint32_t total;
 };
 
@@ -112,7 +113,8 @@ __host__ __device__ inline StackLds stack_lds_layout(int wsize, int bm, int H, i
   L.lens = stack_align(L.layers + (uint32_t)n_layers * (uint32_t)sizeof(StackLayer));
   L.res = stack_align(L.lens + (uint32_t)n_layers * 4u * 4u);
   L.res_n = (uint32_t)rows_per_wg * (uint32_t)bm;
-  L.total = stack_align(L.res + 2u * L.res_n * 4u);
+  L.lnp = stack_align(L.res + 2u * L.res_n * 4u);
+  L.total = stack_align(L.lnp + 2u * 2u * (uint32_t)H * lt);
   return L;
 }
 

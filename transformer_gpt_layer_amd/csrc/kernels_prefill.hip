@@ -39,10 +39,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ lds_void* lds_ptr(const void* p) {
-  return reinterpret_cast<lds_void*>(reinterpret_cast<uintptr_t>(p));
-}
 
 // s_waitcnt vmcnt(n) for 0 <= n <= 15 (expcnt and lgkmcnt left unconstrained); larger n waits
 // for 15, which is stricter and therefore still correct.

@@ -546,38 +546,12 @@ __device__ __forceinline__ void worker(const StackArgs& a, Ctl& c, const typenam
 
 // ------------------------------------------------------------------ sync waves: staging
 // LayerNorm B rows (biased variance) into LDS as LT. gamma and beta (this layer's, in AT) are
-// loaded as 16-byte vectors first, so their latency hides under the rows' loads (fill() puts the
-// rows into `raw` as fp32); they land in LDS next to the rows. Then one reduction of the shifted
-// sums of all rows and the normalized rows.
+// already in LDS at gb (gamma, then beta: prefetched a phase earlier); fill() puts the rows into
+// `raw` as fp32. Then one reduction of the shifted sums of all rows and the normalized rows.
 template <typename LT, typename AT, int BM, typename Fill>
-__device__ __forceinline__ bool stage_ln(Ctl& c, const StackArgs& a, uint32_t& sb, int B, int K,
-                                         const AT* __restrict__ gam, const AT* __restrict__ beta, LT* act, float* raw,
-                                         AT* gb, int st, Fill fill) {
-  constexpr int VG = 16 / (int)sizeof(AT);
-  constexpr int kGB = 3;  // gamma/beta vectors per thread issued ahead of the rows (K <= 6144 at 16 bits)
-  const int ngv = K / VG;
-  const rsrc_t rg = make_rsrc(gam, (uint32_t)(K * sizeof(AT))), rb = make_rsrc(beta, (uint32_t)(K * sizeof(AT)));
-  u32x4 gv[kGB], bv[kGB];
-#pragma unroll
-  for (int u = 0; u < kGB; ++u) {
-    const int j = st + u * NT;
-    const uint32_t off = j < ngv ? (uint32_t)(j * 16) : kOutOfRange;
-    gv[u] = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
-    bv[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-  }
+__device__ __forceinline__ bool stage_ln(Ctl& c, const StackArgs& a, uint32_t& sb, int B, int K, LT* act, float* raw,
+                                         const AT* gb, int st, Fill fill) {
   if (!fill()) return false;
-#pragma unroll
-  for (int u = 0; u < kGB; ++u) {
-    const int j = st + u * NT;
-    if (j < ngv) {
-      *reinterpret_cast<u32x4*>(gb + j * VG) = gv[u];
-      *reinterpret_cast<u32x4*>(gb + K + j * VG) = bv[u];
-    }
-  }
-  for (int j = st + kGB * NT; j < ngv; j += NT) {  // rows longer than kGB*NT vectors
-    *reinterpret_cast<u32x4*>(gb + j * VG) = __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(j * 16), 0, 0);
-    *reinterpret_cast<u32x4*>(gb + K + j * VG) = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(j * 16), 0, 0);
-  }
   if (!sync_bar(c, a, sb, st)) return false;
   // sums of d = x - x[0] and d^2 per row: var = (sum d^2 - (sum d)^2 / K) / K; shifting by an
   // element of the row keeps the subtraction well conditioned
@@ -737,24 +711,24 @@ __device__ __forceinline__ void load_regs_plain(const void* in, int n, int st, f
 
 // LayerNorm (biased variance) of B rows of K elements held as pairs in registers, into act as LT;
 // the rows come from `plain` (the caller's input) when it is given, else from the tagged values at
-// `tagged`. gamma and beta of the thread's pairs are issued first and converted only when used.
+// `tagged`. gamma and beta are already in LDS at gb (gamma, then beta: prefetched a phase earlier);
+// their reads are issued before the rows' poll, whose latency covers them.
 template <typename LT, typename AT, int BM, int PU>
-__device__ __forceinline__ bool stage_ln_regs(Ctl& c, const StackArgs& a, uint32_t& sb, int B, int K,
-                                              const AT* __restrict__ gam, const AT* __restrict__ beta, LT* act,
-                                              int st, const void* plain, const uint2* tagged, uint32_t tag) {
+__device__ __forceinline__ bool stage_ln_regs(Ctl& c, const StackArgs& a, uint32_t& sb, int B, int K, const AT* gb,
+                                              LT* act, int st, const void* plain, const uint2* tagged, uint32_t tag) {
   const int n = B * K, nv = n >> 1;
-  const rsrc_t rg = make_rsrc(gam, (uint32_t)(K * sizeof(AT))), rb = make_rsrc(beta, (uint32_t)(K * sizeof(AT)));
+  // the thread's gamma and beta pairs (LDS reads, overlapping the rows' poll)
   u32x2 gw[PU], bw[PU];  // fp16: the pair in .x; fp32: the two values
 #pragma unroll
   for (int u = 0; u < PU; ++u) {
     const int j = st + u * NT;
-    const uint32_t off = j < nv ? (uint32_t)((2 * j % K) * sizeof(AT)) : kOutOfRange;
+    const int e = j < nv ? 2 * j % K : 0;
     if constexpr (sizeof(AT) == 2) {
-      gw[u].x = __builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0);
-      bw[u].x = __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0);
+      gw[u].x = *reinterpret_cast<const uint32_t*>(gb + e);
+      bw[u].x = *reinterpret_cast<const uint32_t*>(gb + K + e);
     } else {
-      gw[u] = __builtin_amdgcn_raw_buffer_load_b64(rg, off, 0, 0);
-      bw[u] = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
+      gw[u] = *reinterpret_cast<const u32x2*>(gb + e);
+      bw[u] = *reinterpret_cast<const u32x2*>(gb + K + e);
     }
   }
   float x[PU][2];
@@ -1153,6 +1127,24 @@ __device__ __forceinline__ bool attn_merge(Ctl& c, const StackArgs& a, uint32_t&
   return true;
 }
 
+// gamma and beta of a LayerNorm (K values of AT each) into LDS at dst (gamma, then beta) by
+// direct-to-LDS loads, 1 KB per wave instruction, so that no register waits for them: the phase
+// they are issued in hides their latency. K * sizeof(AT) is a whole number of KB (hidden is a
+// multiple of the 1 KB weight slice's element count).
+template <typename AT>
+__device__ __forceinline__ void prefetch_ln(const void* gam, const void* beta, int K, AT* dst, int st) {
+  const uint32_t bytes = (uint32_t)K * (uint32_t)sizeof(AT);
+  const int nkb = (int)(bytes >> 10);
+  const int wave = __builtin_amdgcn_readfirstlane(st >> 6), lane = st & 63;
+  const rsrc_t rg = make_rsrc(gam, bytes), rb = make_rsrc(beta, bytes);
+  unsigned char* d = reinterpret_cast<unsigned char*>(dst);
+  for (int k = wave; k < 2 * nkb; k += NS) {
+    const bool second = k >= nkb;
+    const uint32_t off = (uint32_t)((second ? k - nkb : k) * 1024 + lane * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rb : rg, lds_ptr(d + k * 1024), 16, off, 0, 0, 0);
+  }
+}
+
 // ------------------------------------------------------------------ sync waves: the phase loop
 template <typename WT, typename AT, int BM, int D, bool KV8>
 __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned char* smem, int g, int st_in,
@@ -1160,7 +1152,8 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
   typedef typename WTraits<WT>::LT LT;
   LT* act = reinterpret_cast<LT*>(smem);
   float* raw = reinterpret_cast<float*>(smem + a.lds.raw);
-  AT* gb = reinterpret_cast<AT*>(smem + a.lds.raw + (uint32_t)BM * a.H * 4u);  // LayerNorm gamma, then beta
+  AT* lnp1 = reinterpret_cast<AT*>(smem + a.lds.lnp);  // LN1's (or the LM head's) gamma, then beta
+  AT* lnp2 = lnp1 + 2 * a.H;                            // LN2's
   float* slots = reinterpret_cast<float*>(smem + a.lds.slots);
   half_t* scl = reinterpret_cast<half_t*>(smem + a.lds.scales);
   float* res_x2 = reinterpret_cast<float*>(smem + a.lds.res);        // this workgroup's x2 rows
@@ -1182,14 +1175,14 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
   u32x4 kr[AS::NIT], vr[AS::NIT];    // the past rows of the current attention item
   float ksc[AS::NIT], vsc[AS::NIT];  // and their row scales (an int8 cache)
 
-  // LayerNorm of the B rows of H into act, from `plain` (the caller's input) when given, else from
-  // the tagged values at `tagged`: in registers when the rows fit, else through LDS
-  auto layer_norm = [&](const void* gam, const void* beta, const void* plain, const uint2* tagged,
-                        uint32_t tag) __attribute__((always_inline)) -> bool {
+  // LayerNorm of the B rows of H into act with the gamma and beta prefetched at gb, from `plain` (the
+  // caller's input) when given, else from the tagged values at `tagged`: in registers when the rows
+  // fit, else through LDS
+  auto layer_norm = [&](const AT* gb, const void* plain, const uint2* tagged, uint32_t tag)
+                        __attribute__((always_inline)) -> bool {
     if (B * H <= 2 * NT * kLnPairs)
-      return stage_ln_regs<LT, AT, BM, kLnPairs>(c, a, sb, B, H, (const AT*)gam, (const AT*)beta, act, st, plain,
-                                                 tagged, tag);
-    return stage_ln<LT, AT, BM>(c, a, sb, B, H, (const AT*)gam, (const AT*)beta, act, raw, gb, st, [&]() {
+      return stage_ln_regs<LT, AT, BM, kLnPairs>(c, a, sb, B, H, gb, act, st, plain, tagged, tag);
+    return stage_ln<LT, AT, BM>(c, a, sb, B, H, act, raw, gb, st, [&]() {
       if (plain) {
         load_rows_plain<AT>(plain, B, H, raw, st);
         return true;
@@ -1222,10 +1215,16 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
   auto zero_rows = [&](int K) {  // activation rows past B
     for (int i = B * K + st; i < BM * K; i += NT) act[i] = (LT)0.f;
   };
-  // publish the staged activation of phase `seq`, then wait for every worker to finish it
-  auto hand_over = [&](uint32_t seq) -> bool {
+  // publish the staged activation of phase `seq`, request the phase's epilogue operands (`issue`:
+  // their loads queue behind the weight stream, which the sync waves wait out anyway), then wait for
+  // every worker to finish the phase
+  auto hand_over = [&](uint32_t seq, auto issue) -> bool {
+    // this wave's LayerNorm prefetch of the previous phase has landed in LDS before the barrier
+    // (its later loads, the staging polls, have already been waited for)
+    wait_vm_at_most<0>();
     if (!sync_bar(c, a, sb, st)) return false;
     if (st == 0) lds_st(&c.act_ready, seq + 1u);
+    issue();
     bool ok = spin_until(c, a, [&] {
       bool all = true;
 #pragma unroll
@@ -1236,6 +1235,10 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     return ok;
   };
 
+  prefetch_ln<AT>(reinterpret_cast<const StackLayer*>(smem + a.lds.layers)[0].ln1_g,
+                  reinterpret_cast<const StackLayer*>(smem + a.lds.layers)[0].ln1_b, H, lnp1, st);
+  wait_vm_at_most<0>();
+  if (!sync_bar(c, a, sb, st)) return;
   for (int l = 0; l < a.n_layers; ++l) {
     const StackLayer& L = reinterpret_cast<const StackLayer*>(smem + a.lds.layers)[l];
     const int32_t* lens = reinterpret_cast<const int32_t*>(smem + a.lds.lens) + l * 4;  // d_len[b] at launch
@@ -1252,14 +1255,18 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 
     // ---- region 1: LN1 + QKV + bias; q, k, v tagged; k, v also into the cache row d_len[b]
     fresh();
-    const uint32_t pre_q = pre_ld(L.b_qkv, q0, nq);
+    uint32_t pre_q = 0u;
     const int pre_pos = lens[st % B];
     if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nq);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_qkv, q0, nq, H, a.group, scl, st);
-    if (!layer_norm(L.ln1_g, L.ln1_b, l == 0 ? a.x : nullptr, a.ybuf, l == 0 ? 0u : stack_tag(launch, l - 1, TAG_Y)))
+    if (!layer_norm(lnp1, l == 0 ? a.x : nullptr, a.ybuf, l == 0 ? 0u : stack_tag(launch, l - 1, TAG_Y)))
       return;
-    if (!hand_over(seq0)) return;
+    if (!hand_over(seq0, [&] {
+          pre_q = pre_ld(L.b_qkv, q0, nq);
+          prefetch_ln<AT>(L.ln2_g, L.ln2_b, H, lnp2, st);  // LN2 reads it after the next hand-over
+        }))
+      return;
     {
       const rsrc_t rqo = make_rsrc(a.q, (uint32_t)(B * H * 8));
       const rsrc_t rkn = make_rsrc(a.knew, (uint32_t)(B * H * 8)), rvn = make_rsrc(a.vnew, (uint32_t)(B * H * 8));
@@ -1302,13 +1309,13 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 
     // ---- output projection + bias + residual: x2 = x + Wo ctx + bo
     fresh();
-    const uint32_t pre_o = pre_ld(L.b_o, o0, no);
+    uint32_t pre_o = 0u;
     if (!sync_bar(c, a, sb, st)) return;  // the attention scratch (same LDS) and the slots are free
     clear_slots(no);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_o, o0, no, H, a.group, scl, st);
     zero_rows(H);
     if (!poll_range(c, a, a.ctx, B * H, t_ctx, st, [&](int i, float v) { act[i] = (LT)v; })) return;
-    if (!hand_over(seq0 + 1u)) return;
+    if (!hand_over(seq0 + 1u, [&] { pre_o = pre_ld(L.b_o, o0, no); })) return;
     {
       const rsrc_t rx2 = make_rsrc(a.x2, (uint32_t)(B * H * 8));
       for (int t = st; t < no * B; t += NT) {
@@ -1323,15 +1330,24 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 
     // ---- region 3: LN2 + FF1 + bias + GeLU
     fresh();
-    // fp16: this thread's first pair of rows; otherwise its first row
-    const uint32_t pre_f0 = sizeof(AT) == 2 ? (st < (nf / 2) * B ? ldraw<AT>(L.b_ff1, f0 + 2 * (st / B)) : 0u)
-                                            : pre_ld(L.b_ff1, f0, nf);
-    const uint32_t pre_f1 = sizeof(AT) == 2 && st < (nf / 2) * B ? ldraw<AT>(L.b_ff1, f0 + 2 * (st / B) + 1) : 0u;
+    uint32_t pre_f0 = 0u, pre_f1 = 0u;
     if (!sync_bar(c, a, sb, st)) return;  // the previous epilogue's slot reads are done
     clear_slots(nf);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff1, f0, nf, H, a.group_mlp, scl, st);
-    if (!layer_norm(L.ln2_g, L.ln2_b, nullptr, a.x2, t_x2)) return;
-    if (!hand_over(seq0 + 2u)) return;
+    if (!layer_norm(lnp2, nullptr, a.x2, t_x2)) return;
+    if (!hand_over(seq0 + 2u, [&] {
+          // the next layer's LN1 (or the LM head's final LayerNorm) reads it after the next hand-over
+          if (!last)
+            prefetch_ln<AT>(reinterpret_cast<const StackLayer*>(smem + a.lds.layers)[l + 1].ln1_g,
+                            reinterpret_cast<const StackLayer*>(smem + a.lds.layers)[l + 1].ln1_b, H, lnp1, st);
+          else if (a.head)
+            prefetch_ln<AT>(a.head_g, a.head_b, H, lnp1, st);
+          // fp16: this thread's first pair of rows; otherwise its first row
+          pre_f0 = sizeof(AT) == 2 ? (st < (nf / 2) * B ? ldraw<AT>(L.b_ff1, f0 + 2 * (st / B)) : 0u)
+                                   : pre_ld(L.b_ff1, f0, nf);
+          pre_f1 = sizeof(AT) == 2 && st < (nf / 2) * B ? ldraw<AT>(L.b_ff1, f0 + 2 * (st / B) + 1) : 0u;
+        }))
+      return;
     {
       const rsrc_t rf = make_rsrc(a.f, (uint32_t)(B * F * 8));
       if constexpr (sizeof(AT) == 2) {
@@ -1355,7 +1371,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
 
     // ---- region 4: FF2 + bias + residual: y = x2 + W2 f + b2
     fresh();
-    const uint32_t pre_y = pre_ld(L.b_ff2, y0, ny);
+    uint32_t pre_y = 0u;
     if (!sync_bar(c, a, sb, st)) return;  // the LayerNorm rows (same LDS) and the slots are free
     clear_slots(ny);
     if constexpr (sizeof(WT) == 1) stage_scales(L.s_ff2, y0, ny, F, a.group_mlp, scl, st);
@@ -1370,7 +1386,7 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     } else if (!poll_range(c, a, a.f, B * F, t_f, st, [&](int i, float v) { act[i] = (LT)v; })) {
       return;
     }
-    if (!hand_over(seq0 + 3u)) return;
+    if (!hand_over(seq0 + 3u, [&] { pre_y = pre_ld(L.b_ff2, y0, ny); })) return;
     {
       const rsrc_t ryt = make_rsrc(a.ybuf, (uint32_t)(B * H * 8));
       const rsrc_t ry = make_rsrc(a.y, (uint32_t)(B * H * sizeof(AT)));
@@ -1395,8 +1411,8 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     clear_slots(nv);
     if constexpr (sizeof(WT) == 1) stage_scales(a.head_s, v0, nv, H, a.group, scl, st);
     const uint32_t t_last = stack_tag(launch, a.n_layers - 1, TAG_Y);
-    if (!layer_norm(a.head_g, a.head_b, nullptr, a.ybuf, t_last)) return;
-    if (!hand_over(4u * (uint32_t)a.n_layers)) return;
+    if (!layer_norm(lnp1, nullptr, a.ybuf, t_last)) return;
+    if (!hand_over(4u * (uint32_t)a.n_layers, [] {})) return;
     // each logit as a 64-bit key that orders like (value, -index): the order-preserving bits of the
     // float above the inverted row index, so the largest key is the largest logit at its smallest
     // index (both zeros count as +0)
