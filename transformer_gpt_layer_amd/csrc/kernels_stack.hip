@@ -1294,7 +1294,9 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
     }
 
     // ---- region 2: attention over the cache; first every partial of this workgroup, then the
-    // merges it owns (chunk 0 of a head), so that no merge waits on a partial queued behind it
+    // merges it owns, so that no merge waits on a partial queued behind it. Items go to workgroups
+    // in order (workgroup g takes items g, g + G, ...) and merges from the last workgroup down, so
+    // that the merges land on the workgroups with the fewest items (or none).
     fresh();
     for (int item = g; item < nitems; item += G) {
       const AttnItem it = attn_item(a, lens, nvmax, item);
@@ -1302,10 +1304,8 @@ __device__ __forceinline__ void sync_side(const StackArgs& a, Ctl& c, unsigned c
       attn_load<KT, D>(a, L, lens[it.b], it, st, kr, vr, ksc, vsc);
       if (!attn_partial<KT, D>(c, a, sb, L, lens[it.b], it, t_q, t_part, s_acc, st, kr, vr, ksc, vsc)) return;
     }
-    for (int item = g; item < nitems; item += G) {
-      const AttnItem it = attn_item(a, lens, nvmax, item);
-      if (it.valid && it.cc == 0 && !attn_merge<AT, D>(c, a, sb, lens, it.b, it.j, t_part, t_ctx, s_part, st)) return;
-    }
+    for (int m = G - 1 - g; m < B * a.nh; m += G)
+      if (!attn_merge<AT, D>(c, a, sb, lens, m / a.nh, m % a.nh, t_part, t_ctx, s_part, st)) return;
 
     // ---- output projection + bias + residual: x2 = x + Wo ctx + bo
     fresh();
