@@ -87,6 +87,14 @@ CASES = {
                              act_dtype="f16", group=64, batch=1, past=33, cfg_id=219, **AFFINE), 2, False),
     "f32-d128-b1-L2-g5": (_wl("c1", hidden=1280, heads=10, head_dim=128, ffn=2560, weight_dtype="f32",
                               act_dtype="f32", batch=1, past=20, cfg_id=220, **AFFINE), 2, True),
+    # more attention items than workgroups (several per workgroup): each later item's rows arrive
+    # through the LDS prefetch; fp16 at head_dim 128 over two sequences, bf16 at head_dim 64
+    "f16-d128-b2-L2-long": (_wl("c1", hidden=2560, heads=20, head_dim=128, ffn=5120, weight_dtype="f16",
+                                act_dtype="f16", batch=2, past=900, cfg_id=227, **AFFINE), 2, False),
+    "bf16-d64-b1-L2-long": (_wl("c1", hidden=1024, heads=16, head_dim=64, ffn=2048, weight_dtype="bf16",
+                                act_dtype="bf16", batch=1, past=1100, cfg_id=228, **AFFINE), 2, True),
+    "i8-d128-b1-L2-long": (_wl("c1", hidden=5120, heads=40, head_dim=128, ffn=5120, weight_dtype="i8",
+                               act_dtype="f16", group=64, batch=1, past=700, cfg_id=229, **AFFINE), 2, False),
 }
 
 
