@@ -1,6 +1,6 @@
 """Decode throughput of the fused GPT-layer stack on one MI355X, with nested records for the other
 workloads of the metric (batch 8 fp16 and int8, int8 batch 1, the generation step with the LM head,
-and prefill).
+the headline step in bf16 and with an int8 KV cache, prefill, and the MoE expert FF).
 
 One decode step = one new token for every sequence of the batch through all L layers of the stack
 (LN1+QKV, attention over the KV cache, output projection, LN2+FF1+GeLU, FF2), starting from the
@@ -107,14 +107,22 @@ def _sizes(wl):
     return a, wbytes
 
 
+def kv_row_bytes(wl) -> int:
+    """Bytes of one cached position's K (or V) over all heads: the activation type, or an int8 cache's
+    codes with one fp16 scale per head."""
+    a, _ = _sizes(wl)
+    return wl.hidden + 2 * wl.heads if wl.extra.get("kv_dtype") == "int8" else wl.hidden * a
+
+
 def part_bytes(wl) -> dict:
     """Bytes each kernel of one decode layer step must move at least once: its weights (and scales),
     biases and LayerNorm vectors, the past K/V rows it reads, the new K/V rows it writes, x read by
     the first and y written by the last. Intermediates between kernels are not counted."""
     H, F, B, P, T = wl.hidden, wl.ffn, wl.batch, wl.past, wl.seq
     a, wb = _sizes(wl)
-    return {"ln1": B * T * H * a + 2 * H * a, "qkv": wb(3 * H, H) + 3 * H * a + 2 * B * T * H * a,
-            "attn": 2 * B * P * H * a, "o": wb(H, H) + H * a, "ln2": 2 * H * a, "ff1": wb(F, H) + F * a,
+    kr = kv_row_bytes(wl)
+    return {"ln1": B * T * H * a + 2 * H * a, "qkv": wb(3 * H, H) + 3 * H * a + 2 * B * T * kr,
+            "attn": 2 * B * P * kr, "o": wb(H, H) + H * a, "ln2": 2 * H * a, "ff1": wb(F, H) + F * a,
             "ff2": wb(H, F) + H * a + B * T * H * a, "len": 0}
 
 
@@ -124,7 +132,8 @@ def algorithmic_bytes_per_layer(wl) -> dict:
     a, wb = _sizes(wl)
     weights = wb(3 * H, H) + wb(H, H) + wb(F, H) + wb(H, F)
     small = (3 * H + H + F + H + 4 * H) * a
-    kv_read, kv_write, xy = 2 * B * P * H * a, 2 * B * T * H * a, 2 * B * T * H * a
+    kr = kv_row_bytes(wl)
+    kv_read, kv_write, xy = 2 * B * P * kr, 2 * B * T * kr, 2 * B * T * H * a
     total = weights + small + kv_read + kv_write + xy
     assert total == sum(part_bytes(wl).values())
     return {"weights": weights, "small": small, "kv_read": kv_read, "kv_write": kv_write, "xy": xy, "total": total}
@@ -152,10 +161,12 @@ def prefill_flops(wl) -> dict:
 def build_stack(wl, torch, tg, syn, layers):
     """Device weights and caches (P seeded rows each) for every layer, one [L, B] length tensor."""
     dev = "cuda"
-    act = torch.float32 if wl.act_dtype == "f32" else torch.float16
+    act = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.act_dtype]
+    kv8 = wl.extra.get("kv_dtype") == "int8"
     cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
-                         dtype={"f32": "fp32", "f16": "fp16", "i8": "int8"}[wl.weight_dtype],
-                         quant_group=wl.group if wl.weight_dtype == "i8" else None)
+                         dtype={"f32": "fp32", "f16": "fp16", "i8": "int8", "bf16": "bf16"}[wl.weight_dtype],
+                         quant_group=wl.group if wl.weight_dtype == "i8" else None,
+                         **({"kv_dtype": "int8"} if kv8 else {}))
     stack, kvs = [], []
     lens = torch.zeros((layers, wl.batch), dtype=torch.int32, device=dev)
     for l in range(layers):
@@ -169,7 +180,7 @@ def build_stack(wl, torch, tg, syn, layers):
                 gw[name] = t.to(act).contiguous()
         del w32
         layer = tg.Layer(cfg, gw)
-        kv = tg.KVCache(wl.batch, wl.heads, wl.capacity, wl.head_dim, act, dev, track_host=False)
+        kv = tg.KVCache(wl.batch, wl.heads, wl.capacity, wl.head_dim, torch.int8 if kv8 else act, dev, track_host=False)
         kv.d_len = lens[l]  # one [L, B] tensor so one fill resets every layer
         if wl.past:
             kp, vp = syn.past_kv_f32(wl, l, dev)
@@ -376,7 +387,9 @@ def decode_record(args, wl, torch, tg, syn, layers, mode="auto", cpu_s=0.0, voca
     per = algorithmic_bytes_per_layer(wl)
     step_bytes = per["total"] * layers
     use_stack = mode == "stack" or (mode == "auto" and wl.batch <= 4)
-    dtype = {"f32": "f32", "f16": "f16", "i8": "i8w-f16"}[wl.weight_dtype]
+    dtype = {"f32": "f32", "f16": "f16", "i8": "i8w-f16", "bf16": "bf16"}[wl.weight_dtype]
+    if wl.extra.get("kv_dtype") == "int8":
+        dtype += "-kv8"
     reset = lambda: lens.fill_(wl.past)
     extra = {}
     if use_stack:
@@ -571,10 +584,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle sample per leg (one thread, all threads) for the headline (0 disables)")
     ap.add_argument("--record-cpu-seconds", type=float, default=4.0, help="the same for each nested record")
-    ap.add_argument("--records", default="c2gen,c3,c4b8,c4b1,c5,moe,moe1",
+    ap.add_argument("--records", default="c2gen,c2bf16,c2kv8,c3,c4b8,c4b1,c5,moe,moe1",
                     help="nested records after the c2 headline (comma list; empty for none): c2gen (the "
-                         "generation step with the LM head), c3, c4b8, c4b1, c5, moe (the MoE expert FF "
-                         "of the 1.3B + MoE-128 model, 8 tokens), moe1 (the same, 1 token)")
+                         "generation step with the LM head), c2bf16 (bf16 weights and activations), c2kv8 "
+                         "(an int8 KV cache), c3, c4b8, c4b1, c5, moe (the MoE expert FF of the 1.3B + "
+                         "MoE-128 model, 8 tokens), moe1 (the same, 1 token)")
     ap.add_argument("--mode", choices=["auto", "stack", "layers"], default="auto",
                     help="stack: one persistent launch per step; layers: the per-layer kernels")
     ap.add_argument("--no-read-probe", dest="read_probe", action="store_false",
@@ -625,7 +639,9 @@ def main():
         elif syn.WORKLOADS[name].seq != 1:
             rec = prefill_record(args, syn.WORKLOADS[name], torch, tg, syn, syn.WORKLOADS[name].layers, cs)
         else:
-            rec = decode_record(args, syn.WORKLOADS[name], torch, tg, syn, syn.WORKLOADS[name].layers, "auto", cs)
+            # the C2 precision variants carry no CPU baseline of their own (the headline's covers C2)
+            cs_rec = 0.0 if name in ("c2bf16", "c2kv8") else cs
+            rec = decode_record(args, syn.WORKLOADS[name], torch, tg, syn, syn.WORKLOADS[name].layers, "auto", cs_rec)
         result["records"][name] = rec
         _free(torch)
     print(json.dumps(result))

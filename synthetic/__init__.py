@@ -72,6 +72,11 @@ WORKLOADS = {
     "c4b8": Workload("c4-13b-i8g64-b8-p1024", 4, 5120, 40, 128, 20480, 40, "i8", "f16", 8, 1024, group=64),
     # prefill on the GPT-Neo-2.7B shapes: batch 4 x 512 prompt rows, causal
     "c5": Workload("c5-gptneo2.7b-f16-prefill-b4s512", 5, 2560, 20, 128, 10240, 32, "f16", "f16", 4, 0, seq=512),
+    # the C2 decode step in the other precisions the config table names: bf16 weights and
+    # activations, and fp16 with an int8 KV cache (one int8 row and fp16 scale per cached head row)
+    "c2bf16": Workload("c2-gptneo2.7b-bf16-b1-p512", 6, 2560, 20, 128, 10240, 32, "bf16", "bf16", 1, 512),
+    "c2kv8": Workload("c2-gptneo2.7b-f16-kv8-b1-p512", 7, 2560, 20, 128, 10240, 32, "f16", "f16", 1, 512,
+                      extra={"kv_dtype": "int8"}),
 }
 
 

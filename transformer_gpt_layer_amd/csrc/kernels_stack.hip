@@ -955,7 +955,9 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
     if (key == len && key < a.cap) {
       const rsrc_t rkn = make_rsrc(a.knew, (uint32_t)(a.B * H * 8)), rvn = make_rsrc(a.vnew, (uint32_t)(a.B * H * 8));
       if constexpr (sizeof(KT) == 1) {
-        // the key's LPK lanes hold its D values: amax over them, the row scale, the codes; K, then V
+        // the key's LPK lanes hold its D values: amax over them, the row scale (from amax / 127 in
+        // double, as the quantizer rounds it), the codes in fp32 (the projection's values are fp32,
+        // so a code differs from the double rule's only at a near-tie); K, then V
         const size_t row = ((size_t)b * a.nh + j) * a.cap + key;
         auto quantize = [&](rsrc_t src, void* cache, void* scales, u32x4& codes, float& scale) -> bool {
           float xn[EK];
@@ -965,16 +967,16 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
           for (int e = 0; e < EK; ++e) am = fmaxf(am, fabsf(xn[e]));
           am = group_max<LPK>(am);
           const uint16_t bits = f64_to_f16_bits_rne((double)am / 127.0);
-          const double sv = f16_bits_to_f64(bits);
+          const float sv = (float)f16_bits_to_f64(bits);
           uint32_t w[4];
 #pragma unroll
           for (int h = 0; h < 4; ++h) {
             w[h] = 0u;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) w[h] |= ((uint32_t)i8_code((double)xn[4 * h + q], sv) & 0xffu) << (8 * q);
+            for (int q = 0; q < 4; ++q) w[h] |= ((uint32_t)i8_code_f32(xn[4 * h + q], sv) & 0xffu) << (8 * q);
           }
           codes = u32x4{w[0], w[1], w[2], w[3]};
-          scale = (float)sv;
+          scale = sv;
           *reinterpret_cast<u32x4*>(static_cast<int8_t*>(cache) + row * D + e0) = codes;
           if (lane % LPK == 0) static_cast<uint16_t*>(scales)[row] = bits;
           return true;
