@@ -100,9 +100,10 @@ def copy_calibration(torch, gib: int = 1):
 def _sizes(wl):
     a = 4 if wl.act_dtype == "f32" else 2
 
-    def wbytes(n, k):
+    def wbytes(n, k, mlp=False):
         if wl.weight_dtype == "i8":
-            return n * k + (n * k // wl.group) * 2
+            g = wl.group_mlp if mlp and wl.group_mlp else wl.group
+            return n * k + (n * k // g) * 2
         return n * k * (4 if wl.weight_dtype == "f32" else 2)
     return a, wbytes
 
@@ -122,15 +123,15 @@ def part_bytes(wl) -> dict:
     a, wb = _sizes(wl)
     kr = kv_row_bytes(wl)
     return {"ln1": B * T * H * a + 2 * H * a, "qkv": wb(3 * H, H) + 3 * H * a + 2 * B * T * kr,
-            "attn": 2 * B * P * kr, "o": wb(H, H) + H * a, "ln2": 2 * H * a, "ff1": wb(F, H) + F * a,
-            "ff2": wb(H, F) + H * a + B * T * H * a, "len": 0}
+            "attn": 2 * B * P * kr, "o": wb(H, H) + H * a, "ln2": 2 * H * a, "ff1": wb(F, H, True) + F * a,
+            "ff2": wb(H, F, True) + H * a + B * T * H * a, "len": 0}
 
 
 def algorithmic_bytes_per_layer(wl) -> dict:
     """Bytes one layer step must move at least once (the sum over its kernels of part_bytes)."""
     H, F, B, P, T = wl.hidden, wl.ffn, wl.batch, wl.past, wl.seq
     a, wb = _sizes(wl)
-    weights = wb(3 * H, H) + wb(H, H) + wb(F, H) + wb(H, F)
+    weights = wb(3 * H, H) + wb(H, H) + wb(F, H, True) + wb(H, F, True)
     small = (3 * H + H + F + H + 4 * H) * a
     kr = kv_row_bytes(wl)
     kv_read, kv_write, xy = 2 * B * P * kr, 2 * B * T * kr, 2 * B * T * H * a
@@ -166,6 +167,7 @@ def build_stack(wl, torch, tg, syn, layers):
     cfg = tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn,
                          dtype={"f32": "fp32", "f16": "fp16", "i8": "int8", "bf16": "bf16"}[wl.weight_dtype],
                          quant_group=wl.group if wl.weight_dtype == "i8" else None,
+                         quant_group_mlp=wl.group_mlp if wl.weight_dtype == "i8" and wl.group_mlp else None,
                          **({"kv_dtype": "int8"} if kv8 else {}))
     stack, kvs = [], []
     lens = torch.zeros((layers, wl.batch), dtype=torch.int32, device=dev)
@@ -174,7 +176,8 @@ def build_stack(wl, torch, tg, syn, layers):
         gw = {}
         for name, t in w32.items():
             if name.startswith("w_") and wl.weight_dtype == "i8":
-                q, s = tg.quantize_i8(t.contiguous(), wl.group)
+                g = wl.group_mlp if wl.group_mlp and name in ("w_ff1", "w_ff2") else wl.group
+                q, s = tg.quantize_i8(t.contiguous(), g)
                 gw[name], gw["s" + name[1:]] = q, s
             else:
                 gw[name] = t.to(act).contiguous()
@@ -390,6 +393,8 @@ def decode_record(args, wl, torch, tg, syn, layers, mode="auto", cpu_s=0.0, voca
     dtype = {"f32": "f32", "f16": "f16", "i8": "i8w-f16", "bf16": "bf16"}[wl.weight_dtype]
     if wl.extra.get("kv_dtype") == "int8":
         dtype += "-kv8"
+    if wl.weight_dtype == "i8" and wl.group_mlp:
+        dtype += f"-mlpg{wl.group_mlp}"
     reset = lambda: lens.fill_(wl.past)
     extra = {}
     if use_stack:
@@ -584,10 +589,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle sample per leg (one thread, all threads) for the headline (0 disables)")
     ap.add_argument("--record-cpu-seconds", type=float, default=4.0, help="the same for each nested record")
-    ap.add_argument("--records", default="c2gen,c2bf16,c2kv8,c3,c4b8,c4b1,c5,moe,moe1",
+    ap.add_argument("--records", default="c2gen,c2bf16,c2kv8,c3,c4b8,c4b1,c4b1m32,c5,moe,moe1",
                     help="nested records after the c2 headline (comma list; empty for none): c2gen (the "
                          "generation step with the LM head), c2bf16 (bf16 weights and activations), c2kv8 "
-                         "(an int8 KV cache), c3, c4b8, c4b1, c5, moe (the MoE expert FF of the 1.3B + "
+                         "(an int8 KV cache), c3, c4b8, c4b1, c4b1m32 (int8 with groups of 32 in the MLP matrices), c5, moe (the MoE expert FF of the 1.3B + "
                          "MoE-128 model, 8 tokens), moe1 (the same, 1 token)")
     ap.add_argument("--mode", choices=["auto", "stack", "layers"], default="auto",
                     help="stack: one persistent launch per step; layers: the per-layer kernels")
@@ -640,7 +645,7 @@ def main():
             rec = prefill_record(args, syn.WORKLOADS[name], torch, tg, syn, syn.WORKLOADS[name].layers, cs)
         else:
             # the C2 precision variants carry no CPU baseline of their own (the headline's covers C2)
-            cs_rec = 0.0 if name in ("c2bf16", "c2kv8") else cs
+            cs_rec = 0.0 if name in ("c2bf16", "c2kv8", "c4b1m32") else cs
             rec = decode_record(args, syn.WORKLOADS[name], torch, tg, syn, syn.WORKLOADS[name].layers, "auto", cs_rec)
         result["records"][name] = rec
         _free(torch)

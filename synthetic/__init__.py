@@ -70,6 +70,9 @@ WORKLOADS = {
     # 13B shapes, int8 weights (group 64, fp16 scales), fp16 activations, batch 1 and 8
     "c4b1": Workload("c4-13b-i8g64-b1-p1024", 4, 5120, 40, 128, 20480, 40, "i8", "f16", 1, 1024, group=64),
     "c4b8": Workload("c4-13b-i8g64-b8-p1024", 4, 5120, 40, 128, 20480, 40, "i8", "f16", 8, 1024, group=64),
+    # mlp_extra_grouping: twice the groups (size 32) in the two MLP matrices
+    "c4b1m32": Workload("c4-13b-i8g64-mlp32-b1-p1024", 8, 5120, 40, 128, 20480, 40, "i8", "f16", 1, 1024, group=64,
+                        group_mlp=32),
     # prefill on the GPT-Neo-2.7B shapes: batch 4 x 512 prompt rows, causal
     "c5": Workload("c5-gptneo2.7b-f16-prefill-b4s512", 5, 2560, 20, 128, 10240, 32, "f16", "f16", 4, 0, seq=512),
     # the C2 decode step in the other precisions the config table names: bf16 weights and

@@ -72,6 +72,20 @@ __host__ __device__ inline int stack_tile_rows(int N, int G, bool even) {
   return even ? (r + 1) & ~1 : r;
 }
 
+// int8 group scales (fp16) the workgroup stages for its largest phase: its row tile of each
+// projection (and of the LM head's V rows) times the scales per row of that matrix.
+__host__ __device__ inline uint32_t stack_scale_halves(int H, int F, int V, int G, int group, int group_mlp) {
+  const uint32_t q = (uint32_t)stack_tile_rows(3 * H, G, false) * (uint32_t)(H / group);
+  const uint32_t o = (uint32_t)stack_tile_rows(H, G, false) * (uint32_t)(H / group);
+  const uint32_t f1 = (uint32_t)stack_tile_rows(F, G, true) * (uint32_t)(H / group_mlp);
+  const uint32_t f2 = (uint32_t)stack_tile_rows(H, G, false) * (uint32_t)(F / group_mlp);
+  const uint32_t hd = V > 0 ? (uint32_t)stack_tile_rows(V, G, false) * (uint32_t)(H / group) : 0u;
+  uint32_t m = q > o ? q : o;
+  m = m > f1 ? m : f1;
+  m = m > f2 ? m : f2;
+  return m > hd ? m : hd;
+}
+
 // Dynamic LDS layout of one workgroup (byte offsets; the activation rows start at 0). Identical on
 // the host and the device.
 struct StackLds {
@@ -94,7 +108,7 @@ __host__ __device__ inline uint32_t stack_align(uint32_t v) { return (v + 255u) 
 // activation region also holds the attention scratch (per-wave partials, then the chunk partials
 // of the merge), which is never live at the same time as staged activations.
 __host__ __device__ inline StackLds stack_lds_layout(int wsize, int bm, int H, int F, int rows_per_wg, int nchunk,
-                                                     int D, int group, int n_layers) {
+                                                     int D, uint32_t scale_halves, int n_layers) {
   // the weight table holds 4 entries per layer and one for the LM head
   StackLds L{};
   const uint32_t lt = wsize == 4 ? 4u : 2u;
@@ -107,7 +121,7 @@ __host__ __device__ inline StackLds stack_lds_layout(int wsize, int bm, int H, i
   L.raw = (uint32_t)bm * (uint32_t)H * lt;
   L.slots = stack_align(region);
   L.scales = stack_align(L.slots + (uint32_t)rows_per_wg * kStackWorkers * bm * 4u);
-  const uint32_t sc = wsize == 1 ? (uint32_t)rows_per_wg * (kmax / (uint32_t)group) * 2u : 0u;
+  const uint32_t sc = wsize == 1 ? scale_halves * 2u : 0u;
   L.wtab = stack_align(L.scales + sc);
   L.layers = stack_align(L.wtab + ((uint32_t)n_layers * 4u + 1u) * 8u);
   L.lens = stack_align(L.layers + (uint32_t)n_layers * (uint32_t)sizeof(StackLayer));

@@ -96,12 +96,14 @@ int slice_elems(int wdt) { return wdt == DS_F32 ? 256 : (wdt == DS_I8 ? 1024 : 5
 int weight_bytes(int wdt) { return wdt == DS_F32 ? 4 : (wdt == DS_I8 ? 1 : 2); }
 size_t act_bytes(int adt) { return adt == DS_F32 ? 4 : 2; }
 
-// The smallest int8 scale group among the stack's matrices (1 for other weight dtypes).
-int min_group(const ds_layer_desc& d) {
-  if (d.weight_dtype != DS_I8) return 1;
+// fp16 group scales the workgroup stages for its largest phase (int8 weights; 0 otherwise)
+uint32_t scale_halves(const ds_layer_desc& d, int V, int G) {
+  if (d.weight_dtype != DS_I8) return 0u;
   const int gm = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
-  return gm < d.quant_group ? gm : d.quant_group;
+  return ds::stack_scale_halves(d.hidden, d.ffn, V, G, d.quant_group, gm);
 }
+
+// The largest int8 scale group among the stack's matrices (1 for other weight dtypes).
 int max_group(const ds_layer_desc& d) {
   if (d.weight_dtype != DS_I8) return 1;
   const int gm = d.quant_group_mlp ? d.quant_group_mlp : d.quant_group;
@@ -235,7 +237,7 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
   int G = cus;  // one workgroup of kStackThreads per CU
   for (int iter = 0; e == hipSuccess && iter < 3; ++iter) {
     const ds::StackLds lay = ds::stack_lds_layout(wsz_i, bm, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->head.V, G),
-                                                  S->nchunk, d.head_dim, min_group(d), n_layers);
+                                                  S->nchunk, d.head_dim, scale_halves(d, S->head.V, G), n_layers);
     if (lay.total > (uint32_t)ds::kStackLdsMax - 4096u) {  // the static control block takes the rest
       delete S;
       return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode: %u bytes of LDS per workgroup needed", lay.total);
@@ -385,7 +387,7 @@ int stack_forward(ds_stack_t* S, const void* x, void* y, float* logits, int32_t*
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
   const int wsz_i = weight_bytes(d.weight_dtype);
   a.lds = ds::stack_lds_layout(wsz_i, batch <= 1 ? 1 : 4, d.hidden, d.ffn, ds::stack_rows_per_wg(d.hidden, d.ffn, S->head.V, S->G),
-                               S->nchunk, d.head_dim, min_group(d), S->n_layers);
+                               S->nchunk, d.head_dim, scale_halves(d, S->head.V, S->G), S->n_layers);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (int rc = prepare_workspace(*S, ws, W.total, st)) return rc;
   if (hipError_t e = ds::launch_stack_decode(wdt, adt, a, st))
