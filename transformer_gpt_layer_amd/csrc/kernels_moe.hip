@@ -313,8 +313,17 @@ __device__ __forceinline__ void ffn_tiles(const MoeArgs& a, const Route& RT, int
           if (lane != r * BM + b || r >= nrows || b >= nb) continue;
           const int n = row0 + r, p = RT.pairs[first + c0 + b];
           const float z = acc[r][b] + ldm<AT>(bias, boff + n);
-          if (FF1) reinterpret_cast<LT*>(a.f)[(size_t)p * F + n] = (LT)gelu(z, a.gelu_tanh != 0);
-          else a.z[(size_t)p * H + n] = z;
+          if (FF1) {
+            reinterpret_cast<LT*>(a.f)[(size_t)p * F + n] = (LT)gelu(z, a.gelu_tanh != 0);
+          } else if (a.KS == 1) {
+            // one slot per token (top-1 without the residual MLP): the combination is this slot
+            // alone, written here as the combination kernel would (pair p is token p)
+            float v = ldm<AT>(a.x2, (size_t)p * H + n);
+            v += a.wgt[p] * z;
+            reinterpret_cast<AT*>(a.y)[(size_t)p * H + n] = from_f32<AT>(v);
+          } else {
+            a.z[(size_t)p * H + n] = z;
+          }
         }
     }
   }
@@ -405,8 +414,10 @@ hipError_t launch_moe_t(const MoeArgs& a, hipStream_t st, MoeKernelHook hook, vo
   if (hook) hook(hook_ctx, st, 2);
   if (hipError_t e = launch_ffn<WT, AT, false>(a, st)) return e;
   if (hook) hook(hook_ctx, st, 3);
-  hipLaunchKernelGGL((moe_combine_kernel<AT>), dim3(a.T), dim3(256), 0, st, a);
-  if (hipError_t e = hipGetLastError()) return e;
+  if (a.KS > 1) {  // with one slot per token FF2 wrote y itself
+    hipLaunchKernelGGL((moe_combine_kernel<AT>), dim3(a.T), dim3(256), 0, st, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
   if (hook) hook(hook_ctx, st, 4);
   return hipSuccess;
 }
