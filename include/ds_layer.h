@@ -363,8 +363,7 @@ int ds_moe_forward(const ds_moe_t* moe, const void* x2, void* y, int32_t tokens,
 /* The same step with a HIP event after each of the five launches; ms[i] (host, max entries)
  * receives their durations in launch order (0 gate, 1 routing, 2 FF1, 3 FF2, 4 combination).
  * With one slot per token (top_k 1, standard type) FF2 writes y itself and entry 4 is the empty
- * interval after it. */
- * Synchronizes the stream. Returns the number of launches or a negative status. */
+ * interval after it. Synchronizes the stream. Returns the number of launches or a negative status. */
 int ds_moe_time_kernels(const ds_moe_t* moe, const void* x2, void* y, int32_t tokens, void* workspace,
                         size_t workspace_bytes, void* stream, float* ms, int32_t max);
 
