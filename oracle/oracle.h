@@ -16,7 +16,7 @@
  *         row triangular_masking (default True: the attention score mask type); the MoE sections:
  *         a number of experts per MoE layer, MoE types 'standard' and 'residual' (PR-MoE).
  *
- * Where the pages are silent the oracle takes these readings (each is listed in the design doc):
+ * Where the pages are silent the oracle takes these readings:
  *   LayerNorm uses the biased variance and eps = 1e-5 unless the caller passes another eps;
  *   GeLU is the exact erf form u*Phi(u) unless gelu_tanh is set; the attention scale is 1/sqrt(d);
  *   Q, K, V are rows [0,H), [H,2H), [2H,3H) of the fused projection, head j owning [j*d,(j+1)*d);
@@ -88,7 +88,7 @@ void ora_lm_head(const double* y, int H, const double* g, const double* b, doubl
 int  ora_argmax(const double* v, int n);
 
 /* ---- the MoE expert FF ([MP]: num_experts per layer, type standard | residual) ----
- * The pages name the experts and the two types but not the gate. Readings (listed in the design doc):
+ * The pages name the experts and the two types but not the gate. Readings:
  * h = LN(x2; ln_g, ln_b); gate logits = W_gate h (no bias); p = softmax over the E experts; the
  * top_k experts are the k largest p, taken one at a time, the smallest index first among equal
  * values; an expert is the dense FF, FF_e(h) = W2_e GeLU(W1_e h + b1_e) + b2_e; the combine
