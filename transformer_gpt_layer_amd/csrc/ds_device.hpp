@@ -206,14 +206,6 @@ __device__ __forceinline__ int32_t i8_code(double x, double sv) {
   return (int32_t)fmin(127.0, fmax(-127.0, c));
 }
 
-// The same rule in fp32 (a correctly rounded division, then round-half-even): for fp32 x the
-// quotient's rounding can only move the result where x / sv lies within an fp32 ulp of a
-// half-integer, so the code is the double rule's or one step from it at such a near-tie.
-__device__ __forceinline__ int32_t i8_code_f32(float x, float sv) {
-  const float c = sv == 0.f ? 0.f : rintf(x / sv);
-  return (int32_t)fminf(127.f, fmaxf(-127.f, c));
-}
-
 // ---------------------------------------------------------------- GeLU
 // u * Phi(u) = u/2 (1 + erf(u / sqrt 2)), or the tanh approximation
 // u/2 (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))); erf and tanh come from the ROCm device library.

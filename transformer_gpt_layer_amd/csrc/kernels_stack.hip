@@ -956,8 +956,11 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
       const rsrc_t rkn = make_rsrc(a.knew, (uint32_t)(a.B * H * 8)), rvn = make_rsrc(a.vnew, (uint32_t)(a.B * H * 8));
       if constexpr (sizeof(KT) == 1) {
         // the key's LPK lanes hold its D values: amax over them, the row scale (from amax / 127 in
-        // double, as the quantizer rounds it), the codes in fp32 (the projection's values are fp32,
-        // so a code differs from the double rule's only at a near-tie); K, then V
+        // double, as the quantizer rounds it), the codes as rint(x * (1 / scale)) in fp32: the
+        // product is within two fp32 ulps of x / scale, so a code differs from the double rule's
+        // only where x / scale lies that close to a half-integer (the projection's values are
+        // fp32 and differ from exact ones by more anyway); K, then V (polled one after the other:
+        // both rows' values at once would spill the sync waves' registers)
         const size_t row = ((size_t)b * a.nh + j) * a.cap + key;
         auto quantize = [&](rsrc_t src, void* cache, void* scales, u32x4& codes, float& scale) -> bool {
           float xn[EK];
@@ -968,12 +971,16 @@ __device__ __forceinline__ bool attn_partial(Ctl& c, const StackArgs& a, uint32_
           am = group_max<LPK>(am);
           const uint16_t bits = f64_to_f16_bits_rne((double)am / 127.0);
           const float sv = (float)f16_bits_to_f64(bits);
+          const float rs = sv == 0.f ? 0.f : 1.f / sv;
           uint32_t w[4];
 #pragma unroll
           for (int h = 0; h < 4; ++h) {
             w[h] = 0u;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) w[h] |= ((uint32_t)i8_code_f32(xn[4 * h + q], sv) & 0xffu) << (8 * q);
+            for (int q = 0; q < 4; ++q) {
+              const int32_t code = (int32_t)fminf(127.f, fmaxf(-127.f, rintf(xn[4 * h + q] * rs)));
+              w[h] |= ((uint32_t)code & 0xffu) << (8 * q);
+            }
           }
           codes = u32x4{w[0], w[1], w[2], w[3]};
           scale = sv;
