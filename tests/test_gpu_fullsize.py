@@ -3,7 +3,8 @@
 - GPT-Neo-2.7B shapes (hidden 2560, 20 heads, FF 10240, fp16, batch 1, 512 past rows): the whole
   32-layer persistent generation step with the final LayerNorm and the LM head over the GPT-Neo
   vocabulary (50257), every output element, every new cache row, the logits and the greedy token
-  checked against the oracle run layer after layer.
+  checked against the oracle run layer after layer; the same 32-layer decode step in bf16 and
+  with an int8 KV cache.
 - 13B shapes (hidden 5120, 40 heads, FF 20480, batch 8, 1024 past rows), fp16 and int8 (group 64):
   one full-size layer through the per-layer kernels the benchmark uses at batch 8, and the int8
   batch-1 layer through the persistent kernel. The kernels and their grids depend on the shapes,
@@ -26,16 +27,18 @@ from tests._common import TOL, rel_l2
 
 pytestmark = pytest.mark.gpu
 
-_DT = {"f16": "fp16", "i8": "int8", "f32": "fp32"}
+_DT = {"f16": "fp16", "i8": "int8", "f32": "fp32", "bf16": "bf16"}
+_ACT = {"f16": torch.float16, "f32": torch.float32, "bf16": torch.bfloat16}
 
 
 def _config(wl):
+    kv = {"kv_dtype": "int8"} if wl.extra.get("kv_dtype") == "int8" else {}
     return tg.make_config(hidden=wl.hidden, heads=wl.heads, ffn=wl.ffn, dtype=_DT[wl.weight_dtype],
-                          quant_group=wl.group if wl.weight_dtype == "i8" else None)
+                          quant_group=wl.group if wl.weight_dtype == "i8" else None, **kv)
 
 
 def _gpu_layer(wl, layer, cfg):
-    act = torch.float16 if wl.act_dtype == "f16" else torch.float32
+    act = _ACT[wl.act_dtype]
     gw = {}
     for name, t in syn.layer_weights_f32(wl, layer, "cuda").items():
         if name.startswith("w_") and wl.weight_dtype == "i8":
@@ -59,8 +62,11 @@ def _oracle_weights(gl, wl):
     return w
 
 
-def _filled_cache(wl, layer, gl, act):
-    kv = tg.KVCache(wl.batch, wl.heads, wl.capacity, wl.head_dim, act, "cuda")
+def _filled_cache(wl, layer, gl, cache_dtype):
+    """The cache (of cache_dtype: the activation type or int8) holding the workload's past rows,
+    appended in the activation type (an int8 cache quantizes them on append)."""
+    act = _ACT[wl.act_dtype]
+    kv = tg.KVCache(wl.batch, wl.heads, wl.capacity, wl.head_dim, cache_dtype, "cuda")
     if wl.past:
         kp, vp = syn.past_kv_f32(wl, layer, "cuda")
         rows = lambda t: t.permute(0, 2, 1, 3).reshape(wl.batch, wl.past, wl.hidden).to(act).contiguous()
@@ -69,10 +75,15 @@ def _filled_cache(wl, layer, gl, act):
 
 
 def _oracle_cache(kv, past):
+    """float64 copies of the cache's first `past` rows (an int8 cache: codes x row scales, exact)."""
     ok = np.zeros(tuple(kv.k.shape))
     ov = np.zeros_like(ok)
-    ok[:, :, :past] = kv.k[:, :, :past].double().cpu().numpy()
-    ov[:, :, :past] = kv.v[:, :, :past].double().cpu().numpy()
+    if kv.k_scale is not None:
+        ok[:, :, :past] = kv.k[:, :, :past].double().cpu().numpy() * kv.k_scale[:, :, :past, None].double().cpu().numpy()
+        ov[:, :, :past] = kv.v[:, :, :past].double().cpu().numpy() * kv.v_scale[:, :, :past, None].double().cpu().numpy()
+    else:
+        ok[:, :, :past] = kv.k[:, :, :past].double().cpu().numpy()
+        ov[:, :, :past] = kv.v[:, :, :past].double().cpu().numpy()
     return ok, ov
 
 
@@ -122,6 +133,44 @@ def test_c2_full_stack_32_layers_matches_oracle():
         assert int(tokens[0]) == oracle.argmax(lo)
     else:
         assert lo[int(tokens[0])] >= lo.max() - margin
+
+
+@pytest.mark.parametrize("name", ["c2bf16", "c2kv8"])
+def test_c2_full_stack_precision_variants_match_oracle(name):
+    """The 32-layer GPT-Neo-2.7B decode step in bf16 and with an int8 KV cache, as the benchmark's
+    records run it: every output element and every new cache row against the oracle run layer after
+    layer (an int8 cache: the oracle quantizes the new rows by its own rule, and the GPU's
+    dequantized rows are compared with them)."""
+    wl = syn.WORKLOADS[name]
+    kv8 = wl.extra.get("kv_dtype") == "int8"
+    print(f"[full size] {wl.name}: persistent decode, {wl.layers} layers", flush=True)
+    cfg = _config(wl)
+    act = _ACT[wl.act_dtype]
+    layers = [_gpu_layer(wl, l, cfg) for l in range(wl.layers)]
+    kvs = [_filled_cache(wl, l, layers[l], torch.int8 if kv8 else act) for l in range(wl.layers)]
+    past = [_oracle_cache(kv, wl.past) for kv in kvs]
+    st = tg.Stack(layers, kvs, max_batch=1)
+    x = syn.normal((1, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").to(act)
+    y = st.decode(x)
+    st.check()
+    st.close()
+    tol = TOL[wl.act_dtype]
+    desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn, kv_int8=kv8)
+    h = x.double().cpu().numpy()[:, None, :]
+    P = wl.past
+    worst = 0.0
+    for l in range(wl.layers):
+        ok, ov = past[l]
+        lens = np.full(1, P, dtype=np.int32)
+        h = oracle.layer_forward(desc, _oracle_weights(layers[l], wl), ok, ov, lens, h)
+        gk, gv = _oracle_cache(kvs[l], P + 1)
+        ek, ev = rel_l2(gk[:, :, P], ok[:, :, P]), rel_l2(gv[:, :, P], ov[:, :, P])
+        worst = max(worst, ek, ev)
+        assert ek <= tol and ev <= tol, (l, ek, ev)
+        assert kvs[l].lengths() == [P + 1]
+    err = rel_l2(y.double().cpu().numpy(), h[:, 0])
+    print(f"  32-layer output rel L2 {err:.3e}; new cache rows worst {worst:.3e}", flush=True)
+    assert err <= tol, err
 
 
 @pytest.mark.parametrize("name", ["c3", "c4b8", "c4b1"])
