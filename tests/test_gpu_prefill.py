@@ -1,5 +1,5 @@
-"""GPU parity of the MFMA (many-row) path against the oracle: fp16 layers with at least 16 rows
-per step run LayerNorm rows, the fused-epilogue GEMMs and flash attention on matrix cores.
+"""GPU parity of the MFMA (many-row) path against the oracle: fp16 and bf16 layers with at least 16
+rows per step run LayerNorm rows, the fused-epilogue GEMMs and flash attention on matrix cores.
 
 Shapes span several GEMM tiles (128 rows by 160/256/320 columns) with ragged row and column tails,
 several 64-key attention tiles, past rows that are not a multiple of 64, head_dim 64 and 128, and
@@ -45,7 +45,7 @@ def _prefill_case(wl, S, P0, **cfg_kw):
     cap = ((P0 + S + 1 + 63) // 64) * 64
     gl, ow = gpu_layer_and_oracle_weights(wl, 0, **cfg_kw)
     kv, ok, ov, lens = filled_caches(wl, 0, gl, past=P0, cap=cap)
-    x = syn.normal((wl.batch, S, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 7, "cuda").to(torch.float16)
+    x = syn.normal((wl.batch, S, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 7, "cuda").to(gl.cfg.torch_act_dtype)
     return wl, gl, ow, kv, ok, ov, lens, x
 
 
@@ -67,10 +67,11 @@ def _check_prefill(name, wl, S, P0, tanh):
     yd, xd = y.double().cpu().numpy(), x.double().cpu().numpy()
     err, err_d = rel_l2(yd, yo), rel_l2(yd - xd, yo - xd)
     print(f"  rel L2 {err:.3e}, of y - x {err_d:.3e}", flush=True)
-    assert err <= TOL["f16"] and err_d <= TOL["f16"], (err, err_d)
+    tol = TOL[wl.act_dtype]
+    assert err <= tol and err_d <= tol, (err, err_d)
     n = P0 + S
-    assert rel_l2(kv.k.double().cpu().numpy()[:, :, :n], ok[:, :, :n]) <= TOL["f16"]
-    assert rel_l2(kv.v.double().cpu().numpy()[:, :, :n], ov[:, :, :n]) <= TOL["f16"]
+    assert rel_l2(kv.k.double().cpu().numpy()[:, :, :n], ok[:, :, :n]) <= tol
+    assert rel_l2(kv.v.double().cpu().numpy()[:, :, :n], ov[:, :, :n]) <= tol
     assert kv.lengths() == [n] * wl.batch
 
 
@@ -154,3 +155,39 @@ def test_large_batch_decode_uses_mfma_path_and_matches_oracle():
     desc = oracle.Desc(wl.hidden, wl.heads, wl.head_dim, wl.ffn)
     yo = oracle.layer_forward(desc, ow, ok, ov, lens, x.double().cpu().numpy()[:, None, :])[:, 0]
     assert rel_l2(y.double().cpu().numpy(), yo) <= TOL["f16"]
+
+
+# bf16 weights and activations on the same kernels (the 16-bit type is a template parameter of the
+# LayerNorm, GEMM and attention kernels): ragged tiles, head_dim 64 and 128, past rows, K = 2048
+BF16 = dict(weight_dtype="bf16", act_dtype="bf16")
+BF16_CASES = {
+    "bf16-d128-b2-s100-affine-tanh": (_wl(cfg_id=241, **BF16, **AFFINE), 100, 0, True),
+    "bf16-d64-b3-s70-p33-affine": (_wl(hidden=320, heads=5, head_dim=64, ffn=640, batch=3, cfg_id=242, **BF16,
+                                       **AFFINE), 70, 33, False),
+    "bf16-d128-b2-s256": (_wl(hidden=512, heads=4, ffn=2048, cfg_id=243, **BF16), 256, 0, False),
+}
+
+
+@pytest.mark.parametrize("cfg", [None, 0, 1, 2])
+@pytest.mark.parametrize("name", list(BF16_CASES))
+def test_prefill_mfma_bf16_matches_oracle(name, cfg, monkeypatch):
+    """bf16 prefill on matrix cores (automatic tile choice, then each configuration forced) against
+    the oracle, within the bf16 tolerance."""
+    if cfg is not None:
+        monkeypatch.setenv("DS_GEMM_CONFIG", str(cfg))
+    wl, S, P0, tanh = BF16_CASES[name]
+    _check_prefill(f"{name} config {cfg}", wl, S, P0, tanh)
+
+
+def test_bf16_many_rows_take_the_mfma_kernels():
+    """A bf16 prefill of 2 x 40 rows runs the MFMA path's launches (separate LayerNorm launches,
+    which the per-row path does not make) and matches the untimed step bit for bit."""
+    wl, S, P0 = _wl(cfg_id=244, batch=2, **BF16), 40, 6
+    wl, gl, ow, kv, ok, ov, lens, x = _prefill_case(wl, S, P0)
+    y1 = gl.prefill(kv, x)
+    kv2, _, _, _ = filled_caches(wl, 0, gl, past=P0, cap=kv.capacity)
+    y2 = torch.empty_like(y1)
+    timed = gl.time_kernels(kv2, x, y2)
+    torch.cuda.synchronize()
+    assert [p for p, _ in timed] == ["ln1", "qkv", "attn", "o", "ln2", "ff1", "ff2"]
+    assert torch.equal(y1, y2) and torch.equal(kv.k, kv2.k) and torch.equal(kv.v, kv2.v)

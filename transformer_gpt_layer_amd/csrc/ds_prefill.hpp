@@ -10,13 +10,14 @@ namespace ds {
 
 enum GemmEpi { EPI_QKV = 0, EPI_OPROJ = 1, EPI_FF1 = 2, EPI_FF2 = 3 };
 
-// C[M][N] = A[M][K] W[N][K]^T + bias, then by epilogue:
-//   EPI_QKV   columns [0,H) -> out fp16 [M][H] (q); [H,2H) and [2H,3H) -> k_cache / v_cache rows
+// C[M][N] = A[M][K] W[N][K]^T + bias, then by epilogue (T: the layer's 16-bit type, fp16 or bf16;
+// the half_t pointers below then hold T elements):
+//   EPI_QKV   columns [0,H) -> out T [M][H] (q); [H,2H) and [2H,3H) -> k_cache / v_cache rows
 //             d_len[b] + t of sequence b = m / tokens, t = m % tokens, head-major [B][heads][cap][D]
-//   EPI_OPROJ out fp32 [M][N] = resid fp16 [M][N] + C
-//   EPI_FF1   out fp16 [M][N] = GeLU(C)
-//   EPI_FF2   out fp16 [M][N] = resid fp32 [M][N] + C
-// A, W: fp16, K a multiple of 64, M*K*2 and N*K*2 below 2^31 bytes.
+//   EPI_OPROJ out fp32 [M][N] = resid T [M][N] + C
+//   EPI_FF1   out T [M][N] = GeLU(C)
+//   EPI_FF2   out T [M][N] = resid fp32 [M][N] + C
+// A, W, bias: T, K a multiple of 64, M*K*2 and N*K*2 below 2^31 bytes. The skinny path is fp16 only.
 struct GemmArgs {
   const half_t* a;
   const half_t* w;
@@ -45,7 +46,8 @@ struct GemmArgs {
 };
 
 // Attention of `tokens` new rows per sequence over keys 0..d_len[b]+tokens-1 of the cache (the new
-// rows already appended at d_len[b]..), causal or not; d_len is the length before this step.
+// rows already appended at d_len[b]..), causal or not; d_len is the length before this step. The
+// 16-bit pointers hold the layer's type (fp16, or bf16 with bf16 set at launch).
 struct AttnPrefillArgs {
   const half_t* q;        // [batch*tokens][H]
   const half_t* k_cache;  // [batch][heads][cap][head_dim]
@@ -58,13 +60,15 @@ struct AttnPrefillArgs {
 
 // Tile configuration for an M x N x K product on `cus` compute units.
 int gemm_pick(int M, int N, int K, int cus);
-hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int cfg, hipStream_t st);
-// LayerNorm of `rows` rows of H elements (fp32 or fp16 input) into fp16. With d_len, the same
-// launch also advances the cache lengths (d_len[b] += ntok for b < batch, unless that would pass
-// cap): for a LayerNorm that runs after every reader of the lengths in the step.
-hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const half_t* b, half_t* out, int rows, int H,
-                          float eps, hipStream_t st, int32_t* d_len = nullptr, int batch = 0, int ntok = 0, int cap = 0);
-hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t st);
+hipError_t launch_gemm(GemmEpi epi, bool bf16, const GemmArgs& a, int cfg, hipStream_t st);
+// LayerNorm of `rows` rows of H elements (fp32 input, or the 16-bit type) into the 16-bit type
+// (bf16 when bf16 is set, else fp16; gamma and beta in that type). With d_len, the same launch also
+// advances the cache lengths (d_len[b] += ntok for b < batch, unless that would pass cap): for a
+// LayerNorm that runs after every reader of the lengths in the step.
+hipError_t launch_ln_rows(bool bf16, bool in_f32, const void* x, const void* g, const void* b, void* out, int rows,
+                          int H, float eps, hipStream_t st, int32_t* d_len = nullptr, int batch = 0, int ntok = 0,
+                          int cap = 0);
+hipError_t launch_attn_prefill(bool bf16, const AttnPrefillArgs& a, hipStream_t st);
 // The same product and epilogues for M <= 16 rows (decode of a few sequences): every weight row is
 // streamed once, with fp16 weights (w) or int8 codes and group-64 scales (wq, wscale, group).
 hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, int cus, hipStream_t st);

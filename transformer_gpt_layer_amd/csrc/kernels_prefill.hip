@@ -1,16 +1,17 @@
 // kernels_prefill.hip -- the many-row path of one layer (prefill, or decode with a large batch) on
-// gfx950 matrix cores, for fp16 weights and activations.
+// gfx950 matrix cores, for fp16 weights and activations, or bf16 ones (the GEMM, LayerNorm and
+// attention kernels take the 16-bit type as a template parameter; the skinny kernels are fp16 only).
 //
 // The layer is the one of the page "DeepSpeed Inference 内核优化深度解析" (blog.gitcode.com), section
 // 三 3.2, with its four fusion regions. With many rows per weight the projections are dense GEMMs
 // (the QKV, output, FF1 and FF2 GeMMs of section 三 3.2), so they run on MFMA; the regions' element-
 // wise work rides in the GEMM epilogues:
-//   ln_rows       LayerNorm of each row into an fp16 copy (the A operand of the next GEMM)
+//   ln_rows       LayerNorm of each row into a 16-bit copy (the A operand of the next GEMM)
 //   gemm QKV      h Wqkv^T + b; q to the workspace, k and v straight into the head-major cache
 //                 rows d_len[b] + t (the head "transform" of region 2 done by addressing)
 //   attn_prefill  causal attention over the cache, flash style (online softmax), on MFMA
 //   gemm OPROJ    x + ctx Wo^T + bo -> x2 (fp32)                              (region 3 start)
-//   gemm FF1      GeLU(h2 W1^T + b1) -> f (fp16)                              (region 3)
+//   gemm FF1      GeLU(h2 W1^T + b1) -> f (16-bit)                            (region 3)
 //   gemm FF2      x2 + f W2^T + b2 -> y                                       (region 4)
 // The attention mask follows the triangular_masking option of the inference-config table on the
 // page "DeepSpeed MoE 大规模稀疏模型推理实战指南" (blog.gitcode.com): with it, the row at absolute
@@ -67,41 +68,57 @@ __device__ __forceinline__ void lds_barrier() {
 // One wave per row with 16-byte input loads: the mean, then the biased variance around it, then
 // (x - mean) rstd g + b written as fp16. The second and third passes re-read the row from cache.
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-template <int V> __device__ __forceinline__ void ld_halves(const half_t* p, float (&v)[V]) {
+// The 16-bit activation type T of a layer on this path (fp16, or bf16 for bf16 layers): its
+// vectors and its 16 x 16 x 32 product (both forms take the same operand layout on gfx950).
+template <typename T> struct Act16;
+template <> struct Act16<half_t> { typedef half8_t v8; typedef half4_t v4; };
+template <> struct Act16<bf16_t> { typedef bf16x8_t v8; typedef bf16x4_t v4; };
+template <typename T>
+__device__ __forceinline__ float4_t mfma_16x16x32(typename Act16<T>::v8 a, typename Act16<T>::v8 b, float4_t c) {
+  if constexpr (sizeof(T) == 2 && __is_same(T, bf16_t)) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int V, typename T> __device__ __forceinline__ void ld_halves(const T* p, float (&v)[V]) {
   if constexpr (V == 8) {
-    const half8_t h = *reinterpret_cast<const half8_t*>(p);
+    const typename Act16<T>::v8 h = *reinterpret_cast<const typename Act16<T>::v8*>(p);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = (float)h[e];
   } else {
-    const half4_t h = *reinterpret_cast<const half4_t*>(p);
+    const typename Act16<T>::v4 h = *reinterpret_cast<const typename Act16<T>::v4*>(p);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (float)h[e];
   }
 }
-template <int V> __device__ __forceinline__ void ld_row(const half_t* p, float (&v)[V]) { ld_halves<V>(p, v); }
-template <int V> __device__ __forceinline__ void ld_row(const float* p, float (&v)[V]) {
-  const float4_t f = *reinterpret_cast<const float4_t*>(p);
+template <int V, typename IT> __device__ __forceinline__ void ld_row(const IT* p, float (&v)[V]) {
+  if constexpr (sizeof(IT) == 4) {
+    const float4_t f = *reinterpret_cast<const float4_t*>(p);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = f[e];
-}
-template <int V> __device__ __forceinline__ void st_halves(half_t* p, const float (&v)[V]) {
-  if constexpr (V == 8) {
-    half8_t h;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (half_t)v[e];
-    *reinterpret_cast<half8_t*>(p) = h;
+    for (int e = 0; e < 4; ++e) v[e] = f[e];
   } else {
-    half4_t h;
+    ld_halves<V, IT>(p, v);
+  }
+}
+template <int V, typename T> __device__ __forceinline__ void st_halves(T* p, const float (&v)[V]) {
+  if constexpr (V == 8) {
+    typename Act16<T>::v8 h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) h[e] = (half_t)v[e];
-    *reinterpret_cast<half4_t*>(p) = h;
+    for (int e = 0; e < 8; ++e) h[e] = (T)v[e];
+    *reinterpret_cast<typename Act16<T>::v8*>(p) = h;
+  } else {
+    typename Act16<T>::v4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (T)v[e];
+    *reinterpret_cast<typename Act16<T>::v4*>(p) = h;
   }
 }
 
-template <typename IT>
-__global__ __launch_bounds__(256) void ln_rows_kernel(const IT* __restrict__ x, const half_t* __restrict__ g,
-                                                      const half_t* __restrict__ beta, half_t* __restrict__ out,
+template <typename T, typename IT>
+__global__ __launch_bounds__(256) void ln_rows_kernel(const IT* __restrict__ x, const T* __restrict__ g,
+                                                      const T* __restrict__ beta, T* __restrict__ out,
                                                       int rows, int H, float eps) {
   constexpr int V = 16 / (int)sizeof(IT);  // elements per 16-byte load
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -122,7 +139,7 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(const IT* __restrict__ x, 
     for (int e = 0; e < V; ++e) q += (v[e] - mean) * (v[e] - mean);
   }
   const float rstd = rsqrtf(wave_sum(q) / (float)H + eps);
-  half_t* o = out + (size_t)row * H;
+  T* o = out + (size_t)row * H;
   for (int k = lane * V; k < H; k += kWave * V) {
     float gv[V], bv[V];
     ld_row<V>(xr + k, v);
@@ -152,9 +169,9 @@ __device__ __forceinline__ void len_advance(const LenAdvance& la) {
 
 // One wave per row with the whole row in registers (NR 16-byte pieces per lane): one pass over
 // memory, exact two-pass statistics on the registers.
-template <typename IT, int NR>
-__global__ __launch_bounds__(256) void ln_rows_reg_kernel(const IT* __restrict__ x, const half_t* __restrict__ g,
-                                                          const half_t* __restrict__ beta, half_t* __restrict__ out,
+template <typename T, typename IT, int NR>
+__global__ __launch_bounds__(256) void ln_rows_reg_kernel(const IT* __restrict__ x, const T* __restrict__ g,
+                                                          const T* __restrict__ beta, T* __restrict__ out,
                                                           int rows, int H, float eps, const LenAdvance la) {
   constexpr int V = 16 / (int)sizeof(IT);
   len_advance(la);
@@ -182,7 +199,7 @@ __global__ __launch_bounds__(256) void ln_rows_reg_kernel(const IT* __restrict__
 #pragma unroll
       for (int e = 0; e < V; ++e) q += (v[j][e] - mean) * (v[j][e] - mean);
   const float rstd = rsqrtf(wave_sum(q) / (float)H + eps);
-  half_t* o = out + (size_t)row * H;
+  T* o = out + (size_t)row * H;
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     const int i = lane + j * kWave;
@@ -197,9 +214,9 @@ __global__ __launch_bounds__(256) void ln_rows_reg_kernel(const IT* __restrict__
   }
 }
 
-template <typename IT, int NR>
-__global__ __launch_bounds__(256) void ln_row_wg_kernel(const IT* __restrict__ x, const half_t* __restrict__ g,
-                                                       const half_t* __restrict__ beta, half_t* __restrict__ out, int H,
+template <typename T, typename IT, int NR>
+__global__ __launch_bounds__(256) void ln_row_wg_kernel(const IT* __restrict__ x, const T* __restrict__ g,
+                                                       const T* __restrict__ beta, T* __restrict__ out, int H,
                                                        float eps, const LenAdvance la) {
   constexpr int V = 16 / (int)sizeof(IT);
   len_advance(la);
@@ -240,7 +257,7 @@ __global__ __launch_bounds__(256) void ln_row_wg_kernel(const IT* __restrict__ x
   const float dm = t1 / (float)H;
   const float mean = c0 + dm;
   const float rstd = rsqrtf(fmaxf(t2 / (float)H - dm * dm, 0.f) + eps);
-  half_t* o = out + (size_t)row * H;
+  T* o = out + (size_t)row * H;
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     const int i = tid + j * 256;
@@ -312,27 +329,28 @@ __device__ __forceinline__ void issue_stage(unsigned char* stage, int wave, uint
 
 // One wave's operands of one 32-wide half (ks) of a stage: FM A blocks and FN W blocks of 16 rows;
 // lane l takes row l%16, k-chunk l/16 (8 halves), the MFMA operand layout.
-template <typename S>
+template <typename T, typename S>
 __device__ __forceinline__ void read_half(const unsigned char* stage, int ks, int arow, int brow, int fch,
-                                          half8_t (&af)[S::FM], half8_t (&bf)[S::FN]) {
+                                          typename Act16<T>::v8 (&af)[S::FM], typename Act16<T>::v8 (&bf)[S::FN]) {
+  typedef typename Act16<T>::v8 V8;
 #pragma unroll
   for (int a = 0; a < S::FM; ++a)
-    af[a] = *reinterpret_cast<const half8_t*>(stage + swz(arow + 16 * a, 4 * ks + fch));
+    af[a] = *reinterpret_cast<const V8*>(stage + swz(arow + 16 * a, 4 * ks + fch));
 #pragma unroll
   for (int b = 0; b < S::FN; ++b)
-    bf[b] = *reinterpret_cast<const half8_t*>(stage + S::A_BYTES + swz(brow + 16 * b, 4 * ks + fch));
+    bf[b] = *reinterpret_cast<const V8*>(stage + S::A_BYTES + swz(brow + 16 * b, 4 * ks + fch));
 }
 
 // The products of one half, with the FM + FN operand reads issued just before (for the other half)
 // spread between them: one read after every second product.
-template <typename S>
-__device__ __forceinline__ void mfma_half(float4_t (&acc)[S::FM][S::FN], const half8_t (&af)[S::FM],
-                                          const half8_t (&bf)[S::FN]) {
+template <typename T, typename S>
+__device__ __forceinline__ void mfma_half(float4_t (&acc)[S::FM][S::FN], const typename Act16<T>::v8 (&af)[S::FM],
+                                          const typename Act16<T>::v8 (&bf)[S::FN]) {
 #pragma unroll
   for (int a = 0; a < S::FM; ++a)
 #pragma unroll
     for (int b = 0; b < S::FN; ++b)
-      acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+      acc[a][b] = mfma_16x16x32<T>(af[a], bf[b], acc[a][b]);
 #pragma unroll
   for (int i = 0; i < S::FM + S::FN; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
@@ -375,8 +393,11 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& g, int m, int n, 
 // Epilogue of one wave's FM x FN blocks of 16 x 16 at rows mb.., columns nb..: lane l holds
 // C[16a + 4(l/16) + r][16b + l%16]. Column terms (bias, destination) are computed once per column
 // and row terms once per row.
-template <int EPI, int FM, int FN>
+template <typename T, int EPI, int FM, int FN>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, int mb, int nb, const float4_t (&acc)[FM][FN], int lane) {
+  const T* gbias = reinterpret_cast<const T*>(g.bias);
+  T* kc = reinterpret_cast<T*>(g.k_cache);
+  T* vc = reinterpret_cast<T*>(g.v_cache);
   const int frow = lane & 15, fch = lane >> 4;
   float bias[FN];
   size_t col[FN];  // EPI_QKV: offset within the q row or within a sequence's head-major cache block
@@ -388,7 +409,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, int mb, int nb, cons
     col[b] = n;
     bias[b] = 0.f;
     if (n < g.N) {
-      bias[b] = (float)g.bias[n];
+      bias[b] = (float)gbias[n];
       kind[b] = 0;
       if constexpr (EPI == EPI_QKV) {
         const int H = g.hidden;
@@ -415,12 +436,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, int mb, int nb, cons
         // the host rejects a full cache; a bad device length writes no cache row
         const bool okc = pos >= 0 && pos < g.cap;
         const size_t rc = ((size_t)bb * g.heads * g.cap + (okc ? pos : 0)) * g.head_dim;
-        half_t* q = static_cast<half_t*>(g.out) + (size_t)m * H;
+        T* q = static_cast<T*>(g.out) + (size_t)m * H;
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
-          const half_t z = (half_t)(acc[a][b][r] + bias[b]);
+          const T z = (T)(acc[a][b][r] + bias[b]);
           if (kind[b] == 0) q[col[b]] = z;
-          else if (kind[b] > 0 && okc) (kind[b] == 1 ? g.k_cache : g.v_cache)[rc + col[b]] = z;
+          else if (kind[b] > 0 && okc) (kind[b] == 1 ? kc : vc)[rc + col[b]] = z;
         }
       } else {
         const size_t row = (size_t)m * g.N;
@@ -430,11 +451,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, int mb, int nb, cons
           const float z = acc[a][b][r] + bias[b];
           const size_t i = row + col[b];
           if constexpr (EPI == EPI_OPROJ) {
-            static_cast<float*>(g.out)[i] = (float)static_cast<const half_t*>(g.resid)[i] + z;
+            static_cast<float*>(g.out)[i] = (float)static_cast<const T*>(g.resid)[i] + z;
           } else if constexpr (EPI == EPI_FF1) {
-            static_cast<half_t*>(g.out)[i] = (half_t)gelu(z, g.gelu_tanh != 0);
+            static_cast<T*>(g.out)[i] = (T)gelu(z, g.gelu_tanh != 0);
           } else {
-            static_cast<half_t*>(g.out)[i] = (half_t)(static_cast<const float*>(g.resid)[i] + z);
+            static_cast<T*>(g.out)[i] = (T)(static_cast<const float*>(g.resid)[i] + z);
           }
         }
       }
@@ -454,9 +475,10 @@ __device__ __forceinline__ void issue_mine(unsigned char* stage, int q, int grp,
   }
 }
 
-template <int BM, int BN, int ST, int KG, int NWN, int EPI>
+template <typename T, int BM, int BN, int ST, int KG, int NWN, int EPI>
 __global__ __launch_bounds__(gemm_threads(KG, NWN)) void gemm_kernel(const GemmArgs g) {
   typedef GemmShape<BM, BN, ST, KG, NWN> S;
+  typedef typename Act16<T>::v8 V8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load set-up stays scalar
@@ -464,8 +486,8 @@ __global__ __launch_bounds__(gemm_threads(KG, NWN)) void gemm_kernel(const GemmA
   const int wm = q % S::NWM, wn = q / S::NWM;
 
   // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a contiguous tile range.
-  const int T = g.tiles_m * g.tiles_n, i = blockIdx.x;
-  const int x = i & 7, per = T >> 3, rem = T & 7;
+  const int ntiles = g.tiles_m * g.tiles_n, i = blockIdx.x;
+  const int x = i & 7, per = ntiles >> 3, rem = ntiles & 7;
   const int t = x * per + min(x, rem) + (i >> 3);
   const int tm = t % g.tiles_m, tn = t / g.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -492,35 +514,35 @@ __global__ __launch_bounds__(gemm_threads(KG, NWN)) void gemm_kernel(const GemmA
 
   const int fch = lane >> 4;
   const int arow = wm * S::WM + (lane & 15), brow = wn * S::WN + (lane & 15);
-  half8_t a0[S::FM], b0[S::FN], a1[S::FM], b1[S::FN];
+  V8 a0[S::FM], b0[S::FN], a1[S::FM], b1[S::FN];
   wait_vm_dyn((ST - 1) * nl);
   lds_barrier();
   if constexpr (KG == 1) {
-    read_half<S>(smem, 0, arow, brow, fch, a0, b0);
+    read_half<T, S>(smem, 0, arow, brow, fch, a0, b0);
     for (int kt = 0; kt + 1 < nk; ++kt) {
       unsigned char* cur = smem + (kt % ST) * S::STAGE;
-      read_half<S>(cur, 1, arow, brow, fch, a1, b1);
-      mfma_half<S>(acc, a0, b0);
+      read_half<T, S>(cur, 1, arow, brow, fch, a1, b1);
+      mfma_half<T, S>(acc, a0, b0);
       // step kt+1's stage is in LDS and every wave has finished reading step kt's
       wait_vm_dyn((ST - 2) * nl);
       lds_barrier();
       issue_mine<BM, BN, KG, S::NQ>(cur, q, grp, kt + ST, nk, g, va, vw, row_step);
-      read_half<S>(smem + ((kt + 1) % ST) * S::STAGE, 0, arow, brow, fch, a0, b0);
-      mfma_half<S>(acc, a1, b1);
+      read_half<T, S>(smem + ((kt + 1) % ST) * S::STAGE, 0, arow, brow, fch, a0, b0);
+      mfma_half<T, S>(acc, a1, b1);
     }
-    read_half<S>(smem + ((nk - 1) % ST) * S::STAGE, 1, arow, brow, fch, a1, b1);
-    mfma_half<S>(acc, a0, b0);
-    mfma_half<S>(acc, a1, b1);
+    read_half<T, S>(smem + ((nk - 1) % ST) * S::STAGE, 1, arow, brow, fch, a1, b1);
+    mfma_half<T, S>(acc, a0, b0);
+    mfma_half<T, S>(acc, a1, b1);
   } else {
     // this group's half of step kt+1 is read under the products of step kt
-    auto step = [&](int kt, half8_t (&xa)[S::FM], half8_t (&xb)[S::FN], half8_t (&ya)[S::FM], half8_t (&yb)[S::FN]) {
+    auto step = [&](int kt, V8 (&xa)[S::FM], V8 (&xb)[S::FN], V8 (&ya)[S::FM], V8 (&yb)[S::FN]) {
       wait_vm_dyn((ST - 2) * nl);
       lds_barrier();
       issue_mine<BM, BN, KG, S::NQ>(smem + (kt % ST) * S::STAGE, q, grp, kt + ST, nk, g, va, vw, row_step);
-      read_half<S>(smem + ((kt + 1) % ST) * S::STAGE, grp, arow, brow, fch, ya, yb);
-      mfma_half<S>(acc, xa, xb);
+      read_half<T, S>(smem + ((kt + 1) % ST) * S::STAGE, grp, arow, brow, fch, ya, yb);
+      mfma_half<T, S>(acc, xa, xb);
     };
-    read_half<S>(smem, grp, arow, brow, fch, a0, b0);
+    read_half<T, S>(smem, grp, arow, brow, fch, a0, b0);
     int kt = 0;
     for (; kt + 2 < nk; kt += 2) {
       step(kt, a0, b0, a1, b1);
@@ -528,9 +550,9 @@ __global__ __launch_bounds__(gemm_threads(KG, NWN)) void gemm_kernel(const GemmA
     }
     if (kt + 1 < nk) {
       step(kt, a0, b0, a1, b1);
-      mfma_half<S>(acc, a1, b1);
+      mfma_half<T, S>(acc, a1, b1);
     } else {
-      mfma_half<S>(acc, a0, b0);
+      mfma_half<T, S>(acc, a0, b0);
     }
   }
   wait_vm<0>();  // the out-of-range requests past the end
@@ -552,7 +574,7 @@ __global__ __launch_bounds__(gemm_threads(KG, NWN)) void gemm_kernel(const GemmA
 #pragma unroll
       for (int b = 0; b < S::FN; ++b) acc[a][b] += red[(a * S::FN + b) * 64];
   }
-  epilogue<EPI, S::FM, S::FN>(g, m0 + wm * S::WM, n0 + wn * S::WN, acc, lane);
+  epilogue<T, EPI, S::FM, S::FN>(g, m0 + wm * S::WM, n0 + wn * S::WN, acc, lane);
 }
 
 // ------------------------------------------------------------------ attention over the cache
@@ -584,9 +606,10 @@ __device__ __forceinline__ short4_t lds_read_tr16(const unsigned char* p) {
 
 template <int D> constexpr size_t attn_lds_bytes() { return (size_t)AttnShape<D>::LDS; }
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs g) {
   typedef AttnShape<D> S;
+  typedef typename Act16<T>::v8 V8;
   constexpr int NCH = D / 8;  // 16-byte chunks per K row
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* Ks = smem;
@@ -609,13 +632,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
   const int vis = g.causal ? len + trow + 1 : kend;  // keys visible to this lane's row
 
   // q of this lane's row as B operand: Q^T[k = d][n = row], d = 32 s + 8 grp + 0..7
-  half8_t qf[D / 32];
+  V8 qf[D / 32];
   {
-    const half_t* qr = g.q + ((size_t)b * g.tokens + (row_ok ? trow : 0)) * H + (size_t)j * D;
+    const T* qr = reinterpret_cast<const T*>(g.q) + ((size_t)b * g.tokens + (row_ok ? trow : 0)) * H + (size_t)j * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      qf[s] = *reinterpret_cast<const half8_t*>(qr + 32 * s + 8 * grp);
-      if (!row_ok) qf[s] = half8_t{};
+      qf[s] = *reinterpret_cast<const V8*>(qr + 32 * s + 8 * grp);
+      if (!row_ok) qf[s] = V8{};
     }
   }
   const float qscale = g.scale * 1.4426950408889634f;  // softmax in base 2
@@ -624,8 +647,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
   for (int f = 0; f < D / 16; ++f) o[f] = float4_t{0.f, 0.f, 0.f, 0.f};
   float mrun = -1e30f, lrun = 0.f;
 
-  const half_t* kbase = g.k_cache + ((size_t)b * g.heads + j) * g.cap * D;
-  const half_t* vbase = g.v_cache + ((size_t)b * g.heads + j) * g.cap * D;
+  const T* kbase = reinterpret_cast<const T*>(g.k_cache) + ((size_t)b * g.heads + j) * g.cap * D;
+  const T* vbase = reinterpret_cast<const T*>(g.v_cache) + ((size_t)b * g.heads + j) * g.cap * D;
   // each thread carries NT 16-byte pieces of K and of V of a key tile; the next tile's pieces
   // are requested before the current tile's products, so their latency hides behind them
   constexpr int NT = kAttnKeys * NCH / 256;
@@ -664,8 +687,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         const int kr = 16 * f + frow, ch = 4 * s + grp;
-        const half8_t kf = *reinterpret_cast<const half8_t*>(Ks + kr * S::KROW + ((ch ^ (kr & 7)) << 4));
-        st[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], st[f], 0, 0, 0);
+        const V8 kf = *reinterpret_cast<const V8*>(Ks + kr * S::KROW + ((ch ^ (kr & 7)) << 4));
+        st[f] = mfma_16x16x32<T>(kf, qf[s], st[f]);
       }
     }
     float tmax = -1e30f;
@@ -683,14 +706,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
     const float mnew = fmaxf(mrun, tmax);
     const float corr = exp2f(mrun - mnew);
     float psum = 0.f;
-    half8_t pf[2];
+    V8 pf[2];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = st[f][r] <= -1e29f ? 0.f : exp2f(st[f][r] - mnew);
         psum += p;
-        pf[f >> 1][(f & 1) * 4 + r] = (half_t)p;
+        pf[f >> 1][(f & 1) * 4 + r] = (T)p;
       }
     psum += __shfl_xor(psum, 16, kWave);
     psum += __shfl_xor(psum, 32, kWave);
@@ -710,16 +733,16 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
         const short4_t lo = lds_read_tr16(va);
         const short4_t hi = lds_read_tr16(va + 16 * S::VROW);
         const short8_t vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, vv), pf[s], o[f], 0, 0, 0);
+        o[f] = mfma_16x16x32<T>(__builtin_bit_cast(V8, vv), pf[s], o[f]);
       }
   }
   if (!row_ok) return;
   const float inv = 1.f / lrun;
-  half_t* cr = g.ctx + ((size_t)b * g.tokens + trow) * H + (size_t)j * D;
+  T* cr = reinterpret_cast<T*>(g.ctx) + ((size_t)b * g.tokens + trow) * H + (size_t)j * D;
 #pragma unroll
   for (int f = 0; f < D / 16; ++f)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cr[16 * f + 4 * grp + r] = (half_t)(o[f][r] * inv);
+    for (int r = 0; r < 4; ++r) cr[16 * f + 4 * grp + r] = (T)(o[f][r] * inv);
 }
 
 
@@ -974,17 +997,17 @@ hipError_t launch_skinny_t(const GemmArgs& a, int cus, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int ST, int KG, int NWN, int EPI>
+template <typename T, int BM, int BN, int ST, int KG, int NWN, int EPI>
 hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t st) {
   typedef GemmShape<BM, BN, ST, KG, NWN> S;
   GemmArgs a = a0;
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
   // above the default 64 KB of dynamic LDS; set on every launch (cheap, and per device)
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, ST, KG, NWN, EPI>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<T, BM, BN, ST, KG, NWN, EPI>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, ST, KG, NWN, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(S::THREADS), S::LDS, st, a);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, ST, KG, NWN, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(S::THREADS), S::LDS, st, a);
   return hipGetLastError();
 }
 
@@ -996,12 +1019,12 @@ hipError_t launch_gemm_t(const GemmArgs& a0, hipStream_t st) {
 //   2: 256 x 256, two-stage ring, eight waves of 128 x 64, one workgroup per CU: half the bytes
 //      loaded per FLOP of 128 x 160 (the ring's loads set the pace), for products that come out
 //      at 85-100 % of one such tile per CU.
-template <int EPI>
+template <typename T, int EPI>
 hipError_t launch_gemm_epi(const GemmArgs& a, int cfg, hipStream_t st) {
   switch (cfg) {
-    case 0: return launch_gemm_t<128, 160, 2, 1, 2, EPI>(a, st);
-    case 1: return launch_gemm_t<128, 160, 3, 2, 2, EPI>(a, st);
-    case 2: return launch_gemm_t<256, 256, 2, 1, 4, EPI>(a, st);
+    case 0: return launch_gemm_t<T, 128, 160, 2, 1, 2, EPI>(a, st);
+    case 1: return launch_gemm_t<T, 128, 160, 3, 2, 2, EPI>(a, st);
+    case 2: return launch_gemm_t<T, 256, 256, 2, 1, 4, EPI>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1041,28 +1064,34 @@ hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, int 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, int cfg, hipStream_t st) {
-  if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.K < kBK || a.K % kBK) return hipErrorInvalidValue;
+template <typename T>
+hipError_t launch_gemm_type(GemmEpi epi, const GemmArgs& a, int cfg, hipStream_t st) {
   switch (epi) {
-    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(a, cfg, st);
-    case EPI_OPROJ: return launch_gemm_epi<EPI_OPROJ>(a, cfg, st);
-    case EPI_FF1: return launch_gemm_epi<EPI_FF1>(a, cfg, st);
-    case EPI_FF2: return launch_gemm_epi<EPI_FF2>(a, cfg, st);
+    case EPI_QKV: return launch_gemm_epi<T, EPI_QKV>(a, cfg, st);
+    case EPI_OPROJ: return launch_gemm_epi<T, EPI_OPROJ>(a, cfg, st);
+    case EPI_FF1: return launch_gemm_epi<T, EPI_FF1>(a, cfg, st);
+    case EPI_FF2: return launch_gemm_epi<T, EPI_FF2>(a, cfg, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const half_t* b, half_t* out, int rows, int H,
-                          float eps, hipStream_t st, int32_t* d_len, int batch, int ntok, int cap) {
+hipError_t launch_gemm(GemmEpi epi, bool bf16, const GemmArgs& a, int cfg, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.K < kBK || a.K % kBK) return hipErrorInvalidValue;
+  return bf16 ? launch_gemm_type<bf16_t>(epi, a, cfg, st) : launch_gemm_type<half_t>(epi, a, cfg, st);
+}
+
+template <typename T>
+hipError_t launch_ln_rows_t(bool in_f32, const void* x, const T* g, const T* b, T* out, int rows, int H, float eps,
+                            hipStream_t st, int32_t* d_len, int batch, int ntok, int cap) {
   if (rows <= 0) return hipSuccess;
   const LenAdvance la{d_len, batch, ntok, cap};
   constexpr int kNR = 8;  // 16-byte vectors per thread of the workgroup-per-row kernel
   if (rows < 64 && H <= 256 * kNR * (in_f32 ? 4 : 8)) {
     if (in_f32)
-      hipLaunchKernelGGL((ln_row_wg_kernel<float, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const float*>(x), g, b, out, H, eps, la);
+      hipLaunchKernelGGL((ln_row_wg_kernel<T, float, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const float*>(x), g, b, out, H, eps, la);
     else
-      hipLaunchKernelGGL((ln_row_wg_kernel<half_t, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const half_t*>(x), g, b, out, H, eps, la);
+      hipLaunchKernelGGL((ln_row_wg_kernel<T, T, kNR>), dim3(rows), dim3(256), 0, st, static_cast<const T*>(x), g, b, out, H, eps, la);
     return hipGetLastError();
   }
   const dim3 grid((rows + 3) / 4);
@@ -1073,10 +1102,10 @@ hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const hal
 #define DS_LNR(NR)                                                                                                   \
   if (pieces <= NR) {                                                                                                \
     if (in_f32)                                                                                                      \
-      hipLaunchKernelGGL((ln_rows_reg_kernel<float, NR>), grid, dim3(256), 0, st, static_cast<const float*>(x), g, b, \
+      hipLaunchKernelGGL((ln_rows_reg_kernel<T, float, NR>), grid, dim3(256), 0, st, static_cast<const float*>(x), g, b, \
                          out, rows, H, eps, la);                                                                     \
     else                                                                                                             \
-      hipLaunchKernelGGL((ln_rows_reg_kernel<half_t, NR>), grid, dim3(256), 0, st, static_cast<const half_t*>(x), g, \
+      hipLaunchKernelGGL((ln_rows_reg_kernel<T, T, NR>), grid, dim3(256), 0, st, static_cast<const T*>(x), g, \
                          b, out, rows, H, eps, la);                                                                  \
     return hipGetLastError();                                                                                        \
   }
@@ -1087,22 +1116,33 @@ hipError_t launch_ln_rows(bool in_f32, const void* x, const half_t* g, const hal
 #undef DS_LNR
   }
   if (in_f32)
-    hipLaunchKernelGGL(ln_rows_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(x), g, b, out, rows, H, eps);
+    hipLaunchKernelGGL((ln_rows_kernel<T, float>), grid, dim3(256), 0, st, static_cast<const float*>(x), g, b, out, rows, H, eps);
   else
-    hipLaunchKernelGGL(ln_rows_kernel<half_t>, grid, dim3(256), 0, st, static_cast<const half_t*>(x), g, b, out, rows, H, eps);
+    hipLaunchKernelGGL((ln_rows_kernel<T, T>), grid, dim3(256), 0, st, static_cast<const T*>(x), g, b, out, rows, H, eps);
   if (hipError_t e = hipGetLastError()) return e;
   if (d_len) return launch_len_advance(d_len, batch, ntok, cap, st);
   return hipSuccess;
 }
 
-hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t st) {
+hipError_t launch_ln_rows(bool bf16, bool in_f32, const void* x, const void* g, const void* b, void* out, int rows,
+                          int H, float eps, hipStream_t st, int32_t* d_len, int batch, int ntok, int cap) {
+  if (bf16)
+    return launch_ln_rows_t<bf16_t>(in_f32, x, static_cast<const bf16_t*>(g), static_cast<const bf16_t*>(b),
+                                    static_cast<bf16_t*>(out), rows, H, eps, st, d_len, batch, ntok, cap);
+  return launch_ln_rows_t<half_t>(in_f32, x, static_cast<const half_t*>(g), static_cast<const half_t*>(b),
+                                  static_cast<half_t*>(out), rows, H, eps, st, d_len, batch, ntok, cap);
+}
+
+hipError_t launch_attn_prefill(bool bf16, const AttnPrefillArgs& a, hipStream_t st) {
   const int qtiles = (a.tokens + kAttnRows - 1) / kAttnRows;
   const dim3 grid(a.batch * a.heads * qtiles);
   if (a.batch <= 0 || a.tokens <= 0) return hipSuccess;
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), attn_lds_bytes<128>(), st, a);
+    if (bf16) hipLaunchKernelGGL((attn_prefill_kernel<bf16_t, 128>), grid, dim3(256), attn_lds_bytes<128>(), st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<half_t, 128>), grid, dim3(256), attn_lds_bytes<128>(), st, a);
   } else if (a.head_dim == 64) {
-    hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), attn_lds_bytes<64>(), st, a);
+    if (bf16) hipLaunchKernelGGL((attn_prefill_kernel<bf16_t, 64>), grid, dim3(256), attn_lds_bytes<64>(), st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<half_t, 64>), grid, dim3(256), attn_lds_bytes<64>(), st, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -9,8 +9,9 @@
 //   3 output projection + bias + residual                                 (all-reduce point 1)
 //   4 LN2 + FF1 + bias + GeLU                                             (region 3)
 //   5 FF2 + bias + residual, then the cache length advances               (region 4, point 2)
-// With fp16 weights and at least kMfmaMinRows rows per step (prefill, or a large decode batch) the
-// projections are dense GEMMs and run on the MFMA path instead (kernels_prefill.hip): LayerNorm
+// With fp16 (or bf16) weights and activations and at least kMfmaMinRows rows per step (prefill, or a
+// large decode batch) the projections are dense GEMMs and run on the MFMA path instead
+// (kernels_prefill.hip): LayerNorm
 // rows, the QKV GEMM scattering k/v into the cache, flash attention, and the O, FF1, FF2 GEMMs with
 // their bias, residual and GeLU epilogues.
 #include <hip/hip_runtime.h>
@@ -131,10 +132,12 @@ int check_kv(const ds_layer* L, const ds_kv_cache* kv, int batch, int ntok) {
 
 constexpr int kMfmaMinRows = 16;
 
-// The MFMA path takes fp16 weights and activations, at least kMfmaMinRows rows, and operands whose
-// byte sizes stay inside one buffer descriptor's 31-bit range.
+// The MFMA path takes fp16 or bf16 weights with activations of the same type, at least kMfmaMinRows
+// rows, and operands whose byte sizes stay inside one buffer descriptor's 31-bit range.
 bool use_mfma(const ds_layer_desc& d, int rows) {
-  if (d.weight_dtype != DS_F16 || d.act_dtype != DS_F16 || rows < kMfmaMinRows || kv_int8(d)) return false;
+  const bool f16 = d.weight_dtype == DS_F16 && d.act_dtype == DS_F16;
+  const bool bf16 = d.weight_dtype == DS_BF16 && d.act_dtype == DS_BF16;
+  if (!(f16 || bf16) || rows < kMfmaMinRows || kv_int8(d)) return false;
   const int64_t kmax = d.hidden > d.ffn ? d.hidden : d.ffn;
   const int64_t lim = int64_t(1) << 31;
   return (int64_t)rows * kmax * 2 < lim && (int64_t)d.ffn * d.hidden * 2 < lim && 3 * (int64_t)d.hidden * d.hidden * 2 < lim;
@@ -181,6 +184,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     g.n_sk_cnt = W.n_sk_cnt;
   }
   const bool i8 = d.weight_dtype == DS_I8;
+  const bool bf16 = d.act_dtype == DS_BF16;  // the 16-bit type of this path's rows (bf16 or fp16)
   g.group = d.quant_group;
   // one weight matrix (fp16, or int8 codes with their scales) and its product
   auto gemm = [&](ds::GemmEpi epi, ds::GemmArgs& a, const void* w, const void* s) -> hipError_t {
@@ -191,11 +195,11 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
       a.w = static_cast<const ds::half_t*>(w);
     }
     if (skinny) return ds::launch_skinny(epi, i8, a, cus, st);
-    return ds::launch_gemm(epi, a, L->gemm_cfg >= 0 ? L->gemm_cfg : ds::gemm_pick(a.M, a.N, a.K, cus), st);
+    return ds::launch_gemm(epi, bf16, a, L->gemm_cfg >= 0 ? L->gemm_cfg : ds::gemm_pick(a.M, a.N, a.K, cus), st);
   };
 
   // 1: h = LN1(x); [q | k | v] = h Wqkv^T + bqkv, k and v into the cache rows d_len[b] + t
-  if (hipError_t e = ds::launch_ln_rows(false, x, hp(L->w.ln1_g), hp(L->w.ln1_b), h, rows, H, d.ln_eps, st))
+  if (hipError_t e = ds::launch_ln_rows(bf16, false, x, L->w.ln1_g, L->w.ln1_b, h, rows, H, d.ln_eps, st))
     return hip_fail(e, "ln1 launch");
   mark(st, DS_PART_LN1);
   ds::GemmArgs a = g;
@@ -223,7 +227,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     ad.cap = kv->capacity; ad.chunk = W.chunk; ad.causal = d.triangular_masking;
     ad.nchunk = ds::attn_chunks_for(rows, d.heads, kv->capacity, W.chunk, W.nchunk, cus);
     if (hipError_t e = ds::launch_attn_decode_f16(ad, st)) return hip_fail(e, "attention launch");
-  } else if (hipError_t e = ds::launch_attn_prefill(at, st)) {
+  } else if (hipError_t e = ds::launch_attn_prefill(bf16, at, st)) {
     return hip_fail(e, "attention launch");
   }
   mark(st, DS_PART_ATTN);
@@ -236,7 +240,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
 
   // 4: f = GeLU(LN2(x2) W1^T + b1); the LN2 launch also advances d_len by ntok (the QKV epilogue
   // and attention, its only readers in this step, have run)
-  if (hipError_t e = ds::launch_ln_rows(true, x2, hp(L->w.ln2_g), hp(L->w.ln2_b), h, rows, H, d.ln_eps, st, kv->d_len,
+  if (hipError_t e = ds::launch_ln_rows(bf16, true, x2, L->w.ln2_g, L->w.ln2_b, h, rows, H, d.ln_eps, st, kv->d_len,
                                         batch, ntok, kv->capacity))
     return hip_fail(e, "ln2 launch");
   mark(st, DS_PART_LN2);
