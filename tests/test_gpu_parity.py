@@ -51,11 +51,14 @@ SMALL = {
                              batch=15, past=300, cfg_id=106),
     "i8-d64-b15-h2048": _wl("c1", hidden=2048, heads=32, head_dim=64, ffn=8192, weight_dtype="i8", act_dtype="f16",
                             group=64, batch=15, past=301, cfg_id=107),
-    # bf16 weights and activations (the per-row GEMV path at every batch)
+    # bf16 weights and activations (the skinny MFMA path with bf16 operands below 16 rows), one case
+    # wide enough to split K over workgroups and to take 256-position attention chunks
     "bf16-d128-b3": _wl("c1", hidden=256, heads=2, head_dim=128, ffn=768, weight_dtype="bf16", act_dtype="bf16",
                         batch=3, past=70, cfg_id=140),
     "bf16-d64-b9": _wl("c1", hidden=320, heads=5, head_dim=64, ffn=640, weight_dtype="bf16", act_dtype="bf16",
                        batch=9, past=129, cfg_id=141),
+    "bf16-d64-b15-h2048": _wl("c1", hidden=2048, heads=32, head_dim=64, ffn=4096, weight_dtype="bf16",
+                              act_dtype="bf16", batch=15, past=300, cfg_id=144),
 }
 
 # Per-layer LayerNorm gamma ~ 1 + N(0, 0.2), beta ~ N(0, 0.2) and biases ~ N(0, 0.1), on every
@@ -252,6 +255,7 @@ def test_prefill_matches_oracle(name, S, P0, tanh):
 
 @pytest.mark.parametrize("name,parts", [
     ("f16-d64-b9", ["ln1", "qkv", "attn", "o", "ln2", "ff1", "ff2"]),
+    ("bf16-d64-b9", ["ln1", "qkv", "attn", "o", "ln2", "ff1", "ff2"]),
     ("c1", ["qkv", "attn", "o", "ff1", "ff2", "len"]),
 ])
 def test_time_kernels_runs_the_same_step(name, parts):

@@ -40,7 +40,7 @@ struct AttnArgs {
   uint32_t* counters;  // [rows][heads]
   float* ctx;          // [rows][H] fp32 output
   int rows, tokens, heads, head_dim, cap, chunk, nchunk, causal;
-  // fp16 q and ctx in place of q and ctx (launch_attn_decode_f16)
+  // 16-bit q and ctx in place of q and ctx (launch_attn_decode_16: fp16, or bf16 values)
   const _Float16* q16;
   _Float16* ctx16;
   // an int8 cache: fp16 row scales [batch][heads][cap] (null for a cache in the activation type)
@@ -78,8 +78,9 @@ hipError_t launch_moe(Dt wdt, Dt adt, const MoeArgs& a, hipStream_t st, MoeKerne
 
 hipError_t launch_gemv(Dt wdt, Dt adt, GemvKind kind, const GemvArgs& a, hipStream_t st);
 hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st);
-// The same attention with fp16 q and ctx (q16, ctx16) and an fp16 cache.
-hipError_t launch_attn_decode_f16(const AttnArgs& a, hipStream_t st);
+// The same attention with 16-bit q and ctx (q16, ctx16) and a cache of that type: fp16, or bf16
+// with bf16 set (the pointers then hold bf16 values).
+hipError_t launch_attn_decode_16(bool bf16, const AttnArgs& a, hipStream_t st);
 int attn_chunk_for(int rows, int heads, int cap);
 // Chunks per (row, head) for one launch, at most nmax (see the definition).
 int attn_chunks_for(int rows, int heads, int cap, int chunk, int nmax, int cus);

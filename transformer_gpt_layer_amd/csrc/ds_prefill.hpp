@@ -17,7 +17,7 @@ enum GemmEpi { EPI_QKV = 0, EPI_OPROJ = 1, EPI_FF1 = 2, EPI_FF2 = 3 };
 //   EPI_OPROJ out fp32 [M][N] = resid T [M][N] + C
 //   EPI_FF1   out T [M][N] = GeLU(C)
 //   EPI_FF2   out T [M][N] = resid fp32 [M][N] + C
-// A, W, bias: T, K a multiple of 64, M*K*2 and N*K*2 below 2^31 bytes. The skinny path is fp16 only.
+// A, W, bias: T, K a multiple of 64, M*K*2 and N*K*2 below 2^31 bytes.
 struct GemmArgs {
   const half_t* a;
   const half_t* w;
@@ -70,8 +70,9 @@ hipError_t launch_ln_rows(bool bf16, bool in_f32, const void* x, const void* g, 
                           int cap = 0);
 hipError_t launch_attn_prefill(bool bf16, const AttnPrefillArgs& a, hipStream_t st);
 // The same product and epilogues for M <= 16 rows (decode of a few sequences): every weight row is
-// streamed once, with fp16 weights (w) or int8 codes and group-64 scales (wq, wscale, group).
-hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, int cus, hipStream_t st);
+// streamed once, with 16-bit weights (w: fp16, or bf16 with bf16 set) or int8 codes and group-64
+// scales (wq, wscale, group; fp16 activations).
+hipError_t launch_skinny(GemmEpi epi, bool int8_weights, bool bf16, const GemmArgs& a, int cus, hipStream_t st);
 constexpr int kSkinnyMaxRows = 16;
 constexpr int kSkinnyMaxSplit = 8;  // K splits over workgroups at most
 // Workspace of the split skinny launches for products of up to n_max columns.

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < EK; ++e) {
     const size_t qi = (size_t)rr * H + j * D + e0 + e;
-    if constexpr (QH) qv[e] = (float)a.q16[qi] * qs;
+    if constexpr (QH) qv[e] = (float)reinterpret_cast<const AT*>(a.q16)[qi] * qs;
     else qv[e] = a.q[qi] * qs;
   }
 
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
       L += w * lc;
       A += w * ld(pc + 2 + tid);
     }
-    if constexpr (QH) a.ctx16[(size_t)rr * H + j * D + tid] = (half_t)(A / L);
+    if constexpr (QH) reinterpret_cast<AT*>(a.ctx16)[(size_t)rr * H + j * D + tid] = (AT)(A / L);
     else a.ctx[(size_t)rr * H + j * D + tid] = A / L;
   }
   if (tid == 0) *cnt = 0u;
@@ -419,7 +419,9 @@ static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_decode_f16(const AttnArgs& a, hipStream_t st) { return launch_attn_d<half_t, true>(a, st); }
+hipError_t launch_attn_decode_16(bool bf16, const AttnArgs& a, hipStream_t st) {
+  return bf16 ? launch_attn_d<bf16_t, true>(a, st) : launch_attn_d<half_t, true>(a, st);
+}
 
 hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st) {
   if (a.k_scale) return adt == F16 || adt == BF16 ? launch_attn_d<int8_t, false>(a, st) : hipErrorInvalidValue;

@@ -1,6 +1,7 @@
 // kernels_prefill.hip -- the many-row path of one layer (prefill, or decode with a large batch) on
-// gfx950 matrix cores, for fp16 weights and activations, or bf16 ones (the GEMM, LayerNorm and
-// attention kernels take the 16-bit type as a template parameter; the skinny kernels are fp16 only).
+// gfx950 matrix cores, for fp16 weights and activations, or bf16 ones (the GEMM, skinny GEMM,
+// LayerNorm and attention kernels take the 16-bit type as a template parameter; int8 weights go
+// with fp16 activations).
 //
 // The layer is the one of the page "DeepSpeed Inference 内核优化深度解析" (blog.gitcode.com), section
 // 三 3.2, with its four fusion regions. With many rows per weight the projections are dense GEMMs
@@ -361,32 +362,32 @@ __device__ __forceinline__ void mfma_half(float4_t (&acc)[S::FM][S::FN], const t
   if constexpr (rest > 0) __builtin_amdgcn_sched_group_barrier(0x008, rest, 0);
 }
 
-template <int EPI>
+template <typename T, int EPI>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& g, int m, int n, float acc) {
   if (m >= g.M || n >= g.N) return;
-  const float z = acc + (float)g.bias[n];
+  const float z = acc + (float)reinterpret_cast<const T*>(g.bias)[n];
   if constexpr (EPI == EPI_QKV) {
     const int H = g.hidden;
     if (n < H) {
-      static_cast<half_t*>(g.out)[(size_t)m * H + n] = (half_t)z;
+      static_cast<T*>(g.out)[(size_t)m * H + n] = (T)z;
     } else {
       int nn = n - H;
-      half_t* cache = nn < H ? g.k_cache : g.v_cache;
+      T* cache = reinterpret_cast<T*>(nn < H ? g.k_cache : g.v_cache);
       nn = nn < H ? nn : nn - H;
       const int j = nn / g.head_dim, e = nn - j * g.head_dim;
       const int b = m / g.tokens, t = m - b * g.tokens;
       const int pos = g.d_len[b] + t;
       if (pos >= 0 && pos < g.cap)  // the host rejects a full cache; a bad device length writes nothing
-        cache[(((size_t)b * g.heads + j) * g.cap + pos) * g.head_dim + e] = (half_t)z;
+        cache[(((size_t)b * g.heads + j) * g.cap + pos) * g.head_dim + e] = (T)z;
     }
   } else if constexpr (EPI == EPI_OPROJ) {
     const size_t i = (size_t)m * g.N + n;
-    static_cast<float*>(g.out)[i] = (float)static_cast<const half_t*>(g.resid)[i] + z;
+    static_cast<float*>(g.out)[i] = (float)static_cast<const T*>(g.resid)[i] + z;
   } else if constexpr (EPI == EPI_FF1) {
-    static_cast<half_t*>(g.out)[(size_t)m * g.N + n] = (half_t)gelu(z, g.gelu_tanh != 0);
+    static_cast<T*>(g.out)[(size_t)m * g.N + n] = (T)gelu(z, g.gelu_tanh != 0);
   } else {
     const size_t i = (size_t)m * g.N + n;
-    static_cast<half_t*>(g.out)[i] = (half_t)(static_cast<const float*>(g.resid)[i] + z);
+    static_cast<T*>(g.out)[i] = (T)(static_cast<const float*>(g.resid)[i] + z);
   }
 }
 
@@ -786,8 +787,10 @@ constexpr int kSkMinStages = 8;  // stages per wave worth a wave of its own
 // A1: at most 8 activation rows, so one activation load per 64 k (fp16) or two per 128 k (int8)
 // fill the operands of both MFMA halves of a stage: lanes of rows 8-15 (whose products are
 // discarded) load the second half of rows 0-7, which a row rotate by 8 lanes hands to rows 0-7.
-template <bool I8, int EPI, bool A1, int R = kSkR>
+template <typename T, bool I8, int EPI, bool A1, int R = kSkR>
 __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const GemmArgs g) {
+  static_assert(!I8 || sizeof(T) == 2, "int8 weights with fp16 activations");
+  typedef typename Act16<T>::v8 V8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63, KS = blockDim.x >> 6;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -872,8 +875,8 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
         if constexpr (!I8) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const half8_t b = *reinterpret_cast<const half8_t*>(st + swz(r, 4 * t + j));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, op[t]), b, acc, 0, 0, 0);
+            const V8 b = *reinterpret_cast<const V8*>(st + swz(r, 4 * t + j));
+            acc = mfma_16x16x32<T>(__builtin_bit_cast(V8, op[t]), b, acc);
           }
         } else {
 #pragma unroll
@@ -929,18 +932,18 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void skinny_dma_kernel(const 
     if (lane == 0) __hip_atomic_store(g.sk_cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) epilogue_store<EPI>(g, 4 * j + e, n0 + r, acc[e]);
+  for (int e = 0; e < 4; ++e) epilogue_store<T, EPI>(g, 4 * j + e, n0 + r, acc[e]);
 }
 
 // Resident workgroups per CU of a skinny variant with `waves` waves (the runtime's occupancy
 // figure: registers, LDS and wave slots), cached per variant and wave count.
-template <bool I8, int EPI, bool A1>
+template <typename T, bool I8, int EPI, bool A1>
 int skinny_slots(int waves) {
   static int cache[kSkinnyMaxWaves + 1] = {};
   int& c = cache[waves];
   if (c == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&skinny_dma_kernel<I8, EPI, A1>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&skinny_dma_kernel<T, I8, EPI, A1>),
                                                      64 * waves, (size_t)waves * kSkR * 2048) != hipSuccess)
       n = 0;
     c = n > 0 ? n : -1;
@@ -956,7 +959,7 @@ int skinny_slots(int waves) {
 struct SkPlan {
   int split = 0, ks = 0, per_cu = 0;
 };
-template <bool I8, int EPI, bool A1>
+template <typename T, bool I8, int EPI, bool A1>
 SkPlan skinny_plan(const GemmArgs& a, int cus) {
   const int kq = I8 ? 128 : 64;  // k per stage
   const int nblk = (a.N + 15) / 16;
@@ -967,7 +970,7 @@ SkPlan skinny_plan(const GemmArgs& a, int cus) {
     if (a.K % (split * kq) != 0) continue;
     const int kp = a.K / split, nwg = nblk * split, per_cu = (nwg + cus - 1) / cus;
     for (int ks = kSkinnyMaxWaves; ks >= 1; ks >>= 1) {
-      if (kp % (ks * kq) != 0 || kp / (ks * kq) < kSkMinStages || skinny_slots<I8, EPI, A1>(ks) < per_cu) continue;
+      if (kp % (ks * kq) != 0 || kp / (ks * kq) < kSkMinStages || skinny_slots<T, I8, EPI, A1>(ks) < per_cu) continue;
       const bool better = best.split == 0 || (long)per_cu * best.split < (long)best.per_cu * split;
       if (better) best = SkPlan{split, ks, per_cu};
       break;  // the most waves that fit this split
@@ -981,19 +984,19 @@ SkPlan skinny_plan(const GemmArgs& a, int cus) {
   return best;
 }
 
-template <bool I8, int EPI, bool A1>
+template <typename T, bool I8, int EPI, bool A1>
 hipError_t launch_skinny_t(const GemmArgs& a, int cus, hipStream_t st) {
-  const SkPlan p = skinny_plan<I8, EPI, A1>(a, cus);
+  const SkPlan p = skinny_plan<T, I8, EPI, A1>(a, cus);
   if (p.split == 0) return hipErrorInvalidValue;
   const int nblk = (a.N + 15) / 16;
   GemmArgs g = a;
   g.tiles_n = p.split;
   if (p.split == 1 && EPI != EPI_QKV) g.n_sk_cnt = 0;
   const size_t lds = (size_t)p.ks * kSkR * 2048;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_dma_kernel<I8, EPI, A1>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_dma_kernel<T, I8, EPI, A1>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((skinny_dma_kernel<I8, EPI, A1>), dim3(nblk * p.split), dim3(64 * p.ks), lds, st, g);
+  hipLaunchKernelGGL((skinny_dma_kernel<T, I8, EPI, A1>), dim3(nblk * p.split), dim3(64 * p.ks), lds, st, g);
   return hipGetLastError();
 }
 
@@ -1046,20 +1049,21 @@ int gemm_pick(int M, int N, int K, int cus) {
 }
 
 template <int E>
-hipError_t launch_skinny_e(bool i8, const GemmArgs& a, int cus, hipStream_t st) {
+hipError_t launch_skinny_e(bool i8, bool bf16, const GemmArgs& a, int cus, hipStream_t st) {
   const bool a1 = a.M <= 8;  // one activation load serves both halves of a stage
-  if (i8) return a1 ? launch_skinny_t<true, E, true>(a, cus, st) : launch_skinny_t<true, E, false>(a, cus, st);
-  return a1 ? launch_skinny_t<false, E, true>(a, cus, st) : launch_skinny_t<false, E, false>(a, cus, st);
+  if (i8) return a1 ? launch_skinny_t<half_t, true, E, true>(a, cus, st) : launch_skinny_t<half_t, true, E, false>(a, cus, st);
+  if (bf16) return a1 ? launch_skinny_t<bf16_t, false, E, true>(a, cus, st) : launch_skinny_t<bf16_t, false, E, false>(a, cus, st);
+  return a1 ? launch_skinny_t<half_t, false, E, true>(a, cus, st) : launch_skinny_t<half_t, false, E, false>(a, cus, st);
 }
 
-hipError_t launch_skinny(GemmEpi epi, bool int8_weights, const GemmArgs& a, int cus, hipStream_t st) {
+hipError_t launch_skinny(GemmEpi epi, bool int8_weights, bool bf16, const GemmArgs& a, int cus, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.M > kSkinnyMaxRows) return hipErrorInvalidValue;
+  if (a.M > kSkinnyMaxRows || (int8_weights && bf16)) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_QKV: return launch_skinny_e<EPI_QKV>(int8_weights, a, cus, st);
-    case EPI_OPROJ: return launch_skinny_e<EPI_OPROJ>(int8_weights, a, cus, st);
-    case EPI_FF1: return launch_skinny_e<EPI_FF1>(int8_weights, a, cus, st);
-    case EPI_FF2: return launch_skinny_e<EPI_FF2>(int8_weights, a, cus, st);
+    case EPI_QKV: return launch_skinny_e<EPI_QKV>(int8_weights, bf16, a, cus, st);
+    case EPI_OPROJ: return launch_skinny_e<EPI_OPROJ>(int8_weights, bf16, a, cus, st);
+    case EPI_FF1: return launch_skinny_e<EPI_FF1>(int8_weights, bf16, a, cus, st);
+    case EPI_FF2: return launch_skinny_e<EPI_FF2>(int8_weights, bf16, a, cus, st);
   }
   return hipErrorInvalidValue;
 }

@@ -144,10 +144,12 @@ bool use_mfma(const ds_layer_desc& d, int rows) {
 }
 
 // Steps of a few rows (fewer than the MFMA tile path takes) with fp16 activations and fp16 or int8
-// weights run the same LayerNorm / attention kernels with the skinny GEMM, which streams every
-// weight row once whatever the row count.
+// weights, or bf16 weights and activations, run the same LayerNorm / attention kernels with the
+// skinny GEMM, which streams every weight row once whatever the row count.
 bool use_skinny(const ds_layer_desc& d, int rows) {
-  if (d.act_dtype != DS_F16 || rows < 1 || rows > ds::kSkinnyMaxRows || kv_int8(d)) return false;
+  if (rows < 1 || rows > ds::kSkinnyMaxRows || kv_int8(d)) return false;
+  if (d.act_dtype == DS_BF16) return d.weight_dtype == DS_BF16 && rows < kMfmaMinRows;
+  if (d.act_dtype != DS_F16) return false;
   if (d.weight_dtype == DS_F16) return rows < kMfmaMinRows;
   // the int8 skinny kernel applies one scale per 64-element block of K
   return d.weight_dtype == DS_I8 && d.quant_group == 64 && (d.quant_group_mlp == 0 || d.quant_group_mlp == 64);
@@ -194,7 +196,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     } else {
       a.w = static_cast<const ds::half_t*>(w);
     }
-    if (skinny) return ds::launch_skinny(epi, i8, a, cus, st);
+    if (skinny) return ds::launch_skinny(epi, i8, bf16, a, cus, st);
     return ds::launch_gemm(epi, bf16, a, L->gemm_cfg >= 0 ? L->gemm_cfg : ds::gemm_pick(a.M, a.N, a.K, cus), st);
   };
 
@@ -226,7 +228,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     ad.rows = rows; ad.tokens = ntok; ad.heads = d.heads; ad.head_dim = d.head_dim;
     ad.cap = kv->capacity; ad.chunk = W.chunk; ad.causal = d.triangular_masking;
     ad.nchunk = ds::attn_chunks_for(rows, d.heads, kv->capacity, W.chunk, W.nchunk, cus);
-    if (hipError_t e = ds::launch_attn_decode_f16(ad, st)) return hip_fail(e, "attention launch");
+    if (hipError_t e = ds::launch_attn_decode_16(bf16, ad, st)) return hip_fail(e, "attention launch");
   } else if (hipError_t e = ds::launch_attn_prefill(bf16, at, st)) {
     return hip_fail(e, "attention launch");
   }
