@@ -33,6 +33,10 @@ CASES = {
                        batch=9, past=300, cfg_id=603),
     "bf16-d128-b2-affine": _wl(hidden=512, heads=4, head_dim=128, ffn=2048, weight_dtype="bf16", act_dtype="bf16",
                                batch=2, past=45, cfg_id=604, ln_std=0.2, bias_std=0.1),
+    # wide enough that the few-row products split K over workgroups and that attention takes
+    # 256-position chunks (15 rows x 32 heads)
+    "f16-d64-b15-h2048": _wl(hidden=2048, heads=32, head_dim=64, ffn=4096, weight_dtype="f16", act_dtype="f16",
+                             batch=15, past=300, cfg_id=605),
 }
 
 
@@ -64,6 +68,25 @@ def test_decode_with_int8_kv_matches_oracle(name):
         codes = kv.k[:, :, P].cpu().numpy().astype(int)
         assert np.all(np.abs(codes).max(-1) == 127)
         assert kv.lengths() == [P + 1] * wl.batch
+
+
+@pytest.mark.parametrize("name", ["f16-d64-b3-affine", "bf16-d128-b2-affine", "i8w-d128-b9"])
+def test_int8_kv_decode_takes_the_skinny_mfma_path(name):
+    """Decode with an int8 cache and at most 15 rows runs the skinny MFMA launches (with their own
+    LayerNorm launches; the new k and v rows are quantized inside the QKV part), with the same
+    outputs and cache bytes as the untimed step."""
+    wl = CASES[name]
+    gl, _ = gpu_layer_and_oracle_weights(wl, 0, gelu_tanh="affine" in name, kv_dtype="int8")
+    kv1, *_ = kv8_caches(wl, 0, gl)
+    kv2, *_ = kv8_caches(wl, 0, gl)
+    x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, 0, "cuda").to(TORCH[wl.act_dtype])
+    y1 = gl.decode(kv1, x)
+    y2 = torch.empty_like(y1)
+    timed = gl.time_kernels(kv2, x, y2)
+    torch.cuda.synchronize()
+    assert [p for p, _ in timed] == ["ln1", "qkv", "attn", "o", "ln2", "ff1", "ff2"]
+    assert torch.equal(y1, y2) and torch.equal(kv1.k, kv2.k) and torch.equal(kv1.v, kv2.v)
+    assert kv1.lengths() == kv2.lengths()
 
 
 @pytest.mark.parametrize("name,S,P0", [("f16-d128-b1", 6, 5), ("f16-d64-b3-affine", 4, 0)])

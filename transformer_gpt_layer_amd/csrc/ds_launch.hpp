@@ -78,8 +78,8 @@ hipError_t launch_moe(Dt wdt, Dt adt, const MoeArgs& a, hipStream_t st, MoeKerne
 
 hipError_t launch_gemv(Dt wdt, Dt adt, GemvKind kind, const GemvArgs& a, hipStream_t st);
 hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st);
-// The same attention with 16-bit q and ctx (q16, ctx16) and a cache of that type: fp16, or bf16
-// with bf16 set (the pointers then hold bf16 values).
+// The same attention with 16-bit q and ctx (q16, ctx16: fp16, or bf16 with bf16 set, the pointers
+// then holding bf16 values) over a cache of that type, or an int8 cache when k_scale is set.
 hipError_t launch_attn_decode_16(bool bf16, const AttnArgs& a, hipStream_t st);
 int attn_chunk_for(int rows, int heads, int cap);
 // Chunks per (row, head) for one launch, at most nmax (see the definition).

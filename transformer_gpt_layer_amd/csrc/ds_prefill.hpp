@@ -35,6 +35,9 @@ struct GemmArgs {
   const int8_t* wq;
   const half_t* wscale;
   int group;
+  // skinny QKV launch with an int8 cache: k and v as fp32 [M][2H] here instead of into the cache
+  // (quantized afterwards, one scale per head row); null otherwise
+  float* kv_new;
   // skinny QKV launch: zeroes these attention merge counters (and the split counters below) first
   uint32_t* attn_counters;
   int n_counters;

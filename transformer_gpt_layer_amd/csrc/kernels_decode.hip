@@ -181,8 +181,10 @@ hipError_t launch_gemv(Dt wdt, Dt adt, GemvKind kind, const GemvArgs& a, hipStre
 // Region 2: for one (row, head) and one chunk of cached positions, q.K/sqrt(d) scores, a
 // wave-reduced max and sum, and the exp-weighted V sum; the last chunk workgroup to finish merges
 // the chunk partials (log-sum-exp) into ctx. grid = (nchunk, heads, rows).
-template <typename AT, int D, int C, bool QH = false>
+// QT: the type of q and ctx (float: q, ctx; fp16 or bf16: q16, ctx16), independent of the cache's AT.
+template <typename AT, int D, int C, typename QT = float>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
+  constexpr bool QH = sizeof(QT) == 2;
   constexpr int EK = 16 / (int)sizeof(AT);  // elements per 16-byte load
   constexpr int LPK = D / EK;               // lanes per key
   constexpr int KPI = kWave / LPK;          // keys per wave per load
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < EK; ++e) {
     const size_t qi = (size_t)rr * H + j * D + e0 + e;
-    if constexpr (QH) qv[e] = (float)reinterpret_cast<const AT*>(a.q16)[qi] * qs;
+    if constexpr (QH) qv[e] = (float)reinterpret_cast<const QT*>(a.q16)[qi] * qs;
     else qv[e] = a.q[qi] * qs;
   }
 
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnArgs a) {
       L += w * lc;
       A += w * ld(pc + 2 + tid);
     }
-    if constexpr (QH) reinterpret_cast<AT*>(a.ctx16)[(size_t)rr * H + j * D + tid] = (AT)(A / L);
+    if constexpr (QH) reinterpret_cast<QT*>(a.ctx16)[(size_t)rr * H + j * D + tid] = (QT)(A / L);
     else a.ctx[(size_t)rr * H + j * D + tid] = A / L;
   }
   if (tid == 0) *cnt = 0u;
@@ -401,33 +403,34 @@ int attn_chunk_for(int rows, int heads, int cap) {
   return (long)rows * heads >= 256 ? kAttnChunkWide : kAttnChunk;
 }
 
-template <typename AT, int D, int C, bool QH>
+template <typename AT, int D, int C, typename QT>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.nchunk, a.heads, a.rows);
-  hipLaunchKernelGGL((attn_decode_kernel<AT, D, C, QH>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_decode_kernel<AT, D, C, QT>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename AT, bool QH>
+template <typename AT, typename QT>
 static hipError_t launch_attn_d(const AttnArgs& a, hipStream_t st) {
   const bool wide = a.chunk == kAttnChunkWide;
   if (!wide && a.chunk != kAttnChunk) return hipErrorInvalidValue;
   if (a.head_dim == 64)
-    return wide ? launch_attn_t<AT, 64, kAttnChunkWide, QH>(a, st) : launch_attn_t<AT, 64, kAttnChunk, QH>(a, st);
+    return wide ? launch_attn_t<AT, 64, kAttnChunkWide, QT>(a, st) : launch_attn_t<AT, 64, kAttnChunk, QT>(a, st);
   if (a.head_dim == 128)
-    return wide ? launch_attn_t<AT, 128, kAttnChunkWide, QH>(a, st) : launch_attn_t<AT, 128, kAttnChunk, QH>(a, st);
+    return wide ? launch_attn_t<AT, 128, kAttnChunkWide, QT>(a, st) : launch_attn_t<AT, 128, kAttnChunk, QT>(a, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_decode_16(bool bf16, const AttnArgs& a, hipStream_t st) {
-  return bf16 ? launch_attn_d<bf16_t, true>(a, st) : launch_attn_d<half_t, true>(a, st);
+  if (a.k_scale) return bf16 ? launch_attn_d<int8_t, bf16_t>(a, st) : launch_attn_d<int8_t, half_t>(a, st);
+  return bf16 ? launch_attn_d<bf16_t, bf16_t>(a, st) : launch_attn_d<half_t, half_t>(a, st);
 }
 
 hipError_t launch_attn_decode(Dt adt, const AttnArgs& a, hipStream_t st) {
-  if (a.k_scale) return adt == F16 || adt == BF16 ? launch_attn_d<int8_t, false>(a, st) : hipErrorInvalidValue;
-  if (adt == F32) return launch_attn_d<float, false>(a, st);
-  if (adt == F16) return launch_attn_d<half_t, false>(a, st);
-  if (adt == BF16) return launch_attn_d<bf16_t, false>(a, st);
+  if (a.k_scale) return adt == F16 || adt == BF16 ? launch_attn_d<int8_t, float>(a, st) : hipErrorInvalidValue;
+  if (adt == F32) return launch_attn_d<float, float>(a, st);
+  if (adt == F16) return launch_attn_d<half_t, float>(a, st);
+  if (adt == BF16) return launch_attn_d<bf16_t, float>(a, st);
   return hipErrorInvalidValue;
 }
 

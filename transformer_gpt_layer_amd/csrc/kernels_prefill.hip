@@ -370,6 +370,8 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& g, int m, int n, 
     const int H = g.hidden;
     if (n < H) {
       static_cast<T*>(g.out)[(size_t)m * H + n] = (T)z;
+    } else if (g.kv_new) {
+      g.kv_new[(size_t)m * 2 * H + (n - H)] = z;
     } else {
       int nn = n - H;
       T* cache = reinterpret_cast<T*>(nn < H ? g.k_cache : g.v_cache);

@@ -145,9 +145,11 @@ bool use_mfma(const ds_layer_desc& d, int rows) {
 
 // Steps of a few rows (fewer than the MFMA tile path takes) with fp16 activations and fp16 or int8
 // weights, or bf16 weights and activations, run the same LayerNorm / attention kernels with the
-// skinny GEMM, which streams every weight row once whatever the row count.
-bool use_skinny(const ds_layer_desc& d, int rows) {
-  if (rows < 1 || rows > ds::kSkinnyMaxRows || kv_int8(d)) return false;
+// skinny GEMM, which streams every weight row once whatever the row count. With an int8 cache only
+// decode steps (one row per sequence) take it: the new k and v rows leave the QKV product in fp32
+// and are quantized by the store kernel before the chunked decode attention reads the cache.
+bool use_skinny(const ds_layer_desc& d, int rows, int ntok) {
+  if (rows < 1 || rows > ds::kSkinnyMaxRows || (kv_int8(d) && ntok != 1)) return false;
   if (d.act_dtype == DS_BF16) return d.weight_dtype == DS_BF16 && rows < kMfmaMinRows;
   if (d.act_dtype != DS_F16) return false;
   if (d.weight_dtype == DS_F16) return rows < kMfmaMinRows;
@@ -211,7 +213,14 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     a.attn_counters = reinterpret_cast<uint32_t*>(base + W.cnt);
     a.n_counters = rows * d.heads;
   }
+  float* kvn = kv_int8(d) ? reinterpret_cast<float*>(base + W.kvn) : nullptr;
+  a.kv_new = kvn;  // an int8 cache (skinny decode only): k and v in fp32, quantized next
   if (hipError_t e = gemm(ds::EPI_QKV, a, L->w.w_qkv, L->w.s_qkv)) return hip_fail(e, "qkv gemm launch");
+  if (kvn) {
+    if (hipError_t e = ds::launch_kv_store_i8(ds::F32, kvn, kvn + H, 2 * H, kv->k, kv->v, kv->k_scale, kv->v_scale,
+                                              kv->d_len, batch, ntok, d.heads, d.head_dim, kv->capacity, st))
+      return hip_fail(e, "int8 kv store launch");
+  }
   mark(st, DS_PART_QKV);
 
   // 2: attention of the new rows over the cache
@@ -228,6 +237,8 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     ad.rows = rows; ad.tokens = ntok; ad.heads = d.heads; ad.head_dim = d.head_dim;
     ad.cap = kv->capacity; ad.chunk = W.chunk; ad.causal = d.triangular_masking;
     ad.nchunk = ds::attn_chunks_for(rows, d.heads, kv->capacity, W.chunk, W.nchunk, cus);
+    ad.k_scale = kvn ? kv->k_scale : nullptr;
+    ad.v_scale = kvn ? kv->v_scale : nullptr;
     if (hipError_t e = ds::launch_attn_decode_16(bf16, ad, st)) return hip_fail(e, "attention launch");
   } else if (hipError_t e = ds::launch_attn_prefill(bf16, at, st)) {
     return hip_fail(e, "attention launch");
@@ -276,7 +287,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   if (use_mfma(L->desc, rows)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, false, st);
-  if (use_skinny(L->desc, rows)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, true, st);
+  if (use_skinny(L->desc, rows, ntok)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, true, st);
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
   const int H = d.hidden, F = d.ffn;
 
