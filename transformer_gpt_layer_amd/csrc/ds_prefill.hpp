@@ -57,6 +57,10 @@ struct AttnPrefillArgs {
   const half_t* v_cache;
   const int32_t* d_len;
   half_t* ctx;            // [batch*tokens][H]
+  // an int8 cache: k_cache and v_cache hold int8 codes and these their fp16 row scales
+  // [batch][heads][cap] (the kernel dequantizes while staging); null for a 16-bit cache
+  const void* k_scale;
+  const void* v_scale;
   int batch, tokens, heads, head_dim, cap, causal;
   float scale;            // 1/sqrt(head_dim)
 };

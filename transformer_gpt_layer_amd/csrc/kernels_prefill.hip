@@ -442,9 +442,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, int mb, int nb, cons
         T* q = static_cast<T*>(g.out) + (size_t)m * H;
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
-          const T z = (T)(acc[a][b][r] + bias[b]);
-          if (kind[b] == 0) q[col[b]] = z;
-          else if (kind[b] > 0 && okc) (kind[b] == 1 ? kc : vc)[rc + col[b]] = z;
+          const float zf = acc[a][b][r] + bias[b];
+          if (kind[b] == 0) q[col[b]] = (T)zf;
+          else if (kind[b] > 0 && g.kv_new) g.kv_new[(size_t)m * 2 * H + (nb + 16 * b + frow - H)] = zf;
+          else if (kind[b] > 0 && okc) (kind[b] == 1 ? kc : vc)[rc + col[b]] = (T)zf;
         }
       } else {
         const size_t row = (size_t)m * g.N;
@@ -609,7 +610,7 @@ __device__ __forceinline__ short4_t lds_read_tr16(const unsigned char* p) {
 
 template <int D> constexpr size_t attn_lds_bytes() { return (size_t)AttnShape<D>::LDS; }
 
-template <typename T, int D>
+template <typename T, int D, bool KV8>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs g) {
   typedef AttnShape<D> S;
   typedef typename Act16<T>::v8 V8;
@@ -650,8 +651,21 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
   for (int f = 0; f < D / 16; ++f) o[f] = float4_t{0.f, 0.f, 0.f, 0.f};
   float mrun = -1e30f, lrun = 0.f;
 
-  const T* kbase = reinterpret_cast<const T*>(g.k_cache) + ((size_t)b * g.heads + j) * g.cap * D;
-  const T* vbase = reinterpret_cast<const T*>(g.v_cache) + ((size_t)b * g.heads + j) * g.cap * D;
+  const size_t hrow = ((size_t)b * g.heads + j) * g.cap;  // first cache row of this (sequence, head)
+  const T* kbase = reinterpret_cast<const T*>(g.k_cache) + hrow * D;
+  const T* vbase = reinterpret_cast<const T*>(g.v_cache) + hrow * D;
+  // an int8 cache: 8 codes of a row times its scale become one 16-byte piece of 16-bit values
+  auto deq8 = [&](const void* cache, const void* scales, int key, int ch) -> u32x4 {
+    const uint2 c = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(cache) + (hrow + key) * D + ch * 8);
+    const float s = (float)static_cast<const half_t*>(scales)[hrow + key];
+    V8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = e < 4 ? c.x : c.y;
+      v[e] = (T)((float)(int8_t)(w >> (8 * (e & 3))) * s);
+    }
+    return __builtin_bit_cast(u32x4, v);
+  };
   // each thread carries NT 16-byte pieces of K and of V of a key tile; the next tile's pieces
   // are requested before the current tile's products, so their latency hides behind them
   constexpr int NT = kAttnKeys * NCH / 256;
@@ -664,8 +678,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
       kpre[i] = u32x4{0u, 0u, 0u, 0u};
       vpre[i] = u32x4{0u, 0u, 0u, 0u};
       if (key < kend) {
-        kpre[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + ch * 8);
-        vpre[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * D + ch * 8);
+        if constexpr (KV8) {
+          kpre[i] = deq8(g.k_cache, g.k_scale, key, ch);
+          vpre[i] = deq8(g.v_cache, g.v_scale, key, ch);
+        } else {
+          kpre[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + ch * 8);
+          vpre[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * D + ch * 8);
+        }
       }
     }
   };
@@ -1139,16 +1158,23 @@ hipError_t launch_ln_rows(bool bf16, bool in_f32, const void* x, const void* g, 
                                   static_cast<half_t*>(out), rows, H, eps, st, d_len, batch, ntok, cap);
 }
 
+template <typename T, int D>
+static void launch_attn_prefill_t(const AttnPrefillArgs& a, dim3 grid, hipStream_t st) {
+  if (a.k_scale) hipLaunchKernelGGL((attn_prefill_kernel<T, D, true>), grid, dim3(256), attn_lds_bytes<D>(), st, a);
+  else hipLaunchKernelGGL((attn_prefill_kernel<T, D, false>), grid, dim3(256), attn_lds_bytes<D>(), st, a);
+}
+
 hipError_t launch_attn_prefill(bool bf16, const AttnPrefillArgs& a, hipStream_t st) {
   const int qtiles = (a.tokens + kAttnRows - 1) / kAttnRows;
   const dim3 grid(a.batch * a.heads * qtiles);
   if (a.batch <= 0 || a.tokens <= 0) return hipSuccess;
+  if ((a.k_scale == nullptr) != (a.v_scale == nullptr)) return hipErrorInvalidValue;
   if (a.head_dim == 128) {
-    if (bf16) hipLaunchKernelGGL((attn_prefill_kernel<bf16_t, 128>), grid, dim3(256), attn_lds_bytes<128>(), st, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<half_t, 128>), grid, dim3(256), attn_lds_bytes<128>(), st, a);
+    if (bf16) launch_attn_prefill_t<bf16_t, 128>(a, grid, st);
+    else launch_attn_prefill_t<half_t, 128>(a, grid, st);
   } else if (a.head_dim == 64) {
-    if (bf16) hipLaunchKernelGGL((attn_prefill_kernel<bf16_t, 64>), grid, dim3(256), attn_lds_bytes<64>(), st, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<half_t, 64>), grid, dim3(256), attn_lds_bytes<64>(), st, a);
+    if (bf16) launch_attn_prefill_t<bf16_t, 64>(a, grid, st);
+    else launch_attn_prefill_t<half_t, 64>(a, grid, st);
   } else {
     return hipErrorInvalidValue;
   }

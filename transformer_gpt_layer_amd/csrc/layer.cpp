@@ -132,12 +132,13 @@ int check_kv(const ds_layer* L, const ds_kv_cache* kv, int batch, int ntok) {
 
 constexpr int kMfmaMinRows = 16;
 
-// The MFMA path takes fp16 or bf16 weights with activations of the same type, at least kMfmaMinRows
-// rows, and operands whose byte sizes stay inside one buffer descriptor's 31-bit range.
+// The MFMA path takes fp16 or bf16 weights with activations of the same type (and a cache of that
+// type or int8), at least kMfmaMinRows rows, and operands whose byte sizes stay inside one buffer
+// descriptor's 31-bit range.
 bool use_mfma(const ds_layer_desc& d, int rows) {
   const bool f16 = d.weight_dtype == DS_F16 && d.act_dtype == DS_F16;
   const bool bf16 = d.weight_dtype == DS_BF16 && d.act_dtype == DS_BF16;
-  if (!(f16 || bf16) || rows < kMfmaMinRows || kv_int8(d)) return false;
+  if (!(f16 || bf16) || rows < kMfmaMinRows) return false;
   const int64_t kmax = d.hidden > d.ffn ? d.hidden : d.ffn;
   const int64_t lim = int64_t(1) << 31;
   return (int64_t)rows * kmax * 2 < lim && (int64_t)d.ffn * d.hidden * 2 < lim && 3 * (int64_t)d.hidden * d.hidden * 2 < lim;
@@ -145,11 +146,11 @@ bool use_mfma(const ds_layer_desc& d, int rows) {
 
 // Steps of a few rows (fewer than the MFMA tile path takes) with fp16 activations and fp16 or int8
 // weights, or bf16 weights and activations, run the same LayerNorm / attention kernels with the
-// skinny GEMM, which streams every weight row once whatever the row count. With an int8 cache only
-// decode steps (one row per sequence) take it: the new k and v rows leave the QKV product in fp32
-// and are quantized by the store kernel before the chunked decode attention reads the cache.
-bool use_skinny(const ds_layer_desc& d, int rows, int ntok) {
-  if (rows < 1 || rows > ds::kSkinnyMaxRows || (kv_int8(d) && ntok != 1)) return false;
+// skinny GEMM, which streams every weight row once whatever the row count. With an int8 cache the
+// new k and v rows leave the QKV product in fp32 and are quantized by the store kernel before the
+// attention reads the cache.
+bool use_skinny(const ds_layer_desc& d, int rows) {
+  if (rows < 1 || rows > ds::kSkinnyMaxRows) return false;
   if (d.act_dtype == DS_BF16) return d.weight_dtype == DS_BF16 && rows < kMfmaMinRows;
   if (d.act_dtype != DS_F16) return false;
   if (d.weight_dtype == DS_F16) return rows < kMfmaMinRows;
@@ -214,7 +215,7 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
     a.n_counters = rows * d.heads;
   }
   float* kvn = kv_int8(d) ? reinterpret_cast<float*>(base + W.kvn) : nullptr;
-  a.kv_new = kvn;  // an int8 cache (skinny decode only): k and v in fp32, quantized next
+  a.kv_new = kvn;  // an int8 cache: k and v leave the product in fp32 and are quantized next
   if (hipError_t e = gemm(ds::EPI_QKV, a, L->w.w_qkv, L->w.s_qkv)) return hip_fail(e, "qkv gemm launch");
   if (kvn) {
     if (hipError_t e = ds::launch_kv_store_i8(ds::F32, kvn, kvn + H, 2 * H, kv->k, kv->v, kv->k_scale, kv->v_scale,
@@ -228,6 +229,8 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   at.q = q; at.k_cache = g.k_cache; at.v_cache = g.v_cache; at.d_len = kv->d_len; at.ctx = ctx;
   at.batch = batch; at.tokens = ntok; at.heads = d.heads; at.head_dim = d.head_dim; at.cap = kv->capacity;
   at.causal = d.triangular_masking; at.scale = 1.f / std::sqrt((float)d.head_dim);
+  at.k_scale = kvn ? kv->k_scale : nullptr;
+  at.v_scale = kvn ? kv->v_scale : nullptr;
   if (chunked_attn) {
     ds::AttnArgs ad{};
     ad.q16 = q; ad.ctx16 = ctx;
@@ -287,7 +290,7 @@ int forward_rows(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   if (use_mfma(L->desc, rows)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, false, st);
-  if (use_skinny(L->desc, rows, ntok)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, true, st);
+  if (use_skinny(L->desc, rows)) return forward_mfma(L, kv, x, y, batch, ntok, base, W, true, st);
   const ds::Dt wdt = static_cast<ds::Dt>(d.weight_dtype), adt = static_cast<ds::Dt>(d.act_dtype);
   const int H = d.hidden, F = d.ffn;
 
