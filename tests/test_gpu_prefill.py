@@ -191,3 +191,34 @@ def test_bf16_many_rows_take_the_mfma_kernels():
     torch.cuda.synchronize()
     assert [p for p, _ in timed] == ["ln1", "qkv", "attn", "o", "ln2", "ff1", "ff2"]
     assert torch.equal(y1, y2) and torch.equal(kv.k, kv2.k) and torch.equal(kv.v, kv2.v)
+
+
+# int8 weights (codes with fp16 group scales) above the skinny kernel's 16 rows: each matrix is
+# dequantized into fp16 just before its MFMA product; groups of 64, 128 with 64 in the MLP, and 32
+I8 = dict(weight_dtype="i8", act_dtype="f16")
+I8_CASES = {
+    "i8-g64-d128-b2-s100-affine": (_wl(group=64, cfg_id=251, **I8, **AFFINE), 100, 0, False),
+    "i8-g128-mlp64-d64-b3-s70-p33-tanh": (_wl(hidden=512, heads=8, head_dim=64, ffn=1024, batch=3, group=128,
+                                              group_mlp=64, cfg_id=252, **I8, **AFFINE), 70, 33, True),
+    "i8-g32-d128-b1-s17-p5": (_wl(batch=1, group=32, cfg_id=253, **I8), 17, 5, False),
+}
+
+
+@pytest.mark.parametrize("name", list(I8_CASES))
+def test_prefill_mfma_int8_weights_matches_oracle(name):
+    wl, S, P0, tanh = I8_CASES[name]
+    _check_prefill(name, wl, S, P0, tanh)
+
+
+def test_int8_prefill_takes_the_mfma_kernels():
+    """An int8 prefill of 2 x 40 rows runs the MFMA path's launches (separate LayerNorm launches,
+    which the per-row path does not make) and matches the untimed step bit for bit."""
+    wl, S, P0 = _wl(cfg_id=254, batch=2, group=64, **I8), 40, 6
+    wl, gl, ow, kv, ok, ov, lens, x = _prefill_case(wl, S, P0)
+    y1 = gl.prefill(kv, x)
+    kv2, _, _, _ = filled_caches(wl, 0, gl, past=P0, cap=kv.capacity)
+    y2 = torch.empty_like(y1)
+    timed = gl.time_kernels(kv2, x, y2)
+    torch.cuda.synchronize()
+    assert [p for p, _ in timed] == ["ln1", "qkv", "attn", "o", "ln2", "ff1", "ff2"]
+    assert torch.equal(y1, y2) and torch.equal(kv.k, kv2.k) and torch.equal(kv.v, kv2.v)

@@ -106,5 +106,8 @@ hipError_t launch_quantize_i8(const float* w, int8_t* q, uint16_t* s, int n, int
                               hipStream_t st);
 hipError_t launch_dequantize_i8(const int8_t* q, const uint16_t* s, float* w, int n, int k,
                                 int group, hipStream_t st);
+// The same into fp16 (each weight rounded once): the operand of the many-row GEMM for int8 layers.
+hipError_t launch_dequantize_i8_f16(const int8_t* q, const uint16_t* s, _Float16* w, int n, int k, int group,
+                                    hipStream_t st);
 
 }  // namespace ds

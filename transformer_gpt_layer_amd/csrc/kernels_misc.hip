@@ -219,22 +219,39 @@ __global__ __launch_bounds__(256) void quantize_i8_kernel(const float* __restric
   }
 }
 
-// w = q * s through the same int8 -> fp16 conversion the GEMV kernels use (16 codes per thread).
+// w = q * s through the same int8 -> fp16 conversion the GEMV kernels use (16 codes per thread; a
+// run of 16 never straddles a scale group, whose size is a multiple of 16). OT: fp32, or fp16 (the
+// product rounded once: the operand of the many-row GEMM for int8 layers).
+template <typename OT>
 __global__ __launch_bounds__(256) void dequantize_i8_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ s,
-                                                            float* __restrict__ w, int n, int k, int group) {
+                                                            OT* __restrict__ w, int n, int k, int group) {
   const size_t v = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (v >= (size_t)n * k / 16) return;
   const size_t el = v * 16, row = el / k, col = el - row * k;
   const float sc = (float)__builtin_bit_cast(half_t, s[row * (k / group) + col / group]);
   const u32x4 raw = ld16(q + el);
   const uint32_t words[4] = {raw.x ^ 0x80808080u, raw.y ^ 0x80808080u, raw.z ^ 0x80808080u, raw.w ^ 0x80808080u};
+  float o[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const half2_t lo = i8pair_to_half2(words[i], false), hi = i8pair_to_half2(words[i], true);
-    w[el + 4 * i + 0] = (float)lo.x * sc;
-    w[el + 4 * i + 1] = (float)lo.y * sc;
-    w[el + 4 * i + 2] = (float)hi.x * sc;
-    w[el + 4 * i + 3] = (float)hi.y * sc;
+    o[4 * i + 0] = (float)lo.x * sc;
+    o[4 * i + 1] = (float)lo.y * sc;
+    o[4 * i + 2] = (float)hi.x * sc;
+    o[4 * i + 3] = (float)hi.y * sc;
+  }
+  if constexpr (sizeof(OT) == 4) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w[el + e] = o[e];
+  } else {
+    uint32_t p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      p[e] = (uint32_t)__builtin_bit_cast(uint16_t, (OT)o[2 * e]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (OT)o[2 * e + 1]) << 16);
+    u32x4* dst = reinterpret_cast<u32x4*>(w + el);
+    dst[0] = u32x4{p[0], p[1], p[2], p[3]};
+    dst[1] = u32x4{p[4], p[5], p[6], p[7]};
   }
 }
 
@@ -248,7 +265,18 @@ hipError_t launch_quantize_i8(const float* w, int8_t* q, uint16_t* s, int n, int
 hipError_t launch_dequantize_i8(const int8_t* q, const uint16_t* s, float* w, int n, int k, int group, hipStream_t st) {
   const size_t vecs = (size_t)n * k / 16;
   if (vecs == 0) return hipSuccess;
-  hipLaunchKernelGGL(dequantize_i8_kernel, dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, st, q, s, w, n, k, group);
+  hipLaunchKernelGGL(dequantize_i8_kernel<float>, dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, st, q, s, w, n, k,
+                     group);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_i8_f16(const int8_t* q, const uint16_t* s, half_t* w, int n, int k, int group,
+                                    hipStream_t st) {
+  const size_t vecs = (size_t)n * k / 16;
+  if (vecs == 0) return hipSuccess;
+  if (k % 16 || group % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dequantize_i8_kernel<half_t>, dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, st, q, s, w, n, k,
+                     group);
   return hipGetLastError();
 }
 

@@ -82,7 +82,7 @@ void mark(hipStream_t st, int kind) {
 }
 
 struct WsLayout {
-  size_t q, part, cnt, ctx, x2, f, h, sk_part, sk_cnt, kvn, total;
+  size_t q, part, cnt, ctx, x2, f, h, sk_part, sk_cnt, kvn, wdq, total;
   int chunk, nchunk, n_sk_cnt;
 };
 
@@ -106,6 +106,10 @@ WsLayout ws_layout(const ds_layer_desc& d, int rows, int cap) {
   L.n_sk_cnt = (n_max + 15) / 16;
   // an int8 cache: the new k and v rows (fp32) between the QKV product and their quantization
   L.kvn = kv_int8(d) ? take((size_t)rows * 2 * d.hidden * 4) : 0;
+  // int8 weights at more rows than the skinny kernel takes: one matrix at a time dequantized into
+  // fp16 for the many-row GEMM (the largest of Wqkv [3H][H], W1 [F][H], W2 [H][F])
+  const size_t wmax = (size_t)d.hidden * (size_t)(3 * d.hidden > d.ffn ? 3 * d.hidden : d.ffn);
+  L.wdq = d.weight_dtype == DS_I8 && rows > ds::kSkinnyMaxRows ? take(wmax * 2) : 0;
   L.total = off;
   return L;
 }
@@ -134,11 +138,13 @@ constexpr int kMfmaMinRows = 16;
 
 // The MFMA path takes fp16 or bf16 weights with activations of the same type (and a cache of that
 // type or int8), at least kMfmaMinRows rows, and operands whose byte sizes stay inside one buffer
-// descriptor's 31-bit range.
+// descriptor's 31-bit range. int8 weights with fp16 activations take it above the skinny kernel's
+// row limit, each matrix dequantized into fp16 in the workspace just before its product.
 bool use_mfma(const ds_layer_desc& d, int rows) {
   const bool f16 = d.weight_dtype == DS_F16 && d.act_dtype == DS_F16;
   const bool bf16 = d.weight_dtype == DS_BF16 && d.act_dtype == DS_BF16;
-  if (!(f16 || bf16) || rows < kMfmaMinRows) return false;
+  const bool i8 = d.weight_dtype == DS_I8 && d.act_dtype == DS_F16 && rows > ds::kSkinnyMaxRows;
+  if (!(f16 || bf16 || i8) || rows < kMfmaMinRows) return false;
   const int64_t kmax = d.hidden > d.ffn ? d.hidden : d.ffn;
   const int64_t lim = int64_t(1) << 31;
   return (int64_t)rows * kmax * 2 < lim && (int64_t)d.ffn * d.hidden * 2 < lim && 3 * (int64_t)d.hidden * d.hidden * 2 < lim;
@@ -193,9 +199,18 @@ int forward_mfma(const ds_layer* L, ds_kv_cache* kv, const void* x, void* y, int
   g.group = d.quant_group;
   // one weight matrix (fp16, or int8 codes with their scales) and its product
   auto gemm = [&](ds::GemmEpi epi, ds::GemmArgs& a, const void* w, const void* s) -> hipError_t {
-    if (i8) {
+    if (i8 && skinny) {
       a.wq = static_cast<const int8_t*>(w);
       a.wscale = static_cast<const ds::half_t*>(s);
+    } else if (i8) {
+      // the many-row GEMM takes fp16 operands: the codes times their group scales, rounded once
+      const int grp = epi == ds::EPI_FF1 || epi == ds::EPI_FF2 ? (d.quant_group_mlp ? d.quant_group_mlp : d.quant_group)
+                                                               : d.quant_group;
+      auto* wdq = reinterpret_cast<ds::half_t*>(base + W.wdq);
+      if (hipError_t e = ds::launch_dequantize_i8_f16(static_cast<const int8_t*>(w), static_cast<const uint16_t*>(s),
+                                                      wdq, a.N, a.K, grp, st))
+        return e;
+      a.w = wdq;
     } else {
       a.w = static_cast<const ds::half_t*>(w);
     }
