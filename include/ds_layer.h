@@ -141,7 +141,9 @@ int ds_layer_create(const ds_layer_desc* desc, const ds_layer_weights* weights, 
 int ds_layer_destroy(ds_layer_t* layer);
 
 /* Bytes of device workspace that decode (max_tokens == 1) or prefill needs for up to max_batch
- * sequences of max_tokens new rows against caches of `capacity` rows. Returns 0 on bad input. */
+ * sequences of max_tokens new rows against caches of `capacity` rows. For int8 weights and more
+ * than 16 rows this includes an fp16 copy of the largest weight matrix (each matrix is expanded
+ * there just before its product). Returns 0 on bad input. */
 size_t ds_layer_workspace_bytes(const ds_layer_t* layer, int32_t max_batch, int32_t max_tokens,
                                 int32_t capacity);
 
