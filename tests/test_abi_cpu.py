@@ -116,6 +116,25 @@ def test_workspace_bytes():
     L.ds_layer_destroy(h)
 
 
+def test_int8_workspace_holds_one_fp16_matrix_above_sixteen_rows():
+    """int8 layers above the skinny kernel's 16 rows expand each matrix into fp16 in the workspace
+    before its MFMA product: the size grows by the largest matrix in fp16 (here Wqkv, 3H x H, which
+    is larger than W1 and W2 at F = 2H) plus the row buffers of one more row."""
+    L = _lib.lib()
+    rc, h = _create(_desc(weight_dtype=2, quant_group=64), _weights(int8=True))
+    assert rc == 0, L.ds_last_error()
+    H, F = 256, 512
+    wmax = max(3 * H * H, F * H) * 2
+    at16 = L.ds_layer_workspace_bytes(h, 16, 1, 64)
+    at17 = L.ds_layer_workspace_bytes(h, 17, 1, 64)
+    assert wmax <= at17 - at16 < wmax + 64 * 1024
+    L.ds_layer_destroy(h)
+    # fp16 layers carry no such copy
+    h16 = _layer()
+    assert L.ds_layer_workspace_bytes(h16, 17, 1, 64) - L.ds_layer_workspace_bytes(h16, 16, 1, 64) < 64 * 1024
+    L.ds_layer_destroy(h16)
+
+
 def test_forward_rejects_before_enqueue():
     L, h = _lib.lib(), _layer()
     hl = np.array([63, 10], dtype=np.int32)
