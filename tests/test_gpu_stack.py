@@ -12,7 +12,7 @@ import torch
 import oracle
 import synthetic as syn
 import transformer_gpt_layer_amd as tg
-from tests._common import TOL, filled_caches, gpu_layer_and_oracle_weights, kv8_caches, rel_l2
+from tests._common import TOL, TORCH, filled_caches, gpu_layer_and_oracle_weights, kv8_caches, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +135,11 @@ KV8_CASES = {
                                   act_dtype="f16", batch=2, past=127, cfg_id=233, **AFFINE), 2, False),
     "i8-d128-b1-L2-g5-kv8": (_wl("c1", hidden=5120, heads=40, head_dim=128, ffn=5120, weight_dtype="i8",
                                  act_dtype="f16", group=64, batch=1, past=5, cfg_id=234, **AFFINE), 2, False),
+    # bf16 weights and activations over int8 caches
+    "bf16-d64-b3-L2-tanh-kv8": (_wl("c1", hidden=1024, heads=16, head_dim=64, ffn=2048, weight_dtype="bf16",
+                                    act_dtype="bf16", batch=3, past=41, cfg_id=236, **AFFINE), 2, True),
+    "bf16-d128-b1-L2-g5-kv8": (_wl("c1", hidden=2560, heads=20, head_dim=128, ffn=5120, weight_dtype="bf16",
+                                   act_dtype="bf16", batch=1, past=90, cfg_id=237, **AFFINE), 2, False),
 }
 
 
@@ -146,7 +151,7 @@ def test_stack_decode_with_int8_kv_matches_oracle(name):
     with tg.Stack(gls, kvs, max_batch=wl.batch) as st:
         ws = st.workspace(wl.batch)
         for step in range(3):
-            x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, step, "cuda").half()
+            x = syn.normal((wl.batch, wl.hidden), 1.0, wl.cfg_id, syn.X_LAYER, step, "cuda").to(TORCH[wl.act_dtype])
             y = st.decode(x, workspace=ws)
             st.check()
             xd = x.double().cpu().numpy()
@@ -163,7 +168,8 @@ def test_stack_decode_with_int8_kv_matches_oracle(name):
                 codes = torch.cat([kvs[l].k[:, :, P], kvs[l].v[:, :, P]], 1).cpu().numpy().astype(int)
                 assert np.all(np.abs(codes).max(-1) == 127), "a new row's codes do not reach 127"
             print(f"  step {step}: rel L2 {err:.3e}, of y - x {err_d:.3e}; new rows worst {max(news):.3e}", flush=True)
-            assert err <= TOL["f16"] and err_d <= TOL["f16"] and max(news) <= TOL["f16"], (step, err, err_d, news)
+            tol = TOL[wl.act_dtype]
+            assert err <= tol and err_d <= tol and max(news) <= tol, (step, err, err_d, news)
 
 
 def test_stack_with_int8_kv_matches_the_per_layer_path():

@@ -1550,7 +1550,7 @@ int stack_group_slices(Dt wdt, int H, int F) {
 }
 
 // Instantiated variants: batch tiles of 1 or 4 rows (2..4 sequences use the 4-row tile), head_dim 64
-// or 128, groups of 1 or 5 slices; an int8 cache with fp16 activations.
+// or 128, groups of 1 or 5 slices; an int8 cache with fp16 or bf16 activations.
 static const void* pick(Dt wdt, Dt adt, bool kv8, int B, int D, int GS) {
   const bool one = B <= 1;
 #define DS_PICK_G(WT_, AT_, G_, K_)                                                                           \
@@ -1568,10 +1568,10 @@ static const void* pick(Dt wdt, Dt adt, bool kv8, int B, int D, int GS) {
     if (kv8) DS_PICK_K(WT_, AT_, true)            \
     DS_PICK_K(WT_, AT_, false)                    \
   }
-  if (kv8 && adt != F16) return nullptr;
+  if (kv8 && adt != F16 && adt != BF16) return nullptr;
   if (wdt == F16 && adt == F16) DS_PICK(half_t, half_t)
   if (wdt == I8 && adt == F16) DS_PICK(int8_t, half_t)
-  if (wdt == BF16 && adt == BF16) DS_PICK_K(bf16_t, bf16_t, false)
+  if (wdt == BF16 && adt == BF16) DS_PICK(bf16_t, bf16_t)
   if (wdt == F32 && adt == F32 && one) {
     if (GS == 5) return D == 64 ? kernel_ptr<float, float, 1, 64, 5>() : kernel_ptr<float, float, 1, 128, 5>();
     return D == 64 ? kernel_ptr<float, float, 1, 64, 1>() : kernel_ptr<float, float, 1, 128, 1>();

@@ -182,8 +182,8 @@ int ds_stack_create(const ds_layer_t* const* layers, const ds_kv_cache* caches, 
     if (!layers[l]) return ds::set_error(DS_ERR_NULL, "layer %d is NULL", l);
   const ds_layer_desc d = layers[0]->desc;
   const bool kv8 = d.kv_dtype == DS_I8;
-  if (kv8 && d.act_dtype != DS_F16)
-    return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode with an int8 kv cache needs fp16 activations");
+  if (kv8 && d.act_dtype != DS_F16 && d.act_dtype != DS_BF16)
+    return ds::set_error(DS_ERR_UNSUPPORTED, "persistent decode with an int8 kv cache needs fp16 or bf16 activations");
   for (int l = 1; l < n_layers; ++l)
     if (std::memcmp(&layers[l]->desc, &d, sizeof d) != 0)
       return ds::set_error(DS_ERR_SHAPE, "layer %d has a different description from layer 0", l);
