@@ -49,7 +49,7 @@ struct Route {
 // two passes over the row in LDS; the workgroups of one token compute the same h), the first one
 // stores h rounded to the staged type LT for the experts, and each wave takes kGateExperts / 4
 // experts of the block, its lanes 16-byte pieces of the gate rows, against that same rounded h.
-constexpr int kGateExperts = 16;
+constexpr int kGateExperts = 4;
 
 template <typename AT, typename LT>
 __global__ __launch_bounds__(256) void moe_gate_kernel(const MoeArgs a) {
