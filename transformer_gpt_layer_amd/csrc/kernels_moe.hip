@@ -108,11 +108,24 @@ __global__ __launch_bounds__(256) void moe_gate_kernel(const MoeArgs a) {
 __device__ void moe_topk_token(const MoeArgs& a, int t, int lane) {
   const int E = a.E, K = a.k, KS = a.KS;
   const float* lg = a.logits + (size_t)t * E;
+  // the lane's logits (experts lane + 64 j) read once, all loads in flight together, then their
+  // probabilities kept in registers for the k rounds
+  constexpr int kPerLane = (kMoeMaxExperts + kWave - 1) / kWave;
+  float pv[kPerLane];
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) pv[j] = lane + kWave * j < E ? lg[lane + kWave * j] : -3.0e38f;
   float m = -3.0e38f;
-  for (int e = lane; e < E; e += kWave) m = fmaxf(m, lg[e]);
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) m = fmaxf(m, pv[j]);
   m = wave_max(m);
   float sum = 0.f;
-  for (int e = lane; e < E; e += kWave) sum += expf(lg[e] - m);
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
+    if (lane + kWave * j < E) {
+      pv[j] = expf(pv[j] - m);
+      sum += pv[j];
+    }
+  }
   sum = wave_sum(sum);
   uint32_t taken = 0u;  // bit j: expert lane + 64 j has been chosen
   int esel[kMoeMaxK];
@@ -124,10 +137,11 @@ __device__ void moe_topk_token(const MoeArgs& a, int t, int lane) {
     psel[i] = 0.f;
     if (i >= K) continue;
     uint64_t best = 0ull;
-    for (int e = lane, j = 0; e < E; e += kWave, ++j) {
-      if (taken & (1u << j)) continue;
-      const float p = expf(lg[e] - m);
-      const uint64_t key = ((uint64_t)__builtin_bit_cast(uint32_t, p) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const int e = lane + kWave * j;
+      if (e >= E || (taken & (1u << j))) continue;
+      const uint64_t key = ((uint64_t)__builtin_bit_cast(uint32_t, pv[j]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
       best = key > best ? key : best;
     }
     best = wave_max_u64(best);
