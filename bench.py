@@ -159,6 +159,16 @@ def prefill_flops(wl) -> dict:
 
 
 # ------------------------------------------------------------------ building a stack
+def dtype_label(wl) -> str:
+    """The arithmetic types of a workload: weights (int8 with fp16 activations), cache, MLP groups."""
+    dtype = {"f32": "f32", "f16": "f16", "i8": "i8w-f16", "bf16": "bf16"}[wl.weight_dtype]
+    if wl.extra.get("kv_dtype") == "int8":
+        dtype += "-kv8"
+    if wl.weight_dtype == "i8" and wl.group_mlp:
+        dtype += f"-mlpg{wl.group_mlp}"
+    return dtype
+
+
 def build_stack(wl, torch, tg, syn, layers):
     """Device weights and caches (P seeded rows each) for every layer, one [L, B] length tensor."""
     dev = "cuda"
@@ -390,11 +400,7 @@ def decode_record(args, wl, torch, tg, syn, layers, mode="auto", cpu_s=0.0, voca
     per = algorithmic_bytes_per_layer(wl)
     step_bytes = per["total"] * layers
     use_stack = mode == "stack" or (mode == "auto" and wl.batch <= 4)
-    dtype = {"f32": "f32", "f16": "f16", "i8": "i8w-f16", "bf16": "bf16"}[wl.weight_dtype]
-    if wl.extra.get("kv_dtype") == "int8":
-        dtype += "-kv8"
-    if wl.weight_dtype == "i8" and wl.group_mlp:
-        dtype += f"-mlpg{wl.group_mlp}"
+    dtype = dtype_label(wl)
     reset = lambda: lens.fill_(wl.past)
     extra = {}
     if use_stack:
@@ -482,7 +488,7 @@ def prefill_record(args, wl, torch, tg, syn, layers, cpu_s=0.0):
     dom = max(gemms, key=kt.get)
     tf_dom = fl[dom] / (kt[dom] * 1e-3) / 1e12
     tflops = fl["total"] * layers / (ms * 1e-3) / 1e12
-    rec = _base(wl, layers, ms, args.steps, args.warmup, wl.batch * wl.seq / (ms * 1e-3), "prompt tokens/s", wl.act_dtype,
+    rec = _base(wl, layers, ms, args.steps, args.warmup, wl.batch * wl.seq / (ms * 1e-3), "prompt tokens/s", dtype_label(wl),
                 "per-layer kernels (LN, 4 MFMA GEMMs, flash attention) under a HIP graph")
     rec["metric"] = "prefill prompt tokens/s + MFMA utilization of the prefill GEMMs"
     rec["config"].update({"seq": wl.seq})
@@ -589,11 +595,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle sample per leg (one thread, all threads) for the headline (0 disables)")
     ap.add_argument("--record-cpu-seconds", type=float, default=4.0, help="the same for each nested record")
-    ap.add_argument("--records", default="c2gen,c2bf16,c2kv8,c3,c4b8,c4b1,c4b1m32,c5,c5bf16,moe,moe1",
+    ap.add_argument("--records", default="c2gen,c2bf16,c2kv8,c3,c4b8,c4b1,c4b1m32,c5,c5bf16,c5kv8,c5i8,moe,moe1",
                     help="nested records after the c2 headline (comma list; empty for none): c2gen (the "
                          "generation step with the LM head), c2bf16 (bf16 weights and activations), c2kv8 "
                          "(an int8 KV cache), c3, c4b8, c4b1, c4b1m32 (int8 with groups of 32 in the MLP matrices), c5, c5bf16 "
-                         "(C5 in bf16), moe (the MoE expert FF of the 1.3B + "
+                         "(C5 in bf16), c5kv8 (C5 with an int8 KV cache), c5i8 (C5 with int8 weights), moe (the MoE expert FF of the 1.3B + "
                          "MoE-128 model, 8 tokens), moe1 (the same, 1 token)")
     ap.add_argument("--mode", choices=["auto", "stack", "layers"], default="auto",
                     help="stack: one persistent launch per step; layers: the per-layer kernels")
@@ -643,7 +649,7 @@ def main():
             rec = decode_record(args, w2, torch, tg, syn, w2.layers, "stack", 0.0, vocab=syn.GPT_NEO_VOCAB)
             rec["metric"] = "generation-step tokens/s (32 layers + final LayerNorm + LM head + greedy choice)"
         elif syn.WORKLOADS[name].seq != 1:
-            cs_rec = 0.0 if name == "c5bf16" else cs  # the C5 record's CPU baseline covers the shapes
+            cs_rec = 0.0 if name in ("c5bf16", "c5kv8", "c5i8") else cs  # the C5 record's baseline covers the shapes
             rec = prefill_record(args, syn.WORKLOADS[name], torch, tg, syn, syn.WORKLOADS[name].layers, cs_rec)
         else:
             # the C2 precision variants carry no CPU baseline of their own (the headline's covers C2)

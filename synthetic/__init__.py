@@ -80,9 +80,13 @@ WORKLOADS = {
     "c2bf16": Workload("c2-gptneo2.7b-bf16-b1-p512", 6, 2560, 20, 128, 10240, 32, "bf16", "bf16", 1, 512),
     "c2kv8": Workload("c2-gptneo2.7b-f16-kv8-b1-p512", 7, 2560, 20, 128, 10240, 32, "f16", "f16", 1, 512,
                       extra={"kv_dtype": "int8"}),
-    # the C5 prefill in bf16 weights and activations
+    # the C5 prefill in bf16 weights and activations, with an int8 KV cache, and with int8 weights
     "c5bf16": Workload("c5-gptneo2.7b-bf16-prefill-b4s512", 9, 2560, 20, 128, 10240, 32, "bf16", "bf16", 4, 0,
                        seq=512),
+    "c5kv8": Workload("c5-gptneo2.7b-f16-kv8-prefill-b4s512", 10, 2560, 20, 128, 10240, 32, "f16", "f16", 4, 0,
+                      seq=512, extra={"kv_dtype": "int8"}),
+    "c5i8": Workload("c5-gptneo2.7b-i8g64-prefill-b4s512", 11, 2560, 20, 128, 10240, 32, "i8", "f16", 4, 0,
+                     seq=512, group=64),
 }
 
 
